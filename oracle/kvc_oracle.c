@@ -1,0 +1,652 @@
+/*
+ * kvc_oracle.c -- plain scalar CPU oracle for the paged KV-cache codecs.
+ *
+ * TEST INFRASTRUCTURE ONLY (see kvc_oracle.h).  Build:
+ *   gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC \
+ *       -o libkvc_oracle.so kvc_oracle.c -lm
+ * x86-64 evaluates float expressions in binary32 (SSE, FLT_EVAL_METHOD 0),
+ * so each C float operation below is exactly one RN binary32 operation.
+ *
+ * Citations name the page and its section:
+ *   [OKV-SF] OrbitKV "KV precision and storage encoding":
+ *            "FP8 and TurboQuant" (E4M3FN RNE with signed zero and
+ *            subnormals; nonfinite or |x|>448 segments stay raw; TurboQuant K
+ *            = normalize, deterministic random signs, orthonormal WHT,
+ *            Gaussian Lloyd-Max centroids, norm-corrected inverse with the
+ *            original FP16 norm; V = per-vector uniform quantization with FP16
+ *            minimum and scale; D in {32,64,128,256}; 66/68 and 50/52 byte
+ *            payloads at D=128) and "Ownership, storage and GDS" (segment
+ *            carries version, original length, format, stored length, CRC32;
+ *            keep only when the aligned footprint saves >= 12.5%; sources up
+ *            to 16 MiB are encoded).
+ *   [HIQ]    "Building a quantized HiCache for SGLang": "Building the INT8
+ *            codec" (symmetric per-head INT8: amax floor, scale = amax/127,
+ *            FP32 quotient, round, clamp to +-127; all-zero head restores
+ *            to exact zero).
+ *   [KNLP]   "Asymmetric KV: methods and results": "Precision and scaling
+ *            reference" (FP32 amax clamped at 1e-12, times the rounded FP32
+ *            reciprocal of 448, FP32 divide, clip to +-448, E4M3FN RNE;
+ *            dynamic = per token/head vector; FP32 scales).
+ */
+#define _GNU_SOURCE
+#include "kvc_oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+#define SLOT_ALIGN 256u
+#define HEADER_BYTES 32u
+#define MAX_SEGMENT_BYTES (16u << 20)
+#define MAX_D 256
+
+static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* BF16 is the upper half of a binary32 pattern: widening is exact. */
+float kvo_bf16_to_f32(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+float kvo_f16_to_f32(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31) {
+    if (m) return s ? -NAN : NAN;
+    return s ? -INFINITY : INFINITY;
+  }
+  if (e == 0) v = ldexp((double)m, -24);              /* subnormal */
+  else        v = ldexp((double)(1024 + m), e - 25);  /* normal    */
+  return (float)(s ? -v : v);                         /* exact     */
+}
+
+/* Nearest value of a binary format with p significand bits (hidden bit
+ * included) and minimum normal exponent emin, ties to the even significand.
+ * x / quantum and rint(.) * quantum are exact in double; rint rounds to
+ * nearest-even in the default rounding mode.  No overflow handling here. */
+static double round_to_format(double x, int p, int emin) {
+  int e;
+  if (x == 0.0) return x;
+  frexp(fabs(x), &e);          /* |x| = f * 2^e, f in [0.5, 1) */
+  int ex = e - 1;              /* floor(log2 |x|)               */
+  if (ex < emin) ex = emin;    /* subnormal range: fixed quantum */
+  double quantum = ldexp(1.0, ex - (p - 1));
+  return rint(x / quantum) * quantum;
+}
+
+uint16_t kvo_f32_to_bf16(float x) {
+  if (isnan(x)) return signbit(x) ? 0xFFC0 : 0x7FC0;
+  double q = round_to_format((double)x, 8, -126);
+  if (fabs(q) >= ldexp(1.0, 128)) q = signbit(x) ? -INFINITY : INFINITY;
+  float f = (float)q;          /* exact: q is a bf16 value or infinity */
+  if (f == 0.0f && signbit(x)) f = -0.0f;
+  return (uint16_t)(f2u(f) >> 16);
+}
+
+uint16_t kvo_f32_to_f16(float x) {
+  uint16_t s = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return s | 0x7E00;
+  double q = round_to_format((double)x, 11, -14);
+  double a = fabs(q);
+  if (a >= 65536.0) return s | 0x7C00;          /* rounds past 65504 */
+  if (a == 0.0) return s;
+  int e;
+  frexp(a, &e);
+  int ex = e - 1;
+  if (ex < -14) return s | (uint16_t)(a / ldexp(1.0, -24));   /* subnormal */
+  int mant = (int)(a / ldexp(1.0, ex - 10)) - 1024;
+  return s | (uint16_t)((ex + 15) << 10) | (uint16_t)mant;
+}
+
+/* OCP OFP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; largest finite 448; subnormals step 2^-9.
+ * Precondition |x| <= 448 (the codecs gate or clip before converting). */
+uint8_t kvo_f32_to_e4m3(float x) {
+  uint8_t s = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x) || fabs((double)x) > 448.0) return s | 0x7F;
+  double q = round_to_format((double)x, 4, -6);
+  double a = fabs(q);
+  if (a == 0.0) return s;                       /* signed zero kept */
+  int e;
+  frexp(a, &e);
+  int ex = e - 1;
+  if (ex < -6) return s | (uint8_t)(a / ldexp(1.0, -9));      /* subnormal */
+  int mant = (int)(a / ldexp(1.0, ex - 3)) - 8;
+  return s | (uint8_t)((ex + 7) << 3) | (uint8_t)mant;
+}
+
+float kvo_e4m3_to_f32(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return s ? -NAN : NAN;
+  double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (float)(s ? -v : v);
+}
+
+/* Brute force: the nearest of the finite E4M3FN codes of the same sign as x;
+ * among equidistant candidates the one with an even code (mantissa LSB 0). */
+uint8_t kvo_e4m3_nearest_search(float x) {
+  uint8_t s = signbit(x) ? 0x80 : 0x00;
+  double ax = fabs((double)x);
+  int best = -1;
+  double bestd = 0.0;
+  for (int c = 0; c < 0x7F; c++) {
+    double d = fabs((double)kvo_e4m3_to_f32((uint8_t)c) - ax);
+    if (best < 0 || d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return s | (uint8_t)best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Method constants                                                         */
+/* ------------------------------------------------------------------------ */
+
+static double std_pdf(double t) { return exp(-0.5 * t * t) / sqrt(2.0 * 3.14159265358979323846); }
+static double std_upper_tail(double t) { return 0.5 * erfc(t / sqrt(2.0)); }
+
+/* Lloyd-Max scalar quantizer for the standard Gaussian [OKV-SF "FP8 and
+ * TurboQuant": "Gaussian Lloyd-Max centroids"].  The optimal quantizer is a
+ * fixed point of (1) thresholds at midpoints of neighbouring centroids and
+ * (2) each centroid the conditional mean of its cell:
+ *     c = (pdf(lo) - pdf(hi)) / (P(X > lo) - P(X > hi)).
+ * The quantizer is symmetric, so only the positive half is iterated; the
+ * middle threshold is exactly 0. */
+int kvo_lloyd_max(int bits, double *centroids, double *thresholds) {
+  int n = 1 << bits, m = n / 2, it;
+  double pc[128], tb[129];
+  for (int j = 0; j < m; j++) pc[j] = (j + 0.5) * 3.0 / m;
+  for (it = 1; it <= 2000000; it++) {
+    double maxd = 0.0;
+    tb[0] = 0.0;
+    for (int j = 1; j < m; j++) tb[j] = 0.5 * (pc[j - 1] + pc[j]);
+    for (int j = 0; j < m; j++) {
+      double lo = tb[j];
+      double num, den;
+      if (j == m - 1) {
+        num = std_pdf(lo);
+        den = std_upper_tail(lo);
+      } else {
+        double hi = tb[j + 1];
+        num = std_pdf(lo) - std_pdf(hi);
+        den = std_upper_tail(lo) - std_upper_tail(hi);
+      }
+      double c = num / den;
+      double dd = fabs(c - pc[j]);
+      if (dd > maxd) maxd = dd;
+      pc[j] = c;
+    }
+    if (maxd < 1e-15) break;
+  }
+  for (int j = 0; j < m; j++) {
+    centroids[m + j] = pc[j];
+    centroids[m - 1 - j] = -pc[j];
+  }
+  for (int k = 0; k < n - 1; k++) thresholds[k] = 0.5 * (centroids[k] + centroids[k + 1]);
+  thresholds[m - 1] = 0.0;
+  return it;
+}
+
+/* The FP32 tables for 1..4 bits are computed once when the library loads
+ * (the fixed-point iteration takes milliseconds). */
+static float g_cent[5][16], g_thr[5][15];
+
+__attribute__((constructor)) static void kvo_init_codebooks(void) {
+  double c[16], t[15];
+  for (int bits = 1; bits <= 4; bits++) {
+    int n = 1 << bits;
+    kvo_lloyd_max(bits, c, t);
+    for (int k = 0; k < n; k++) g_cent[bits][k] = (float)c[k];
+    for (int k = 0; k < n - 1; k++) g_thr[bits][k] = (float)t[k];
+  }
+}
+
+void kvo_codebook_f32(int bits, float *centroids, float *thresholds) {
+  int n = 1 << bits;
+  for (int k = 0; k < n; k++) centroids[k] = g_cent[bits][k];
+  for (int k = 0; k < n - 1; k++) thresholds[k] = g_thr[bits][k];
+}
+
+/* SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom number
+ * generators", OOPSLA 2014): state += golden gamma, then the variant-13
+ * finaliser. */
+uint64_t kvo_splitmix64_next(uint64_t *state) {
+  uint64_t z = (*state += 0x9E3779B97F4A7C15ULL);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+/* "deterministic random signs" [OKV-SF "FP8 and TurboQuant"]; the generator
+ * is versioned and our own ("OrbitKV's versioned sign generator ... are its
+ * own").  Version 1: one sign vector per (seed, D), shared by every layer,
+ * head and token. */
+void kvo_signs(uint64_t seed, int d, int8_t *sigma) {
+  uint64_t st = seed;
+  for (int i = 0; i < d; i++) sigma[i] = (kvo_splitmix64_next(&st) >> 63) ? -1 : 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Vector building blocks                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Unnormalised Walsh-Hadamard transform in Sylvester (natural) order: the
+ * matrix H_{2n} = [[H_n, H_n], [H_n, -H_n]]; stage h pairs i and i+h. */
+void kvo_wht_f32(float *v, int d) {
+  for (int h = 1; h < d; h *= 2)
+    for (int i = 0; i < d; i++)
+      if (!(i & h)) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+}
+
+/* sum of squares as a pairwise tree: leaves RN(x_i^2), then adjacent pairs,
+ * then adjacent pairs of pairs, ... */
+float kvo_sumsq_tree(const float *x, int d) {
+  float s[MAX_D];
+  for (int i = 0; i < d; i++) s[i] = x[i] * x[i];
+  for (int w = d; w > 1; w /= 2)
+    for (int i = 0; i < w / 2; i++) s[i] = s[2 * i] + s[2 * i + 1];
+  return s[0];
+}
+
+static float src_to_f32(uint16_t h, int dtype) {
+  return dtype == KVO_BF16 ? kvo_bf16_to_f32(h) : kvo_f16_to_f32(h);
+}
+static uint16_t f32_to_out(float x, int dtype) {
+  return dtype == KVO_BF16 ? kvo_f32_to_bf16(x) : kvo_f32_to_f16(x);
+}
+
+static void put_u16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+static void put_u32(uint8_t *p, uint32_t v) { for (int i = 0; i < 4; i++) p[i] = (uint8_t)(v >> (8 * i)); }
+static void put_u64(uint8_t *p, uint64_t v) { for (int i = 0; i < 8; i++) p[i] = (uint8_t)(v >> (8 * i)); }
+static uint16_t get_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static uint32_t get_u32(const uint8_t *p) { uint32_t v = 0; for (int i = 0; i < 4; i++) v |= (uint32_t)p[i] << (8 * i); return v; }
+static uint64_t get_u64(const uint8_t *p) { uint64_t v = 0; for (int i = 0; i < 8; i++) v |= (uint64_t)p[i] << (8 * i); return v; }
+
+static int codec_bits(int codec) {
+  switch (codec) {
+    case KVO_UNIFORM3: case KVO_TQ3: return 3;
+    case KVO_UNIFORM4: case KVO_TQ4: return 4;
+    case KVO_RAW: return 16;
+    default: return 8;
+  }
+}
+
+/* code k of a vector: LSB-first bit stream, element i at bits [b*i, b*i+b) */
+static void put_code(uint8_t *blk, int i, int b, unsigned code) {
+  for (int k = 0; k < b; k++) {
+    int bit = b * i + k;
+    if ((code >> k) & 1u) blk[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+  }
+}
+static unsigned get_code(const uint8_t *blk, int i, int b) {
+  unsigned c = 0;
+  for (int k = 0; k < b; k++) {
+    int bit = b * i + k;
+    c |= (unsigned)((blk[bit >> 3] >> (bit & 7)) & 1u) << k;
+  }
+  return c;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Format sizes                                                             */
+/* ------------------------------------------------------------------------ */
+
+int kvo_code_bytes(int codec, int d) { return codec_bits(codec) * d / 8; }
+
+int kvo_meta_bytes(int codec) {
+  switch (codec) {
+    case KVO_FP8_DYNAMIC: case KVO_INT8: return 4;          /* FP32 scale   */
+    case KVO_UNIFORM3: case KVO_UNIFORM4: return 4;         /* FP16 min, scale */
+    case KVO_TQ3: case KVO_TQ4: return 2;                   /* FP16 norm    */
+    default: return 0;                                      /* raw, FP8 direct/fixed */
+  }
+}
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t kvo_slot_bytes(int codec, int d, int n_vec) {
+  size_t payload = (size_t)n_vec * (size_t)(kvo_code_bytes(codec, d) + kvo_meta_bytes(codec));
+  return align_up(HEADER_BYTES + payload, SLOT_ALIGN);
+}
+
+/* [OKV-SF "Ownership, storage and GDS"]: keep an encoded segment only when
+ * its aligned footprint saves at least 12.5%; segments above 16 MiB stay raw.
+ * [OKV-SF "FP8 and TurboQuant"]: protected layers stay exact. */
+int kvo_effective_codec(int codec, int d, int n_vec, int is_protected) {
+  size_t orig = (size_t)n_vec * (size_t)d * 2;
+  if (is_protected || codec == KVO_RAW) return KVO_RAW;
+  if (orig > MAX_SEGMENT_BYTES) return KVO_RAW;
+  if (8 * kvo_slot_bytes(codec, d, n_vec) > 7 * orig) return KVO_RAW;
+  return codec;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-vector encoders.  Return 1 if the vector forces the segment raw.      */
+/* ------------------------------------------------------------------------ */
+
+/* [OKV-SF "FP8 and TurboQuant"] direct cast, no scale. */
+static int enc_fp8_direct(const float *x, int d, uint8_t *codes) {
+  for (int i = 0; i < d; i++) codes[i] = kvo_f32_to_e4m3(x[i]);
+  return 0;
+}
+
+/* [KNLP "Precision and scaling reference"]: q = RN(x / s), clip to +-448,
+ * E4M3FN RNE. */
+static void enc_fp8_scaled(const float *x, int d, float s, uint8_t *codes) {
+  for (int i = 0; i < d; i++) {
+    float q = x[i] / s;
+    if (q > 448.0f) q = 448.0f;
+    if (q < -448.0f) q = -448.0f;
+    codes[i] = kvo_f32_to_e4m3(q);
+  }
+}
+
+/* [KNLP]: dynamic scale per token/head vector:
+ * s = RN(max(amax, 1e-12) * RN(1/448)). */
+static float fp8_dynamic_scale(const float *x, int d) {
+  float amax = 0.0f;
+  for (int i = 0; i < d; i++) if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+  if (amax < 1e-12f) amax = 1e-12f;
+  const float r448 = 1.0f / 448.0f;
+  return amax * r448;
+}
+
+/* [HIQ "Building the INT8 codec"]: amax clamped below at the floor (1e-12),
+ * scale = RN(amax / 127) kept in FP32, q = RNE(RN(x / scale)), clamp +-127. */
+static float int8_scale(const float *x, int d) {
+  float amax = 0.0f;
+  for (int i = 0; i < d; i++) if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+  if (amax < 1e-12f) amax = 1e-12f;
+  return amax / 127.0f;
+}
+static void enc_int8(const float *x, int d, float s, uint8_t *codes) {
+  for (int i = 0; i < d; i++) {
+    float q = rintf(x[i] / s);
+    if (q > 127.0f) q = 127.0f;
+    if (q < -127.0f) q = -127.0f;
+    codes[i] = (uint8_t)(int8_t)q;
+  }
+}
+
+/* [OKV-SF "FP8 and TurboQuant"] V: per-vector uniform b-bit quantization with
+ * FP16 minimum and scale.  sigma = RN(RN(max - min) / (2^b - 1)); both are
+ * stored as FP16 and the codes are taken against the stored values:
+ * code = clamp(RNE(RN(x - m_h) * (1/sigma_h)), 0, 2^b - 1), where the product
+ * uses the FP32 reciprocal RN(1/sigma_h) and is rounded once, to an integer.
+ * sigma_h == 0 gives all-zero codes. */
+static int enc_uniform(const float *x, int d, int bits, uint8_t *codes, uint8_t *meta) {
+  int top = (1 << bits) - 1;
+  float mn = x[0], mx = x[0];
+  for (int i = 1; i < d; i++) {
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  float sig = (mx - mn) / (float)top;
+  uint16_t mh = kvo_f32_to_f16(mn), sh = kvo_f32_to_f16(sig);
+  float mhf = kvo_f16_to_f32(mh), shf = kvo_f16_to_f32(sh);
+  put_u16(meta, mh);
+  put_u16(meta + 2, sh);
+  if (!isfinite(mhf) || !isfinite(shf)) return 1;
+  memset(codes, 0, (size_t)(bits * d / 8));
+  if (shf == 0.0f) return 0;
+  float y = 1.0f / shf;
+  for (int i = 0; i < d; i++) {
+    float dd = x[i] - mhf;
+    double p = (double)dd * (double)y;        /* exact: 24 x 24 bits */
+    double c = rint(p);
+    if (c < 0.0) c = 0.0;
+    if (c > (double)top) c = (double)top;
+    put_code(codes, i, bits, (unsigned)c);
+  }
+  return 0;
+}
+
+/* [OKV-SF "FP8 and TurboQuant"] K: normalise, deterministic random signs,
+ * orthonormal WHT, Gaussian Lloyd-Max codes.
+ *   1. ss = pairwise tree of RN(x_i^2); n = RN(sqrt(ss)); n_h = FP16(n).
+ *   2. u_i = RN(x_i * RN(1/n))  (u = 0 when n == 0).
+ *   3. v_i = sigma_i * u_i.
+ *   4. z = unnormalised WHT(v).  The orthonormal transform is WHT/sqrt(D);
+ *      a rotated unit vector has coordinates of variance 1/D, so z (which is
+ *      sqrt(D) times the orthonormal output) is compared with the N(0,1)
+ *      codebook directly.
+ *   5. code_i = #{k : B_k < z_i}  (a value equal to a threshold takes the
+ *      lower cell). */
+static int enc_tq(const float *x, int d, int bits, const int8_t *sigma,
+                  const float *thr, uint8_t *codes, uint8_t *meta) {
+  int nthr = (1 << bits) - 1;
+  float v[MAX_D];
+  float ss = kvo_sumsq_tree(x, d);
+  float n = sqrtf(ss);
+  uint16_t nh = kvo_f32_to_f16(n);
+  put_u16(meta, nh);
+  if (!isfinite(kvo_f16_to_f32(nh))) return 1;
+  if (n == 0.0f) {
+    for (int i = 0; i < d; i++) v[i] = 0.0f;
+  } else {
+    float r = 1.0f / n;
+    for (int i = 0; i < d; i++) {
+      float u = x[i] * r;
+      v[i] = sigma[i] < 0 ? -u : u;
+    }
+  }
+  kvo_wht_f32(v, d);
+  memset(codes, 0, (size_t)(bits * d / 8));
+  for (int i = 0; i < d; i++) {
+    unsigned c = 0;
+    for (int k = 0; k < nthr; k++) if (thr[k] < v[i]) c++;
+    put_code(codes, i, bits, c);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-vector decoders                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* TurboQuant K restore [OKV-SF "FP8 and TurboQuant"]: centroid vector c_hat,
+ * its norm q = tree sum of RN(c_hat_i^2), w = WHT(c_hat) (the inverse of the
+ * orthonormal transform up to the factor sqrt(D)), norm correction
+ * g = RN(n_h / RN(RN(sqrt(q)) * RN(sqrt(D)))), x_hat_i = sigma_i * RN(w_i * g),
+ * rounded to the output type. */
+static void dec_tq(const uint8_t *codes, const uint8_t *meta, int d, int bits,
+                   const int8_t *sigma, const float *cent, int dtype, uint16_t *out) {
+  float c[MAX_D], w[MAX_D];
+  for (int i = 0; i < d; i++) c[i] = cent[get_code(codes, i, bits)];
+  float q = kvo_sumsq_tree(c, d);
+  memcpy(w, c, sizeof(float) * (size_t)d);
+  kvo_wht_f32(w, d);
+  float rd = sqrtf((float)d);
+  float den = sqrtf(q) * rd;
+  float g = kvo_f16_to_f32(get_u16(meta)) / den;
+  for (int i = 0; i < d; i++) {
+    float y = w[i] * g;
+    if (sigma[i] < 0) y = -y;
+    out[i] = f32_to_out(y, dtype);
+  }
+}
+
+static void dec_uniform(const uint8_t *codes, const uint8_t *meta, int d, int bits,
+                        int dtype, uint16_t *out) {
+  float mhf = kvo_f16_to_f32(get_u16(meta));
+  float shf = kvo_f16_to_f32(get_u16(meta + 2));
+  for (int i = 0; i < d; i++) {
+    float t = (float)get_code(codes, i, bits) * shf;   /* exact */
+    out[i] = f32_to_out(mhf + t, dtype);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Segments                                                                 */
+/* ------------------------------------------------------------------------ */
+
+static void write_header(uint8_t *slot, int format, int flags, int dtype, int component,
+                         int d, int n_vec, uint32_t stored, uint64_t spill_off, uint32_t aux) {
+  memset(slot, 0, HEADER_BYTES);
+  slot[0] = 1;                                   /* format version */
+  slot[1] = (uint8_t)format;
+  slot[2] = (uint8_t)flags;
+  slot[3] = (uint8_t)(dtype | (component << 4));
+  put_u16(slot + 4, (uint16_t)d);
+  put_u16(slot + 6, (uint16_t)n_vec);
+  put_u32(slot + 8, (uint32_t)(n_vec * d * 2));  /* original length */
+  put_u32(slot + 12, stored);
+  put_u64(slot + 16, spill_off);
+  put_u32(slot + 24, 0);                         /* CRC32: reserved */
+  put_u32(slot + 28, aux);
+}
+
+int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
+                       int component, int codec, int is_protected,
+                       float fixed_scale, uint64_t seed,
+                       uint8_t *slot, uint8_t *spill, uint64_t spill_offset) {
+  int eff = kvo_effective_codec(codec, d, n_vec, is_protected);
+  size_t orig = (size_t)n_vec * (size_t)d * 2;
+  size_t slot_bytes = kvo_slot_bytes(eff, d, n_vec);
+  memset(slot, 0, slot_bytes);
+  if (eff == KVO_RAW) {
+    write_header(slot, KVO_RAW, 1, dtype, component, d, n_vec, (uint32_t)orig, 0, 0);
+    for (size_t i = 0; i < (size_t)n_vec * (size_t)d; i++) put_u16(slot + HEADER_BYTES + 2 * i, vec[i]);
+    return KVO_SEG_RAW_POLICY;
+  }
+
+  int bits = codec_bits(eff), cb = kvo_code_bytes(eff, d), mb = kvo_meta_bytes(eff);
+  uint8_t *codes = slot + HEADER_BYTES;
+  uint8_t *meta = codes + (size_t)n_vec * (size_t)cb;
+  int8_t sigma[MAX_D];
+  float cent[16], thr[15];
+  if (eff == KVO_TQ3 || eff == KVO_TQ4) {
+    kvo_signs(seed, d, sigma);
+    kvo_codebook_f32(bits, cent, thr);
+  }
+
+  /* segment gate [OKV-SF "FP8 and TurboQuant"]: nonfinite values keep the
+   * segment raw for every codec; FP8 codecs also for any |x| > 448 (source
+   * value) instead of clipping. */
+  int raw = 0;
+  for (size_t i = 0; i < (size_t)n_vec * (size_t)d; i++) {
+    float xv = src_to_f32(vec[i], dtype);
+    if (!isfinite(xv)) raw = 1;
+    if ((eff == KVO_FP8_DIRECT || eff == KVO_FP8_FIXED || eff == KVO_FP8_DYNAMIC) &&
+        fabsf(xv) > 448.0f) raw = 1;
+  }
+
+  float x[MAX_D];
+  for (int v = 0; v < n_vec && !raw; v++) {
+    for (int i = 0; i < d; i++) x[i] = src_to_f32(vec[(size_t)v * d + i], dtype);
+    uint8_t *cv = codes + (size_t)v * cb;
+    uint8_t *mv = meta + (size_t)v * mb;
+    switch (eff) {
+      case KVO_FP8_DIRECT: enc_fp8_direct(x, d, cv); break;
+      case KVO_FP8_FIXED: enc_fp8_scaled(x, d, fixed_scale, cv); break;
+      case KVO_FP8_DYNAMIC: {
+        float s = fp8_dynamic_scale(x, d);
+        put_u32(mv, f2u(s));
+        enc_fp8_scaled(x, d, s, cv);
+        break;
+      }
+      case KVO_INT8: {
+        float s = int8_scale(x, d);
+        put_u32(mv, f2u(s));
+        enc_int8(x, d, s, cv);
+        break;
+      }
+      case KVO_UNIFORM3: case KVO_UNIFORM4: raw |= enc_uniform(x, d, bits, cv, mv); break;
+      case KVO_TQ3: case KVO_TQ4: raw |= enc_tq(x, d, bits, sigma, thr, cv, mv); break;
+      default: return -1;
+    }
+  }
+
+  if (raw) {
+    memset(slot, 0, slot_bytes);
+    write_header(slot, KVO_RAW, 2, dtype, component, d, n_vec, (uint32_t)orig, spill_offset, 0);
+    if (spill)
+      for (size_t i = 0; i < (size_t)n_vec * (size_t)d; i++) put_u16(spill + 2 * i, vec[i]);
+    return KVO_SEG_RAW_DATA;
+  }
+  write_header(slot, eff, 0, dtype, component, d, n_vec, (uint32_t)((size_t)n_vec * (cb + mb)), 0,
+               eff == KVO_FP8_FIXED ? f2u(fixed_scale) : 0);
+  return KVO_SEG_ENCODED;
+}
+
+int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
+                       int dtype, int d, int n_vec, uint64_t seed, uint16_t *out) {
+  if (slot[0] != 1) return -1;
+  int format = slot[1], flags = slot[2];
+  if ((slot[3] & 15) != dtype || get_u16(slot + 4) != d || get_u16(slot + 6) != n_vec) return -1;
+  if (get_u32(slot + 8) != (uint32_t)(n_vec * d * 2)) return -1;
+  size_t nel = (size_t)n_vec * (size_t)d;
+  if (flags & 2) {                                   /* raw, spilled */
+    if (flags & 4) return -1;                        /* spill capacity was exhausted */
+    const uint8_t *src = buf_base + get_u64(slot + 16);
+    for (size_t i = 0; i < nel; i++) out[i] = get_u16(src + 2 * i);
+    return 0;
+  }
+  if (format == KVO_RAW) {
+    for (size_t i = 0; i < nel; i++) out[i] = get_u16(slot + HEADER_BYTES + 2 * i);
+    return 0;
+  }
+  int bits = codec_bits(format), cb = kvo_code_bytes(format, d), mb = kvo_meta_bytes(format);
+  const uint8_t *codes = slot + HEADER_BYTES;
+  const uint8_t *meta = codes + (size_t)n_vec * cb;
+  int8_t sigma[MAX_D];
+  float cent[16], thr[15];
+  if (format == KVO_TQ3 || format == KVO_TQ4) {
+    kvo_signs(seed, d, sigma);
+    kvo_codebook_f32(bits, cent, thr);
+  }
+  float fixed = u2f(get_u32(slot + 28));
+  for (int v = 0; v < n_vec; v++) {
+    const uint8_t *cv = codes + (size_t)v * cb;
+    const uint8_t *mv = meta + (size_t)v * mb;
+    uint16_t *ov = out + (size_t)v * d;
+    switch (format) {
+      case KVO_FP8_DIRECT:
+        for (int i = 0; i < d; i++) ov[i] = f32_to_out(kvo_e4m3_to_f32(cv[i]), dtype);
+        break;
+      case KVO_FP8_FIXED: case KVO_FP8_DYNAMIC: {
+        float s = format == KVO_FP8_FIXED ? fixed : u2f(get_u32(mv));
+        for (int i = 0; i < d; i++) ov[i] = f32_to_out(kvo_e4m3_to_f32(cv[i]) * s, dtype);
+        break;
+      }
+      case KVO_INT8: {
+        float s = u2f(get_u32(mv));
+        for (int i = 0; i < d; i++) ov[i] = f32_to_out((float)(int8_t)cv[i] * s, dtype);
+        break;
+      }
+      case KVO_UNIFORM3: case KVO_UNIFORM4: dec_uniform(cv, mv, d, bits, dtype, ov); break;
+      case KVO_TQ3: case KVO_TQ4: dec_tq(cv, mv, d, bits, sigma, cent, dtype, ov); break;
+      default: return -1;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Array helpers for the test harness (loops over the scalar definitions)    */
+/* ------------------------------------------------------------------------ */
+void kvo_f32_to_e4m3_n(const float *x, uint8_t *out, size_t n) {
+  for (size_t i = 0; i < n; i++) out[i] = kvo_f32_to_e4m3(x[i]);
+}
+void kvo_e4m3_nearest_search_n(const float *x, uint8_t *out, size_t n) {
+  for (size_t i = 0; i < n; i++) out[i] = kvo_e4m3_nearest_search(x[i]);
+}
+void kvo_e4m3_to_f32_n(const uint8_t *c, float *out, size_t n) {
+  for (size_t i = 0; i < n; i++) out[i] = kvo_e4m3_to_f32(c[i]);
+}
+void kvo_f32_to_bf16_n(const float *x, uint16_t *out, size_t n) {
+  for (size_t i = 0; i < n; i++) out[i] = kvo_f32_to_bf16(x[i]);
+}
+void kvo_f32_to_f16_n(const float *x, uint16_t *out, size_t n) {
+  for (size_t i = 0; i < n; i++) out[i] = kvo_f32_to_f16(x[i]);
+}
+void kvo_f16_to_f32_n(const uint16_t *h, float *out, size_t n) {
+  for (size_t i = 0; i < n; i++) out[i] = kvo_f16_to_f32(h[i]);
+}

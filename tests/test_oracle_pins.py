@@ -1,0 +1,499 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print (tests/golden/*.json, each with its citation), library routines
+(torch/numpy dtype casts, scipy's Hadamard matrix, numerical integration),
+closed forms, invariants and brute force on tiny inputs.  No GPU needed.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def f32bits(x):
+    return int(np.float32(x).view(np.uint32))
+
+
+# ------------------------------------------------------------------ E4M3FN
+def _all_bf16_finite_inrange():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = (h.astype(np.uint32) << 16).view(np.float32)
+    m = np.isfinite(x) & (np.abs(x) <= 448)
+    return x[m]
+
+
+def _all_f16_finite_inrange():
+    x = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    m = np.isfinite(x) & (np.abs(x) <= 448)
+    return x[m]
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16"])
+def test_e4m3_exhaustive_vs_nearest_search(oracle, src):
+    """Every finite in-range BF16/FP16 source value: the arithmetic RNE
+    conversion equals a brute-force nearest-value search (ties to the even
+    code) over the 254 finite E4M3FN values."""
+    x = _all_bf16_finite_inrange() if src == "bf16" else _all_f16_finite_inrange()
+    assert x.size == (34754 if src == "bf16" else 48642)
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(x), oracle.e4m3_nearest_search(x))
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16"])
+def test_e4m3_exhaustive_vs_torch(oracle, src):
+    """Library routine: torch's CPU float8_e4m3fn cast (RNE, OCP E4M3FN)."""
+    torch = pytest.importorskip("torch")
+    x = _all_bf16_finite_inrange() if src == "bf16" else _all_f16_finite_inrange()
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(x), ref)
+
+
+def test_e4m3_f32_sweep_vs_torch(oracle):
+    """Random binary32 values in [-448, 448] plus +-4 ulp around every
+    rounding midpoint between neighbouring E4M3FN values."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    lim = f32bits(448.0)
+    bits = rng.integers(0, lim + 1, 400000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32) * np.where(rng.random(bits.size) < 0.5, -1, 1).astype(np.float32)
+    vals = np.sort(oracle.e4m3_to_f32(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = ((vals[1:].astype(np.float64) + vals[:-1]) / 2).astype(np.float32)
+    near = (mids.view(np.uint32)[:, None].astype(np.int64) + np.arange(-4, 5)[None, :]).ravel()
+    near = near[(near >= 0) & (near <= lim)].astype(np.uint32).view(np.float32)
+    x = np.concatenate([x, near, -near])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(x), ref)
+
+
+def test_e4m3_special_values(oracle):
+    for name, val, code in golden("e4m3fn_special_values.json")["cases"]:
+        got = int(oracle.f32_to_e4m3(np.array([val], np.float32))[0])
+        assert got == int(code, 16), name
+
+
+def test_e4m3_decode_table(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3_to_f32(codes)
+    fin = np.isfinite(v)
+    assert fin.sum() == 254 and set(np.nonzero(~fin)[0]) == {0x7F, 0xFF}
+    assert v[fin].max() == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    # decode then encode is the identity on every finite code (incl. -0)
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(v[fin]), codes[fin])
+
+
+# ------------------------------------------------------------ BF16 / FP16
+def test_f16_conversion_vs_numpy(oracle):
+    rng = np.random.default_rng(2)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(1000.0),
+        (rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)).view(np.float32),
+        np.array([65504, 65519.99, 65520, 1e-8, 2 ** -25, 2 ** -24 * 1.5, -0.0], np.float32)])
+    x = x[~np.isnan(x)]
+    np.testing.assert_array_equal(oracle.f32_to_f16(x), x.astype(np.float16).view(np.uint16))
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = oracle.f16_to_f32(h)
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_bf16_conversion_vs_torch(oracle):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    x = (rng.integers(0, 2 ** 32, 500000, dtype=np.uint64).astype(np.uint32)).view(np.float32)
+    x = x[~np.isnan(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_bf16(x), ref)
+
+
+# ------------------------------------------------------------ Lloyd-Max
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lloyd_max_vs_table(oracle, bits):
+    g = golden("lloyd_max_gaussian.json")
+    ref = g["levels"][str(bits)]
+    c, t, _ = oracle.lloyd_max(bits)
+    n = 1 << bits
+    np.testing.assert_allclose(c[n // 2:], ref["centroids"], atol=g["tolerance"])
+    np.testing.assert_allclose(t[n // 2 - 1:], ref["thresholds"], atol=g["tolerance"])
+    np.testing.assert_array_equal(c, -c[::-1])
+    assert t[n // 2 - 1] == 0.0
+    # distortion by numerical integration of (x - Q(x))^2 phi(x)
+    from scipy import integrate
+    pdf = lambda x: math.exp(-x * x / 2) / math.sqrt(2 * math.pi)
+    edges = [-math.inf] + list(t) + [math.inf]
+    mse = sum(integrate.quad(lambda x, ck=ck: (x - ck) ** 2 * pdf(x), edges[k], edges[k + 1],
+                             epsabs=1e-13)[0] for k, ck in enumerate(c))
+    assert abs(mse - ref["mse"]) < 2e-5 * max(1.0, ref["mse"] * 100)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lloyd_max_optimality_conditions(oracle, bits):
+    """Independent check of the fixed point: each centroid equals the
+    conditional mean of its cell computed by numerical integration, and each
+    threshold is the midpoint of its neighbours."""
+    from scipy import integrate
+    c, t, _ = oracle.lloyd_max(bits)
+    pdf = lambda x: math.exp(-x * x / 2) / math.sqrt(2 * math.pi)
+    edges = [-math.inf] + list(t) + [math.inf]
+    for k in range(len(c)):
+        m1 = integrate.quad(lambda x: x * pdf(x), edges[k], edges[k + 1], epsabs=1e-14)[0]
+        m0 = integrate.quad(pdf, edges[k], edges[k + 1], epsabs=1e-14)[0]
+        assert abs(m1 / m0 - c[k]) < 1e-9
+    np.testing.assert_allclose(t, (c[1:] + c[:-1]) / 2, rtol=0, atol=1e-15)
+
+
+def test_codebook_f32_rounding(oracle):
+    for bits in (3, 4):
+        c, t, _ = oracle.lloyd_max(bits)
+        cf, tf = oracle.codebook_f32(bits)
+        np.testing.assert_array_equal(cf, c.astype(np.float32))
+        np.testing.assert_array_equal(tf, t.astype(np.float32))
+        assert np.all(np.diff(tf) > 0) and np.array_equal(tf, -tf[::-1])
+
+
+# ------------------------------------------------------------ signs
+def test_splitmix64_published_vector(oracle):
+    g = golden("splitmix64_seed0.json")
+    assert oracle.splitmix64(g["seed"], 3) == [int(v, 16) for v in g["outputs"]]
+
+
+def test_signs_from_bit63(oracle):
+    outs = oracle.splitmix64(12345, 256)
+    exp = np.array([-1 if (o >> 63) else 1 for o in outs], np.int8)
+    np.testing.assert_array_equal(oracle.signs(12345, 256), exp)
+    s = oracle.signs(0, 256)
+    assert 96 < int((s < 0).sum()) < 160          # roughly balanced
+    assert np.array_equal(oracle.signs(7, 64), oracle.signs(7, 128)[:64])
+
+
+# ------------------------------------------------------------ WHT
+@pytest.mark.parametrize("d", [2, 4, 8, 32, 64, 128, 256])
+def test_wht_equals_hadamard_matrix(oracle, d):
+    """On small integers every FP32 sum is exact, so the fast transform must
+    equal scipy's Sylvester-ordered Hadamard matrix times the vector."""
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(d)
+    v = rng.integers(-1000, 1000, d).astype(np.float32)
+    ref = hadamard(d).astype(np.float64) @ v.astype(np.float64)
+    np.testing.assert_array_equal(oracle.wht(v), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_wht_involution_and_orthonormality(oracle, d):
+    rng = np.random.default_rng(100 + d)
+    v = rng.integers(-1000, 1000, d).astype(np.float32)
+    np.testing.assert_array_equal(oracle.wht(oracle.wht(v)), v * d)   # H H = D I, exact
+    x = rng.standard_normal(d).astype(np.float32)
+    z = oracle.wht(x).astype(np.float64) / math.sqrt(d)               # orthonormal version
+    gamma = d * 2.0 ** -24 / (1 - d * 2.0 ** -24)
+    assert abs(np.linalg.norm(z) - np.linalg.norm(x.astype(np.float64))) <= \
+        4 * math.log2(d) * gamma * np.linalg.norm(x)
+
+
+def test_sumsq_tree(oracle):
+    rng = np.random.default_rng(5)
+    v = rng.integers(-300, 300, 128).astype(np.float32)
+    assert oracle.sumsq_tree(v) == float((v.astype(np.int64) ** 2).sum())    # exact
+    x = rng.standard_normal(256).astype(np.float32)
+    ref = math.fsum(float(a) * float(a) for a in x)
+    assert abs(oracle.sumsq_tree(x) - ref) <= 9 * 2.0 ** -24 * ref
+
+
+# ------------------------------------------------------------ sizes / rules
+def test_payload_sizes(oracle):
+    g = golden("payload_sizes.json")
+    d = g["head_dim"]
+    per = lambda c: oracle.code_bytes(c, d) + oracle.meta_bytes(c)
+    assert per(oracle.TQ4) == g["tq4_k"] and per(oracle.UNIFORM4) == g["uniform4_v"]
+    assert per(oracle.TQ3) == g["tq3_k"] and per(oracle.UNIFORM3) == g["uniform3_v"]
+    assert per(oracle.RAW) == g["original"]
+    assert [per(oracle.TQ3) for d in (32,)] and \
+        [oracle.code_bytes(oracle.TQ3, dd) + 2 for dd in (32, 64, 256)] == [14, 26, 98]
+    assert [oracle.code_bytes(oracle.UNIFORM3, dd) + 4 for dd in (32, 64, 256)] == [16, 28, 100]
+
+
+def test_slot_and_keep_rules(oracle):
+    # 16 tokens x 8 heads x 128: slot = align256(32 + 128*66) = 8704 B
+    assert oracle.slot_bytes(oracle.TQ4, 128, 128) == 8704
+    assert oracle.slot_bytes(oracle.RAW, 128, 128) == 32768 + 256
+    assert oracle.effective_codec(oracle.TQ4, 128, 128, False) == oracle.TQ4
+    assert oracle.effective_codec(oracle.TQ4, 128, 128, True) == oracle.RAW
+    # a single 32-dim vector: 256-B slot saves nothing -> raw (12.5% rule)
+    assert oracle.effective_codec(oracle.INT8, 32, 1, False) == oracle.RAW
+    # > 16 MiB source segment -> raw
+    assert oracle.effective_codec(oracle.FP8_DIRECT, 256, 32769, False) == oracle.RAW
+    assert oracle.effective_codec(oracle.FP8_DIRECT, 256, 32768, False) == oracle.FP8_DIRECT
+
+
+# ------------------------------------------------------------ INT8
+def _bits(vals, dtype):
+    import oracle.kvc_oracle as O
+    vals = np.asarray(vals, np.float32)
+    return O.f32_to_bf16(vals) if dtype == 1 else O.f32_to_f16(vals)
+
+
+def test_int8_worked_example(oracle):
+    g = golden("int8_worked_example.json")
+    vec = np.zeros((16, 128), np.uint16)
+    vec[0, :4] = _bits(g["values"], oracle.BF16)
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.INT8)
+    assert st == oracle.SEG_ENCODED and slot[1] == oracle.INT8
+    assert list(slot[32:36].view(np.int8)) == g["codes"]
+    # all-zero vectors: zero codes, restore to exactly zero
+    assert not slot[32 + 128:32 + 16 * 128].any()
+    out = oracle.decode_segment(slot, None, oracle.BF16, 128, 16)
+    assert not out[1:].any()
+
+
+def test_int8_error_bound(oracle):
+    """|x - x_hat| <= s/2 + 2*127*s*2^-24 + half an output ulp."""
+    rng = np.random.default_rng(6)
+    for dtype in (oracle.BF16, oracle.FP16):
+        x = (rng.standard_normal((64, 128)) * np.exp(rng.standard_normal((64, 1)))).astype(np.float32)
+        vec = _bits(x, dtype)
+        xs = oracle.src_to_f32(vec, dtype)
+        slot, st, _ = oracle.encode_segment(vec, dtype, oracle.INT8)
+        s = slot[32 + 64 * 128:32 + 64 * 132].view(np.float32)
+        # scale rule: s = RN(max(amax, 1e-12) / 127)
+        amax = np.abs(xs).max(axis=1)
+        np.testing.assert_array_equal(s, (np.maximum(amax, np.float32(1e-12)) / np.float32(127)))
+        out = oracle.src_to_f32(oracle.decode_segment(slot, None, dtype, 128, 64), dtype)
+        ulp = np.spacing(np.abs(out)).astype(np.float64) * (2 ** 16 if dtype == oracle.BF16 else 2 ** 13)
+        bound = s[:, None] * (0.5 + 254 * 2.0 ** -24) + ulp / 2 + 1e-30
+        assert np.all(np.abs(out.astype(np.float64) - xs) <= bound)
+
+
+# ------------------------------------------------------------ FP8
+def test_fp8_scale_rule_constants():
+    g = golden("fp8_scale_rule.json")
+    assert hex(f32bits(np.float32(1) / np.float32(448))) == g["recip_448_bits"]
+    assert hex(f32bits(g["amax_floor"])) == g["amax_floor_bits"]
+    assert float(np.float32(1) / np.float32(448)) > 1 / 448  # rounded up: s*448 >= amax
+
+
+def test_fp8_dynamic_invariants(oracle):
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((128, 128)) * np.exp(rng.standard_normal((1, 128)))).astype(np.float32)
+    vec = _bits(x, oracle.BF16)
+    xs = oracle.src_to_f32(vec, oracle.BF16)
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.FP8_DYNAMIC)
+    assert st == oracle.SEG_ENCODED
+    codes = slot[32:32 + 128 * 128].reshape(128, 128)
+    s = slot[32 + 128 * 128:32 + 128 * 132].view(np.float32)
+    r = np.float32(1) / np.float32(448)
+    np.testing.assert_array_equal(s, np.abs(xs).max(1) * r)
+    am = np.abs(xs).argmax(1)
+    picked = codes[np.arange(128), am]
+    assert set(picked.tolist()) <= {0x7E, 0xFE}               # amax element -> +-448
+    np.testing.assert_array_equal(picked >> 7, (xs[np.arange(128), am] < 0).astype(np.uint8))
+    # decode error: half an E4M3 step (relative 2^-4) of the scaled value
+    out = oracle.src_to_f32(oracle.decode_segment(slot, None, oracle.BF16, 128, 128), oracle.BF16)
+    err = np.abs(out - xs)
+    assert np.all(err <= np.maximum(np.abs(xs) * 2.0 ** -4, s[:, None] * 2.0 ** -10) * 1.02 +
+                  np.abs(out) * 2.0 ** -8)
+
+
+@pytest.mark.parametrize("codec", ["FP8_DIRECT", "FP8_FIXED", "FP8_DYNAMIC", "INT8", "UNIFORM4", "TQ4"])
+def test_segment_gate(oracle, codec):
+    c = getattr(oracle, codec)
+    fp8 = codec.startswith("FP8")
+    base = np.full((16, 128), 0x3F80, np.uint16)          # bf16 1.0
+    cases = {0x7FC0: True, 0x7F80: True, 0xFF80: True,    # NaN, +Inf, -Inf
+             0x43E1: fp8, 0xC3E1: fp8, 0x447A: fp8,       # +-450 (next bf16 above 448), 1000
+             0x43E0: False, 0xC3E0: False}                # +-448 exactly: never raw
+    for bits, raw in cases.items():
+        v = base.copy()
+        v[5, 17] = bits
+        slot, st, spill = oracle.encode_segment(v, oracle.BF16, c, fixed_scale=0.25,
+                                                spill_offset=1 << 20)
+        assert (st == oracle.SEG_RAW_DATA) == raw, hex(bits)
+        if raw:
+            assert slot[1] == oracle.RAW and slot[2] == 2
+            assert slot[16:24].view(np.uint64)[0] == 1 << 20
+            np.testing.assert_array_equal(spill.view(np.uint16), v.ravel())   # bit-exact
+            buf = np.zeros((1 << 20) + spill.size, np.uint8)
+            buf[1 << 20:] = spill
+            np.testing.assert_array_equal(oracle.decode_segment(slot, buf, oracle.BF16, 128, 16), v)
+
+
+def test_fp8_direct_roundtrip_exact_on_representable(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3_to_f32(codes)
+    vals = vals[np.isfinite(vals)]
+    vec = np.resize(oracle.f32_to_bf16(vals), (16, 128)).astype(np.uint16)
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.FP8_DIRECT)
+    out = oracle.decode_segment(slot, None, oracle.BF16, 128, 16)
+    np.testing.assert_array_equal(out, vec)
+
+
+# ------------------------------------------------------------ uniform
+@pytest.mark.parametrize("bits", [3, 4])
+def test_uniform_nearest_level(oracle, bits):
+    """Brute force: every code is the nearest level m_h + k*sigma_h of the
+    stored FP16 grid (clamped to the code range), ties to even k."""
+    rng = np.random.default_rng(8)
+    codec = oracle.UNIFORM3 if bits == 3 else oracle.UNIFORM4
+    x = rng.standard_normal((16, 32)).astype(np.float32) * 3
+    vec = _bits(x, oracle.BF16)
+    xs = oracle.src_to_f32(vec, oracle.BF16)
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, codec)
+    assert st == oracle.SEG_ENCODED
+    cb = bits * 32 // 8
+    top = (1 << bits) - 1
+    meta = slot[32 + 16 * cb:32 + 16 * (cb + 4)].view(np.uint16).reshape(16, 2)
+    for v in range(16):
+        m = float(oracle.f16_to_f32(meta[v, 0]))
+        sg = float(oracle.f16_to_f32(meta[v, 1]))
+        # FP16 min and scale: sigma = RN(RN(max - min) / (2^b - 1))
+        assert meta[v, 0] == oracle.f32_to_f16(xs[v].min())
+        assert meta[v, 1] == oracle.f32_to_f16((xs[v].max() - xs[v].min()) / np.float32(top))
+        blk = slot[32 + v * cb:32 + (v + 1) * cb]
+        stream = np.unpackbits(blk, bitorder="little")
+        codes = [int(sum(stream[bits * i + k] << k for k in range(bits))) for i in range(32)]
+        y = np.float32(1) / np.float32(sg)
+        for i in range(32):
+            t = float(np.float32(xs[v, i] - np.float32(m))) * float(y)   # exact in double
+            dist = [abs(t - k) for k in range(top + 1)]
+            best = min(dist)
+            cands = [k for k in range(top + 1) if dist[k] == best]
+            assert codes[i] in cands and (len(cands) == 1 or codes[i] % 2 == 0)
+        dec = oracle.src_to_f32(oracle.decode_segment(slot, None, oracle.BF16, 32, 16)[v], oracle.BF16)
+        assert np.all(np.abs(dec - xs[v]) <= sg / 2 * 1.001 + abs(m - xs[v].min()) +
+                      np.abs(dec) * 2.0 ** -8)
+
+
+def test_uniform_constant_vector(oracle):
+    vec = np.full((16, 64), 0x4040, np.uint16)            # bf16 3.0
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.UNIFORM4)
+    assert st == oracle.SEG_ENCODED and not slot[32:32 + 16 * 32].any()
+    np.testing.assert_array_equal(oracle.decode_segment(slot, None, oracle.BF16, 64, 16), vec)
+
+
+# ------------------------------------------------------------ TurboQuant
+def _tq_codes(slot, n_vec, d, bits):
+    cb = bits * d // 8
+    out = np.zeros((n_vec, d), np.int64)
+    for v in range(n_vec):
+        stream = np.unpackbits(slot[32 + v * cb:32 + (v + 1) * cb], bitorder="little")
+        out[v] = stream.reshape(d, bits) @ (1 << np.arange(bits))
+    return out
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_tq_closed_form_basis_vector(oracle, bits):
+    """x = sigma (.) H_j (a signed Hadamard row, D = 64, |x_i| = 1): n = 8,
+    u = x/8 exactly, v = H_j / 8, z = H v = 8 e_j exactly.  So every code is
+    the code of 0 (2^(b-1) - 1) except position j, which takes the top code."""
+    from scipy.linalg import hadamard
+    d, seed = 64, 99
+    sig = oracle.signs(seed, d).astype(np.float32)
+    H = hadamard(d).astype(np.float32)
+    vecs = np.stack([sig * H[j] for j in range(16)])
+    slot, st, _ = oracle.encode_segment(_bits(vecs, oracle.BF16), oracle.BF16,
+                                        oracle.TQ3 if bits == 3 else oracle.TQ4, seed=seed)
+    assert st == oracle.SEG_ENCODED
+    codes = _tq_codes(slot, 16, d, bits)
+    exp = np.full((16, d), (1 << (bits - 1)) - 1)
+    exp[np.arange(16), np.arange(16)] = (1 << bits) - 1
+    np.testing.assert_array_equal(codes, exp)
+    norms = slot[32 + 16 * bits * 8:32 + 16 * bits * 8 + 32].view(np.uint16)
+    assert np.all(norms == 0x4800)                           # FP16 8.0
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_tq_bucketize_is_nearest_centroid(oracle, bits):
+    """Brute force over a segment: each code is the index of the nearest
+    FP32 centroid to z = WHT(sigma * RN(x * RN(1/n)))."""
+    rng = np.random.default_rng(9)
+    d, seed = 32, 5
+    x = rng.standard_normal((16, d)).astype(np.float32)
+    vec = _bits(x, oracle.BF16)
+    xs = oracle.src_to_f32(vec, oracle.BF16)
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.TQ3 if bits == 3 else oracle.TQ4,
+                                        seed=seed)
+    codes = _tq_codes(slot, 16, d, bits)
+    cent, _ = oracle.codebook_f32(bits)
+    sig = oracle.signs(seed, d).astype(np.float32)
+    for v in range(16):
+        n = np.float32(math.sqrt(oracle.sumsq_tree(xs[v])))
+        u = xs[v] * (np.float32(1) / n)
+        z = oracle.wht(sig * u)
+        dist = np.abs(z[:, None].astype(np.float64) - cent[None, :])
+        np.testing.assert_array_equal(codes[v], dist.argmin(1))
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_tq_scale_invariance_and_norm(oracle, d):
+    """Scaling x by a power of two leaves every code unchanged (u is exactly
+    the same); the restored vector has the stored FP16 norm."""
+    rng = np.random.default_rng(10 + d)
+    x = rng.standard_normal((16, d)).astype(np.float32)
+    a, st, _ = oracle.encode_segment(_bits(x, oracle.BF16), oracle.BF16, oracle.TQ4, seed=3)
+    b, st2, _ = oracle.encode_segment(_bits(x * 8, oracle.BF16), oracle.BF16, oracle.TQ4, seed=3)
+    cb = d // 2
+    np.testing.assert_array_equal(a[32:32 + 16 * cb], b[32:32 + 16 * cb])
+    nh = oracle.f16_to_f32(a[32 + 16 * cb:32 + 16 * cb + 32].view(np.uint16))
+    out = oracle.src_to_f32(oracle.decode_segment(a, None, oracle.BF16, d, 16, seed=3), oracle.BF16)
+    np.testing.assert_allclose(np.linalg.norm(out.astype(np.float64), axis=1), nh, rtol=2 ** -7)
+
+
+def test_tq_distortion_matches_lloyd_max(oracle):
+    """Statistical: for Gaussian vectors the relative reconstruction error
+    ||x - x_hat||^2 / ||x||^2 is close to the per-coordinate Lloyd-Max
+    distortion (norm correction adds a little)."""
+    g = golden("lloyd_max_gaussian.json")
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((128, 128)).astype(np.float32)
+    for bits, codec in ((3, oracle.TQ3), (4, oracle.TQ4)):
+        vec = _bits(x, oracle.FP16)
+        xs = oracle.src_to_f32(vec, oracle.FP16)
+        slot, st, _ = oracle.encode_segment(vec, oracle.FP16, codec, seed=1)
+        out = oracle.src_to_f32(oracle.decode_segment(slot, None, oracle.FP16, 128, 128, seed=1),
+                                oracle.FP16)
+        rel = ((out - xs) ** 2).sum() / (xs ** 2).sum()
+        mse = g["levels"][str(bits)]["mse"]
+        assert 0.7 * mse < rel < 1.3 * mse
+
+
+def test_raw_policy_roundtrip_bit_exact(oracle):
+    rng = np.random.default_rng(12)
+    vec = rng.integers(0, 65536, (128, 128), dtype=np.uint64).astype(np.uint16)   # incl. NaNs
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.TQ4, is_protected=True)
+    assert st == oracle.SEG_RAW_POLICY and slot[1] == oracle.RAW and slot[2] == 1
+    np.testing.assert_array_equal(oracle.decode_segment(slot, None, oracle.BF16, 128, 128), vec)
+
+
+def test_header_fields(oracle):
+    rng = np.random.default_rng(13)
+    vec = _bits(rng.standard_normal((128, 128)), oracle.FP16)
+    slot, st, _ = oracle.encode_segment(vec, oracle.FP16, oracle.FP8_FIXED, component=1,
+                                        fixed_scale=0.5)
+    h = slot[:32]
+    assert h[0] == 1 and h[1] == oracle.FP8_FIXED and h[2] == 0 and h[3] == (2 | 1 << 4)
+    assert h[4:6].view(np.uint16)[0] == 128 and h[6:8].view(np.uint16)[0] == 128
+    assert h[8:12].view(np.uint32)[0] == 32768 and h[12:16].view(np.uint32)[0] == 128 * 128
+    assert h[28:32].view(np.float32)[0] == 0.5
+    assert len(slot) == 16640 and not slot[32 + 16384:].any()   # zero padding
+
+
+def test_int8_round_half_to_even(oracle):
+    """The page's codec rounds the FP32 quotient with torch's round(), which
+    is half-to-even.  With amax = 127 the scale is exactly 1.0, so x itself is
+    the quotient: 62.5 -> 62, 63.5 -> 64, -62.5 -> -62, 0.5 -> 0, 2.5 -> 2."""
+    vals = [127.0, 62.5, 63.5, -62.5, 0.5, 1.5, 2.5, -0.5]
+    vec = np.zeros((16, 32), np.uint16)
+    vec[0, :len(vals)] = _bits(vals, oracle.BF16)
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.INT8)
+    assert st == oracle.SEG_ENCODED
+    assert list(slot[32:32 + len(vals)].view(np.int8)) == [127, 62, 64, -62, 0, 2, 2, 0]
+    assert slot[32 + 16 * 32:36 + 16 * 32].view(np.float32)[0] == 1.0
