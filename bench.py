@@ -1,0 +1,181 @@
+#!/usr/bin/env python3
+"""Benchmark: encode + decode of paged KV blocks on one MI355X.
+
+Workload (default): TurboQuant-4 K + uniform-4 V on a Llama-3-8B-shaped
+cache -- 32 layers, 8 KV heads, head_dim 128, BF16, separate K/V tensors,
+16-token pages, a pool of 8192 blocks of which 4096 (64K tokens) are picked
+at random; layers 0, 1, 30, 31 are protected (stored raw).  Inputs are
+synthetic (seeded N(0,1) K with lognormal channel scales, N(0,1) V) and
+resident in HBM before timing starts.
+
+One step = kvc_encode_pages over all 4096 pages x 32 layers (one launch)
++ kvc_decode_pages of the result into a second pool (one launch).
+value = original KV bytes / step time (GB/s of original KV round-tripped).
+
+Prints one JSON line.  --gpus N > 1 is not supported (single-GPU path).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(L, n_pages, H, T, D, prot, kb, vb):
+    """Bytes one launch must move (either direction): every source element
+    (2 B) plus, per segment, the 32-B header and the payload -- b*D/8 code
+    bytes + metadata per vector for encoded segments, 2*D per vector for
+    policy-raw segments."""
+    n_vec = H * T
+    tot = 0
+    for l in range(L):
+        for per_vec in ((2 * D, 2 * D) if l in prot else (kb, vb)):
+            tot += n_pages * (n_vec * 2 * D + 32 + n_vec * per_vec)
+    return tot
+
+
+def cpu_baseline(ks, vs, ids, H, T, D, prot, seed, pages_sample, threads):
+    """The CPU oracle on a bounded sample (pages_sample pages, all layers)."""
+    import numpy as np
+    import torch
+
+    from oracle import kvc_oracle as O
+    L = len(ks)
+    sample = ids[:pages_sample]
+    idx = torch.tensor(sorted(set(int(p) for p in sample)), dtype=torch.long, device=ks[0].device)
+    remap = {int(b): j for j, b in enumerate(idx.tolist())}
+
+    def u16(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+
+    host = O.HostLayout(O.BF16, L, H, D, T, len(remap), T * H * D, H * D, D,
+                        [u16(t.index_select(0, idx)) for t in ks], [u16(t.index_select(0, idx)) for t in vs])
+    mapped = np.array([remap[int(p)] for p in sample], np.int32)
+    protl = [1 if l in prot else 0 for l in range(L)]
+    t0 = time.perf_counter()
+    buf, st, offs, total = O.encode_pages(host, O.TQ4, O.UNIFORM4, seed, mapped, protected=protl,
+                                          threads=threads)
+    t1 = time.perf_counter()
+    out = O.HostLayout(O.BF16, L, H, D, T, len(remap), T * H * D, H * D, D,
+                       [np.zeros_like(a) for a in host.k], [np.zeros_like(a) for a in host.v])
+    O.decode_pages(buf, out, O.TQ4, O.UNIFORM4, seed, mapped, protected=protl, threads=threads)
+    t2 = time.perf_counter()
+    orig = L * len(sample) * 2 * T * H * D * 2
+    return {"value": round(orig / (t2 - t0) / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sample)} pages x {L} layers x K,V ({orig / 2**20:.0f} MiB of original KV), "
+                      f"encode {t1 - t0:.2f} s + decode {t2 - t1:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-pages", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this path runs on one GPU only (no multi-GPU sharding is built); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_page_kvc_amd as kvc
+    from kv_cache_page_kvc_amd import inputs
+
+    cfg = inputs.CONFIGS["tq4_u4_llama3"]
+    L, H, D, T, pool, n = cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], cfg["pages"]
+    prot = list(cfg["protected"])
+    seed = 0
+    torch.cuda.set_device(0)
+    ks, vs = inputs.separate_kv(L, pool, T, H, D, torch.bfloat16, seed=seed, device="cuda")
+    dks = [torch.empty_like(t) for t in ks]
+    dvs = [torch.empty_like(t) for t in vs]
+    lay = kvc.Layout.separate(ks, vs, H, D, T)
+    dlay = kvc.Layout.separate(dks, dvs, H, D, T)
+    ids = inputs.random_page_ids(pool, n, seed=seed)
+    codec = kvc.Codec("TQ4", "UNIFORM4", seed=seed, protected_layers=prot, layers=L)
+    slot, spill, bpt = kvc.kvc_plan(lay, codec, n)
+    total = slot + spill
+    out = torch.empty(total, dtype=torch.uint8, device="cuda")
+    desc = torch.empty(L * n * 2 * 32, dtype=torch.uint8, device="cuda")
+    ctx = kvc.kvc_create(0, 0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        kvc.kvc_encode_pages(ctx, lay, codec, ids, out.data_ptr(), total, desc.data_ptr(), sh)
+        if ev:
+            ev[1].record(stream)
+        kvc.kvc_decode_pages(ctx, dlay, codec, out.data_ptr(), total, ids, 0, sh)
+        if ev:
+            ev[2].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    d = desc.cpu().numpy().view(kvc.DESC_DTYPE)
+    n_raw_data = int((d["status"] == kvc.KVC_SEG_RAW_DATA).sum() + (d["status"] == kvc.KVC_SEG_CAPACITY).sum())
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    orig = L * n * 2 * T * H * D * 2
+    kb, vb = D // 2 + 2, D // 2 + 4
+    alg = algorithmic_bytes(L, n, H, T, D, prot, kb, vb)
+    enc_gbps, dec_gbps = alg / enc_ms / 1e6, alg / dec_ms / 1e6
+    dom = "encode" if enc_ms >= dec_ms else "decode"
+    dom_ms = max(enc_ms, dec_ms)
+    achieved = alg / dom_ms / 1e6
+    result = {
+        "metric": "encode+decode GB/s of original KV and % of HBM peak, TurboQuant-4 D=128",
+        "value": round(orig / (ms_per_step / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "TurboQuant-4 K + uniform-4 V, Llama-3-8B shape: 32 layers, 8 KV heads, "
+                               "D=128, BF16, separate K/V, 16-token pages, 4096 random pages of an "
+                               "8192-block pool (64K tokens), layers 0,1,30,31 raw",
+                   "layers": L, "kv_heads": H, "head_dim": D, "tokens_per_page": T, "pages": n,
+                   "pool_blocks": pool, "original_bytes": orig, "parallelism": "none"},
+        "encode_ms": round(enc_ms, 4), "decode_ms": round(dec_ms, 4),
+        "encode_GBps_original": round(orig / enc_ms / 1e6, 1),
+        "decode_GBps_original": round(orig / dec_ms / 1e6, 1),
+        "encode_hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
+        "decode_hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_launch": alg, "bytes_per_token_encoded": bpt,
+        "raw_data_segments": n_raw_data,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    kvc.kvc_destroy(ctx)
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        print(f"[bench] cpu baseline ({threads} threads)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(ks, vs, ids, H, T, D, prot, seed, args.cpu_sample_pages, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

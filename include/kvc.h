@@ -1,0 +1,224 @@
+/*
+ * kvc.h -- C ABI of libkvc: GPU encode/decode of paged KV-cache blocks on
+ * AMD Instinct MI355X (gfx950), before offload and on restore.
+ *
+ * The operations are the ones described on these pages:
+ *   [OKV-SF] OrbitKV docs, "KV precision and storage encoding":
+ *            "FP8 and TurboQuant" (codecs, raw fallback, head dims, protected
+ *            layers, payload sizes, layout validation for vLLM's packed
+ *            [block, head, token, 2 x head_dim] layout and separate K/V
+ *            tensors) and "Ownership, storage and GDS" (segment header:
+ *            version, original length, format, stored length, CRC32; 12.5%
+ *            keep rule; 16 MiB source cap; batched descriptor-based launches
+ *            with statuses collected once per batch; retained arena;
+ *            destinations validated for the whole request; teardown drains).
+ *   [HIQ]    "Building a quantized HiCache for SGLang": "Building the INT8
+ *            codec" (per-vector symmetric INT8) and "Integrating the codec"
+ *            (the pool reports the encoded size per token).
+ *   [KNLP]   "Asymmetric KV: methods and results": "Precision and scaling
+ *            reference" (FP8 E4M3FN scale rule, fixed or per token/head).
+ *
+ * Conventions
+ *  - All sizes are in bytes, all strides in elements.  Pointers are device
+ *    pointers unless the comment says host.
+ *  - Every call validates its arguments on the host first.  On any error it
+ *    returns a nonzero kvc_status and has enqueued nothing and written
+ *    nothing.
+ *  - Encode/decode are asynchronous on the caller's HIP stream (never a host
+ *    synchronisation, except to recycle the library's own small staging
+ *    memory when more than a handful of calls are still in flight).  The
+ *    caller owns the KV tensors, the page-id arrays, the encoded buffer and
+ *    the descriptor array; the library owns only its arena.
+ *  - A context may be used from one host thread at a time.
+ *
+ * Encoded format (version 1)
+ *  Segment = (page, layer, component K or V) = T*H vectors of D elements, in
+ *  canonical vector order v = token*H + head.  Segments of one call are laid
+ *  out layer-major: s = ((layer * n_pages) + i) * 2 + component, each in its
+ *  own slot at a deterministic offset (kvc_plan):
+ *      slot = [32-B header][codes block: n_vec * code_bytes]
+ *             [metadata block: n_vec * meta_bytes][zero padding to 256 B]
+ *  Header (little-endian): u8 version=1, u8 format (codec of the stored
+ *  bytes, KVC_RAW when raw), u8 flags (KVC_FLAG_*), u8 dtype | component<<4,
+ *  u16 head_dim, u16 n_vec, u32 original_len, u32 stored_len,
+ *  u64 spill_offset, u32 crc32 (0: reserved), u32 aux (FP8_FIXED scale bits).
+ *  Codes are packed LSB-first (element i at bits [b*i, b*i+b) of the vector's
+ *  code block); metadata per vector: FP32 scale (FP8_DYNAMIC, INT8), FP16 min
+ *  + FP16 scale (UNIFORM*), FP16 norm (TQ*).
+ *  A segment that must stay raw because of its data (a nonfinite value, an
+ *  FP8 source value with |x| > 448, an FP16 metadata overflow) keeps its
+ *  slot header (flags RAW_DATA) and its raw bytes go to the spill region of
+ *  the output buffer (everything after the slot region), at spill_offset.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1u
+#define KVC_FORMAT_VERSION 1u
+#define KVC_SLOT_ALIGN 256u
+#define KVC_HEADER_BYTES 32u
+#define KVC_MAX_SEGMENT_BYTES (16u << 20)
+#define KVC_DEFAULT_WORKSPACE (64u << 20)
+
+typedef struct kvc_ctx kvc_ctx;   /* opaque: one HIP device, its arena */
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_E_ARG = 1,          /* null pointer, bad enum, bad stride/alignment, bad scale */
+  KVC_E_UNSUPPORTED = 2,  /* head_dim not in {32,64,128,256}, layout/dtype not supported */
+  KVC_E_PAGE_RANGE = 3,   /* a page id outside [0, num_blocks) */
+  KVC_E_DUP_DST = 4,      /* the same destination page twice in one decode */
+  KVC_E_CAPACITY = 5,     /* output/input buffer smaller than the plan */
+  KVC_E_BUDGET = 6,       /* per-call metadata exceeds the workspace budget */
+  KVC_E_HIP = 7           /* a HIP runtime call failed */
+} kvc_status;
+
+typedef enum { KVC_BF16 = 1, KVC_FP16 = 2 } kvc_dtype;
+
+typedef enum {
+  KVC_SEPARATE_NHD = 1,   /* per layer two tensors, K and V: [block][token][head][D] */
+  KVC_PACKED_HT2D = 2     /* per layer one tensor (vLLM): [block][head][token][2*D], K then V */
+} kvc_layout_kind;
+
+/* Engine tensor geometry [OKV-SF "FP8 and TurboQuant": the packed and the
+ * separate K/V layouts are validated explicitly; layout is never inferred
+ * from byte counts].  Element (block b, token t, head h, dim i) of component
+ * c is at  base_c + b*stride_block + t*stride_token + h*stride_head + i,
+ * where base_K = k_base[l] and base_V = v_base[l] (separate) or
+ * k_base[l] + head_dim (packed).  The innermost dimension is contiguous.
+ * Requirements: base pointers 16-B aligned, strides positive multiples of 8
+ * elements; SEPARATE_NHD: stride_head >= D, stride_token >= H*stride_head,
+ * stride_block >= T*stride_token; PACKED_HT2D: stride_token >= 2*D,
+ * stride_head >= T*stride_token, stride_block >= H*stride_head. */
+typedef struct {
+  uint32_t abi;                 /* KVC_ABI_VERSION */
+  uint32_t kind;                /* kvc_layout_kind */
+  uint32_t dtype;               /* kvc_dtype */
+  uint32_t layers, kv_heads, head_dim, tokens_per_page;
+  uint32_t reserved;
+  uint64_t num_blocks;          /* pages per layer tensor */
+  int64_t stride_block, stride_token, stride_head;
+  void *const *k_base;          /* host array [layers] of device pointers */
+  void *const *v_base;          /* host array [layers]; NULL for PACKED_HT2D */
+} kvc_layout;
+
+typedef enum {
+  KVC_RAW = 0,          /* stored unchanged */
+  KVC_FP8_DIRECT = 1,   /* E4M3FN RNE cast, no scale [OKV-SF "FP8 and TurboQuant"] */
+  KVC_FP8_FIXED = 2,    /* E4M3FN of RN(x/s), s per layer/component, clip +-448 [KNLP] */
+  KVC_FP8_DYNAMIC = 3,  /* same with s = RN(max(amax,1e-12) * RN(1/448)) per vector [KNLP] */
+  KVC_INT8 = 4,         /* s = RN(max(amax,1e-12)/127), q = RNE(RN(x/s)) clamp +-127 [HIQ] */
+  KVC_UNIFORM3 = 5,     /* per-vector uniform 3-bit, FP16 min and scale [OKV-SF] */
+  KVC_UNIFORM4 = 6,     /* per-vector uniform 4-bit, FP16 min and scale [OKV-SF] */
+  KVC_TQ3 = 7,          /* TurboQuant MSE 3-bit + FP16 norm [OKV-SF] */
+  KVC_TQ4 = 8           /* TurboQuant MSE 4-bit + FP16 norm [OKV-SF] */
+} kvc_codec_id;
+
+/* Codec choice per component.  fixed_scales: host array [layers][2] (K, V)
+ * of FP32 scales, required iff a component uses KVC_FP8_FIXED (each must be
+ * finite and in [2^-100, 2^100]).  protected_layers: host bitmap
+ * [ceil(layers/8)] (bit l%8 of byte l/8), or NULL; protected layers stay
+ * exact [OKV-SF "FP8 and TurboQuant": the first and last two layers of each
+ * pipeline stage remain exact -- the caller marks them].  seed: rotation
+ * seed of the TurboQuant sign generator (SplitMix64, version 1). */
+typedef struct {
+  uint32_t k, v;                       /* kvc_codec_id */
+  uint64_t seed;
+  const float *fixed_scales;
+  const uint8_t *protected_layers;
+} kvc_codec;
+
+/* Segment status, written by encode into kvc_segment_desc.status */
+enum {
+  KVC_SEG_ENCODED = 0,    /* stored with the requested codec */
+  KVC_SEG_RAW_POLICY = 1, /* raw in its slot: protected layer, KVC_RAW, keep rule, size cap */
+  KVC_SEG_RAW_DATA = 2,   /* raw because of its data, bytes in the spill region */
+  KVC_SEG_CAPACITY = 3,   /* raw because of its data but the spill region was full: NOT stored */
+  KVC_SEG_GUARD = 4       /* the kernel's own range check on its staged descriptor failed:
+                             nothing was read or written for this segment (never expected) */
+};
+/* header / descriptor flags */
+enum { KVC_FLAG_RAW_POLICY = 1, KVC_FLAG_RAW_DATA = 2, KVC_FLAG_CAPACITY = 4 };
+
+/* One per segment, written by encode on the device (32 B).  Offsets are
+ * relative to the start of the encode output buffer. */
+typedef struct {
+  uint64_t offset;        /* slot offset */
+  uint64_t spill_offset;  /* raw bytes for KVC_SEG_RAW_DATA, else 0 */
+  uint32_t stored_len;    /* payload bytes (codes + metadata, or raw bytes) */
+  uint32_t original_len;  /* n_vec * D * element size */
+  uint8_t version, format, flags, status;
+  uint32_t crc32;         /* 0: reserved */
+} kvc_segment_desc;
+
+/* Create a context on HIP device `hip_device` with a retained device arena
+ * of `workspace_budget` bytes (0 = KVC_DEFAULT_WORKSPACE, the analogue of
+ * OrbitKV's --storage-codec-budget default of 64 MB) holding per-call
+ * descriptors and codebooks [OKV-SF "Ownership, storage and GDS"].
+ * Errors: KVC_E_ARG (ctx NULL), KVC_E_HIP. */
+kvc_status kvc_create(kvc_ctx **ctx, int hip_device, size_t workspace_budget);
+
+/* Wait for all work the context launched, then free its memory
+ * [OKV-SF: teardown drains GPU work before releasing memory].  NULL is a
+ * no-op. */
+kvc_status kvc_destroy(kvc_ctx *ctx);
+
+/* Sizes for a call over n_pages pages (host only, no GPU needed):
+ *  slot_bytes: bytes of the slot region (the output must be at least this);
+ *  spill_bytes_suggested: a spill region for ~3% of the encodable segments
+ *    (at least one segment) -- data-dependent raw segments beyond the spill
+ *    capacity get KVC_SEG_CAPACITY;
+ *  bytes_per_token: slot bytes per token of all layers, the encoded size a
+ *    host pool reports [HIQ "Integrating the codec": get_size_per_token].
+ * Any output pointer may be NULL. */
+kvc_status kvc_plan(const kvc_layout *layout, const kvc_codec *codec, uint32_t n_pages,
+                    size_t *slot_bytes, size_t *spill_bytes_suggested,
+                    size_t *bytes_per_token);
+
+/* Host-only validation used by kvc_encode_pages (exposed so callers and
+ * tests can check arguments without a GPU).  page_ids: host [n_pages]. */
+kvc_status kvc_validate_encode(const kvc_layout *layout, const kvc_codec *codec,
+                               const int32_t *page_ids, uint32_t n_pages, size_t out_bytes);
+/* Same for kvc_decode_pages; also rejects duplicate destination pages. */
+kvc_status kvc_validate_decode(const kvc_layout *layout, const kvc_codec *codec,
+                               const int32_t *dst_page_ids, uint32_t n_pages, size_t in_bytes);
+
+/* Encode the pages page_ids (host [n_pages], source block ids) of every
+ * layer into `out` (device, out_bytes >= slot_bytes; the remainder is the
+ * spill region).  desc (device, [layers*n_pages*2]) receives one
+ * descriptor per segment.  Everything is enqueued on `stream` (hipStream_t,
+ * NULL = default stream).  Segments are independent: one launch covers the
+ * whole call, and the caller reads the statuses once per batch. */
+kvc_status kvc_encode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
+                            const int32_t *page_ids, uint32_t n_pages,
+                            void *out, size_t out_bytes, kvc_segment_desc *desc,
+                            void *stream);
+
+/* Decode a buffer produced by kvc_encode_pages with the same layout
+ * geometry, codec and n_pages into the destination pages dst_page_ids (host
+ * [n_pages], distinct, validated for the whole request before anything is
+ * enqueued [OKV-SF "Ownership, storage and GDS"]).  Raw segments are copied
+ * bit-exactly.  seg_status (device [layers*n_pages*2] u8, may be NULL)
+ * receives 0 per decoded segment, 1 when the slot header does not match
+ * the geometry/codec or the segment was not stored (KVC_SEG_CAPACITY), or 2
+ * when the kernel's range check on its staged descriptor failed; in the last
+ * two cases the destination page is left unchanged.  Enqueued on `stream`. */
+kvc_status kvc_decode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
+                            const void *in, size_t in_bytes,
+                            const int32_t *dst_page_ids, uint32_t n_pages,
+                            uint8_t *seg_status, void *stream);
+
+/* Short text for a status code (static storage). */
+const char *kvc_status_string(kvc_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H */

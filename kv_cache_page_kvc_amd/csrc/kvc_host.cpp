@@ -1,0 +1,524 @@
+// kvc_host.cpp -- host half of libkvc: argument validation, the slot plan,
+// the retained device arena, format constants (Lloyd-Max codebook, sign
+// generator) and the launches.
+//
+// Behaviour follows OrbitKV docs, "KV precision and storage encoding":
+//  "FP8 and TurboQuant": layouts and K/V roles are validated explicitly;
+//    head dims 32/64/128/256; protected layers stay exact; the sign
+//    generator is versioned and seeded.
+//  "Ownership, storage and GDS": keep an encoded segment only when its
+//    aligned footprint saves >= 12.5%; sources up to 16 MiB are encoded;
+//    one descriptor-driven launch per batch with statuses collected once;
+//    a retained arena bounded by the workspace budget; restore validates
+//    destinations for the whole request first; teardown drains GPU work.
+// and "Building a quantized HiCache for SGLang", "Integrating the codec":
+//    the encoded size per token is reported for capacity accounting.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <vector>
+
+#include "kvc.h"
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+struct kvc_ctx {
+  int device = 0;
+  size_t budget = 0;
+  uint8_t* arena = nullptr;          // device: [Tables | ring]
+  uint8_t* staging = nullptr;        // pinned host mirror of the ring
+  size_t ring_begin = 0, ring_end = 0, head = 0;
+  struct InFlight {
+    size_t off, size;
+    hipEvent_t ev;
+  };
+  std::vector<InFlight> inflight;
+  std::vector<hipEvent_t> free_events;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------------------------ formats
+int codec_bits(int c) {
+  switch (c) {
+    case KVC_UNIFORM3: case KVC_TQ3: return 3;
+    case KVC_UNIFORM4: case KVC_TQ4: return 4;
+    case KVC_RAW: return 16;
+    default: return 8;
+  }
+}
+int codec_meta(int c) {
+  switch (c) {
+    case KVC_FP8_DYNAMIC: case KVC_INT8: case KVC_UNIFORM3: case KVC_UNIFORM4: return 4;
+    case KVC_TQ3: case KVC_TQ4: return 2;
+    default: return 0;
+  }
+}
+uint64_t slot_size(int codec, uint32_t d, uint32_t n_vec) {
+  const uint64_t per_vec = (uint64_t)codec_bits(codec) * d / 8 + (uint64_t)codec_meta(codec);
+  return align_up(KVC_HEADER_BYTES + per_vec * n_vec, KVC_SLOT_ALIGN);
+}
+// codec used after the static rules: raw for protected layers and KVC_RAW,
+// raw for sources above 16 MiB, raw if the aligned slot saves < 12.5%.
+int effective_codec(int codec, uint32_t d, uint32_t n_vec, bool prot) {
+  const uint64_t orig = (uint64_t)n_vec * d * 2;
+  if (prot || codec == KVC_RAW) return KVC_RAW;
+  if (orig > KVC_MAX_SEGMENT_BYTES) return KVC_RAW;
+  if (8 * slot_size(codec, d, n_vec) > 7 * orig) return KVC_RAW;
+  return codec;
+}
+bool is_protected(const kvc_codec* c, uint32_t l) {
+  return c->protected_layers && ((c->protected_layers[l >> 3] >> (l & 7)) & 1);
+}
+
+// ------------------------------------------------------------------ constants
+// Gaussian Lloyd-Max quantizer with n levels, by alternating the two
+// optimality conditions (cell boundaries at midpoints, levels at the
+// conditional means of their cells) until nothing moves.
+double phi(double x) { return std::exp(-0.5 * x * x) * 0.3989422804014326779399461; }
+double upper(double x) { return 0.5 * std::erfc(x * 0.7071067811865475244008444); }
+// P(lo < X < hi), accurate in both tails
+double cell_mass(double lo, double hi) {
+  if (lo >= 0) return upper(lo) - upper(hi);
+  if (hi <= 0) return upper(-hi) - upper(-lo);
+  return 1.0 - upper(hi) - upper(-lo);
+}
+void lloyd_max(int n, std::vector<double>& lev) {
+  lev.resize(n);
+  for (int k = 0; k < n; k++) lev[k] = -3.0 + 6.0 * (k + 0.5) / n;
+  std::vector<double> b(n + 1);
+  for (int it = 0; it < 4000000; it++) {
+    b[0] = -INFINITY;
+    b[n] = INFINITY;
+    for (int k = 1; k < n; k++) b[k] = 0.5 * (lev[k - 1] + lev[k]);
+    double moved = 0.0;
+    for (int k = 0; k < n; k++) {
+      const double num = (std::isinf(b[k]) ? 0.0 : phi(b[k])) - (std::isinf(b[k + 1]) ? 0.0 : phi(b[k + 1]));
+      const double m = num / cell_mass(b[k], b[k + 1]);
+      moved = std::max(moved, std::fabs(m - lev[k]));
+      lev[k] = m;
+    }
+    if (moved < 1e-15) break;
+  }
+  for (int k = 0; k < n / 2; k++) {            // exact symmetry
+    const double a = 0.5 * (lev[n - 1 - k] - lev[k]);
+    lev[k] = -a;
+    lev[n - 1 - k] = a;
+  }
+}
+
+void build_tables(Tables& t) {
+  for (int which = 0; which < 2; which++) {
+    const int bits = which ? 4 : 3, n = 1 << bits;
+    std::vector<double> lev;
+    lloyd_max(n, lev);
+    float thr[15];
+    for (int k = 0; k < n; k++) t.centroids[which][k] = (float)lev[k];
+    for (int k = 0; k < n - 1; k++) thr[k] = (float)(0.5 * (lev[k] + lev[k + 1]));
+    // cells: c = RNE(4 z) + 64, i.e. 4z in [c-64-0.5, c-64+0.5]
+    for (int c = 0; c < kCells; c++) {
+      const double lo = (c - kCellOffset - 0.5) / kCellScale, hi = (c - kCellOffset + 0.5) / kCellScale;
+      uint32_t below = 0;
+      int inside = -1;
+      for (int k = 0; k < n - 1; k++) {
+        if ((double)thr[k] < lo) below++;
+        else if ((double)thr[k] <= hi) inside = k;
+      }
+      t.cells[which][c].thr = inside >= 0 ? thr[inside] : INFINITY;
+      t.cells[which][c].base = below;
+    }
+  }
+}
+
+// SplitMix64 (Steele, Lea, Flood, OOPSLA 2014); sign generator version 1:
+// sigma_i = -1 iff bit 63 of the i-th output from state = seed.
+void sign_mask(uint64_t seed, uint32_t d, uint32_t mask[8]) {
+  std::memset(mask, 0, 8 * sizeof(uint32_t));
+  uint64_t state = seed;
+  for (uint32_t i = 0; i < d; i++) {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    if (z >> 63) mask[i >> 5] |= 1u << (i & 31);
+  }
+}
+
+// ------------------------------------------------------------------ validation
+kvc_status check_layout(const kvc_layout* L) {
+  if (!L || L->abi != KVC_ABI_VERSION) return KVC_E_ARG;
+  if (L->dtype != KVC_BF16 && L->dtype != KVC_FP16) return KVC_E_UNSUPPORTED;
+  if (L->kind != KVC_SEPARATE_NHD && L->kind != KVC_PACKED_HT2D) return KVC_E_UNSUPPORTED;
+  const uint32_t D = L->head_dim;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return KVC_E_UNSUPPORTED;
+  if (L->layers == 0 || L->kv_heads == 0 || L->tokens_per_page == 0 || L->num_blocks == 0) return KVC_E_ARG;
+  const uint64_t n_vec = (uint64_t)L->kv_heads * L->tokens_per_page;
+  if (n_vec > 65535) return KVC_E_UNSUPPORTED;                 // header field is 16 bits
+  if (L->num_blocks > (uint64_t)std::numeric_limits<int32_t>::max()) return KVC_E_ARG;
+  const int64_t sb = L->stride_block, st = L->stride_token, sh = L->stride_head;
+  if (sb <= 0 || st <= 0 || sh <= 0 || (sb % 8) || (st % 8) || (sh % 8)) return KVC_E_ARG;
+  const int64_t H = L->kv_heads, T = L->tokens_per_page;
+  if (L->kind == KVC_SEPARATE_NHD) {
+    if (sh < (int64_t)D || st < H * sh || sb < T * st) return KVC_E_ARG;
+    if (!L->v_base) return KVC_E_ARG;
+  } else {
+    if (st < 2 * (int64_t)D || sh < T * st || sb < H * sh) return KVC_E_ARG;
+    if (L->v_base) return KVC_E_ARG;
+  }
+  if (!L->k_base) return KVC_E_ARG;
+  for (uint32_t l = 0; l < L->layers; l++) {
+    const void* k = L->k_base[l];
+    if (!k || ((uintptr_t)k & 15)) return KVC_E_ARG;
+    if (L->kind == KVC_SEPARATE_NHD) {
+      const void* v = L->v_base[l];
+      if (!v || ((uintptr_t)v & 15)) return KVC_E_ARG;
+    }
+  }
+  return KVC_OK;
+}
+
+kvc_status check_codec(const kvc_layout* L, const kvc_codec* c) {
+  if (!c || c->k > KVC_TQ4 || c->v > KVC_TQ4) return KVC_E_ARG;
+  if (c->k == KVC_FP8_FIXED || c->v == KVC_FP8_FIXED) {
+    if (!c->fixed_scales) return KVC_E_ARG;
+    for (uint32_t l = 0; l < L->layers; l++)
+      for (int comp = 0; comp < 2; comp++) {
+        if ((comp ? c->v : c->k) != KVC_FP8_FIXED) continue;
+        const float s = c->fixed_scales[2 * l + comp];
+        if (!(s >= 0x1p-100f && s <= 0x1p100f)) return KVC_E_ARG;   // also rejects NaN
+      }
+  }
+  return KVC_OK;
+}
+
+struct Plan {
+  std::vector<uint64_t> layer_off;
+  std::vector<uint32_t> slot[2];
+  std::vector<uint8_t> eff[2];
+  uint64_t total = 0;
+  uint64_t per_page = 0;      // slot bytes of one page over all layers
+  uint64_t encodable = 0;     // segments not raw by policy
+};
+
+Plan make_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages) {
+  Plan p;
+  const uint32_t n_vec = L->kv_heads * L->tokens_per_page;
+  p.layer_off.resize(L->layers);
+  for (int comp = 0; comp < 2; comp++) {
+    p.slot[comp].resize(L->layers);
+    p.eff[comp].resize(L->layers);
+  }
+  uint64_t off = 0;
+  for (uint32_t l = 0; l < L->layers; l++) {
+    const bool prot = is_protected(c, l);
+    for (int comp = 0; comp < 2; comp++) {
+      const int e = effective_codec(comp ? c->v : c->k, L->head_dim, n_vec, prot);
+      p.eff[comp][l] = (uint8_t)e;
+      p.slot[comp][l] = (uint32_t)slot_size(e, L->head_dim, n_vec);
+      if (e != KVC_RAW) p.encodable += n_pages;
+    }
+    p.layer_off[l] = off;
+    const uint64_t page = (uint64_t)p.slot[0][l] + p.slot[1][l];
+    p.per_page += page;
+    off += page * n_pages;
+  }
+  p.total = off;
+  return p;
+}
+
+kvc_status check_pages(const kvc_layout* L, const int32_t* ids, uint32_t n, bool distinct) {
+  if (n == 0) return KVC_OK;
+  if (!ids) return KVC_E_ARG;
+  for (uint32_t i = 0; i < n; i++)
+    if (ids[i] < 0 || (uint64_t)ids[i] >= L->num_blocks) return KVC_E_PAGE_RANGE;
+  if (distinct) {
+    std::vector<int32_t> s(ids, ids + n);
+    std::sort(s.begin(), s.end());
+    if (std::adjacent_find(s.begin(), s.end()) != s.end()) return KVC_E_DUP_DST;
+  }
+  return KVC_OK;
+}
+
+kvc_status check_grid(const kvc_layout* L, uint32_t n) {
+  const uint64_t nseg = (uint64_t)L->layers * n * 2;
+  return nseg > 0x7FFFFFFFull ? KVC_E_ARG : KVC_OK;
+}
+
+// per-call metadata in the arena: [SideEntry x 2L][page ids][spill cursor]
+size_t call_bytes(uint32_t layers, uint32_t n) {
+  return align_up(sizeof(SideEntry) * 2 * layers, kAlign) + align_up(sizeof(int32_t) * (size_t)n, kAlign) + kAlign;
+}
+
+size_t tables_bytes() { return align_up(sizeof(Tables), kAlign); }
+
+struct DeviceGuard {
+  int old = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&old) != hipSuccess) old = -1;
+    ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (old >= 0) (void)hipSetDevice(old);
+  }
+};
+
+// reserve `size` bytes of the ring; waits only for calls whose metadata
+// occupies the bytes about to be reused
+kvc_status ring_alloc(kvc_ctx* ctx, size_t size, size_t* off) {
+  if (size > ctx->ring_end - ctx->ring_begin) return KVC_E_BUDGET;
+  // retire finished calls
+  for (size_t i = 0; i < ctx->inflight.size();) {
+    if (hipEventQuery(ctx->inflight[i].ev) == hipSuccess) {
+      ctx->free_events.push_back(ctx->inflight[i].ev);
+      ctx->inflight.erase(ctx->inflight.begin() + (long)i);
+    } else {
+      i++;
+    }
+  }
+  if (ctx->head + size > ctx->ring_end) ctx->head = ctx->ring_begin;
+  const size_t a = ctx->head, b = ctx->head + size;
+  for (size_t i = 0; i < ctx->inflight.size();) {
+    const auto& f = ctx->inflight[i];
+    if (f.off < b && a < f.off + f.size) {
+      if (hipEventSynchronize(f.ev) != hipSuccess) return KVC_E_HIP;
+      ctx->free_events.push_back(f.ev);
+      ctx->inflight.erase(ctx->inflight.begin() + (long)i);
+    } else {
+      i++;
+    }
+  }
+  *off = a;
+  ctx->head = b;
+  return KVC_OK;
+}
+
+kvc_status ring_commit(kvc_ctx* ctx, size_t off, size_t size, hipStream_t stream) {
+  hipEvent_t ev;
+  if (!ctx->free_events.empty()) {
+    ev = ctx->free_events.back();
+    ctx->free_events.pop_back();
+  } else if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+    return KVC_E_HIP;
+  }
+  if (hipEventRecord(ev, stream) != hipSuccess) return KVC_E_HIP;
+  ctx->inflight.push_back({off, size, ev});
+  return KVC_OK;
+}
+
+// stage layer table + page ids + zeroed spill cursor, upload, fill params
+kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, const Plan& plan,
+                      const int32_t* pages, uint32_t n, hipStream_t stream, CallParams* P, size_t* ring_off,
+                      size_t* ring_size) {
+  const size_t need = call_bytes(L->layers, n);
+  size_t off = 0;
+  kvc_status st = ring_alloc(ctx, need, &off);
+  if (st != KVC_OK) return st;
+  uint8_t* h = ctx->staging + off;
+  SideEntry* se = reinterpret_cast<SideEntry*>(h);
+  uint64_t lo = ~0ull, hi = 0;
+  for (uint32_t l = 0; l < L->layers; l++) {
+    const uint16_t* bases[2] = {
+        static_cast<const uint16_t*>(L->k_base[l]),
+        L->kind == KVC_PACKED_HT2D ? static_cast<const uint16_t*>(L->k_base[l]) + L->head_dim
+                                   : static_cast<const uint16_t*>(L->v_base[l])};
+    for (int comp = 0; comp < 2; comp++) {
+      SideEntry e{};
+      e.base = bases[comp];
+      e.slot_base = plan.layer_off[l] + (comp ? plan.slot[0][l] : 0u);
+      e.page_stride = plan.slot[0][l] + plan.slot[1][l];
+      e.slot_bytes = plan.slot[comp][l];
+      e.codec = plan.eff[comp][l];
+      e.fixed = c->fixed_scales ? c->fixed_scales[2 * l + comp] : 1.0f;
+      se[2 * l + comp] = e;
+      lo = std::min<uint64_t>(lo, (uint64_t)(uintptr_t)e.base);
+      hi = std::max<uint64_t>(hi, (uint64_t)(uintptr_t)e.base);
+    }
+  }
+  P->base_lo = lo;
+  P->base_hi = hi;
+  P->num_blocks = (uint32_t)L->num_blocks;
+  const size_t pages_off = align_up(sizeof(SideEntry) * 2 * L->layers, kAlign);
+  std::memcpy(h + pages_off, pages, sizeof(int32_t) * (size_t)n);
+  const size_t cur_off = pages_off + align_up(sizeof(int32_t) * (size_t)n, kAlign);
+  std::memset(h + cur_off, 0, kAlign);
+  if (hipMemcpyAsync(ctx->arena + off, h, need, hipMemcpyHostToDevice, stream) != hipSuccess) return KVC_E_HIP;
+  uint8_t* d = ctx->arena + off;
+  P->sides = reinterpret_cast<const SideEntry*>(d);
+  P->pages = reinterpret_cast<const int32_t*>(d + pages_off);
+  P->spill_cursor = reinterpret_cast<unsigned long long*>(d + cur_off);
+  P->tables = reinterpret_cast<const Tables*>(ctx->arena);
+  P->sb = L->stride_block;
+  P->st = L->stride_token;
+  P->sh = L->stride_head;
+  P->n_pages = n;
+  P->n_layers = L->layers;
+  P->heads = L->kv_heads;
+  P->tokens = L->tokens_per_page;
+  P->dtype = L->dtype;
+  sign_mask(c->seed, L->head_dim, P->sign_mask);
+  *ring_off = off;
+  *ring_size = need;
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_status_string(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_E_ARG: return "invalid argument";
+    case KVC_E_UNSUPPORTED: return "unsupported geometry";
+    case KVC_E_PAGE_RANGE: return "page id out of range";
+    case KVC_E_DUP_DST: return "duplicate destination page";
+    case KVC_E_CAPACITY: return "buffer smaller than the plan";
+    case KVC_E_BUDGET: return "workspace budget exceeded";
+    case KVC_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+kvc_status kvc_plan(const kvc_layout* layout, const kvc_codec* codec, uint32_t n_pages, size_t* slot_bytes,
+                    size_t* spill_bytes_suggested, size_t* bytes_per_token) {
+  kvc_status st = check_layout(layout);
+  if (st == KVC_OK) st = check_codec(layout, codec);
+  if (st != KVC_OK) return st;
+  const Plan p = make_plan(layout, codec, n_pages);
+  const uint64_t raw_seg = align_up((uint64_t)layout->kv_heads * layout->tokens_per_page * layout->head_dim * 2,
+                                    KVC_SLOT_ALIGN);
+  if (slot_bytes) *slot_bytes = p.total;
+  if (spill_bytes_suggested) *spill_bytes_suggested = raw_seg * std::max<uint64_t>(1, (p.encodable + 31) / 32);
+  if (bytes_per_token) *bytes_per_token = (p.per_page + layout->tokens_per_page - 1) / layout->tokens_per_page;
+  return KVC_OK;
+}
+
+kvc_status kvc_validate_encode(const kvc_layout* layout, const kvc_codec* codec, const int32_t* page_ids,
+                               uint32_t n_pages, size_t out_bytes) {
+  kvc_status st = check_layout(layout);
+  if (st == KVC_OK) st = check_codec(layout, codec);
+  if (st == KVC_OK) st = check_grid(layout, n_pages);
+  if (st == KVC_OK) st = check_pages(layout, page_ids, n_pages, false);
+  if (st != KVC_OK) return st;
+  if (make_plan(layout, codec, n_pages).total > out_bytes) return KVC_E_CAPACITY;
+  return KVC_OK;
+}
+
+kvc_status kvc_validate_decode(const kvc_layout* layout, const kvc_codec* codec, const int32_t* dst_page_ids,
+                               uint32_t n_pages, size_t in_bytes) {
+  kvc_status st = check_layout(layout);
+  if (st == KVC_OK) st = check_codec(layout, codec);
+  if (st == KVC_OK) st = check_grid(layout, n_pages);
+  if (st == KVC_OK) st = check_pages(layout, dst_page_ids, n_pages, true);
+  if (st != KVC_OK) return st;
+  if (make_plan(layout, codec, n_pages).total > in_bytes) return KVC_E_CAPACITY;
+  return KVC_OK;
+}
+
+kvc_status kvc_create(kvc_ctx** out, int hip_device, size_t workspace_budget) {
+  if (!out) return KVC_E_ARG;
+  *out = nullptr;
+  if (workspace_budget == 0) workspace_budget = KVC_DEFAULT_WORKSPACE;
+  const size_t tb = tables_bytes();
+  if (workspace_budget < tb + 4 * kAlign) return KVC_E_BUDGET;
+  DeviceGuard g(hip_device);
+  if (!g.ok) return KVC_E_HIP;
+  kvc_ctx* ctx = new kvc_ctx();
+  ctx->device = hip_device;
+  ctx->budget = workspace_budget;
+  ctx->ring_begin = tb;
+  ctx->ring_end = workspace_budget / kAlign * kAlign;
+  ctx->head = ctx->ring_begin;
+  Tables* t = new Tables();
+  build_tables(*t);
+  bool ok = hipMalloc(&ctx->arena, workspace_budget) == hipSuccess &&
+            hipHostMalloc(&ctx->staging, ctx->ring_end, hipHostMallocDefault) == hipSuccess &&
+            hipMemcpy(ctx->arena, t, sizeof(Tables), hipMemcpyHostToDevice) == hipSuccess;
+  delete t;
+  if (!ok) {
+    kvc_destroy(ctx);
+    return KVC_E_HIP;
+  }
+  *out = ctx;
+  return KVC_OK;
+}
+
+kvc_status kvc_destroy(kvc_ctx* ctx) {
+  if (!ctx) return KVC_OK;
+  kvc_status st = KVC_OK;
+  {
+    DeviceGuard g(ctx->device);
+    for (auto& f : ctx->inflight) {
+      if (hipEventSynchronize(f.ev) != hipSuccess) st = KVC_E_HIP;
+      (void)hipEventDestroy(f.ev);
+    }
+    for (auto e : ctx->free_events) (void)hipEventDestroy(e);
+    if (ctx->arena) (void)hipFree(ctx->arena);
+    if (ctx->staging) (void)hipHostFree(ctx->staging);
+  }
+  delete ctx;
+  return st;
+}
+
+kvc_status kvc_encode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec,
+                            const int32_t* page_ids, uint32_t n_pages, void* out, size_t out_bytes,
+                            kvc_segment_desc* desc, void* stream) {
+  if (!ctx) return KVC_E_ARG;
+  kvc_status st = kvc_validate_encode(layout, codec, page_ids, n_pages, out_bytes);
+  if (st != KVC_OK) return st;
+  if (n_pages == 0) return KVC_OK;
+  if (!out || !desc || ((uintptr_t)out & 255) || ((uintptr_t)desc & 15)) return KVC_E_ARG;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return KVC_E_HIP;
+  const Plan plan = make_plan(layout, codec, n_pages);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CallParams P{};
+  size_t roff = 0, rsize = 0;
+  st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize);
+  if (st != KVC_OK) return st;
+  P.buf = static_cast<uint8_t*>(out);
+  P.buf_bytes = out_bytes;
+  P.slot_region = plan.total;
+  P.desc = desc;
+  P.seg_status = nullptr;
+  const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
+  if (launch_encode(P, layout->head_dim, nseg, s) != hipSuccess) return KVC_E_HIP;
+  return ring_commit(ctx, roff, rsize, s);
+}
+
+kvc_status kvc_decode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec, const void* in,
+                            size_t in_bytes, const int32_t* dst_page_ids, uint32_t n_pages, uint8_t* seg_status,
+                            void* stream) {
+  if (!ctx) return KVC_E_ARG;
+  kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
+  if (st != KVC_OK) return st;
+  if (n_pages == 0) return KVC_OK;
+  if (!in || ((uintptr_t)in & 255)) return KVC_E_ARG;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return KVC_E_HIP;
+  const Plan plan = make_plan(layout, codec, n_pages);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CallParams P{};
+  size_t roff = 0, rsize = 0;
+  st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+  if (st != KVC_OK) return st;
+  P.buf = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
+  P.buf_bytes = in_bytes;
+  P.slot_region = plan.total;
+  P.desc = nullptr;
+  P.seg_status = seg_status;
+  const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
+  if (launch_decode(P, layout->head_dim, nseg, s) != hipSuccess) return KVC_E_HIP;
+  return ring_commit(ctx, roff, rsize, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// kvc_internal.h -- structures shared by the host half of libkvc and its
+// gfx950 kernels.  Not part of the public ABI (include/kvc.h is).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kThreads = 256;                 // one workgroup per segment
+constexpr uint64_t kSlotAlign = KVC_SLOT_ALIGN;
+constexpr uint32_t kHeaderBytes = KVC_HEADER_BYTES;
+
+// Bucketize table for TurboQuant encode: cell c of the real line,
+// c = RNE(kCellScale * z) + kCellOffset, holds the one threshold that may lie
+// inside the cell (or +inf) and the count of thresholds below the cell, so
+// that #{k : B_k < z} = base + (z > T).  kCellScale = 4 makes every cell
+// (width 1/4) narrower than the closest pair of 3- or 4-bit thresholds.
+constexpr float kCellScale = 4.0f;
+constexpr int kCellOffset = 64;               // |z| <= sqrt(256) = 16 -> |4z| <= 64
+constexpr int kCells = 2 * kCellOffset + 1;   // 129
+
+struct CellEntry {
+  float thr;
+  uint32_t base;
+};
+
+// Per-ctx constant tables (device, in the arena).
+struct Tables {
+  CellEntry cells[2][kCells];                 // [0]: 3-bit, [1]: 4-bit
+  float centroids[2][16];
+};
+
+// Per-(layer, component) entry of a call (device, in the arena), indexed by
+// 2*layer + component.  Every field sits at a fixed, naturally aligned offset
+// of a 32-byte record, so the kernels read it with aligned scalar loads.
+struct SideEntry {
+  const uint16_t* base;                       // element 0 of block 0 of this component
+  uint64_t slot_base;                         // slot offset of (layer, page 0, component)
+  uint32_t page_stride;                       // slot bytes of one page of the layer (K + V)
+  uint32_t slot_bytes;                        // slot size of this component's segments
+  uint32_t codec;                             // effective codec (KVC_RAW for policy raw)
+  float fixed;                                // FP8_FIXED scale
+};
+static_assert(sizeof(SideEntry) == 32, "SideEntry is a 32-byte record");
+
+struct CallParams {
+  const SideEntry* sides;                     // [2 * n_layers]
+  const int32_t* pages;                       // source (encode) / destination (decode) block ids
+  const Tables* tables;
+  uint8_t* buf;                               // encode output / decode input
+  uint64_t buf_bytes;
+  uint64_t slot_region;                       // spill region = [slot_region, buf_bytes)
+  kvc_segment_desc* desc;                     // encode: descriptors (device)
+  uint8_t* seg_status;                        // decode: statuses (device, may be null)
+  unsigned long long* spill_cursor;           // encode: bytes used in the spill region
+  uint64_t base_lo, base_hi;                  // range of every layer base pointer (guard)
+  int64_t sb, st, sh;                         // element strides
+  uint32_t n_pages, n_layers, heads, tokens;
+  uint32_t dtype;                             // kvc_dtype
+  uint32_t num_blocks;                        // page ids must be below this (guard)
+  uint32_t sign_mask[8];                      // TurboQuant signs, bit i = (sigma_i < 0)
+};
+
+// Launchers (kvc_kernels.hip).  Return hipSuccess or the launch error.
+hipError_t launch_encode(const CallParams& p, uint32_t head_dim, uint64_t n_segments,
+                         hipStream_t stream);
+hipError_t launch_decode(const CallParams& p, uint32_t head_dim, uint64_t n_segments,
+                         hipStream_t stream);
+
+}  // namespace kvc

@@ -1,0 +1,896 @@
+// kvc_kernels.hip -- gfx950 kernels of libkvc: fused page gather + encode +
+// store, and load + decode + page scatter, for the codecs described on
+//   OrbitKV docs, "KV precision and storage encoding", section "FP8 and
+//     TurboQuant" (E4M3FN, TurboQuant K, uniform V, raw fallback),
+//   "Building a quantized HiCache for SGLang", section "Building the INT8
+//     codec" (per-vector INT8),
+//   knlp "Asymmetric KV: methods and results", section "Precision and scaling
+//     reference" (FP8 scale rule).
+//
+// Work decomposition.  One 256-thread workgroup per segment (page, layer,
+// component).  A head vector of D elements is held by a group of P lanes, each
+// lane owning E = D/P elements as NCH = E/8 chunks of 8 contiguous elements
+// (one 16-byte load per chunk):
+//     element i = k*8P + 8p + j   (chunk k, lane p of the group, j < 8).
+// So WHT stages / reduction levels over element bits 0..2 are in-lane, bits
+// 3..3+log2(P)-1 are cross-lane (DPP: quad_perm for lane xor 1 and xor 2,
+// row_ror:8 for lane xor 8) and the chunk bits are in-lane again.  Group
+// lanes use lane-id bits {0, 1, 3}, so every cross-lane partner is one DPP
+// away.  Each load instruction of a wave reads 128-byte aligned pieces of
+// eight consecutive vectors.
+//
+// Arithmetic: binary32 with round-to-nearest-even, built with
+// -ffp-contract=off; '/' and sqrtf are correctly rounded (HIP default);
+// fmaf is used only where the fused single rounding is the defined result.
+// Data-dependent raw segments: codes are written speculatively, then the
+// workgroup OR-reduces the per-vector gate; a raw segment gets a header with
+// RAW_DATA and its bytes in the spill region (the encoded codes left in its
+// slot are ignored by decode).
+#include <hip/hip_runtime.h>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load of engine pages (read once per call)
+__device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ------------------------------------------------------------------ geometry
+template <int D>
+struct Geo {
+  static constexpr int P = D == 32 ? 2 : (D == 64 ? 4 : 8);   // lanes per vector
+  static constexpr int LOGP = D == 32 ? 1 : (D == 64 ? 2 : 3);
+  static constexpr int E = D / P;                             // elements per lane
+  static constexpr int NCH = E / 8;                           // 16-byte chunks per lane
+  static constexpr int GPW = 64 / P;                          // groups per wave
+  static constexpr int GW = GPW * (kThreads / 64);            // groups per workgroup
+  static constexpr int U = NCH <= 2 ? 4 : 2;                  // vectors in flight per group
+};
+
+struct Lane {
+  int p;        // lane index within the group
+  int g;        // group index within the workgroup
+};
+
+template <int D>
+__device__ __forceinline__ Lane lane_info() {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Lane r;
+  if constexpr (Geo<D>::P == 8) {
+    r.p = (lane & 3) | (((lane >> 3) & 1) << 2);
+    r.g = wave * 8 + (((lane >> 2) & 1) | ((lane >> 4) << 1));
+  } else if constexpr (Geo<D>::P == 4) {
+    r.p = lane & 3;
+    r.g = wave * 16 + (lane >> 2);
+  } else {
+    r.p = lane & 1;
+    r.g = wave * 32 + (lane >> 1);
+  }
+  return r;
+}
+
+// cross-lane partner for the q-th group bit (element bit 3+q)
+template <int Q>
+__device__ __forceinline__ float xlane(float x) {
+  constexpr int ctrl = Q == 0 ? 0xB1 : (Q == 1 ? 0x4E : 0x128);   // xor1, xor2, row_ror:8
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, true));
+}
+template <int Q>
+__device__ __forceinline__ uint32_t xlane_u(uint32_t x) {
+  constexpr int ctrl = Q == 0 ? 0xB1 : (Q == 1 ? 0x4E : 0x128);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, true);
+}
+// lane-id bit that carries group bit Q
+template <int Q>
+__device__ __forceinline__ bool upper_lane() {
+  constexpr int bit = Q == 0 ? 0 : (Q == 1 ? 1 : 3);
+  return (threadIdx.x >> bit) & 1;
+}
+
+template <int LOGP>
+__device__ __forceinline__ float group_sum(float v) {   // sum over element bits 3.. (ascending)
+  if constexpr (LOGP >= 1) v = v + xlane<0>(v);
+  if constexpr (LOGP >= 2) v = v + xlane<1>(v);
+  if constexpr (LOGP >= 3) v = v + xlane<2>(v);
+  return v;
+}
+template <int LOGP>
+__device__ __forceinline__ float group_min(float v) {
+  if constexpr (LOGP >= 1) v = fminf(v, xlane<0>(v));
+  if constexpr (LOGP >= 2) v = fminf(v, xlane<1>(v));
+  if constexpr (LOGP >= 3) v = fminf(v, xlane<2>(v));
+  return v;
+}
+template <int LOGP>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (LOGP >= 1) v = fmaxf(v, xlane<0>(v));
+  if constexpr (LOGP >= 2) v = fmaxf(v, xlane<1>(v));
+  if constexpr (LOGP >= 3) v = fmaxf(v, xlane<2>(v));
+  return v;
+}
+template <int LOGP>
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+  if constexpr (LOGP >= 1) v = max(v, xlane_u<0>(v));
+  if constexpr (LOGP >= 2) v = max(v, xlane_u<1>(v));
+  if constexpr (LOGP >= 3) v = max(v, xlane_u<2>(v));
+  return v;
+}
+
+// ------------------------------------------------------------------ formats
+template <int DT>
+__device__ __forceinline__ void unpack8(const uint4& w, float* x) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    if constexpr (DT == KVC_BF16) {
+      x[2 * m] = __uint_as_float(a[m] << 16);
+      x[2 * m + 1] = __uint_as_float(a[m] & 0xFFFF0000u);
+    } else {
+      f32x2 f = __builtin_convertvector(__builtin_bit_cast(f16x2, a[m]), f32x2);
+      x[2 * m] = f.x;
+      x[2 * m + 1] = f.y;
+    }
+  }
+}
+
+// two floats -> packed output pair, round to nearest even
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  f32x2 v = {a, b};
+  if constexpr (DT == KVC_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 pack8(const float* y) {
+  uint4 w;
+  w.x = pack2<DT>(y[0], y[1]);
+  w.y = pack2<DT>(y[2], y[3]);
+  w.z = pack2<DT>(y[4], y[5]);
+  w.w = pack2<DT>(y[6], y[7]);
+  return w;
+}
+
+// largest |x| bit pattern (sign cleared) of the lane's elements: orders like
+// |x| for finite values, and any NaN/Inf pattern is above every finite one.
+__device__ __forceinline__ uint32_t absmax_bits(const uint4& w) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) m = max(m, max(a[q] & 0x7FFFu, (a[q] >> 16) & 0x7FFFu));
+  return m;
+}
+template <int DT>
+__device__ __forceinline__ float bits_to_f32(uint32_t h) {
+  if constexpr (DT == KVC_BF16) return __uint_as_float(h << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+template <int DT> struct Lim {
+  static constexpr uint32_t nonfinite = DT == KVC_BF16 ? 0x7F80u : 0x7C00u;  // |x| bits >= : NaN/Inf
+  static constexpr uint32_t fp8max = DT == KVC_BF16 ? 0x43E0u : 0x5F00u;     // 448
+};
+
+__device__ __forceinline__ float f16_round(float x) { return (float)(_Float16)x; }
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// FP8 E4M3FN (OCP) pack of 8 values (gfx950 v_cvt_pk_fp8_f32: RNE)
+__device__ __forceinline__ uint2 fp8x8(const float* q) {
+  uint2 r;
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+  r.x = (uint32_t)lo;
+  r.y = (uint32_t)hi;
+  return r;
+}
+
+// ------------------------------------------------------------------ addressing
+struct SegCtx {
+  const uint16_t* src;      // element (t=0, h=0, i=0) of the page's component
+  uint8_t* slot;            // slot start (header)
+  int n_vec;
+  int heads;
+  int64_t st, sh;
+};
+
+__device__ __forceinline__ const uint16_t* vec_ptr(const SegCtx& s, int v) {
+  const int t = v / s.heads, h = v - t * s.heads;
+  return s.src + (int64_t)t * s.st + (int64_t)h * s.sh;
+}
+
+// ------------------------------------------------------------------ encoders
+// Each returns 1 if this vector forces the segment raw.
+enum Codec { C_RAW = 0, C_FP8D = 1, C_FP8F = 2, C_FP8Y = 3, C_INT8 = 4, C_U3 = 5, C_U4 = 6, C_TQ3 = 7, C_TQ4 = 8 };
+
+template <int C> struct CodecInfo {
+  static constexpr int bits = (C == C_U3 || C == C_TQ3) ? 3 : ((C == C_U4 || C == C_TQ4) ? 4 : 8);
+  static constexpr int meta = (C == C_FP8Y || C == C_INT8 || C == C_U3 || C == C_U4) ? 4
+                            : ((C == C_TQ3 || C == C_TQ4) ? 2 : 0);
+  static constexpr bool tq = C == C_TQ3 || C == C_TQ4;
+  static constexpr bool uni = C == C_U3 || C == C_U4;
+  static constexpr bool fp8 = C == C_FP8D || C == C_FP8F || C == C_FP8Y;
+};
+
+// store the codes of one chunk (8 elements) of vector v
+template <int D, int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* code_blk, int k, int p, uint64_t c64) {
+  constexpr int P = Geo<D>::P;
+  const int e0 = k * 8 * P + 8 * p;                 // first element of the chunk
+  if constexpr (BITS == 8) {
+    uint2 w;
+    w.x = (uint32_t)c64;
+    w.y = (uint32_t)(c64 >> 32);
+    *reinterpret_cast<uint2*>(code_blk + e0) = w;
+  } else if constexpr (BITS == 4) {
+    *reinterpret_cast<uint32_t*>(code_blk + e0 / 2) = (uint32_t)c64;
+  } else {                                          // 3 bits: 24-bit piece at byte 3*e0/8
+    uint8_t* q = code_blk + (3 * e0) / 8;
+    q[0] = (uint8_t)c64;
+    q[1] = (uint8_t)(c64 >> 8);
+    q[2] = (uint8_t)(c64 >> 16);
+  }
+}
+
+template <int D, int DT, int C>
+__device__ __forceinline__ int encode_vector(const uint4* w, int v, const Lane& ln, uint8_t* code_blk,
+                                             uint8_t* meta_blk, float fixed, uint32_t sign_bits,
+                                             const CellEntry* cells) {
+  constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP;
+  constexpr int BITS = CodecInfo<C>::bits;
+  constexpr int CB = BITS * D / 8;
+  uint8_t* cv = code_blk + (size_t)v * CB;
+  float x[E];
+#pragma unroll
+  for (int k = 0; k < NCH; k++) unpack8<DT>(w[k], x + 8 * k);
+  int bad = 0;
+
+  if constexpr (CodecInfo<C>::fp8 || C == C_INT8) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int k = 0; k < NCH; k++) am = max(am, absmax_bits(w[k]));
+    am = group_umax<LOGP>(am);
+    bad = CodecInfo<C>::fp8 ? (am > Lim<DT>::fp8max) : (am >= Lim<DT>::nonfinite);
+    float s = 1.0f;
+    if constexpr (C == C_FP8F) s = fixed;
+    if constexpr (C == C_FP8Y) {
+      const float r448 = 1.0f / 448.0f;
+      s = fmaxf(bits_to_f32<DT>(am), 1e-12f) * r448;
+    }
+    if constexpr (C == C_INT8) s = fmaxf(bits_to_f32<DT>(am), 1e-12f) / 127.0f;
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      uint64_t c64;
+      if constexpr (C == C_INT8) {
+        uint32_t b[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          float q = rintf(x[8 * k + j] / s);
+          q = fminf(fmaxf(q, -127.0f), 127.0f);
+          b[j] = (uint32_t)(int)q & 0xFFu;
+        }
+        const uint32_t lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+        const uint32_t hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+        c64 = (uint64_t)lo | ((uint64_t)hi << 32);
+      } else {
+        float q[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          float t = x[8 * k + j];
+          if constexpr (C != C_FP8D) {
+            t = t / s;
+            t = fminf(fmaxf(t, -448.0f), 448.0f);
+          }
+          q[j] = t;
+        }
+        const uint2 r = fp8x8(q);
+        c64 = (uint64_t)r.x | ((uint64_t)r.y << 32);
+      }
+      store_codes<D, 8>(cv, k, ln.p, c64);
+    }
+    if constexpr (C == C_FP8Y || C == C_INT8)
+      if (ln.p == 0) *reinterpret_cast<float*>(meta_blk + (size_t)v * 4) = s;
+  }
+
+  if constexpr (CodecInfo<C>::uni) {
+    constexpr int TOP = (1 << BITS) - 1;
+    uint32_t am = 0;
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int k = 0; k < NCH; k++) am = max(am, absmax_bits(w[k]));
+#pragma unroll
+    for (int e = 1; e < E; e++) {
+      mn = fminf(mn, x[e]);
+      mx = fmaxf(mx, x[e]);
+    }
+    am = group_umax<LOGP>(am);
+    mn = group_min<LOGP>(mn);
+    mx = group_max<LOGP>(mx);
+    const float sig = (mx - mn) / (float)TOP;
+    const float mh = f16_round(mn), sh = f16_round(sig);
+    bad = (am >= Lim<DT>::nonfinite) || !__builtin_isfinite(mh) || !__builtin_isfinite(sh);
+    const float y = sh == 0.0f ? 0.0f : 1.0f / sh;
+    constexpr int MAGIC = 0x4B400000;   // bits of 1.5 * 2^23
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      uint64_t c64 = 0;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float d = x[8 * k + j] - mh;
+        // RN(d*y + 1.5*2^23) = 1.5*2^23 + RNE(d*y) when |d*y| < 2^22; the
+        // integer clamp also maps every out-of-range case to 0 or TOP.
+        const int t = __float_as_int(fmaf(d, y, 12582912.0f));
+        const int q = min(max(t, MAGIC), MAGIC + TOP) - MAGIC;
+        c64 |= (uint64_t)q << (BITS * j);
+      }
+      store_codes<D, BITS>(cv, k, ln.p, c64);
+    }
+    if (ln.p == 0)
+      *reinterpret_cast<uint32_t*>(meta_blk + (size_t)v * 4) = f16_bits(mh) | (f16_bits(sh) << 16);
+  }
+
+  if constexpr (CodecInfo<C>::tq) {
+    // 1. sum of squares: in-lane tree over j, cross-lane over group bits,
+    //    then the chunk tree -- the pairwise order of the element index.
+    float part[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      float s[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) s[j] = x[8 * k + j] * x[8 * k + j];
+#pragma unroll
+      for (int wdt = 8; wdt > 1; wdt >>= 1)
+#pragma unroll
+        for (int j = 0; j < wdt / 2; j++) s[j] = s[2 * j] + s[2 * j + 1];
+      part[k] = group_sum<LOGP>(s[0]);
+    }
+#pragma unroll
+    for (int wdt = NCH; wdt > 1; wdt >>= 1)
+#pragma unroll
+      for (int k = 0; k < wdt / 2; k++) part[k] = part[2 * k] + part[2 * k + 1];
+    const float n = sqrtf(part[0]);
+    const float nh = f16_round(n);
+    bad = !__builtin_isfinite(nh);
+    const float r = (n == 0.0f || bad) ? 0.0f : 1.0f / n;
+    // 2.-3. normalise, then the sign flip (exact)
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      const float u = x[e] * r;
+      y[e] = __uint_as_float(__float_as_uint(u) ^ (((sign_bits >> e) & 1u) << 31));
+    }
+    // 4. WHT, stages in ascending span
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int k = 0; k < NCH; k++)
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          if (!(j & h)) {
+            const float a = y[8 * k + j], b = y[8 * k + j + h];
+            y[8 * k + j] = a + b;
+            y[8 * k + j + h] = a - b;
+          }
+    // cross-lane: lower lane a + b, upper lane a - b = partner - own
+    if constexpr (LOGP >= 1) {
+      const float sg = upper_lane<0>() ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < E; e++) y[e] = xlane<0>(y[e]) + y[e] * sg;
+    }
+    if constexpr (LOGP >= 2) {
+      const float sg = upper_lane<1>() ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < E; e++) y[e] = xlane<1>(y[e]) + y[e] * sg;
+    }
+    if constexpr (LOGP >= 3) {
+      const float sg = upper_lane<2>() ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < E; e++) y[e] = xlane<2>(y[e]) + y[e] * sg;
+    }
+#pragma unroll
+    for (int kh = 1; kh < NCH; kh <<= 1)
+#pragma unroll
+      for (int k = 0; k < NCH; k++)
+        if (!(k & kh))
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const float a = y[8 * k + j], b = y[8 * (k + kh) + j];
+            y[8 * k + j] = a + b;
+            y[8 * (k + kh) + j] = a - b;
+          }
+    // 5. bucketize: code = #{B_k < z} = base(cell) + (z > T(cell))
+    constexpr int LO = 0x4B400000 - kCellOffset, HI = 0x4B400000 + kCellOffset;
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      uint64_t c64 = 0;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float z = y[8 * k + j];
+        const int t = __float_as_int(fmaf(z, kCellScale, 12582912.0f));
+        const int idx = min(max(t, LO), HI) - LO;
+        const CellEntry ce = cells[idx];
+        const uint32_t q = ce.base + (z > ce.thr ? 1u : 0u);
+        c64 |= (uint64_t)q << (BITS * j);
+      }
+      store_codes<D, BITS>(cv, k, ln.p, c64);
+    }
+    if (ln.p == 0) *reinterpret_cast<uint16_t*>(meta_blk + (size_t)v * 2) = (uint16_t)f16_bits(nh);
+  }
+  return bad;
+}
+
+// lane's TurboQuant sign bits: bit e of the result = sign of its element e
+template <int D>
+__device__ __forceinline__ uint32_t lane_signs(const uint32_t* mask, int p) {
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH;
+  uint32_t r = 0;
+#pragma unroll
+  for (int k = 0; k < NCH; k++) {
+    const int e0 = k * 8 * P + 8 * p;            // multiple of 8: one byte of the mask
+    r |= ((mask[e0 >> 5] >> (e0 & 31)) & 0xFFu) << (8 * k);
+  }
+  return r;
+}
+
+template <int D, int DT, int C>
+__device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, uint32_t sign_bits,
+                                      const CellEntry* cells) {
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
+  constexpr int CB = CodecInfo<C>::bits * D / 8;
+  uint8_t* code_blk = s.slot + kHeaderBytes;
+  uint8_t* meta_blk = code_blk + (size_t)s.n_vec * CB;
+  int bad = 0;
+  for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
+    uint4 w[U][NCH];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int v = v0 + u * GW;
+      if (v < s.n_vec) {
+        const uint16_t* src = vec_ptr(s, v);
+#pragma unroll
+        for (int k = 0; k < NCH; k++)
+          w[u][k] = ld_stream(src + k * 8 * P + 8 * ln.p);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int v = v0 + u * GW;
+      if (v < s.n_vec) bad |= encode_vector<D, DT, C>(w[u], v, ln, code_blk, meta_blk, fixed, sign_bits, cells);
+    }
+  }
+  return bad;
+}
+
+// copy a segment from the engine layout into contiguous canonical order
+template <int D>
+__device__ void copy_out_raw(const SegCtx& s, uint8_t* dst) {
+  constexpr int CPV = D / 8;                        // 16-byte chunks per vector
+  const int total = s.n_vec * CPV;
+  for (int q = threadIdx.x; q < total; q += kThreads) {
+    const int v = q / CPV, c = q - v * CPV;
+    const uint4 val = ld_stream(vec_ptr(s, v) + 8 * c);
+    *reinterpret_cast<uint4*>(dst + (size_t)q * 16) = val;
+  }
+}
+
+__device__ __forceinline__ void zero_fill(uint8_t* p, size_t n) {
+  // bytes [0, n) of a region whose start may be unaligned
+  size_t head = (16 - ((uintptr_t)p & 15)) & 15;
+  if (head > n) head = n;
+  for (size_t b = threadIdx.x; b < head; b += kThreads) p[b] = 0;
+  uint8_t* a = p + head;
+  const size_t n16 = (n - head) / 16;
+  for (size_t q = threadIdx.x; q < n16; q += kThreads) reinterpret_cast<uint4*>(a)[q] = make_uint4(0, 0, 0, 0);
+  for (size_t b = head + n16 * 16 + threadIdx.x; b < n; b += kThreads) p[b] = 0;
+}
+
+__device__ __forceinline__ void write_header_desc(uint8_t* slot, kvc_segment_desc* desc, uint64_t slot_off,
+                                                  int format, int flags, int status, int dtype, int comp,
+                                                  int d, int n_vec, uint32_t stored, uint64_t spill,
+                                                  uint32_t aux) {
+  uint4 h0, h1;
+  h0.x = 1u | ((uint32_t)format << 8) | ((uint32_t)flags << 16) | ((uint32_t)(dtype | (comp << 4)) << 24);
+  h0.y = (uint32_t)d | ((uint32_t)n_vec << 16);
+  h0.z = (uint32_t)(n_vec * d * 2);
+  h0.w = stored;
+  h1.x = (uint32_t)spill;
+  h1.y = (uint32_t)(spill >> 32);
+  h1.z = 0;
+  h1.w = aux;
+  reinterpret_cast<uint4*>(slot)[0] = h0;
+  reinterpret_cast<uint4*>(slot)[1] = h1;
+  uint4 d0, d1;
+  d0.x = (uint32_t)slot_off;
+  d0.y = (uint32_t)(slot_off >> 32);
+  d0.z = (uint32_t)spill;
+  d0.w = (uint32_t)(spill >> 32);
+  d1.x = stored;
+  d1.y = (uint32_t)(n_vec * d * 2);
+  d1.z = 1u | ((uint32_t)format << 8) | ((uint32_t)flags << 16) | ((uint32_t)status << 24);
+  d1.w = 0;
+  reinterpret_cast<uint4*>(desc)[0] = d0;
+  reinterpret_cast<uint4*>(desc)[1] = d1;
+}
+
+// ------------------------------------------------------------------ encode kernel
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
+  __shared__ CellEntry s_cells[kCells];
+  __shared__ unsigned long long s_spill;
+
+  const uint32_t seg = blockIdx.x;
+  const uint32_t two_n = 2u * p.n_pages;
+  const uint32_t l = seg / two_n;
+  const uint32_t rem = seg - l * two_n;
+  const uint32_t pi = rem >> 1, comp = rem & 1;
+  const SideEntry& E = p.sides[2 * l + comp];
+  const int codec = (int)E.codec;
+  const uint64_t slot_off = E.slot_base + (uint64_t)pi * E.page_stride;
+  const int32_t page = p.pages[pi];
+  // guard: the side table and page list come from memory; never follow a
+  // base pointer outside the caller's set or a page id outside the pool
+  if ((uint64_t)(uintptr_t)E.base < p.base_lo || (uint64_t)(uintptr_t)E.base > p.base_hi || page < 0 ||
+      (uint32_t)page >= p.num_blocks || slot_off + E.slot_bytes > p.slot_region) {
+    if (threadIdx.x == 0) reinterpret_cast<uint4*>(p.desc + seg)[1] = make_uint4(0, 0, (uint32_t)KVC_SEG_GUARD << 24, 0);
+    return;
+  }
+  SegCtx s;
+  s.src = E.base + (int64_t)page * p.sb;
+  s.slot = p.buf + slot_off;
+  s.heads = (int)p.heads;
+  s.n_vec = (int)(p.heads * p.tokens);
+  s.st = p.st;
+  s.sh = p.sh;
+  const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
+  const uint32_t slot_bytes = E.slot_bytes;
+  kvc_segment_desc* desc = p.desc + seg;
+
+  if (codec == C_RAW) {                                        // raw by policy
+    copy_out_raw<D>(s, s.slot + kHeaderBytes);
+    zero_fill(s.slot + kHeaderBytes + raw_bytes, slot_bytes - kHeaderBytes - raw_bytes);
+    if (threadIdx.x == 0)
+      write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY, KVC_SEG_RAW_POLICY, DT, comp, D,
+                        s.n_vec, raw_bytes, 0, 0);
+    return;
+  }
+
+  const Lane ln = lane_info<D>();
+  const bool tq = codec == C_TQ3 || codec == C_TQ4;
+  if (tq) {
+    const CellEntry* src = p.tables->cells[codec == C_TQ4 ? 1 : 0];
+    for (int q = threadIdx.x; q < kCells; q += kThreads) s_cells[q] = src[q];
+    __syncthreads();
+  }
+  const uint32_t sign_bits = tq ? lane_signs<D>(p.sign_mask, ln.p) : 0u;
+  const float fixed = E.fixed;
+
+  int bad = 0;
+  switch (codec) {
+    case C_FP8D: bad = encode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, sign_bits, s_cells); break;
+    case C_FP8F: bad = encode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, sign_bits, s_cells); break;
+    case C_FP8Y: bad = encode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, sign_bits, s_cells); break;
+    case C_INT8: bad = encode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, sign_bits, s_cells); break;
+    case C_U3: bad = encode_segment_vectors<D, DT, C_U3>(s, ln, fixed, sign_bits, s_cells); break;
+    case C_U4: bad = encode_segment_vectors<D, DT, C_U4>(s, ln, fixed, sign_bits, s_cells); break;
+    case C_TQ3: bad = encode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, sign_bits, s_cells); break;
+    case C_TQ4: bad = encode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, sign_bits, s_cells); break;
+    default: break;
+  }
+  const int any_bad = __syncthreads_or(bad);
+
+  int bits = 8, meta = 0;
+  switch (codec) {
+    case C_U3: case C_TQ3: bits = 3; break;
+    case C_U4: case C_TQ4: bits = 4; break;
+    default: break;
+  }
+  if (codec == C_FP8Y || codec == C_INT8 || codec == C_U3 || codec == C_U4) meta = 4;
+  if (codec == C_TQ3 || codec == C_TQ4) meta = 2;
+  const uint32_t payload = (uint32_t)s.n_vec * (uint32_t)(bits * D / 8 + meta);
+  zero_fill(s.slot + kHeaderBytes + payload, slot_bytes - kHeaderBytes - payload);
+
+  if (!any_bad) {
+    if (threadIdx.x == 0)
+      write_header_desc(s.slot, desc, slot_off, codec, 0, KVC_SEG_ENCODED, DT, comp, D, s.n_vec, payload, 0,
+                        codec == C_FP8F ? __float_as_uint(fixed) : 0u);
+    return;
+  }
+  // raw because of its data: reserve spill space, copy the source bytes
+  const uint64_t need = (raw_bytes + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
+  if (threadIdx.x == 0) s_spill = atomicAdd(p.spill_cursor, (unsigned long long)need);
+  __syncthreads();
+  const uint64_t off = s_spill;
+  const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
+  if (fits) copy_out_raw<D>(s, p.buf + p.slot_region + off);
+  if (threadIdx.x == 0) {
+    if (fits)
+      write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA, KVC_SEG_RAW_DATA, DT, comp, D, s.n_vec,
+                        raw_bytes, p.slot_region + off, 0);
+    else
+      write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | KVC_FLAG_CAPACITY, KVC_SEG_CAPACITY,
+                        DT, comp, D, s.n_vec, raw_bytes, 0, 0);
+  }
+}
+
+// ------------------------------------------------------------------ decoders
+template <int D, int BITS>
+__device__ __forceinline__ uint64_t load_codes(const uint8_t* code_blk, int k, int p) {
+  constexpr int P = Geo<D>::P;
+  const int e0 = k * 8 * P + 8 * p;
+  if constexpr (BITS == 8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(code_blk + e0);
+    return (uint64_t)w.x | ((uint64_t)w.y << 32);
+  } else if constexpr (BITS == 4) {
+    return *reinterpret_cast<const uint32_t*>(code_blk + e0 / 2);
+  } else {
+    const uint8_t* q = code_blk + (3 * e0) / 8;
+    return (uint64_t)q[0] | ((uint64_t)q[1] << 8) | ((uint64_t)q[2] << 16);
+  }
+}
+
+template <int D, int DT, int C>
+__device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uint8_t* meta_blk, int v,
+                                              const Lane& ln, uint16_t* dst, float fixed, uint32_t sign_bits,
+                                              const float* cent) {
+  constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP, P = Geo<D>::P;
+  constexpr int BITS = CodecInfo<C>::bits;
+  constexpr int CB = BITS * D / 8;
+  const uint8_t* cv = code_blk + (size_t)v * CB;
+  float y[E];
+  if constexpr (CodecInfo<C>::fp8 || C == C_INT8) {
+    float s = 1.0f;
+    if constexpr (C == C_FP8F) s = fixed;
+    if constexpr (C == C_FP8Y || C == C_INT8) s = *reinterpret_cast<const float*>(meta_blk + (size_t)v * 4);
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      const uint64_t c64 = load_codes<D, 8>(cv, k, ln.p);
+      const uint32_t lo = (uint32_t)c64, hi = (uint32_t)(c64 >> 32);
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const uint32_t word = j < 4 ? lo : hi;
+        float val;
+        if constexpr (C == C_INT8) {
+          val = (float)(int8_t)(word >> (8 * (j & 3)));
+        } else {
+          switch (j & 3) {
+            case 0: val = __builtin_amdgcn_cvt_f32_fp8((int)word, 0); break;
+            case 1: val = __builtin_amdgcn_cvt_f32_fp8((int)word, 1); break;
+            case 2: val = __builtin_amdgcn_cvt_f32_fp8((int)word, 2); break;
+            default: val = __builtin_amdgcn_cvt_f32_fp8((int)word, 3); break;
+          }
+        }
+        if constexpr (C != C_FP8D) val = val * s;
+        y[8 * k + j] = val;
+      }
+    }
+  }
+  if constexpr (CodecInfo<C>::uni) {
+    const uint32_t mw = *reinterpret_cast<const uint32_t*>(meta_blk + (size_t)v * 4);
+    const float mh = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
+    const float sh = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      const uint64_t c64 = load_codes<D, BITS>(cv, k, ln.p);
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float code = (float)(uint32_t)((c64 >> (BITS * j)) & ((1u << BITS) - 1));
+        y[8 * k + j] = fmaf(code, sh, mh);    // code*sh is exact: one rounding either way
+      }
+    }
+  }
+  if constexpr (CodecInfo<C>::tq) {
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      const uint64_t c64 = load_codes<D, BITS>(cv, k, ln.p);
+#pragma unroll
+      for (int j = 0; j < 8; j++) y[8 * k + j] = cent[(uint32_t)(c64 >> (BITS * j)) & ((1u << BITS) - 1)];
+    }
+    float part[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      float s[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) s[j] = y[8 * k + j] * y[8 * k + j];
+#pragma unroll
+      for (int wdt = 8; wdt > 1; wdt >>= 1)
+#pragma unroll
+        for (int j = 0; j < wdt / 2; j++) s[j] = s[2 * j] + s[2 * j + 1];
+      part[k] = group_sum<LOGP>(s[0]);
+    }
+#pragma unroll
+    for (int wdt = NCH; wdt > 1; wdt >>= 1)
+#pragma unroll
+      for (int k = 0; k < wdt / 2; k++) part[k] = part[2 * k] + part[2 * k + 1];
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int k = 0; k < NCH; k++)
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          if (!(j & h)) {
+            const float a = y[8 * k + j], b = y[8 * k + j + h];
+            y[8 * k + j] = a + b;
+            y[8 * k + j + h] = a - b;
+          }
+    if constexpr (LOGP >= 1) {
+      const float sg = upper_lane<0>() ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < E; e++) y[e] = xlane<0>(y[e]) + y[e] * sg;
+    }
+    if constexpr (LOGP >= 2) {
+      const float sg = upper_lane<1>() ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < E; e++) y[e] = xlane<1>(y[e]) + y[e] * sg;
+    }
+    if constexpr (LOGP >= 3) {
+      const float sg = upper_lane<2>() ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < E; e++) y[e] = xlane<2>(y[e]) + y[e] * sg;
+    }
+#pragma unroll
+    for (int kh = 1; kh < NCH; kh <<= 1)
+#pragma unroll
+      for (int k = 0; k < NCH; k++)
+        if (!(k & kh))
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const float a = y[8 * k + j], b = y[8 * (k + kh) + j];
+            y[8 * k + j] = a + b;
+            y[8 * (k + kh) + j] = a - b;
+          }
+    const float nh = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(meta_blk + (size_t)v * 2));
+    const float rd = sqrtf((float)D);
+    const float g = nh / (sqrtf(part[0]) * rd);
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      const float t = y[e] * g;
+      y[e] = __uint_as_float(__float_as_uint(t) ^ (((sign_bits >> e) & 1u) << 31));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NCH; k++)
+    *reinterpret_cast<uint4*>(dst + k * 8 * P + 8 * ln.p) = pack8<DT>(y + 8 * k);
+}
+
+template <int D, int DT, int C>
+__device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, uint32_t sign_bits,
+                                       const float* cent) {
+  constexpr int GW = Geo<D>::GW;
+  constexpr int CB = CodecInfo<C>::bits * D / 8;
+  const uint8_t* code_blk = s.slot + kHeaderBytes;
+  const uint8_t* meta_blk = code_blk + (size_t)s.n_vec * CB;
+  for (int v = ln.g; v < s.n_vec; v += GW)
+    decode_vector<D, DT, C>(code_blk, meta_blk, v, ln, const_cast<uint16_t*>(vec_ptr(s, v)), fixed, sign_bits,
+                            cent);
+}
+
+template <int D>
+__device__ void copy_in_raw(const SegCtx& s, const uint8_t* srcb) {
+  constexpr int CPV = D / 8;
+  const int total = s.n_vec * CPV;
+  for (int q = threadIdx.x; q < total; q += kThreads) {
+    const int v = q / CPV, c = q - v * CPV;
+    const uint4 val = *reinterpret_cast<const uint4*>(srcb + (size_t)q * 16);
+    *reinterpret_cast<uint4*>(const_cast<uint16_t*>(vec_ptr(s, v)) + 8 * c) = val;
+  }
+}
+
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
+  __shared__ float s_cent[16];
+  const uint32_t seg = blockIdx.x;
+  const uint32_t two_n = 2u * p.n_pages;
+  const uint32_t l = seg / two_n;
+  const uint32_t rem = seg - l * two_n;
+  const uint32_t pi = rem >> 1, comp = rem & 1;
+  const SideEntry& E = p.sides[2 * l + comp];
+  const int codec = (int)E.codec;
+  const uint64_t slot_off = E.slot_base + (uint64_t)pi * E.page_stride;
+  const int32_t page = p.pages[pi];
+  if ((uint64_t)(uintptr_t)E.base < p.base_lo || (uint64_t)(uintptr_t)E.base > p.base_hi || page < 0 ||
+      (uint32_t)page >= p.num_blocks || slot_off + E.slot_bytes > p.slot_region) {
+    if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 2;
+    return;
+  }
+  SegCtx s;
+  s.src = E.base + (int64_t)page * p.sb;                  // destination page
+  s.slot = p.buf + slot_off;
+  s.heads = (int)p.heads;
+  s.n_vec = (int)(p.heads * p.tokens);
+  s.st = p.st;
+  s.sh = p.sh;
+  const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
+
+  // header check (wave-uniform loads)
+  const uint4 h0 = reinterpret_cast<const uint4*>(s.slot)[0];
+  const uint4 h1 = reinterpret_cast<const uint4*>(s.slot)[1];
+  const int version = h0.x & 0xFF, format = (h0.x >> 8) & 0xFF, flags = (h0.x >> 16) & 0xFF;
+  const int dc = (h0.x >> 24) & 0xFF;
+  bool ok = version == 1 && dc == (DT | (int)(comp << 4)) && (h0.y & 0xFFFF) == (uint32_t)D &&
+            (h0.y >> 16) == (uint32_t)s.n_vec && h0.z == raw_bytes;
+  const bool raw_data = flags & KVC_FLAG_RAW_DATA;
+  uint64_t spill = (uint64_t)h1.x | ((uint64_t)h1.y << 32);
+  if (raw_data) ok = ok && format == KVC_RAW && !(flags & KVC_FLAG_CAPACITY) && raw_bytes <= p.buf_bytes &&
+                     spill >= p.slot_region && spill <= p.buf_bytes - raw_bytes;
+  else ok = ok && format == codec;
+  if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = ok ? 0 : 1;
+  if (!ok) return;
+
+  if (raw_data) {
+    copy_in_raw<D>(s, p.buf + spill);
+    return;
+  }
+  if (codec == C_RAW) {
+    copy_in_raw<D>(s, s.slot + kHeaderBytes);
+    return;
+  }
+  const Lane ln = lane_info<D>();
+  const bool tq = codec == C_TQ3 || codec == C_TQ4;
+  if (tq) {
+    if (threadIdx.x < 16) s_cent[threadIdx.x] = p.tables->centroids[codec == C_TQ4 ? 1 : 0][threadIdx.x];
+    __syncthreads();
+  }
+  const uint32_t sign_bits = tq ? lane_signs<D>(p.sign_mask, ln.p) : 0u;
+  const float fixed = __uint_as_float(h1.w);
+  switch (codec) {
+    case C_FP8D: decode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, sign_bits, s_cent); break;
+    case C_FP8F: decode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, sign_bits, s_cent); break;
+    case C_FP8Y: decode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, sign_bits, s_cent); break;
+    case C_INT8: decode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, sign_bits, s_cent); break;
+    case C_U3: decode_segment_vectors<D, DT, C_U3>(s, ln, fixed, sign_bits, s_cent); break;
+    case C_U4: decode_segment_vectors<D, DT, C_U4>(s, ln, fixed, sign_bits, s_cent); break;
+    case C_TQ3: decode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, sign_bits, s_cent); break;
+    case C_TQ4: decode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, sign_bits, s_cent); break;
+    default: break;
+  }
+}
+
+template <int D>
+hipError_t launch_encode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
+  dim3 grid((unsigned)nseg), block(kThreads);
+  if (p.dtype == KVC_BF16) hipLaunchKernelGGL((encode_kernel<D, KVC_BF16>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((encode_kernel<D, KVC_FP16>), grid, block, 0, st, p);
+  return hipGetLastError();
+}
+template <int D>
+hipError_t launch_decode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
+  dim3 grid((unsigned)nseg), block(kThreads);
+  if (p.dtype == KVC_BF16) hipLaunchKernelGGL((decode_kernel<D, KVC_BF16>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((decode_kernel<D, KVC_FP16>), grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode(const CallParams& p, uint32_t head_dim, uint64_t nseg, hipStream_t st) {
+  switch (head_dim) {
+    case 32: return launch_encode_d<32>(p, nseg, st);
+    case 64: return launch_encode_d<64>(p, nseg, st);
+    case 128: return launch_encode_d<128>(p, nseg, st);
+    case 256: return launch_encode_d<256>(p, nseg, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode(const CallParams& p, uint32_t head_dim, uint64_t nseg, hipStream_t st) {
+  switch (head_dim) {
+    case 32: return launch_decode_d<32>(p, nseg, st);
+    case 64: return launch_decode_d<64>(p, nseg, st);
+    case 128: return launch_decode_d<128>(p, nseg, st);
+    case 256: return launch_decode_d<256>(p, nseg, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvc

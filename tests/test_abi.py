@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads and exports every entry point
+include/kvc.h declares; kvc_plan agrees with the oracle's independent plan
+and with the pages' payload sizes; host-side validation rejects bad
+arguments before anything would be enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_page_kvc_amd as kvc
+from oracle import kvc_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    declared = set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", hdr))
+    assert declared == set(kvc.EXPORTS)
+    L = kvc.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert kvc.status_string(kvc.KVC_E_DUP_DST) == "duplicate destination page"
+
+
+def test_struct_sizes():
+    assert ctypes.sizeof(kvc.kvc_segment_desc) == 32
+    assert ctypes.sizeof(kvc.kvc_layout) == 80
+
+
+FAKE = 1 << 40          # aligned fake device addresses: validation never dereferences them
+
+
+def layout(kind=kvc.KVC_SEPARATE_NHD, dtype=kvc.KVC_BF16, L=4, H=8, D=128, T=16, nb=100, strides=None):
+    if strides is None:
+        strides = (T * H * D, H * D, D) if kind == kvc.KVC_SEPARATE_NHD else (H * T * 2 * D, 2 * D, T * 2 * D)
+    k = [FAKE + l * (1 << 30) for l in range(L)]
+    v = [FAKE + (1 << 38) + l * (1 << 30) for l in range(L)] if kind == kvc.KVC_SEPARATE_NHD else None
+    return kvc.Layout(kind, dtype, L, H, D, T, nb, *strides, k, v)
+
+
+@pytest.mark.parametrize("ck,cv", [("TQ4", "UNIFORM4"), ("TQ3", "UNIFORM3"), ("FP8_DYNAMIC", "INT8"),
+                                   ("RAW", "FP8_FIXED"), ("FP8_DIRECT", "RAW")])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
+def test_plan_matches_oracle(ck, cv, D):
+    L, H, T, n = 6, 8, 16, 37
+    prot = [0, 5]
+    lay = layout(D=D, L=L, H=H, T=T)
+    fixed = np.full((L, 2), 0.5, np.float32)
+    codec = kvc.Codec(ck, cv, seed=1, fixed_scales=fixed, protected_layers=prot, layers=L)
+    slot, spill, bpt = kvc.kvc_plan(lay, codec, n)
+    offs, sizes, effs, total = O.plan(L, H, D, T, kvc.CODECS[ck], kvc.CODECS[cv],
+                                      [1 if l in prot else 0 for l in range(L)], n)
+    assert slot == total
+    per_page = sum(sizes[:2 * L * n:2 * n]) + sum(sizes[1:2 * L * n:2 * n])
+    assert bpt == -(-per_page // T)
+    assert spill >= 256 * -(-H * T * D * 2 // 256)
+
+
+def test_plan_pages_sizes_d128():
+    """16 tokens x 8 heads x D128 per segment: 128 vectors at the pages'
+    66/68 (4-bit) and 50/52 (3-bit) bytes plus the 32-byte header, rounded to
+    256 bytes."""
+    for ck, cv, kb, vb in (("TQ4", "UNIFORM4", 66, 68), ("TQ3", "UNIFORM3", 50, 52)):
+        lay = layout(L=1)
+        slot, _, bpt = kvc.kvc_plan(lay, kvc.Codec(ck, cv), 1)
+        exp = sum(-(-(32 + 128 * b) // 256) * 256 for b in (kb, vb))
+        assert slot == exp
+
+
+def _st(fn, *a):
+    return fn(*a)
+
+
+def test_validation_errors():
+    codec = kvc.Codec("TQ4", "UNIFORM4")
+    ok = layout()
+    ids = np.arange(10, dtype=np.int32)
+    slot, _, _ = kvc.kvc_plan(ok, codec, 10)
+    V = kvc.kvc_validate_encode
+    assert V(ok, codec, ids, slot) == kvc.KVC_OK
+    assert V(ok, codec, ids, slot - 1) == kvc.KVC_E_CAPACITY
+    assert V(layout(D=96), codec, ids, slot) == kvc.KVC_E_UNSUPPORTED
+    assert V(layout(D=512), codec, ids, slot) == kvc.KVC_E_UNSUPPORTED
+    assert V(layout(dtype=3), codec, ids, slot) == kvc.KVC_E_UNSUPPORTED
+    assert V(ok, codec, np.array([0, 100], np.int32), slot) == kvc.KVC_E_PAGE_RANGE
+    assert V(ok, codec, np.array([-1], np.int32), slot) == kvc.KVC_E_PAGE_RANGE
+    # strides must be positive multiples of 8 and non-overlapping for the kind
+    assert V(layout(strides=(16 * 8 * 128, 8 * 128, 100)), codec, ids, slot) == kvc.KVC_E_ARG
+    assert V(layout(strides=(16 * 8 * 128, 8 * 64, 128)), codec, ids, slot) == kvc.KVC_E_ARG
+    assert V(layout(kind=kvc.KVC_PACKED_HT2D, strides=(8 * 16 * 128, 128, 16 * 128)), codec, ids,
+             slot) == kvc.KVC_E_ARG
+    # packed layout must not carry V pointers, separate must
+    bad = layout()
+    bad.c.v_base = None
+    assert V(bad, codec, ids, slot) == kvc.KVC_E_ARG
+    # unaligned base pointer
+    lay = layout()
+    lay._k[1] = FAKE + 8
+    assert V(lay, codec, ids, slot) == kvc.KVC_E_ARG
+    # FP8_FIXED needs sane scales
+    assert V(ok, kvc.Codec("FP8_FIXED", "RAW"), ids, 1 << 40) == kvc.KVC_E_ARG
+    for badscale in (0.0, -1.0, np.inf, np.nan, 1e-35):
+        fs = np.full((4, 2), 1.0, np.float32)
+        fs[2, 0] = badscale
+        assert V(ok, kvc.Codec("FP8_FIXED", "RAW", fixed_scales=fs), ids, 1 << 40) == kvc.KVC_E_ARG
+    assert V(ok, kvc.Codec(9, 0), ids, 1 << 40) == kvc.KVC_E_ARG
+
+
+def test_decode_rejects_duplicate_destinations():
+    codec = kvc.Codec("INT8", "INT8")
+    ok = layout()
+    slot, _, _ = kvc.kvc_plan(ok, codec, 3)
+    assert kvc.kvc_validate_decode(ok, codec, np.array([3, 7, 9], np.int32), slot) == kvc.KVC_OK
+    assert kvc.kvc_validate_decode(ok, codec, np.array([3, 7, 3], np.int32), slot) == kvc.KVC_E_DUP_DST
+    # encode may read the same page twice
+    assert kvc.kvc_validate_encode(ok, codec, np.array([3, 7, 3], np.int32), slot) == kvc.KVC_OK
+
+
+def test_keep_rule_makes_tiny_segments_raw():
+    # 1 token x 1 head x D32: a 256-B slot never saves 12.5% of 64 B -> raw slot
+    lay = layout(H=1, T=1, D=32, L=1)
+    slot, _, _ = kvc.kvc_plan(lay, kvc.Codec("INT8", "TQ4"), 1)
+    assert slot == 2 * 256

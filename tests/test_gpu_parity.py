@@ -1,0 +1,350 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: encoded bytes (codes, metadata, headers, padding) and segment statuses
+bit-exact for every codec; decoded values bit-exact for FP8, INT8, uniform
+and raw; TurboQuant decodes within 1e-3 absolute (and reported bit-equal up
+to the sign of zero).  Small cases cover every codec, head dim, dtype and
+layout over several tiles and a ragged page count; the workload-sized cases
+run at full size in the launch configuration the benchmark times, checked
+on sampled segments.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():      # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import kv_cache_page_kvc_amd as kvc                      # noqa: E402
+from kv_cache_page_kvc_amd import inputs                 # noqa: E402
+from oracle import kvc_oracle as O                       # noqa: E402
+from tests import gpu_helpers as G                       # noqa: E402
+
+TQ_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = kvc.kvc_create(0, 0)
+    yield c
+    kvc.kvc_destroy(c)
+
+
+def _codec_ids(ck, cv):
+    return kvc.CODECS[ck], kvc.CODECS[cv]
+
+
+def _fixed_scales(L, seed=0):
+    rng = np.random.default_rng(seed)
+    return (2.0 ** rng.uniform(-9, -2, (L, 2))).astype(np.float32)
+
+
+def _check_decoded(dec_gpu: np.ndarray, dec_ora: np.ndarray, dt, lossy_tq: bool, where=""):
+    if not lossy_tq:
+        assert np.array_equal(dec_gpu, dec_ora), f"decode bits differ {where}"
+        return
+    a = G.bits_to_f32(dec_gpu, dt).astype(np.float64)
+    b = G.bits_to_f32(dec_ora, dt).astype(np.float64)
+    err = np.abs(a - b).max()
+    assert err <= TQ_TOL, f"TurboQuant decode error {err} {where}"
+
+
+def _roundtrip_case(ctx, wl, ck, cv, seed, page_ids, protected=None, fixed=None, segments=None,
+                    dst_ids=None, decode_from_oracle=True):
+    """Encode on GPU and oracle; compare.  Decode (a) the oracle's buffer on
+    the GPU and (b) the GPU's buffer on the GPU; compare both with the
+    oracle's decode of its own buffer."""
+    n_pages = len(page_ids)
+    kc, vc = _codec_ids(ck, cv)
+    codec = kvc.Codec(kc, vc, seed=seed, fixed_scales=fixed, protected_layers=protected, layers=wl.L)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, page_ids)
+    torch.cuda.synchronize()
+    nseg = wl.L * n_pages * 2
+    segs = list(range(nseg)) if segments is None else segments
+    ora_buf, ora_st, offs, ora_total = G.oracle_encode(wl, kc, vc, seed, page_ids, fixed, protected, segs)
+    assert ora_total == slot
+    gbuf = out.cpu().numpy()
+    gdesc = G.desc_np(desc)
+    bad = G.compare_encoded(gbuf, gdesc, ora_buf, ora_st, offs, ora_total, segs)
+    assert not bad, f"encode mismatches (first 5 of {len(bad)}): {bad[:5]}"
+
+    dst_ids = np.asarray(page_ids if dst_ids is None else dst_ids, np.int32)
+    ora_dec = G.oracle_decode_segments(ora_buf, wl, kc, vc, seed, n_pages, protected, segs)
+    seglist = G.segments_of(wl.L, n_pages)
+    lossy = lambda s: (kc if seglist[s][2] == 0 else vc) in (kvc.KVC_TQ3, kvc.KVC_TQ4) and ora_st[s] == 0
+
+    runs = [("gpu-encoded", out, total)]
+    if decode_from_oracle:
+        runs.append(("oracle-encoded", torch.from_numpy(ora_buf).cuda(), ora_buf.size))
+    for name, buf, nbytes in runs:
+        dst = wl.empty_like(fill_bits=0x7FC1)            # NaN sentinel poison
+        st = G.gpu_decode(ctx, dst, codec, buf, nbytes, dst_ids)
+        torch.cuda.synchronize()
+        stn = st.cpu().numpy()
+        for s in segs:
+            l, i, c = seglist[s]
+            assert stn[s] == 0, f"{name}: decode status {stn[s]} for segment {s}"
+            got = G.gpu_segment_vectors(dst, l, c, int(dst_ids[i]))
+            _check_decoded(got, ora_dec[s], wl.dt, lossy(s), f"{name} segment {s}")
+    return ora_st, gdesc
+
+
+# ----------------------------------------------------------------- small grid
+PAIRS = [("FP8_DIRECT", "FP8_DYNAMIC"), ("FP8_FIXED", "INT8"), ("TQ4", "UNIFORM4"),
+         ("TQ3", "UNIFORM3"), ("UNIFORM4", "TQ3"), ("INT8", "RAW")]
+
+
+@pytest.mark.parametrize("layout", ["separate", "packed"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("dim", [32, 64, 128, 256])
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}-{p[1]}")
+def test_small_grid(ctx, pair, dim, dtype, layout):
+    """3 layers (layer 1 protected), 2 heads, 16 tokens, 5 of 11 blocks in
+    random order: every segment compared, both decode directions."""
+    print(f"[case] small {pair} D={dim} {dtype} {layout}", flush=True)
+    L, H, T, pool = 3, 2, 16, 11
+    wl = G.Workload(L, H, dim, T, pool, dtype, layout, seed=dim + (7 if dtype == "fp16" else 0))
+    ids = inputs.random_page_ids(pool, 5, seed=dim)
+    fixed = _fixed_scales(L) if "FP8_FIXED" in pair else None
+    dst = inputs.random_page_ids(pool, 5, seed=dim + 1)
+    _roundtrip_case(ctx, wl, pair[0], pair[1], seed=1234 + dim, page_ids=ids, protected=[1], fixed=fixed,
+                    dst_ids=dst)
+
+
+def test_fp8_dynamic_small_full(ctx):
+    """FP8 E4M3FN dynamic workload, 2 layers x 8 heads x D128 BF16, 64 pages:
+    all 256 segments."""
+    cfg = inputs.CONFIGS["fp8_dynamic_small"]
+    print("[case] fp8_dynamic_small", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
+    ids = np.arange(cfg["pages"], dtype=np.int32)
+    _roundtrip_case(ctx, wl, "FP8_DYNAMIC", "FP8_DYNAMIC", 0, ids)
+
+
+def test_fp8_direct_every_source_value(ctx):
+    """Hardware E4M3FN conversion: every finite BF16 and FP16 pattern with
+    |x| <= 448, packed into segments, must encode to the oracle's codes."""
+    for dtype in ("bf16", "fp16"):
+        print(f"[case] fp8 exhaustive {dtype}", flush=True)
+        h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        x = O.src_to_f32(h, O.BF16 if dtype == "bf16" else O.FP16)
+        vals = h[np.isfinite(x) & (np.abs(x) <= 448)]
+        H, D, T = 8, 128, 16
+        per_page = T * H * D
+        n_pages = -(-vals.size // per_page)
+        pool = np.resize(vals, n_pages * per_page).reshape(n_pages, T, H, D)
+        wl = G.Workload(1, H, D, T, n_pages, dtype, "separate", 0)
+        wl.k[0].view(torch.int16).copy_(torch.from_numpy(pool.view(np.int16)).cuda())
+        wl.v[0].view(torch.int16).copy_(torch.from_numpy(pool[::-1].copy().view(np.int16)).cuda())
+        ids = np.arange(n_pages, dtype=np.int32)
+        _roundtrip_case(ctx, wl, "FP8_DIRECT", "FP8_DIRECT", 0, ids)
+
+
+def test_fp8_scaled_quotients(ctx):
+    """Scaled FP8 over many FP32 quotients: fixed scales spanning 2^-12..2^4
+    (clipping included) and dynamic scales."""
+    print("[case] fp8 scaled sweep", flush=True)
+    L, H, D, T, pool = 4, 8, 128, 16, 24
+    wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 5)
+    fixed = (2.0 ** np.linspace(-12, 4, 2 * L)).reshape(L, 2).astype(np.float32) * 1.37
+    ids = np.arange(pool, dtype=np.int32)
+    _roundtrip_case(ctx, wl, "FP8_FIXED", "FP8_DYNAMIC", 0, ids, fixed=fixed)
+
+
+def test_zero_and_tiny_vectors(ctx):
+    """All-zero vectors (INT8/FP8 floor, TurboQuant n = 0, uniform sigma = 0)
+    and subnormal-scale vectors."""
+    print("[case] zero/tiny", flush=True)
+    for ck, cv in (("INT8", "FP8_DYNAMIC"), ("TQ4", "UNIFORM4"), ("TQ3", "UNIFORM3")):
+        wl = G.Workload(2, 4, 64, 16, 6, "bf16", "separate", 9)
+        for t in wl.k + wl.v:
+            t[0].zero_()
+            t[1].mul_(1e-30)
+            t[2].fill_(3.0)
+        ids = np.arange(6, dtype=np.int32)
+        _roundtrip_case(ctx, wl, ck, cv, 77, ids)
+
+
+def test_gate_small(ctx):
+    """Injected NaN/Inf/|x|>448 values: the exact set of data-raw segments
+    per codec, bit-exact raw round trip, +-448 controls stay encoded."""
+    for ck, cv in (("INT8", "FP8_DIRECT"), ("FP8_DYNAMIC", "FP8_FIXED"), ("TQ4", "UNIFORM3")):
+        print(f"[case] gate {ck}/{cv}", flush=True)
+        L, H, D, T, pool = 4, 8, 128, 16, 40
+        wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 11)
+        ids = inputs.random_page_ids(pool, 32, seed=3)
+        inj, ctl, kind = inputs.inject_specials(wl.k, wl.v, ids, frac=0.1, seed=4, controls=16)
+        fixed = _fixed_scales(L) if "FP8_FIXED" in (ck, cv) else None
+        ora_st, gdesc = _roundtrip_case(ctx, wl, ck, cv, 5, ids, fixed=fixed,
+                                        dst_ids=inputs.permutation(pool, 1)[:32])
+        seglist = G.segments_of(L, 32)
+        for s, (l, i, c) in enumerate(seglist):
+            codec = ck if c == 0 else cv
+            fp8 = codec.startswith("FP8")
+            k = kind.get((l, i, c))
+            expect_raw = k is not None and (fp8 or k in ("nan", "+inf", "-inf"))
+            assert (gdesc[s]["status"] == kvc.KVC_SEG_RAW_DATA) == expect_raw, (s, codec, k)
+
+
+def test_spill_capacity_exhausted(ctx):
+    """A spill region for only two raw segments: later raw segments report
+    KVC_SEG_CAPACITY; their destination pages are left untouched and the
+    decode status says so; every other segment decodes."""
+    print("[case] spill capacity", flush=True)
+    L, H, D, T, pool = 2, 8, 128, 16, 16
+    wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 12)
+    ids = np.arange(pool, dtype=np.int32)
+    inj = inputs.inject_specials(wl.k, wl.v, ids, frac=0.2, seed=6, controls=0)
+    codec = kvc.Codec(kvc.KVC_INT8, kvc.KVC_INT8, seed=0)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids, spill_bytes=2 * (32768 + 0))
+    torch.cuda.synchronize()
+    d = G.desc_np(desc)
+    st = d["status"]
+    _, _, kinds = inj
+    n_inj = len([1 for k in kinds.values() if k in ("nan", "+inf", "-inf")])
+    assert n_inj > 2
+    assert (st == kvc.KVC_SEG_RAW_DATA).sum() == 2
+    assert (st == kvc.KVC_SEG_CAPACITY).sum() == n_inj - 2
+    dst = wl.empty_like(fill_bits=0x1234)
+    dec = G.gpu_decode(ctx, dst, codec, out, total, ids)
+    torch.cuda.synchronize()
+    decn = dec.cpu().numpy()
+    seglist = G.segments_of(L, pool)
+    for s, (l, i, c) in enumerate(seglist):
+        got = G.gpu_segment_vectors(dst, l, c, int(ids[i]))
+        if st[s] == kvc.KVC_SEG_CAPACITY:
+            assert decn[s] == 1 and np.all(got == 0x1234)
+        else:
+            assert decn[s] == 0 and not np.all(got == 0x1234)
+
+
+def test_stream_ordered_and_untouched_pages(ctx):
+    """Encode then decode on a side stream with no host sync in between;
+    pages not named in the decode stay bit-identical."""
+    print("[case] stream order", flush=True)
+    L, H, D, T, pool = 3, 8, 128, 16, 20
+    wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 13)
+    ids = inputs.random_page_ids(pool, 8, seed=8)
+    codec = kvc.Codec(kvc.KVC_TQ4, kvc.KVC_UNIFORM4, seed=42)
+    s = torch.cuda.Stream()
+    dst = wl.empty_like(fill_bits=0x4321)
+    with torch.cuda.stream(s):
+        out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids, stream=s.cuda_stream)
+        st = G.gpu_decode(ctx, dst, codec, out, total, ids[::-1].copy(), stream=s.cuda_stream)
+    s.synchronize()
+    assert np.all(st.cpu().numpy() == 0)
+    untouched = sorted(set(range(pool)) - set(int(x) for x in ids))
+    for l in range(L):
+        for c, tl in ((0, dst.k), (1, dst.v)):
+            for b in untouched:
+                assert np.all(G.u16(tl[l][b]) == 0x4321)
+
+
+# ----------------------------------------------------------------- workload-sized
+def _sample_segments(L, n_pages, count, seed, layers=None):
+    rng = np.random.default_rng(seed)
+    nseg = L * n_pages * 2
+    segs = set(int(x) for x in rng.choice(nseg, size=count, replace=False))
+    if layers:
+        for l in layers:                                   # make sure policy-raw layers are covered
+            segs.add((l * n_pages + int(rng.integers(n_pages))) * 2)
+    return sorted(segs)
+
+
+def test_tq4_u4_llama3_full_size(ctx):
+    """TurboQuant-4 K + uniform-4 V, 32 layers x 8 heads x D128 BF16, 4096 of
+    8192 blocks in random order, protected layers 0, 1, 30, 31: one full-size
+    launch each way (as timed by the benchmark), 96 sampled segments checked."""
+    cfg = inputs.CONFIGS["tq4_u4_llama3"]
+    print("[case] tq4_u4_llama3 full size", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
+    ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
+    segs = _sample_segments(cfg["layers"], cfg["pages"], 96, 1, layers=[0, 31])
+    _roundtrip_case(ctx, wl, "TQ4", "UNIFORM4", 0, ids, protected=list(cfg["protected"]), segments=segs,
+                    decode_from_oracle=False)
+
+
+@pytest.mark.parametrize("dim", [32, 64, 256])
+def test_tq3_u3_dsweep_full_size(ctx, dim):
+    """TurboQuant-3 K (outlier channels) + uniform-3 V, 28 layers x 4 heads,
+    2048 pages: full-size launch, sampled segments, 3-bit sizes."""
+    cfg = inputs.CONFIGS["tq3_u3_dsweep"]
+    print(f"[case] tq3_u3 D={dim} full size", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], dim, cfg["tokens"], cfg["pool"], "bf16", "separate", 0,
+                    k_kind="outliers")
+    ids = np.arange(cfg["pages"], dtype=np.int32)
+    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, dim)
+    ora_st, gdesc = _roundtrip_case(ctx, wl, "TQ3", "UNIFORM3", 0, ids, segments=segs, decode_from_oracle=False)
+    n_vec = cfg["heads"] * cfg["tokens"]
+    assert set(gdesc["stored_len"][0::2]) == {n_vec * (3 * dim // 8 + 2)}
+    assert set(gdesc["stored_len"][1::2]) == {n_vec * (3 * dim // 8 + 4)}
+
+
+@pytest.mark.parametrize("vcodec", ["FP8_FIXED", "FP8_DYNAMIC"])
+def test_k16v8_packed_full_size(ctx, vcodec):
+    """vLLM packed FP16 [2048 blocks, 8 heads, 16 tokens, 256], 36 layers,
+    K raw, V FP8 with a fixed per-layer scale (calibrated on sequence 0's V)
+    or per-vector scales: full-size launch, sampled segments."""
+    cfg = inputs.CONFIGS["k16v8_packed"]
+    print(f"[case] k16v8 packed {vcodec}", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "fp16", "packed", 0)
+    fixed = None
+    if vcodec == "FP8_FIXED":
+        amax = np.array([float(t[:512, :, :, cfg["dim"]:].abs().max()) for t in wl.k])
+        fixed = np.stack([np.ones(cfg["layers"]), amax / 448.0], 1).astype(np.float32)
+    ids = np.arange(cfg["pages"], dtype=np.int32)
+    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 3)
+    _roundtrip_case(ctx, wl, "RAW", vcodec, 0, ids, fixed=fixed, segments=segs, decode_from_oracle=False)
+
+
+@pytest.mark.parametrize("codec", ["INT8", "FP8_DYNAMIC", "FP8_DIRECT"])
+def test_int8_fp8_stress_full_size(ctx, codec):
+    """32 layers x 8 heads x D128 BF16, 8192 pages (128K tokens), 1% of the
+    524,288 segments injected with NaN/Inf/+-450/+-1000 (plus +-448
+    controls), decoded into a shuffled destination pool: exact raw set over
+    all segments; sampled parity; every raw segment round-trips bit-exactly."""
+    cfg = inputs.CONFIGS["int8_fp8_stress"]
+    print(f"[case] stress {codec}", flush=True)
+    L, n = cfg["layers"], cfg["pages"]
+    wl = G.Workload(L, cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
+    ids = np.arange(n, dtype=np.int32)
+    inj, ctl, kind = inputs.inject_specials(wl.k, wl.v, ids, frac=cfg["inject"], seed=0)
+    kc = vc = kvc.CODECS[codec]
+    c = kvc.Codec(kc, vc, seed=0)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, c, ids)
+    torch.cuda.synchronize()
+    d = G.desc_np(desc)
+    fp8 = codec.startswith("FP8")
+    expect = np.zeros(L * n * 2, bool)
+    for (l, i, cc), k in kind.items():
+        if fp8 or k in ("nan", "+inf", "-inf"):
+            expect[(l * n + i) * 2 + cc] = True
+    assert np.array_equal(d["status"] == kvc.KVC_SEG_RAW_DATA, expect)
+    assert not np.any(d["status"] == kvc.KVC_SEG_CAPACITY)
+    # decode into a shuffled destination pool
+    perm = inputs.permutation(n, 0)
+    dst = wl.empty_like(fill_bits=0x7FC1)
+    st = G.gpu_decode(ctx, dst, c, out, total, perm)
+    torch.cuda.synchronize()
+    assert np.all(st.cpu().numpy() == 0)
+    raw_segs = np.nonzero(expect)[0]
+    rng = np.random.default_rng(5)
+    seglist = G.segments_of(L, n)
+    for s in rng.choice(raw_segs, size=min(200, raw_segs.size), replace=False):
+        l, i, cc = seglist[int(s)]
+        src = G.gpu_segment_vectors(wl, l, cc, int(ids[i]))
+        got = G.gpu_segment_vectors(dst, l, cc, int(perm[i]))
+        assert np.array_equal(src, got)
+    # sampled parity against the oracle (encode bytes + decode values)
+    segs = _sample_segments(L, n, 48, 9) + [int(x) for x in raw_segs[:16]]
+    segs = sorted(set(segs))
+    ora_buf, ora_st, offs, ora_total = G.oracle_encode(wl, kc, vc, 0, ids, segments=segs)
+    bad = G.compare_encoded(out.cpu().numpy(), d, ora_buf, ora_st, offs, ora_total, segs)
+    assert not bad, bad[:5]
+    ora_dec = G.oracle_decode_segments(ora_buf, wl, kc, vc, 0, n, None, segs)
+    for s in segs:
+        l, i, cc = seglist[s]
+        got = G.gpu_segment_vectors(dst, l, cc, int(perm[i]))
+        assert np.array_equal(got, ora_dec[s]), s
