@@ -52,14 +52,14 @@ def _check_decoded(dec_gpu: np.ndarray, dec_ora: np.ndarray, dt, lossy_tq: bool,
 
 
 def _roundtrip_case(ctx, wl, ck, cv, seed, page_ids, protected=None, fixed=None, segments=None,
-                    dst_ids=None, decode_from_oracle=True):
+                    dst_ids=None, decode_from_oracle=True, spill_bytes=None):
     """Encode on GPU and oracle; compare.  Decode (a) the oracle's buffer on
     the GPU and (b) the GPU's buffer on the GPU; compare both with the
     oracle's decode of its own buffer."""
     n_pages = len(page_ids)
     kc, vc = _codec_ids(ck, cv)
     codec = kvc.Codec(kc, vc, seed=seed, fixed_scales=fixed, protected_layers=protected, layers=wl.L)
-    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, page_ids)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, page_ids, spill_bytes=spill_bytes)
     torch.cuda.synchronize()
     nseg = wl.L * n_pages * 2
     segs = list(range(nseg)) if segments is None else segments
@@ -177,8 +177,10 @@ def test_gate_small(ctx):
         ids = inputs.random_page_ids(pool, 32, seed=3)
         inj, ctl, kind = inputs.inject_specials(wl.k, wl.v, ids, frac=0.1, seed=4, controls=16)
         fixed = _fixed_scales(L) if "FP8_FIXED" in (ck, cv) else None
+        # spill region large enough for every segment: no KVC_SEG_CAPACITY here
         ora_st, gdesc = _roundtrip_case(ctx, wl, ck, cv, 5, ids, fixed=fixed,
-                                        dst_ids=inputs.permutation(pool, 1)[:32])
+                                        dst_ids=inputs.permutation(pool, 1)[:32],
+                                        spill_bytes=L * 32 * 2 * (H * T * D * 2))
         seglist = G.segments_of(L, 32)
         for s, (l, i, c) in enumerate(seglist):
             codec = ck if c == 0 else cv
