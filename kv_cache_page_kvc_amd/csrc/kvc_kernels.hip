@@ -118,6 +118,13 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 template <int LOGP>
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+  if constexpr (LOGP >= 1) v |= xlane_u<0>(v);
+  if constexpr (LOGP >= 2) v |= xlane_u<1>(v);
+  if constexpr (LOGP >= 3) v |= xlane_u<2>(v);
+  return v;
+}
+template <int LOGP>
 __device__ __forceinline__ uint32_t group_umax(uint32_t v) {
   if constexpr (LOGP >= 1) v = max(v, xlane_u<0>(v));
   if constexpr (LOGP >= 2) v = max(v, xlane_u<1>(v));
@@ -223,34 +230,157 @@ template <int C> struct CodecInfo {
   static constexpr bool fp8 = C == C_FP8D || C == C_FP8F || C == C_FP8Y;
 };
 
-// store the codes of one chunk (8 elements) of vector v
-template <int D, int BITS>
-__device__ __forceinline__ void store_codes(uint8_t* code_blk, int k, int p, uint64_t c64) {
-  constexpr int P = Geo<D>::P;
-  const int e0 = k * 8 * P + 8 * p;                 // first element of the chunk
-  if constexpr (BITS == 8) {
-    uint2 w;
-    w.x = (uint32_t)c64;
-    w.y = (uint32_t)(c64 >> 32);
-    *reinterpret_cast<uint2*>(code_blk + e0) = w;
-  } else if constexpr (BITS == 4) {
-    *reinterpret_cast<uint32_t*>(code_blk + e0 / 2) = (uint32_t)c64;
-  } else {                                          // 3 bits: 24-bit piece at byte 3*e0/8
-    uint8_t* q = code_blk + (3 * e0) / 8;
-    q[0] = (uint8_t)c64;
-    q[1] = (uint8_t)(c64 >> 8);
-    q[2] = (uint8_t)(c64 >> 16);
+// Per-lane sign masks for TurboQuant: flip[4k+m] is the XOR mask of the
+// lane's m-th packed 16-bit pair of chunk k -- bit 15 for its element 2m,
+// bit 31 for element 2m+1 (the sign-bit positions of BF16 and FP16 pairs).
+template <int D>
+struct LaneSigns {
+  uint32_t flip[Geo<D>::NCH * 4];
+};
+
+// sigma_i for the lane's elements, read from the D-bit mask (bit i set:
+// sigma_i = -1).  With `parity`, every element of a lane whose position in
+// its group has odd bit parity is flipped once more: the cross-lane
+// butterflies then reduce to own + partner in both lanes (see wht_cross).
+template <int D>
+__device__ __forceinline__ void make_lane_signs(const uint32_t* mask, int p, bool parity, LaneSigns<D>& ls) {
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH;
+  const uint32_t par = (parity && (__builtin_popcount(p) & 1)) ? 0x80008000u : 0u;
+#pragma unroll
+  for (int k = 0; k < NCH; k++) {
+    const int e0 = k * 8 * P + 8 * p;            // multiple of 8: one byte of the mask
+    const uint32_t byte = (mask[e0 >> 5] >> (e0 & 31)) & 0xFFu;
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+      ls.flip[4 * k + m] = ((((byte >> (2 * m)) & 1u) << 15) | (((byte >> (2 * m + 1)) & 1u) << 31)) ^ par;
   }
 }
 
+// Cross-lane WHT stages.  Stage q pairs lanes whose group position differs
+// in bit q; the lower lane needs RN(a+b), the upper RN(a-b).  Every value
+// enters with the lane's sign (-1)^parity(position) already applied, so a
+// lower lane holds pi*a and sees -pi*b, an upper lane holds -pi*b and sees
+// pi*a.  Both then compute one FMA with a +-1 multiplier, own + c*partner
+// (c = -1 in the lower lane, +1 in the upper): pi*RN(a+b) and pi*RN(a-b),
+// a single rounding because c*partner is exact.  Each stage removes one
+// parity bit from the sign, so after the last stage every sign is +1.
+template <int LOGP, int E>
+__device__ __forceinline__ void wht_cross(float* y) {
+  if constexpr (LOGP >= 1) {
+    const float c = upper_lane<0>() ? 1.0f : -1.0f;
+#pragma unroll
+    for (int e = 0; e < E; e++) y[e] = fmaf(xlane<0>(y[e]), c, y[e]);
+  }
+  if constexpr (LOGP >= 2) {
+    const float c = upper_lane<1>() ? 1.0f : -1.0f;
+#pragma unroll
+    for (int e = 0; e < E; e++) y[e] = fmaf(xlane<1>(y[e]), c, y[e]);
+  }
+  if constexpr (LOGP >= 3) {
+    const float c = upper_lane<2>() ? 1.0f : -1.0f;
+#pragma unroll
+    for (int e = 0; e < E; e++) y[e] = fmaf(xlane<2>(y[e]), c, y[e]);
+  }
+}
+
+// in-lane WHT stages over element bits 0..2 (within each chunk)
+template <int NCH>
+__device__ __forceinline__ void wht_inlane_low(float* y) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int k = 0; k < NCH; k++)
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (!(j & h)) {
+          const float a = y[8 * k + j], b = y[8 * k + j + h];
+          y[8 * k + j] = a + b;
+          y[8 * k + j + h] = a - b;
+        }
+}
+// in-lane WHT stages over the chunk bits (element bits above the group bits)
+template <int NCH>
+__device__ __forceinline__ void wht_inlane_high(float* y) {
+#pragma unroll
+  for (int kh = 1; kh < NCH; kh <<= 1)
+#pragma unroll
+    for (int k = 0; k < NCH; k++)
+      if (!(k & kh))
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const float a = y[8 * k + j], b = y[8 * (k + kh) + j];
+          y[8 * k + j] = a + b;
+          y[8 * (k + kh) + j] = a - b;
+        }
+}
+
+// pairwise sum of squares in element-index order: in-lane over bits 0..2,
+// cross-lane over the group bits, then in-lane over the chunk bits
+template <int NCH, int LOGP>
+__device__ __forceinline__ float sumsq_tree(const float* y) {
+  float part[NCH];
+#pragma unroll
+  for (int k = 0; k < NCH; k++) {
+    float s[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) s[j] = y[8 * k + j] * y[8 * k + j];
+#pragma unroll
+    for (int wdt = 8; wdt > 1; wdt >>= 1)
+#pragma unroll
+      for (int j = 0; j < wdt / 2; j++) s[j] = s[2 * j] + s[2 * j + 1];
+    part[k] = group_sum<LOGP>(s[0]);
+  }
+#pragma unroll
+  for (int wdt = NCH; wdt > 1; wdt >>= 1)
+#pragma unroll
+    for (int k = 0; k < wdt / 2; k++) part[k] = part[2 * k] + part[2 * k + 1];
+  return part[0];
+}
+
+// store the codes of one chunk (8 elements) of a vector's code block
+template <int D, int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* cv, int k, int p, uint32_t lo, uint32_t hi) {
+  constexpr int P = Geo<D>::P;
+  const int e0 = k * 8 * P + 8 * p;                 // first element of the chunk
+  if constexpr (BITS == 8) {
+    *reinterpret_cast<uint2*>(cv + e0) = make_uint2(lo, hi);
+  } else if constexpr (BITS == 4) {
+    *reinterpret_cast<uint32_t*>(cv + e0 / 2) = lo;
+  } else {                                          // 3 bits: 24-bit piece at byte 3*e0/8
+    uint8_t* q = cv + (3 * e0) / 8;                 // any byte alignment
+    q[0] = (uint8_t)lo;
+    q[1] = (uint8_t)(lo >> 8);
+    q[2] = (uint8_t)(lo >> 16);
+  }
+}
+
+// sum over j of (MAGIC << BITS*j), modulo 2^32: the uniform codes are
+// accumulated as raw FMA result bits MAGIC + code and corrected once
+template <int BITS>
+__device__ __forceinline__ constexpr uint32_t magic_sum() {
+  uint32_t s = 0;
+  for (int j = 0; j < 8; j++) s += 0x4B400000u << (BITS * j);
+  return s;
+}
+
 template <int D, int DT, int C>
-__device__ __forceinline__ int encode_vector(const uint4* w, int v, const Lane& ln, uint8_t* code_blk,
-                                             uint8_t* meta_blk, float fixed, uint32_t sign_bits,
+__device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, uint8_t* code_blk,
+                                             uint8_t* meta_blk, float fixed, const LaneSigns<D>& ls,
                                              const CellEntry* cells) {
   constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP;
   constexpr int BITS = CodecInfo<C>::bits;
   constexpr int CB = BITS * D / 8;
   uint8_t* cv = code_blk + (size_t)v * CB;
+  if constexpr (CodecInfo<C>::tq) {
+    // sigma (and the lane parity sign) applied to the packed source words
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      w[k].x ^= ls.flip[4 * k];
+      w[k].y ^= ls.flip[4 * k + 1];
+      w[k].z ^= ls.flip[4 * k + 2];
+      w[k].w ^= ls.flip[4 * k + 3];
+    }
+  }
   float x[E];
 #pragma unroll
   for (int k = 0; k < NCH; k++) unpack8<DT>(w[k], x + 8 * k);
@@ -271,7 +401,7 @@ __device__ __forceinline__ int encode_vector(const uint4* w, int v, const Lane& 
     if constexpr (C == C_INT8) s = fmaxf(bits_to_f32<DT>(am), 1e-12f) / 127.0f;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      uint64_t c64;
+      uint32_t lo, hi;
       if constexpr (C == C_INT8) {
         uint32_t b[8];
 #pragma unroll
@@ -280,9 +410,8 @@ __device__ __forceinline__ int encode_vector(const uint4* w, int v, const Lane& 
           q = fminf(fmaxf(q, -127.0f), 127.0f);
           b[j] = (uint32_t)(int)q & 0xFFu;
         }
-        const uint32_t lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-        const uint32_t hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-        c64 = (uint64_t)lo | ((uint64_t)hi << 32);
+        lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+        hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
       } else {
         float q[8];
 #pragma unroll
@@ -295,9 +424,10 @@ __device__ __forceinline__ int encode_vector(const uint4* w, int v, const Lane& 
           q[j] = t;
         }
         const uint2 r = fp8x8(q);
-        c64 = (uint64_t)r.x | ((uint64_t)r.y << 32);
+        lo = r.x;
+        hi = r.y;
       }
-      store_codes<D, 8>(cv, k, ln.p, c64);
+      store_codes<D, 8>(cv, k, ln.p, lo, hi);
     }
     if constexpr (C == C_FP8Y || C == C_INT8)
       if (ln.p == 0) *reinterpret_cast<float*>(meta_blk + (size_t)v * 4) = s;
@@ -305,146 +435,78 @@ __device__ __forceinline__ int encode_vector(const uint4* w, int v, const Lane& 
 
   if constexpr (CodecInfo<C>::uni) {
     constexpr int TOP = (1 << BITS) - 1;
-    uint32_t am = 0;
     float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int k = 0; k < NCH; k++) am = max(am, absmax_bits(w[k]));
 #pragma unroll
     for (int e = 1; e < E; e++) {
       mn = fminf(mn, x[e]);
       mx = fmaxf(mx, x[e]);
     }
-    am = group_umax<LOGP>(am);
     mn = group_min<LOGP>(mn);
     mx = group_max<LOGP>(mx);
     const float sig = (mx - mn) / (float)TOP;
     const float mh = f16_round(mn), sh = f16_round(sig);
-    bad = (am >= Lim<DT>::nonfinite) || !__builtin_isfinite(mh) || !__builtin_isfinite(sh);
+    // +-Inf reach mn/mx and overflow the FP16 metadata; NaN is caught below
+    bad = !__builtin_isfinite(mh) || !__builtin_isfinite(sh);
     const float y = sh == 0.0f ? 0.0f : 1.0f / sh;
     constexpr int MAGIC = 0x4B400000;   // bits of 1.5 * 2^23
+    uint32_t tor = 0;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      uint64_t c64 = 0;
+      uint32_t acc = 0;
 #pragma unroll
       for (int j = 0; j < 8; j++) {
-        const float d = x[8 * k + j] - mh;
-        // RN(d*y + 1.5*2^23) = 1.5*2^23 + RNE(d*y) when |d*y| < 2^22; the
-        // integer clamp also maps every out-of-range case to 0 or TOP.
-        const int t = __float_as_int(fmaf(d, y, 12582912.0f));
-        const int q = min(max(t, MAGIC), MAGIC + TOP) - MAGIC;
-        c64 |= (uint64_t)q << (BITS * j);
+        // RN(d*y + 1.5*2^23) = 1.5*2^23 + RNE(d*y) while |d*y| < 2^22; the
+        // integer clamp maps every out-of-range result to 0 or TOP
+        const int t = __float_as_int(fmaf(x[8 * k + j] - mh, y, 12582912.0f));
+        tor |= (uint32_t)t;
+        acc += (uint32_t)min(max(t, MAGIC), MAGIC + TOP) << (BITS * j);
       }
-      store_codes<D, BITS>(cv, k, ln.p, c64);
+      store_codes<D, BITS>(cv, k, ln.p, acc - magic_sum<BITS>(), 0);
     }
+    // For finite inputs every t lies in (2^22, 2^41) in magnitude (|d*y| is
+    // bounded by the FP16 range of d and by y <= 2^24), so bit 29 (exponent
+    // bit 6) of t is clear; a NaN source value makes t NaN, which sets it.
+    bad |= (int)((group_or<LOGP>(tor) >> 29) & 1u);
     if (ln.p == 0)
       *reinterpret_cast<uint32_t*>(meta_blk + (size_t)v * 4) = f16_bits(mh) | (f16_bits(sh) << 16);
   }
 
   if constexpr (CodecInfo<C>::tq) {
-    // 1. sum of squares: in-lane tree over j, cross-lane over group bits,
-    //    then the chunk tree -- the pairwise order of the element index.
-    float part[NCH];
-#pragma unroll
-    for (int k = 0; k < NCH; k++) {
-      float s[8];
-#pragma unroll
-      for (int j = 0; j < 8; j++) s[j] = x[8 * k + j] * x[8 * k + j];
-#pragma unroll
-      for (int wdt = 8; wdt > 1; wdt >>= 1)
-#pragma unroll
-        for (int j = 0; j < wdt / 2; j++) s[j] = s[2 * j] + s[2 * j + 1];
-      part[k] = group_sum<LOGP>(s[0]);
-    }
-#pragma unroll
-    for (int wdt = NCH; wdt > 1; wdt >>= 1)
-#pragma unroll
-      for (int k = 0; k < wdt / 2; k++) part[k] = part[2 * k] + part[2 * k + 1];
-    const float n = sqrtf(part[0]);
+    // 1. norm (signs do not change the squares)
+    const float n = sqrtf(sumsq_tree<NCH, LOGP>(x));
     const float nh = f16_round(n);
     bad = !__builtin_isfinite(nh);
     const float r = (n == 0.0f || bad) ? 0.0f : 1.0f / n;
-    // 2.-3. normalise, then the sign flip (exact)
+    // 2.-3. normalise the signed values
     float y[E];
 #pragma unroll
-    for (int e = 0; e < E; e++) {
-      const float u = x[e] * r;
-      y[e] = __uint_as_float(__float_as_uint(u) ^ (((sign_bits >> e) & 1u) << 31));
-    }
+    for (int e = 0; e < E; e++) y[e] = x[e] * r;
     // 4. WHT, stages in ascending span
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-      for (int k = 0; k < NCH; k++)
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-          if (!(j & h)) {
-            const float a = y[8 * k + j], b = y[8 * k + j + h];
-            y[8 * k + j] = a + b;
-            y[8 * k + j + h] = a - b;
-          }
-    // cross-lane: lower lane a + b, upper lane a - b = partner - own
-    if constexpr (LOGP >= 1) {
-      const float sg = upper_lane<0>() ? -1.0f : 1.0f;
-#pragma unroll
-      for (int e = 0; e < E; e++) y[e] = xlane<0>(y[e]) + y[e] * sg;
-    }
-    if constexpr (LOGP >= 2) {
-      const float sg = upper_lane<1>() ? -1.0f : 1.0f;
-#pragma unroll
-      for (int e = 0; e < E; e++) y[e] = xlane<1>(y[e]) + y[e] * sg;
-    }
-    if constexpr (LOGP >= 3) {
-      const float sg = upper_lane<2>() ? -1.0f : 1.0f;
-#pragma unroll
-      for (int e = 0; e < E; e++) y[e] = xlane<2>(y[e]) + y[e] * sg;
-    }
-#pragma unroll
-    for (int kh = 1; kh < NCH; kh <<= 1)
-#pragma unroll
-      for (int k = 0; k < NCH; k++)
-        if (!(k & kh))
-#pragma unroll
-          for (int j = 0; j < 8; j++) {
-            const float a = y[8 * k + j], b = y[8 * (k + kh) + j];
-            y[8 * k + j] = a + b;
-            y[8 * (k + kh) + j] = a - b;
-          }
+    wht_inlane_low<NCH>(y);
+    wht_cross<LOGP, E>(y);
+    wht_inlane_high<NCH>(y);
     // 5. bucketize: code = #{B_k < z} = base(cell) + (z > T(cell))
     constexpr int LO = 0x4B400000 - kCellOffset, HI = 0x4B400000 + kCellOffset;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      uint64_t c64 = 0;
+      uint32_t acc = 0;
 #pragma unroll
       for (int j = 0; j < 8; j++) {
         const float z = y[8 * k + j];
         const int t = __float_as_int(fmaf(z, kCellScale, 12582912.0f));
         const int idx = min(max(t, LO), HI) - LO;
         const CellEntry ce = cells[idx];
-        const uint32_t q = ce.base + (z > ce.thr ? 1u : 0u);
-        c64 |= (uint64_t)q << (BITS * j);
+        acc += (ce.base + (z > ce.thr ? 1u : 0u)) << (BITS * j);
       }
-      store_codes<D, BITS>(cv, k, ln.p, c64);
+      store_codes<D, BITS>(cv, k, ln.p, acc, 0);
     }
     if (ln.p == 0) *reinterpret_cast<uint16_t*>(meta_blk + (size_t)v * 2) = (uint16_t)f16_bits(nh);
   }
   return bad;
 }
 
-// lane's TurboQuant sign bits: bit e of the result = sign of its element e
-template <int D>
-__device__ __forceinline__ uint32_t lane_signs(const uint32_t* mask, int p) {
-  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH;
-  uint32_t r = 0;
-#pragma unroll
-  for (int k = 0; k < NCH; k++) {
-    const int e0 = k * 8 * P + 8 * p;            // multiple of 8: one byte of the mask
-    r |= ((mask[e0 >> 5] >> (e0 & 31)) & 0xFFu) << (8 * k);
-  }
-  return r;
-}
-
 template <int D, int DT, int C>
-__device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, uint32_t sign_bits,
+__device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, const LaneSigns<D>& ls,
                                       const CellEntry* cells) {
   constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
   constexpr int CB = CodecInfo<C>::bits * D / 8;
@@ -466,7 +528,7 @@ __device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fix
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int v = v0 + u * GW;
-      if (v < s.n_vec) bad |= encode_vector<D, DT, C>(w[u], v, ln, code_blk, meta_blk, fixed, sign_bits, cells);
+      if (v < s.n_vec) bad |= encode_vector<D, DT, C>(w[u], v, ln, code_blk, meta_blk, fixed, ls, cells);
     }
   }
   return bad;
@@ -572,19 +634,20 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
     for (int q = threadIdx.x; q < kCells; q += kThreads) s_cells[q] = src[q];
     __syncthreads();
   }
-  const uint32_t sign_bits = tq ? lane_signs<D>(p.sign_mask, ln.p) : 0u;
+  LaneSigns<D> ls;
+  if (tq) make_lane_signs<D>(p.sign_mask, ln.p, true, ls);
   const float fixed = E.fixed;
 
   int bad = 0;
   switch (codec) {
-    case C_FP8D: bad = encode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, sign_bits, s_cells); break;
-    case C_FP8F: bad = encode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, sign_bits, s_cells); break;
-    case C_FP8Y: bad = encode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, sign_bits, s_cells); break;
-    case C_INT8: bad = encode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, sign_bits, s_cells); break;
-    case C_U3: bad = encode_segment_vectors<D, DT, C_U3>(s, ln, fixed, sign_bits, s_cells); break;
-    case C_U4: bad = encode_segment_vectors<D, DT, C_U4>(s, ln, fixed, sign_bits, s_cells); break;
-    case C_TQ3: bad = encode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, sign_bits, s_cells); break;
-    case C_TQ4: bad = encode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, sign_bits, s_cells); break;
+    case C_FP8D: bad = encode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, ls, s_cells); break;
+    case C_FP8F: bad = encode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, ls, s_cells); break;
+    case C_FP8Y: bad = encode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, ls, s_cells); break;
+    case C_INT8: bad = encode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, ls, s_cells); break;
+    case C_U3: bad = encode_segment_vectors<D, DT, C_U3>(s, ln, fixed, ls, s_cells); break;
+    case C_U4: bad = encode_segment_vectors<D, DT, C_U4>(s, ln, fixed, ls, s_cells); break;
+    case C_TQ3: bad = encode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, ls, s_cells); break;
+    case C_TQ4: bad = encode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, ls, s_cells); break;
     default: break;
   }
   const int any_bad = __syncthreads_or(bad);
@@ -624,24 +687,27 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
 }
 
 // ------------------------------------------------------------------ decoders
+// the codes of one chunk (8 elements) of a vector's code block
 template <int D, int BITS>
-__device__ __forceinline__ uint64_t load_codes(const uint8_t* code_blk, int k, int p) {
+__device__ __forceinline__ uint2 load_codes(const uint8_t* cv, int k, int p) {
   constexpr int P = Geo<D>::P;
   const int e0 = k * 8 * P + 8 * p;
   if constexpr (BITS == 8) {
-    const uint2 w = *reinterpret_cast<const uint2*>(code_blk + e0);
-    return (uint64_t)w.x | ((uint64_t)w.y << 32);
+    return *reinterpret_cast<const uint2*>(cv + e0);
   } else if constexpr (BITS == 4) {
-    return *reinterpret_cast<const uint32_t*>(code_blk + e0 / 2);
+    return make_uint2(*reinterpret_cast<const uint32_t*>(cv + e0 / 2), 0u);
   } else {
-    const uint8_t* q = code_blk + (3 * e0) / 8;
-    return (uint64_t)q[0] | ((uint64_t)q[1] << 8) | ((uint64_t)q[2] << 16);
+    const uint8_t* q = cv + (3 * e0) / 8;
+    return make_uint2((uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16), 0u);
   }
 }
 
+// byte m of a word, as a float (v_cvt_f32_ubyte*)
+__device__ __forceinline__ float ubyte_f32(uint32_t w, int m) { return (float)((w >> (8 * m)) & 0xFFu); }
+
 template <int D, int DT, int C>
 __device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uint8_t* meta_blk, int v,
-                                              const Lane& ln, uint16_t* dst, float fixed, uint32_t sign_bits,
+                                              const Lane& ln, uint16_t* dst, float fixed, const LaneSigns<D>& ls,
                                               const float* cent) {
   constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP, P = Geo<D>::P;
   constexpr int BITS = CodecInfo<C>::bits;
@@ -654,11 +720,10 @@ __device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uin
     if constexpr (C == C_FP8Y || C == C_INT8) s = *reinterpret_cast<const float*>(meta_blk + (size_t)v * 4);
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      const uint64_t c64 = load_codes<D, 8>(cv, k, ln.p);
-      const uint32_t lo = (uint32_t)c64, hi = (uint32_t)(c64 >> 32);
+      const uint2 c = load_codes<D, 8>(cv, k, ln.p);
 #pragma unroll
       for (int j = 0; j < 8; j++) {
-        const uint32_t word = j < 4 ? lo : hi;
+        const uint32_t word = j < 4 ? c.x : c.y;
         float val;
         if constexpr (C == C_INT8) {
           val = (float)(int8_t)(word >> (8 * (j & 3)));
@@ -681,98 +746,64 @@ __device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uin
     const float sh = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      const uint64_t c64 = load_codes<D, BITS>(cv, k, ln.p);
+      const uint32_t w = load_codes<D, BITS>(cv, k, ln.p).x;
+      float code[8];
+      if constexpr (BITS == 4) {
+        const uint32_t even = w & 0x0F0F0F0Fu, odd = (w >> 4) & 0x0F0F0F0Fu;   // nibbles to bytes
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const float code = (float)(uint32_t)((c64 >> (BITS * j)) & ((1u << BITS) - 1));
-        y[8 * k + j] = fmaf(code, sh, mh);    // code*sh is exact: one rounding either way
+        for (int m = 0; m < 4; m++) {
+          code[2 * m] = ubyte_f32(even, m);
+          code[2 * m + 1] = ubyte_f32(odd, m);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) code[j] = (float)((w >> (BITS * j)) & ((1u << BITS) - 1));
       }
+#pragma unroll
+      for (int j = 0; j < 8; j++) y[8 * k + j] = fmaf(code[j], sh, mh);   // code*sh is exact
     }
   }
   if constexpr (CodecInfo<C>::tq) {
+    // centroids, negated in lanes of odd group parity (cent + 16 holds -C)
+    const int base = (__builtin_popcount(ln.p) & 1) ? 16 : 0;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      const uint64_t c64 = load_codes<D, BITS>(cv, k, ln.p);
+      const uint32_t w = load_codes<D, BITS>(cv, k, ln.p).x;
 #pragma unroll
-      for (int j = 0; j < 8; j++) y[8 * k + j] = cent[(uint32_t)(c64 >> (BITS * j)) & ((1u << BITS) - 1)];
+      for (int j = 0; j < 8; j++) y[8 * k + j] = cent[base + ((w >> (BITS * j)) & ((1u << BITS) - 1))];
     }
-    float part[NCH];
-#pragma unroll
-    for (int k = 0; k < NCH; k++) {
-      float s[8];
-#pragma unroll
-      for (int j = 0; j < 8; j++) s[j] = y[8 * k + j] * y[8 * k + j];
-#pragma unroll
-      for (int wdt = 8; wdt > 1; wdt >>= 1)
-#pragma unroll
-        for (int j = 0; j < wdt / 2; j++) s[j] = s[2 * j] + s[2 * j + 1];
-      part[k] = group_sum<LOGP>(s[0]);
-    }
-#pragma unroll
-    for (int wdt = NCH; wdt > 1; wdt >>= 1)
-#pragma unroll
-      for (int k = 0; k < wdt / 2; k++) part[k] = part[2 * k] + part[2 * k + 1];
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-      for (int k = 0; k < NCH; k++)
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-          if (!(j & h)) {
-            const float a = y[8 * k + j], b = y[8 * k + j + h];
-            y[8 * k + j] = a + b;
-            y[8 * k + j + h] = a - b;
-          }
-    if constexpr (LOGP >= 1) {
-      const float sg = upper_lane<0>() ? -1.0f : 1.0f;
-#pragma unroll
-      for (int e = 0; e < E; e++) y[e] = xlane<0>(y[e]) + y[e] * sg;
-    }
-    if constexpr (LOGP >= 2) {
-      const float sg = upper_lane<1>() ? -1.0f : 1.0f;
-#pragma unroll
-      for (int e = 0; e < E; e++) y[e] = xlane<1>(y[e]) + y[e] * sg;
-    }
-    if constexpr (LOGP >= 3) {
-      const float sg = upper_lane<2>() ? -1.0f : 1.0f;
-#pragma unroll
-      for (int e = 0; e < E; e++) y[e] = xlane<2>(y[e]) + y[e] * sg;
-    }
-#pragma unroll
-    for (int kh = 1; kh < NCH; kh <<= 1)
-#pragma unroll
-      for (int k = 0; k < NCH; k++)
-        if (!(k & kh))
-#pragma unroll
-          for (int j = 0; j < 8; j++) {
-            const float a = y[8 * k + j], b = y[8 * (k + kh) + j];
-            y[8 * k + j] = a + b;
-            y[8 * (k + kh) + j] = a - b;
-          }
+    const float q = sumsq_tree<NCH, LOGP>(y);
+    wht_inlane_low<NCH>(y);
+    wht_cross<LOGP, E>(y);
+    wht_inlane_high<NCH>(y);
     const float nh = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(meta_blk + (size_t)v * 2));
     const float rd = sqrtf((float)D);
-    const float g = nh / (sqrtf(part[0]) * rd);
+    const float g = nh / (sqrtf(q) * rd);
 #pragma unroll
-    for (int e = 0; e < E; e++) {
-      const float t = y[e] * g;
-      y[e] = __uint_as_float(__float_as_uint(t) ^ (((sign_bits >> e) & 1u) << 31));
-    }
+    for (int e = 0; e < E; e++) y[e] = y[e] * g;
   }
 #pragma unroll
-  for (int k = 0; k < NCH; k++)
-    *reinterpret_cast<uint4*>(dst + k * 8 * P + 8 * ln.p) = pack8<DT>(y + 8 * k);
+  for (int k = 0; k < NCH; k++) {
+    uint4 o = pack8<DT>(y + 8 * k);
+    if constexpr (CodecInfo<C>::tq) {        // sigma_i on the packed output (sign bits 15, 31)
+      o.x ^= ls.flip[4 * k];
+      o.y ^= ls.flip[4 * k + 1];
+      o.z ^= ls.flip[4 * k + 2];
+      o.w ^= ls.flip[4 * k + 3];
+    }
+    *reinterpret_cast<uint4*>(dst + k * 8 * P + 8 * ln.p) = o;
+  }
 }
 
 template <int D, int DT, int C>
-__device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, uint32_t sign_bits,
+__device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, const LaneSigns<D>& ls,
                                        const float* cent) {
   constexpr int GW = Geo<D>::GW;
   constexpr int CB = CodecInfo<C>::bits * D / 8;
   const uint8_t* code_blk = s.slot + kHeaderBytes;
   const uint8_t* meta_blk = code_blk + (size_t)s.n_vec * CB;
   for (int v = ln.g; v < s.n_vec; v += GW)
-    decode_vector<D, DT, C>(code_blk, meta_blk, v, ln, const_cast<uint16_t*>(vec_ptr(s, v)), fixed, sign_bits,
-                            cent);
+    decode_vector<D, DT, C>(code_blk, meta_blk, v, ln, const_cast<uint16_t*>(vec_ptr(s, v)), fixed, ls, cent);
 }
 
 template <int D>
@@ -788,7 +819,7 @@ __device__ void copy_in_raw(const SegCtx& s, const uint8_t* srcb) {
 
 template <int D, int DT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
-  __shared__ float s_cent[16];
+  __shared__ float s_cent[32];
   const uint32_t seg = blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
@@ -838,20 +869,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
   const Lane ln = lane_info<D>();
   const bool tq = codec == C_TQ3 || codec == C_TQ4;
   if (tq) {
-    if (threadIdx.x < 16) s_cent[threadIdx.x] = p.tables->centroids[codec == C_TQ4 ? 1 : 0][threadIdx.x];
+    if (threadIdx.x < 32) {
+      const float c = p.tables->centroids[codec == C_TQ4 ? 1 : 0][threadIdx.x & 15];
+      s_cent[threadIdx.x] = threadIdx.x < 16 ? c : -c;
+    }
     __syncthreads();
   }
-  const uint32_t sign_bits = tq ? lane_signs<D>(p.sign_mask, ln.p) : 0u;
+  LaneSigns<D> ls;
+  if (tq) make_lane_signs<D>(p.sign_mask, ln.p, false, ls);
   const float fixed = __uint_as_float(h1.w);
   switch (codec) {
-    case C_FP8D: decode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, sign_bits, s_cent); break;
-    case C_FP8F: decode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, sign_bits, s_cent); break;
-    case C_FP8Y: decode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, sign_bits, s_cent); break;
-    case C_INT8: decode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, sign_bits, s_cent); break;
-    case C_U3: decode_segment_vectors<D, DT, C_U3>(s, ln, fixed, sign_bits, s_cent); break;
-    case C_U4: decode_segment_vectors<D, DT, C_U4>(s, ln, fixed, sign_bits, s_cent); break;
-    case C_TQ3: decode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, sign_bits, s_cent); break;
-    case C_TQ4: decode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, sign_bits, s_cent); break;
+    case C_FP8D: decode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, ls, s_cent); break;
+    case C_FP8F: decode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, ls, s_cent); break;
+    case C_FP8Y: decode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, ls, s_cent); break;
+    case C_INT8: decode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, ls, s_cent); break;
+    case C_U3: decode_segment_vectors<D, DT, C_U3>(s, ln, fixed, ls, s_cent); break;
+    case C_U4: decode_segment_vectors<D, DT, C_U4>(s, ln, fixed, ls, s_cent); break;
+    case C_TQ3: decode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, ls, s_cent); break;
+    case C_TQ4: decode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, ls, s_cent); break;
     default: break;
   }
 }
