@@ -24,6 +24,48 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_tq4_u4_llama3.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_page_kvc_amd", "csrc", f)
+                  for f in ("kvc_kernels.hip", "kvc_arch.h", "kvc_internal.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    b = re.search(rf"{kernel}_hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not m or not b or m.group(1) != kernel_source_hash():
+        return None
+    return int(b.group(1))
+
+
+def calibrate_copy(gib):
+    """A plain device-to-device copy of known size, for scaling the byte
+    counters: each launch reads and writes `gib` GiB once."""
+    import torch
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
 def algorithmic_bytes(L, n_pages, H, T, D, prot, kb, vb):
@@ -76,13 +118,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-pages", type=int, default=128)
+    ap.add_argument("--cpu-sample-pages", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="GIB",
+                    help="only run a plain GIB-GiB device copy (byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU only (no multi-GPU sharding is built); "
               "use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import numpy as np
     import torch
@@ -167,7 +214,8 @@ def main():
         "algorithmic_bytes_per_launch": alg, "bytes_per_token_encoded": bpt,
         "raw_data_segments": n_raw_data,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dom)},
     }
     kvc.kvc_destroy(ctx)
     if not args.no_cpu_baseline:

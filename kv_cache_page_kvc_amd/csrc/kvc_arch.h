@@ -1,0 +1,60 @@
+// kvc_arch.h -- gfx950-specific helpers of libkvc's kernels: global-memory
+// access through address-space-1 pointers (global_load/global_store rather
+// than flat, which would also count against the LDS wait counter) and the
+// DPP-fused FMA used by the cross-lane WHT butterflies.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+
+// 16-byte load of source pages, which are read once per call
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const g_u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld_global16(const void* p) {
+  const u32x4 v = *(const g_u32x4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_global16(void* p, uint4 v) {
+  u32x4 w = {v.x, v.y, v.z, v.w};
+  *(g_u32x4*)p = w;
+}
+
+// y[e] += c * y[e] of the partner lane, for e < 8, in one v_fmac_f32_dpp
+// each (single rounding; c = +-1 makes the product exact).  Partner of
+// stage Q: lane xor 1 (Q=0), xor 2 (Q=1), xor 8 within the row (Q=2).
+// The compiler does not see DPP inside the asm, so the block opens with
+// five wait states (a VALU write of a VGPR needs two before a DPP read of
+// it, a VALU write of EXEC five) and closes with two, for any DPP reader
+// of its results that the compiler places right after it.
+#define KVC_FMAC_DPP8(CTRL)                                                                        \
+  asm("s_nop 4\n\t"                                                                                \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+      "s_nop 1"                                                                                    \
+      : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7]) \
+      : "v"(c))
+
+template <int Q>
+__device__ __forceinline__ void fmac_xlane8(float* y, float c) {
+  if constexpr (Q == 0) KVC_FMAC_DPP8("quad_perm:[1,0,3,2]");
+  else if constexpr (Q == 1) KVC_FMAC_DPP8("quad_perm:[2,3,0,1]");
+  else KVC_FMAC_DPP8("row_ror:8");
+}
+
+#undef KVC_FMAC_DPP8
+
+}  // namespace kvc

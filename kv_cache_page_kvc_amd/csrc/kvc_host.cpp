@@ -362,6 +362,8 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   P->n_pages = n;
   P->n_layers = L->layers;
   P->heads = L->kv_heads;
+  // exact for every vector index v < 2^16 because heads <= 2^16 (v * heads < 2^32)
+  P->heads_magic = ((1ull << 32) + L->kv_heads - 1) / L->kv_heads;
   P->tokens = L->tokens_per_page;
   P->dtype = L->dtype;
   sign_mask(c->seed, L->head_dim, P->sign_mask);

@@ -59,6 +59,7 @@ struct CallParams {
   unsigned long long* spill_cursor;           // encode: bytes used in the spill region
   uint64_t base_lo, base_hi;                  // range of every layer base pointer (guard)
   int64_t sb, st, sh;                         // element strides
+  uint64_t heads_magic;                       // ceil(2^32 / heads): t = (v * magic) >> 32 = v / heads
   uint32_t n_pages, n_layers, heads, tokens;
   uint32_t dtype;                             // kvc_dtype
   uint32_t num_blocks;                        // page ids must be below this (guard)

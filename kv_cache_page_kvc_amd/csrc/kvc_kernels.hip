@@ -28,6 +28,7 @@
 // slot are ignored by decode).
 #include <hip/hip_runtime.h>
 
+#include "kvc_arch.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -36,13 +37,6 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte streaming load of engine pages (read once per call)
-__device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // ------------------------------------------------------------------ geometry
 template <int D>
@@ -53,7 +47,10 @@ struct Geo {
   static constexpr int NCH = E / 8;                           // 16-byte chunks per lane
   static constexpr int GPW = 64 / P;                          // groups per wave
   static constexpr int GW = GPW * (kThreads / 64);            // groups per workgroup
-  static constexpr int U = NCH <= 2 ? 4 : 2;                  // vectors in flight per group
+  // vectors per group whose loads are in flight together: 2 keeps the encode
+  // kernel at <= 80 VGPRs for D <= 128 (six waves per SIMD), and more vectors
+  // per batch measured slower through the lost occupancy
+  static constexpr int U = 2;
 };
 
 struct Lane {
@@ -203,17 +200,40 @@ __device__ __forceinline__ uint2 fp8x8(const float* q) {
   return r;
 }
 
+// RN(a / N) for a >= 0 (or +Inf/NaN, which stay non-finite) from the
+// constant RN(1/N) and one FMA residual step: q0 = RN(a*r), e = a - N*q0
+// (exact), RN(q0 + e*r).  Checked against the IEEE quotient for every
+// non-negative binary32 a, for N = 7, 15 and 127.
+template <int N>
+__device__ __forceinline__ float div_const(float a) {
+  static_assert(N == 7 || N == 15 || N == 127, "verified divisors only");
+  constexpr float r = 1.0f / (float)N;
+  const float q0 = a * r;
+  return fmaf(fmaf(-q0, (float)N, a), r, q0);
+}
+
+// RN(1/h) for a positive finite h that is an FP16 value: one Newton step
+// e = 1 - h*y0, y0 + e*y0 from the hardware estimate (within 1 ulp).  For
+// every such h, every start within 1 ulp of 1/h gives the correctly rounded
+// reciprocal (checked exhaustively), so the estimate's own rounding does not
+// matter.
+__device__ __forceinline__ float recip_f16val(float h) {
+  const float y0 = __builtin_amdgcn_rcpf(h);
+  return fmaf(fmaf(-h, y0, 1.0f), y0, y0);
+}
+
 // ------------------------------------------------------------------ addressing
 struct SegCtx {
   const uint16_t* src;      // element (t=0, h=0, i=0) of the page's component
   uint8_t* slot;            // slot start (header)
   int n_vec;
   int heads;
+  uint64_t heads_magic;     // v / heads = (v * heads_magic) >> 32 for v < 2^16
   int64_t st, sh;
 };
 
 __device__ __forceinline__ const uint16_t* vec_ptr(const SegCtx& s, int v) {
-  const int t = v / s.heads, h = v - t * s.heads;
+  const int t = (int)(((uint64_t)(uint32_t)v * s.heads_magic) >> 32), h = v - t * s.heads;
   return s.src + (int64_t)t * s.st + (int64_t)h * s.sh;
 }
 
@@ -266,20 +286,21 @@ __device__ __forceinline__ void make_lane_signs(const uint32_t* mask, int p, boo
 // parity bit from the sign, so after the last stage every sign is +1.
 template <int LOGP, int E>
 __device__ __forceinline__ void wht_cross(float* y) {
+  static_assert(E % 8 == 0, "lanes hold whole 8-element chunks");
   if constexpr (LOGP >= 1) {
     const float c = upper_lane<0>() ? 1.0f : -1.0f;
 #pragma unroll
-    for (int e = 0; e < E; e++) y[e] = fmaf(xlane<0>(y[e]), c, y[e]);
+    for (int e = 0; e < E; e += 8) fmac_xlane8<0>(y + e, c);
   }
   if constexpr (LOGP >= 2) {
     const float c = upper_lane<1>() ? 1.0f : -1.0f;
 #pragma unroll
-    for (int e = 0; e < E; e++) y[e] = fmaf(xlane<1>(y[e]), c, y[e]);
+    for (int e = 0; e < E; e += 8) fmac_xlane8<1>(y + e, c);
   }
   if constexpr (LOGP >= 3) {
     const float c = upper_lane<2>() ? 1.0f : -1.0f;
 #pragma unroll
-    for (int e = 0; e < E; e++) y[e] = fmaf(xlane<2>(y[e]), c, y[e]);
+    for (int e = 0; e < E; e += 8) fmac_xlane8<2>(y + e, c);
   }
 }
 
@@ -398,7 +419,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
       const float r448 = 1.0f / 448.0f;
       s = fmaxf(bits_to_f32<DT>(am), 1e-12f) * r448;
     }
-    if constexpr (C == C_INT8) s = fmaxf(bits_to_f32<DT>(am), 1e-12f) / 127.0f;
+    if constexpr (C == C_INT8) s = div_const<127>(fmaxf(bits_to_f32<DT>(am), 1e-12f));
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
       uint32_t lo, hi;
@@ -443,11 +464,11 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
     }
     mn = group_min<LOGP>(mn);
     mx = group_max<LOGP>(mx);
-    const float sig = (mx - mn) / (float)TOP;
+    const float sig = div_const<TOP>(mx - mn);
     const float mh = f16_round(mn), sh = f16_round(sig);
     // +-Inf reach mn/mx and overflow the FP16 metadata; NaN is caught below
     bad = !__builtin_isfinite(mh) || !__builtin_isfinite(sh);
-    const float y = sh == 0.0f ? 0.0f : 1.0f / sh;
+    const float y = sh == 0.0f ? 0.0f : recip_f16val(sh);
     constexpr int MAGIC = 0x4B400000;   // bits of 1.5 * 2^23
     uint32_t tor = 0;
 #pragma unroll
@@ -489,14 +510,14 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
     constexpr int LO = 0x4B400000 - kCellOffset, HI = 0x4B400000 + kCellOffset;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      uint32_t acc = 0;
+      uint32_t acc = 0;                  // element j ends up at bits [BITS*j, BITS*j + BITS)
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
+      for (int j = 7; j >= 0; j--) {
         const float z = y[8 * k + j];
         const int t = __float_as_int(fmaf(z, kCellScale, 12582912.0f));
         const int idx = min(max(t, LO), HI) - LO;
         const CellEntry ce = cells[idx];
-        acc += (ce.base + (z > ce.thr ? 1u : 0u)) << (BITS * j);
+        acc = (acc << BITS) + ce.base + (z > ce.thr ? 1u : 0u);
       }
       store_codes<D, BITS>(cv, k, ln.p, acc, 0);
     }
@@ -505,26 +526,35 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
   return bad;
 }
 
+// the source chunks of vectors v0 + u*GW (u < U) that this lane holds
+template <int D>
+__device__ __forceinline__ void load_batch(const SegCtx& s, const Lane& ln, int v0,
+                                           uint4 (&w)[Geo<D>::U][Geo<D>::NCH]) {
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const int v = v0 + u * GW;
+    if (v < s.n_vec) {
+      const uint16_t* src = vec_ptr(s, v);
+#pragma unroll
+      for (int k = 0; k < NCH; k++) w[u][k] = ld_stream16(src + k * 8 * P + 8 * ln.p);
+    }
+  }
+}
+
+// Encode the segment's vectors.  Returns nonzero if any vector forces the
+// segment raw.
 template <int D, int DT, int C>
 __device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, const LaneSigns<D>& ls,
                                       const CellEntry* cells) {
-  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
+  constexpr int GW = Geo<D>::GW, U = Geo<D>::U;
   constexpr int CB = CodecInfo<C>::bits * D / 8;
   uint8_t* code_blk = s.slot + kHeaderBytes;
   uint8_t* meta_blk = code_blk + (size_t)s.n_vec * CB;
   int bad = 0;
+  uint4 w[U][Geo<D>::NCH];
   for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
-    uint4 w[U][NCH];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int v = v0 + u * GW;
-      if (v < s.n_vec) {
-        const uint16_t* src = vec_ptr(s, v);
-#pragma unroll
-        for (int k = 0; k < NCH; k++)
-          w[u][k] = ld_stream(src + k * 8 * P + 8 * ln.p);
-      }
-    }
+    load_batch<D>(s, ln, v0, w);
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int v = v0 + u * GW;
@@ -541,8 +571,7 @@ __device__ void copy_out_raw(const SegCtx& s, uint8_t* dst) {
   const int total = s.n_vec * CPV;
   for (int q = threadIdx.x; q < total; q += kThreads) {
     const int v = q / CPV, c = q - v * CPV;
-    const uint4 val = ld_stream(vec_ptr(s, v) + 8 * c);
-    *reinterpret_cast<uint4*>(dst + (size_t)q * 16) = val;
+    st_global16(dst + (size_t)q * 16, ld_stream16(vec_ptr(s, v) + 8 * c));
   }
 }
 
@@ -611,6 +640,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   s.src = E.base + (int64_t)page * p.sb;
   s.slot = p.buf + slot_off;
   s.heads = (int)p.heads;
+  s.heads_magic = p.heads_magic;
   s.n_vec = (int)(p.heads * p.tokens);
   s.st = p.st;
   s.sh = p.sh;
@@ -705,22 +735,38 @@ __device__ __forceinline__ uint2 load_codes(const uint8_t* cv, int k, int p) {
 // byte m of a word, as a float (v_cvt_f32_ubyte*)
 __device__ __forceinline__ float ubyte_f32(uint32_t w, int m) { return (float)((w >> (8 * m)) & 0xFFu); }
 
+// what a lane reads of one stored vector: its code chunks and the metadata
+template <int D>
+struct VecCodes {
+  uint2 c[Geo<D>::NCH];
+  uint32_t meta;
+};
+
+template <int D, int C>
+__device__ __forceinline__ void load_vec_codes(const uint8_t* code_blk, const uint8_t* meta_blk, int v,
+                                               const Lane& ln, VecCodes<D>& vc) {
+  constexpr int BITS = CodecInfo<C>::bits, CB = BITS * D / 8, META = CodecInfo<C>::meta;
+  const uint8_t* cv = code_blk + (size_t)v * CB;
+#pragma unroll
+  for (int k = 0; k < Geo<D>::NCH; k++) vc.c[k] = load_codes<D, BITS>(cv, k, ln.p);
+  if constexpr (META == 4) vc.meta = *reinterpret_cast<const uint32_t*>(meta_blk + (size_t)v * 4);
+  else if constexpr (META == 2) vc.meta = *reinterpret_cast<const uint16_t*>(meta_blk + (size_t)v * 2);
+  else vc.meta = 0;
+}
+
 template <int D, int DT, int C>
-__device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uint8_t* meta_blk, int v,
-                                              const Lane& ln, uint16_t* dst, float fixed, const LaneSigns<D>& ls,
-                                              const float* cent) {
+__device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane& ln, uint16_t* dst, float fixed,
+                                              const LaneSigns<D>& ls, const float* cent) {
   constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP, P = Geo<D>::P;
   constexpr int BITS = CodecInfo<C>::bits;
-  constexpr int CB = BITS * D / 8;
-  const uint8_t* cv = code_blk + (size_t)v * CB;
   float y[E];
   if constexpr (CodecInfo<C>::fp8 || C == C_INT8) {
     float s = 1.0f;
     if constexpr (C == C_FP8F) s = fixed;
-    if constexpr (C == C_FP8Y || C == C_INT8) s = *reinterpret_cast<const float*>(meta_blk + (size_t)v * 4);
+    if constexpr (C == C_FP8Y || C == C_INT8) s = __uint_as_float(vc.meta);
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      const uint2 c = load_codes<D, 8>(cv, k, ln.p);
+      const uint2 c = vc.c[k];
 #pragma unroll
       for (int j = 0; j < 8; j++) {
         const uint32_t word = j < 4 ? c.x : c.y;
@@ -741,12 +787,12 @@ __device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uin
     }
   }
   if constexpr (CodecInfo<C>::uni) {
-    const uint32_t mw = *reinterpret_cast<const uint32_t*>(meta_blk + (size_t)v * 4);
+    const uint32_t mw = vc.meta;
     const float mh = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
     const float sh = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      const uint32_t w = load_codes<D, BITS>(cv, k, ln.p).x;
+      const uint32_t w = vc.c[k].x;
       float code[8];
       if constexpr (BITS == 4) {
         const uint32_t even = w & 0x0F0F0F0Fu, odd = (w >> 4) & 0x0F0F0F0Fu;   // nibbles to bytes
@@ -768,7 +814,7 @@ __device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uin
     const int base = (__builtin_popcount(ln.p) & 1) ? 16 : 0;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      const uint32_t w = load_codes<D, BITS>(cv, k, ln.p).x;
+      const uint32_t w = vc.c[k].x;
 #pragma unroll
       for (int j = 0; j < 8; j++) y[8 * k + j] = cent[base + ((w >> (BITS * j)) & ((1u << BITS) - 1))];
     }
@@ -776,7 +822,7 @@ __device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uin
     wht_inlane_low<NCH>(y);
     wht_cross<LOGP, E>(y);
     wht_inlane_high<NCH>(y);
-    const float nh = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(meta_blk + (size_t)v * 2));
+    const float nh = (float)__builtin_bit_cast(_Float16, (uint16_t)vc.meta);
     const float rd = sqrtf((float)D);
     const float g = nh / (sqrtf(q) * rd);
 #pragma unroll
@@ -791,19 +837,28 @@ __device__ __forceinline__ void decode_vector(const uint8_t* code_blk, const uin
       o.z ^= ls.flip[4 * k + 2];
       o.w ^= ls.flip[4 * k + 3];
     }
-    *reinterpret_cast<uint4*>(dst + k * 8 * P + 8 * ln.p) = o;
+    st_global16(dst + k * 8 * P + 8 * ln.p, o);
   }
 }
 
 template <int D, int DT, int C>
 __device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, const LaneSigns<D>& ls,
                                        const float* cent) {
-  constexpr int GW = Geo<D>::GW;
+  constexpr int GW = Geo<D>::GW, U = Geo<D>::U;      // vectors whose codes are in flight together
   constexpr int CB = CodecInfo<C>::bits * D / 8;
   const uint8_t* code_blk = s.slot + kHeaderBytes;
   const uint8_t* meta_blk = code_blk + (size_t)s.n_vec * CB;
-  for (int v = ln.g; v < s.n_vec; v += GW)
-    decode_vector<D, DT, C>(code_blk, meta_blk, v, ln, const_cast<uint16_t*>(vec_ptr(s, v)), fixed, ls, cent);
+  for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
+    VecCodes<D> vc[U];
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (v0 + u * GW < s.n_vec) load_vec_codes<D, C>(code_blk, meta_blk, v0 + u * GW, ln, vc[u]);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int v = v0 + u * GW;
+      if (v < s.n_vec) decode_vector<D, DT, C>(vc[u], ln, const_cast<uint16_t*>(vec_ptr(s, v)), fixed, ls, cent);
+    }
+  }
 }
 
 template <int D>
@@ -812,8 +867,7 @@ __device__ void copy_in_raw(const SegCtx& s, const uint8_t* srcb) {
   const int total = s.n_vec * CPV;
   for (int q = threadIdx.x; q < total; q += kThreads) {
     const int v = q / CPV, c = q - v * CPV;
-    const uint4 val = *reinterpret_cast<const uint4*>(srcb + (size_t)q * 16);
-    *reinterpret_cast<uint4*>(const_cast<uint16_t*>(vec_ptr(s, v)) + 8 * c) = val;
+    st_global16(const_cast<uint16_t*>(vec_ptr(s, v)) + 8 * c, ld_global16(srcb + (size_t)q * 16));
   }
 }
 
@@ -838,6 +892,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
   s.src = E.base + (int64_t)page * p.sb;                  // destination page
   s.slot = p.buf + slot_off;
   s.heads = (int)p.heads;
+  s.heads_magic = p.heads_magic;
   s.n_vec = (int)(p.heads * p.tokens);
   s.st = p.st;
   s.sh = p.sh;
