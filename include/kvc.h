@@ -96,7 +96,9 @@ typedef enum {
  * Requirements: base pointers 16-B aligned, strides positive multiples of 8
  * elements; SEPARATE_NHD: stride_head >= D, stride_token >= H*stride_head,
  * stride_block >= T*stride_token; PACKED_HT2D: stride_token >= 2*D,
- * stride_head >= T*stride_token, stride_block >= H*stride_head. */
+ * stride_head >= T*stride_token, stride_block >= H*stride_head.  One page
+ * of one layer must span fewer than 2^31 elements ((T-1)*stride_token +
+ * (H-1)*stride_head + D, or + 2*D packed), else KVC_E_UNSUPPORTED. */
 typedef struct {
   uint32_t abi;                 /* KVC_ABI_VERSION */
   uint32_t kind;                /* kvc_layout_kind */

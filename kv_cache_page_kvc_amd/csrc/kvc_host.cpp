@@ -173,6 +173,9 @@ kvc_status check_layout(const kvc_layout* L) {
     if (st < 2 * (int64_t)D || sh < T * st || sb < H * sh) return KVC_E_ARG;
     if (L->v_base) return KVC_E_ARG;
   }
+  // the kernels address a page's elements with 32-bit offsets
+  const int64_t page_extent = (T - 1) * st + (H - 1) * sh + (L->kind == KVC_SEPARATE_NHD ? 1 : 2) * (int64_t)D;
+  if (page_extent >= (int64_t)1 << 31) return KVC_E_UNSUPPORTED;
   if (!L->k_base) return KVC_E_ARG;
   for (uint32_t l = 0; l < L->layers; l++) {
     const void* k = L->k_base[l];
@@ -364,6 +367,15 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   P->heads = L->kv_heads;
   // exact for every vector index v < 2^16 because heads <= 2^16 (v * heads < 2^32)
   P->heads_magic = ((1ull << 32) + L->kv_heads - 1) / L->kv_heads;
+  {
+    const uint32_t H = L->kv_heads, gw = (uint32_t)groups_per_workgroup((int)L->head_dim);
+    const uint32_t st = (uint32_t)L->stride_token, sh = (uint32_t)L->stride_head;   // < 2^31 (check_layout)
+    P->st32 = st;
+    P->sh32 = sh;
+    P->walk_dh = gw % H;
+    P->walk_step = (gw / H) * st + (gw % H) * sh;      // modulo 2^32
+    P->walk_wrap = st - H * sh;                         // modulo 2^32
+  }
   P->tokens = L->tokens_per_page;
   P->dtype = L->dtype;
   sign_mask(c->seed, L->head_dim, P->sign_mask);

@@ -11,6 +11,13 @@
 namespace kvc {
 
 constexpr int kThreads = 256;                 // one workgroup per segment
+
+// A head vector of D elements is held by a group of lanes_per_vector(D)
+// lanes; a workgroup holds groups_per_workgroup(D) groups, and group g
+// handles vectors g, g + GW, g + 2*GW, ... of a segment (GW = groups per
+// workgroup).
+constexpr int lanes_per_vector(int d) { return d == 32 ? 2 : (d == 64 ? 4 : 8); }
+constexpr int groups_per_workgroup(int d) { return kThreads / lanes_per_vector(d); }
 constexpr uint64_t kSlotAlign = KVC_SLOT_ALIGN;
 constexpr uint32_t kHeaderBytes = KVC_HEADER_BYTES;
 
@@ -60,6 +67,12 @@ struct CallParams {
   uint64_t base_lo, base_hi;                  // range of every layer base pointer (guard)
   int64_t sb, st, sh;                         // element strides
   uint64_t heads_magic;                       // ceil(2^32 / heads): t = (v * magic) >> 32 = v / heads
+  // Walking a lane from vector v to v + GW (GW = groups_per_workgroup(D)):
+  // head h -> h + walk_dh (minus heads on wrap), element offset within the
+  // page -> + walk_step (+ walk_wrap on wrap); all modulo 2^32.  A page spans
+  // fewer than 2^31 elements, so every offset actually used is exact.
+  uint32_t st32, sh32;                        // stride_token, stride_head
+  uint32_t walk_dh, walk_step, walk_wrap;
   uint32_t n_pages, n_layers, heads, tokens;
   uint32_t dtype;                             // kvc_dtype
   uint32_t num_blocks;                        // page ids must be below this (guard)

@@ -41,12 +41,13 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // ------------------------------------------------------------------ geometry
 template <int D>
 struct Geo {
-  static constexpr int P = D == 32 ? 2 : (D == 64 ? 4 : 8);   // lanes per vector
-  static constexpr int LOGP = D == 32 ? 1 : (D == 64 ? 2 : 3);
+  static constexpr int P = lanes_per_vector(D);               // lanes per vector
+  static constexpr int LOGP = P == 2 ? 1 : (P == 4 ? 2 : 3);
   static constexpr int E = D / P;                             // elements per lane
   static constexpr int NCH = E / 8;                           // 16-byte chunks per lane
   static constexpr int GPW = 64 / P;                          // groups per wave
-  static constexpr int GW = GPW * (kThreads / 64);            // groups per workgroup
+  static constexpr int GW = groups_per_workgroup(D);          // groups per workgroup
+  static_assert(GW == GPW * (kThreads / 64), "group geometry");
   // vectors per group whose loads are in flight together: 2 keeps the encode
   // kernel at <= 80 VGPRs for D <= 128 (six waves per SIMD), and more vectors
   // per batch measured slower through the lost occupancy
@@ -229,12 +230,42 @@ struct SegCtx {
   int n_vec;
   int heads;
   uint64_t heads_magic;     // v / heads = (v * heads_magic) >> 32 for v < 2^16
-  int64_t st, sh;
+  uint32_t st, sh;          // element strides of token and head
+  uint32_t walk_dh, walk_step, walk_wrap;
 };
 
-__device__ __forceinline__ const uint16_t* vec_ptr(const SegCtx& s, int v) {
+// A lane's current vector: its head and its element offset in the page
+// (below 2^31, checked on the host).
+struct VecPos {
+  int h;
+  uint32_t off;
+};
+
+__device__ __forceinline__ VecPos vec_pos(const SegCtx& s, int v) {
   const int t = (int)(((uint64_t)(uint32_t)v * s.heads_magic) >> 32), h = v - t * s.heads;
-  return s.src + (int64_t)t * s.st + (int64_t)h * s.sh;
+  VecPos q;
+  q.h = h;
+  q.off = (uint32_t)t * s.st + (uint32_t)h * s.sh;
+  return q;
+}
+// from vector v to v + GW: the head advances by GW mod heads, with a carry
+// into the token
+__device__ __forceinline__ void vec_advance(const SegCtx& s, VecPos& q) {
+  q.h += (int)s.walk_dh;
+  q.off += s.walk_step;
+  if (q.h >= s.heads) {
+    q.h -= s.heads;
+    q.off += s.walk_wrap;
+  }
+}
+// base + a 32-bit byte offset (global_load/store with a scalar base)
+template <class T>
+__device__ __forceinline__ T* byte_at(T* base, uint32_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+template <class T>
+__device__ __forceinline__ const T* byte_at(const T* base, uint32_t off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
 }
 
 // ------------------------------------------------------------------ encoders
@@ -360,15 +391,15 @@ __device__ __forceinline__ float sumsq_tree(const float* y) {
 
 // store the codes of one chunk (8 elements) of a vector's code block
 template <int D, int BITS>
-__device__ __forceinline__ void store_codes(uint8_t* cv, int k, int p, uint32_t lo, uint32_t hi) {
+__device__ __forceinline__ void store_codes(uint8_t* slot, uint32_t cv, int k, int p, uint32_t lo, uint32_t hi) {
   constexpr int P = Geo<D>::P;
-  const int e0 = k * 8 * P + 8 * p;                 // first element of the chunk
+  const uint32_t e0 = k * 8 * P + 8 * p;            // first element of the chunk
   if constexpr (BITS == 8) {
-    *reinterpret_cast<uint2*>(cv + e0) = make_uint2(lo, hi);
+    *byte_at(reinterpret_cast<uint2*>(slot), cv + e0) = make_uint2(lo, hi);
   } else if constexpr (BITS == 4) {
-    *reinterpret_cast<uint32_t*>(cv + e0 / 2) = lo;
+    *byte_at(reinterpret_cast<uint32_t*>(slot), cv + e0 / 2) = lo;
   } else {                                          // 3 bits: 24-bit piece at byte 3*e0/8
-    uint8_t* q = cv + (3 * e0) / 8;                 // any byte alignment
+    uint8_t* q = byte_at(slot, cv + (3 * e0) / 8);  // any byte alignment
     q[0] = (uint8_t)lo;
     q[1] = (uint8_t)(lo >> 8);
     q[2] = (uint8_t)(lo >> 16);
@@ -385,13 +416,12 @@ __device__ __forceinline__ constexpr uint32_t magic_sum() {
 }
 
 template <int D, int DT, int C>
-__device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, uint8_t* code_blk,
-                                             uint8_t* meta_blk, float fixed, const LaneSigns<D>& ls,
-                                             const CellEntry* cells) {
+__device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, uint8_t* slot, uint32_t meta_blk,
+                                             float fixed, const LaneSigns<D>& ls, const CellEntry* cells) {
   constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP;
   constexpr int BITS = CodecInfo<C>::bits;
   constexpr int CB = BITS * D / 8;
-  uint8_t* cv = code_blk + (size_t)v * CB;
+  const uint32_t cv = kHeaderBytes + (uint32_t)v * CB;   // byte offset of the vector's codes
   if constexpr (CodecInfo<C>::tq) {
     // sigma (and the lane parity sign) applied to the packed source words
 #pragma unroll
@@ -448,10 +478,10 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
         lo = r.x;
         hi = r.y;
       }
-      store_codes<D, 8>(cv, k, ln.p, lo, hi);
+      store_codes<D, 8>(slot, cv, k, ln.p, lo, hi);
     }
     if constexpr (C == C_FP8Y || C == C_INT8)
-      if (ln.p == 0) *reinterpret_cast<float*>(meta_blk + (size_t)v * 4) = s;
+      if (ln.p == 0) *byte_at(reinterpret_cast<float*>(slot), meta_blk + (uint32_t)v * 4) = s;
   }
 
   if constexpr (CodecInfo<C>::uni) {
@@ -473,23 +503,23 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
     uint32_t tor = 0;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      uint32_t acc = 0;
+      uint32_t acc = 0;                  // sum over j of (MAGIC + code_j) << BITS*j
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
+      for (int j = 7; j >= 0; j--) {
         // RN(d*y + 1.5*2^23) = 1.5*2^23 + RNE(d*y) while |d*y| < 2^22; the
         // integer clamp maps every out-of-range result to 0 or TOP
         const int t = __float_as_int(fmaf(x[8 * k + j] - mh, y, 12582912.0f));
         tor |= (uint32_t)t;
-        acc += (uint32_t)min(max(t, MAGIC), MAGIC + TOP) << (BITS * j);
+        acc = (acc << BITS) + (uint32_t)min(max(t, MAGIC), MAGIC + TOP);
       }
-      store_codes<D, BITS>(cv, k, ln.p, acc - magic_sum<BITS>(), 0);
+      store_codes<D, BITS>(slot, cv, k, ln.p, acc - magic_sum<BITS>(), 0);
     }
     // For finite inputs every t lies in (2^22, 2^41) in magnitude (|d*y| is
     // bounded by the FP16 range of d and by y <= 2^24), so bit 29 (exponent
     // bit 6) of t is clear; a NaN source value makes t NaN, which sets it.
     bad |= (int)((group_or<LOGP>(tor) >> 29) & 1u);
     if (ln.p == 0)
-      *reinterpret_cast<uint32_t*>(meta_blk + (size_t)v * 4) = f16_bits(mh) | (f16_bits(sh) << 16);
+      *byte_at(reinterpret_cast<uint32_t*>(slot), meta_blk + (uint32_t)v * 4) = f16_bits(mh) | (f16_bits(sh) << 16);
   }
 
   if constexpr (CodecInfo<C>::tq) {
@@ -519,26 +549,27 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
         const CellEntry ce = cells[idx];
         acc = (acc << BITS) + ce.base + (z > ce.thr ? 1u : 0u);
       }
-      store_codes<D, BITS>(cv, k, ln.p, acc, 0);
+      store_codes<D, BITS>(slot, cv, k, ln.p, acc, 0);
     }
-    if (ln.p == 0) *reinterpret_cast<uint16_t*>(meta_blk + (size_t)v * 2) = (uint16_t)f16_bits(nh);
+    if (ln.p == 0) *byte_at(reinterpret_cast<uint16_t*>(slot), meta_blk + (uint32_t)v * 2) = (uint16_t)f16_bits(nh);
   }
   return bad;
 }
 
-// the source chunks of vectors v0 + u*GW (u < U) that this lane holds
+// the source chunks of vectors v0 + u*GW (u < U) that this lane holds; pos
+// is the lane's position at v0 and ends at v0 + U*GW
 template <int D>
-__device__ __forceinline__ void load_batch(const SegCtx& s, const Lane& ln, int v0,
+__device__ __forceinline__ void load_batch(const SegCtx& s, const Lane& ln, int v0, VecPos& pos,
                                            uint4 (&w)[Geo<D>::U][Geo<D>::NCH]) {
   constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
 #pragma unroll
   for (int u = 0; u < U; u++) {
-    const int v = v0 + u * GW;
-    if (v < s.n_vec) {
-      const uint16_t* src = vec_ptr(s, v);
+    if (v0 + u * GW < s.n_vec) {
+      const uint32_t b = 2 * (pos.off + 8 * ln.p);
 #pragma unroll
-      for (int k = 0; k < NCH; k++) w[u][k] = ld_stream16(src + k * 8 * P + 8 * ln.p);
+      for (int k = 0; k < NCH; k++) w[u][k] = ld_stream16(byte_at(s.src, b + 16 * P * k));
     }
+    vec_advance(s, pos);
   }
 }
 
@@ -549,16 +580,16 @@ __device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fix
                                       const CellEntry* cells) {
   constexpr int GW = Geo<D>::GW, U = Geo<D>::U;
   constexpr int CB = CodecInfo<C>::bits * D / 8;
-  uint8_t* code_blk = s.slot + kHeaderBytes;
-  uint8_t* meta_blk = code_blk + (size_t)s.n_vec * CB;
+  const uint32_t meta_blk = kHeaderBytes + (uint32_t)s.n_vec * CB;   // byte offset in the slot
   int bad = 0;
   uint4 w[U][Geo<D>::NCH];
+  VecPos pos = vec_pos(s, ln.g);
   for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
-    load_batch<D>(s, ln, v0, w);
+    load_batch<D>(s, ln, v0, pos, w);
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int v = v0 + u * GW;
-      if (v < s.n_vec) bad |= encode_vector<D, DT, C>(w[u], v, ln, code_blk, meta_blk, fixed, ls, cells);
+      if (v < s.n_vec) bad |= encode_vector<D, DT, C>(w[u], v, ln, s.slot, meta_blk, fixed, ls, cells);
     }
   }
   return bad;
@@ -566,24 +597,28 @@ __device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fix
 
 // copy a segment from the engine layout into contiguous canonical order
 template <int D>
-__device__ void copy_out_raw(const SegCtx& s, uint8_t* dst) {
-  constexpr int CPV = D / 8;                        // 16-byte chunks per vector
-  const int total = s.n_vec * CPV;
-  for (int q = threadIdx.x; q < total; q += kThreads) {
-    const int v = q / CPV, c = q - v * CPV;
-    st_global16(dst + (size_t)q * 16, ld_stream16(vec_ptr(s, v) + 8 * c));
+__device__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
+  uint4 w[U][NCH];
+  VecPos pos = vec_pos(s, ln.g);
+  for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
+    load_batch<D>(s, ln, v0, pos, w);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int v = v0 + u * GW;
+      if (v < s.n_vec) {
+        const uint32_t b = (uint32_t)v * (2 * D) + 16 * ln.p;
+#pragma unroll
+        for (int k = 0; k < NCH; k++) st_global16(byte_at(dst, b + 16 * P * k), w[u][k]);
+      }
+    }
   }
 }
 
-__device__ __forceinline__ void zero_fill(uint8_t* p, size_t n) {
-  // bytes [0, n) of a region whose start may be unaligned
-  size_t head = (16 - ((uintptr_t)p & 15)) & 15;
-  if (head > n) head = n;
-  for (size_t b = threadIdx.x; b < head; b += kThreads) p[b] = 0;
-  uint8_t* a = p + head;
-  const size_t n16 = (n - head) / 16;
-  for (size_t q = threadIdx.x; q < n16; q += kThreads) reinterpret_cast<uint4*>(a)[q] = make_uint4(0, 0, 0, 0);
-  for (size_t b = head + n16 * 16 + threadIdx.x; b < n; b += kThreads) p[b] = 0;
+// zero bytes [from, to) of a slot; from is even (headers and payloads have
+// even sizes) and the padding is shorter than one 256-byte slot unit
+__device__ __forceinline__ void zero_pad(uint8_t* slot, uint32_t from, uint32_t to) {
+  for (uint32_t b = from + 2 * threadIdx.x; b < to; b += 2 * kThreads) *byte_at(reinterpret_cast<uint16_t*>(slot), b) = 0;
 }
 
 __device__ __forceinline__ void write_header_desc(uint8_t* slot, kvc_segment_desc* desc, uint64_t slot_off,
@@ -642,22 +677,25 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   s.heads = (int)p.heads;
   s.heads_magic = p.heads_magic;
   s.n_vec = (int)(p.heads * p.tokens);
-  s.st = p.st;
-  s.sh = p.sh;
+  s.st = p.st32;
+  s.sh = p.sh32;
+  s.walk_dh = p.walk_dh;
+  s.walk_step = p.walk_step;
+  s.walk_wrap = p.walk_wrap;
   const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
   const uint32_t slot_bytes = E.slot_bytes;
   kvc_segment_desc* desc = p.desc + seg;
 
+  const Lane ln = lane_info<D>();
   if (codec == C_RAW) {                                        // raw by policy
-    copy_out_raw<D>(s, s.slot + kHeaderBytes);
-    zero_fill(s.slot + kHeaderBytes + raw_bytes, slot_bytes - kHeaderBytes - raw_bytes);
+    copy_out_raw<D>(s, ln, s.slot + kHeaderBytes);
+    zero_pad(s.slot, kHeaderBytes + raw_bytes, slot_bytes);
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY, KVC_SEG_RAW_POLICY, DT, comp, D,
                         s.n_vec, raw_bytes, 0, 0);
     return;
   }
 
-  const Lane ln = lane_info<D>();
   const bool tq = codec == C_TQ3 || codec == C_TQ4;
   if (tq) {
     const CellEntry* src = p.tables->cells[codec == C_TQ4 ? 1 : 0];
@@ -691,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   if (codec == C_FP8Y || codec == C_INT8 || codec == C_U3 || codec == C_U4) meta = 4;
   if (codec == C_TQ3 || codec == C_TQ4) meta = 2;
   const uint32_t payload = (uint32_t)s.n_vec * (uint32_t)(bits * D / 8 + meta);
-  zero_fill(s.slot + kHeaderBytes + payload, slot_bytes - kHeaderBytes - payload);
+  zero_pad(s.slot, kHeaderBytes + payload, slot_bytes);
 
   if (!any_bad) {
     if (threadIdx.x == 0)
@@ -705,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   __syncthreads();
   const uint64_t off = s_spill;
   const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
-  if (fits) copy_out_raw<D>(s, p.buf + p.slot_region + off);
+  if (fits) copy_out_raw<D>(s, ln, p.buf + p.slot_region + off);
   if (threadIdx.x == 0) {
     if (fits)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA, KVC_SEG_RAW_DATA, DT, comp, D, s.n_vec,
@@ -719,15 +757,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
 // ------------------------------------------------------------------ decoders
 // the codes of one chunk (8 elements) of a vector's code block
 template <int D, int BITS>
-__device__ __forceinline__ uint2 load_codes(const uint8_t* cv, int k, int p) {
+__device__ __forceinline__ uint2 load_codes(const uint8_t* slot, uint32_t cv, int k, int p) {
   constexpr int P = Geo<D>::P;
-  const int e0 = k * 8 * P + 8 * p;
+  const uint32_t e0 = k * 8 * P + 8 * p;
   if constexpr (BITS == 8) {
-    return *reinterpret_cast<const uint2*>(cv + e0);
+    return *byte_at(reinterpret_cast<const uint2*>(slot), cv + e0);
   } else if constexpr (BITS == 4) {
-    return make_uint2(*reinterpret_cast<const uint32_t*>(cv + e0 / 2), 0u);
+    return make_uint2(*byte_at(reinterpret_cast<const uint32_t*>(slot), cv + e0 / 2), 0u);
   } else {
-    const uint8_t* q = cv + (3 * e0) / 8;
+    const uint8_t* q = byte_at(slot, cv + (3 * e0) / 8);
     return make_uint2((uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16), 0u);
   }
 }
@@ -742,20 +780,22 @@ struct VecCodes {
   uint32_t meta;
 };
 
+// meta_blk: byte offset of the metadata block in the slot
 template <int D, int C>
-__device__ __forceinline__ void load_vec_codes(const uint8_t* code_blk, const uint8_t* meta_blk, int v,
-                                               const Lane& ln, VecCodes<D>& vc) {
+__device__ __forceinline__ void load_vec_codes(const uint8_t* slot, uint32_t meta_blk, int v, const Lane& ln,
+                                               VecCodes<D>& vc) {
   constexpr int BITS = CodecInfo<C>::bits, CB = BITS * D / 8, META = CodecInfo<C>::meta;
-  const uint8_t* cv = code_blk + (size_t)v * CB;
+  const uint32_t cv = kHeaderBytes + (uint32_t)v * CB;
 #pragma unroll
-  for (int k = 0; k < Geo<D>::NCH; k++) vc.c[k] = load_codes<D, BITS>(cv, k, ln.p);
-  if constexpr (META == 4) vc.meta = *reinterpret_cast<const uint32_t*>(meta_blk + (size_t)v * 4);
-  else if constexpr (META == 2) vc.meta = *reinterpret_cast<const uint16_t*>(meta_blk + (size_t)v * 2);
+  for (int k = 0; k < Geo<D>::NCH; k++) vc.c[k] = load_codes<D, BITS>(slot, cv, k, ln.p);
+  if constexpr (META == 4) vc.meta = *byte_at(reinterpret_cast<const uint32_t*>(slot), meta_blk + (uint32_t)v * 4);
+  else if constexpr (META == 2) vc.meta = *byte_at(reinterpret_cast<const uint16_t*>(slot), meta_blk + (uint32_t)v * 2);
   else vc.meta = 0;
 }
 
 template <int D, int DT, int C>
-__device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane& ln, uint16_t* dst, float fixed,
+__device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane& ln, uint16_t* page, uint32_t voff,
+                                              float fixed,
                                               const LaneSigns<D>& ls, const float* cent) {
   constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP, P = Geo<D>::P;
   constexpr int BITS = CodecInfo<C>::bits;
@@ -837,7 +877,7 @@ __device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane&
       o.z ^= ls.flip[4 * k + 2];
       o.w ^= ls.flip[4 * k + 3];
     }
-    st_global16(dst + k * 8 * P + 8 * ln.p, o);
+    st_global16(byte_at(page, 2 * (voff + 8 * ln.p) + 16 * P * k), o);
   }
 }
 
@@ -846,28 +886,48 @@ __device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fi
                                        const float* cent) {
   constexpr int GW = Geo<D>::GW, U = Geo<D>::U;      // vectors whose codes are in flight together
   constexpr int CB = CodecInfo<C>::bits * D / 8;
-  const uint8_t* code_blk = s.slot + kHeaderBytes;
-  const uint8_t* meta_blk = code_blk + (size_t)s.n_vec * CB;
+  const uint32_t meta_blk = kHeaderBytes + (uint32_t)s.n_vec * CB;
+  uint16_t* page = const_cast<uint16_t*>(s.src);
+  VecPos pos = vec_pos(s, ln.g);
   for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
     VecCodes<D> vc[U];
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (v0 + u * GW < s.n_vec) load_vec_codes<D, C>(code_blk, meta_blk, v0 + u * GW, ln, vc[u]);
+      if (v0 + u * GW < s.n_vec) load_vec_codes<D, C>(s.slot, meta_blk, v0 + u * GW, ln, vc[u]);
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int v = v0 + u * GW;
-      if (v < s.n_vec) decode_vector<D, DT, C>(vc[u], ln, const_cast<uint16_t*>(vec_ptr(s, v)), fixed, ls, cent);
+      if (v0 + u * GW < s.n_vec) decode_vector<D, DT, C>(vc[u], ln, page, pos.off, fixed, ls, cent);
+      vec_advance(s, pos);
     }
   }
 }
 
+// copy a segment from contiguous canonical order into the engine layout
 template <int D>
-__device__ void copy_in_raw(const SegCtx& s, const uint8_t* srcb) {
-  constexpr int CPV = D / 8;
-  const int total = s.n_vec * CPV;
-  for (int q = threadIdx.x; q < total; q += kThreads) {
-    const int v = q / CPV, c = q - v * CPV;
-    st_global16(const_cast<uint16_t*>(vec_ptr(s, v)) + 8 * c, ld_global16(srcb + (size_t)q * 16));
+__device__ void copy_in_raw(const SegCtx& s, const Lane& ln, const uint8_t* srcb) {
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
+  uint16_t* page = const_cast<uint16_t*>(s.src);
+  VecPos pos = vec_pos(s, ln.g);
+  for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
+    uint4 w[U][NCH];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int v = v0 + u * GW;
+      if (v < s.n_vec) {
+        const uint32_t b = (uint32_t)v * (2 * D) + 16 * ln.p;
+#pragma unroll
+        for (int k = 0; k < NCH; k++) w[u][k] = ld_global16(byte_at(srcb, b + 16 * P * k));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (v0 + u * GW < s.n_vec) {
+        const uint32_t b = 2 * (pos.off + 8 * ln.p);
+#pragma unroll
+        for (int k = 0; k < NCH; k++) st_global16(byte_at(page, b + 16 * P * k), w[u][k]);
+      }
+      vec_advance(s, pos);
+    }
   }
 }
 
@@ -894,8 +954,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
   s.heads = (int)p.heads;
   s.heads_magic = p.heads_magic;
   s.n_vec = (int)(p.heads * p.tokens);
-  s.st = p.st;
-  s.sh = p.sh;
+  s.st = p.st32;
+  s.sh = p.sh32;
+  s.walk_dh = p.walk_dh;
+  s.walk_step = p.walk_step;
+  s.walk_wrap = p.walk_wrap;
   const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
 
   // header check (wave-uniform loads)
@@ -913,15 +976,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
   if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = ok ? 0 : 1;
   if (!ok) return;
 
+  const Lane ln = lane_info<D>();
   if (raw_data) {
-    copy_in_raw<D>(s, p.buf + spill);
+    copy_in_raw<D>(s, ln, p.buf + spill);
     return;
   }
   if (codec == C_RAW) {
-    copy_in_raw<D>(s, s.slot + kHeaderBytes);
+    copy_in_raw<D>(s, ln, s.slot + kHeaderBytes);
     return;
   }
-  const Lane ln = lane_info<D>();
   const bool tq = codec == C_TQ3 || codec == C_TQ4;
   if (tq) {
     if (threadIdx.x < 32) {
