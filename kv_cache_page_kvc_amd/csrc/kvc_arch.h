@@ -27,6 +27,15 @@ __device__ __forceinline__ void st_global16(void* p, uint4 v) {
   *(g_u32x4*)p = w;
 }
 
+// x as a binary32 register value: an empty asm the compiler cannot look
+// through, so a later rounding of x (to FP16, say) is not merged into the
+// instruction that produced x (e.g. an FMA fused with the FP16 conversion,
+// which would round once instead of twice).
+__device__ __forceinline__ float materialize_f32(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 // y[e] += c * y[e] of the partner lane, for e < 8, in one v_fmac_f32_dpp
 // each (single rounding; c = +-1 makes the product exact).  Partner of
 // stage Q: lane xor 1 (Q=0), xor 2 (Q=1), xor 8 within the row (Q=2).

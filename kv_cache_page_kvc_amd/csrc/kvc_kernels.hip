@@ -494,7 +494,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
     }
     mn = group_min<LOGP>(mn);
     mx = group_max<LOGP>(mx);
-    const float sig = div_const<TOP>(mx - mn);
+    const float sig = materialize_f32(div_const<TOP>(mx - mn));   // RN to binary32, then to FP16
     const float mh = f16_round(mn), sh = f16_round(sig);
     // +-Inf reach mn/mx and overflow the FP16 metadata; NaN is caught below
     bad = !__builtin_isfinite(mh) || !__builtin_isfinite(sh);

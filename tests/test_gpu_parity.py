@@ -167,6 +167,28 @@ def test_zero_and_tiny_vectors(ctx):
         _roundtrip_case(ctx, wl, ck, cv, 77, ids)
 
 
+def test_uniform_sigma_fp16_midpoint(ctx):
+    """FP16 vectors with max = 8.5859375, min = 0.005615234375: the binary32
+    scale RN(RN(max - min)/15) is exactly the FP16 midpoint 0.572021484375, so
+    the stored FP16 scale must be its even neighbour 0.572265625 (0x3894), as
+    in the oracle -- not a single rounding of an unrounded quotient."""
+    print("[case] uniform sigma FP16 midpoint", flush=True)
+    wl = G.Workload(1, 4, 32, 16, 2, "fp16", "separate", 3)
+    for t in wl.k + wl.v:
+        t[0].fill_(1.0)
+        t[0][..., 0] = 8.5859375
+        t[0][..., 1] = 0.005615234375
+    ids = np.arange(2, dtype=np.int32)
+    _roundtrip_case(ctx, wl, "UNIFORM4", "UNIFORM4", 0, ids)
+    c = kvc.Codec("UNIFORM4", "UNIFORM4", seed=0, layers=1)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, c, np.zeros(1, np.int32))
+    torch.cuda.synchronize()
+    buf = out.cpu().numpy()
+    n_vec = 4 * 16
+    meta = buf[32 + n_vec * 16:32 + n_vec * 20].view(np.uint16).reshape(n_vec, 2)
+    assert np.all(meta[:, 1] == 0x3894)
+
+
 def test_gate_small(ctx):
     """Injected NaN/Inf/|x|>448 values: the exact set of data-raw segments
     per codec, bit-exact raw round trip, +-448 controls stay encoded."""

@@ -372,6 +372,30 @@ def test_uniform_nearest_level(oracle, bits):
                       np.abs(dec) * 2.0 ** -8)
 
 
+def test_uniform_sigma_rounds_to_binary32_then_fp16(oracle):
+    """sigma is a binary32 value, RN(RN(max - min) / 15), that is then
+    rounded to FP16.  With max = 8.5859375 and min = 0.005615234375 (FP16
+    values), max - min = 15 * 0.572021484375 exactly, so sigma is exactly the
+    FP16 midpoint 0.572021484375 and the stored scale is its even neighbour
+    0.572265625 (0x3894).  A single rounding of a slightly different
+    quotient (e.g. an FMA residual step rounded straight to FP16) can land on
+    the odd neighbour 0.57177734375 (0x3893) instead."""
+    from fractions import Fraction
+    hi, lo = np.float16(8.5859375), np.float16(0.005615234375)
+    assert float(hi) == 8.5859375 and float(lo) == 0.005615234375
+    vec = np.full((16, 32), np.float16(1.0)).view(np.uint16)
+    vec[:, 0] = hi.view(np.uint16)
+    vec[:, 1] = lo.view(np.uint16)
+    a = np.float32(hi) - np.float32(lo)
+    assert Fraction(float(a)) == 15 * Fraction(0.572021484375)
+    assert float(a / np.float32(15)) == 0.572021484375
+    slot, st, _ = oracle.encode_segment(vec, oracle.FP16, oracle.UNIFORM4)
+    assert st == oracle.SEG_ENCODED
+    meta = slot[32 + 16 * 16:32 + 16 * 20].view(np.uint16).reshape(16, 2)
+    assert np.all(meta[:, 1] == np.float16(0.572265625).view(np.uint16))
+    assert np.all(meta[:, 0] == lo.view(np.uint16))
+
+
 def test_uniform_constant_vector(oracle):
     vec = np.full((16, 64), 0x4040, np.uint16)            # bf16 3.0
     slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.UNIFORM4)
