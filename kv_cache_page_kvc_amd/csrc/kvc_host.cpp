@@ -328,6 +328,7 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   uint8_t* h = ctx->staging + off;
   SideEntry* se = reinterpret_cast<SideEntry*>(h);
   uint64_t lo = ~0ull, hi = 0;
+  uint32_t stage = 0;
   for (uint32_t l = 0; l < L->layers; l++) {
     const uint16_t* bases[2] = {
         static_cast<const uint16_t*>(L->k_base[l]),
@@ -342,12 +343,14 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
       e.codec = plan.eff[comp][l];
       e.fixed = c->fixed_scales ? c->fixed_scales[2 * l + comp] : 1.0f;
       se[2 * l + comp] = e;
+      if (e.codec != KVC_RAW) stage = std::max<uint32_t>(stage, e.slot_bytes);
       lo = std::min<uint64_t>(lo, (uint64_t)(uintptr_t)e.base);
       hi = std::max<uint64_t>(hi, (uint64_t)(uintptr_t)e.base);
     }
   }
   P->base_lo = lo;
   P->base_hi = hi;
+  P->stage_bytes = stage <= kMaxStageBytes ? stage : 0;   // slot sizes are multiples of 256
   P->num_blocks = (uint32_t)L->num_blocks;
   const size_t pages_off = align_up(sizeof(SideEntry) * 2 * L->layers, kAlign);
   std::memcpy(h + pages_off, pages, sizeof(int32_t) * (size_t)n);

@@ -30,6 +30,8 @@ constexpr float kCellScale = 4.0f;
 constexpr int kCellOffset = 64;               // |z| <= sqrt(256) = 16 -> |4z| <= 64
 constexpr int kCells = 2 * kCellOffset + 1;   // 129
 
+constexpr uint32_t kMaxStageBytes = 32768;    // LDS staging limit per workgroup
+
 struct CellEntry {
   float thr;
   uint32_t base;
@@ -73,6 +75,10 @@ struct CallParams {
   // fewer than 2^31 elements, so every offset actually used is exact.
   uint32_t st32, sh32;                        // stride_token, stride_head
   uint32_t walk_dh, walk_step, walk_wrap;
+  // Encode: bytes of dynamic LDS in which each coded (non-raw) segment's slot
+  // is assembled before it is written out with full-line stores; 0 when
+  // some coded slot exceeds kMaxStageBytes (then codes go straight out).
+  uint32_t stage_bytes;
   uint32_t n_pages, n_layers, heads, tokens;
   uint32_t dtype;                             // kvc_dtype
   uint32_t num_blocks;                        // page ids must be below this (guard)

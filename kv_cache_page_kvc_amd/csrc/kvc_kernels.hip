@@ -390,6 +390,8 @@ __device__ __forceinline__ float sumsq_tree(const float* y) {
 }
 
 // store the codes of one chunk (8 elements) of a vector's code block
+// The stores below go to an image of the slot: the LDS stage when the slot is
+// assembled there, else the output slot itself (the caller's pointer decides).
 template <int D, int BITS>
 __device__ __forceinline__ void store_codes(uint8_t* slot, uint32_t cv, int k, int p, uint32_t lo, uint32_t hi) {
   constexpr int P = Geo<D>::P;
@@ -576,8 +578,9 @@ __device__ __forceinline__ void load_batch(const SegCtx& s, const Lane& ln, int 
 // Encode the segment's vectors.  Returns nonzero if any vector forces the
 // segment raw.
 template <int D, int DT, int C>
-__device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, const LaneSigns<D>& ls,
-                                      const CellEntry* cells) {
+__device__ __forceinline__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed,
+                                                      const LaneSigns<D>& ls, const CellEntry* cells,
+                                                      uint8_t* image) {
   constexpr int GW = Geo<D>::GW, U = Geo<D>::U;
   constexpr int CB = CodecInfo<C>::bits * D / 8;
   const uint32_t meta_blk = kHeaderBytes + (uint32_t)s.n_vec * CB;   // byte offset in the slot
@@ -589,14 +592,16 @@ __device__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fix
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int v = v0 + u * GW;
-      if (v < s.n_vec) bad |= encode_vector<D, DT, C>(w[u], v, ln, s.slot, meta_blk, fixed, ls, cells);
+      if (v < s.n_vec) bad |= encode_vector<D, DT, C>(w[u], v, ln, image, meta_blk, fixed, ls, cells);
     }
   }
   return bad;
 }
 
-// copy a segment from the engine layout into contiguous canonical order
-template <int D>
+// copy a segment from the engine layout into contiguous canonical order; NT:
+// nontemporal stores, for a destination whose lines each store covers whole
+// (the 256-byte aligned spill copies; a slot body starts 32 bytes into a line)
+template <int D, bool NT>
 __device__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
   constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
   uint4 w[U][NCH];
@@ -609,7 +614,10 @@ __device__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
       if (v < s.n_vec) {
         const uint32_t b = (uint32_t)v * (2 * D) + 16 * ln.p;
 #pragma unroll
-        for (int k = 0; k < NCH; k++) st_global16(byte_at(dst, b + 16 * P * k), w[u][k]);
+        for (int k = 0; k < NCH; k++) {
+          if constexpr (NT) st_stream16(byte_at(dst, b + 16 * P * k), w[u][k]);
+          else st_global16(byte_at(dst, b + 16 * P * k), w[u][k]);
+        }
       }
     }
   }
@@ -621,21 +629,25 @@ __device__ __forceinline__ void zero_pad(uint8_t* slot, uint32_t from, uint32_t 
   for (uint32_t b = from + 2 * threadIdx.x; b < to; b += 2 * kThreads) *byte_at(reinterpret_cast<uint16_t*>(slot), b) = 0;
 }
 
-__device__ __forceinline__ void write_header_desc(uint8_t* slot, kvc_segment_desc* desc, uint64_t slot_off,
-                                                  int format, int flags, int status, int dtype, int comp,
-                                                  int d, int n_vec, uint32_t stored, uint64_t spill,
-                                                  uint32_t aux) {
+// the two 16-byte words of a slot header
+struct Header {
   uint4 h0, h1;
-  h0.x = 1u | ((uint32_t)format << 8) | ((uint32_t)flags << 16) | ((uint32_t)(dtype | (comp << 4)) << 24);
-  h0.y = (uint32_t)d | ((uint32_t)n_vec << 16);
-  h0.z = (uint32_t)(n_vec * d * 2);
-  h0.w = stored;
-  h1.x = (uint32_t)spill;
-  h1.y = (uint32_t)(spill >> 32);
-  h1.z = 0;
-  h1.w = aux;
-  reinterpret_cast<uint4*>(slot)[0] = h0;
-  reinterpret_cast<uint4*>(slot)[1] = h1;
+};
+__device__ __forceinline__ Header make_header(int format, int flags, int dtype, int comp, int d, int n_vec,
+                                              uint32_t stored, uint64_t spill, uint32_t aux) {
+  Header h;
+  h.h0.x = 1u | ((uint32_t)format << 8) | ((uint32_t)flags << 16) | ((uint32_t)(dtype | (comp << 4)) << 24);
+  h.h0.y = (uint32_t)d | ((uint32_t)n_vec << 16);
+  h.h0.z = (uint32_t)(n_vec * d * 2);
+  h.h0.w = stored;
+  h.h1.x = (uint32_t)spill;
+  h.h1.y = (uint32_t)(spill >> 32);
+  h.h1.z = 0;
+  h.h1.w = aux;
+  return h;
+}
+__device__ __forceinline__ void write_desc(kvc_segment_desc* desc, uint64_t slot_off, int format, int flags,
+                                           int status, int d, int n_vec, uint32_t stored, uint64_t spill) {
   uint4 d0, d1;
   d0.x = (uint32_t)slot_off;
   d0.y = (uint32_t)(slot_off >> 32);
@@ -648,12 +660,38 @@ __device__ __forceinline__ void write_header_desc(uint8_t* slot, kvc_segment_des
   reinterpret_cast<uint4*>(desc)[0] = d0;
   reinterpret_cast<uint4*>(desc)[1] = d1;
 }
+__device__ __forceinline__ void write_header_desc(uint8_t* slot, kvc_segment_desc* desc, uint64_t slot_off,
+                                                  int format, int flags, int status, int dtype, int comp,
+                                                  int d, int n_vec, uint32_t stored, uint64_t spill,
+                                                  uint32_t aux) {
+  const Header h = make_header(format, flags, dtype, comp, d, n_vec, stored, spill, aux);
+  st_global16(slot, h.h0);
+  st_global16(slot + 16, h.h1);
+  write_desc(desc, slot_off, format, flags, status, d, n_vec, stored, spill);
+}
+
+template <int D, int DT>
+__device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const Lane& ln, float fixed,
+                                            const LaneSigns<D>& ls, const CellEntry* cells, uint8_t* image) {
+  switch (codec) {
+    case C_FP8D: return encode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, ls, cells, image);
+    case C_FP8F: return encode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, ls, cells, image);
+    case C_FP8Y: return encode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, ls, cells, image);
+    case C_INT8: return encode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, ls, cells, image);
+    case C_U3: return encode_segment_vectors<D, DT, C_U3>(s, ln, fixed, ls, cells, image);
+    case C_U4: return encode_segment_vectors<D, DT, C_U4>(s, ln, fixed, ls, cells, image);
+    case C_TQ3: return encode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, ls, cells, image);
+    case C_TQ4: return encode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, ls, cells, image);
+    default: return 0;
+  }
+}
 
 // ------------------------------------------------------------------ encode kernel
 template <int D, int DT>
 __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   __shared__ CellEntry s_cells[kCells];
   __shared__ unsigned long long s_spill;
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
 
   const uint32_t seg = blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
@@ -688,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
 
   const Lane ln = lane_info<D>();
   if (codec == C_RAW) {                                        // raw by policy
-    copy_out_raw<D>(s, ln, s.slot + kHeaderBytes);
+    copy_out_raw<D, false>(s, ln, s.slot + kHeaderBytes);
     zero_pad(s.slot, kHeaderBytes + raw_bytes, slot_bytes);
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY, KVC_SEG_RAW_POLICY, DT, comp, D,
@@ -706,20 +744,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   if (tq) make_lane_signs<D>(p.sign_mask, ln.p, true, ls);
   const float fixed = E.fixed;
 
-  int bad = 0;
-  switch (codec) {
-    case C_FP8D: bad = encode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, ls, s_cells); break;
-    case C_FP8F: bad = encode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, ls, s_cells); break;
-    case C_FP8Y: bad = encode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, ls, s_cells); break;
-    case C_INT8: bad = encode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, ls, s_cells); break;
-    case C_U3: bad = encode_segment_vectors<D, DT, C_U3>(s, ln, fixed, ls, s_cells); break;
-    case C_U4: bad = encode_segment_vectors<D, DT, C_U4>(s, ln, fixed, ls, s_cells); break;
-    case C_TQ3: bad = encode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, ls, s_cells); break;
-    case C_TQ4: bad = encode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, ls, s_cells); break;
-    default: break;
-  }
-  const int any_bad = __syncthreads_or(bad);
-
   int bits = 8, meta = 0;
   switch (codec) {
     case C_U3: case C_TQ3: bits = 3; break;
@@ -729,12 +753,39 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   if (codec == C_FP8Y || codec == C_INT8 || codec == C_U3 || codec == C_U4) meta = 4;
   if (codec == C_TQ3 || codec == C_TQ4) meta = 2;
   const uint32_t payload = (uint32_t)s.n_vec * (uint32_t)(bits * D / 8 + meta);
-  zero_pad(s.slot, kHeaderBytes + payload, slot_bytes);
 
+  // The slot body (codes, metadata, zero padding) is assembled in LDS when it
+  // fits, then written with full-line nontemporal stores; partial-line
+  // nontemporal stores straight from the lanes would not be merged.
+  int bad;
+  const bool staged = slot_bytes <= p.stage_bytes;
+  if (staged) {
+    bad = encode_codec<D, DT>(codec, s, ln, fixed, ls, s_cells, s_stage);
+    zero_pad(s_stage, kHeaderBytes + payload, slot_bytes);
+  } else {
+    bad = encode_codec<D, DT>(codec, s, ln, fixed, ls, s_cells, s.slot);
+    zero_pad(s.slot, kHeaderBytes + payload, slot_bytes);
+  }
+  const int any_bad = __syncthreads_or(bad);
+  const uint32_t aux = codec == C_FP8F ? __float_as_uint(fixed) : 0u;
+  if (staged && !any_bad) {
+    // header + body from unit 0, so every wave store covers whole lines
+    const Header h = make_header(codec, 0, DT, comp, D, s.n_vec, payload, 0, aux);
+    for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += kThreads) {
+      uint4 w = *reinterpret_cast<const uint4*>(s_stage + 16 * u);
+      if (u == 0) w = h.h0;
+      if (u == 1) w = h.h1;
+      st_stream16(s.slot + 16 * u, w);
+    }
+    if (threadIdx.x == 0) write_desc(desc, slot_off, codec, 0, KVC_SEG_ENCODED, D, s.n_vec, payload, 0);
+    return;
+  }
+  if (staged)
+    for (uint32_t u = 2 + threadIdx.x; u < slot_bytes / 16; u += kThreads)
+      st_stream16(s.slot + 16 * u, *reinterpret_cast<const uint4*>(s_stage + 16 * u));
   if (!any_bad) {
     if (threadIdx.x == 0)
-      write_header_desc(s.slot, desc, slot_off, codec, 0, KVC_SEG_ENCODED, DT, comp, D, s.n_vec, payload, 0,
-                        codec == C_FP8F ? __float_as_uint(fixed) : 0u);
+      write_header_desc(s.slot, desc, slot_off, codec, 0, KVC_SEG_ENCODED, DT, comp, D, s.n_vec, payload, 0, aux);
     return;
   }
   // raw because of its data: reserve spill space, copy the source bytes
@@ -743,7 +794,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   __syncthreads();
   const uint64_t off = s_spill;
   const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
-  if (fits) copy_out_raw<D>(s, ln, p.buf + p.slot_region + off);
+  if (fits) copy_out_raw<D, true>(s, ln, p.buf + p.slot_region + off);
   if (threadIdx.x == 0) {
     if (fits)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA, KVC_SEG_RAW_DATA, DT, comp, D, s.n_vec,
@@ -1012,8 +1063,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
 template <int D>
 hipError_t launch_encode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
   dim3 grid((unsigned)nseg), block(kThreads);
-  if (p.dtype == KVC_BF16) hipLaunchKernelGGL((encode_kernel<D, KVC_BF16>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((encode_kernel<D, KVC_FP16>), grid, block, 0, st, p);
+  if (p.dtype == KVC_BF16) hipLaunchKernelGGL((encode_kernel<D, KVC_BF16>), grid, block, p.stage_bytes, st, p);
+  else hipLaunchKernelGGL((encode_kernel<D, KVC_FP16>), grid, block, p.stage_bytes, st, p);
   return hipGetLastError();
 }
 template <int D>
