@@ -20,6 +20,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -68,17 +70,12 @@ def calibrate_copy(gib):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
-def algorithmic_bytes(L, n_pages, H, T, D, prot, kb, vb):
-    """Bytes one launch must move (either direction): every source element
-    (2 B) plus, per segment, the 32-B header and the payload -- b*D/8 code
-    bytes + metadata per vector for encoded segments, 2*D per vector for
-    policy-raw segments."""
-    n_vec = H * T
-    tot = 0
-    for l in range(L):
-        for per_vec in ((2 * D, 2 * D) if l in prot else (kb, vb)):
-            tot += n_pages * (n_vec * 2 * D + 32 + n_vec * per_vec)
-    return tot
+def algorithmic_bytes(desc):
+    """Bytes one launch must move (either direction), from the encode
+    descriptors: per segment the source elements, the 32-byte header and the
+    stored payload (codes and metadata, or the raw bytes of a raw segment)."""
+    return int(desc["original_len"].astype(np.int64).sum() + 32 * len(desc) +
+               desc["stored_len"].astype(np.int64).sum())
 
 
 def cpu_baseline(ks, vs, ids, H, T, D, prot, seed, pages_sample, threads):
@@ -113,6 +110,70 @@ def cpu_baseline(ks, vs, ids, H, T, D, prot, seed, pages_sample, threads):
                       f"encode {t1 - t0:.2f} s + decode {t2 - t1:.2f} s wall"}
 
 
+DEFAULT_WORKLOAD = "tq4_u4_llama3"
+WORKLOADS = {
+    "tq4_u4_llama3": "TurboQuant-4 K + uniform-4 V, Llama-3-8B shape: 32 layers, 8 KV heads, D=128, BF16, "
+                     "separate K/V, 16-token pages, 4096 random pages of an 8192-block pool (64K tokens), "
+                     "layers 0,1,30,31 raw",
+    "fp8_dynamic_small": "FP8 E4M3FN dynamic per-token/head K and V: 2 layers, 8 KV heads, D=128, BF16, "
+                         "separate K/V, 64 pages of 16 tokens",
+    "k16v8_packed": "K raw, V FP8 ({vcodec}), Qwen3-8B shape: 36 layers, 8 KV heads, D=128, FP16, vLLM packed "
+                    "[2048 blocks, 8, 16, 256] (4 sequences x 8192 tokens)",
+    "tq3_u3_dsweep": "TurboQuant-3 K (2% outlier channels x20) + uniform-3 V: 28 layers, 4 KV heads, D={dim}, "
+                     "BF16, separate K/V, 2048 pages (32K tokens)",
+    "int8_fp8_stress": "{codec} K and V with 1% of segments holding NaN/Inf/+-450/+-1000: 32 layers, 8 KV heads, "
+                       "D=128, BF16, separate K/V, 8192 pages (128K tokens), decoded into shuffled pages",
+}
+
+
+def build_workload(args):
+    """Synthetic engine tensors, page lists and codec of one workload."""
+    import torch
+
+    import kv_cache_page_kvc_amd as kvc
+    from kv_cache_page_kvc_amd import inputs
+    name = args.workload
+    cfg = inputs.CONFIGS[name]
+    L, H, T, pool = cfg["layers"], cfg["heads"], cfg["tokens"], cfg["pool"]
+    D = args.dim if name == "tq3_u3_dsweep" else cfg["dim"]
+    td = inputs.torch_dtype(cfg["dtype"])
+    seed = 0
+    w = {"L": L, "H": H, "D": D, "T": T, "pool": pool, "seed": seed, "protected": list(cfg.get("protected", ())),
+         "describe": WORKLOADS[name].format(dim=D, vcodec=args.vcodec, codec=args.codec)}
+    if cfg["layout"] == "separate":
+        ks, vs = inputs.separate_kv(L, pool, T, H, D, td, seed=seed, device="cuda",
+                                    k_kind=cfg.get("k_kind", "lognormal"))
+        w["ks"], w["vs"] = ks, vs
+        w["lay"] = kvc.Layout.separate(ks, vs, H, D, T)
+        dst = ([torch.empty_like(t) for t in ks], [torch.empty_like(t) for t in vs])
+        w["dst"] = dst
+        w["dlay"] = kvc.Layout.separate(dst[0], dst[1], H, D, T)
+    else:
+        pk = inputs.packed_kv(L, pool, H, T, D, td, seed=seed, device="cuda")
+        w["ks"] = pk
+        w["lay"] = kvc.Layout.packed(pk, H, D, T)
+        dst = [torch.empty_like(t) for t in pk]
+        w["dst"] = dst
+        w["dlay"] = kvc.Layout.packed(dst, H, D, T)
+    n = cfg["pages"]
+    ids = inputs.random_page_ids(pool, n, seed=seed) if cfg.get("random_pages") else np.arange(n, dtype=np.int32)
+    w["ids"], w["dst_ids"] = ids, ids
+    fixed = None
+    if name == "k16v8_packed":
+        k, v = "RAW", args.vcodec
+        if v == "FP8_FIXED":      # per-layer scale from the first sequence's V absmax (calibration stand-in)
+            amax = np.array([float(t[:512, :, :, D:].abs().max()) for t in w["ks"]])
+            fixed = np.stack([np.ones(L), amax / 448.0], 1).astype(np.float32)
+    elif name == "int8_fp8_stress":
+        k = v = args.codec
+        inputs.inject_specials(w["ks"], w["vs"], ids, frac=cfg["inject"], seed=seed)
+        w["dst_ids"] = inputs.permutation(n, seed)
+    else:
+        k, v = cfg["k"], cfg["v"]
+    w["codec"] = kvc.Codec(k, v, seed=seed, fixed_scales=fixed, protected_layers=w["protected"], layers=L)
+    return w
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +183,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="GIB",
                     help="only run a plain GIB-GiB device copy (byte-counter calibration)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS),
+                    help="the timed workload (the others are the parity-test shapes, timed on request)")
+    ap.add_argument("--dim", type=int, default=256, choices=[32, 64, 256], help="head_dim for tq3_u3_dsweep")
+    ap.add_argument("--vcodec", default="FP8_FIXED", choices=["FP8_FIXED", "FP8_DYNAMIC"],
+                    help="V codec for k16v8_packed")
+    ap.add_argument("--codec", default="INT8", choices=["INT8", "FP8_DYNAMIC", "FP8_DIRECT"],
+                    help="codec for int8_fp8_stress")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU only (no multi-GPU sharding is built); "
@@ -131,24 +199,14 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
 
-    import numpy as np
     import torch
 
     import kv_cache_page_kvc_amd as kvc
-    from kv_cache_page_kvc_amd import inputs
 
-    cfg = inputs.CONFIGS["tq4_u4_llama3"]
-    L, H, D, T, pool, n = cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], cfg["pages"]
-    prot = list(cfg["protected"])
-    seed = 0
     torch.cuda.set_device(0)
-    ks, vs = inputs.separate_kv(L, pool, T, H, D, torch.bfloat16, seed=seed, device="cuda")
-    dks = [torch.empty_like(t) for t in ks]
-    dvs = [torch.empty_like(t) for t in vs]
-    lay = kvc.Layout.separate(ks, vs, H, D, T)
-    dlay = kvc.Layout.separate(dks, dvs, H, D, T)
-    ids = inputs.random_page_ids(pool, n, seed=seed)
-    codec = kvc.Codec("TQ4", "UNIFORM4", seed=seed, protected_layers=prot, layers=L)
+    w = build_workload(args)
+    L, H, D, T, n = w["L"], w["H"], w["D"], w["T"], len(w["ids"])
+    codec, lay, dlay = w["codec"], w["lay"], w["dlay"]
     slot, spill, bpt = kvc.kvc_plan(lay, codec, n)
     total = slot + spill
     out = torch.empty(total, dtype=torch.uint8, device="cuda")
@@ -160,14 +218,14 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        kvc.kvc_encode_pages(ctx, lay, codec, ids, out.data_ptr(), total, desc.data_ptr(), sh)
+        kvc.kvc_encode_pages(ctx, lay, codec, w["ids"], out.data_ptr(), total, desc.data_ptr(), sh)
         if ev:
             ev[1].record(stream)
-        kvc.kvc_decode_pages(ctx, dlay, codec, out.data_ptr(), total, ids, 0, sh)
+        kvc.kvc_decode_pages(ctx, dlay, codec, out.data_ptr(), total, w["dst_ids"], 0, sh)
         if ev:
             ev[2].record(stream)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] {args.workload}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -187,12 +245,12 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     orig = L * n * 2 * T * H * D * 2
-    kb, vb = D // 2 + 2, D // 2 + 4
-    alg = algorithmic_bytes(L, n, H, T, D, prot, kb, vb)
+    alg = algorithmic_bytes(d)
     enc_gbps, dec_gbps = alg / enc_ms / 1e6, alg / dec_ms / 1e6
     dom = "encode" if enc_ms >= dec_ms else "decode"
     dom_ms = max(enc_ms, dec_ms)
     achieved = alg / dom_ms / 1e6
+    default = args.workload == DEFAULT_WORKLOAD
     result = {
         "metric": "encode+decode GB/s of original KV and % of HBM peak, TurboQuant-4 D=128",
         "value": round(orig / (ms_per_step / 1e3) / 1e9, 2),
@@ -201,11 +259,8 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "TurboQuant-4 K + uniform-4 V, Llama-3-8B shape: 32 layers, 8 KV heads, "
-                               "D=128, BF16, separate K/V, 16-token pages, 4096 random pages of an "
-                               "8192-block pool (64K tokens), layers 0,1,30,31 raw",
-                   "layers": L, "kv_heads": H, "head_dim": D, "tokens_per_page": T, "pages": n,
-                   "pool_blocks": pool, "original_bytes": orig, "parallelism": "none"},
+        "config": {"workload": w["describe"], "layers": L, "kv_heads": H, "head_dim": D, "tokens_per_page": T,
+                   "pages": n, "pool_blocks": w["pool"], "original_bytes": orig, "parallelism": "none"},
         "encode_ms": round(enc_ms, 4), "decode_ms": round(dec_ms, 4),
         "encode_GBps_original": round(orig / enc_ms / 1e6, 1),
         "decode_GBps_original": round(orig / dec_ms / 1e6, 1),
@@ -215,13 +270,16 @@ def main():
         "raw_data_segments": n_raw_data,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(dom)},
+                     "traffic": measured_traffic(dom) if default else None},
     }
+    if not default:
+        result["metric"] = "encode+decode GB/s of original KV and % of HBM peak"
     kvc.kvc_destroy(ctx)
-    if not args.no_cpu_baseline:
+    if default and not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         print(f"[bench] cpu baseline ({threads} threads)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(ks, vs, ids, H, T, D, prot, seed, args.cpu_sample_pages, threads)
+        result["cpu_baseline"] = cpu_baseline(w["ks"], w["vs"], w["ids"], H, T, D, w["protected"], w["seed"],
+                                              args.cpu_sample_pages, threads)
     print(json.dumps(result), flush=True)
 
 
