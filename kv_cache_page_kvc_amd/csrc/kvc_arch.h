@@ -76,6 +76,30 @@ __device__ __forceinline__ float materialize_f32(float x) {
       : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7]) \
       : "v"(c))
 
+// Group minimum and maximum over the lanes of a vector group: lane bits 0, 1
+// (LOGP >= 2) and 3 (LOGP == 3), each step one v_min_f32_dpp / v_max_f32_dpp
+// with the partner lane.  The hardware min/max is used directly (no
+// quieting of signalling NaNs): callers detect NaN separately.  Two wait
+// states separate each step from the previous one (DPP reads of a VGPR
+// written by VALU), five open the block.
+#define KVC_MINMAX_STEP(CTRL)                                                                      \
+  "v_min_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                             \
+  "v_max_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                             \
+  "s_nop 1\n\t"
+template <int LOGP>
+__device__ __forceinline__ void group_minmax_dpp(float& mn, float& mx) {
+  if constexpr (LOGP == 1)
+    asm("s_nop 4\n\t" KVC_MINMAX_STEP("quad_perm:[1,0,3,2]") : "+v"(mn), "+v"(mx));
+  else if constexpr (LOGP == 2)
+    asm("s_nop 4\n\t" KVC_MINMAX_STEP("quad_perm:[1,0,3,2]") KVC_MINMAX_STEP("quad_perm:[2,3,0,1]")
+        : "+v"(mn), "+v"(mx));
+  else
+    asm("s_nop 4\n\t" KVC_MINMAX_STEP("quad_perm:[1,0,3,2]") KVC_MINMAX_STEP("quad_perm:[2,3,0,1]")
+            KVC_MINMAX_STEP("row_ror:8")
+        : "+v"(mn), "+v"(mx));
+}
+#undef KVC_MINMAX_STEP
+
 template <int Q>
 __device__ __forceinline__ void fmac_xlane8(float* y, float c) {
   if constexpr (Q == 0) KVC_FMAC_DPP8("quad_perm:[1,0,3,2]");

@@ -494,8 +494,9 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
       mn = fminf(mn, x[e]);
       mx = fmaxf(mx, x[e]);
     }
-    mn = group_min<LOGP>(mn);
-    mx = group_max<LOGP>(mx);
+    group_minmax_dpp<LOGP>(mn, mx);
+    mn = mn + 0.0f;                      // a zero extreme is +0, whichever zeros the vector holds
+    mx = mx + 0.0f;
     const float sig = materialize_f32(div_const<TOP>(mx - mn));   // RN to binary32, then to FP16
     const float mh = f16_round(mn), sh = f16_round(sig);
     // +-Inf reach mn/mx and overflow the FP16 metadata; NaN is caught below

@@ -388,6 +388,10 @@ static int enc_uniform(const float *x, int d, int bits, uint8_t *codes, uint8_t 
     if (x[i] < mn) mn = x[i];
     if (x[i] > mx) mx = x[i];
   }
+  /* min and max are values, and a zero extreme is +0 whatever the signs of
+   * the zeros in the vector (x + 0 turns -0 into +0, nothing else) */
+  mn = mn + 0.0f;
+  mx = mx + 0.0f;
   float sig = (mx - mn) / (float)top;
   uint16_t mh = kvo_f32_to_f16(mn), sh = kvo_f32_to_f16(sig);
   float mhf = kvo_f16_to_f32(mh), shf = kvo_f16_to_f32(sh);

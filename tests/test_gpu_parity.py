@@ -189,6 +189,26 @@ def test_uniform_sigma_fp16_midpoint(ctx):
     assert np.all(meta[:, 1] == 0x3894)
 
 
+def test_uniform_signed_zero_extremes(ctx):
+    """Vectors whose minimum (or, for all-zero vectors, both extremes) is a
+    zero held as -0 and +0 in either order: the stored FP16 minimum and scale
+    are the same as the oracle's (+0 for a zero extreme)."""
+    print("[case] uniform signed zero extremes", flush=True)
+    for bits in ("UNIFORM4", "UNIFORM3"):
+        wl = G.Workload(1, 4, 64, 16, 4, "fp16", "separate", 5)
+        for t in wl.k + wl.v:
+            t[0].fill_(1.0)
+            t[0].view(torch.int16)[..., 3] = -32768       # -0
+            t[0].view(torch.int16)[..., 40] = 0           # +0
+            t[1].fill_(2.0)
+            t[1].view(torch.int16)[..., 3] = 0
+            t[1].view(torch.int16)[..., 40] = -32768
+            t[2].zero_()
+            t[2].view(torch.int16)[::2, :, 1::3] = -32768
+        ids = np.arange(4, dtype=np.int32)
+        _roundtrip_case(ctx, wl, bits, bits, 0, ids)
+
+
 def test_gate_small(ctx):
     """Injected NaN/Inf/|x|>448 values: the exact set of data-raw segments
     per codec, bit-exact raw round trip, +-448 controls stay encoded."""

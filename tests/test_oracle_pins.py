@@ -396,6 +396,24 @@ def test_uniform_sigma_rounds_to_binary32_then_fp16(oracle):
     assert np.all(meta[:, 0] == lo.view(np.uint16))
 
 
+def test_uniform_zero_extremes_are_plus_zero(oracle):
+    """A zero minimum or maximum is stored as +0 whichever signed zeros the
+    vector holds and in whatever order (min and max are values)."""
+    for first, second in ((0x8000, 0x0000), (0x0000, 0x8000), (0x8000, 0x8000)):
+        vec = np.full((16, 32), np.float16(1.0)).view(np.uint16)
+        vec[:, 3], vec[:, 7] = first, second
+        slot, st, _ = oracle.encode_segment(vec, oracle.FP16, oracle.UNIFORM4)
+        meta = slot[32 + 16 * 16:32 + 16 * 20].view(np.uint16).reshape(16, 2)
+        assert np.all(meta[:, 0] == 0x0000)
+        assert np.all(meta[:, 1] == np.float16(np.float32(1.0) / np.float32(15)).view(np.uint16))
+        zero = np.zeros((16, 32), np.uint16)
+        zero[:, 5] = first
+        zero[:, 9] = second
+        slot, st, _ = oracle.encode_segment(zero, oracle.FP16, oracle.UNIFORM4)
+        meta = slot[32 + 16 * 16:32 + 16 * 20].view(np.uint16).reshape(16, 2)
+        assert np.all(meta == 0)
+
+
 def test_uniform_constant_vector(oracle):
     vec = np.full((16, 64), 0x4040, np.uint16)            # bf16 3.0
     slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.UNIFORM4)
