@@ -371,7 +371,9 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   // exact for every vector index v < 2^16 because heads <= 2^16 (v * heads < 2^32)
   P->heads_magic = ((1ull << 32) + L->kv_heads - 1) / L->kv_heads;
   {
-    const uint32_t H = L->kv_heads, gw = (uint32_t)groups_per_workgroup((int)L->head_dim);
+    const uint32_t seg_bytes = L->kv_heads * L->tokens_per_page * L->head_dim * 2;
+    P->threads = seg_bytes <= kSmallSegmentBytes ? kThreadsSmall : kThreads;
+    const uint32_t H = L->kv_heads, gw = (uint32_t)groups_per_workgroup((int)L->head_dim, (int)P->threads);
     const uint32_t st = (uint32_t)L->stride_token, sh = (uint32_t)L->stride_head;   // < 2^31 (check_layout)
     P->st32 = st;
     P->sh32 = sh;

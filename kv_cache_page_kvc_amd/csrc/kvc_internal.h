@@ -10,14 +10,20 @@
 
 namespace kvc {
 
-constexpr int kThreads = 256;                 // one workgroup per segment
+// One workgroup per segment: 256 threads, or one wave (64 threads) for
+// segments of at most kSmallSegmentBytes source bytes -- a small segment
+// would leave a 256-thread workgroup with little data in flight per wave,
+// while one-wave workgroups keep up to 32 segments in flight per CU.
+constexpr int kThreads = 256;
+constexpr int kThreadsSmall = 64;
+constexpr uint32_t kSmallSegmentBytes = 16384;
 
 // A head vector of D elements is held by a group of lanes_per_vector(D)
-// lanes; a workgroup holds groups_per_workgroup(D) groups, and group g
-// handles vectors g, g + GW, g + 2*GW, ... of a segment (GW = groups per
-// workgroup).
+// lanes; a workgroup of nt threads holds groups_per_workgroup(D, nt)
+// groups, and group g handles vectors g, g + GW, g + 2*GW, ... of a segment
+// (GW = groups per workgroup).
 constexpr int lanes_per_vector(int d) { return d == 32 ? 2 : (d == 64 ? 4 : 8); }
-constexpr int groups_per_workgroup(int d) { return kThreads / lanes_per_vector(d); }
+constexpr int groups_per_workgroup(int d, int nt) { return nt / lanes_per_vector(d); }
 constexpr uint64_t kSlotAlign = KVC_SLOT_ALIGN;
 constexpr uint32_t kHeaderBytes = KVC_HEADER_BYTES;
 
@@ -69,7 +75,8 @@ struct CallParams {
   uint64_t base_lo, base_hi;                  // range of every layer base pointer (guard)
   int64_t sb, st, sh;                         // element strides
   uint64_t heads_magic;                       // ceil(2^32 / heads): t = (v * magic) >> 32 = v / heads
-  // Walking a lane from vector v to v + GW (GW = groups_per_workgroup(D)):
+  uint32_t threads;                           // threads per workgroup: kThreads or kThreadsSmall
+  // Walking a lane from vector v to v + GW (GW = groups_per_workgroup(D, threads)):
   // head h -> h + walk_dh (minus heads on wrap), element offset within the
   // page -> + walk_step (+ walk_wrap on wrap); all modulo 2^32.  A page spans
   // fewer than 2^31 elements, so every offset actually used is exact.

@@ -39,15 +39,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ geometry
-template <int D>
+template <int D, int NT = kThreads>
 struct Geo {
   static constexpr int P = lanes_per_vector(D);               // lanes per vector
   static constexpr int LOGP = P == 2 ? 1 : (P == 4 ? 2 : 3);
   static constexpr int E = D / P;                             // elements per lane
   static constexpr int NCH = E / 8;                           // 16-byte chunks per lane
   static constexpr int GPW = 64 / P;                          // groups per wave
-  static constexpr int GW = groups_per_workgroup(D);          // groups per workgroup
-  static_assert(GW == GPW * (kThreads / 64), "group geometry");
+  static constexpr int GW = groups_per_workgroup(D, NT);      // groups per workgroup
+  static_assert(GW == GPW * (NT / 64), "group geometry");
   // vectors per group whose loads are in flight together: 2 keeps the encode
   // kernel at <= 80 VGPRs for D <= 128 (six waves per SIMD), and more vectors
   // per batch measured slower through the lost occupancy
@@ -561,10 +561,10 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
 
 // the source chunks of vectors v0 + u*GW (u < U) that this lane holds; pos
 // is the lane's position at v0 and ends at v0 + U*GW
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void load_batch(const SegCtx& s, const Lane& ln, int v0, VecPos& pos,
                                            uint4 (&w)[Geo<D>::U][Geo<D>::NCH]) {
-  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D, NT>::GW, U = Geo<D>::U;
 #pragma unroll
   for (int u = 0; u < U; u++) {
     if (v0 + u * GW < s.n_vec) {
@@ -578,18 +578,18 @@ __device__ __forceinline__ void load_batch(const SegCtx& s, const Lane& ln, int 
 
 // Encode the segment's vectors.  Returns nonzero if any vector forces the
 // segment raw.
-template <int D, int DT, int C>
+template <int D, int DT, int C, int NT>
 __device__ __forceinline__ int encode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed,
                                                       const LaneSigns<D>& ls, const CellEntry* cells,
                                                       uint8_t* image) {
-  constexpr int GW = Geo<D>::GW, U = Geo<D>::U;
+  constexpr int GW = Geo<D, NT>::GW, U = Geo<D>::U;
   constexpr int CB = CodecInfo<C>::bits * D / 8;
   const uint32_t meta_blk = kHeaderBytes + (uint32_t)s.n_vec * CB;   // byte offset in the slot
   int bad = 0;
   uint4 w[U][Geo<D>::NCH];
   VecPos pos = vec_pos(s, ln.g);
   for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
-    load_batch<D>(s, ln, v0, pos, w);
+    load_batch<D, NT>(s, ln, v0, pos, w);
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int v = v0 + u * GW;
@@ -599,16 +599,16 @@ __device__ __forceinline__ int encode_segment_vectors(const SegCtx& s, const Lan
   return bad;
 }
 
-// copy a segment from the engine layout into contiguous canonical order; NT:
+// copy a segment from the engine layout into contiguous canonical order; STREAM:
 // nontemporal stores, for a destination whose lines each store covers whole
 // (the 256-byte aligned spill copies; a slot body starts 32 bytes into a line)
-template <int D, bool NT>
+template <int D, int NT, bool STREAM>
 __device__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
-  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D, NT>::GW, U = Geo<D>::U;
   uint4 w[U][NCH];
   VecPos pos = vec_pos(s, ln.g);
   for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
-    load_batch<D>(s, ln, v0, pos, w);
+    load_batch<D, NT>(s, ln, v0, pos, w);
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int v = v0 + u * GW;
@@ -616,7 +616,7 @@ __device__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
         const uint32_t b = (uint32_t)v * (2 * D) + 16 * ln.p;
 #pragma unroll
         for (int k = 0; k < NCH; k++) {
-          if constexpr (NT) st_stream16(byte_at(dst, b + 16 * P * k), w[u][k]);
+          if constexpr (STREAM) st_stream16(byte_at(dst, b + 16 * P * k), w[u][k]);
           else st_global16(byte_at(dst, b + 16 * P * k), w[u][k]);
         }
       }
@@ -626,8 +626,9 @@ __device__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
 
 // zero bytes [from, to) of a slot; from is even (headers and payloads have
 // even sizes) and the padding is shorter than one 256-byte slot unit
+template <int NT>
 __device__ __forceinline__ void zero_pad(uint8_t* slot, uint32_t from, uint32_t to) {
-  for (uint32_t b = from + 2 * threadIdx.x; b < to; b += 2 * kThreads) *byte_at(reinterpret_cast<uint16_t*>(slot), b) = 0;
+  for (uint32_t b = from + 2 * threadIdx.x; b < to; b += 2 * NT) *byte_at(reinterpret_cast<uint16_t*>(slot), b) = 0;
 }
 
 // the two 16-byte words of a slot header
@@ -671,25 +672,25 @@ __device__ __forceinline__ void write_header_desc(uint8_t* slot, kvc_segment_des
   write_desc(desc, slot_off, format, flags, status, d, n_vec, stored, spill);
 }
 
-template <int D, int DT>
+template <int D, int DT, int NT>
 __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const Lane& ln, float fixed,
                                             const LaneSigns<D>& ls, const CellEntry* cells, uint8_t* image) {
   switch (codec) {
-    case C_FP8D: return encode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, ls, cells, image);
-    case C_FP8F: return encode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, ls, cells, image);
-    case C_FP8Y: return encode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, ls, cells, image);
-    case C_INT8: return encode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, ls, cells, image);
-    case C_U3: return encode_segment_vectors<D, DT, C_U3>(s, ln, fixed, ls, cells, image);
-    case C_U4: return encode_segment_vectors<D, DT, C_U4>(s, ln, fixed, ls, cells, image);
-    case C_TQ3: return encode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, ls, cells, image);
-    case C_TQ4: return encode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, ls, cells, image);
+    case C_FP8D: return encode_segment_vectors<D, DT, C_FP8D, NT>(s, ln, fixed, ls, cells, image);
+    case C_FP8F: return encode_segment_vectors<D, DT, C_FP8F, NT>(s, ln, fixed, ls, cells, image);
+    case C_FP8Y: return encode_segment_vectors<D, DT, C_FP8Y, NT>(s, ln, fixed, ls, cells, image);
+    case C_INT8: return encode_segment_vectors<D, DT, C_INT8, NT>(s, ln, fixed, ls, cells, image);
+    case C_U3: return encode_segment_vectors<D, DT, C_U3, NT>(s, ln, fixed, ls, cells, image);
+    case C_U4: return encode_segment_vectors<D, DT, C_U4, NT>(s, ln, fixed, ls, cells, image);
+    case C_TQ3: return encode_segment_vectors<D, DT, C_TQ3, NT>(s, ln, fixed, ls, cells, image);
+    case C_TQ4: return encode_segment_vectors<D, DT, C_TQ4, NT>(s, ln, fixed, ls, cells, image);
     default: return 0;
   }
 }
 
 // ------------------------------------------------------------------ encode kernel
-template <int D, int DT>
-__global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
+template <int D, int DT, int NT>
+__global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   __shared__ CellEntry s_cells[kCells];
   __shared__ unsigned long long s_spill;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
@@ -727,8 +728,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
 
   const Lane ln = lane_info<D>();
   if (codec == C_RAW) {                                        // raw by policy
-    copy_out_raw<D, false>(s, ln, s.slot + kHeaderBytes);
-    zero_pad(s.slot, kHeaderBytes + raw_bytes, slot_bytes);
+    copy_out_raw<D, NT, false>(s, ln, s.slot + kHeaderBytes);
+    zero_pad<NT>(s.slot, kHeaderBytes + raw_bytes, slot_bytes);
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY, KVC_SEG_RAW_POLICY, DT, comp, D,
                         s.n_vec, raw_bytes, 0, 0);
@@ -738,7 +739,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   const bool tq = codec == C_TQ3 || codec == C_TQ4;
   if (tq) {
     const CellEntry* src = p.tables->cells[codec == C_TQ4 ? 1 : 0];
-    for (int q = threadIdx.x; q < kCells; q += kThreads) s_cells[q] = src[q];
+    for (int q = threadIdx.x; q < kCells; q += NT) s_cells[q] = src[q];
     __syncthreads();
   }
   LaneSigns<D> ls;
@@ -761,18 +762,18 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   int bad;
   const bool staged = slot_bytes <= p.stage_bytes;
   if (staged) {
-    bad = encode_codec<D, DT>(codec, s, ln, fixed, ls, s_cells, s_stage);
-    zero_pad(s_stage, kHeaderBytes + payload, slot_bytes);
+    bad = encode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cells, s_stage);
+    zero_pad<NT>(s_stage, kHeaderBytes + payload, slot_bytes);
   } else {
-    bad = encode_codec<D, DT>(codec, s, ln, fixed, ls, s_cells, s.slot);
-    zero_pad(s.slot, kHeaderBytes + payload, slot_bytes);
+    bad = encode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cells, s.slot);
+    zero_pad<NT>(s.slot, kHeaderBytes + payload, slot_bytes);
   }
   const int any_bad = __syncthreads_or(bad);
   const uint32_t aux = codec == C_FP8F ? __float_as_uint(fixed) : 0u;
   if (staged && !any_bad) {
     // header + body from unit 0, so every wave store covers whole lines
     const Header h = make_header(codec, 0, DT, comp, D, s.n_vec, payload, 0, aux);
-    for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += kThreads) {
+    for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT) {
       uint4 w = *reinterpret_cast<const uint4*>(s_stage + 16 * u);
       if (u == 0) w = h.h0;
       if (u == 1) w = h.h1;
@@ -782,7 +783,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
     return;
   }
   if (staged)
-    for (uint32_t u = 2 + threadIdx.x; u < slot_bytes / 16; u += kThreads)
+    for (uint32_t u = 2 + threadIdx.x; u < slot_bytes / 16; u += NT)
       st_stream16(s.slot + 16 * u, *reinterpret_cast<const uint4*>(s_stage + 16 * u));
   if (!any_bad) {
     if (threadIdx.x == 0)
@@ -795,7 +796,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(CallParams p) {
   __syncthreads();
   const uint64_t off = s_spill;
   const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
-  if (fits) copy_out_raw<D, true>(s, ln, p.buf + p.slot_region + off);
+  if (fits) copy_out_raw<D, NT, true>(s, ln, p.buf + p.slot_region + off);
   if (threadIdx.x == 0) {
     if (fits)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA, KVC_SEG_RAW_DATA, DT, comp, D, s.n_vec,
@@ -933,10 +934,10 @@ __device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane&
   }
 }
 
-template <int D, int DT, int C>
+template <int D, int DT, int C, int NT>
 __device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, const LaneSigns<D>& ls,
                                        const float* cent) {
-  constexpr int GW = Geo<D>::GW, U = Geo<D>::U;      // vectors whose codes are in flight together
+  constexpr int GW = Geo<D, NT>::GW, U = Geo<D>::U;      // vectors whose codes are in flight together
   constexpr int CB = CodecInfo<C>::bits * D / 8;
   const uint32_t meta_blk = kHeaderBytes + (uint32_t)s.n_vec * CB;
   uint16_t* page = const_cast<uint16_t*>(s.src);
@@ -955,9 +956,9 @@ __device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fi
 }
 
 // copy a segment from contiguous canonical order into the engine layout
-template <int D>
+template <int D, int NT>
 __device__ void copy_in_raw(const SegCtx& s, const Lane& ln, const uint8_t* srcb) {
-  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D>::GW, U = Geo<D>::U;
+  constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D, NT>::GW, U = Geo<D>::U;
   uint16_t* page = const_cast<uint16_t*>(s.src);
   VecPos pos = vec_pos(s, ln.g);
   for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
@@ -983,8 +984,8 @@ __device__ void copy_in_raw(const SegCtx& s, const Lane& ln, const uint8_t* srcb
   }
 }
 
-template <int D, int DT>
-__global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
+template <int D, int DT, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   __shared__ float s_cent[32];
   const uint32_t seg = blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
@@ -1030,11 +1031,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
 
   const Lane ln = lane_info<D>();
   if (raw_data) {
-    copy_in_raw<D>(s, ln, p.buf + spill);
+    copy_in_raw<D, NT>(s, ln, p.buf + spill);
     return;
   }
   if (codec == C_RAW) {
-    copy_in_raw<D>(s, ln, s.slot + kHeaderBytes);
+    copy_in_raw<D, NT>(s, ln, s.slot + kHeaderBytes);
     return;
   }
   const bool tq = codec == C_TQ3 || codec == C_TQ4;
@@ -1049,30 +1050,44 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(CallParams p) {
   if (tq) make_lane_signs<D>(p.sign_mask, ln.p, false, ls);
   const float fixed = __uint_as_float(h1.w);
   switch (codec) {
-    case C_FP8D: decode_segment_vectors<D, DT, C_FP8D>(s, ln, fixed, ls, s_cent); break;
-    case C_FP8F: decode_segment_vectors<D, DT, C_FP8F>(s, ln, fixed, ls, s_cent); break;
-    case C_FP8Y: decode_segment_vectors<D, DT, C_FP8Y>(s, ln, fixed, ls, s_cent); break;
-    case C_INT8: decode_segment_vectors<D, DT, C_INT8>(s, ln, fixed, ls, s_cent); break;
-    case C_U3: decode_segment_vectors<D, DT, C_U3>(s, ln, fixed, ls, s_cent); break;
-    case C_U4: decode_segment_vectors<D, DT, C_U4>(s, ln, fixed, ls, s_cent); break;
-    case C_TQ3: decode_segment_vectors<D, DT, C_TQ3>(s, ln, fixed, ls, s_cent); break;
-    case C_TQ4: decode_segment_vectors<D, DT, C_TQ4>(s, ln, fixed, ls, s_cent); break;
+    case C_FP8D: decode_segment_vectors<D, DT, C_FP8D, NT>(s, ln, fixed, ls, s_cent); break;
+    case C_FP8F: decode_segment_vectors<D, DT, C_FP8F, NT>(s, ln, fixed, ls, s_cent); break;
+    case C_FP8Y: decode_segment_vectors<D, DT, C_FP8Y, NT>(s, ln, fixed, ls, s_cent); break;
+    case C_INT8: decode_segment_vectors<D, DT, C_INT8, NT>(s, ln, fixed, ls, s_cent); break;
+    case C_U3: decode_segment_vectors<D, DT, C_U3, NT>(s, ln, fixed, ls, s_cent); break;
+    case C_U4: decode_segment_vectors<D, DT, C_U4, NT>(s, ln, fixed, ls, s_cent); break;
+    case C_TQ3: decode_segment_vectors<D, DT, C_TQ3, NT>(s, ln, fixed, ls, s_cent); break;
+    case C_TQ4: decode_segment_vectors<D, DT, C_TQ4, NT>(s, ln, fixed, ls, s_cent); break;
     default: break;
   }
 }
 
 template <int D>
 hipError_t launch_encode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
-  dim3 grid((unsigned)nseg), block(kThreads);
-  if (p.dtype == KVC_BF16) hipLaunchKernelGGL((encode_kernel<D, KVC_BF16>), grid, block, p.stage_bytes, st, p);
-  else hipLaunchKernelGGL((encode_kernel<D, KVC_FP16>), grid, block, p.stage_bytes, st, p);
+  const dim3 grid((unsigned)nseg);
+  if (p.threads == kThreadsSmall) {
+    if (p.dtype == KVC_BF16)
+      hipLaunchKernelGGL((encode_kernel<D, KVC_BF16, kThreadsSmall>), grid, dim3(kThreadsSmall), p.stage_bytes, st, p);
+    else
+      hipLaunchKernelGGL((encode_kernel<D, KVC_FP16, kThreadsSmall>), grid, dim3(kThreadsSmall), p.stage_bytes, st, p);
+  } else {
+    if (p.dtype == KVC_BF16)
+      hipLaunchKernelGGL((encode_kernel<D, KVC_BF16, kThreads>), grid, dim3(kThreads), p.stage_bytes, st, p);
+    else
+      hipLaunchKernelGGL((encode_kernel<D, KVC_FP16, kThreads>), grid, dim3(kThreads), p.stage_bytes, st, p);
+  }
   return hipGetLastError();
 }
 template <int D>
 hipError_t launch_decode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
-  dim3 grid((unsigned)nseg), block(kThreads);
-  if (p.dtype == KVC_BF16) hipLaunchKernelGGL((decode_kernel<D, KVC_BF16>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((decode_kernel<D, KVC_FP16>), grid, block, 0, st, p);
+  const dim3 grid((unsigned)nseg);
+  if (p.threads == kThreadsSmall) {
+    if (p.dtype == KVC_BF16) hipLaunchKernelGGL((decode_kernel<D, KVC_BF16, kThreadsSmall>), grid, dim3(kThreadsSmall), 0, st, p);
+    else hipLaunchKernelGGL((decode_kernel<D, KVC_FP16, kThreadsSmall>), grid, dim3(kThreadsSmall), 0, st, p);
+  } else {
+    if (p.dtype == KVC_BF16) hipLaunchKernelGGL((decode_kernel<D, KVC_BF16, kThreads>), grid, dim3(kThreads), 0, st, p);
+    else hipLaunchKernelGGL((decode_kernel<D, KVC_FP16, kThreads>), grid, dim3(kThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 
