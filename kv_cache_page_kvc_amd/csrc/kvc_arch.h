@@ -27,24 +27,13 @@ __device__ __forceinline__ void st_global16(void* p, uint4 v) {
   *(g_u32x4*)p = w;
 }
 
-// Nontemporal stores, for the encoded slots: written once per call and not
-// read back by this kernel, so they should not displace cached lines (on
-// this GPU they raise the write rate of the encode stream markedly).
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(1))) u32x2 g_u32x2;
-typedef __attribute__((address_space(1))) uint16_t g_u16;
-typedef __attribute__((address_space(1))) uint8_t g_u8;
+// Nontemporal 16-byte store, for encoded slots written whole lines at a time
+// (on gfx950 that raises the write rate of the encode stream; stores of
+// partial lines are not merged and must not use it).
 __device__ __forceinline__ void st_stream16(void* p, uint4 v) {
   u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, (g_u32x4*)p);
 }
-__device__ __forceinline__ void st_stream8(void* p, uint2 v) {
-  u32x2 w = {v.x, v.y};
-  __builtin_nontemporal_store(w, (g_u32x2*)p);
-}
-__device__ __forceinline__ void st_stream4(void* p, uint32_t v) { __builtin_nontemporal_store(v, (g_u32*)p); }
-__device__ __forceinline__ void st_stream2(void* p, uint16_t v) { __builtin_nontemporal_store(v, (g_u16*)p); }
-__device__ __forceinline__ void st_stream1(void* p, uint8_t v) { __builtin_nontemporal_store(v, (g_u8*)p); }
 
 // x as a binary32 register value: an empty asm the compiler cannot look
 // through, so a later rounding of x (to FP16, say) is not merged into the

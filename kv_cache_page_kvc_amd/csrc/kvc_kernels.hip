@@ -102,20 +102,6 @@ __device__ __forceinline__ float group_sum(float v) {   // sum over element bits
   return v;
 }
 template <int LOGP>
-__device__ __forceinline__ float group_min(float v) {
-  if constexpr (LOGP >= 1) v = fminf(v, xlane<0>(v));
-  if constexpr (LOGP >= 2) v = fminf(v, xlane<1>(v));
-  if constexpr (LOGP >= 3) v = fminf(v, xlane<2>(v));
-  return v;
-}
-template <int LOGP>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (LOGP >= 1) v = fmaxf(v, xlane<0>(v));
-  if constexpr (LOGP >= 2) v = fmaxf(v, xlane<1>(v));
-  if constexpr (LOGP >= 3) v = fmaxf(v, xlane<2>(v));
-  return v;
-}
-template <int LOGP>
 __device__ __forceinline__ uint32_t group_or(uint32_t v) {
   if constexpr (LOGP >= 1) v |= xlane_u<0>(v);
   if constexpr (LOGP >= 2) v |= xlane_u<1>(v);
