@@ -920,9 +920,11 @@ __device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane&
   }
 }
 
+// image: the slot's bytes -- staged in LDS, or the encoded buffer itself
 template <int D, int DT, int C, int NT>
-__device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed, const LaneSigns<D>& ls,
-                                       const float* cent) {
+__device__ __forceinline__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fixed,
+                                                       const LaneSigns<D>& ls, const float* cent,
+                                                       const uint8_t* image) {
   constexpr int GW = Geo<D, NT>::GW, U = Geo<D>::U;      // vectors whose codes are in flight together
   constexpr int CB = CodecInfo<C>::bits * D / 8;
   const uint32_t meta_blk = kHeaderBytes + (uint32_t)s.n_vec * CB;
@@ -932,7 +934,7 @@ __device__ void decode_segment_vectors(const SegCtx& s, const Lane& ln, float fi
     VecCodes<D> vc[U];
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (v0 + u * GW < s.n_vec) load_vec_codes<D, C>(s.slot, meta_blk, v0 + u * GW, ln, vc[u]);
+      if (v0 + u * GW < s.n_vec) load_vec_codes<D, C>(image, meta_blk, v0 + u * GW, ln, vc[u]);
 #pragma unroll
     for (int u = 0; u < U; u++) {
       if (v0 + u * GW < s.n_vec) decode_vector<D, DT, C>(vc[u], ln, page, pos.off, fixed, ls, cent);
@@ -971,8 +973,25 @@ __device__ void copy_in_raw(const SegCtx& s, const Lane& ln, const uint8_t* srcb
 }
 
 template <int D, int DT, int NT>
+__device__ __forceinline__ void decode_codec(int codec, const SegCtx& s, const Lane& ln, float fixed,
+                                             const LaneSigns<D>& ls, const float* cent, const uint8_t* image) {
+  switch (codec) {
+    case C_FP8D: decode_segment_vectors<D, DT, C_FP8D, NT>(s, ln, fixed, ls, cent, image); break;
+    case C_FP8F: decode_segment_vectors<D, DT, C_FP8F, NT>(s, ln, fixed, ls, cent, image); break;
+    case C_FP8Y: decode_segment_vectors<D, DT, C_FP8Y, NT>(s, ln, fixed, ls, cent, image); break;
+    case C_INT8: decode_segment_vectors<D, DT, C_INT8, NT>(s, ln, fixed, ls, cent, image); break;
+    case C_U3: decode_segment_vectors<D, DT, C_U3, NT>(s, ln, fixed, ls, cent, image); break;
+    case C_U4: decode_segment_vectors<D, DT, C_U4, NT>(s, ln, fixed, ls, cent, image); break;
+    case C_TQ3: decode_segment_vectors<D, DT, C_TQ3, NT>(s, ln, fixed, ls, cent, image); break;
+    case C_TQ4: decode_segment_vectors<D, DT, C_TQ4, NT>(s, ln, fixed, ls, cent, image); break;
+    default: break;
+  }
+}
+
+template <int D, int DT, int NT>
 __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   __shared__ float s_cent[32];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
   const uint32_t seg = blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
@@ -1000,9 +1019,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   s.walk_wrap = p.walk_wrap;
   const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
 
-  // header check (wave-uniform loads)
-  const uint4 h0 = reinterpret_cast<const uint4*>(s.slot)[0];
-  const uint4 h1 = reinterpret_cast<const uint4*>(s.slot)[1];
+  // A coded slot that fits is read whole into LDS in one round of 16-byte
+  // loads (header and codes together); otherwise the header is read first.
+  const uint32_t slot_bytes = E.slot_bytes;
+  const bool staged = codec != C_RAW && slot_bytes <= p.stage_bytes;
+  uint4 h0, h1;
+  if (staged) {
+    for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT)
+      *reinterpret_cast<uint4*>(s_stage + 16 * u) = ld_stream16(s.slot + 16 * u);
+    __syncthreads();
+    h0 = *reinterpret_cast<const uint4*>(s_stage);
+    h1 = *reinterpret_cast<const uint4*>(s_stage + 16);
+  } else {
+    h0 = ld_global16(s.slot);
+    h1 = ld_global16(s.slot + 16);
+  }
   const int version = h0.x & 0xFF, format = (h0.x >> 8) & 0xFF, flags = (h0.x >> 16) & 0xFF;
   const int dc = (h0.x >> 24) & 0xFF;
   bool ok = version == 1 && dc == (DT | (int)(comp << 4)) && (h0.y & 0xFFFF) == (uint32_t)D &&
@@ -1035,17 +1066,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   LaneSigns<D> ls;
   if (tq) make_lane_signs<D>(p.sign_mask, ln.p, false, ls);
   const float fixed = __uint_as_float(h1.w);
-  switch (codec) {
-    case C_FP8D: decode_segment_vectors<D, DT, C_FP8D, NT>(s, ln, fixed, ls, s_cent); break;
-    case C_FP8F: decode_segment_vectors<D, DT, C_FP8F, NT>(s, ln, fixed, ls, s_cent); break;
-    case C_FP8Y: decode_segment_vectors<D, DT, C_FP8Y, NT>(s, ln, fixed, ls, s_cent); break;
-    case C_INT8: decode_segment_vectors<D, DT, C_INT8, NT>(s, ln, fixed, ls, s_cent); break;
-    case C_U3: decode_segment_vectors<D, DT, C_U3, NT>(s, ln, fixed, ls, s_cent); break;
-    case C_U4: decode_segment_vectors<D, DT, C_U4, NT>(s, ln, fixed, ls, s_cent); break;
-    case C_TQ3: decode_segment_vectors<D, DT, C_TQ3, NT>(s, ln, fixed, ls, s_cent); break;
-    case C_TQ4: decode_segment_vectors<D, DT, C_TQ4, NT>(s, ln, fixed, ls, s_cent); break;
-    default: break;
-  }
+  if (staged) decode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cent, s_stage);
+  else decode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cent, s.slot);
 }
 
 template <int D>
@@ -1068,11 +1090,15 @@ template <int D>
 hipError_t launch_decode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
   const dim3 grid((unsigned)nseg);
   if (p.threads == kThreadsSmall) {
-    if (p.dtype == KVC_BF16) hipLaunchKernelGGL((decode_kernel<D, KVC_BF16, kThreadsSmall>), grid, dim3(kThreadsSmall), 0, st, p);
-    else hipLaunchKernelGGL((decode_kernel<D, KVC_FP16, kThreadsSmall>), grid, dim3(kThreadsSmall), 0, st, p);
+    if (p.dtype == KVC_BF16)
+      hipLaunchKernelGGL((decode_kernel<D, KVC_BF16, kThreadsSmall>), grid, dim3(kThreadsSmall), p.stage_bytes, st, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, KVC_FP16, kThreadsSmall>), grid, dim3(kThreadsSmall), p.stage_bytes, st, p);
   } else {
-    if (p.dtype == KVC_BF16) hipLaunchKernelGGL((decode_kernel<D, KVC_BF16, kThreads>), grid, dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL((decode_kernel<D, KVC_FP16, kThreads>), grid, dim3(kThreads), 0, st, p);
+    if (p.dtype == KVC_BF16)
+      hipLaunchKernelGGL((decode_kernel<D, KVC_BF16, kThreads>), grid, dim3(kThreads), p.stage_bytes, st, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, KVC_FP16, kThreads>), grid, dim3(kThreads), p.stage_bytes, st, p);
   }
   return hipGetLastError();
 }
