@@ -113,6 +113,37 @@ def test_small_grid(ctx, pair, dim, dtype, layout):
                     dst_ids=dst)
 
 
+@pytest.mark.parametrize("layout", ["separate", "packed"])
+@pytest.mark.parametrize("dim", [32, 64, 128, 256])
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}-{p[1]}")
+def test_wide_grid(ctx, pair, dim, layout):
+    """Segments of 32 KiB (16 tokens x 16384/D/16 heads), so the 256-thread
+    workgroups and LDS-staged slots run for every codec pair and head_dim:
+    2 layers (layer 0 protected), 3 of 6 blocks, every segment compared."""
+    dtype = "bf16" if layout == "separate" else "fp16"
+    H = 16384 // dim // 16
+    print(f"[case] wide {pair} D={dim} H={H} {dtype} {layout}", flush=True)
+    wl = G.Workload(2, H, dim, 16, 6, dtype, layout, seed=3 * dim + 1)
+    ids = inputs.random_page_ids(6, 3, seed=dim + 5)
+    fixed = _fixed_scales(2) if "FP8_FIXED" in pair else None
+    dst = inputs.random_page_ids(6, 3, seed=dim + 6)
+    _roundtrip_case(ctx, wl, pair[0], pair[1], seed=99 + dim, page_ids=ids, protected=[0], fixed=fixed,
+                    dst_ids=dst)
+
+
+@pytest.mark.parametrize("heads", [3, 12, 40])
+@pytest.mark.parametrize("pair", [("TQ4", "UNIFORM4"), ("INT8", "FP8_DYNAMIC")], ids=lambda p: f"{p[0]}-{p[1]}")
+def test_odd_head_counts(ctx, pair, heads):
+    """Head counts that do not divide the group count (the per-lane vector
+    walk wraps across tokens): 3 heads (12 KiB segments, one-wave
+    workgroups), 12 (48 KiB) and 40 (160 KiB, slots above the 32 KiB LDS
+    stage, written directly), D=128, every segment compared."""
+    print(f"[case] heads={heads} {pair}", flush=True)
+    wl = G.Workload(2, heads, 128, 16, 5, "bf16", "separate", seed=heads)
+    ids = inputs.random_page_ids(5, 3, seed=heads)
+    _roundtrip_case(ctx, wl, pair[0], pair[1], seed=7 + heads, page_ids=ids, dst_ids=ids[::-1].copy())
+
+
 def test_fp8_dynamic_small_full(ctx):
     """FP8 E4M3FN dynamic workload, 2 layers x 8 heads x D128 BF16, 64 pages:
     all 256 segments."""
