@@ -491,6 +491,18 @@ static void dec_uniform(const uint8_t *codes, const uint8_t *meta, int d, int bi
 /* Segments                                                                 */
 /* ------------------------------------------------------------------------ */
 
+/* [OKV-SF "Ownership, storage and GDS"] a segment carries a CRC32.  The
+ * common CRC-32 (reflected polynomial 0xEDB88320, register preset to all
+ * ones, result complemented), bit by bit. */
+uint32_t kvo_crc32(const uint8_t *p, size_t n) {
+  uint32_t c = 0xFFFFFFFFu;
+  for (size_t i = 0; i < n; i++) {
+    c ^= p[i];
+    for (int k = 0; k < 8; k++) c = (c >> 1) ^ (0xEDB88320u & (0u - (c & 1u)));
+  }
+  return c ^ 0xFFFFFFFFu;
+}
+
 static void write_header(uint8_t *slot, int format, int flags, int dtype, int component,
                          int d, int n_vec, uint32_t stored, uint64_t spill_off, uint32_t aux) {
   memset(slot, 0, HEADER_BYTES);
@@ -507,17 +519,26 @@ static void write_header(uint8_t *slot, int format, int flags, int dtype, int co
   put_u32(slot + 28, aux);
 }
 
+/* the CRC32 of the stored bytes goes into the header (offset 24), with flag
+ * bit 3 set; the spill offset is not covered, so it can be patched later */
+static void set_crc(uint8_t *slot, const uint8_t *stored, size_t n) {
+  slot[2] |= KVO_FLAG_CRC32;
+  put_u32(slot + 24, kvo_crc32(stored, n));
+}
+
 int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
                        int component, int codec, int is_protected,
                        float fixed_scale, uint64_t seed,
-                       uint8_t *slot, uint8_t *spill, uint64_t spill_offset) {
+                       uint8_t *slot, uint8_t *spill, uint64_t spill_offset, int flags) {
   int eff = kvo_effective_codec(codec, d, n_vec, is_protected);
+  const int with_crc = flags & KVO_ENC_CRC32;
   size_t orig = (size_t)n_vec * (size_t)d * 2;
   size_t slot_bytes = kvo_slot_bytes(eff, d, n_vec);
   memset(slot, 0, slot_bytes);
   if (eff == KVO_RAW) {
     write_header(slot, KVO_RAW, 1, dtype, component, d, n_vec, (uint32_t)orig, 0, 0);
     for (size_t i = 0; i < (size_t)n_vec * (size_t)d; i++) put_u16(slot + HEADER_BYTES + 2 * i, vec[i]);
+    if (with_crc) set_crc(slot, slot + HEADER_BYTES, orig);
     return KVO_SEG_RAW_POLICY;
   }
 
@@ -571,12 +592,16 @@ int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
   if (raw) {
     memset(slot, 0, slot_bytes);
     write_header(slot, KVO_RAW, 2, dtype, component, d, n_vec, (uint32_t)orig, spill_offset, 0);
-    if (spill)
+    if (spill) {
       for (size_t i = 0; i < (size_t)n_vec * (size_t)d; i++) put_u16(spill + 2 * i, vec[i]);
+      if (with_crc) set_crc(slot, spill, orig);
+    }
     return KVO_SEG_RAW_DATA;
   }
-  write_header(slot, eff, 0, dtype, component, d, n_vec, (uint32_t)((size_t)n_vec * (cb + mb)), 0,
+  const size_t stored = (size_t)n_vec * (cb + mb);
+  write_header(slot, eff, 0, dtype, component, d, n_vec, (uint32_t)stored, 0,
                eff == KVO_FP8_FIXED ? f2u(fixed_scale) : 0);
+  if (with_crc) set_crc(slot, slot + HEADER_BYTES, stored);
   return KVO_SEG_ENCODED;
 }
 
@@ -587,6 +612,12 @@ int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
   if ((slot[3] & 15) != dtype || get_u16(slot + 4) != d || get_u16(slot + 6) != n_vec) return -1;
   if (get_u32(slot + 8) != (uint32_t)(n_vec * d * 2)) return -1;
   size_t nel = (size_t)n_vec * (size_t)d;
+  /* a CRC32, when present, is checked before anything is decoded */
+  if (flags & KVO_FLAG_CRC32) {
+    const uint8_t *stored = (flags & 2) ? buf_base + get_u64(slot + 16) : slot + HEADER_BYTES;
+    if ((flags & 2) && (flags & 4)) return -1;
+    if (kvo_crc32(stored, get_u32(slot + 12)) != get_u32(slot + 24)) return -2;
+  }
   if (flags & 2) {                                   /* raw, spilled */
     if (flags & 4) return -1;                        /* spill capacity was exhausted */
     const uint8_t *src = buf_base + get_u64(slot + 16);

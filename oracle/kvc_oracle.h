@@ -53,6 +53,11 @@ enum {
 enum { KVO_BF16 = 1, KVO_FP16 = 2 };
 /* segment status returned by the encoder */
 enum { KVO_SEG_ENCODED = 0, KVO_SEG_RAW_POLICY = 1, KVO_SEG_RAW_DATA = 2 };
+/* encode option: compute a CRC32 of the stored bytes; header flag bit 3 */
+enum { KVO_ENC_CRC32 = 1, KVO_FLAG_CRC32 = 8 };
+
+/* CRC-32 (reflected polynomial 0xEDB88320, preset and final complement) */
+uint32_t kvo_crc32(const uint8_t *p, size_t n);
 
 /* ---- number formats (bit-level definitions) ---- */
 float    kvo_bf16_to_f32(uint16_t h);
@@ -98,15 +103,18 @@ int    kvo_effective_codec(int codec, int d, int n_vec, int is_protected);
  * slot: kvo_slot_bytes(effective codec) bytes, fully written (header, payload,
  * zero padding).  For a data-dependent RAW segment the slot carries only the
  * header (payload zero) and the raw bytes go to spill (n_vec*d*2 bytes, if
- * spill != NULL); spill_offset is written into the header.
+ * spill != NULL); spill_offset is written into the header.  flags:
+ * KVO_ENC_CRC32 stores the CRC32 of the stored bytes (the payload, or the raw
+ * bytes in the slot or the spill) in the header.
  * Returns KVO_SEG_*. */
 int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
                        int component, int codec, int is_protected,
                        float fixed_scale, uint64_t seed,
-                       uint8_t *slot, uint8_t *spill, uint64_t spill_offset);
+                       uint8_t *slot, uint8_t *spill, uint64_t spill_offset, int flags);
 /* Decode one slot into n_vec*d output bit patterns (canonical order).
  * buf_base is the start of the buffer the spill offsets refer to.
- * Returns 0 on success, -1 on a malformed header. */
+ * Returns 0 on success, -1 on a malformed header, -2 when the segment
+ * carries a CRC32 that its stored bytes do not match. */
 int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
                        int dtype, int d, int n_vec, uint64_t seed,
                        uint16_t *out);

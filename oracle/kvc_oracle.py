@@ -92,7 +92,10 @@ def lib():
         L.kvo_encode_segment.restype = ctypes.c_int
         L.kvo_encode_segment.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_float, ctypes.c_uint64, P, P, ctypes.c_uint64]
+                                         ctypes.c_float, ctypes.c_uint64, P, P, ctypes.c_uint64,
+                                         ctypes.c_int]
+        L.kvo_crc32.restype = ctypes.c_uint32
+        L.kvo_crc32.argtypes = [P, ctypes.c_size_t]
         L.kvo_decode_segment.restype = ctypes.c_int
         L.kvo_decode_segment.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_uint64, P]
@@ -213,10 +216,25 @@ def effective_codec(codec, d, n_vec, is_protected):
 
 
 # ---------------------------------------------------------------- segments
+ENC_CRC32 = 1          # encode option: CRC32 of the stored bytes in the header
+FLAG_CRC32 = 8         # header flag bit
+
+
+class ChecksumError(ValueError):
+    """A segment's stored bytes do not match its CRC32."""
+
+
+def crc32(data) -> int:
+    b = np.ascontiguousarray(np.frombuffer(bytes(data), np.uint8) if isinstance(data, (bytes, bytearray))
+                             else data, dtype=np.uint8)
+    return int(lib().kvo_crc32(_ptr(b), b.size))
+
+
 def encode_segment(vec: np.ndarray, dtype: int, codec: int, component: int = 0,
                    is_protected: bool = False, fixed_scale: float = 1.0, seed: int = 0,
-                   spill_offset: int = 0):
-    """vec: uint16 [n_vec, D] source bits.  Returns (slot uint8, status, raw uint8|None)."""
+                   spill_offset: int = 0, crc: bool = False):
+    """vec: uint16 [n_vec, D] source bits.  Returns (slot uint8, status, raw uint8|None).
+    crc: store the CRC32 of the stored bytes in the header."""
     vec = np.ascontiguousarray(vec, dtype=np.uint16)
     n_vec, d = vec.shape
     eff = effective_codec(codec, d, n_vec, is_protected)
@@ -225,7 +243,7 @@ def encode_segment(vec: np.ndarray, dtype: int, codec: int, component: int = 0,
     st = lib().kvo_encode_segment(_ptr(vec), dtype, d, n_vec, component, codec,
                                   int(bool(is_protected)), ctypes.c_float(fixed_scale),
                                   ctypes.c_uint64(seed), _ptr(slot), _ptr(spill),
-                                  ctypes.c_uint64(spill_offset))
+                                  ctypes.c_uint64(spill_offset), ENC_CRC32 if crc else 0)
     if st < 0:
         raise ValueError("oracle encode failed")
     return slot, st, (spill if st == SEG_RAW_DATA else None)
@@ -236,6 +254,8 @@ def decode_segment(slot: np.ndarray, buf_base, dtype: int, d: int, n_vec: int, s
     out = np.zeros((n_vec, d), np.uint16)
     base = _ptr(buf_base) if buf_base is not None else None
     rc = lib().kvo_decode_segment(_ptr(slot), base, dtype, d, n_vec, ctypes.c_uint64(seed), _ptr(out))
+    if rc == -2:
+        raise ChecksumError("oracle decode: CRC32 mismatch")
     if rc != 0:
         raise ValueError("oracle decode: malformed segment header")
     return out
@@ -303,7 +323,7 @@ def plan(L, H, D, T, codec_k, codec_v, protected, n_pages):
 
 
 def encode_pages(lay: HostLayout, codec_k, codec_v, seed, page_ids, fixed_scales=None,
-                 protected=None, segments=None, threads=1):
+                 protected=None, segments=None, threads=1, crc=False):
     """Oracle encode of a whole call.
 
     Returns (buf, statuses, offsets, slot_region_bytes).  ``buf`` holds the
@@ -325,7 +345,7 @@ def encode_pages(lay: HostLayout, codec_k, codec_v, seed, page_ids, fixed_scales
         prot = bool(protected[l]) if protected is not None else False
         fs = float(fixed_scales[l][c]) if fixed_scales is not None else 1.0
         vec = lay.gather(l, c, int(page_ids[i]))
-        return encode_segment(vec, lay.dtype, codec_k if c == 0 else codec_v, c, prot, fs, seed)
+        return encode_segment(vec, lay.dtype, codec_k if c == 0 else codec_v, c, prot, fs, seed, crc=crc)
 
     if threads > 1:
         with ThreadPoolExecutor(threads) as ex:

@@ -539,3 +539,58 @@ def test_int8_round_half_to_even(oracle):
     assert st == oracle.SEG_ENCODED
     assert list(slot[32:32 + len(vals)].view(np.int8)) == [127, 62, 64, -62, 0, 2, 2, 0]
     assert slot[32 + 16 * 32:36 + 16 * 32].view(np.float32)[0] == 1.0
+
+
+# ------------------------------------------------------------ CRC32
+def test_crc32_check_value(oracle):
+    g = json.load(open(os.path.join(GOLDEN, "crc32_check.json")))
+    assert oracle.crc32(g["input_ascii"].encode()) == int(g["crc32"], 16)
+
+
+def test_crc32_matches_zlib(oracle):
+    """The library routine zlib.crc32 computes the same CRC-32."""
+    import zlib
+    rng = np.random.default_rng(12)
+    for n in (0, 1, 2, 3, 15, 16, 17, 255, 4096, 8480, 33000):
+        b = rng.integers(0, 256, n, dtype=np.uint8)
+        assert oracle.crc32(b) == zlib.crc32(b.tobytes())
+
+
+@pytest.mark.parametrize("codec", ["TQ4", "UNIFORM3", "INT8", "FP8_DYNAMIC", "RAW"])
+def test_segment_crc32(oracle, codec):
+    """With the CRC option the header carries flag 8 and the CRC32 of the
+    stored bytes (payload, raw slot body, or spilled raw bytes); a flipped
+    stored byte makes decode fail; without it the field stays 0."""
+    import zlib
+    c = getattr(oracle, codec if codec != "RAW" else "RAW")
+    rng = np.random.default_rng(5)
+    vec = _bits(rng.standard_normal((16, 64)).astype(np.float32), oracle.BF16)
+    slot, st, raw = oracle.encode_segment(vec, oracle.BF16, c, crc=True)
+    stored = int(slot[12:16].view(np.uint32)[0])
+    assert slot[2] & oracle.FLAG_CRC32
+    assert int(slot[24:28].view(np.uint32)[0]) == zlib.crc32(slot[32:32 + stored].tobytes())
+    out = oracle.decode_segment(slot, None, oracle.BF16, 64, 16)
+    bad = slot.copy()
+    bad[32 + stored // 2] ^= 0x10
+    with pytest.raises(oracle.ChecksumError):
+        oracle.decode_segment(bad, None, oracle.BF16, 64, 16)
+    plain, st2, _ = oracle.encode_segment(vec, oracle.BF16, c)
+    assert not (plain[2] & oracle.FLAG_CRC32) and not plain[24:28].any()
+    np.testing.assert_array_equal(out, oracle.decode_segment(plain, None, oracle.BF16, 64, 16))
+
+
+def test_segment_crc32_spilled(oracle):
+    """A segment raw because of its data: the CRC covers the spilled bytes."""
+    import zlib
+    vec = np.full((16, 32), 0x3F80, np.uint16)
+    vec[3, 4] = 0x7FC0                                    # NaN
+    slot, st, raw = oracle.encode_segment(vec, oracle.BF16, oracle.TQ4, crc=True)
+    assert st == oracle.SEG_RAW_DATA and slot[2] & oracle.FLAG_CRC32
+    assert int(slot[24:28].view(np.uint32)[0]) == zlib.crc32(raw.tobytes())
+    buf = np.concatenate([slot, raw])
+    slot2 = slot.copy()
+    slot2[16:24] = np.frombuffer(np.uint64(slot.size).tobytes(), np.uint8)
+    np.testing.assert_array_equal(oracle.decode_segment(slot2, buf, oracle.BF16, 32, 16), vec)
+    buf[slot.size + 7] ^= 1
+    with pytest.raises(oracle.ChecksumError):
+        oracle.decode_segment(slot2, buf, oracle.BF16, 32, 16)
