@@ -170,7 +170,8 @@ def build_workload(args):
         w["dst_ids"] = inputs.permutation(n, seed)
     else:
         k, v = cfg["k"], cfg["v"]
-    w["codec"] = kvc.Codec(k, v, seed=seed, fixed_scales=fixed, protected_layers=w["protected"], layers=L)
+    w["codec"] = kvc.Codec(k, v, seed=seed, fixed_scales=fixed, protected_layers=w["protected"], layers=L,
+                           crc=args.crc)
     return w
 
 
@@ -190,6 +191,8 @@ def main():
                     help="V codec for k16v8_packed")
     ap.add_argument("--codec", default="INT8", choices=["INT8", "FP8_DYNAMIC", "FP8_DIRECT"],
                     help="codec for int8_fp8_stress")
+    ap.add_argument("--crc", action="store_true",
+                    help="store a CRC32 per segment on encode and verify it on decode")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU only (no multi-GPU sharding is built); "
@@ -250,7 +253,7 @@ def main():
     dom = "encode" if enc_ms >= dec_ms else "decode"
     dom_ms = max(enc_ms, dec_ms)
     achieved = alg / dom_ms / 1e6
-    default = args.workload == DEFAULT_WORKLOAD
+    default = args.workload == DEFAULT_WORKLOAD and not args.crc
     result = {
         "metric": "encode+decode GB/s of original KV and % of HBM peak, TurboQuant-4 D=128",
         "value": round(orig / (ms_per_step / 1e3) / 1e9, 2),
@@ -260,7 +263,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w["describe"], "layers": L, "kv_heads": H, "head_dim": D, "tokens_per_page": T,
-                   "pages": n, "pool_blocks": w["pool"], "original_bytes": orig, "parallelism": "none"},
+                   "pages": n, "pool_blocks": w["pool"], "original_bytes": orig, "crc32": bool(args.crc),
+                   "parallelism": "none"},
         "encode_ms": round(enc_ms, 4), "decode_ms": round(dec_ms, 4),
         "encode_GBps_original": round(orig / enc_ms / 1e6, 1),
         "decode_GBps_original": round(orig / dec_ms / 1e6, 1),

@@ -41,7 +41,13 @@
  *  Header (little-endian): u8 version=1, u8 format (codec of the stored
  *  bytes, KVC_RAW when raw), u8 flags (KVC_FLAG_*), u8 dtype | component<<4,
  *  u16 head_dim, u16 n_vec, u32 original_len, u32 stored_len,
- *  u64 spill_offset, u32 crc32 (0: reserved), u32 aux (FP8_FIXED scale bits).
+ *  u64 spill_offset, u32 crc32, u32 aux (FP8_FIXED scale bits).
+ *  crc32 (flag KVC_FLAG_CRC32, requested with KVC_CODEC_CRC32) is the CRC-32
+ *  of zlib -- reflected polynomial 0xEDB88320, register preset to
+ *  0xFFFFFFFF, result complemented -- of the stored_len stored bytes (the
+ *  codes and metadata, or the raw bytes wherever they are kept) [OKV-SF
+ *  "Ownership, storage and GDS": each segment carries a CRC32]; 0 without
+ *  the flag.
  *  Codes are packed LSB-first (element i at bits [b*i, b*i+b) of the vector's
  *  code block); metadata per vector: FP32 scale (FP8_DYNAMIC, INT8), FP16 min
  *  + FP16 scale (UNIFORM*), FP16 norm (TQ*).
@@ -60,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1u
+#define KVC_ABI_VERSION 2u
 #define KVC_FORMAT_VERSION 1u
 #define KVC_SLOT_ALIGN 256u
 #define KVC_HEADER_BYTES 32u
@@ -129,12 +135,18 @@ typedef enum {
  * [ceil(layers/8)] (bit l%8 of byte l/8), or NULL; protected layers stay
  * exact [OKV-SF "FP8 and TurboQuant": the first and last two layers of each
  * pipeline stage remain exact -- the caller marks them].  seed: rotation
- * seed of the TurboQuant sign generator (SplitMix64, version 1). */
+ * seed of the TurboQuant sign generator (SplitMix64, version 1).  flags:
+ * KVC_CODEC_CRC32 makes encode store each segment's CRC32 (KVC_FLAG_CRC32)
+ * and makes decode verify it before it writes the page; other bits and
+ * `reserved` must be 0 (else KVC_E_ARG). */
+#define KVC_CODEC_CRC32 1u
 typedef struct {
   uint32_t k, v;                       /* kvc_codec_id */
   uint64_t seed;
   const float *fixed_scales;
   const uint8_t *protected_layers;
+  uint32_t flags;                      /* KVC_CODEC_* */
+  uint32_t reserved;
 } kvc_codec;
 
 /* Segment status, written by encode into kvc_segment_desc.status */
@@ -147,7 +159,7 @@ enum {
                              nothing was read or written for this segment (never expected) */
 };
 /* header / descriptor flags */
-enum { KVC_FLAG_RAW_POLICY = 1, KVC_FLAG_RAW_DATA = 2, KVC_FLAG_CAPACITY = 4 };
+enum { KVC_FLAG_RAW_POLICY = 1, KVC_FLAG_RAW_DATA = 2, KVC_FLAG_CAPACITY = 4, KVC_FLAG_CRC32 = 8 };
 
 /* One per segment, written by encode on the device (32 B).  Offsets are
  * relative to the start of the encode output buffer. */
@@ -157,7 +169,7 @@ typedef struct {
   uint32_t stored_len;    /* payload bytes (codes + metadata, or raw bytes) */
   uint32_t original_len;  /* n_vec * D * element size */
   uint8_t version, format, flags, status;
-  uint32_t crc32;         /* 0: reserved */
+  uint32_t crc32;         /* the header's crc32 (0 without KVC_FLAG_CRC32) */
 } kvc_segment_desc;
 
 /* Create a context on HIP device `hip_device` with a retained device arena
@@ -179,6 +191,7 @@ kvc_status kvc_destroy(kvc_ctx *ctx);
  *    capacity get KVC_SEG_CAPACITY;
  *  bytes_per_token: slot bytes per token of all layers, the encoded size a
  *    host pool reports [HIQ "Integrating the codec": get_size_per_token].
+ * The CRC option changes no size (the CRC lives in the header).
  * Any output pointer may be NULL. */
 kvc_status kvc_plan(const kvc_layout *layout, const kvc_codec *codec, uint32_t n_pages,
                     size_t *slot_bytes, size_t *spill_bytes_suggested,
@@ -209,9 +222,12 @@ kvc_status kvc_encode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_co
  * enqueued [OKV-SF "Ownership, storage and GDS"]).  Raw segments are copied
  * bit-exactly.  seg_status (device [layers*n_pages*2] u8, may be NULL)
  * receives 0 per decoded segment, 1 when the slot header does not match
- * the geometry/codec or the segment was not stored (KVC_SEG_CAPACITY), or 2
- * when the kernel's range check on its staged descriptor failed; in the last
- * two cases the destination page is left unchanged.  Enqueued on `stream`. */
+ * the geometry/codec (including its stored length and whether it carries a
+ * CRC32, which must agree with codec->flags) or the segment was not stored
+ * (KVC_SEG_CAPACITY), 2 when the kernel's range check on its staged
+ * descriptor failed, or 3 when the stored bytes do not match the header's
+ * CRC32 (KVC_CODEC_CRC32 only); in cases 1-3 the destination page is left
+ * unchanged.  Enqueued on `stream`. */
 kvc_status kvc_decode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
                             const void *in, size_t in_bytes,
                             const int32_t *dst_page_ids, uint32_t n_pages,

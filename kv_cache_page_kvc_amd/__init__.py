@@ -15,7 +15,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvc.so")
 
-KVC_ABI_VERSION = 1
+KVC_ABI_VERSION = 2
 KVC_SLOT_ALIGN = 256
 KVC_HEADER_BYTES = 32
 KVC_DEFAULT_WORKSPACE = 64 << 20
@@ -33,7 +33,11 @@ CODECS = {"RAW": 0, "FP8_DIRECT": 1, "FP8_FIXED": 2, "FP8_DYNAMIC": 3, "INT8": 4
           "UNIFORM3": 5, "UNIFORM4": 6, "TQ3": 7, "TQ4": 8}
 # segment status / flags
 KVC_SEG_ENCODED, KVC_SEG_RAW_POLICY, KVC_SEG_RAW_DATA, KVC_SEG_CAPACITY, KVC_SEG_GUARD = range(5)
-KVC_FLAG_RAW_POLICY, KVC_FLAG_RAW_DATA, KVC_FLAG_CAPACITY = 1, 2, 4
+KVC_FLAG_RAW_POLICY, KVC_FLAG_RAW_DATA, KVC_FLAG_CAPACITY, KVC_FLAG_CRC32 = 1, 2, 4, 8
+# kvc_codec.flags
+KVC_CODEC_CRC32 = 1
+# decode seg_status values
+DEC_OK, DEC_HEADER, DEC_GUARD, DEC_CRC = 0, 1, 2, 3
 
 
 class KvcError(RuntimeError):
@@ -56,7 +60,8 @@ class kvc_layout(ctypes.Structure):
 class kvc_codec(ctypes.Structure):
     _fields_ = [("k", ctypes.c_uint32), ("v", ctypes.c_uint32), ("seed", ctypes.c_uint64),
                 ("fixed_scales", ctypes.POINTER(ctypes.c_float)),
-                ("protected_layers", ctypes.POINTER(ctypes.c_uint8))]
+                ("protected_layers", ctypes.POINTER(ctypes.c_uint8)),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class kvc_segment_desc(ctypes.Structure):
@@ -166,7 +171,7 @@ def _dtype_code(t):
 class Codec:
     """Owns a kvc_codec and its host arrays."""
 
-    def __init__(self, k, v, seed=0, fixed_scales=None, protected_layers=None, layers=None):
+    def __init__(self, k, v, seed=0, fixed_scales=None, protected_layers=None, layers=None, crc=False):
         self._fs = None
         self._prot = None
         fs_ptr = None
@@ -182,7 +187,7 @@ class Codec:
             self._prot = bm
             prot_ptr = bm.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
         self.c = kvc_codec(CODECS[k] if isinstance(k, str) else k, CODECS[v] if isinstance(v, str) else v,
-                           seed, fs_ptr, prot_ptr)
+                           seed, fs_ptr, prot_ptr, KVC_CODEC_CRC32 if crc else 0, 0)
 
 
 def _check(status, where):

@@ -114,7 +114,34 @@ void lloyd_max(int n, std::vector<double>& lev) {
   }
 }
 
+// CRC-32 tables (zlib's CRC: reflected polynomial 0xEDB88320), built from
+// the bitwise definition; see CrcTables for how the kernels use them.
+void build_crc_tables(CrcTables& c) {
+  for (uint32_t b = 0; b < 256; b++) {
+    uint32_t r = b;
+    for (int i = 0; i < 8; i++) r = (r >> 1) ^ (0xEDB88320u & (0u - (r & 1u)));
+    c.t[0][b] = r;
+  }
+  auto zero_byte = [&c](uint32_t r) { return (r >> 8) ^ c.t[0][r & 0xFF]; };
+  for (int k = 1; k < 4; k++)
+    for (int b = 0; b < 256; b++) c.t[k][b] = zero_byte(c.t[k - 1][b]);
+  for (int k = 0; k < 4; k++)
+    for (int b = 0; b < 256; b++) {
+      uint32_t r = c.t[k][b];
+      for (uint32_t i = 0; i < kCrcGapBytes; i++) r = zero_byte(r);
+      c.tg[k][b] = r;
+    }
+  for (int lvl = 0; lvl < 6; lvl++)
+    for (int i = 0; i < 8; i++)
+      for (uint32_t v = 0; v < 16; v++) {
+        uint32_t r = v << (4 * i);
+        for (int n = 0; n < (16 << lvl); n++) r = zero_byte(r);
+        c.sh[lvl][i][v] = r;
+      }
+}
+
 void build_tables(Tables& t) {
+  build_crc_tables(t.crc);
   for (int which = 0; which < 2; which++) {
     const int bits = which ? 4 : 3, n = 1 << bits;
     std::vector<double> lev;
@@ -190,6 +217,7 @@ kvc_status check_layout(const kvc_layout* L) {
 
 kvc_status check_codec(const kvc_layout* L, const kvc_codec* c) {
   if (!c || c->k > KVC_TQ4 || c->v > KVC_TQ4) return KVC_E_ARG;
+  if ((c->flags & ~KVC_CODEC_CRC32) || c->reserved) return KVC_E_ARG;
   if (c->k == KVC_FP8_FIXED || c->v == KVC_FP8_FIXED) {
     if (!c->fixed_scales) return KVC_E_ARG;
     for (uint32_t l = 0; l < L->layers; l++)
@@ -383,6 +411,7 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   }
   P->tokens = L->tokens_per_page;
   P->dtype = L->dtype;
+  P->crc = (c->flags & KVC_CODEC_CRC32) ? 1u : 0u;
   sign_mask(c->seed, L->head_dim, P->sign_mask);
   *ring_off = off;
   *ring_size = need;

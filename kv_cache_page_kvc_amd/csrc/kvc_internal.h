@@ -43,10 +43,27 @@ struct CellEntry {
   uint32_t base;
 };
 
+// CRC-32 tables (reflected polynomial 0xEDB88320) for the one-wave CRC of a
+// byte range: lane j takes 16-byte units j, j + 64, j + 128, ... and runs
+// the slice-by-4 table step over each; the last word of a unit that has a
+// successor in the same lane uses tg, which also carries the register over
+// the kCrcGapBytes that the other 63 lanes take in between.  Each lane then
+// carries its register over the (63 - j) units after its last one with the
+// nibble tables sh, and the wave xors the registers.
+constexpr int kCrcLanes = 64;
+constexpr uint32_t kCrcGapBytes = 16 * (kCrcLanes - 1);
+struct CrcTables {
+  uint32_t t[4][256];    // register after byte b followed by k zero bytes, from a zero register
+  uint32_t tg[4][256];   // t[k][b] carried over kCrcGapBytes more zero bytes
+  uint32_t sh[6][8][16]; // register whose nibble i is v (others 0) carried over 16 << lvl zero bytes
+};
+static_assert(sizeof(CrcTables) % 16 == 0, "CRC tables are copied in 16-byte units");
+
 // Per-ctx constant tables (device, in the arena).
 struct Tables {
   CellEntry cells[2][kCells];                 // [0]: 3-bit, [1]: 4-bit
   float centroids[2][16];
+  alignas(16) CrcTables crc;
 };
 
 // Per-(layer, component) entry of a call (device, in the arena), indexed by
@@ -86,6 +103,9 @@ struct CallParams {
   // is assembled before it is written out with full-line stores; 0 when
   // some coded slot exceeds kMaxStageBytes (then codes go straight out).
   uint32_t stage_bytes;
+  // 1: encode stores each segment's CRC32, decode verifies it; the CRC
+  // tables then sit in dynamic LDS right after the staging bytes.
+  uint32_t crc;
   uint32_t n_pages, n_layers, heads, tokens;
   uint32_t dtype;                             // kvc_dtype
   uint32_t num_blocks;                        // page ids must be below this (guard)

@@ -622,7 +622,7 @@ struct Header {
   uint4 h0, h1;
 };
 __device__ __forceinline__ Header make_header(int format, int flags, int dtype, int comp, int d, int n_vec,
-                                              uint32_t stored, uint64_t spill, uint32_t aux) {
+                                              uint32_t stored, uint64_t spill, uint32_t aux, uint32_t crc) {
   Header h;
   h.h0.x = 1u | ((uint32_t)format << 8) | ((uint32_t)flags << 16) | ((uint32_t)(dtype | (comp << 4)) << 24);
   h.h0.y = (uint32_t)d | ((uint32_t)n_vec << 16);
@@ -630,12 +630,13 @@ __device__ __forceinline__ Header make_header(int format, int flags, int dtype, 
   h.h0.w = stored;
   h.h1.x = (uint32_t)spill;
   h.h1.y = (uint32_t)(spill >> 32);
-  h.h1.z = 0;
+  h.h1.z = crc;
   h.h1.w = aux;
   return h;
 }
 __device__ __forceinline__ void write_desc(kvc_segment_desc* desc, uint64_t slot_off, int format, int flags,
-                                           int status, int d, int n_vec, uint32_t stored, uint64_t spill) {
+                                           int status, int d, int n_vec, uint32_t stored, uint64_t spill,
+                                           uint32_t crc) {
   uint4 d0, d1;
   d0.x = (uint32_t)slot_off;
   d0.y = (uint32_t)(slot_off >> 32);
@@ -644,19 +645,129 @@ __device__ __forceinline__ void write_desc(kvc_segment_desc* desc, uint64_t slot
   d1.x = stored;
   d1.y = (uint32_t)(n_vec * d * 2);
   d1.z = 1u | ((uint32_t)format << 8) | ((uint32_t)flags << 16) | ((uint32_t)status << 24);
-  d1.w = 0;
+  d1.w = crc;
   reinterpret_cast<uint4*>(desc)[0] = d0;
   reinterpret_cast<uint4*>(desc)[1] = d1;
 }
 __device__ __forceinline__ void write_header_desc(uint8_t* slot, kvc_segment_desc* desc, uint64_t slot_off,
                                                   int format, int flags, int status, int dtype, int comp,
                                                   int d, int n_vec, uint32_t stored, uint64_t spill,
-                                                  uint32_t aux) {
-  const Header h = make_header(format, flags, dtype, comp, d, n_vec, stored, spill, aux);
+                                                  uint32_t aux, uint32_t crc) {
+  const Header h = make_header(format, flags, dtype, comp, d, n_vec, stored, spill, aux, crc);
   st_global16(slot, h.h0);
   st_global16(slot + 16, h.h1);
-  write_desc(desc, slot_off, format, flags, status, d, n_vec, stored, spill);
+  write_desc(desc, slot_off, format, flags, status, d, n_vec, stored, spill, crc);
 }
+
+// codes + metadata bytes of a coded segment
+__device__ __forceinline__ uint32_t payload_bytes(int codec, int d, uint32_t n_vec) {
+  int bits = 8, meta = 0;
+  switch (codec) {
+    case C_U3: case C_TQ3: bits = 3; break;
+    case C_U4: case C_TQ4: bits = 4; break;
+    default: break;
+  }
+  if (codec == C_FP8Y || codec == C_INT8 || codec == C_U3 || codec == C_U4) meta = 4;
+  if (codec == C_TQ3 || codec == C_TQ4) meta = 2;
+  return n_vec * (uint32_t)(bits * d / 8 + meta);
+}
+
+// ------------------------------------------------------------------ CRC-32
+// CRC-32 of zlib over a byte range [OKV-SF "Ownership, storage and GDS":
+// every stored segment carries a CRC32], computed by one wave from the
+// tables in CrcTables (see there for the lane schedule).  The register is
+// preset to 0xFFFFFFFF by complementing the first word and the result is
+// complemented at the end.
+
+// register after the four bytes of x (x = register ^ next little-endian word)
+__device__ __forceinline__ uint32_t crc_word(uint32_t x, const uint32_t (*t)[256]) {
+  return t[3][x & 0xFF] ^ t[2][(x >> 8) & 0xFF] ^ t[1][(x >> 16) & 0xFF] ^ t[0][x >> 24];
+}
+// register r carried over 16 << lvl zero bytes
+__device__ __forceinline__ uint32_t crc_zeros(uint32_t r, const uint32_t (*sh)[16]) {
+  uint32_t y = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) y ^= sh[i][(r >> (4 * i)) & 15];
+  return y;
+}
+
+// The CRC tables in LDS: a static allocation that only the kernels built
+// with CRC reference (so the others do not pay for its 11 KiB), at an
+// address the compiler knows, so table offsets fold into the LDS loads.
+template <bool CRC>
+__device__ __forceinline__ CrcTables* crc_tables_lds() {
+  if constexpr (CRC) {
+    __shared__ CrcTables s_crc_tables;
+    return &s_crc_tables;
+  } else {
+    return nullptr;
+  }
+}
+
+// Copy the CRC tables into LDS (all threads of the workgroup; the caller
+// synchronises before the first use).
+template <int NT>
+__device__ __forceinline__ void load_crc_tables(CrcTables* dst, const CrcTables* src) {
+  constexpr uint32_t kUnits = sizeof(CrcTables) / 16;
+  for (uint32_t u = threadIdx.x; u < kUnits; u += NT)
+    reinterpret_cast<uint4*>(dst)[u] = ld_global16(reinterpret_cast<const uint8_t*>(src) + 16 * u);
+}
+
+// CRC32 of n bytes; load(o) returns the 16 bytes at offset o of the range
+// (o a multiple of 16).  When n is not a multiple of 16 the 16-byte unit
+// holding the last bytes must be readable as a whole.  Called by all 64
+// lanes of one wave; every lane returns the CRC.
+template <class Load>
+__device__ __forceinline__ uint32_t crc32_wave(const Load& load, uint32_t n, const CrcTables* ct) {
+  const uint32_t lane = threadIdx.x & (kCrcLanes - 1);
+  const uint32_t units = n >> 4;
+  // virtual zero units in front make the unit count a multiple of 64 (a zero
+  // register stays zero over zero bytes), so lane 63 holds the last unit
+  const uint32_t pad = (kCrcLanes - (units & (kCrcLanes - 1))) & (kCrcLanes - 1);
+  const uint32_t rounds = (units + pad) / kCrcLanes;
+  uint32_t r = 0;
+  for (uint32_t k = 0; k < rounds; k++) {
+    const int32_t q = (int32_t)(k * kCrcLanes + lane) - (int32_t)pad;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (q >= 0) w = load(16u * (uint32_t)q);
+    if (q == 0) w.x = ~w.x;
+    r = crc_word(r ^ w.x, ct->t);
+    r = crc_word(r ^ w.y, ct->t);
+    r = crc_word(r ^ w.z, ct->t);
+    r = crc_word(r ^ w.w, k + 1 < rounds ? ct->tg : ct->t);
+  }
+  // carry each register over the units after its last one: 63 - lane
+  const uint32_t after = (kCrcLanes - 1) - lane;
+#pragma unroll
+  for (int lvl = 0; lvl < 6; lvl++) {
+    const uint32_t y = crc_zeros(r, ct->sh[lvl]);
+    r = (after >> lvl) & 1 ? y : r;
+  }
+#pragma unroll
+  for (int m = kCrcLanes / 2; m >= 1; m >>= 1) r ^= __shfl_xor(r, m, kCrcLanes);
+  // the ragged end (n mod 16 bytes), the same in every lane
+  if (!units) r = 0xFFFFFFFFu;
+  const uint32_t tail = n & 15;
+  if (tail) {
+    const uint4 w = load(16u * units);
+    if (tail >= 4) r = crc_word(r ^ w.x, ct->t);
+    if (tail >= 8) r = crc_word(r ^ w.y, ct->t);
+    if (tail >= 12) r = crc_word(r ^ w.z, ct->t);
+    const uint32_t q = tail >> 2;
+    uint32_t last = q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w));
+    for (uint32_t b = 0; b < (tail & 3); b++, last >>= 8) r = (r >> 8) ^ ct->t[0][(r ^ last) & 0xFF];
+  }
+  return ~r;
+}
+// ranges in global memory and in the LDS slot image
+struct GlobalBytes {
+  const uint8_t* p;
+  __device__ __forceinline__ uint4 operator()(uint32_t o) const { return ld_global16(p + o); }
+};
+struct LdsBytes {
+  const uint8_t* p;
+  __device__ __forceinline__ uint4 operator()(uint32_t o) const { return *reinterpret_cast<const uint4*>(p + o); }
+};
 
 template <int D, int DT, int NT>
 __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const Lane& ln, float fixed,
@@ -674,12 +785,22 @@ __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const La
   }
 }
 
+// CRC32 of bytes the workgroup has just written to global memory: the
+// barrier orders every wave's stores before wave 0 reads them back; wave 0
+// returns the CRC, the other waves 0.  Called by all threads.
+__device__ __forceinline__ uint32_t crc32_written(const uint8_t* b, uint32_t n, const CrcTables* ct) {
+  __syncthreads();
+  return threadIdx.x < kCrcLanes ? crc32_wave(GlobalBytes{b}, n, ct) : 0u;
+}
+
 // ------------------------------------------------------------------ encode kernel
-template <int D, int DT, int NT>
+template <int D, int DT, int NT, bool CRC>
 __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   __shared__ CellEntry s_cells[kCells];
   __shared__ unsigned long long s_spill;
+  __shared__ uint32_t s_crc;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
+  CrcTables* const ct = crc_tables_lds<CRC>();
 
   const uint32_t seg = blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
@@ -712,13 +833,21 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const uint32_t slot_bytes = E.slot_bytes;
   kvc_segment_desc* desc = p.desc + seg;
 
+  // CRC32 of the stored bytes, by wave 0, read back from global memory after
+  // all waves have written them (the barrier orders the workgroup's stores
+  // before the loads) or from the LDS slot image
+  constexpr bool crc = CRC;
+  constexpr int crc_flag = CRC ? KVC_FLAG_CRC32 : 0;
+  if constexpr (CRC) load_crc_tables<NT>(ct, &p.tables->crc);
+
   const Lane ln = lane_info<D>();
   if (codec == C_RAW) {                                        // raw by policy
     copy_out_raw<D, NT, false>(s, ln, s.slot + kHeaderBytes);
     zero_pad<NT>(s.slot, kHeaderBytes + raw_bytes, slot_bytes);
+    const uint32_t c = crc ? crc32_written(s.slot + kHeaderBytes, raw_bytes, ct) : 0u;
     if (threadIdx.x == 0)
-      write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY, KVC_SEG_RAW_POLICY, DT, comp, D,
-                        s.n_vec, raw_bytes, 0, 0);
+      write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY | crc_flag, KVC_SEG_RAW_POLICY, DT,
+                        comp, D, s.n_vec, raw_bytes, 0, 0, c);
     return;
   }
 
@@ -732,15 +861,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   if (tq) make_lane_signs<D>(p.sign_mask, ln.p, true, ls);
   const float fixed = E.fixed;
 
-  int bits = 8, meta = 0;
-  switch (codec) {
-    case C_U3: case C_TQ3: bits = 3; break;
-    case C_U4: case C_TQ4: bits = 4; break;
-    default: break;
-  }
-  if (codec == C_FP8Y || codec == C_INT8 || codec == C_U3 || codec == C_U4) meta = 4;
-  if (codec == C_TQ3 || codec == C_TQ4) meta = 2;
-  const uint32_t payload = (uint32_t)s.n_vec * (uint32_t)(bits * D / 8 + meta);
+  const uint32_t payload = payload_bytes(codec, D, (uint32_t)s.n_vec);
 
   // The slot body (codes, metadata, zero padding) is assembled in LDS when it
   // fits, then written with full-line nontemporal stores; partial-line
@@ -757,23 +878,34 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const int any_bad = __syncthreads_or(bad);
   const uint32_t aux = codec == C_FP8F ? __float_as_uint(fixed) : 0u;
   if (staged && !any_bad) {
+    uint32_t c = 0;
+    if (crc) {
+      if (threadIdx.x < kCrcLanes) {
+        c = crc32_wave(LdsBytes{s_stage + kHeaderBytes}, payload, ct);
+        if (threadIdx.x == 0) s_crc = c;
+      }
+      __syncthreads();
+      c = s_crc;
+    }
     // header + body from unit 0, so every wave store covers whole lines
-    const Header h = make_header(codec, 0, DT, comp, D, s.n_vec, payload, 0, aux);
+    const Header h = make_header(codec, crc_flag, DT, comp, D, s.n_vec, payload, 0, aux, c);
     for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT) {
       uint4 w = *reinterpret_cast<const uint4*>(s_stage + 16 * u);
       if (u == 0) w = h.h0;
       if (u == 1) w = h.h1;
       st_stream16(s.slot + 16 * u, w);
     }
-    if (threadIdx.x == 0) write_desc(desc, slot_off, codec, 0, KVC_SEG_ENCODED, D, s.n_vec, payload, 0);
+    if (threadIdx.x == 0) write_desc(desc, slot_off, codec, crc_flag, KVC_SEG_ENCODED, D, s.n_vec, payload, 0, c);
     return;
   }
   if (staged)
     for (uint32_t u = 2 + threadIdx.x; u < slot_bytes / 16; u += NT)
       st_stream16(s.slot + 16 * u, *reinterpret_cast<const uint4*>(s_stage + 16 * u));
   if (!any_bad) {
+    const uint32_t c = crc ? crc32_written(s.slot + kHeaderBytes, payload, ct) : 0u;
     if (threadIdx.x == 0)
-      write_header_desc(s.slot, desc, slot_off, codec, 0, KVC_SEG_ENCODED, DT, comp, D, s.n_vec, payload, 0, aux);
+      write_header_desc(s.slot, desc, slot_off, codec, crc_flag, KVC_SEG_ENCODED, DT, comp, D, s.n_vec, payload, 0,
+                        aux, c);
     return;
   }
   // raw because of its data: reserve spill space, copy the source bytes
@@ -783,13 +915,15 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const uint64_t off = s_spill;
   const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
   if (fits) copy_out_raw<D, NT, true>(s, ln, p.buf + p.slot_region + off);
+  // a segment that was not stored (no spill space) carries no CRC
+  const uint32_t c = crc && fits ? crc32_written(p.buf + p.slot_region + off, raw_bytes, ct) : 0u;
   if (threadIdx.x == 0) {
     if (fits)
-      write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA, KVC_SEG_RAW_DATA, DT, comp, D, s.n_vec,
-                        raw_bytes, p.slot_region + off, 0);
+      write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | crc_flag, KVC_SEG_RAW_DATA, DT, comp,
+                        D, s.n_vec, raw_bytes, p.slot_region + off, 0, c);
     else
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | KVC_FLAG_CAPACITY, KVC_SEG_CAPACITY,
-                        DT, comp, D, s.n_vec, raw_bytes, 0, 0);
+                        DT, comp, D, s.n_vec, raw_bytes, 0, 0, 0);
   }
 }
 
@@ -988,10 +1122,12 @@ __device__ __forceinline__ void decode_codec(int codec, const SegCtx& s, const L
   }
 }
 
-template <int D, int DT, int NT>
+template <int D, int DT, int NT, bool CRC>
 __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   __shared__ float s_cent[32];
+  __shared__ uint32_t s_crc_ok;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
+  CrcTables* const ct = crc_tables_lds<CRC>();
   const uint32_t seg = blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
@@ -1023,6 +1159,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   // loads (header and codes together); otherwise the header is read first.
   const uint32_t slot_bytes = E.slot_bytes;
   const bool staged = codec != C_RAW && slot_bytes <= p.stage_bytes;
+  if constexpr (CRC) load_crc_tables<NT>(ct, &p.tables->crc);
   uint4 h0, h1;
   if (staged) {
     for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT)
@@ -1043,8 +1180,28 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   if (raw_data) ok = ok && format == KVC_RAW && !(flags & KVC_FLAG_CAPACITY) && raw_bytes <= p.buf_bytes &&
                      spill >= p.slot_region && spill <= p.buf_bytes - raw_bytes;
   else ok = ok && format == codec;
-  if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = ok ? 0 : 1;
-  if (!ok) return;
+  const uint32_t stored = raw_data || codec == C_RAW ? raw_bytes : payload_bytes(codec, D, (uint32_t)s.n_vec);
+  ok = ok && h0.w == stored && ((flags & KVC_FLAG_CRC32) != 0) == CRC;
+  if (!ok) {
+    if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 1;
+    return;
+  }
+  // the stored bytes must match the header's CRC32 before the page is written
+  if constexpr (CRC) {
+    __syncthreads();                                      // CRC tables in LDS
+    if (threadIdx.x < kCrcLanes) {
+      const uint32_t c = raw_data ? crc32_wave(GlobalBytes{p.buf + spill}, stored, ct)
+                         : staged ? crc32_wave(LdsBytes{s_stage + kHeaderBytes}, stored, ct)
+                                  : crc32_wave(GlobalBytes{s.slot + kHeaderBytes}, stored, ct);
+      if (threadIdx.x == 0) s_crc_ok = c == h1.z;
+    }
+    __syncthreads();
+    if (!s_crc_ok) {
+      if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 3;
+      return;
+    }
+  }
+  if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 0;
 
   const Lane ln = lane_info<D>();
   if (raw_data) {
@@ -1070,37 +1227,41 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   else decode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cent, s.slot);
 }
 
-template <int D>
-hipError_t launch_encode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
-  const dim3 grid((unsigned)nseg);
-  if (p.threads == kThreadsSmall) {
-    if (p.dtype == KVC_BF16)
-      hipLaunchKernelGGL((encode_kernel<D, KVC_BF16, kThreadsSmall>), grid, dim3(kThreadsSmall), p.stage_bytes, st, p);
-    else
-      hipLaunchKernelGGL((encode_kernel<D, KVC_FP16, kThreadsSmall>), grid, dim3(kThreadsSmall), p.stage_bytes, st, p);
+// dynamic LDS of a launch: the slot staging
+inline uint32_t dynamic_lds(const CallParams& p) { return p.stage_bytes; }
+
+template <int D, int DT, int NT, bool CRC>
+struct EncodeLaunch {
+  static void run(const CallParams& p, uint64_t n, hipStream_t st) {
+    hipLaunchKernelGGL((encode_kernel<D, DT, NT, CRC>), dim3((unsigned)n), dim3(NT), dynamic_lds(p), st, p);
+  }
+};
+template <int D, int DT, int NT, bool CRC>
+struct DecodeLaunch {
+  static void run(const CallParams& p, uint64_t n, hipStream_t st) {
+    hipLaunchKernelGGL((decode_kernel<D, DT, NT, CRC>), dim3((unsigned)n), dim3(NT), dynamic_lds(p), st, p);
+  }
+};
+// instantiation for the call's dtype, workgroup size and CRC option
+template <int D, template <int, int, int, bool> class F>
+hipError_t dispatch(const CallParams& p, uint64_t nseg, hipStream_t st) {
+  const bool bf = p.dtype == KVC_BF16, small = p.threads == kThreadsSmall, crc = p.crc != 0;
+  if (bf) {
+    if (small) crc ? F<D, KVC_BF16, kThreadsSmall, true>::run(p, nseg, st) : F<D, KVC_BF16, kThreadsSmall, false>::run(p, nseg, st);
+    else crc ? F<D, KVC_BF16, kThreads, true>::run(p, nseg, st) : F<D, KVC_BF16, kThreads, false>::run(p, nseg, st);
   } else {
-    if (p.dtype == KVC_BF16)
-      hipLaunchKernelGGL((encode_kernel<D, KVC_BF16, kThreads>), grid, dim3(kThreads), p.stage_bytes, st, p);
-    else
-      hipLaunchKernelGGL((encode_kernel<D, KVC_FP16, kThreads>), grid, dim3(kThreads), p.stage_bytes, st, p);
+    if (small) crc ? F<D, KVC_FP16, kThreadsSmall, true>::run(p, nseg, st) : F<D, KVC_FP16, kThreadsSmall, false>::run(p, nseg, st);
+    else crc ? F<D, KVC_FP16, kThreads, true>::run(p, nseg, st) : F<D, KVC_FP16, kThreads, false>::run(p, nseg, st);
   }
   return hipGetLastError();
 }
 template <int D>
+hipError_t launch_encode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
+  return dispatch<D, EncodeLaunch>(p, nseg, st);
+}
+template <int D>
 hipError_t launch_decode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
-  const dim3 grid((unsigned)nseg);
-  if (p.threads == kThreadsSmall) {
-    if (p.dtype == KVC_BF16)
-      hipLaunchKernelGGL((decode_kernel<D, KVC_BF16, kThreadsSmall>), grid, dim3(kThreadsSmall), p.stage_bytes, st, p);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, KVC_FP16, kThreadsSmall>), grid, dim3(kThreadsSmall), p.stage_bytes, st, p);
-  } else {
-    if (p.dtype == KVC_BF16)
-      hipLaunchKernelGGL((decode_kernel<D, KVC_BF16, kThreads>), grid, dim3(kThreads), p.stage_bytes, st, p);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, KVC_FP16, kThreads>), grid, dim3(kThreads), p.stage_bytes, st, p);
-  }
-  return hipGetLastError();
+  return dispatch<D, DecodeLaunch>(p, nseg, st);
 }
 
 }  // namespace

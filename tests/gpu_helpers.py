@@ -97,7 +97,8 @@ def segments_of(L, n_pages):
     return O.segment_list(L, n_pages)
 
 
-def oracle_encode(wl: Workload, codec_k, codec_v, seed, page_ids, fixed=None, protected=None, segments=None):
+def oracle_encode(wl: Workload, codec_k, codec_v, seed, page_ids, fixed=None, protected=None, segments=None,
+                  crc=False):
     """Oracle encode of the given segments (all if None) of a call."""
     pages_needed = None
     if segments is not None:
@@ -109,14 +110,14 @@ def oracle_encode(wl: Workload, codec_k, codec_v, seed, page_ids, fixed=None, pr
     if protected is not None:
         prot = [1 if l in protected else 0 for l in range(wl.L)]
     return O.encode_pages(lay, codec_k, codec_v, seed, mapped, fixed_scales=fixed, protected=prot,
-                          segments=segments)
+                          segments=segments, crc=crc)
 
 
 def compare_encoded(gpu_buf: np.ndarray, gpu_desc, ora_buf, ora_status, offs, total, segments):
     """Per segment: status equal; slot bytes identical for encoded and
     policy-raw segments; for data-raw segments the header equal except the
     spill offset, and the spilled bytes equal the source (from the oracle's
-    own spill copy)."""
+    own spill copy).  The descriptor's flags and crc32 equal the header's."""
     bad = []
     for s in segments:
         st = int(ora_status[s])
@@ -127,6 +128,8 @@ def compare_encoded(gpu_buf: np.ndarray, gpu_desc, ora_buf, ora_status, offs, to
         o = offs[s]
         hdr_g = gpu_buf[o:o + 32]
         hdr_o = ora_buf[o:o + 32]
+        if int(d["flags"]) != int(hdr_g[2]) or int(d["crc32"]) != int(hdr_g[24:28].view(np.uint32)[0]):
+            bad.append((s, "descriptor flags/crc32"))
         if st == O.SEG_RAW_DATA:
             if not (np.array_equal(hdr_g[:16], hdr_o[:16]) and np.array_equal(hdr_g[24:], hdr_o[24:])):
                 bad.append((s, "raw header"))

@@ -28,6 +28,16 @@ def test_exports_every_declared_symbol():
 def test_struct_sizes():
     assert ctypes.sizeof(kvc.kvc_segment_desc) == 32
     assert ctypes.sizeof(kvc.kvc_layout) == 80
+    assert ctypes.sizeof(kvc.kvc_codec) == 40
+    assert kvc.kvc_codec.flags.offset == 32
+
+
+def test_header_constants_match_binding():
+    """The binding's ABI version and CRC flags are the header's."""
+    hdr = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    assert int(re.search(r"#define KVC_ABI_VERSION (\d+)u", hdr).group(1)) == kvc.KVC_ABI_VERSION == 2
+    assert int(re.search(r"#define KVC_CODEC_CRC32 (\d+)u", hdr).group(1)) == kvc.KVC_CODEC_CRC32
+    assert int(re.search(r"KVC_FLAG_CRC32 = (\d+)", hdr).group(1)) == kvc.KVC_FLAG_CRC32 == O.FLAG_CRC32
 
 
 FAKE = 1 << 40          # aligned fake device addresses: validation never dereferences them
@@ -107,6 +117,16 @@ def test_validation_errors():
         fs[2, 0] = badscale
         assert V(ok, kvc.Codec("FP8_FIXED", "RAW", fixed_scales=fs), ids, 1 << 40) == kvc.KVC_E_ARG
     assert V(ok, kvc.Codec(9, 0), ids, 1 << 40) == kvc.KVC_E_ARG
+    # codec flags: only KVC_CODEC_CRC32 is defined; reserved must be 0
+    assert V(ok, kvc.Codec("TQ4", "UNIFORM4", crc=True), ids, 1 << 40) == kvc.KVC_OK
+    c = kvc.Codec("TQ4", "UNIFORM4")
+    c.c.flags = 2
+    assert V(ok, c, ids, 1 << 40) == kvc.KVC_E_ARG
+    c.c.flags, c.c.reserved = kvc.KVC_CODEC_CRC32, 1
+    assert V(ok, c, ids, 1 << 40) == kvc.KVC_E_ARG
+    lay_old = layout()
+    lay_old.c.abi = 1                                   # callers built against the previous ABI
+    assert V(lay_old, kvc.Codec("TQ4", "UNIFORM4"), ids, 1 << 40) == kvc.KVC_E_ARG
 
 
 def test_decode_rejects_duplicate_destinations():

@@ -52,18 +52,18 @@ def _check_decoded(dec_gpu: np.ndarray, dec_ora: np.ndarray, dt, lossy_tq: bool,
 
 
 def _roundtrip_case(ctx, wl, ck, cv, seed, page_ids, protected=None, fixed=None, segments=None,
-                    dst_ids=None, decode_from_oracle=True, spill_bytes=None):
+                    dst_ids=None, decode_from_oracle=True, spill_bytes=None, crc=False):
     """Encode on GPU and oracle; compare.  Decode (a) the oracle's buffer on
     the GPU and (b) the GPU's buffer on the GPU; compare both with the
     oracle's decode of its own buffer."""
     n_pages = len(page_ids)
     kc, vc = _codec_ids(ck, cv)
-    codec = kvc.Codec(kc, vc, seed=seed, fixed_scales=fixed, protected_layers=protected, layers=wl.L)
+    codec = kvc.Codec(kc, vc, seed=seed, fixed_scales=fixed, protected_layers=protected, layers=wl.L, crc=crc)
     out, desc, slot, total = G.gpu_encode(ctx, wl, codec, page_ids, spill_bytes=spill_bytes)
     torch.cuda.synchronize()
     nseg = wl.L * n_pages * 2
     segs = list(range(nseg)) if segments is None else segments
-    ora_buf, ora_st, offs, ora_total = G.oracle_encode(wl, kc, vc, seed, page_ids, fixed, protected, segs)
+    ora_buf, ora_st, offs, ora_total = G.oracle_encode(wl, kc, vc, seed, page_ids, fixed, protected, segs, crc=crc)
     assert ora_total == slot
     gbuf = out.cpu().numpy()
     gdesc = G.desc_np(desc)
@@ -423,3 +423,147 @@ def test_int8_fp8_stress_full_size(ctx, codec):
         l, i, cc = seglist[s]
         got = G.gpu_segment_vectors(dst, l, cc, int(perm[i]))
         assert np.array_equal(got, ora_dec[s]), s
+
+
+# ----------------------------------------------------------------- CRC32 per segment
+CRC_SHAPES = {
+    # name: (layers, heads, tokens, pool, pages); layer 1 protected (raw by policy)
+    "n15": (3, 3, 5, 9, 4),        # 15 vectors: payloads end mid-unit (ragged CRC tail), 64-thread groups
+    "n231": (2, 7, 33, 6, 3),      # 231 vectors: 256-thread groups; D=256 slots exceed the LDS stage
+}
+
+
+@pytest.mark.parametrize("shape", sorted(CRC_SHAPES))
+@pytest.mark.parametrize("dim", [32, 64, 128, 256])
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}-{p[1]}")
+def test_crc_roundtrip(ctx, pair, dim, shape):
+    """KVC_CODEC_CRC32: every encoded slot (header CRC included) bit-exact
+    with the oracle's, descriptors carry the header's CRC, and both buffers
+    decode with status 0 to the oracle's values."""
+    L, H, T, pool, n = CRC_SHAPES[shape]
+    layout = "packed" if (dim // 32) % 2 else "separate"
+    print(f"[case] crc {pair} D={dim} {shape} {layout}", flush=True)
+    wl = G.Workload(L, H, dim, T, pool, "bf16", layout, seed=dim + 3)
+    ids = inputs.random_page_ids(pool, n, seed=dim + 5)
+    fixed = _fixed_scales(L) if "FP8_FIXED" in pair else None
+    ora_st, gdesc = _roundtrip_case(ctx, wl, pair[0], pair[1], seed=77 + dim, page_ids=ids, protected=[1],
+                                    fixed=fixed, dst_ids=inputs.random_page_ids(pool, n, seed=dim + 6), crc=True)
+    assert np.all(gdesc["flags"] & kvc.KVC_FLAG_CRC32)
+
+
+def _flip_stored_byte(buf: np.ndarray, d, s):
+    """Flip one bit of one stored byte of segment s (first, last or middle
+    byte, by segment) in a host copy of an encoded buffer."""
+    base = int(d["spill_offset"]) if d["status"] == kvc.KVC_SEG_RAW_DATA else int(d["offset"]) + 32
+    n = int(d["stored_len"])
+    at = (0, n - 1, n // 2)[s % 3]
+    buf[base + at] ^= np.uint8(1 << (s % 8))
+
+
+def test_crc_detects_corruption(ctx):
+    """One flipped bit in the stored bytes (coded payload, raw slot body or
+    spilled raw bytes) of every third segment: decode reports 3 for exactly
+    those and leaves their pages untouched, decodes the rest; the oracle
+    rejects the same segments."""
+    print("[case] crc corruption", flush=True)
+    L, H, D, T, pool, n = 3, 8, 128, 16, 24, 12
+    wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 21)
+    ids = inputs.random_page_ids(pool, n, seed=21)
+    inputs.inject_specials(wl.k, wl.v, ids, frac=0.15, seed=22, controls=0)
+    kc, vc = kvc.KVC_TQ4, kvc.KVC_FP8_DYNAMIC
+    codec = kvc.Codec(kc, vc, seed=9, protected_layers=[1], layers=L, crc=True)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids, spill_bytes=L * n * 2 * (H * T * D * 2))
+    torch.cuda.synchronize()
+    d = G.desc_np(desc)
+    assert {int(x) for x in d["status"]} >= {kvc.KVC_SEG_ENCODED, kvc.KVC_SEG_RAW_POLICY, kvc.KVC_SEG_RAW_DATA}
+    nseg = L * n * 2
+    flipped = set(range(0, nseg, 3))
+    buf = out.cpu().numpy().copy()
+    for s in flipped:
+        _flip_stored_byte(buf, d[s], s)
+    dst = wl.empty_like(fill_bits=0x2468)
+    dst_ids = inputs.random_page_ids(pool, n, seed=23)
+    st = G.gpu_decode(ctx, dst, codec, torch.from_numpy(buf).cuda(), total, dst_ids).cpu().numpy()
+    torch.cuda.synchronize()
+    segs = list(range(nseg))
+    ora_buf, ora_st, offs, _ = G.oracle_encode(wl, kc, vc, 9, ids, None, [1], segs, crc=True)
+    ora_dec = G.oracle_decode_segments(ora_buf, wl, kc, vc, 9, n, [1], segs)
+    seglist = G.segments_of(L, n)
+    for s, (l, i, c) in enumerate(seglist):
+        got = G.gpu_segment_vectors(dst, l, c, int(dst_ids[i]))
+        if s in flipped:
+            assert st[s] == 3, (s, st[s])
+            assert np.all(got == 0x2468), s
+        else:
+            assert st[s] == 0, (s, st[s])
+            _check_decoded(got, ora_dec[s], wl.dt, c == 0 and ora_st[s] == 0, f"segment {s}")
+    # the oracle refuses the same corruption in its own buffer
+    for s in sorted(flipped)[:12]:
+        bad = ora_buf.copy()
+        ds = {"status": ora_st[s], "offset": offs[s], "stored_len": int(ora_buf[offs[s] + 12:offs[s] + 16].view(np.uint32)[0]),
+              "spill_offset": int(ora_buf[offs[s] + 16:offs[s] + 24].view(np.uint64)[0])}
+        _flip_stored_byte(bad, ds, s)
+        size = (offs[s + 1] if s + 1 < len(offs) else slot) - offs[s]
+        with pytest.raises(O.ChecksumError):
+            O.decode_segment(bad[offs[s]:offs[s] + size], bad, wl.dt, D, H * T, 9)
+
+
+def test_crc_option_must_match(ctx):
+    """A buffer written with the CRC option decodes only with it, and one
+    written without only without: otherwise every segment reports 1 and no
+    page is written."""
+    print("[case] crc option mismatch", flush=True)
+    L, H, D, T, pool, n = 2, 4, 64, 16, 8, 4
+    wl = G.Workload(L, H, D, T, pool, "fp16", "packed", 31)
+    ids = inputs.random_page_ids(pool, n, seed=31)
+    for enc_crc in (True, False):
+        c_enc = kvc.Codec(kvc.KVC_TQ3, kvc.KVC_UNIFORM3, seed=1, protected_layers=[0], layers=L, crc=enc_crc)
+        c_dec = kvc.Codec(kvc.KVC_TQ3, kvc.KVC_UNIFORM3, seed=1, protected_layers=[0], layers=L, crc=not enc_crc)
+        out, desc, slot, total = G.gpu_encode(ctx, wl, c_enc, ids)
+        dst = wl.empty_like(fill_bits=0x1357)
+        st = G.gpu_decode(ctx, dst, c_dec, out, total, ids).cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.all(st == 1), st
+        for l in range(L):
+            assert np.all(G.u16(dst.k[l]) == 0x1357)
+
+
+def test_crc_spill_capacity(ctx):
+    """With the CRC option and a spill region for two raw segments: stored
+    raw segments carry the CRC of their spilled bytes and decode; segments
+    that were not stored carry none and report 1."""
+    print("[case] crc spill capacity", flush=True)
+    L, H, D, T, pool = 2, 8, 128, 16, 16
+    wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 12)
+    ids = np.arange(pool, dtype=np.int32)
+    inputs.inject_specials(wl.k, wl.v, ids, frac=0.2, seed=6, controls=0)
+    codec = kvc.Codec(kvc.KVC_INT8, kvc.KVC_INT8, seed=0, crc=True)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids, spill_bytes=2 * 32768)
+    torch.cuda.synchronize()
+    d = G.desc_np(desc)
+    buf = out.cpu().numpy()
+    raw = np.nonzero(d["status"] == kvc.KVC_SEG_RAW_DATA)[0]
+    cap = np.nonzero(d["status"] == kvc.KVC_SEG_CAPACITY)[0]
+    assert len(raw) == 2 and len(cap) > 0
+    for s in raw:
+        so, nb = int(d[s]["spill_offset"]), int(d[s]["stored_len"])
+        assert d[s]["flags"] & kvc.KVC_FLAG_CRC32 and int(d[s]["crc32"]) == O.crc32(buf[so:so + nb])
+    for s in cap:
+        assert not d[s]["flags"] & kvc.KVC_FLAG_CRC32 and int(d[s]["crc32"]) == 0
+    dst = wl.empty_like(fill_bits=0x1234)
+    st = G.gpu_decode(ctx, dst, codec, out, total, ids).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.all(st[cap] == 1) and np.all(np.delete(st, cap) == 0)
+
+
+def test_tq4_u4_llama3_full_size_crc(ctx):
+    """The TurboQuant-4 / uniform-4 Llama-3-8B workload with the CRC option:
+    one full-size launch each way, sampled segments bit-exact (CRCs
+    included) and decoded with status 0 after the CRC check."""
+    cfg = inputs.CONFIGS["tq4_u4_llama3"]
+    print("[case] tq4_u4_llama3 full size crc", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
+    ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
+    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 2, layers=[0, 31])
+    _roundtrip_case(ctx, wl, "TQ4", "UNIFORM4", 0, ids, protected=list(cfg["protected"]), segments=segs,
+                    decode_from_oracle=False, crc=True)
