@@ -46,7 +46,8 @@ __device__ __forceinline__ float materialize_f32(float x) {
 
 // y[e] += c * y[e] of the partner lane, for e < 8, in one v_fmac_f32_dpp
 // each (single rounding; c = +-1 makes the product exact).  Partner of
-// stage Q: lane xor 1 (Q=0), xor 2 (Q=1), xor 8 within the row (Q=2).
+// stage Q: lane xor 1 (Q=0), xor 2 (Q=1), xor 8 within the row (Q=2), xor 7
+// within the half-row (Q=3, row_half_mirror).
 // The compiler does not see DPP inside the asm, so the block opens with
 // five wait states (a VALU write of a VGPR needs two before a DPP read of
 // it, a VALU write of EXEC five) and closes with two, for any DPP reader
@@ -65,9 +66,9 @@ __device__ __forceinline__ float materialize_f32(float x) {
       : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7]) \
       : "v"(c))
 
-// Group minimum and maximum over the lanes of a vector group: lane bits 0, 1
-// (LOGP >= 2) and 3 (LOGP == 3), each step one v_min_f32_dpp / v_max_f32_dpp
-// with the partner lane.  The hardware min/max is used directly (no
+// Group minimum and maximum over the lanes of a vector group: partners lane
+// xor 1, xor 2 (LOGP >= 2), xor 8 (LOGP >= 3) and xor 7 (LOGP == 4), each
+// step one v_min_f32_dpp / v_max_f32_dpp with the partner lane.  The hardware min/max is used directly (no
 // quieting of signalling NaNs): callers detect NaN separately.  Two wait
 // states separate each step from the previous one (DPP reads of a VGPR
 // written by VALU), five open the block.
@@ -82,9 +83,13 @@ __device__ __forceinline__ void group_minmax_dpp(float& mn, float& mx) {
   else if constexpr (LOGP == 2)
     asm("s_nop 4\n\t" KVC_MINMAX_STEP("quad_perm:[1,0,3,2]") KVC_MINMAX_STEP("quad_perm:[2,3,0,1]")
         : "+v"(mn), "+v"(mx));
-  else
+  else if constexpr (LOGP == 3)
     asm("s_nop 4\n\t" KVC_MINMAX_STEP("quad_perm:[1,0,3,2]") KVC_MINMAX_STEP("quad_perm:[2,3,0,1]")
             KVC_MINMAX_STEP("row_ror:8")
+        : "+v"(mn), "+v"(mx));
+  else
+    asm("s_nop 4\n\t" KVC_MINMAX_STEP("quad_perm:[1,0,3,2]") KVC_MINMAX_STEP("quad_perm:[2,3,0,1]")
+            KVC_MINMAX_STEP("row_ror:8") KVC_MINMAX_STEP("row_half_mirror")
         : "+v"(mn), "+v"(mx));
 }
 #undef KVC_MINMAX_STEP
@@ -93,7 +98,8 @@ template <int Q>
 __device__ __forceinline__ void fmac_xlane8(float* y, float c) {
   if constexpr (Q == 0) KVC_FMAC_DPP8("quad_perm:[1,0,3,2]");
   else if constexpr (Q == 1) KVC_FMAC_DPP8("quad_perm:[2,3,0,1]");
-  else KVC_FMAC_DPP8("row_ror:8");
+  else if constexpr (Q == 2) KVC_FMAC_DPP8("row_ror:8");
+  else KVC_FMAC_DPP8("row_half_mirror");
 }
 
 #undef KVC_FMAC_DPP8

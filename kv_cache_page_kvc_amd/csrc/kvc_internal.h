@@ -22,7 +22,7 @@ constexpr uint32_t kSmallSegmentBytes = 16384;
 // lanes; a workgroup of nt threads holds groups_per_workgroup(D, nt)
 // groups, and group g handles vectors g, g + GW, g + 2*GW, ... of a segment
 // (GW = groups per workgroup).
-constexpr int lanes_per_vector(int d) { return d == 32 ? 2 : (d == 64 ? 4 : 8); }
+constexpr int lanes_per_vector(int d) { return d == 32 ? 2 : (d == 64 ? 4 : (d == 128 ? 8 : 16)); }
 constexpr int groups_per_workgroup(int d, int nt) { return nt / lanes_per_vector(d); }
 constexpr uint64_t kSlotAlign = KVC_SLOT_ALIGN;
 constexpr uint32_t kHeaderBytes = KVC_HEADER_BYTES;

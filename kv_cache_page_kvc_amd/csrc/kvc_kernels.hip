@@ -13,11 +13,12 @@
 // (one 16-byte load per chunk):
 //     element i = k*8P + 8p + j   (chunk k, lane p of the group, j < 8).
 // So WHT stages / reduction levels over element bits 0..2 are in-lane, bits
-// 3..3+log2(P)-1 are cross-lane (DPP: quad_perm for lane xor 1 and xor 2,
-// row_ror:8 for lane xor 8) and the chunk bits are in-lane again.  Group
-// lanes use lane-id bits {0, 1, 3}, so every cross-lane partner is one DPP
-// away.  Each load instruction of a wave reads 128-byte aligned pieces of
-// eight consecutive vectors.
+// 3..3+log2(P)-1 are cross-lane and the chunk bits are in-lane again.  P is
+// 2, 4, 8, 16 for D = 32, 64, 128, 256.  Positions map onto lanes so that
+// every cross-lane partner is one DPP step away (quad_perm for lane xor 1 and
+// xor 2, row_ror:8 for lane xor 8, row_half_mirror for lane xor 7; see
+// lane_info).  Each load instruction of a wave reads 16 consecutive bytes
+// per lane and whole 128-byte lines of consecutive vectors at D >= 128.
 //
 // Arithmetic: binary32 with round-to-nearest-even, built with
 // -ffp-contract=off; '/' and sqrtf are correctly rounded (HIP default);
@@ -42,7 +43,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 template <int D, int NT = kThreads>
 struct Geo {
   static constexpr int P = lanes_per_vector(D);               // lanes per vector
-  static constexpr int LOGP = P == 2 ? 1 : (P == 4 ? 2 : 3);
+  static constexpr int LOGP = P == 2 ? 1 : (P == 4 ? 2 : (P == 8 ? 3 : 4));
   static constexpr int E = D / P;                             // elements per lane
   static constexpr int NCH = E / 8;                           // 16-byte chunks per lane
   static constexpr int GPW = 64 / P;                          // groups per wave
@@ -59,11 +60,21 @@ struct Lane {
   int g;        // group index within the workgroup
 };
 
+// Group position p -> lane within the group's lanes: a linear map over
+// GF(2) that sends position bit q to the lane mask of the q-th cross-lane
+// partner (1, 2, 8 and, for 16-lane groups, 7): position p and p ^ (1 << q)
+// then sit in lanes l and l ^ mask(q), one DPP step apart (quad_perm for 1
+// and 2, row_ror:8 for 8, row_half_mirror for 7).  The inverse below gives p
+// from the lane id.
 template <int D>
 __device__ __forceinline__ Lane lane_info() {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Lane r;
-  if constexpr (Geo<D>::P == 8) {
+  if constexpr (Geo<D>::P == 16) {
+    const int l = lane & 15, b2 = (l >> 2) & 1;        // lane bit 2 = position bit 3
+    r.p = ((l & 1) ^ b2) | ((((l >> 1) & 1) ^ b2) << 1) | (((l >> 3) & 1) << 2) | (b2 << 3);
+    r.g = wave * 4 + (lane >> 4);
+  } else if constexpr (Geo<D>::P == 8) {
     r.p = (lane & 3) | (((lane >> 3) & 1) << 2);
     r.g = wave * 8 + (((lane >> 2) & 1) | ((lane >> 4) << 1));
   } else if constexpr (Geo<D>::P == 4) {
@@ -76,22 +87,18 @@ __device__ __forceinline__ Lane lane_info() {
   return r;
 }
 
-// cross-lane partner for the q-th group bit (element bit 3+q)
+// cross-lane partner for the q-th group bit (element bit 3+q): DPP control
+// quad_perm:[1,0,3,2] (lane ^ 1), quad_perm:[2,3,0,1] (lane ^ 2), row_ror:8
+// (lane ^ 8), row_half_mirror (lane ^ 7)
+template <int Q>
+constexpr int xlane_ctrl() { return Q == 0 ? 0xB1 : (Q == 1 ? 0x4E : (Q == 2 ? 0x128 : 0x141)); }
 template <int Q>
 __device__ __forceinline__ float xlane(float x) {
-  constexpr int ctrl = Q == 0 ? 0xB1 : (Q == 1 ? 0x4E : 0x128);   // xor1, xor2, row_ror:8
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, true));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), xlane_ctrl<Q>(), 0xF, 0xF, true));
 }
 template <int Q>
 __device__ __forceinline__ uint32_t xlane_u(uint32_t x) {
-  constexpr int ctrl = Q == 0 ? 0xB1 : (Q == 1 ? 0x4E : 0x128);
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, true);
-}
-// lane-id bit that carries group bit Q
-template <int Q>
-__device__ __forceinline__ bool upper_lane() {
-  constexpr int bit = Q == 0 ? 0 : (Q == 1 ? 1 : 3);
-  return (threadIdx.x >> bit) & 1;
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, xlane_ctrl<Q>(), 0xF, 0xF, true);
 }
 
 template <int LOGP>
@@ -99,6 +106,7 @@ __device__ __forceinline__ float group_sum(float v) {   // sum over element bits
   if constexpr (LOGP >= 1) v = v + xlane<0>(v);
   if constexpr (LOGP >= 2) v = v + xlane<1>(v);
   if constexpr (LOGP >= 3) v = v + xlane<2>(v);
+  if constexpr (LOGP >= 4) v = v + xlane<3>(v);
   return v;
 }
 template <int LOGP>
@@ -106,6 +114,7 @@ __device__ __forceinline__ uint32_t group_or(uint32_t v) {
   if constexpr (LOGP >= 1) v |= xlane_u<0>(v);
   if constexpr (LOGP >= 2) v |= xlane_u<1>(v);
   if constexpr (LOGP >= 3) v |= xlane_u<2>(v);
+  if constexpr (LOGP >= 4) v |= xlane_u<3>(v);
   return v;
 }
 template <int LOGP>
@@ -113,6 +122,7 @@ __device__ __forceinline__ uint32_t group_umax(uint32_t v) {
   if constexpr (LOGP >= 1) v = max(v, xlane_u<0>(v));
   if constexpr (LOGP >= 2) v = max(v, xlane_u<1>(v));
   if constexpr (LOGP >= 3) v = max(v, xlane_u<2>(v));
+  if constexpr (LOGP >= 4) v = max(v, xlane_u<3>(v));
   return v;
 }
 
@@ -301,23 +311,29 @@ __device__ __forceinline__ void make_lane_signs(const uint32_t* mask, int p, boo
 // (c = -1 in the lower lane, +1 in the upper): pi*RN(a+b) and pi*RN(a-b),
 // a single rounding because c*partner is exact.  Each stage removes one
 // parity bit from the sign, so after the last stage every sign is +1.
+// p: the lane's position in its group; its bit q says upper or lower.
 template <int LOGP, int E>
-__device__ __forceinline__ void wht_cross(float* y) {
+__device__ __forceinline__ void wht_cross(float* y, int p) {
   static_assert(E % 8 == 0, "lanes hold whole 8-element chunks");
   if constexpr (LOGP >= 1) {
-    const float c = upper_lane<0>() ? 1.0f : -1.0f;
+    const float c = (p & 1) ? 1.0f : -1.0f;
 #pragma unroll
     for (int e = 0; e < E; e += 8) fmac_xlane8<0>(y + e, c);
   }
   if constexpr (LOGP >= 2) {
-    const float c = upper_lane<1>() ? 1.0f : -1.0f;
+    const float c = (p & 2) ? 1.0f : -1.0f;
 #pragma unroll
     for (int e = 0; e < E; e += 8) fmac_xlane8<1>(y + e, c);
   }
   if constexpr (LOGP >= 3) {
-    const float c = upper_lane<2>() ? 1.0f : -1.0f;
+    const float c = (p & 4) ? 1.0f : -1.0f;
 #pragma unroll
     for (int e = 0; e < E; e += 8) fmac_xlane8<2>(y + e, c);
+  }
+  if constexpr (LOGP >= 4) {
+    const float c = (p & 8) ? 1.0f : -1.0f;
+#pragma unroll
+    for (int e = 0; e < E; e += 8) fmac_xlane8<3>(y + e, c);
   }
 }
 
@@ -523,7 +539,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
     for (int e = 0; e < E; e++) y[e] = x[e] * r;
     // 4. WHT, stages in ascending span
     wht_inlane_low<NCH>(y);
-    wht_cross<LOGP, E>(y);
+    wht_cross<LOGP, E>(y, ln.p);
     wht_inlane_high<NCH>(y);
     // 5. bucketize: code = #{B_k < z} = base(cell) + (z > T(cell))
     constexpr int LO = 0x4B400000 - kCellOffset, HI = 0x4B400000 + kCellOffset;
@@ -1033,7 +1049,7 @@ __device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane&
     }
     const float q = sumsq_tree<NCH, LOGP>(y);
     wht_inlane_low<NCH>(y);
-    wht_cross<LOGP, E>(y);
+    wht_cross<LOGP, E>(y, ln.p);
     wht_inlane_high<NCH>(y);
     const float nh = (float)__builtin_bit_cast(_Float16, (uint16_t)vc.meta);
     const float rd = sqrtf((float)D);
