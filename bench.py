@@ -175,6 +175,55 @@ def build_workload(args):
     return w
 
 
+def lane(args):
+    """Offload lane: kvc_offload_pages (encode, then the encoded buffer and
+    descriptors to pinned host memory) and kvc_restore_pages (host to device
+    per layer on the library's copy stream, each layer decoded as it lands),
+    timed with HIP events on the caller's stream.  Rates are GB/s of original
+    KV, host link included."""
+    import torch
+
+    import kv_cache_page_kvc_amd as kvc
+
+    torch.cuda.set_device(0)
+    w = build_workload(args)
+    L, H, D, T, n = w["L"], w["H"], w["D"], w["T"], len(w["ids"])
+    codec, lay, dlay = w["codec"], w["lay"], w["dlay"]
+    slot, spill, _ = kvc.kvc_plan(lay, codec, n)
+    total = slot + spill
+    host = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+    hdesc = torch.empty(L * n * 2 * 32, dtype=torch.uint8, pin_memory=True)
+    ctx = kvc.kvc_create(0, 0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    off_ms, res_ms = [], []
+    for k in range(args.warmup + args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        kvc.kvc_offload_pages(ctx, lay, codec, w["ids"], host.data_ptr(), total, hdesc.data_ptr(), sh)
+        e[1].record(stream)
+        kvc.kvc_restore_pages(ctx, dlay, codec, host.data_ptr(), total, w["dst_ids"], 0, L, 0, None, sh)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if k >= args.warmup:
+            off_ms.append(e[0].elapsed_time(e[1]))
+            res_ms.append(e[1].elapsed_time(e[2]))
+        print(f"[lane] step {k}: offload {e[0].elapsed_time(e[1]):.2f} ms, restore {e[1].elapsed_time(e[2]):.2f} ms",
+              file=sys.stderr, flush=True)
+    kvc.kvc_destroy(ctx)
+    orig = L * n * 2 * T * H * D * 2
+    om, rm = float(np.mean(off_ms)), float(np.mean(res_ms))
+    print(json.dumps({
+        "metric": "offload lane GB/s of original KV (encode + device-to-host, host-to-device + decode)",
+        "value": round(orig / ((om + rm) / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": w["describe"], "original_bytes": orig, "host_bytes": total, "crc32": bool(args.crc)},
+        "offload_ms": round(om, 3), "restore_ms": round(rm, 3),
+        "offload_GBps_original": round(orig / om / 1e6, 1), "restore_GBps_original": round(orig / rm / 1e6, 1),
+        "offload_GBps_host_link": round(total / om / 1e6, 1), "restore_GBps_host_link": round(total / rm / 1e6, 1),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +240,9 @@ def main():
                     help="V codec for k16v8_packed")
     ap.add_argument("--codec", default="INT8", choices=["INT8", "FP8_DYNAMIC", "FP8_DIRECT"],
                     help="codec for int8_fp8_stress")
+    ap.add_argument("--lane", action="store_true",
+                    help="time the offload lane instead: encode + copy to pinned host memory, then copy back "
+                         "+ layer-by-layer decode (PCIe-inclusive; not the headline value)")
     ap.add_argument("--crc", action="store_true",
                     help="store a CRC32 per segment on encode and verify it on decode")
     args = ap.parse_args()
@@ -200,6 +252,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.lane:
+        lane(args)
         return
 
     import torch

@@ -26,7 +26,8 @@
  *    nothing.
  *  - Encode/decode are asynchronous on the caller's HIP stream (never a host
  *    synchronisation, except to recycle the library's own small staging
- *    memory when more than a handful of calls are still in flight).  The
+ *    memory when more than a handful of calls are still in flight, or to
+ *    release an offload-lane staging buffer after it has grown).  The
  *    caller owns the KV tensors, the page-id arrays, the encoded buffer and
  *    the descriptor array; the library owns only its arena.
  *  - A context may be used from one host thread at a time.
@@ -232,6 +233,59 @@ kvc_status kvc_decode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_co
                             const void *in, size_t in_bytes,
                             const int32_t *dst_page_ids, uint32_t n_pages,
                             uint8_t *seg_status, void *stream);
+
+/* Decode only the segments of layers [layer_begin, layer_end) of a buffer
+ * produced by kvc_encode_pages (same arguments otherwise, and the same
+ * in_bytes) -- the per-layer step of a layer-by-layer restore [HIQ
+ * "Integrating the codec": load_to_device_per_layer].  Segment statuses
+ * land at their usual indices of seg_status.  KVC_E_ARG if layer_end <
+ * layer_begin or layer_end > layers; an empty range enqueues nothing. */
+kvc_status kvc_decode_layers(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
+                             const void *in, size_t in_bytes,
+                             const int32_t *dst_page_ids, uint32_t n_pages,
+                             uint32_t layer_begin, uint32_t layer_end,
+                             uint8_t *seg_status, void *stream);
+
+/* Offload lane, device to host [HIQ "Integrating the codec": GPU staging
+ * buffers, separate for backup and restoration, grown when necessary and
+ * never replaced while a stream still uses them].
+ * Encode the pages page_ids of every layer into the context's offload
+ * staging buffer, then copy the encoded buffer (host_bytes bytes: slot
+ * region, then spill region) to host_out and the layers*n_pages*2
+ * descriptors to host_desc, all enqueued on `stream`.  host_out and
+ * host_desc must be pinned host memory (hipHostMalloc, or a pinned torch
+ * tensor); they are written when the stream reaches this call and must stay
+ * allocated until then.  The bytes in host_out are exactly what
+ * kvc_encode_pages writes to a device buffer of host_bytes bytes.
+ * Errors as kvc_validate_encode (host_bytes in place of out_bytes), and
+ * KVC_E_ARG for memory that is not pinned host memory.  The staging buffer
+ * grows to host_bytes + the descriptors; a buffer it replaces is freed once
+ * the work queued on it has finished (freeing may wait for the device). */
+kvc_status kvc_offload_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
+                             const int32_t *page_ids, uint32_t n_pages,
+                             void *host_out, size_t host_bytes, kvc_segment_desc *host_desc,
+                             void *stream);
+
+/* Offload lane, host to device: restore layers [layer_begin, layer_end) of
+ * an encoded buffer held in pinned host memory (host_in, in_bytes: what
+ * kvc_offload_pages wrote, or any kvc_encode_pages output copied to host)
+ * into the destination pages dst_page_ids (host [n_pages], distinct, all
+ * validated before anything is enqueued).  The context's restore staging
+ * buffer receives the spill region, then each layer's slots, on an internal
+ * copy stream that starts after the work already queued on `stream`; layer
+ * l is decoded on `stream` as soon as its bytes have arrived, so copies of
+ * later layers overlap decodes of earlier ones.  After layer l's decode,
+ * layer_ready[l - layer_begin] (a hipEvent_t, may be NULL; the array may be
+ * NULL) is recorded on `stream`: copy, decode and scatter of the layer all
+ * precede it [HIQ "Making asynchronous restoration safe"].  seg_status as
+ * in kvc_decode_pages.  host_in must stay allocated and unchanged until the
+ * stream passes this call.  Errors as kvc_validate_decode, KVC_E_ARG for a
+ * bad layer range or memory that is not pinned host memory. */
+kvc_status kvc_restore_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
+                             const void *host_in, size_t in_bytes,
+                             const int32_t *dst_page_ids, uint32_t n_pages,
+                             uint32_t layer_begin, uint32_t layer_end,
+                             uint8_t *seg_status, void *const *layer_ready, void *stream);
 
 /* Short text for a status code (static storage). */
 const char *kvc_status_string(kvc_status s);

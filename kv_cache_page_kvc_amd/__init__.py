@@ -78,7 +78,8 @@ DESC_DTYPE = np.dtype([("offset", "<u8"), ("spill_offset", "<u8"), ("stored_len"
 assert DESC_DTYPE.itemsize == ctypes.sizeof(kvc_segment_desc) == 32
 
 EXPORTS = ["kvc_create", "kvc_destroy", "kvc_plan", "kvc_validate_encode", "kvc_validate_decode",
-           "kvc_encode_pages", "kvc_decode_pages", "kvc_status_string"]
+           "kvc_encode_pages", "kvc_decode_pages", "kvc_decode_layers", "kvc_offload_pages",
+           "kvc_restore_pages", "kvc_status_string"]
 
 _lib = None
 
@@ -110,6 +111,17 @@ def lib():
         L.kvc_decode_pages.restype = st
         L.kvc_decode_pages.argtypes = [P, ctypes.POINTER(kvc_layout), ctypes.POINTER(kvc_codec), P,
                                        ctypes.c_size_t, P, ctypes.c_uint32, P, P]
+        L.kvc_decode_layers.restype = st
+        L.kvc_decode_layers.argtypes = [P, ctypes.POINTER(kvc_layout), ctypes.POINTER(kvc_codec), P,
+                                        ctypes.c_size_t, P, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                        P, P]
+        L.kvc_offload_pages.restype = st
+        L.kvc_offload_pages.argtypes = [P, ctypes.POINTER(kvc_layout), ctypes.POINTER(kvc_codec), P,
+                                        ctypes.c_uint32, P, ctypes.c_size_t, P, P]
+        L.kvc_restore_pages.restype = st
+        L.kvc_restore_pages.argtypes = [P, ctypes.POINTER(kvc_layout), ctypes.POINTER(kvc_codec), P,
+                                        ctypes.c_size_t, P, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                        P, P, P]
         L.kvc_status_string.restype = ctypes.c_char_p
         L.kvc_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -242,3 +254,34 @@ def kvc_decode_pages(ctx, layout: Layout, codec: Codec, in_ptr: int, in_bytes: i
     _check(lib().kvc_decode_pages(ctx, ctypes.byref(layout.c), ctypes.byref(codec.c), in_ptr, in_bytes,
                                   ptr, arr.size, seg_status_ptr or None, stream or None),
            "kvc_decode_pages")
+
+
+def kvc_decode_layers(ctx, layout: Layout, codec: Codec, in_ptr: int, in_bytes: int, dst_page_ids,
+                      layer_begin: int, layer_end: int, seg_status_ptr: int = 0, stream: int = 0):
+    arr, ptr = _pages(dst_page_ids)
+    _check(lib().kvc_decode_layers(ctx, ctypes.byref(layout.c), ctypes.byref(codec.c), in_ptr, in_bytes,
+                                   ptr, arr.size, layer_begin, layer_end, seg_status_ptr or None,
+                                   stream or None), "kvc_decode_layers")
+
+
+def kvc_offload_pages(ctx, layout: Layout, codec: Codec, page_ids, host_ptr: int, host_bytes: int,
+                      host_desc_ptr: int, stream: int = 0):
+    """host_ptr / host_desc_ptr: pinned host memory (e.g. torch pin_memory tensors)."""
+    arr, ptr = _pages(page_ids)
+    _check(lib().kvc_offload_pages(ctx, ctypes.byref(layout.c), ctypes.byref(codec.c), ptr, arr.size,
+                                   host_ptr, host_bytes, host_desc_ptr, stream or None), "kvc_offload_pages")
+
+
+def kvc_restore_pages(ctx, layout: Layout, codec: Codec, host_ptr: int, host_bytes: int, dst_page_ids,
+                      layer_begin: int, layer_end: int, seg_status_ptr: int = 0, layer_ready=None,
+                      stream: int = 0):
+    """layer_ready: None or a sequence of hipEvent_t handles (ints), one per
+    restored layer (e.g. torch.cuda.Event(...).cuda_event after a first record)."""
+    arr, ptr = _pages(dst_page_ids)
+    evs = None
+    if layer_ready is not None:
+        evs = (ctypes.c_void_p * max(1, len(layer_ready)))(*[e or None for e in layer_ready])
+    _check(lib().kvc_restore_pages(ctx, ctypes.byref(layout.c), ctypes.byref(codec.c), host_ptr, host_bytes,
+                                   ptr, arr.size, layer_begin, layer_end, seg_status_ptr or None,
+                                   ctypes.cast(evs, ctypes.c_void_p) if evs is not None else None,
+                                   stream or None), "kvc_restore_pages")

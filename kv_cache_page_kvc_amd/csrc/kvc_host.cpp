@@ -12,7 +12,11 @@
 //    a retained arena bounded by the workspace budget; restore validates
 //    destinations for the whole request first; teardown drains GPU work.
 // and "Building a quantized HiCache for SGLang", "Integrating the codec":
-//    the encoded size per token is reported for capacity accounting.
+//    the encoded size per token is reported for capacity accounting; the
+//    offload and restore directions have their own persistent GPU staging
+//    buffers, grown when needed and never freed while a stream still uses
+//    them; copy, decode and scatter of a restored layer are ordered before
+//    the layer is signalled ready.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -38,6 +42,25 @@ struct kvc_ctx {
   };
   std::vector<InFlight> inflight;
   std::vector<hipEvent_t> free_events;
+  // Device staging of the offload lane, one per direction (0: offload, 1:
+  // restore), so transfers in the two directions never share bytes.  `last`
+  // is recorded after the last use of `ptr`; the next call on any stream
+  // waits for it before reusing the buffer.
+  struct Staging {
+    uint8_t* ptr = nullptr;
+    size_t cap = 0;
+    hipEvent_t last = nullptr;
+  };
+  Staging lane[2];
+  // buffers replaced by a larger one, freed once their last use has finished
+  struct Retired {
+    uint8_t* ptr;
+    hipEvent_t ev;
+  };
+  std::vector<Retired> retired;
+  hipStream_t copy_stream = nullptr;   // restore: host-to-device copies, ahead of the decodes
+  hipEvent_t fork = nullptr;           // restore: orders the copy stream after the caller's work
+  std::vector<hipEvent_t> layer_copied;
 };
 
 namespace {
@@ -345,6 +368,58 @@ kvc_status ring_commit(kvc_ctx* ctx, size_t off, size_t size, hipStream_t stream
   return KVC_OK;
 }
 
+hipEvent_t new_event() {
+  hipEvent_t e = nullptr;
+  return hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess ? e : nullptr;
+}
+
+// free the retired staging buffers whose last use has finished (all of them
+// when `wait`)
+void reap_retired(kvc_ctx* ctx, bool wait) {
+  for (size_t i = 0; i < ctx->retired.size();) {
+    auto& r = ctx->retired[i];
+    const bool done = !r.ev || (wait ? hipEventSynchronize(r.ev) == hipSuccess : hipEventQuery(r.ev) == hipSuccess);
+    if (done || wait) {
+      (void)hipFree(r.ptr);
+      if (r.ev) (void)hipEventDestroy(r.ev);
+      ctx->retired.erase(ctx->retired.begin() + (long)i);
+    } else {
+      i++;
+    }
+  }
+}
+
+// Make lane `dir` hold at least `bytes`.  A smaller buffer is retired with
+// its last-use event and freed only after that event has completed, so work
+// still queued on it keeps valid memory; the new buffer starts with no use.
+kvc_status lane_reserve(kvc_ctx* ctx, int dir, size_t bytes) {
+  reap_retired(ctx, false);
+  auto& st = ctx->lane[dir];
+  if (st.cap >= bytes) return KVC_OK;
+  const size_t cap = align_up(std::max(bytes, st.cap + st.cap / 4), 1u << 20);
+  uint8_t* p = nullptr;
+  if (hipMalloc(&p, cap) != hipSuccess) return KVC_E_HIP;
+  if (st.ptr) ctx->retired.push_back({st.ptr, st.last});
+  else if (st.last) (void)hipEventDestroy(st.last);
+  st.ptr = p;
+  st.cap = cap;
+  st.last = new_event();
+  return st.last ? KVC_OK : KVC_E_HIP;
+}
+
+// host memory that the copy engines can reach without a bounce (allocated
+// with hipHostMalloc, as torch's pinned tensors are): both ends of the range.
+// A failed query sets the runtime's last error; it is cleared here so that
+// the caller's next error check does not report it.
+bool pinned_range(const void* p, size_t n) {
+  unsigned int f = 0;
+  if (!p || n == 0) return false;
+  const bool ok = hipHostGetFlags(&f, const_cast<void*>(p)) == hipSuccess &&
+                  hipHostGetFlags(&f, static_cast<uint8_t*>(const_cast<void*>(p)) + n - 1) == hipSuccess;
+  if (!ok) (void)hipGetLastError();
+  return ok;
+}
+
 // stage layer table + page ids + zeroed spill cursor, upload, fill params
 kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, const Plan& plan,
                       const int32_t* pages, uint32_t n, hipStream_t stream, CallParams* P, size_t* ring_off,
@@ -510,6 +585,16 @@ kvc_status kvc_destroy(kvc_ctx* ctx) {
       (void)hipEventDestroy(f.ev);
     }
     for (auto e : ctx->free_events) (void)hipEventDestroy(e);
+    for (auto& ln : ctx->lane) {
+      if (ln.last && hipEventSynchronize(ln.last) != hipSuccess) st = KVC_E_HIP;
+      if (ln.ptr) (void)hipFree(ln.ptr);
+      if (ln.last) (void)hipEventDestroy(ln.last);
+    }
+    reap_retired(ctx, true);
+    if (ctx->copy_stream && hipStreamSynchronize(ctx->copy_stream) != hipSuccess) st = KVC_E_HIP;
+    for (auto e : ctx->layer_copied) (void)hipEventDestroy(e);
+    if (ctx->fork) (void)hipEventDestroy(ctx->fork);
+    if (ctx->copy_stream) (void)hipStreamDestroy(ctx->copy_stream);
     if (ctx->arena) (void)hipFree(ctx->arena);
     if (ctx->staging) (void)hipHostFree(ctx->staging);
   }
@@ -566,6 +651,131 @@ kvc_status kvc_decode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_co
   P.seg_status = seg_status;
   const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
   if (launch_decode(P, layout->head_dim, nseg, s) != hipSuccess) return KVC_E_HIP;
+  return ring_commit(ctx, roff, rsize, s);
+}
+
+kvc_status kvc_decode_layers(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec, const void* in,
+                             size_t in_bytes, const int32_t* dst_page_ids, uint32_t n_pages, uint32_t layer_begin,
+                             uint32_t layer_end, uint8_t* seg_status, void* stream) {
+  if (!ctx) return KVC_E_ARG;
+  kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
+  if (st != KVC_OK) return st;
+  if (layer_begin > layer_end || layer_end > layout->layers) return KVC_E_ARG;
+  if (n_pages == 0 || layer_begin == layer_end) return KVC_OK;
+  if (!in || ((uintptr_t)in & 255)) return KVC_E_ARG;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return KVC_E_HIP;
+  const Plan plan = make_plan(layout, codec, n_pages);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CallParams P{};
+  size_t roff = 0, rsize = 0;
+  st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+  if (st != KVC_OK) return st;
+  P.buf = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
+  P.buf_bytes = in_bytes;
+  P.slot_region = plan.total;
+  P.seg_status = seg_status;
+  P.seg_base = layer_begin * n_pages * 2;
+  if (launch_decode(P, layout->head_dim, (uint64_t)(layer_end - layer_begin) * n_pages * 2, s) != hipSuccess)
+    return KVC_E_HIP;
+  return ring_commit(ctx, roff, rsize, s);
+}
+
+kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec,
+                             const int32_t* page_ids, uint32_t n_pages, void* host_out, size_t host_bytes,
+                             kvc_segment_desc* host_desc, void* stream) {
+  if (!ctx) return KVC_E_ARG;
+  kvc_status st = kvc_validate_encode(layout, codec, page_ids, n_pages, host_bytes);
+  if (st != KVC_OK) return st;
+  if (n_pages == 0) return KVC_OK;
+  const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
+  const size_t desc_bytes = nseg * sizeof(kvc_segment_desc);
+  if (!pinned_range(host_out, host_bytes) || !pinned_range(host_desc, desc_bytes)) return KVC_E_ARG;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return KVC_E_HIP;
+  const Plan plan = make_plan(layout, codec, n_pages);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t buf_bytes = align_up(host_bytes, kAlign);
+  st = lane_reserve(ctx, 0, buf_bytes + desc_bytes);
+  if (st != KVC_OK) return st;
+  auto& lane = ctx->lane[0];
+  if (hipStreamWaitEvent(s, lane.last, 0) != hipSuccess) return KVC_E_HIP;   // the previous offload's copies
+  CallParams P{};
+  size_t roff = 0, rsize = 0;
+  st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize);
+  if (st != KVC_OK) return st;
+  P.buf = lane.ptr;
+  P.buf_bytes = host_bytes;
+  P.slot_region = plan.total;
+  P.desc = reinterpret_cast<kvc_segment_desc*>(lane.ptr + buf_bytes);
+  if (launch_encode(P, layout->head_dim, nseg, s) != hipSuccess) return KVC_E_HIP;
+  if (hipMemcpyAsync(host_out, lane.ptr, host_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(host_desc, P.desc, desc_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipEventRecord(lane.last, s) != hipSuccess)
+    return KVC_E_HIP;
+  return ring_commit(ctx, roff, rsize, s);
+}
+
+kvc_status kvc_restore_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec, const void* host_in,
+                             size_t in_bytes, const int32_t* dst_page_ids, uint32_t n_pages, uint32_t layer_begin,
+                             uint32_t layer_end, uint8_t* seg_status, void* const* layer_ready, void* stream) {
+  if (!ctx) return KVC_E_ARG;
+  kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
+  if (st != KVC_OK) return st;
+  if (layer_begin > layer_end || layer_end > layout->layers) return KVC_E_ARG;
+  if (n_pages == 0 || layer_begin == layer_end) return KVC_OK;
+  if (!pinned_range(host_in, in_bytes)) return KVC_E_ARG;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return KVC_E_HIP;
+  const Plan plan = make_plan(layout, codec, n_pages);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t nl = layer_end - layer_begin;
+  // lazily created: the copy stream (default priority), the fork event and
+  // one copy-done event per layer of the widest restore so far
+  if (!ctx->copy_stream && hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking) != hipSuccess)
+    return KVC_E_HIP;
+  if (!ctx->fork && !(ctx->fork = new_event())) return KVC_E_HIP;
+  while (ctx->layer_copied.size() < nl) {
+    hipEvent_t e = new_event();
+    if (!e) return KVC_E_HIP;
+    ctx->layer_copied.push_back(e);
+  }
+  st = lane_reserve(ctx, 1, align_up(in_bytes, kAlign));
+  if (st != KVC_OK) return st;
+  auto& lane = ctx->lane[1];
+  CallParams P{};
+  size_t roff = 0, rsize = 0;
+  st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+  if (st != KVC_OK) return st;
+  P.buf = lane.ptr;
+  P.buf_bytes = in_bytes;
+  P.slot_region = plan.total;
+  P.seg_status = seg_status;
+  // The copy stream starts after the caller's earlier work (which may have
+  // produced host_in) and after the previous restore's decodes have read the
+  // staging buffer.
+  const hipStream_t cs = ctx->copy_stream;
+  const uint8_t* hin = static_cast<const uint8_t*>(host_in);
+  if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(cs, ctx->fork, 0) != hipSuccess ||
+      hipStreamWaitEvent(cs, lane.last, 0) != hipSuccess)
+    return KVC_E_HIP;
+  if (in_bytes > plan.total &&
+      hipMemcpyAsync(lane.ptr + plan.total, hin + plan.total, in_bytes - plan.total, hipMemcpyHostToDevice, cs) !=
+          hipSuccess)
+    return KVC_E_HIP;
+  for (uint32_t l = layer_begin; l < layer_end; l++) {
+    const uint64_t a = plan.layer_off[l], b = l + 1 < layout->layers ? plan.layer_off[l + 1] : plan.total;
+    hipEvent_t copied = ctx->layer_copied[l - layer_begin];
+    if ((b > a && hipMemcpyAsync(lane.ptr + a, hin + a, b - a, hipMemcpyHostToDevice, cs) != hipSuccess) ||
+        hipEventRecord(copied, cs) != hipSuccess || hipStreamWaitEvent(s, copied, 0) != hipSuccess)
+      return KVC_E_HIP;
+    P.seg_base = l * n_pages * 2;
+    if (launch_decode(P, layout->head_dim, (uint64_t)n_pages * 2, s) != hipSuccess) return KVC_E_HIP;
+    if (layer_ready && layer_ready[l - layer_begin] &&
+        hipEventRecord(static_cast<hipEvent_t>(layer_ready[l - layer_begin]), s) != hipSuccess)
+      return KVC_E_HIP;
+  }
+  if (hipEventRecord(lane.last, s) != hipSuccess) return KVC_E_HIP;
   return ring_commit(ctx, roff, rsize, s);
 }
 

@@ -106,13 +106,17 @@ struct CallParams {
   // 1: encode stores each segment's CRC32, decode verifies it; the CRC
   // tables then sit in dynamic LDS right after the staging bytes.
   uint32_t crc;
+  // First segment of the launch: a launch covers the segments [seg_base,
+  // seg_base + workgroups) of the call (a range of whole layers).
+  uint32_t seg_base;
   uint32_t n_pages, n_layers, heads, tokens;
   uint32_t dtype;                             // kvc_dtype
   uint32_t num_blocks;                        // page ids must be below this (guard)
   uint32_t sign_mask[8];                      // TurboQuant signs, bit i = (sigma_i < 0)
 };
 
-// Launchers (kvc_kernels.hip).  Return hipSuccess or the launch error.
+// Launchers (kvc_kernels.hip): segments [p.seg_base, p.seg_base +
+// n_segments).  Return hipSuccess or the launch error.
 hipError_t launch_encode(const CallParams& p, uint32_t head_dim, uint64_t n_segments,
                          hipStream_t stream);
 hipError_t launch_decode(const CallParams& p, uint32_t head_dim, uint64_t n_segments,

@@ -818,7 +818,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
   CrcTables* const ct = crc_tables_lds<CRC>();
 
-  const uint32_t seg = blockIdx.x;
+  const uint32_t seg = p.seg_base + blockIdx.x;       // segments [seg_base, seg_base + grid)
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
   const uint32_t rem = seg - l * two_n;
@@ -1144,7 +1144,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   __shared__ uint32_t s_crc_ok;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
   CrcTables* const ct = crc_tables_lds<CRC>();
-  const uint32_t seg = blockIdx.x;
+  const uint32_t seg = p.seg_base + blockIdx.x;       // segments [seg_base, seg_base + grid)
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
   const uint32_t rem = seg - l * two_n;

@@ -144,3 +144,28 @@ def test_keep_rule_makes_tiny_segments_raw():
     lay = layout(H=1, T=1, D=32, L=1)
     slot, _, _ = kvc.kvc_plan(lay, kvc.Codec("INT8", "TQ4"), 1)
     assert slot == 2 * 256
+
+
+def test_lane_and_layer_entry_points_validate_first():
+    """kvc_decode_layers / kvc_offload_pages / kvc_restore_pages reject a
+    missing context and bad layer ranges on the host, before any GPU call
+    (the fake context below is never dereferenced)."""
+    codec = kvc.Codec("INT8", "INT8")
+    lay = layout(L=4)
+    ids = np.arange(3, dtype=np.int32)
+    idp = ids.ctypes.data_as(ctypes.c_void_p)
+    slot, _, _ = kvc.kvc_plan(lay, codec, 3)
+    L = kvc.lib()
+    lc, cc = ctypes.byref(lay.c), ctypes.byref(codec.c)
+    assert L.kvc_offload_pages(None, lc, cc, idp, 3, None, slot, None, None) == kvc.KVC_E_ARG
+    assert L.kvc_restore_pages(None, lc, cc, None, slot, idp, 3, 0, 4, None, None, None) == kvc.KVC_E_ARG
+    assert L.kvc_decode_layers(None, lc, cc, None, slot, idp, 3, 0, 4, None, None) == kvc.KVC_E_ARG
+    fake = ctypes.c_void_p(16)
+    for lb, le in ((3, 5), (2, 1), (0, 5)):
+        assert L.kvc_decode_layers(fake, lc, cc, None, slot, idp, 3, lb, le, None, None) == kvc.KVC_E_ARG
+        assert L.kvc_restore_pages(fake, lc, cc, None, slot, idp, 3, lb, le, None, None, None) == kvc.KVC_E_ARG
+    # the usual validation comes first: capacity, duplicate destinations
+    assert L.kvc_decode_layers(fake, lc, cc, None, slot - 1, idp, 3, 0, 1, None, None) == kvc.KVC_E_CAPACITY
+    dup = np.array([1, 1, 2], np.int32)
+    assert L.kvc_restore_pages(fake, lc, cc, None, slot, dup.ctypes.data_as(ctypes.c_void_p), 3, 0, 1, None,
+                               None, None) == kvc.KVC_E_DUP_DST
