@@ -22,7 +22,9 @@
  *   [HIQ]    "Building a quantized HiCache for SGLang": "Building the INT8
  *            codec" (symmetric per-head INT8: amax floor, scale = amax/127,
  *            FP32 quotient, round, clamp to +-127; all-zero head restores
- *            to exact zero).
+ *            to exact zero) and "Why exactly 1,152 bytes?" (a token's K or
+ *            V row: H x D INT8 codes, then H BF16 scales, padded to a
+ *            multiple of 128 bytes).
  *   [KNLP]   "Asymmetric KV: methods and results": "Precision and scaling
  *            reference" (FP32 amax clamped at 1e-12, times the rounded FP32
  *            reciprocal of 448, FP32 divide, clip to +-448, E4M3FN RNE;
@@ -38,6 +40,7 @@
 #define HEADER_BYTES 32u
 #define MAX_SEGMENT_BYTES (16u << 20)
 #define MAX_D 256
+#define ROWS_OFFSET 128u    /* INT8_ROWS: the rows start 128 bytes into the slot */
 
 static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
@@ -311,7 +314,16 @@ int kvo_meta_bytes(int codec) {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-size_t kvo_slot_bytes(int codec, int d, int n_vec) {
+/* [HIQ "Why exactly 1,152 bytes?"]: one token's row of the INT8 record
+ * codec -- heads*d INT8 codes and heads BF16 scales (1,040 bytes at 8 x 128),
+ * padded to the next multiple of 128 bytes (1,152 = 9 x 128). */
+size_t kvo_row_bytes(int d, int heads) {
+  return align_up((size_t)heads * (size_t)d + 2u * (size_t)heads, 128);
+}
+
+size_t kvo_slot_bytes(int codec, int d, int n_vec, int heads) {
+  if (codec == KVO_INT8_ROWS)
+    return align_up(ROWS_OFFSET + (size_t)(n_vec / heads) * kvo_row_bytes(d, heads), SLOT_ALIGN);
   size_t payload = (size_t)n_vec * (size_t)(kvo_code_bytes(codec, d) + kvo_meta_bytes(codec));
   return align_up(HEADER_BYTES + payload, SLOT_ALIGN);
 }
@@ -319,11 +331,11 @@ size_t kvo_slot_bytes(int codec, int d, int n_vec) {
 /* [OKV-SF "Ownership, storage and GDS"]: keep an encoded segment only when
  * its aligned footprint saves at least 12.5%; segments above 16 MiB stay raw.
  * [OKV-SF "FP8 and TurboQuant"]: protected layers stay exact. */
-int kvo_effective_codec(int codec, int d, int n_vec, int is_protected) {
+int kvo_effective_codec(int codec, int d, int n_vec, int heads, int is_protected) {
   size_t orig = (size_t)n_vec * (size_t)d * 2;
   if (is_protected || codec == KVO_RAW) return KVO_RAW;
   if (orig > MAX_SEGMENT_BYTES) return KVO_RAW;
-  if (8 * kvo_slot_bytes(codec, d, n_vec) > 7 * orig) return KVO_RAW;
+  if (8 * kvo_slot_bytes(codec, d, n_vec, heads) > 7 * orig) return KVO_RAW;
   return codec;
 }
 
@@ -365,6 +377,18 @@ static float int8_scale(const float *x, int d) {
   for (int i = 0; i < d; i++) if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
   if (amax < 1e-12f) amax = 1e-12f;
   return amax / 127.0f;
+}
+/* [HIQ "Building the INT8 codec"], record form: the same steps on BF16
+ * tensors -- amax (a BF16 value) clamped below at the floor, the floor
+ * itself a BF16 value (1e-12 rounded to BF16); scale = amax / 127 computed
+ * in FP32 and rounded to BF16; quotient formed in FP32 against that BF16
+ * scale, rounded half to even, clamped to +-127. */
+static float int8_rows_scale(const float *x, int d) {
+  const float floor_bf16 = kvo_bf16_to_f32(kvo_f32_to_bf16(1e-12f));
+  float amax = 0.0f;
+  for (int i = 0; i < d; i++) if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+  if (amax < floor_bf16) amax = floor_bf16;
+  return kvo_bf16_to_f32(kvo_f32_to_bf16(amax / 127.0f));
 }
 static void enc_int8(const float *x, int d, float s, uint8_t *codes) {
   for (int i = 0; i < d; i++) {
@@ -526,14 +550,15 @@ static void set_crc(uint8_t *slot, const uint8_t *stored, size_t n) {
   put_u32(slot + 24, kvo_crc32(stored, n));
 }
 
-int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
+int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec, int heads,
                        int component, int codec, int is_protected,
                        float fixed_scale, uint64_t seed,
                        uint8_t *slot, uint8_t *spill, uint64_t spill_offset, int flags) {
-  int eff = kvo_effective_codec(codec, d, n_vec, is_protected);
+  if (heads <= 0 || n_vec % heads) return -1;
+  int eff = kvo_effective_codec(codec, d, n_vec, heads, is_protected);
   const int with_crc = flags & KVO_ENC_CRC32;
   size_t orig = (size_t)n_vec * (size_t)d * 2;
-  size_t slot_bytes = kvo_slot_bytes(eff, d, n_vec);
+  size_t slot_bytes = kvo_slot_bytes(eff, d, n_vec, heads);
   memset(slot, 0, slot_bytes);
   if (eff == KVO_RAW) {
     write_header(slot, KVO_RAW, 1, dtype, component, d, n_vec, (uint32_t)orig, 0, 0);
@@ -545,6 +570,7 @@ int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
   int bits = codec_bits(eff), cb = kvo_code_bytes(eff, d), mb = kvo_meta_bytes(eff);
   uint8_t *codes = slot + HEADER_BYTES;
   uint8_t *meta = codes + (size_t)n_vec * (size_t)cb;
+  const size_t row = kvo_row_bytes(d, heads);     /* INT8_ROWS only */
   int8_t sigma[MAX_D];
   float cent[16], thr[15];
   if (eff == KVO_TQ3 || eff == KVO_TQ4) {
@@ -568,6 +594,11 @@ int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
     for (int i = 0; i < d; i++) x[i] = src_to_f32(vec[(size_t)v * d + i], dtype);
     uint8_t *cv = codes + (size_t)v * cb;
     uint8_t *mv = meta + (size_t)v * mb;
+    if (eff == KVO_INT8_ROWS) {                   /* token t = v / heads, head h = v % heads */
+      uint8_t *r = slot + ROWS_OFFSET + (size_t)(v / heads) * row;
+      cv = r + (size_t)(v % heads) * (size_t)d;
+      mv = r + (size_t)heads * (size_t)d + 2u * (size_t)(v % heads);
+    }
     switch (eff) {
       case KVO_FP8_DIRECT: enc_fp8_direct(x, d, cv); break;
       case KVO_FP8_FIXED: enc_fp8_scaled(x, d, fixed_scale, cv); break;
@@ -580,6 +611,12 @@ int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
       case KVO_INT8: {
         float s = int8_scale(x, d);
         put_u32(mv, f2u(s));
+        enc_int8(x, d, s, cv);
+        break;
+      }
+      case KVO_INT8_ROWS: {
+        float s = int8_rows_scale(x, d);
+        put_u16(mv, kvo_f32_to_bf16(s));
         enc_int8(x, d, s, cv);
         break;
       }
@@ -598,23 +635,27 @@ int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
     }
     return KVO_SEG_RAW_DATA;
   }
-  const size_t stored = (size_t)n_vec * (cb + mb);
+  /* the stored bytes: codes then metadata after the header, or for
+   * INT8_ROWS the token rows at ROWS_OFFSET */
+  const int rows = eff == KVO_INT8_ROWS;
+  const size_t stored = rows ? (size_t)(n_vec / heads) * row : (size_t)n_vec * (cb + mb);
   write_header(slot, eff, 0, dtype, component, d, n_vec, (uint32_t)stored, 0,
                eff == KVO_FP8_FIXED ? f2u(fixed_scale) : 0);
-  if (with_crc) set_crc(slot, slot + HEADER_BYTES, stored);
+  if (with_crc) set_crc(slot, slot + (rows ? ROWS_OFFSET : HEADER_BYTES), stored);
   return KVO_SEG_ENCODED;
 }
 
 int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
-                       int dtype, int d, int n_vec, uint64_t seed, uint16_t *out) {
-  if (slot[0] != 1) return -1;
+                       int dtype, int d, int n_vec, int heads, uint64_t seed, uint16_t *out) {
+  if (slot[0] != 1 || heads <= 0 || n_vec % heads) return -1;
   int format = slot[1], flags = slot[2];
   if ((slot[3] & 15) != dtype || get_u16(slot + 4) != d || get_u16(slot + 6) != n_vec) return -1;
   if (get_u32(slot + 8) != (uint32_t)(n_vec * d * 2)) return -1;
   size_t nel = (size_t)n_vec * (size_t)d;
   /* a CRC32, when present, is checked before anything is decoded */
   if (flags & KVO_FLAG_CRC32) {
-    const uint8_t *stored = (flags & 2) ? buf_base + get_u64(slot + 16) : slot + HEADER_BYTES;
+    const uint8_t *stored = (flags & 2) ? buf_base + get_u64(slot + 16)
+                            : slot + (format == KVO_INT8_ROWS ? ROWS_OFFSET : HEADER_BYTES);
     if ((flags & 2) && (flags & 4)) return -1;
     if (kvo_crc32(stored, get_u32(slot + 12)) != get_u32(slot + 24)) return -2;
   }
@@ -631,6 +672,7 @@ int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
   int bits = codec_bits(format), cb = kvo_code_bytes(format, d), mb = kvo_meta_bytes(format);
   const uint8_t *codes = slot + HEADER_BYTES;
   const uint8_t *meta = codes + (size_t)n_vec * cb;
+  const size_t row = kvo_row_bytes(d, heads);
   int8_t sigma[MAX_D];
   float cent[16], thr[15];
   if (format == KVO_TQ3 || format == KVO_TQ4) {
@@ -642,6 +684,11 @@ int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
     const uint8_t *cv = codes + (size_t)v * cb;
     const uint8_t *mv = meta + (size_t)v * mb;
     uint16_t *ov = out + (size_t)v * d;
+    if (format == KVO_INT8_ROWS) {
+      const uint8_t *r = slot + ROWS_OFFSET + (size_t)(v / heads) * row;
+      cv = r + (size_t)(v % heads) * (size_t)d;
+      mv = r + (size_t)heads * (size_t)d + 2u * (size_t)(v % heads);
+    }
     switch (format) {
       case KVO_FP8_DIRECT:
         for (int i = 0; i < d; i++) ov[i] = f32_to_out(kvo_e4m3_to_f32(cv[i]), dtype);
@@ -653,6 +700,11 @@ int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
       }
       case KVO_INT8: {
         float s = u2f(get_u32(mv));
+        for (int i = 0; i < d; i++) ov[i] = f32_to_out((float)(int8_t)cv[i] * s, dtype);
+        break;
+      }
+      case KVO_INT8_ROWS: {                        /* code x BF16 scale, rounded once */
+        float s = kvo_bf16_to_f32(get_u16(mv));
         for (int i = 0; i < d; i++) ov[i] = f32_to_out((float)(int8_t)cv[i] * s, dtype);
         break;
       }

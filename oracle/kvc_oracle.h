@@ -9,8 +9,8 @@
  * Sources (the pages):
  *   [OKV-SF]  OrbitKV docs, "KV precision and storage encoding",
  *             sections "FP8 and TurboQuant" and "Ownership, storage and GDS".
- *   [HIQ]     "Building a quantized HiCache for SGLang", section
- *             "Building the INT8 codec".
+ *   [HIQ]     "Building a quantized HiCache for SGLang", sections
+ *             "Building the INT8 codec" and "Why exactly 1,152 bytes?".
  *   [KNLP]    knlp, "Asymmetric KV: methods and results", section
  *             "Precision and scaling reference".
  *
@@ -48,7 +48,8 @@ extern "C" {
 /* codec ids == format byte of the encoded segment */
 enum {
   KVO_RAW = 0, KVO_FP8_DIRECT = 1, KVO_FP8_FIXED = 2, KVO_FP8_DYNAMIC = 3,
-  KVO_INT8 = 4, KVO_UNIFORM3 = 5, KVO_UNIFORM4 = 6, KVO_TQ3 = 7, KVO_TQ4 = 8
+  KVO_INT8 = 4, KVO_UNIFORM3 = 5, KVO_UNIFORM4 = 6, KVO_TQ3 = 7, KVO_TQ4 = 8,
+  KVO_INT8_ROWS = 9   /* INT8 with BF16 scales in 128-byte-padded token rows */
 };
 enum { KVO_BF16 = 1, KVO_FP16 = 2 };
 /* segment status returned by the encoder */
@@ -93,21 +94,30 @@ float kvo_sumsq_tree(const float *x, int d);
 /* ---- format sizes ---- */
 int    kvo_code_bytes(int codec, int d);   /* code bytes per vector        */
 int    kvo_meta_bytes(int codec);          /* metadata bytes per vector    */
-size_t kvo_slot_bytes(int codec, int d, int n_vec);  /* aligned slot incl. header */
+/* aligned slot incl. header; heads = vectors per token (n_vec = tokens *
+ * heads), which only the INT8_ROWS layout depends on */
+size_t kvo_slot_bytes(int codec, int d, int n_vec, int heads);
+/* INT8_ROWS: bytes of one token row, heads*d codes + heads BF16 scales
+ * padded to a multiple of 128 */
+size_t kvo_row_bytes(int d, int heads);
 /* codec actually used for a segment after the static rules (RAW policy,
  * 12.5% keep rule, 16 MiB cap) */
-int    kvo_effective_codec(int codec, int d, int n_vec, int is_protected);
+int    kvo_effective_codec(int codec, int d, int n_vec, int heads, int is_protected);
 
 /* ---- segments ----
- * vec: n_vec*d source bit patterns in canonical vector order (v = t*H + h).
+ * vec: n_vec*d source bit patterns in canonical vector order (v = t*H + h),
+ * heads = H (n_vec must be a multiple of it).
  * slot: kvo_slot_bytes(effective codec) bytes, fully written (header, payload,
- * zero padding).  For a data-dependent RAW segment the slot carries only the
+ * zero padding).  INT8_ROWS stores, from byte 128 of the slot, one row per
+ * token: its H vectors' codes (h-major), its H BF16 scales, zero padding to
+ * kvo_row_bytes; every other codec stores the codes block then the metadata
+ * block right after the 32-byte header.  For a data-dependent RAW segment the slot carries only the
  * header (payload zero) and the raw bytes go to spill (n_vec*d*2 bytes, if
  * spill != NULL); spill_offset is written into the header.  flags:
  * KVO_ENC_CRC32 stores the CRC32 of the stored bytes (the payload, or the raw
  * bytes in the slot or the spill) in the header.
  * Returns KVO_SEG_*. */
-int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
+int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec, int heads,
                        int component, int codec, int is_protected,
                        float fixed_scale, uint64_t seed,
                        uint8_t *slot, uint8_t *spill, uint64_t spill_offset, int flags);
@@ -116,7 +126,7 @@ int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec,
  * Returns 0 on success, -1 on a malformed header, -2 when the segment
  * carries a CRC32 that its stored bytes do not match. */
 int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
-                       int dtype, int d, int n_vec, uint64_t seed,
+                       int dtype, int d, int n_vec, int heads, uint64_t seed,
                        uint16_t *out);
 
 /* array loops over the scalar conversions, for the test harness */

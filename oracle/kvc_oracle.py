@@ -7,8 +7,8 @@ and its Python binding never do.
 All arithmetic lives in ``kvc_oracle.c``; this file only marshals arrays and
 walks segments in the order the format defines (layer-major, then page, then
 K before V).  The slot offsets are computed here from the format rules
-(header 32 B, codes block, metadata block, 256-B alignment), independently of
-the GPU library's own plan.
+(header 32 B, codes block, metadata block, or the INT8_ROWS token rows from
+byte 128; 256-B alignment), independently of the GPU library's own plan.
 """
 from __future__ import annotations
 
@@ -23,9 +23,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
 _LIB = os.path.join(_HERE, "libkvc_oracle.so")
 
-RAW, FP8_DIRECT, FP8_FIXED, FP8_DYNAMIC, INT8, UNIFORM3, UNIFORM4, TQ3, TQ4 = range(9)
+RAW, FP8_DIRECT, FP8_FIXED, FP8_DYNAMIC, INT8, UNIFORM3, UNIFORM4, TQ3, TQ4, INT8_ROWS = range(10)
 CODEC_NAMES = ["RAW", "FP8_DIRECT", "FP8_FIXED", "FP8_DYNAMIC", "INT8",
-               "UNIFORM3", "UNIFORM4", "TQ3", "TQ4"]
+               "UNIFORM3", "UNIFORM4", "TQ3", "TQ4", "INT8_ROWS"]
+ROWS_OFFSET = 128      # INT8_ROWS: token rows start 128 bytes into the slot
 BF16, FP16 = 1, 2
 SEG_ENCODED, SEG_RAW_POLICY, SEG_RAW_DATA = 0, 1, 2
 HEADER_BYTES = 32
@@ -86,18 +87,20 @@ def lib():
         L.kvo_meta_bytes.restype = ctypes.c_int
         L.kvo_meta_bytes.argtypes = [ctypes.c_int]
         L.kvo_slot_bytes.restype = ctypes.c_size_t
-        L.kvo_slot_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.kvo_slot_bytes.argtypes = [ctypes.c_int] * 4
+        L.kvo_row_bytes.restype = ctypes.c_size_t
+        L.kvo_row_bytes.argtypes = [ctypes.c_int] * 2
         L.kvo_effective_codec.restype = ctypes.c_int
-        L.kvo_effective_codec.argtypes = [ctypes.c_int] * 4
+        L.kvo_effective_codec.argtypes = [ctypes.c_int] * 5
         L.kvo_encode_segment.restype = ctypes.c_int
-        L.kvo_encode_segment.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        L.kvo_encode_segment.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_float, ctypes.c_uint64, P, P, ctypes.c_uint64,
                                          ctypes.c_int]
         L.kvo_crc32.restype = ctypes.c_uint32
         L.kvo_crc32.argtypes = [P, ctypes.c_size_t]
         L.kvo_decode_segment.restype = ctypes.c_int
-        L.kvo_decode_segment.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        L.kvo_decode_segment.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_uint64, P]
         _lib = L
     return _lib
@@ -207,12 +210,17 @@ def meta_bytes(codec):
     return lib().kvo_meta_bytes(codec)
 
 
-def slot_bytes(codec, d, n_vec):
-    return lib().kvo_slot_bytes(codec, d, n_vec)
+def slot_bytes(codec, d, n_vec, heads=1):
+    """heads: vectors per token (only the INT8_ROWS layout depends on it)."""
+    return lib().kvo_slot_bytes(codec, d, n_vec, heads)
 
 
-def effective_codec(codec, d, n_vec, is_protected):
-    return lib().kvo_effective_codec(codec, d, n_vec, int(bool(is_protected)))
+def row_bytes(d, heads):
+    return lib().kvo_row_bytes(d, heads)
+
+
+def effective_codec(codec, d, n_vec, is_protected, heads=1):
+    return lib().kvo_effective_codec(codec, d, n_vec, heads, int(bool(is_protected)))
 
 
 # ---------------------------------------------------------------- segments
@@ -232,15 +240,16 @@ def crc32(data) -> int:
 
 def encode_segment(vec: np.ndarray, dtype: int, codec: int, component: int = 0,
                    is_protected: bool = False, fixed_scale: float = 1.0, seed: int = 0,
-                   spill_offset: int = 0, crc: bool = False):
-    """vec: uint16 [n_vec, D] source bits.  Returns (slot uint8, status, raw uint8|None).
-    crc: store the CRC32 of the stored bytes in the header."""
+                   spill_offset: int = 0, crc: bool = False, heads: int = 1):
+    """vec: uint16 [n_vec, D] source bits (v = t*heads + h).  Returns (slot
+    uint8, status, raw uint8|None).  crc: store the CRC32 of the stored
+    bytes in the header."""
     vec = np.ascontiguousarray(vec, dtype=np.uint16)
     n_vec, d = vec.shape
-    eff = effective_codec(codec, d, n_vec, is_protected)
-    slot = np.zeros(slot_bytes(eff, d, n_vec), np.uint8)
+    eff = effective_codec(codec, d, n_vec, is_protected, heads)
+    slot = np.zeros(slot_bytes(eff, d, n_vec, heads), np.uint8)
     spill = np.zeros(n_vec * d * 2, np.uint8)
-    st = lib().kvo_encode_segment(_ptr(vec), dtype, d, n_vec, component, codec,
+    st = lib().kvo_encode_segment(_ptr(vec), dtype, d, n_vec, heads, component, codec,
                                   int(bool(is_protected)), ctypes.c_float(fixed_scale),
                                   ctypes.c_uint64(seed), _ptr(slot), _ptr(spill),
                                   ctypes.c_uint64(spill_offset), ENC_CRC32 if crc else 0)
@@ -249,11 +258,11 @@ def encode_segment(vec: np.ndarray, dtype: int, codec: int, component: int = 0,
     return slot, st, (spill if st == SEG_RAW_DATA else None)
 
 
-def decode_segment(slot: np.ndarray, buf_base, dtype: int, d: int, n_vec: int, seed: int = 0):
+def decode_segment(slot: np.ndarray, buf_base, dtype: int, d: int, n_vec: int, seed: int = 0, heads: int = 1):
     slot = np.ascontiguousarray(slot, dtype=np.uint8)
     out = np.zeros((n_vec, d), np.uint16)
     base = _ptr(buf_base) if buf_base is not None else None
-    rc = lib().kvo_decode_segment(_ptr(slot), base, dtype, d, n_vec, ctypes.c_uint64(seed), _ptr(out))
+    rc = lib().kvo_decode_segment(_ptr(slot), base, dtype, d, n_vec, heads, ctypes.c_uint64(seed), _ptr(out))
     if rc == -2:
         raise ChecksumError("oracle decode: CRC32 mismatch")
     if rc != 0:
@@ -313,8 +322,8 @@ def plan(L, H, D, T, codec_k, codec_v, protected, n_pages):
     off = 0
     for (l, i, c) in segment_list(L, n_pages):
         prot = bool(protected[l]) if protected is not None else False
-        eff = effective_codec(codec_k if c == 0 else codec_v, D, n_vec, prot)
-        sz = slot_bytes(eff, D, n_vec)
+        eff = effective_codec(codec_k if c == 0 else codec_v, D, n_vec, prot, H)
+        sz = slot_bytes(eff, D, n_vec, H)
         offs.append(off)
         sizes.append(sz)
         effs.append(eff)
@@ -345,7 +354,8 @@ def encode_pages(lay: HostLayout, codec_k, codec_v, seed, page_ids, fixed_scales
         prot = bool(protected[l]) if protected is not None else False
         fs = float(fixed_scales[l][c]) if fixed_scales is not None else 1.0
         vec = lay.gather(l, c, int(page_ids[i]))
-        return encode_segment(vec, lay.dtype, codec_k if c == 0 else codec_v, c, prot, fs, seed, crc=crc)
+        return encode_segment(vec, lay.dtype, codec_k if c == 0 else codec_v, c, prot, fs, seed, crc=crc,
+                              heads=lay.H)
 
     if threads > 1:
         with ThreadPoolExecutor(threads) as ex:
@@ -379,7 +389,7 @@ def decode_pages(buf: np.ndarray, out: HostLayout, codec_k, codec_v, seed, dst_p
     n_vec = out.T * out.H
 
     def work(s):
-        return decode_segment(buf[offs[s]:offs[s] + sizes[s]], buf, out.dtype, out.D, n_vec, seed)
+        return decode_segment(buf[offs[s]:offs[s] + sizes[s]], buf, out.dtype, out.D, n_vec, seed, heads=out.H)
 
     if threads > 1:
         with ThreadPoolExecutor(threads) as ex:

@@ -156,7 +156,7 @@ def oracle_decode_segments(ora_buf, wl: Workload, codec_k, codec_v, seed, n_page
                                       None if protected is None else
                                       [1 if l in protected else 0 for l in range(wl.L)], n_pages)
     n_vec = wl.T * wl.H
-    return {s: O.decode_segment(ora_buf[offs[s]:offs[s] + sizes[s]], ora_buf, wl.dt, wl.D, n_vec, seed)
+    return {s: O.decode_segment(ora_buf[offs[s]:offs[s] + sizes[s]], ora_buf, wl.dt, wl.D, n_vec, seed, heads=wl.H)
             for s in segments}
 
 

@@ -594,3 +594,148 @@ def test_segment_crc32_spilled(oracle):
     buf[slot.size + 7] ^= 1
     with pytest.raises(oracle.ChecksumError):
         oracle.decode_segment(slot2, buf, oracle.BF16, 32, 16)
+
+
+# ------------------------------------------------------------ INT8 record codec
+def _rows_segment(oracle, values_at, T=4, H=8, D=128, seed=0, dtype=1):
+    """A segment of T tokens x H heads: N(0,1) values, with given vectors
+    overwritten ({(t, h): values})."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T * H, D)).astype(np.float32)
+    for (t, h), vals in values_at.items():
+        x[t * H + h] = 0.0
+        x[t * H + h, :len(vals)] = vals
+    return _bits(x, dtype), x
+
+
+def test_int8_record_sizes(oracle):
+    """Row and record sizes are the page's: 1,040 data bytes padded to 1,152
+    (9 x 128) at 8 heads x 128; 43.75% less than a 2,048-byte BF16 row,
+    about 1.78x the tokens per budget."""
+    g = golden("int8_record_sizes.json")
+    H, D = g["kv_heads"], g["head_dim"]
+    assert H * D == g["int8_bytes"] and 2 * H == g["scale_bytes"]
+    assert g["int8_bytes"] + g["scale_bytes"] == g["raw_record"]
+    assert oracle.row_bytes(D, H) == g["record"] == 9 * 128
+    assert 1 - g["record"] / g["bf16_row"] == g["saving"]
+    assert round(g["bf16_row"] / g["record"], 2) == g["capacity_ratio_rounded"]
+    # slot: 32-byte header, rows from byte 128, 256-byte alignment
+    T = 16
+    assert oracle.slot_bytes(oracle.INT8_ROWS, D, T * H, H) == (128 + T * 1152 + 255) // 256 * 256
+    for D2, H2 in ((32, 1), (64, 3), (256, 40)):
+        assert oracle.row_bytes(D2, H2) % 128 == 0 and 0 <= oracle.row_bytes(D2, H2) - (H2 * D2 + 2 * H2) < 128
+
+
+def test_int8_record_worked_example_and_layout(oracle):
+    """The page's worked example (1.0, 0.5, -0.2, 0.0 -> 127, 64, -25, 0)
+    planted in token 1, head 5: its codes sit at byte 128 + 1*1152 + 5*128
+    of the slot, its BF16 scale after the row's 8 code blocks, the row
+    padding and an all-zero head are zero, and the zero head restores to
+    exactly zero."""
+    g = golden("int8_worked_example.json")
+    vec, _ = _rows_segment(oracle, {(1, 5): g["values"], (2, 3): [0.0]})
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.INT8_ROWS, heads=8)
+    assert st == oracle.SEG_ENCODED and slot[1] == oracle.INT8_ROWS
+    R = 1152
+    row1 = slot[128 + R:128 + 2 * R]
+    assert list(row1[5 * 128:5 * 128 + 4].view(np.int8)) == g["codes"]
+    assert not row1[5 * 128 + 4:6 * 128].any()
+    assert int(slot[12:16].view(np.uint32)[0]) == 4 * R                 # stored length: the rows
+    assert not slot[32:128].any()                                        # gap before the rows
+    for t in range(4):
+        assert not slot[128 + t * R + 1040:128 + (t + 1) * R].any()      # row padding
+    row2 = slot[128 + 2 * R:128 + 3 * R]
+    assert not row2[3 * 128:4 * 128].any()                               # zero head: zero codes
+    out = oracle.decode_segment(slot, None, oracle.BF16, 128, 32, heads=8)
+    assert not out[2 * 8 + 3].any()                                      # ... restored to exact +0
+
+
+def test_int8_record_power_of_two_amax_closed_form(oracle):
+    """amax = 2^k: amax/127 = 2^(k-7) * 1.00787..., whose BF16 rounding is
+    2^(k-7) * 129/128; x = 2^(k-1) then quotes 63.5039 -> code 64, and the
+    amax element restores to 127*129*2^(k-14) = 2^k * 16383/16384, which
+    rounds to 2^k in BF16 (hand-derived; k from -39 to 60, above the 1e-12
+    floor).  Below the floor (2^-60) the scale is the floor's, and every
+    code is 0."""
+    vec, _ = _rows_segment(oracle, {(0, 0): [2.0 ** -60, -(2.0 ** -61)]}, T=16, H=8, D=32)
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.INT8_ROWS, heads=8)
+    assert st == oracle.SEG_ENCODED and not slot[128:128 + 32].any()
+    for k in range(-39, 61, 7):
+        a = np.float32(2.0) ** k
+        vec, _ = _rows_segment(oracle, {(0, 0): [a, a / 2, -a, a / 4]}, T=16, H=8, D=32, seed=k + 100)
+        slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.INT8_ROWS, heads=8)
+        assert st == oracle.SEG_ENCODED and slot[1] == oracle.INT8_ROWS
+        R = oracle.row_bytes(32, 8)
+        row = slot[128:128 + R]
+        codes = list(row[:4].view(np.int8))
+        assert codes == [127, 64, -127, 32], (k, codes)
+        s = float(oracle.bf16_to_f32(row[256:258].view(np.uint16))[0])
+        assert s == float(a) * 129.0 / 16384.0
+        out = oracle.src_to_f32(oracle.decode_segment(slot, None, oracle.BF16, 32, 128, heads=8)[0, :3],
+                                oracle.BF16)
+        assert list(out) == [float(a), float(a) * 64 * 129 / 16384, -float(a)]
+
+
+def test_int8_record_amax_codes_127_over_bf16_values(oracle):
+    """Every third BF16 magnitude from 2^-39 (above the 1e-12 floor) to 2^100
+    as a vector's amax encodes to code 127: the BF16-rounded scale is within
+    2^-9 of amax/127, which keeps the quotient within (126.5, 127.5)."""
+    mags = np.arange(0x2C00, 0x7180, 3, dtype=np.uint32)                 # BF16 bit patterns
+    vals = (mags << 16).view(np.float32)
+    H, D, T = 8, 32, 16
+    per = T * H
+    for i in range(0, len(vals), per):
+        chunk = vals[i:i + per]
+        x = np.zeros((per, D), np.float32)
+        x[:len(chunk), 0] = chunk
+        x[:len(chunk), 1] = -chunk / 3
+        slot, st, _ = oracle.encode_segment(_bits(x, oracle.BF16), oracle.BF16, oracle.INT8_ROWS, heads=H)
+        assert st == oracle.SEG_ENCODED
+        R = oracle.row_bytes(D, H)
+        for v in range(len(chunk)):
+            t, h = divmod(v, H)
+            assert np.int8(slot[128 + t * R + h * D]) == 127
+
+
+def test_int8_record_error_bound(oracle):
+    """|x - x_hat| <= s/2 (rounding to the code) + 127*s*2^-24 (FP32
+    quotient) + half an output ulp, with s the stored BF16 scale; BF16 and
+    FP16 outputs."""
+    rng = np.random.default_rng(12)
+    H, D, T = 4, 64, 16
+    for dtype in (oracle.BF16, oracle.FP16):
+        x = (rng.standard_normal((T * H, D)) * np.exp(rng.standard_normal((T * H, 1)) * 2)).astype(np.float32)
+        bits = _bits(x, dtype)
+        xs = oracle.src_to_f32(bits, dtype).astype(np.float64)
+        slot, st, _ = oracle.encode_segment(bits, dtype, oracle.INT8_ROWS, heads=H)
+        assert st == oracle.SEG_ENCODED
+        out = oracle.src_to_f32(oracle.decode_segment(slot, None, dtype, D, T * H, heads=H), dtype).astype(np.float64)
+        R = oracle.row_bytes(D, H)
+        for v in range(T * H):
+            t, h = divmod(v, H)
+            s = float(oracle.bf16_to_f32(slot[128 + t * R + H * D + 2 * h:128 + t * R + H * D + 2 * h + 2]
+                                         .view(np.uint16))[0])
+            ulp = np.spacing(np.abs(out[v]).astype(np.float32 if dtype == oracle.BF16 else np.float16))
+            half = ulp.astype(np.float64) * (2 ** 16 if dtype == oracle.BF16 else 1) / 2
+            bound = s / 2 + 127 * s * 2.0 ** -24 + half
+            assert np.all(np.abs(xs[v] - out[v]) <= bound + 1e-30), v
+
+
+def test_int8_record_nonfinite_raw_and_crc(oracle):
+    """A nonfinite value keeps the segment raw (spilled bit-exactly); with the
+    CRC option the checksum covers the rows -- padding included -- and a
+    flipped padding byte is caught."""
+    vec, _ = _rows_segment(oracle, {(0, 1): [np.inf]}, T=16, H=4, D=64)
+    slot, st, raw = oracle.encode_segment(vec, oracle.BF16, oracle.INT8_ROWS, heads=4)
+    assert st == oracle.SEG_RAW_DATA and np.array_equal(raw.view(np.uint16).reshape(vec.shape), vec)
+    vec, _ = _rows_segment(oracle, {}, T=16, H=4, D=64)
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, oracle.INT8_ROWS, heads=4, crc=True)
+    assert st == oracle.SEG_ENCODED
+    R = oracle.row_bytes(64, 4)
+    assert slot[2] & oracle.FLAG_CRC32
+    assert int(slot[24:28].view(np.uint32)[0]) == oracle.crc32(slot[128:128 + 16 * R])
+    oracle.decode_segment(slot, None, oracle.BF16, 64, 64, heads=4)
+    bad = slot.copy()
+    bad[128 + R - 1] ^= 1                                                # padding of row 0
+    with pytest.raises(oracle.ChecksumError):
+        oracle.decode_segment(bad, None, oracle.BF16, 64, 64, heads=4)
