@@ -123,6 +123,11 @@ WORKLOADS = {
                      "BF16, separate K/V, 2048 pages (32K tokens)",
     "int8_fp8_stress": "{codec} K and V with 1% of segments holding NaN/Inf/+-450/+-1000: 32 layers, 8 KV heads, "
                        "D=128, BF16, separate K/V, 8192 pages (128K tokens), decoded into shuffled pages",
+    "int8_records_qwen3": "INT8 host-pool records (BF16 scales, 1,152-byte token rows) K and V, Qwen3-8B shape: "
+                          "36 layers, 8 KV heads, D=128, BF16, separate K/V, 3392 random pages of a 4096-block "
+                          "pool (54,272 tokens)",
+    "k8v8_packed": "K8/V8: FP8 E4M3FN K and V with per-token/head scales, Qwen3-8B shape: 36 layers, 8 KV heads, "
+                   "D=128, FP16, vLLM packed [2048 blocks, 8, 16, 256]",
 }
 
 

@@ -52,6 +52,13 @@
  *  Codes are packed LSB-first (element i at bits [b*i, b*i+b) of the vector's
  *  code block); metadata per vector: FP32 scale (FP8_DYNAMIC, INT8), FP16 min
  *  + FP16 scale (UNIFORM*), FP16 norm (TQ*).
+ *  KVC_INT8_ROWS lays its stored bytes out as records instead [HIQ "Why
+ *  exactly 1,152 bytes?"]: from byte 128 of the slot (bytes 32..127 zero),
+ *  one row per token: the INT8 codes of heads 0..H-1 (D bytes each), then
+ *  their BF16 scales, then zeros to a multiple of 128 bytes (1,152 bytes at
+ *  8 heads x 128).  Per vector: a = max(amax, BF16(1e-12)); scale =
+ *  BF16(RN(a/127)); q = clamp(RNE(RN(x/scale)), +-127); decode rounds
+ *  q*scale once to the output type.  stored_len = tokens * row bytes.
  *  A segment that must stay raw because of its data (a nonfinite value, an
  *  FP8 source value with |x| > 448, an FP16 metadata overflow) keeps its
  *  slot header (flags RAW_DATA) and its raw bytes go to the spill region of
@@ -127,7 +134,8 @@ typedef enum {
   KVC_UNIFORM3 = 5,     /* per-vector uniform 3-bit, FP16 min and scale [OKV-SF] */
   KVC_UNIFORM4 = 6,     /* per-vector uniform 4-bit, FP16 min and scale [OKV-SF] */
   KVC_TQ3 = 7,          /* TurboQuant MSE 3-bit + FP16 norm [OKV-SF] */
-  KVC_TQ4 = 8           /* TurboQuant MSE 4-bit + FP16 norm [OKV-SF] */
+  KVC_TQ4 = 8,          /* TurboQuant MSE 4-bit + FP16 norm [OKV-SF] */
+  KVC_INT8_ROWS = 9     /* INT8 record: BF16 scales, 128-byte-padded token rows [HIQ] */
 } kvc_codec_id;
 
 /* Codec choice per component.  fixed_scales: host array [layers][2] (K, V)

@@ -84,17 +84,21 @@ int codec_meta(int c) {
     default: return 0;
   }
 }
-uint64_t slot_size(int codec, uint32_t d, uint32_t n_vec) {
+// heads: vectors per token (n_vec = tokens * heads); only the record codec's
+// slot depends on it
+uint64_t slot_size(int codec, uint32_t d, uint32_t n_vec, uint32_t heads) {
+  if (codec == KVC_INT8_ROWS)
+    return align_up(kRowsOffset + (uint64_t)(n_vec / heads) * row_bytes(d, heads), KVC_SLOT_ALIGN);
   const uint64_t per_vec = (uint64_t)codec_bits(codec) * d / 8 + (uint64_t)codec_meta(codec);
   return align_up(KVC_HEADER_BYTES + per_vec * n_vec, KVC_SLOT_ALIGN);
 }
 // codec used after the static rules: raw for protected layers and KVC_RAW,
 // raw for sources above 16 MiB, raw if the aligned slot saves < 12.5%.
-int effective_codec(int codec, uint32_t d, uint32_t n_vec, bool prot) {
+int effective_codec(int codec, uint32_t d, uint32_t n_vec, uint32_t heads, bool prot) {
   const uint64_t orig = (uint64_t)n_vec * d * 2;
   if (prot || codec == KVC_RAW) return KVC_RAW;
   if (orig > KVC_MAX_SEGMENT_BYTES) return KVC_RAW;
-  if (8 * slot_size(codec, d, n_vec) > 7 * orig) return KVC_RAW;
+  if (8 * slot_size(codec, d, n_vec, heads) > 7 * orig) return KVC_RAW;
   return codec;
 }
 bool is_protected(const kvc_codec* c, uint32_t l) {
@@ -239,7 +243,7 @@ kvc_status check_layout(const kvc_layout* L) {
 }
 
 kvc_status check_codec(const kvc_layout* L, const kvc_codec* c) {
-  if (!c || c->k > KVC_TQ4 || c->v > KVC_TQ4) return KVC_E_ARG;
+  if (!c || c->k > KVC_INT8_ROWS || c->v > KVC_INT8_ROWS) return KVC_E_ARG;
   if ((c->flags & ~KVC_CODEC_CRC32) || c->reserved) return KVC_E_ARG;
   if (c->k == KVC_FP8_FIXED || c->v == KVC_FP8_FIXED) {
     if (!c->fixed_scales) return KVC_E_ARG;
@@ -274,9 +278,9 @@ Plan make_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages) {
   for (uint32_t l = 0; l < L->layers; l++) {
     const bool prot = is_protected(c, l);
     for (int comp = 0; comp < 2; comp++) {
-      const int e = effective_codec(comp ? c->v : c->k, L->head_dim, n_vec, prot);
+      const int e = effective_codec(comp ? c->v : c->k, L->head_dim, n_vec, L->kv_heads, prot);
       p.eff[comp][l] = (uint8_t)e;
-      p.slot[comp][l] = (uint32_t)slot_size(e, L->head_dim, n_vec);
+      p.slot[comp][l] = (uint32_t)slot_size(e, L->head_dim, n_vec, L->kv_heads);
       if (e != KVC_RAW) p.encodable += n_pages;
     }
     p.layer_off[l] = off;
@@ -485,6 +489,7 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
     P->walk_wrap = st - H * sh;                         // modulo 2^32
   }
   P->tokens = L->tokens_per_page;
+  P->row_bytes = row_bytes(L->head_dim, L->kv_heads);
   P->dtype = L->dtype;
   P->crc = (c->flags & KVC_CODEC_CRC32) ? 1u : 0u;
   sign_mask(c->seed, L->head_dim, P->sign_mask);

@@ -27,6 +27,12 @@ constexpr int groups_per_workgroup(int d, int nt) { return nt / lanes_per_vector
 constexpr uint64_t kSlotAlign = KVC_SLOT_ALIGN;
 constexpr uint32_t kHeaderBytes = KVC_HEADER_BYTES;
 
+// INT8 record codec (KVC_INT8_ROWS): one row per token holding its heads'
+// codes and their BF16 scales, padded to a multiple of 128 bytes; the rows
+// start kRowsOffset bytes into the slot.
+constexpr uint32_t kRowsOffset = 128;
+constexpr uint32_t row_bytes(uint32_t d, uint32_t heads) { return (heads * d + 2 * heads + 127) / 128 * 128; }
+
 // Bucketize table for TurboQuant encode: cell c of the real line,
 // c = RNE(kCellScale * z) + kCellOffset, holds the one threshold that may lie
 // inside the cell (or +inf) and the count of thresholds below the cell, so
@@ -110,6 +116,7 @@ struct CallParams {
   // seg_base + workgroups) of the call (a range of whole layers).
   uint32_t seg_base;
   uint32_t n_pages, n_layers, heads, tokens;
+  uint32_t row_bytes;                         // KVC_INT8_ROWS: bytes of one token row
   uint32_t dtype;                             // kvc_dtype
   uint32_t num_blocks;                        // page ids must be below this (guard)
   uint32_t sign_mask[8];                      // TurboQuant signs, bit i = (sigma_i < 0)

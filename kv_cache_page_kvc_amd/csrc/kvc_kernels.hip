@@ -181,6 +181,7 @@ template <int DT> struct Lim {
 };
 
 __device__ __forceinline__ float f16_round(float x) { return (float)(_Float16)x; }
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
 __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
@@ -228,6 +229,7 @@ struct SegCtx {
   uint64_t heads_magic;     // v / heads = (v * heads_magic) >> 32 for v < 2^16
   uint32_t st, sh;          // element strides of token and head
   uint32_t walk_dh, walk_step, walk_wrap;
+  uint32_t row_bytes;       // record codec: bytes of one token row
 };
 
 // A lane's current vector: its head and its element offset in the page
@@ -266,12 +268,14 @@ __device__ __forceinline__ const T* byte_at(const T* base, uint32_t off) {
 
 // ------------------------------------------------------------------ encoders
 // Each returns 1 if this vector forces the segment raw.
-enum Codec { C_RAW = 0, C_FP8D = 1, C_FP8F = 2, C_FP8Y = 3, C_INT8 = 4, C_U3 = 5, C_U4 = 6, C_TQ3 = 7, C_TQ4 = 8 };
+enum Codec { C_RAW = 0, C_FP8D = 1, C_FP8F = 2, C_FP8Y = 3, C_INT8 = 4, C_U3 = 5, C_U4 = 6, C_TQ3 = 7, C_TQ4 = 8,
+             C_I8R = 9 };
 
 template <int C> struct CodecInfo {
   static constexpr int bits = (C == C_U3 || C == C_TQ3) ? 3 : ((C == C_U4 || C == C_TQ4) ? 4 : 8);
   static constexpr int meta = (C == C_FP8Y || C == C_INT8 || C == C_U3 || C == C_U4) ? 4
-                            : ((C == C_TQ3 || C == C_TQ4) ? 2 : 0);
+                            : ((C == C_TQ3 || C == C_TQ4 || C == C_I8R) ? 2 : 0);
+  static constexpr bool rows = C == C_I8R;       // token-row record layout
   static constexpr bool tq = C == C_TQ3 || C == C_TQ4;
   static constexpr bool uni = C == C_U3 || C == C_U4;
   static constexpr bool fp8 = C == C_FP8D || C == C_FP8F || C == C_FP8Y;
@@ -419,13 +423,28 @@ __device__ __forceinline__ constexpr uint32_t magic_sum() {
   return s;
 }
 
+// Byte offsets in the slot of vector v's codes (cv) and metadata (mv):
+// after the header, the codes block then the metadata block; for the record
+// codec, in token row v / heads from kRowsOffset, the codes of head v % heads
+// then, after all the row's codes, its BF16 scale.
+template <int D, int C>
+__device__ __forceinline__ void vec_offsets(const SegCtx& s, int v, uint32_t meta_blk, uint32_t& cv, uint32_t& mv) {
+  if constexpr (CodecInfo<C>::rows) {
+    const uint32_t t = (uint32_t)(((uint64_t)(uint32_t)v * s.heads_magic) >> 32), h = (uint32_t)v - t * s.heads;
+    const uint32_t row = kRowsOffset + t * s.row_bytes;
+    cv = row + h * D;
+    mv = row + (uint32_t)s.heads * D + 2 * h;
+  } else {
+    cv = kHeaderBytes + (uint32_t)v * (CodecInfo<C>::bits * D / 8);
+    mv = meta_blk + (uint32_t)v * CodecInfo<C>::meta;
+  }
+}
+
 template <int D, int DT, int C>
-__device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, uint8_t* slot, uint32_t meta_blk,
+__device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv, const Lane& ln, uint8_t* slot,
                                              float fixed, const LaneSigns<D>& ls, const CellEntry* cells) {
   constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP;
   constexpr int BITS = CodecInfo<C>::bits;
-  constexpr int CB = BITS * D / 8;
-  const uint32_t cv = kHeaderBytes + (uint32_t)v * CB;   // byte offset of the vector's codes
   if constexpr (CodecInfo<C>::tq) {
     // sigma (and the lane parity sign) applied to the packed source words
 #pragma unroll
@@ -441,7 +460,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
   for (int k = 0; k < NCH; k++) unpack8<DT>(w[k], x + 8 * k);
   int bad = 0;
 
-  if constexpr (CodecInfo<C>::fp8 || C == C_INT8) {
+  if constexpr (CodecInfo<C>::fp8 || C == C_INT8 || C == C_I8R) {
     uint32_t am = 0;
 #pragma unroll
     for (int k = 0; k < NCH; k++) am = max(am, absmax_bits(w[k]));
@@ -454,10 +473,14 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
       s = fmaxf(bits_to_f32<DT>(am), 1e-12f) * r448;
     }
     if constexpr (C == C_INT8) s = div_const<127>(fmaxf(bits_to_f32<DT>(am), 1e-12f));
+    // record codec: floor and scale are BF16 values; RN(a/127) is rounded to
+    // binary32 first, then to BF16
+    if constexpr (C == C_I8R)
+      s = bf16_round(materialize_f32(div_const<127>(fmaxf(bits_to_f32<DT>(am), bf16_round(1e-12f)))));
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
       uint32_t lo, hi;
-      if constexpr (C == C_INT8) {
+      if constexpr (C == C_INT8 || C == C_I8R) {
         uint32_t b[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -485,7 +508,9 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
       store_codes<D, 8>(slot, cv, k, ln.p, lo, hi);
     }
     if constexpr (C == C_FP8Y || C == C_INT8)
-      if (ln.p == 0) *byte_at(reinterpret_cast<float*>(slot), meta_blk + (uint32_t)v * 4) = s;
+      if (ln.p == 0) *byte_at(reinterpret_cast<float*>(slot), mv) = s;
+    if constexpr (C == C_I8R)
+      if (ln.p == 0) *byte_at(reinterpret_cast<uint16_t*>(slot), mv) = (uint16_t)(__float_as_uint(s) >> 16);
   }
 
   if constexpr (CodecInfo<C>::uni) {
@@ -523,8 +548,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
     // bounded by the FP16 range of d and by y <= 2^24), so bit 29 (exponent
     // bit 6) of t is clear; a NaN source value makes t NaN, which sets it.
     bad |= (int)((group_or<LOGP>(tor) >> 29) & 1u);
-    if (ln.p == 0)
-      *byte_at(reinterpret_cast<uint32_t*>(slot), meta_blk + (uint32_t)v * 4) = f16_bits(mh) | (f16_bits(sh) << 16);
+    if (ln.p == 0) *byte_at(reinterpret_cast<uint32_t*>(slot), mv) = f16_bits(mh) | (f16_bits(sh) << 16);
   }
 
   if constexpr (CodecInfo<C>::tq) {
@@ -556,7 +580,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, int v, const Lane& ln, ui
       }
       store_codes<D, BITS>(slot, cv, k, ln.p, acc, 0);
     }
-    if (ln.p == 0) *byte_at(reinterpret_cast<uint16_t*>(slot), meta_blk + (uint32_t)v * 2) = (uint16_t)f16_bits(nh);
+    if (ln.p == 0) *byte_at(reinterpret_cast<uint16_t*>(slot), mv) = (uint16_t)f16_bits(nh);
   }
   return bad;
 }
@@ -595,7 +619,11 @@ __device__ __forceinline__ int encode_segment_vectors(const SegCtx& s, const Lan
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int v = v0 + u * GW;
-      if (v < s.n_vec) bad |= encode_vector<D, DT, C>(w[u], v, ln, image, meta_blk, fixed, ls, cells);
+      if (v < s.n_vec) {
+        uint32_t cv, mv;
+        vec_offsets<D, C>(s, v, meta_blk, cv, mv);
+        bad |= encode_vector<D, DT, C>(w[u], cv, mv, ln, image, fixed, ls, cells);
+      }
     }
   }
   return bad;
@@ -631,6 +659,21 @@ __device__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
 template <int NT>
 __device__ __forceinline__ void zero_pad(uint8_t* slot, uint32_t from, uint32_t to) {
   for (uint32_t b = from + 2 * threadIdx.x; b < to; b += 2 * NT) *byte_at(reinterpret_cast<uint16_t*>(slot), b) = 0;
+}
+
+// zero the bytes of a record-codec slot that no vector writes: the gap
+// [32, kRowsOffset) after the header, each token row's padding after its
+// codes and scales, and the slot's tail after the last row
+template <int NT>
+__device__ __forceinline__ void zero_row_gaps(uint8_t* slot, uint32_t tokens, uint32_t heads, uint32_t d,
+                                              uint32_t row_bytes, uint32_t slot_bytes) {
+  zero_pad<NT>(slot, kHeaderBytes, kRowsOffset);
+  const uint32_t used = heads * (d + 2), pad_half = (row_bytes - used) / 2;   // used is even
+  for (uint32_t i = threadIdx.x; i < tokens * pad_half; i += NT) {
+    const uint32_t t = i / pad_half, j = i - t * pad_half;
+    *byte_at(reinterpret_cast<uint16_t*>(slot), kRowsOffset + t * row_bytes + used + 2 * j) = 0;
+  }
+  zero_pad<NT>(slot, kRowsOffset + tokens * row_bytes, slot_bytes);
 }
 
 // the two 16-byte words of a slot header
@@ -675,7 +718,7 @@ __device__ __forceinline__ void write_header_desc(uint8_t* slot, kvc_segment_des
   write_desc(desc, slot_off, format, flags, status, d, n_vec, stored, spill, crc);
 }
 
-// codes + metadata bytes of a coded segment
+// codes + metadata bytes of a coded segment (block layout)
 __device__ __forceinline__ uint32_t payload_bytes(int codec, int d, uint32_t n_vec) {
   int bits = 8, meta = 0;
   switch (codec) {
@@ -686,6 +729,16 @@ __device__ __forceinline__ uint32_t payload_bytes(int codec, int d, uint32_t n_v
   if (codec == C_FP8Y || codec == C_INT8 || codec == C_U3 || codec == C_U4) meta = 4;
   if (codec == C_TQ3 || codec == C_TQ4) meta = 2;
   return n_vec * (uint32_t)(bits * d / 8 + meta);
+}
+// stored bytes of a coded segment and where they start in the slot: the
+// codes and metadata blocks after the header, or the record codec's rows
+__device__ __forceinline__ uint32_t stored_offset(int codec) {
+  return codec == C_I8R ? kRowsOffset : kHeaderBytes;
+}
+__device__ __forceinline__ uint32_t payload_bytes(int codec, int d, uint32_t n_vec, uint32_t heads,
+                                                  uint32_t row_bytes) {
+  if (codec == C_I8R) return n_vec / heads * row_bytes;
+  return payload_bytes(codec, d, n_vec);
 }
 
 // ------------------------------------------------------------------ CRC-32
@@ -797,6 +850,7 @@ __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const La
     case C_U4: return encode_segment_vectors<D, DT, C_U4, NT>(s, ln, fixed, ls, cells, image);
     case C_TQ3: return encode_segment_vectors<D, DT, C_TQ3, NT>(s, ln, fixed, ls, cells, image);
     case C_TQ4: return encode_segment_vectors<D, DT, C_TQ4, NT>(s, ln, fixed, ls, cells, image);
+    case C_I8R: return encode_segment_vectors<D, DT, C_I8R, NT>(s, ln, fixed, ls, cells, image);
     default: return 0;
   }
 }
@@ -845,6 +899,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   s.walk_dh = p.walk_dh;
   s.walk_step = p.walk_step;
   s.walk_wrap = p.walk_wrap;
+  s.row_bytes = p.row_bytes;
   const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
   const uint32_t slot_bytes = E.slot_bytes;
   kvc_segment_desc* desc = p.desc + seg;
@@ -877,7 +932,9 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   if (tq) make_lane_signs<D>(p.sign_mask, ln.p, true, ls);
   const float fixed = E.fixed;
 
-  const uint32_t payload = payload_bytes(codec, D, (uint32_t)s.n_vec);
+  const uint32_t payload = payload_bytes(codec, D, (uint32_t)s.n_vec, p.heads, p.row_bytes);
+  const uint32_t stored_at = stored_offset(codec);
+  const bool rows = codec == C_I8R;
 
   // The slot body (codes, metadata, zero padding) is assembled in LDS when it
   // fits, then written with full-line nontemporal stores; partial-line
@@ -886,10 +943,12 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const bool staged = slot_bytes <= p.stage_bytes;
   if (staged) {
     bad = encode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cells, s_stage);
-    zero_pad<NT>(s_stage, kHeaderBytes + payload, slot_bytes);
+    if (rows) zero_row_gaps<NT>(s_stage, p.tokens, p.heads, D, p.row_bytes, slot_bytes);
+    else zero_pad<NT>(s_stage, kHeaderBytes + payload, slot_bytes);
   } else {
     bad = encode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cells, s.slot);
-    zero_pad<NT>(s.slot, kHeaderBytes + payload, slot_bytes);
+    if (rows) zero_row_gaps<NT>(s.slot, p.tokens, p.heads, D, p.row_bytes, slot_bytes);
+    else zero_pad<NT>(s.slot, kHeaderBytes + payload, slot_bytes);
   }
   const int any_bad = __syncthreads_or(bad);
   const uint32_t aux = codec == C_FP8F ? __float_as_uint(fixed) : 0u;
@@ -897,7 +956,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
     uint32_t c = 0;
     if (crc) {
       if (threadIdx.x < kCrcLanes) {
-        c = crc32_wave(LdsBytes{s_stage + kHeaderBytes}, payload, ct);
+        c = crc32_wave(LdsBytes{s_stage + stored_at}, payload, ct);
         if (threadIdx.x == 0) s_crc = c;
       }
       __syncthreads();
@@ -918,7 +977,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
     for (uint32_t u = 2 + threadIdx.x; u < slot_bytes / 16; u += NT)
       st_stream16(s.slot + 16 * u, *reinterpret_cast<const uint4*>(s_stage + 16 * u));
   if (!any_bad) {
-    const uint32_t c = crc ? crc32_written(s.slot + kHeaderBytes, payload, ct) : 0u;
+    const uint32_t c = crc ? crc32_written(s.slot + stored_at, payload, ct) : 0u;
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, codec, crc_flag, KVC_SEG_ENCODED, DT, comp, D, s.n_vec, payload, 0,
                         aux, c);
@@ -969,16 +1028,15 @@ struct VecCodes {
   uint32_t meta;
 };
 
-// meta_blk: byte offset of the metadata block in the slot
+// cv, mv: byte offsets of the vector's codes and metadata in the slot
 template <int D, int C>
-__device__ __forceinline__ void load_vec_codes(const uint8_t* slot, uint32_t meta_blk, int v, const Lane& ln,
+__device__ __forceinline__ void load_vec_codes(const uint8_t* slot, uint32_t cv, uint32_t mv, const Lane& ln,
                                                VecCodes<D>& vc) {
-  constexpr int BITS = CodecInfo<C>::bits, CB = BITS * D / 8, META = CodecInfo<C>::meta;
-  const uint32_t cv = kHeaderBytes + (uint32_t)v * CB;
+  constexpr int BITS = CodecInfo<C>::bits, META = CodecInfo<C>::meta;
 #pragma unroll
   for (int k = 0; k < Geo<D>::NCH; k++) vc.c[k] = load_codes<D, BITS>(slot, cv, k, ln.p);
-  if constexpr (META == 4) vc.meta = *byte_at(reinterpret_cast<const uint32_t*>(slot), meta_blk + (uint32_t)v * 4);
-  else if constexpr (META == 2) vc.meta = *byte_at(reinterpret_cast<const uint16_t*>(slot), meta_blk + (uint32_t)v * 2);
+  if constexpr (META == 4) vc.meta = *byte_at(reinterpret_cast<const uint32_t*>(slot), mv);
+  else if constexpr (META == 2) vc.meta = *byte_at(reinterpret_cast<const uint16_t*>(slot), mv);
   else vc.meta = 0;
 }
 
@@ -989,10 +1047,11 @@ __device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane&
   constexpr int E = Geo<D>::E, NCH = Geo<D>::NCH, LOGP = Geo<D>::LOGP, P = Geo<D>::P;
   constexpr int BITS = CodecInfo<C>::bits;
   float y[E];
-  if constexpr (CodecInfo<C>::fp8 || C == C_INT8) {
+  if constexpr (CodecInfo<C>::fp8 || C == C_INT8 || C == C_I8R) {
     float s = 1.0f;
     if constexpr (C == C_FP8F) s = fixed;
     if constexpr (C == C_FP8Y || C == C_INT8) s = __uint_as_float(vc.meta);
+    if constexpr (C == C_I8R) s = __uint_as_float(vc.meta << 16);          // BF16 scale
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
       const uint2 c = vc.c[k];
@@ -1000,7 +1059,7 @@ __device__ __forceinline__ void decode_vector(const VecCodes<D>& vc, const Lane&
       for (int j = 0; j < 8; j++) {
         const uint32_t word = j < 4 ? c.x : c.y;
         float val;
-        if constexpr (C == C_INT8) {
+        if constexpr (C == C_INT8 || C == C_I8R) {
           val = (float)(int8_t)(word >> (8 * (j & 3)));
         } else {
           switch (j & 3) {
@@ -1084,7 +1143,11 @@ __device__ __forceinline__ void decode_segment_vectors(const SegCtx& s, const La
     VecCodes<D> vc[U];
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (v0 + u * GW < s.n_vec) load_vec_codes<D, C>(image, meta_blk, v0 + u * GW, ln, vc[u]);
+      if (v0 + u * GW < s.n_vec) {
+        uint32_t cv, mv;
+        vec_offsets<D, C>(s, v0 + u * GW, meta_blk, cv, mv);
+        load_vec_codes<D, C>(image, cv, mv, ln, vc[u]);
+      }
 #pragma unroll
     for (int u = 0; u < U; u++) {
       if (v0 + u * GW < s.n_vec) decode_vector<D, DT, C>(vc[u], ln, page, pos.off, fixed, ls, cent);
@@ -1134,6 +1197,7 @@ __device__ __forceinline__ void decode_codec(int codec, const SegCtx& s, const L
     case C_U4: decode_segment_vectors<D, DT, C_U4, NT>(s, ln, fixed, ls, cent, image); break;
     case C_TQ3: decode_segment_vectors<D, DT, C_TQ3, NT>(s, ln, fixed, ls, cent, image); break;
     case C_TQ4: decode_segment_vectors<D, DT, C_TQ4, NT>(s, ln, fixed, ls, cent, image); break;
+    case C_I8R: decode_segment_vectors<D, DT, C_I8R, NT>(s, ln, fixed, ls, cent, image); break;
     default: break;
   }
 }
@@ -1169,6 +1233,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   s.walk_dh = p.walk_dh;
   s.walk_step = p.walk_step;
   s.walk_wrap = p.walk_wrap;
+  s.row_bytes = p.row_bytes;
   const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
 
   // A coded slot that fits is read whole into LDS in one round of 16-byte
@@ -1196,7 +1261,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   if (raw_data) ok = ok && format == KVC_RAW && !(flags & KVC_FLAG_CAPACITY) && raw_bytes <= p.buf_bytes &&
                      spill >= p.slot_region && spill <= p.buf_bytes - raw_bytes;
   else ok = ok && format == codec;
-  const uint32_t stored = raw_data || codec == C_RAW ? raw_bytes : payload_bytes(codec, D, (uint32_t)s.n_vec);
+  const uint32_t stored =
+      raw_data || codec == C_RAW ? raw_bytes : payload_bytes(codec, D, (uint32_t)s.n_vec, p.heads, p.row_bytes);
+  const uint32_t stored_at = stored_offset(codec);
   ok = ok && h0.w == stored && ((flags & KVC_FLAG_CRC32) != 0) == CRC;
   if (!ok) {
     if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 1;
@@ -1207,8 +1274,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
     __syncthreads();                                      // CRC tables in LDS
     if (threadIdx.x < kCrcLanes) {
       const uint32_t c = raw_data ? crc32_wave(GlobalBytes{p.buf + spill}, stored, ct)
-                         : staged ? crc32_wave(LdsBytes{s_stage + kHeaderBytes}, stored, ct)
-                                  : crc32_wave(GlobalBytes{s.slot + kHeaderBytes}, stored, ct);
+                         : staged ? crc32_wave(LdsBytes{s_stage + stored_at}, stored, ct)
+                                  : crc32_wave(GlobalBytes{s.slot + stored_at}, stored, ct);
       if (threadIdx.x == 0) s_crc_ok = c == h1.z;
     }
     __syncthreads();

@@ -52,10 +52,11 @@ def layout(kind=kvc.KVC_SEPARATE_NHD, dtype=kvc.KVC_BF16, L=4, H=8, D=128, T=16,
 
 
 @pytest.mark.parametrize("ck,cv", [("TQ4", "UNIFORM4"), ("TQ3", "UNIFORM3"), ("FP8_DYNAMIC", "INT8"),
-                                   ("RAW", "FP8_FIXED"), ("FP8_DIRECT", "RAW")])
+                                   ("RAW", "FP8_FIXED"), ("FP8_DIRECT", "RAW"), ("INT8_ROWS", "TQ4")])
 @pytest.mark.parametrize("D", [32, 64, 128, 256])
-def test_plan_matches_oracle(ck, cv, D):
-    L, H, T, n = 6, 8, 16, 37
+@pytest.mark.parametrize("H", [8, 3])
+def test_plan_matches_oracle(ck, cv, D, H):
+    L, T, n = 6, 16, 37
     prot = [0, 5]
     lay = layout(D=D, L=L, H=H, T=T)
     fixed = np.full((L, 2), 0.5, np.float32)
@@ -116,7 +117,7 @@ def test_validation_errors():
         fs = np.full((4, 2), 1.0, np.float32)
         fs[2, 0] = badscale
         assert V(ok, kvc.Codec("FP8_FIXED", "RAW", fixed_scales=fs), ids, 1 << 40) == kvc.KVC_E_ARG
-    assert V(ok, kvc.Codec(9, 0), ids, 1 << 40) == kvc.KVC_E_ARG
+    assert V(ok, kvc.Codec(10, 0), ids, 1 << 40) == kvc.KVC_E_ARG
     # codec flags: only KVC_CODEC_CRC32 is defined; reserved must be 0
     assert V(ok, kvc.Codec("TQ4", "UNIFORM4", crc=True), ids, 1 << 40) == kvc.KVC_OK
     c = kvc.Codec("TQ4", "UNIFORM4")
@@ -169,3 +170,13 @@ def test_lane_and_layer_entry_points_validate_first():
     dup = np.array([1, 1, 2], np.int32)
     assert L.kvc_restore_pages(fake, lc, cc, None, slot, dup.ctypes.data_as(ctypes.c_void_p), 3, 0, 1, None,
                                None, None) == kvc.KVC_E_DUP_DST
+
+
+def test_plan_int8_records_qwen3_row():
+    """The INT8 record codec at 8 heads x D128: each token costs one
+    1,152-byte row per component (the page's record), plus the slot's
+    128-byte lead and its 256-byte rounding."""
+    lay = layout(L=1, H=8, D=128, T=16)
+    slot, _, bpt = kvc.kvc_plan(lay, kvc.Codec("INT8_ROWS", "INT8_ROWS"), 1)
+    assert slot == 2 * ((128 + 16 * 1152 + 255) // 256 * 256)
+    assert bpt == -(-slot // 16)

@@ -89,6 +89,7 @@ CASES = {
     "tq4-u4-prot": dict(ck="TQ4", cv="UNIFORM4", protected=[0]),
     "int8-fp8dyn-spill-crc": dict(ck="INT8", cv="FP8_DYNAMIC", inject=True, crc=True),
     "tq3-u3-d256-packed-fp16": dict(ck="TQ3", cv="UNIFORM3", D=256, H=4, layout="packed", dtype="fp16"),
+    "int8rows-u4-crc": dict(ck="INT8_ROWS", cv="UNIFORM4", crc=True),
 }
 
 

@@ -93,7 +93,7 @@ def _roundtrip_case(ctx, wl, ck, cv, seed, page_ids, protected=None, fixed=None,
 
 # ----------------------------------------------------------------- small grid
 PAIRS = [("FP8_DIRECT", "FP8_DYNAMIC"), ("FP8_FIXED", "INT8"), ("TQ4", "UNIFORM4"),
-         ("TQ3", "UNIFORM3"), ("UNIFORM4", "TQ3"), ("INT8", "RAW")]
+         ("TQ3", "UNIFORM3"), ("UNIFORM4", "TQ3"), ("INT8", "RAW"), ("INT8_ROWS", "TQ4")]
 
 
 @pytest.mark.parametrize("layout", ["separate", "packed"])
@@ -132,7 +132,8 @@ def test_wide_grid(ctx, pair, dim, layout):
 
 
 @pytest.mark.parametrize("heads", [3, 12, 40])
-@pytest.mark.parametrize("pair", [("TQ4", "UNIFORM4"), ("INT8", "FP8_DYNAMIC")], ids=lambda p: f"{p[0]}-{p[1]}")
+@pytest.mark.parametrize("pair", [("TQ4", "UNIFORM4"), ("INT8", "FP8_DYNAMIC"), ("UNIFORM3", "INT8_ROWS")],
+                         ids=lambda p: f"{p[0]}-{p[1]}")
 def test_odd_head_counts(ctx, pair, heads):
     """Head counts that do not divide the group count (the per-lane vector
     walk wraps across tokens): 3 heads (12 KiB segments, one-wave
@@ -372,6 +373,31 @@ def test_k16v8_packed_full_size(ctx, vcodec):
     ids = np.arange(cfg["pages"], dtype=np.int32)
     segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 3)
     _roundtrip_case(ctx, wl, "RAW", vcodec, 0, ids, fixed=fixed, segments=segs, decode_from_oracle=False)
+
+
+def test_int8_records_qwen3_full_size(ctx):
+    """INT8 host-pool records on the Qwen3-8B shape, 36 layers x 8 heads x
+    D128 BF16, 3392 of 4096 blocks in random order: one full-size launch
+    each way, sampled segments checked bit-exactly (codes, BF16 scales, row
+    padding, decode)."""
+    cfg = inputs.CONFIGS["int8_records_qwen3"]
+    print("[case] int8 records qwen3", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
+    ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
+    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 11)
+    _roundtrip_case(ctx, wl, "INT8_ROWS", "INT8_ROWS", 0, ids, segments=segs, decode_from_oracle=False)
+
+
+def test_k8v8_packed_full_size(ctx):
+    """K8/V8 with per-token/head FP8 scales on the vLLM packed FP16 Qwen3-8B
+    layout [2048 blocks, 8 heads, 16 tokens, 256], 36 layers: full-size
+    launch, sampled segments."""
+    cfg = inputs.CONFIGS["k8v8_packed"]
+    print("[case] k8v8 packed", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "fp16", "packed", 0)
+    ids = np.arange(cfg["pages"], dtype=np.int32)
+    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 5)
+    _roundtrip_case(ctx, wl, "FP8_DYNAMIC", "FP8_DYNAMIC", 0, ids, segments=segs, decode_from_oracle=False)
 
 
 @pytest.mark.parametrize("codec", ["INT8", "FP8_DYNAMIC", "FP8_DIRECT"])
