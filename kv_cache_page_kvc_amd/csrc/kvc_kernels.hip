@@ -210,6 +210,17 @@ __device__ __forceinline__ float div_const(float a) {
   return fmaf(fmaf(-q0, (float)N, a), r, q0);
 }
 
+// x / s for a vector's scale s, from r = RN(1/s): q0 = RN(x*r), e = x - s*q0
+// (exact), RN(q0 + e*r).  For every scale the INT8, INT8 record and FP8
+// dynamic codecs form and every |x| <= the vector's amax (BF16 and FP16
+// sources, all checked exhaustively), the stored code is the one the IEEE
+// quotient gives: FP16 quotients are identical, BF16 ones differ only
+// below 2^-10, which both codes map to zero.
+__device__ __forceinline__ float div_scaled(float x, float s, float r) {
+  const float q0 = x * r;
+  return fmaf(fmaf(-q0, s, x), r, q0);
+}
+
 // RN(1/h) for a positive finite h that is an FP16 value: one Newton step
 // e = 1 - h*y0, y0 + e*y0 from the hardware estimate (within 1 ulp).  For
 // every such h, every start within 1 ulp of 1/h gives the correctly rounded
@@ -477,6 +488,8 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
     // binary32 first, then to BF16
     if constexpr (C == C_I8R)
       s = bf16_round(materialize_f32(div_const<127>(fmaxf(bits_to_f32<DT>(am), bf16_round(1e-12f)))));
+    // per-vector scales (not the caller's fixed scale) divide through RN(1/s)
+    const float rs = C == C_FP8Y || C == C_INT8 || C == C_I8R ? 1.0f / s : 0.0f;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
       uint32_t lo, hi;
@@ -484,7 +497,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
         uint32_t b[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-          float q = rintf(x[8 * k + j] / s);
+          float q = rintf(div_scaled(x[8 * k + j], s, rs));
           q = fminf(fmaxf(q, -127.0f), 127.0f);
           b[j] = (uint32_t)(int)q & 0xFFu;
         }
@@ -495,10 +508,9 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
 #pragma unroll
         for (int j = 0; j < 8; j++) {
           float t = x[8 * k + j];
-          if constexpr (C != C_FP8D) {
-            t = t / s;
-            t = fminf(fmaxf(t, -448.0f), 448.0f);
-          }
+          if constexpr (C == C_FP8Y) t = div_scaled(t, s, rs);
+          if constexpr (C == C_FP8F) t = t / s;
+          if constexpr (C != C_FP8D) t = fminf(fmaxf(t, -448.0f), 448.0f);
           q[j] = t;
         }
         const uint2 r = fp8x8(q);

@@ -1,10 +1,13 @@
 """Exhaustive proofs of the kernels' division shortcuts (CPU only).
 
-The encode kernel replaces two IEEE divisions by shorter sequences: RN(a/N)
-for the constants N = 7, 15, 127 (uniform scale, INT8 scale) and RN(1/h) for
-an FP16-valued h (the uniform reciprocal).  `fast_division_check.c` runs the
-same binary32 sequences over every input they can see and counts results
-that differ from the correctly rounded quotient.
+The encode kernel replaces IEEE divisions by shorter sequences: RN(a/N) for
+the constants N = 7, 15, 127 (uniform scale, INT8 scale), RN(1/h) for an
+FP16-valued h (the uniform reciprocal), and the per-element quotient x / s
+by a vector's scale s (INT8, INT8 record, FP8 dynamic) through RN(1/s) and
+one FMA correction.  `fast_division_check.c` and
+`fast_division_scaled_check.c` run the same binary32 sequences over every
+input they can see and count results that differ from the correctly
+rounded quotient, or, for the scaled quotients, the stored codes that differ.
 """
 import os
 import shutil
@@ -37,3 +40,31 @@ def test_div_const_exact_for_all_nonnegative_floats(results, n):
 def test_recip_newton_exact_for_all_fp16_values(results):
     bad, cases = results["recip_f16"]
     assert cases == 3 * (0x7C00 - 1) and bad == 0
+
+
+@pytest.fixture(scope="module")
+def scaled(tmp_path_factory):
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path_factory.mktemp("fastdiv_scaled") / "check")
+    subprocess.run([gcc, "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-o", exe,
+                    os.path.join(HERE, "fast_division_scaled_check.c"), "-lm"], check=True)
+    env = dict(os.environ, OMP_NUM_THREADS=str(min(16, os.cpu_count() or 1)))
+    out = subprocess.run([exe], check=True, capture_output=True, text=True, env=env, timeout=900).stdout
+    return {ln.split()[0]: tuple(int(v) for v in ln.split()[1:]) for ln in out.splitlines()}
+
+
+@pytest.mark.parametrize("src", ["bf16", "fp16"])
+@pytest.mark.parametrize("codec", ["int8", "int8rows", "fp8dyn"])
+def test_scaled_division_gives_identical_codes(scaled, codec, src):
+    """The per-vector shortcut q0 + fma(-q0, s, x) * RN(1/s) against the IEEE
+    quotient x / s, for every scale the codec forms and every |x| <= amax:
+    the stored code is identical in every case.  FP16 sources give identical
+    quotients; BF16 sources differ only for quotients below 2^-10 (deep in
+    the subnormal range), which the INT8 and FP8 codes both map to zero."""
+    badq, badc, badf, cases = scaled[f"{codec}_{src}"]
+    assert cases == (532701120 if src == "bf16" else 503856640)
+    assert (badc if codec != "fp8dyn" else badf) == 0
+    if src == "fp16":
+        assert badq == 0
