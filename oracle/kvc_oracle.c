@@ -25,6 +25,9 @@
  *            to exact zero) and "Why exactly 1,152 bytes?" (a token's K or
  *            V row: H x D INT8 codes, then H BF16 scales, padded to a
  *            multiple of 128 bytes).
+ *            "GPU ANS" (lossless entropy coding of typed 16-bit pages;
+ *            decompression checks the exact output length; incompressible
+ *            pages stay raw; at least 4 KiB of input).
  *   [KNLP]   "Asymmetric KV: methods and results": "Precision and scaling
  *            reference" (FP32 amax clamped at 1e-12, times the rounded FP32
  *            reciprocal of 448, FP32 divide, clip to +-448, E4M3FN RNE;
@@ -34,6 +37,7 @@
 #include "kvc_oracle.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define SLOT_ALIGN 256u
@@ -41,6 +45,15 @@
 #define MAX_SEGMENT_BYTES (16u << 20)
 #define MAX_D 256
 #define ROWS_OFFSET 128u    /* INT8_ROWS: the rows start 128 bytes into the slot */
+/* ANS16: 64 interleaved rANS streams per byte plane, 12-bit probabilities,
+ * 32-bit state in [2^23, 2^31), byte-wise renormalisation */
+#define ANS_STREAMS 64u
+#define ANS_PROB_BITS 12
+#define ANS_M (1u << ANS_PROB_BITS)
+#define ANS_L (1u << 23)
+#define ANS_MIN_BYTES 4096u
+#define ANS_MAX_BYTES 32768u
+#define FLAG_HEAP 16        /* stored bytes sit at spill_offset, outside the slot */
 
 static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
@@ -322,6 +335,7 @@ size_t kvo_row_bytes(int d, int heads) {
 }
 
 size_t kvo_slot_bytes(int codec, int d, int n_vec, int heads) {
+  if (codec == KVO_ANS16) return align_up(HEADER_BYTES, SLOT_ALIGN);   /* the payload goes to the spill region */
   if (codec == KVO_INT8_ROWS)
     return align_up(ROWS_OFFSET + (size_t)(n_vec / heads) * kvo_row_bytes(d, heads), SLOT_ALIGN);
   size_t payload = (size_t)n_vec * (size_t)(kvo_code_bytes(codec, d) + kvo_meta_bytes(codec));
@@ -335,6 +349,9 @@ int kvo_effective_codec(int codec, int d, int n_vec, int heads, int is_protected
   size_t orig = (size_t)n_vec * (size_t)d * 2;
   if (is_protected || codec == KVO_RAW) return KVO_RAW;
   if (orig > MAX_SEGMENT_BYTES) return KVO_RAW;
+  /* [OKV-SF "GPU ANS"]: at least 4 KiB of input; the kernels hold at most
+   * 32 KiB of a segment */
+  if (codec == KVO_ANS16 && (orig < ANS_MIN_BYTES || orig > ANS_MAX_BYTES)) return KVO_RAW;
   if (8 * kvo_slot_bytes(codec, d, n_vec, heads) > 7 * orig) return KVO_RAW;
   return codec;
 }
@@ -512,6 +529,206 @@ static void dec_uniform(const uint8_t *codes, const uint8_t *meta, int d, int bi
 }
 
 /* ------------------------------------------------------------------------ */
+/* Lossless entropy coding: rANS over byte planes (KVO_ANS16)               */
+/* ------------------------------------------------------------------------ */
+
+/* [OKV-SF "GPU ANS"] typed 16-bit pages are entropy coded losslessly.  The
+ * coder here is range asymmetric numeral systems (rANS, J. Duda, "Asymmetric
+ * numeral systems", arXiv:1311.2540, 2013) with a static model per plane:
+ *   - plane 0 holds the low byte of each 16-bit value, plane 1 the high
+ *     byte, in canonical element order;
+ *   - element i belongs to stream (i / 8) mod 64; a stream codes its
+ *     elements in increasing i;
+ *   - a plane serialises as u16 mode, u16 K, then
+ *       mode 0 (raw):  the n bytes;
+ *       mode 1 (rANS): a 32-byte bitmap of the K symbols present, their u16
+ *                      frequencies in increasing symbol order, 64 u16 stream
+ *                      lengths, the streams in stream order, each as [final
+ *                      state, u32 little-endian][renormalisation bytes, last
+ *                      emitted first];
+ *     zero-padded to a multiple of 4 bytes.  rANS is used when it is shorter
+ *     than the raw plane. */
+
+/* Frequencies summing to 2^12 from counts over n symbols: each present
+ * symbol gets 1 plus its share of the remaining 4096 - K (K present
+ * symbols), floored; the rounding remainder goes to the most frequent
+ * symbol (the lowest on ties). */
+void kvo_ans_normalize(const uint32_t *count, uint32_t n, uint16_t *freq) {
+  uint32_t k = 0, best = 0;
+  for (int s = 0; s < 256; s++) {
+    if (count[s]) k++;
+    if (count[s] > count[best]) best = (uint32_t)s;
+  }
+  uint32_t sum = 0;
+  for (int s = 0; s < 256; s++) {
+    freq[s] = count[s] ? (uint16_t)(1 + (uint32_t)(((uint64_t)count[s] * (ANS_M - k)) / n)) : 0;
+    sum += freq[s];
+  }
+  if (n) freq[best] = (uint16_t)(freq[best] + (ANS_M - sum));
+}
+
+/* the rANS body of a plane (from the bitmap on); returns its size */
+static size_t ans_rans_body(const uint8_t *sym, size_t n, uint8_t *out, uint32_t *k_out) {
+  uint32_t count[256] = {0};
+  uint16_t freq[256];
+  uint32_t cum[257];
+  for (size_t i = 0; i < n; i++) count[sym[i]]++;
+  kvo_ans_normalize(count, (uint32_t)n, freq);
+  cum[0] = 0;
+  for (int s = 0; s < 256; s++) cum[s + 1] = cum[s] + freq[s];
+  memset(out, 0, 32);
+  uint8_t *q = out + 32;
+  uint32_t k = 0;
+  for (int s = 0; s < 256; s++)
+    if (freq[s]) {
+      out[s >> 3] |= (uint8_t)(1u << (s & 7));
+      put_u16(q, freq[s]);
+      q += 2;
+      k++;
+    }
+  *k_out = k;
+  uint8_t *lens = q, *dst = q + 2 * ANS_STREAMS;
+  static __thread uint8_t emitted[2 * 16384];  /* per stream: at most 2 bytes per symbol */
+  static __thread size_t idx[16384];
+  for (uint32_t j = 0; j < ANS_STREAMS; j++) {
+    /* the stream's elements: chunks c = j, j + 64, ... of 8 elements */
+    size_t m = 0;
+    for (size_t c = j; 8 * c < n; c += ANS_STREAMS)
+      for (size_t e = 0; e < 8 && 8 * c + e < n; e++) idx[m++] = 8 * c + e;
+    uint32_t x = ANS_L;
+    size_t ne = 0;
+    for (size_t t = m; t-- > 0;) {           /* rANS encodes in reverse */
+      const uint32_t s = sym[idx[t]], f = freq[s];
+      const uint32_t x_max = ((ANS_L >> ANS_PROB_BITS) << 8) * f;
+      while (x >= x_max) {
+        emitted[ne++] = (uint8_t)(x & 0xFF);
+        x >>= 8;
+      }
+      x = (x / f) * ANS_M + (x % f) + cum[s];
+    }
+    put_u32(dst, x);
+    for (size_t b = 0; b < ne; b++) dst[4 + b] = emitted[ne - 1 - b];
+    put_u16(lens + 2 * j, (uint16_t)(4 + ne));
+    dst += 4 + ne;
+  }
+  return (size_t)(dst - out);
+}
+
+/* Encode n symbols (n <= 2^20); returns the serialised size, a multiple of
+ * 4 (out must hold 4 + 32 + 512 + 128 + 4 * 64 + 2 * n + 3 bytes: a symbol
+ * emits at most two bytes). */
+size_t kvo_ans_encode_plane(const uint8_t *sym, size_t n, uint8_t *out) {
+  if (n > ((size_t)1 << 20)) return 0;
+  uint32_t k = 0;
+  size_t body = ans_rans_body(sym, n, out + 4, &k);
+  size_t size;
+  if (body < n) {
+    put_u16(out, 1);
+    put_u16(out + 2, (uint16_t)k);
+    size = 4 + body;
+  } else {
+    put_u16(out, 0);
+    put_u16(out + 2, 0);
+    memcpy(out + 4, sym, n);
+    size = 4 + n;
+  }
+  while (size & 3) out[size++] = 0;
+  return size;
+}
+
+/* Decode n symbols from `in` (avail bytes).  Returns the bytes consumed, or
+ * 0 on any inconsistency: an unknown mode, a bitmap not holding K symbols,
+ * frequencies not summing to 2^12, a stream running past its length or not
+ * ending exactly at its length in the initial state (the exact-length
+ * check), nonzero padding. */
+size_t kvo_ans_decode_plane(const uint8_t *in, size_t avail, size_t n, uint8_t *sym) {
+  if (avail < 4) return 0;
+  const uint32_t mode = get_u16(in), k = get_u16(in + 2);
+  size_t off;
+  if (mode == 0) {
+    if (k || avail < 4 + n) return 0;
+    memcpy(sym, in + 4, n);
+    off = 4 + n;
+  } else if (mode == 1) {
+    if (avail < 4 + 32 + 2 * (size_t)k + 2 * ANS_STREAMS) return 0;
+    uint16_t freq[256];
+    uint32_t cum[257], sum = 0, present = 0;
+    const uint8_t *fq = in + 36;
+    for (int s = 0; s < 256; s++) {
+      freq[s] = 0;
+      if ((in[4 + (s >> 3)] >> (s & 7)) & 1) {
+        if (present == k) return 0;
+        freq[s] = get_u16(fq + 2 * present++);
+        if (!freq[s]) return 0;
+      }
+    }
+    if (present != k) return 0;
+    cum[0] = 0;
+    for (int s = 0; s < 256; s++) {
+      cum[s + 1] = cum[s] + freq[s];
+      sum += freq[s];
+    }
+    if (sum != ANS_M) return 0;
+    const uint8_t *lens = fq + 2 * k;
+    off = (size_t)(lens - in) + 2 * ANS_STREAMS;
+    for (uint32_t j = 0; j < ANS_STREAMS; j++) {
+      const size_t len = get_u16(lens + 2 * j);
+      if (len < 4 || off + len > avail) return 0;
+      const uint8_t *st = in + off;
+      uint32_t x = get_u32(st);
+      size_t pos = 4;
+      for (size_t c = j; 8 * c < n; c += ANS_STREAMS)
+        for (size_t e = 0; e < 8 && 8 * c + e < n; e++) {
+          const uint32_t slot = x & (ANS_M - 1);
+          int s = 0;
+          while (cum[s + 1] <= slot) s++;        /* the symbol whose interval holds the slot */
+          sym[8 * c + e] = (uint8_t)s;
+          x = freq[s] * (x >> ANS_PROB_BITS) + slot - cum[s];
+          while (x < ANS_L) {
+            if (pos >= len) return 0;
+            x = (x << 8) | st[pos++];
+          }
+        }
+      if (pos != len || x != ANS_L) return 0;
+      off += len;
+    }
+  } else {
+    return 0;
+  }
+  while (off & 3) {
+    if (off >= avail || in[off]) return 0;
+    off++;
+  }
+  return off;
+}
+
+/* both planes of n 16-bit values; returns the payload size */
+static size_t ans_encode_segment(const uint16_t *vec, size_t n, uint8_t *out) {
+  uint8_t *plane = (uint8_t *)malloc(n);
+  size_t total = 0;
+  for (int p = 0; p < 2; p++) {
+    for (size_t i = 0; i < n; i++) plane[i] = (uint8_t)(vec[i] >> (8 * p));
+    total += kvo_ans_encode_plane(plane, n, out + total);
+  }
+  free(plane);
+  return total;
+}
+static int ans_decode_segment(const uint8_t *in, size_t stored, size_t n, uint16_t *out) {
+  uint8_t *plane = (uint8_t *)malloc(n);
+  size_t used = 0;
+  int ok = 1;
+  for (size_t i = 0; i < n; i++) out[i] = 0;
+  for (int p = 0; p < 2 && ok; p++) {
+    const size_t u = kvo_ans_decode_plane(in + used, stored - used, n, plane);
+    if (!u) ok = 0;
+    used += u;
+    for (size_t i = 0; i < n && ok; i++) out[i] = (uint16_t)(out[i] | (plane[i] << (8 * p)));
+  }
+  free(plane);
+  return ok && used == stored;                 /* exact length */
+}
+
+/* ------------------------------------------------------------------------ */
 /* Segments                                                                 */
 /* ------------------------------------------------------------------------ */
 
@@ -565,6 +782,30 @@ int kvo_encode_segment(const uint16_t *vec, int dtype, int d, int n_vec, int hea
     for (size_t i = 0; i < (size_t)n_vec * (size_t)d; i++) put_u16(slot + HEADER_BYTES + 2 * i, vec[i]);
     if (with_crc) set_crc(slot, slot + HEADER_BYTES, orig);
     return KVO_SEG_RAW_POLICY;
+  }
+  if (eff == KVO_ANS16) {
+    /* lossless: no gate.  Kept only when slot plus the 256-byte aligned
+     * payload saves 12.5% over the source; otherwise the segment stays raw
+     * [OKV-SF "GPU ANS": incompressible pages remain raw]. */
+    const size_t n = (size_t)n_vec * (size_t)d;
+    uint8_t *pay = (uint8_t *)malloc(2 * (1024 + 2 * n));
+    const size_t len = ans_encode_segment(vec, n, pay);
+    const int keep = 8 * (slot_bytes + align_up(len, SLOT_ALIGN)) <= 7 * orig;
+    if (keep) {
+      write_header(slot, KVO_ANS16, FLAG_HEAP, dtype, component, d, n_vec, (uint32_t)len, spill_offset, 0);
+      if (spill) {
+        memcpy(spill, pay, len);
+        if (with_crc) set_crc(slot, spill, len);
+      }
+    } else {
+      write_header(slot, KVO_RAW, 2, dtype, component, d, n_vec, (uint32_t)orig, spill_offset, 0);
+      if (spill) {
+        for (size_t i = 0; i < n; i++) put_u16(spill + 2 * i, vec[i]);
+        if (with_crc) set_crc(slot, spill, orig);
+      }
+    }
+    free(pay);
+    return keep ? KVO_SEG_ENCODED : KVO_SEG_RAW_DATA;
   }
 
   int bits = codec_bits(eff), cb = kvo_code_bytes(eff, d), mb = kvo_meta_bytes(eff);
@@ -654,7 +895,7 @@ int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
   size_t nel = (size_t)n_vec * (size_t)d;
   /* a CRC32, when present, is checked before anything is decoded */
   if (flags & KVO_FLAG_CRC32) {
-    const uint8_t *stored = (flags & 2) ? buf_base + get_u64(slot + 16)
+    const uint8_t *stored = (flags & (2 | FLAG_HEAP)) ? buf_base + get_u64(slot + 16)
                             : slot + (format == KVO_INT8_ROWS ? ROWS_OFFSET : HEADER_BYTES);
     if ((flags & 2) && (flags & 4)) return -1;
     if (kvo_crc32(stored, get_u32(slot + 12)) != get_u32(slot + 24)) return -2;
@@ -668,6 +909,10 @@ int kvo_decode_segment(const uint8_t *slot, const uint8_t *buf_base,
   if (format == KVO_RAW) {
     for (size_t i = 0; i < nel; i++) out[i] = get_u16(slot + HEADER_BYTES + 2 * i);
     return 0;
+  }
+  if (format == KVO_ANS16) {
+    if (!(flags & FLAG_HEAP)) return -1;
+    return ans_decode_segment(buf_base + get_u64(slot + 16), get_u32(slot + 12), nel, out) ? 0 : -1;
   }
   int bits = codec_bits(format), cb = kvo_code_bytes(format, d), mb = kvo_meta_bytes(format);
   const uint8_t *codes = slot + HEADER_BYTES;

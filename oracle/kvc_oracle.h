@@ -49,13 +49,28 @@ extern "C" {
 enum {
   KVO_RAW = 0, KVO_FP8_DIRECT = 1, KVO_FP8_FIXED = 2, KVO_FP8_DYNAMIC = 3,
   KVO_INT8 = 4, KVO_UNIFORM3 = 5, KVO_UNIFORM4 = 6, KVO_TQ3 = 7, KVO_TQ4 = 8,
-  KVO_INT8_ROWS = 9   /* INT8 with BF16 scales in 128-byte-padded token rows */
+  KVO_INT8_ROWS = 9,  /* INT8 with BF16 scales in 128-byte-padded token rows */
+  KVO_ANS16 = 10      /* lossless rANS of the low and high byte planes */
 };
 enum { KVO_BF16 = 1, KVO_FP16 = 2 };
 /* segment status returned by the encoder */
 enum { KVO_SEG_ENCODED = 0, KVO_SEG_RAW_POLICY = 1, KVO_SEG_RAW_DATA = 2 };
 /* encode option: compute a CRC32 of the stored bytes; header flag bit 3 */
 enum { KVO_ENC_CRC32 = 1, KVO_FLAG_CRC32 = 8 };
+/* header flag bit 4: the stored bytes sit at spill_offset (ANS16 payloads) */
+enum { KVO_FLAG_HEAP = 16 };
+
+/* ---- lossless entropy stage (ANS16) ----
+ * Frequencies summing to 4096 from 256 counts over n symbols. */
+void   kvo_ans_normalize(const uint32_t *count, uint32_t n, uint16_t *freq);
+/* One byte plane of n symbols: 64 interleaved rANS streams, or the raw
+ * bytes when that is shorter; returns the serialised size (a multiple of
+ * 4).  out: at least 1024 + 2n bytes. */
+size_t kvo_ans_encode_plane(const uint8_t *sym, size_t n, uint8_t *out);
+/* Inverse; returns the bytes consumed, 0 on any inconsistency (bad table,
+ * stream overrun, a stream not ending exactly at its length in the initial
+ * state). */
+size_t kvo_ans_decode_plane(const uint8_t *in, size_t avail, size_t n, uint8_t *sym);
 
 /* CRC-32 (reflected polynomial 0xEDB88320, preset and final complement) */
 uint32_t kvo_crc32(const uint8_t *p, size_t n);
@@ -111,7 +126,10 @@ int    kvo_effective_codec(int codec, int d, int n_vec, int heads, int is_protec
  * zero padding).  INT8_ROWS stores, from byte 128 of the slot, one row per
  * token: its H vectors' codes (h-major), its H BF16 scales, zero padding to
  * kvo_row_bytes; every other codec stores the codes block then the metadata
- * block right after the 32-byte header.  For a data-dependent RAW segment the slot carries only the
+ * block right after the 32-byte header.  ANS16 writes only the header into
+ * the slot (flag KVO_FLAG_HEAP) and its payload -- plane 0 then plane 1 --
+ * into spill, at spill_offset; an ANS16 segment whose slot plus 256-byte
+ * aligned payload would not save 12.5% is stored raw (KVO_SEG_RAW_DATA).  For a data-dependent RAW segment the slot carries only the
  * header (payload zero) and the raw bytes go to spill (n_vec*d*2 bytes, if
  * spill != NULL); spill_offset is written into the header.  flags:
  * KVO_ENC_CRC32 stores the CRC32 of the stored bytes (the payload, or the raw

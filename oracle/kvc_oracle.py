@@ -23,9 +23,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
 _LIB = os.path.join(_HERE, "libkvc_oracle.so")
 
-RAW, FP8_DIRECT, FP8_FIXED, FP8_DYNAMIC, INT8, UNIFORM3, UNIFORM4, TQ3, TQ4, INT8_ROWS = range(10)
+RAW, FP8_DIRECT, FP8_FIXED, FP8_DYNAMIC, INT8, UNIFORM3, UNIFORM4, TQ3, TQ4, INT8_ROWS, ANS16 = range(11)
 CODEC_NAMES = ["RAW", "FP8_DIRECT", "FP8_FIXED", "FP8_DYNAMIC", "INT8",
-               "UNIFORM3", "UNIFORM4", "TQ3", "TQ4", "INT8_ROWS"]
+               "UNIFORM3", "UNIFORM4", "TQ3", "TQ4", "INT8_ROWS", "ANS16"]
+FLAG_HEAP = 16         # header flag: the stored bytes sit at spill_offset (ANS16)
 ROWS_OFFSET = 128      # INT8_ROWS: token rows start 128 bytes into the slot
 BF16, FP16 = 1, 2
 SEG_ENCODED, SEG_RAW_POLICY, SEG_RAW_DATA = 0, 1, 2
@@ -97,6 +98,12 @@ def lib():
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_float, ctypes.c_uint64, P, P, ctypes.c_uint64,
                                          ctypes.c_int]
+        L.kvo_ans_normalize.restype = None
+        L.kvo_ans_normalize.argtypes = [P, ctypes.c_uint32, P]
+        L.kvo_ans_encode_plane.restype = ctypes.c_size_t
+        L.kvo_ans_encode_plane.argtypes = [P, ctypes.c_size_t, P]
+        L.kvo_ans_decode_plane.restype = ctypes.c_size_t
+        L.kvo_ans_decode_plane.argtypes = [P, ctypes.c_size_t, ctypes.c_size_t, P]
         L.kvo_crc32.restype = ctypes.c_uint32
         L.kvo_crc32.argtypes = [P, ctypes.c_size_t]
         L.kvo_decode_segment.restype = ctypes.c_int
@@ -242,8 +249,10 @@ def encode_segment(vec: np.ndarray, dtype: int, codec: int, component: int = 0,
                    is_protected: bool = False, fixed_scale: float = 1.0, seed: int = 0,
                    spill_offset: int = 0, crc: bool = False, heads: int = 1):
     """vec: uint16 [n_vec, D] source bits (v = t*heads + h).  Returns (slot
-    uint8, status, raw uint8|None).  crc: store the CRC32 of the stored
-    bytes in the header."""
+    uint8, status, spilled uint8|None): the spilled bytes are the raw source
+    of a data-dependent raw segment, or an ANS16 segment's payload (header
+    flag FLAG_HEAP).  crc: store the CRC32 of the stored bytes in the
+    header."""
     vec = np.ascontiguousarray(vec, dtype=np.uint16)
     n_vec, d = vec.shape
     eff = effective_codec(codec, d, n_vec, is_protected, heads)
@@ -255,7 +264,11 @@ def encode_segment(vec: np.ndarray, dtype: int, codec: int, component: int = 0,
                                   ctypes.c_uint64(spill_offset), ENC_CRC32 if crc else 0)
     if st < 0:
         raise ValueError("oracle encode failed")
-    return slot, st, (spill if st == SEG_RAW_DATA else None)
+    if st == SEG_RAW_DATA:
+        return slot, st, spill
+    if slot[2] & FLAG_HEAP:
+        return slot, st, spill[:int(slot[12:16].view(np.uint32)[0])].copy()
+    return slot, st, None
 
 
 def decode_segment(slot: np.ndarray, buf_base, dtype: int, d: int, n_vec: int, seed: int = 0, heads: int = 1):
@@ -364,17 +377,17 @@ def encode_pages(lay: HostLayout, codec_k, codec_v, seed, page_ids, fixed_scales
         results = [work(s) for s in todo]
 
     statuses = np.full(len(seglist), -1, np.int32)
-    n_raw = sum(1 for r in results if r[1] == SEG_RAW_DATA)
-    raw_slot = (raw_bytes + SLOT_ALIGN - 1) // SLOT_ALIGN * SLOT_ALIGN
-    buf = np.zeros(total + n_raw * raw_slot, np.uint8)
+    align = lambda n: (n + SLOT_ALIGN - 1) // SLOT_ALIGN * SLOT_ALIGN
+    spilled = sum(align(r[2].size) for r in results if r[2] is not None)
+    buf = np.zeros(total + spilled, np.uint8)
     spill_cur = total
-    for s, (slot, st, raw) in zip(todo, results):
+    for s, (slot, st, extra) in zip(todo, results):
         statuses[s] = st
         buf[offs[s]:offs[s] + sizes[s]] = slot
-        if st == SEG_RAW_DATA:
+        if extra is not None:              # raw source or ANS16 payload, in segment order
             buf[offs[s] + 16:offs[s] + 24] = np.frombuffer(np.uint64(spill_cur).tobytes(), np.uint8)
-            buf[spill_cur:spill_cur + raw_bytes] = raw
-            spill_cur += raw_slot
+            buf[spill_cur:spill_cur + extra.size] = extra
+            spill_cur += align(extra.size)
     return buf, statuses, offs, total
 
 
@@ -399,3 +412,27 @@ def decode_pages(buf: np.ndarray, out: HostLayout, codec_k, codec_v, seed, dst_p
     for s, vecs in zip(todo, results):
         l, i, c = seglist[s]
         out.scatter(l, c, int(dst_page_ids[i]), vecs)
+
+
+# ---------------------------------------------------------------- entropy stage
+def ans_normalize(counts) -> np.ndarray:
+    c = np.ascontiguousarray(counts, dtype=np.uint32)
+    assert c.size == 256
+    f = np.zeros(256, np.uint16)
+    lib().kvo_ans_normalize(_ptr(c), int(c.sum()), _ptr(f))
+    return f
+
+
+def ans_encode_plane(sym) -> np.ndarray:
+    sym = np.ascontiguousarray(sym, dtype=np.uint8)
+    out = np.zeros(1024 + 2 * sym.size, np.uint8)
+    n = lib().kvo_ans_encode_plane(_ptr(sym), sym.size, _ptr(out))
+    return out[:n].copy()
+
+
+def ans_decode_plane(data, n):
+    """Returns (symbols, bytes consumed); bytes consumed 0 means rejected."""
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    sym = np.zeros(n, np.uint8)
+    used = lib().kvo_ans_decode_plane(_ptr(data), data.size, n, _ptr(sym))
+    return sym, int(used)

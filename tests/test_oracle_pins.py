@@ -739,3 +739,184 @@ def test_int8_record_nonfinite_raw_and_crc(oracle):
     bad[128 + R - 1] ^= 1                                                # padding of row 0
     with pytest.raises(oracle.ChecksumError):
         oracle.decode_segment(bad, None, oracle.BF16, 64, 64, heads=4)
+
+
+# ------------------------------------------------------------ lossless entropy stage (rANS)
+def _plane(kind, n, rng):
+    if kind == "uniform":
+        return rng.integers(0, 256, n).astype(np.uint8)
+    if kind == "geometric":
+        return np.minimum(rng.geometric(0.3, n) - 1, 255).astype(np.uint8)
+    if kind == "constant":
+        return np.full(n, 77, np.uint8)
+    if kind == "two":
+        return rng.choice(np.array([3, 200], np.uint8), n, p=[0.9, 0.1])
+    raise ValueError(kind)
+
+
+def test_ans_normalize_invariants(oracle):
+    """Frequencies sum to 4096, a symbol gets a frequency iff it occurs, each
+    present symbol gets at least 1 + floor(count * (4096 - K) / n), and only
+    the most frequent symbol (lowest on ties) gets the remainder."""
+    rng = np.random.default_rng(30)
+    cases = [np.bincount(_plane(k, n, rng), minlength=256) for k in ("uniform", "geometric", "two", "constant")
+             for n in (1, 8, 2048, 16384)]
+    cases.append(np.arange(256))
+    cases.append(np.r_[np.full(255, 1), 100000])
+    for c in cases:
+        c = c.astype(np.uint32)
+        n, K = int(c.sum()), int((c > 0).sum())
+        f = oracle.ans_normalize(c).astype(np.int64)
+        if n == 0:
+            continue
+        assert f.sum() == 4096 and np.array_equal(f > 0, c > 0)
+        base = np.where(c > 0, 1 + (c.astype(np.int64) * (4096 - K)) // n, 0)
+        extra = f - base
+        assert np.all(extra >= 0) and np.count_nonzero(extra) <= 1
+        if extra.any():
+            assert int(np.argmax(extra)) == int(np.argmax(c))
+
+
+@pytest.mark.parametrize("kind", ["uniform", "geometric", "two", "constant"])
+@pytest.mark.parametrize("n", [8, 2000, 2048, 16384, 16392])
+def test_ans_plane_round_trip(oracle, kind, n):
+    """decode(encode(plane)) is the plane, consuming exactly the encoded
+    bytes, for several symbol distributions and lengths (streams of unequal
+    length when n is not a multiple of 2048)."""
+    sym = _plane(kind, n, np.random.default_rng(n))
+    enc = oracle.ans_encode_plane(sym)
+    dec, used = oracle.ans_decode_plane(enc, n)
+    assert used == enc.size and np.array_equal(dec, sym)
+
+
+def test_ans_constant_plane_closed_form(oracle):
+    """A plane of one repeated symbol has probability 1: every stream is just
+    the untouched initial state L = 2^23 (bytes 00 00 80 00).  The plane is
+    mode 1, K = 1, the bitmap with only that symbol, its frequency 4096, 64
+    stream lengths of 4, 64 copies of L, padded to a multiple of 4."""
+    enc = oracle.ans_encode_plane(np.full(16384, 9, np.uint8))
+    want = [1, 0, 1, 0] + [0] * 32 + [0x00, 0x10] + [4, 0] * 64 + [0x00, 0x00, 0x80, 0x00] * 64 + [0, 0]
+    want[4 + 1] = 0x02                                              # symbol 9: byte 1, bit 1
+    assert list(enc) == want and enc.size % 4 == 0
+
+
+def test_ans_raw_plane_when_coding_does_not_shrink(oracle):
+    """Uniform random bytes do not compress: the plane is stored raw (mode 0,
+    K = 0, the bytes, zero padding) and still round-trips."""
+    sym = _plane("uniform", 16383, np.random.default_rng(4))
+    enc = oracle.ans_encode_plane(sym)
+    assert list(enc[:4]) == [0, 0, 0, 0] and np.array_equal(enc[4:4 + sym.size], sym)
+    assert enc.size == 4 + 16384 and enc[-1] == 0
+    dec, used = oracle.ans_decode_plane(enc, sym.size)
+    assert used == enc.size and np.array_equal(dec, sym)
+
+
+def _rans_layout(enc):
+    """(K, offset of the stream lengths, offset of the first stream) of a mode-1 plane."""
+    k = int(enc[2:4].view(np.uint16)[0])
+    lens = 4 + 32 + 2 * k
+    return k, lens, lens + 128
+
+
+@pytest.mark.parametrize("kind", ["geometric", "two"])
+def test_ans_size_tracks_model_entropy(oracle, kind):
+    """The streams of a coded plane hold its cross-entropy under the quantised
+    model, sum of log2(4096 / f(s)) over the symbols: each stream adds its
+    31-bit final state, and rANS with a 2^23..2^31 state loses well under
+    1e-5 bits per symbol, so the renormalisation bytes lie between
+    bits/8 - 4 per stream and bits/8 + 1 per stream."""
+    n = 16384
+    sym = _plane(kind, n, np.random.default_rng(7))
+    enc = oracle.ans_encode_plane(sym)
+    assert enc[0] == 1
+    k, lens, first = _rans_layout(enc)
+    f = oracle.ans_normalize(np.bincount(sym, minlength=256)).astype(np.float64)
+    bits = np.log2(4096.0 / f[sym]).sum()
+    renorm = int(enc[lens:lens + 128].view(np.uint16).astype(np.int64).sum()) - 4 * 64
+    assert bits / 8 - 4 * 64 <= renorm <= bits / 8 * (1 + 1e-5) + 64
+
+
+def test_ans_exact_length_check(oracle):
+    """A stream that ends early, runs long, or is corrupted is rejected, as is
+    a frequency table that does not sum to 4096: the decoder must consume
+    each stream to exactly its recorded length and end in the encoder's
+    initial state."""
+    rng = np.random.default_rng(3)
+    sym = _plane("geometric", 16384, rng)
+    enc = oracle.ans_encode_plane(sym)
+    n = sym.size
+    k, lens, first = _rans_layout(enc)
+    assert oracle.ans_decode_plane(enc, n)[1] == enc.size
+    short = enc.copy()
+    short[lens:lens + 2] = (short[lens:lens + 2].view(np.uint16) - 1).view(np.uint8)   # stream 0 one byte shorter
+    assert oracle.ans_decode_plane(short, n)[1] == 0
+    longer = np.r_[enc[:first + 4], np.uint8(0), enc[first + 4:]]
+    longer[lens:lens + 2] = (longer[lens:lens + 2].view(np.uint16) + 1).view(np.uint8)  # one byte longer
+    assert oracle.ans_decode_plane(longer, n)[1] == 0
+    rejected = 0
+    for pos in rng.choice(np.arange(first, enc.size - 4), 40, replace=False):
+        bad = enc.copy()
+        bad[pos] ^= 1 << int(rng.integers(8))
+        dec, used = oracle.ans_decode_plane(bad, n)
+        assert used == 0 or not np.array_equal(dec, sym)     # never silently accepted as the original
+        rejected += used == 0
+    assert rejected >= 36                                     # the final-state check catches nearly all
+    table = enc.copy()
+    table[36:38] = (table[36:38].view(np.uint16) + 1).view(np.uint8)                    # frequencies sum to 4097
+    assert oracle.ans_decode_plane(table, n)[1] == 0
+
+
+def _kv_bits(rng, n_vec, d, dtype, scale=None):
+    x = rng.standard_normal((n_vec, d)).astype(np.float32)
+    if scale is not None:
+        x *= scale
+    return _bits(x, dtype)
+
+
+def test_ans16_segment_lossless_and_compressing(oracle):
+    """BF16 and FP16 KV segments (N(0,1) with lognormal channel scales, and
+    with NaN, Inf and signed zeros planted) round-trip bit-exactly.  BF16:
+    the payload sits in the spill region behind a header-only slot and the
+    sign/exponent plane compresses the segment to about 71%; FP16 saves less
+    than 12.5% and is stored raw."""
+    rng = np.random.default_rng(8)
+    for dtype in (oracle.BF16, oracle.FP16):
+        vec = _kv_bits(rng, 128, 128, dtype, np.exp(rng.standard_normal(128)).astype(np.float32))
+        vec[3, 5], vec[9, 0], vec[100, 127] = 0x7FC0 if dtype == oracle.BF16 else 0x7E00, 0x8000, \
+            0x7F80 if dtype == oracle.BF16 else 0x7C00
+        slot, st, pay = oracle.encode_segment(vec, dtype, oracle.ANS16)
+        assert slot.size == 256
+        if dtype == oracle.BF16:      # sign + 7 exponent bits: the high plane codes to ~3.3 bits
+            assert st == oracle.SEG_ENCODED and slot[1] == oracle.ANS16
+            assert slot[2] & oracle.FLAG_HEAP and int(slot[12:16].view(np.uint32)[0]) == pay.size
+            assert pay.size < 0.72 * vec.nbytes
+        else:                         # FP16 keeps 2 mantissa bits in the high byte: under 12.5% saved
+            assert st == oracle.SEG_RAW_DATA and slot[1] == oracle.RAW
+        buf = np.zeros(4096 + pay.size, np.uint8)
+        buf[4096:] = pay
+        slot[16:24] = np.frombuffer(np.uint64(4096).tobytes(), np.uint8)
+        out = oracle.decode_segment(slot, buf, dtype, 128, 128)
+        assert np.array_equal(out, vec)
+
+
+def test_ans16_incompressible_size_and_crc(oracle):
+    """Uniformly random 16-bit patterns do not compress: the segment is stored
+    raw (data-dependent).  Sources below 4 KiB or above 32 KiB are raw by
+    policy.  With the CRC option the checksum covers the payload."""
+    rng = np.random.default_rng(9)
+    vec = rng.integers(0, 1 << 16, (128, 128)).astype(np.uint16)
+    slot, st, raw = oracle.encode_segment(vec, oracle.BF16, oracle.ANS16)
+    assert st == oracle.SEG_RAW_DATA and np.array_equal(raw.view(np.uint16).reshape(vec.shape), vec)
+    for n_vec, d in ((15, 64), (129, 128)):                  # 1,920 B and 33,024 B of source
+        assert oracle.effective_codec(oracle.ANS16, d, n_vec, False) == oracle.RAW
+    assert oracle.effective_codec(oracle.ANS16, 128, 16, False) == oracle.ANS16   # 4 KiB
+    vec = _kv_bits(rng, 64, 64, oracle.BF16)
+    slot, st, pay = oracle.encode_segment(vec, oracle.BF16, oracle.ANS16, crc=True)
+    assert st == oracle.SEG_ENCODED and slot[2] & oracle.FLAG_CRC32
+    assert int(slot[24:28].view(np.uint32)[0]) == oracle.crc32(pay)
+    buf = np.r_[np.zeros(256, np.uint8), pay]
+    slot[16:24] = np.frombuffer(np.uint64(256).tobytes(), np.uint8)
+    assert np.array_equal(oracle.decode_segment(slot, buf, oracle.BF16, 64, 64), vec)
+    buf[256 + pay.size // 2] ^= 0x10
+    with pytest.raises(oracle.ChecksumError):
+        oracle.decode_segment(slot, buf, oracle.BF16, 64, 64)
