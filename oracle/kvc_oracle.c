@@ -539,15 +539,17 @@ static void dec_uniform(const uint8_t *codes, const uint8_t *meta, int d, int bi
  *     byte, in canonical element order;
  *   - element i belongs to stream (i / 8) mod 64; a stream codes its
  *     elements in increasing i;
- *   - a plane serialises as u16 mode, u16 K, then
+ *   - a plane serialises as a 16-byte header (u16 mode, u16 K, 12 zero
+ *     bytes), then
  *       mode 0 (raw):  the n bytes;
  *       mode 1 (rANS): a 32-byte bitmap of the K symbols present, their u16
  *                      frequencies in increasing symbol order, 64 u16 stream
  *                      lengths, the streams in stream order, each as [final
  *                      state, u32 little-endian][renormalisation bytes, last
  *                      emitted first];
- *     zero-padded to a multiple of 4 bytes.  rANS is used when it is shorter
- *     than the raw plane. */
+ *     zero-padded to a multiple of 16 bytes, so that a plane -- and a raw
+ *     plane's bytes -- start 16-byte aligned.  rANS is used when it is
+ *     shorter than the raw plane. */
 
 /* Frequencies summing to 2^12 from counts over n symbols: each present
  * symbol gets 1 plus its share of the remaining 4096 - K (K present
@@ -615,24 +617,23 @@ static size_t ans_rans_body(const uint8_t *sym, size_t n, uint8_t *out, uint32_t
 }
 
 /* Encode n symbols (n <= 2^20); returns the serialised size, a multiple of
- * 4 (out must hold 4 + 32 + 512 + 128 + 4 * 64 + 2 * n + 3 bytes: a symbol
- * emits at most two bytes). */
+ * 16 (out must hold 16 + 32 + 512 + 128 + 4 * 64 + 2 * n + 15 bytes: a
+ * symbol emits at most two bytes). */
 size_t kvo_ans_encode_plane(const uint8_t *sym, size_t n, uint8_t *out) {
   if (n > ((size_t)1 << 20)) return 0;
   uint32_t k = 0;
-  size_t body = ans_rans_body(sym, n, out + 4, &k);
+  memset(out, 0, 16);
+  size_t body = ans_rans_body(sym, n, out + 16, &k);
   size_t size;
   if (body < n) {
     put_u16(out, 1);
     put_u16(out + 2, (uint16_t)k);
-    size = 4 + body;
+    size = 16 + body;
   } else {
-    put_u16(out, 0);
-    put_u16(out + 2, 0);
-    memcpy(out + 4, sym, n);
-    size = 4 + n;
+    memcpy(out + 16, sym, n);
+    size = 16 + n;
   }
-  while (size & 3) out[size++] = 0;
+  while (size & 15) out[size++] = 0;
   return size;
 }
 
@@ -642,21 +643,23 @@ size_t kvo_ans_encode_plane(const uint8_t *sym, size_t n, uint8_t *out) {
  * ending exactly at its length in the initial state (the exact-length
  * check), nonzero padding. */
 size_t kvo_ans_decode_plane(const uint8_t *in, size_t avail, size_t n, uint8_t *sym) {
-  if (avail < 4) return 0;
+  if (avail < 16) return 0;
   const uint32_t mode = get_u16(in), k = get_u16(in + 2);
+  for (int b = 4; b < 16; b++)
+    if (in[b]) return 0;
   size_t off;
   if (mode == 0) {
-    if (k || avail < 4 + n) return 0;
-    memcpy(sym, in + 4, n);
-    off = 4 + n;
+    if (k || avail < 16 + n) return 0;
+    memcpy(sym, in + 16, n);
+    off = 16 + n;
   } else if (mode == 1) {
-    if (avail < 4 + 32 + 2 * (size_t)k + 2 * ANS_STREAMS) return 0;
+    if (avail < 16 + 32 + 2 * (size_t)k + 2 * ANS_STREAMS) return 0;
     uint16_t freq[256];
     uint32_t cum[257], sum = 0, present = 0;
-    const uint8_t *fq = in + 36;
+    const uint8_t *fq = in + 48;
     for (int s = 0; s < 256; s++) {
       freq[s] = 0;
-      if ((in[4 + (s >> 3)] >> (s & 7)) & 1) {
+      if ((in[16 + (s >> 3)] >> (s & 7)) & 1) {
         if (present == k) return 0;
         freq[s] = get_u16(fq + 2 * present++);
         if (!freq[s]) return 0;
@@ -695,7 +698,7 @@ size_t kvo_ans_decode_plane(const uint8_t *in, size_t avail, size_t n, uint8_t *
   } else {
     return 0;
   }
-  while (off & 3) {
+  while (off & 15) {
     if (off >= avail || in[off]) return 0;
     off++;
   }

@@ -65,7 +65,7 @@ enum { KVO_FLAG_HEAP = 16 };
 void   kvo_ans_normalize(const uint32_t *count, uint32_t n, uint16_t *freq);
 /* One byte plane of n symbols: 64 interleaved rANS streams, or the raw
  * bytes when that is shorter; returns the serialised size (a multiple of
- * 4).  out: at least 1024 + 2n bytes. */
+ * 16).  out: at least 1024 + 2n bytes. */
 size_t kvo_ans_encode_plane(const uint8_t *sym, size_t n, uint8_t *out);
 /* Inverse; returns the bytes consumed, 0 on any inconsistency (bad table,
  * stream overrun, a stream not ending exactly at its length in the initial

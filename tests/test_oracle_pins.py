@@ -792,21 +792,23 @@ def test_ans_plane_round_trip(oracle, kind, n):
 def test_ans_constant_plane_closed_form(oracle):
     """A plane of one repeated symbol has probability 1: every stream is just
     the untouched initial state L = 2^23 (bytes 00 00 80 00).  The plane is
-    mode 1, K = 1, the bitmap with only that symbol, its frequency 4096, 64
-    stream lengths of 4, 64 copies of L, padded to a multiple of 4."""
+    the 16-byte header (mode 1, K = 1), the bitmap with only that symbol, its
+    frequency 4096, 64 stream lengths of 4, 64 copies of L, padded to a
+    multiple of 16."""
     enc = oracle.ans_encode_plane(np.full(16384, 9, np.uint8))
-    want = [1, 0, 1, 0] + [0] * 32 + [0x00, 0x10] + [4, 0] * 64 + [0x00, 0x00, 0x80, 0x00] * 64 + [0, 0]
-    want[4 + 1] = 0x02                                              # symbol 9: byte 1, bit 1
-    assert list(enc) == want and enc.size % 4 == 0
+    want = [1, 0, 1, 0] + [0] * 12 + [0] * 32 + [0x00, 0x10] + [4, 0] * 64 + [0x00, 0x00, 0x80, 0x00] * 64
+    want[16 + 1] = 0x02                                             # symbol 9: byte 1, bit 1
+    want += [0] * (-len(want) % 16)
+    assert list(enc) == want and enc.size % 16 == 0
 
 
 def test_ans_raw_plane_when_coding_does_not_shrink(oracle):
-    """Uniform random bytes do not compress: the plane is stored raw (mode 0,
-    K = 0, the bytes, zero padding) and still round-trips."""
+    """Uniform random bytes do not compress: the plane is stored raw (a zero
+    16-byte header, the bytes, zero padding to 16) and still round-trips."""
     sym = _plane("uniform", 16383, np.random.default_rng(4))
     enc = oracle.ans_encode_plane(sym)
-    assert list(enc[:4]) == [0, 0, 0, 0] and np.array_equal(enc[4:4 + sym.size], sym)
-    assert enc.size == 4 + 16384 and enc[-1] == 0
+    assert not enc[:16].any() and np.array_equal(enc[16:16 + sym.size], sym)
+    assert enc.size == 16 + 16384 and enc[-1] == 0
     dec, used = oracle.ans_decode_plane(enc, sym.size)
     assert used == enc.size and np.array_equal(dec, sym)
 
@@ -814,7 +816,7 @@ def test_ans_raw_plane_when_coding_does_not_shrink(oracle):
 def _rans_layout(enc):
     """(K, offset of the stream lengths, offset of the first stream) of a mode-1 plane."""
     k = int(enc[2:4].view(np.uint16)[0])
-    lens = 4 + 32 + 2 * k
+    lens = 16 + 32 + 2 * k
     return k, lens, lens + 128
 
 
@@ -862,7 +864,7 @@ def test_ans_exact_length_check(oracle):
         rejected += used == 0
     assert rejected >= 36                                     # the final-state check catches nearly all
     table = enc.copy()
-    table[36:38] = (table[36:38].view(np.uint16) + 1).view(np.uint8)                    # frequencies sum to 4097
+    table[48:50] = (table[48:50].view(np.uint16) + 1).view(np.uint8)                    # frequencies sum to 4097
     assert oracle.ans_decode_plane(table, n)[1] == 0
 
 
