@@ -126,6 +126,8 @@ WORKLOADS = {
     "int8_records_qwen3": "INT8 host-pool records (BF16 scales, 1,152-byte token rows) K and V, Qwen3-8B shape: "
                           "36 layers, 8 KV heads, D=128, BF16, separate K/V, 3392 random pages of a 4096-block "
                           "pool (54,272 tokens)",
+    "ans16_llama3": "lossless rANS of the byte planes (ANS16) K and V, Llama-3-8B shape: 32 layers, 8 KV heads, "
+                    "D=128, BF16, separate K/V, 4096 random pages of an 8192-block pool (64K tokens)",
     "k8v8_packed": "K8/V8: FP8 E4M3FN K and V with per-token/head scales, Qwen3-8B shape: 36 layers, 8 KV heads, "
                    "D=128, FP16, vLLM packed [2048 blocks, 8, 16, 256]",
 }

@@ -59,6 +59,22 @@
  *  8 heads x 128).  Per vector: a = max(amax, BF16(1e-12)); scale =
  *  BF16(RN(a/127)); q = clamp(RNE(RN(x/scale)), +-127); decode rounds
  *  q*scale once to the output type.  stored_len = tokens * row bytes.
+ *  KVC_ANS16 is lossless [OKV-SF "GPU ANS": typed 16-bit pages entropy coded,
+ *  the exact output length checked on decompression, incompressible pages
+ *  raw]: rANS (Duda 2013) over the low and the high byte plane of the
+ *  segment's values in canonical order.  Each plane: a 16-byte header (u16
+ *  mode, u16 K, zeros), then for mode 0 the raw n bytes, for mode 1 a 32-byte
+ *  bitmap of the K symbols present, their u16 frequencies (summing to 4096:
+ *  1 + floor(count * (4096 - K) / n) each, the remainder to the most
+ *  frequent, lowest symbol on ties), 64 u16 stream lengths and the 64
+ *  streams (element i in stream (i / 8) mod 64; state in [2^23, 2^31), byte
+ *  renormalisation; a stream is [final state u32][renormalisation bytes,
+ *  last emitted first]); zero padding to 16.  A plane is coded when that is
+ *  shorter than raw.  The slot holds only the header (flag KVC_FLAG_HEAP);
+ *  the payload goes to the spill region at spill_offset.  A segment whose
+ *  256-byte slot plus 256-byte aligned payload does not save 12.5% is stored
+ *  raw there (KVC_SEG_RAW_DATA); segments outside 4..32 KiB of source are raw
+ *  by policy.
  *  A segment that must stay raw because of its data (a nonfinite value, an
  *  FP8 source value with |x| > 448, an FP16 metadata overflow) keeps its
  *  slot header (flags RAW_DATA) and its raw bytes go to the spill region of
@@ -135,7 +151,8 @@ typedef enum {
   KVC_UNIFORM4 = 6,     /* per-vector uniform 4-bit, FP16 min and scale [OKV-SF] */
   KVC_TQ3 = 7,          /* TurboQuant MSE 3-bit + FP16 norm [OKV-SF] */
   KVC_TQ4 = 8,          /* TurboQuant MSE 4-bit + FP16 norm [OKV-SF] */
-  KVC_INT8_ROWS = 9     /* INT8 record: BF16 scales, 128-byte-padded token rows [HIQ] */
+  KVC_INT8_ROWS = 9,    /* INT8 record: BF16 scales, 128-byte-padded token rows [HIQ] */
+  KVC_ANS16 = 10        /* lossless rANS of the 16-bit values' byte planes [OKV-SF "GPU ANS"] */
 } kvc_codec_id;
 
 /* Codec choice per component.  fixed_scales: host array [layers][2] (K, V)
@@ -168,7 +185,8 @@ enum {
                              nothing was read or written for this segment (never expected) */
 };
 /* header / descriptor flags */
-enum { KVC_FLAG_RAW_POLICY = 1, KVC_FLAG_RAW_DATA = 2, KVC_FLAG_CAPACITY = 4, KVC_FLAG_CRC32 = 8 };
+enum { KVC_FLAG_RAW_POLICY = 1, KVC_FLAG_RAW_DATA = 2, KVC_FLAG_CAPACITY = 4, KVC_FLAG_CRC32 = 8,
+       KVC_FLAG_HEAP = 16 /* the stored bytes are at spill_offset (KVC_ANS16) */ };
 
 /* One per segment, written by encode on the device (32 B).  Offsets are
  * relative to the start of the encode output buffer. */

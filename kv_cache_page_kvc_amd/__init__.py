@@ -28,12 +28,12 @@ KVC_BF16, KVC_FP16 = 1, 2
 KVC_SEPARATE_NHD, KVC_PACKED_HT2D = 1, 2
 # kvc_codec_id
 KVC_RAW, KVC_FP8_DIRECT, KVC_FP8_FIXED, KVC_FP8_DYNAMIC, KVC_INT8, KVC_UNIFORM3, KVC_UNIFORM4, \
-    KVC_TQ3, KVC_TQ4, KVC_INT8_ROWS = range(10)
+    KVC_TQ3, KVC_TQ4, KVC_INT8_ROWS, KVC_ANS16 = range(11)
 CODECS = {"RAW": 0, "FP8_DIRECT": 1, "FP8_FIXED": 2, "FP8_DYNAMIC": 3, "INT8": 4,
-          "UNIFORM3": 5, "UNIFORM4": 6, "TQ3": 7, "TQ4": 8, "INT8_ROWS": 9}
+          "UNIFORM3": 5, "UNIFORM4": 6, "TQ3": 7, "TQ4": 8, "INT8_ROWS": 9, "ANS16": 10}
 # segment status / flags
 KVC_SEG_ENCODED, KVC_SEG_RAW_POLICY, KVC_SEG_RAW_DATA, KVC_SEG_CAPACITY, KVC_SEG_GUARD = range(5)
-KVC_FLAG_RAW_POLICY, KVC_FLAG_RAW_DATA, KVC_FLAG_CAPACITY, KVC_FLAG_CRC32 = 1, 2, 4, 8
+KVC_FLAG_RAW_POLICY, KVC_FLAG_RAW_DATA, KVC_FLAG_CAPACITY, KVC_FLAG_CRC32, KVC_FLAG_HEAP = 1, 2, 4, 8, 16
 # kvc_codec.flags
 KVC_CODEC_CRC32 = 1
 # decode seg_status values

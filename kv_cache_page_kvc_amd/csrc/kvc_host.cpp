@@ -87,6 +87,7 @@ int codec_meta(int c) {
 // heads: vectors per token (n_vec = tokens * heads); only the record codec's
 // slot depends on it
 uint64_t slot_size(int codec, uint32_t d, uint32_t n_vec, uint32_t heads) {
+  if (codec == KVC_ANS16) return align_up(KVC_HEADER_BYTES, KVC_SLOT_ALIGN);   // payload in the spill region
   if (codec == KVC_INT8_ROWS)
     return align_up(kRowsOffset + (uint64_t)(n_vec / heads) * row_bytes(d, heads), KVC_SLOT_ALIGN);
   const uint64_t per_vec = (uint64_t)codec_bits(codec) * d / 8 + (uint64_t)codec_meta(codec);
@@ -98,6 +99,7 @@ int effective_codec(int codec, uint32_t d, uint32_t n_vec, uint32_t heads, bool 
   const uint64_t orig = (uint64_t)n_vec * d * 2;
   if (prot || codec == KVC_RAW) return KVC_RAW;
   if (orig > KVC_MAX_SEGMENT_BYTES) return KVC_RAW;
+  if (codec == KVC_ANS16 && (orig < kAnsMinBytes || orig > kAnsMaxBytes)) return KVC_RAW;
   if (8 * slot_size(codec, d, n_vec, heads) > 7 * orig) return KVC_RAW;
   return codec;
 }
@@ -243,7 +245,7 @@ kvc_status check_layout(const kvc_layout* L) {
 }
 
 kvc_status check_codec(const kvc_layout* L, const kvc_codec* c) {
-  if (!c || c->k > KVC_INT8_ROWS || c->v > KVC_INT8_ROWS) return KVC_E_ARG;
+  if (!c || c->k > KVC_ANS16 || c->v > KVC_ANS16) return KVC_E_ARG;
   if ((c->flags & ~KVC_CODEC_CRC32) || c->reserved) return KVC_E_ARG;
   if (c->k == KVC_FP8_FIXED || c->v == KVC_FP8_FIXED) {
     if (!c->fixed_scales) return KVC_E_ARG;
@@ -264,6 +266,7 @@ struct Plan {
   uint64_t total = 0;
   uint64_t per_page = 0;      // slot bytes of one page over all layers
   uint64_t encodable = 0;     // segments not raw by policy
+  uint64_t ans = 0;           // of which KVC_ANS16 (payload in the spill region)
 };
 
 Plan make_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages) {
@@ -282,6 +285,7 @@ Plan make_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages) {
       p.eff[comp][l] = (uint8_t)e;
       p.slot[comp][l] = (uint32_t)slot_size(e, L->head_dim, n_vec, L->kv_heads);
       if (e != KVC_RAW) p.encodable += n_pages;
+      if (e == KVC_ANS16) p.ans += n_pages;
     }
     p.layer_off[l] = off;
     const uint64_t page = (uint64_t)p.slot[0][l] + p.slot[1][l];
@@ -498,6 +502,26 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   return KVC_OK;
 }
 
+// Encode / decode launches of a call: the fixed-size codecs' kernel, then,
+// when some component uses KVC_ANS16, the entropy stage's kernel over the
+// same segments (each skips the other's segments).  The entropy decode
+// stages a payload of at most 7/8 of the segment's source bytes in LDS.
+hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
+  hipError_t e = launch_encode(P, L->head_dim, nseg, s);
+  if (e == hipSuccess && plan.ans) e = launch_ans_encode(P, L->head_dim, nseg, s);
+  return e;
+}
+hipError_t run_decode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
+  hipError_t e = launch_decode(P, L->head_dim, nseg, s);
+  if (e == hipSuccess && plan.ans) {
+    CallParams A = P;
+    const uint32_t raw = L->kv_heads * L->tokens_per_page * L->head_dim * 2;
+    A.stage_bytes = (uint32_t)align_up(7ull * raw / 8, 16);
+    e = launch_ans_decode(A, L->head_dim, nseg, s);
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -525,7 +549,10 @@ kvc_status kvc_plan(const kvc_layout* layout, const kvc_codec* codec, uint32_t n
   const uint64_t raw_seg = align_up((uint64_t)layout->kv_heads * layout->tokens_per_page * layout->head_dim * 2,
                                     KVC_SLOT_ALIGN);
   if (slot_bytes) *slot_bytes = p.total;
-  if (spill_bytes_suggested) *spill_bytes_suggested = raw_seg * std::max<uint64_t>(1, (p.encodable + 31) / 32);
+  // ~3% of the fixed-size segments may fall back to raw, and every KVC_ANS16
+  // segment needs its payload -- at most its raw size -- in the spill region
+  if (spill_bytes_suggested)
+    *spill_bytes_suggested = raw_seg * (std::max<uint64_t>(1, (p.encodable - p.ans + 31) / 32) + p.ans);
   if (bytes_per_token) *bytes_per_token = (p.per_page + layout->tokens_per_page - 1) / layout->tokens_per_page;
   return KVC_OK;
 }
@@ -629,7 +656,7 @@ kvc_status kvc_encode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_co
   P.desc = desc;
   P.seg_status = nullptr;
   const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
-  if (launch_encode(P, layout->head_dim, nseg, s) != hipSuccess) return KVC_E_HIP;
+  if (run_encode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
   return ring_commit(ctx, roff, rsize, s);
 }
 
@@ -655,7 +682,7 @@ kvc_status kvc_decode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_co
   P.desc = nullptr;
   P.seg_status = seg_status;
   const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
-  if (launch_decode(P, layout->head_dim, nseg, s) != hipSuccess) return KVC_E_HIP;
+  if (run_decode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
   return ring_commit(ctx, roff, rsize, s);
 }
 
@@ -681,7 +708,7 @@ kvc_status kvc_decode_layers(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
   P.slot_region = plan.total;
   P.seg_status = seg_status;
   P.seg_base = layer_begin * n_pages * 2;
-  if (launch_decode(P, layout->head_dim, (uint64_t)(layer_end - layer_begin) * n_pages * 2, s) != hipSuccess)
+  if (run_decode(P, layout, plan, (uint64_t)(layer_end - layer_begin) * n_pages * 2, s) != hipSuccess)
     return KVC_E_HIP;
   return ring_commit(ctx, roff, rsize, s);
 }
@@ -713,7 +740,7 @@ kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
   P.buf_bytes = host_bytes;
   P.slot_region = plan.total;
   P.desc = reinterpret_cast<kvc_segment_desc*>(lane.ptr + buf_bytes);
-  if (launch_encode(P, layout->head_dim, nseg, s) != hipSuccess) return KVC_E_HIP;
+  if (run_encode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
   if (hipMemcpyAsync(host_out, lane.ptr, host_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipMemcpyAsync(host_desc, P.desc, desc_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipEventRecord(lane.last, s) != hipSuccess)
@@ -775,7 +802,7 @@ kvc_status kvc_restore_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
         hipEventRecord(copied, cs) != hipSuccess || hipStreamWaitEvent(s, copied, 0) != hipSuccess)
       return KVC_E_HIP;
     P.seg_base = l * n_pages * 2;
-    if (launch_decode(P, layout->head_dim, (uint64_t)n_pages * 2, s) != hipSuccess) return KVC_E_HIP;
+    if (run_decode(P, layout, plan, (uint64_t)n_pages * 2, s) != hipSuccess) return KVC_E_HIP;
     if (layer_ready && layer_ready[l - layer_begin] &&
         hipEventRecord(static_cast<hipEvent_t>(layer_ready[l - layer_begin]), s) != hipSuccess)
       return KVC_E_HIP;

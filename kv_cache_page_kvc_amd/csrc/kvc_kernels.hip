@@ -280,7 +280,7 @@ __device__ __forceinline__ const T* byte_at(const T* base, uint32_t off) {
 // ------------------------------------------------------------------ encoders
 // Each returns 1 if this vector forces the segment raw.
 enum Codec { C_RAW = 0, C_FP8D = 1, C_FP8F = 2, C_FP8Y = 3, C_INT8 = 4, C_U3 = 5, C_U4 = 6, C_TQ3 = 7, C_TQ4 = 8,
-             C_I8R = 9 };
+             C_I8R = 9, C_ANS = 10 };
 
 template <int C> struct CodecInfo {
   static constexpr int bits = (C == C_U3 || C == C_TQ3) ? 3 : ((C == C_U4 || C == C_TQ4) ? 4 : 8);
@@ -891,6 +891,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const uint32_t pi = rem >> 1, comp = rem & 1;
   const SideEntry& E = p.sides[2 * l + comp];
   const int codec = (int)E.codec;
+  if (codec == C_ANS) return;                                   // the entropy stage's own kernel
   const uint64_t slot_off = E.slot_base + (uint64_t)pi * E.page_stride;
   const int32_t page = p.pages[pi];
   // guard: the side table and page list come from memory; never follow a
@@ -1227,6 +1228,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   const uint32_t pi = rem >> 1, comp = rem & 1;
   const SideEntry& E = p.sides[2 * l + comp];
   const int codec = (int)E.codec;
+  if (codec == C_ANS) return;                                   // the entropy stage's own kernel
   const uint64_t slot_off = E.slot_base + (uint64_t)pi * E.page_stride;
   const int32_t page = p.pages[pi];
   if ((uint64_t)(uintptr_t)E.base < p.base_lo || (uint64_t)(uintptr_t)E.base > p.base_hi || page < 0 ||
@@ -1322,6 +1324,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   else decode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cent, s.slot);
 }
 
+// ------------------------------------------------------------------ entropy stage
+#include "kvc_ans_device.h"
+
 // dynamic LDS of a launch: the slot staging
 inline uint32_t dynamic_lds(const CallParams& p) { return p.stage_bytes; }
 
@@ -1369,6 +1374,30 @@ hipError_t launch_encode(const CallParams& p, uint32_t head_dim, uint64_t nseg, 
     case 256: return launch_encode_d<256>(p, nseg, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_ans_encode(const CallParams& p, uint32_t head_dim, uint64_t nseg, hipStream_t st) {
+  const bool crc = p.crc != 0;
+  switch (head_dim) {
+    case 32: crc ? launch_ans_encode_dc<32, true>(p, nseg, st) : launch_ans_encode_dc<32, false>(p, nseg, st); break;
+    case 64: crc ? launch_ans_encode_dc<64, true>(p, nseg, st) : launch_ans_encode_dc<64, false>(p, nseg, st); break;
+    case 128: crc ? launch_ans_encode_dc<128, true>(p, nseg, st) : launch_ans_encode_dc<128, false>(p, nseg, st); break;
+    case 256: crc ? launch_ans_encode_dc<256, true>(p, nseg, st) : launch_ans_encode_dc<256, false>(p, nseg, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ans_decode(const CallParams& p, uint32_t head_dim, uint64_t nseg, hipStream_t st) {
+  const bool crc = p.crc != 0;
+  switch (head_dim) {
+    case 32: crc ? launch_ans_decode_dc<32, true>(p, nseg, st) : launch_ans_decode_dc<32, false>(p, nseg, st); break;
+    case 64: crc ? launch_ans_decode_dc<64, true>(p, nseg, st) : launch_ans_decode_dc<64, false>(p, nseg, st); break;
+    case 128: crc ? launch_ans_decode_dc<128, true>(p, nseg, st) : launch_ans_decode_dc<128, false>(p, nseg, st); break;
+    case 256: crc ? launch_ans_decode_dc<256, true>(p, nseg, st) : launch_ans_decode_dc<256, false>(p, nseg, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const CallParams& p, uint32_t head_dim, uint64_t nseg, hipStream_t st) {

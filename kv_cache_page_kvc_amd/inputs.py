@@ -135,6 +135,9 @@ CONFIGS = {
     # tokens, about the 54,254 BF16 tokens an 8 GB host budget holds
     "int8_records_qwen3": dict(layers=36, heads=8, dim=128, dtype="bf16", layout="separate", tokens=16,
                                pool=4096, pages=3392, k="INT8_ROWS", v="INT8_ROWS", random_pages=True),
+    # the lossless entropy stage on the Llama-3-8B shape
+    "ans16_llama3": dict(layers=32, heads=8, dim=128, dtype="bf16", layout="separate", tokens=16,
+                         pool=8192, pages=4096, k="ANS16", v="ANS16", random_pages=True),
     # K8/V8 with per-token/head scales on the vLLM packed Qwen3-8B layout
     "k8v8_packed": dict(layers=36, heads=8, dim=128, dtype="fp16", layout="packed", tokens=16,
                         pool=2048, pages=2048, k="FP8_DYNAMIC", v="FP8_DYNAMIC"),

@@ -130,13 +130,18 @@ def compare_encoded(gpu_buf: np.ndarray, gpu_desc, ora_buf, ora_status, offs, to
         hdr_o = ora_buf[o:o + 32]
         if int(d["flags"]) != int(hdr_g[2]) or int(d["crc32"]) != int(hdr_g[24:28].view(np.uint32)[0]):
             bad.append((s, "descriptor flags/crc32"))
-        if st == O.SEG_RAW_DATA:
+        if st == O.SEG_RAW_DATA or (st == O.SEG_ENCODED and hdr_o[2] & O.FLAG_HEAP):
+            # bytes in the spill region (raw source, or an entropy-coded payload):
+            # headers equal but for the spill offset, stored bytes equal, rest of the slot zero
             if not (np.array_equal(hdr_g[:16], hdr_o[:16]) and np.array_equal(hdr_g[24:], hdr_o[24:])):
-                bad.append((s, "raw header"))
+                bad.append((s, "spilled segment header"))
                 continue
+            size = (offs[s + 1] if s + 1 < len(offs) else total) - o
+            if hdr_o[2] & O.FLAG_HEAP and gpu_buf[o + 32:o + size].any():
+                bad.append((s, "slot padding"))      # a header-only slot is zero after the header
             so_g = int(hdr_g[16:24].view(np.uint64)[0])
             so_o = int(hdr_o[16:24].view(np.uint64)[0])
-            n = int(hdr_o[8:12].view(np.uint32)[0])
+            n = int(hdr_o[12:16].view(np.uint32)[0])
             if int(d["spill_offset"]) != so_g or not np.array_equal(gpu_buf[so_g:so_g + n], ora_buf[so_o:so_o + n]):
                 bad.append((s, "spill bytes"))
             continue

@@ -117,7 +117,7 @@ def test_validation_errors():
         fs = np.full((4, 2), 1.0, np.float32)
         fs[2, 0] = badscale
         assert V(ok, kvc.Codec("FP8_FIXED", "RAW", fixed_scales=fs), ids, 1 << 40) == kvc.KVC_E_ARG
-    assert V(ok, kvc.Codec(10, 0), ids, 1 << 40) == kvc.KVC_E_ARG
+    assert V(ok, kvc.Codec(11, 0), ids, 1 << 40) == kvc.KVC_E_ARG
     # codec flags: only KVC_CODEC_CRC32 is defined; reserved must be 0
     assert V(ok, kvc.Codec("TQ4", "UNIFORM4", crc=True), ids, 1 << 40) == kvc.KVC_OK
     c = kvc.Codec("TQ4", "UNIFORM4")

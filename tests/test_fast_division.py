@@ -68,3 +68,20 @@ def test_scaled_division_gives_identical_codes(scaled, codec, src):
     assert (badc if codec != "fp8dyn" else badf) == 0
     if src == "fp16":
         assert badq == 0
+
+
+def test_rans_reciprocal_division_exact():
+    """The rANS encoder's floor(x / f) through a 32-bit reciprocal, for every
+    frequency f of a 12-bit model (checked over small x, the top of the
+    encoder's state range and random x; exact for all x < 2^31 by
+    Granlund-Montgomery)."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        exe = os.path.join(d, "check")
+        subprocess.run([gcc, "-O2", "-o", exe, os.path.join(HERE, "ans_division_check.c")], check=True)
+        bad, cases = (int(v) for v in subprocess.run([exe], check=True, capture_output=True, text=True,
+                                                     timeout=300).stdout.split())
+    assert cases > 4096 * 65536 and bad == 0

@@ -93,7 +93,7 @@ def _roundtrip_case(ctx, wl, ck, cv, seed, page_ids, protected=None, fixed=None,
 
 # ----------------------------------------------------------------- small grid
 PAIRS = [("FP8_DIRECT", "FP8_DYNAMIC"), ("FP8_FIXED", "INT8"), ("TQ4", "UNIFORM4"),
-         ("TQ3", "UNIFORM3"), ("UNIFORM4", "TQ3"), ("INT8", "RAW"), ("INT8_ROWS", "TQ4")]
+         ("TQ3", "UNIFORM3"), ("UNIFORM4", "TQ3"), ("INT8", "RAW"), ("INT8_ROWS", "TQ4"), ("ANS16", "FP8_DYNAMIC")]
 
 
 @pytest.mark.parametrize("layout", ["separate", "packed"])
@@ -386,6 +386,20 @@ def test_int8_records_qwen3_full_size(ctx):
     ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
     segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 11)
     _roundtrip_case(ctx, wl, "INT8_ROWS", "INT8_ROWS", 0, ids, segments=segs, decode_from_oracle=False)
+
+
+def test_ans16_llama3_full_size(ctx):
+    """The lossless entropy stage on the Llama-3-8B shape, 32 layers x 8 heads
+    x D128 BF16, 4096 of 8192 blocks in random order: one full-size launch
+    each way; sampled segments' headers and payloads equal the oracle's and
+    every sampled page decodes bit-exactly."""
+    cfg = inputs.CONFIGS["ans16_llama3"]
+    print("[case] ans16 llama3", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
+    ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
+    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 13)
+    ora_st, gdesc = _roundtrip_case(ctx, wl, "ANS16", "ANS16", 0, ids, segments=segs, decode_from_oracle=False)
+    assert all(int(ora_st[s]) == O.SEG_ENCODED for s in segs)
 
 
 def test_k8v8_packed_full_size(ctx):
