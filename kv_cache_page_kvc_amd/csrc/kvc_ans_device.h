@@ -20,19 +20,42 @@ constexpr uint32_t kAnsStreams = 64;
 constexpr uint32_t kAnsProbBits = 12;
 constexpr uint32_t kAnsM = 1u << kAnsProbBits;
 constexpr uint32_t kAnsL = 1u << 23;
-constexpr int kAnsHistCopies = 4;              // sub-histograms: fewer lanes per LDS atomic address
 
-// encode constants of one symbol: frequency, cumulative frequency and the
-// reciprocal of the frequency for floor(x / f) = (x * m) >> (31 + l), exact
-// for every x < 2^31 (Granlund and Montgomery, "Division by invariant
-// integers using multiplication", PLDI 1994, Thm 4.2, with N = 31 and
-// l = ceil(log2 f), m = ceil(2^(31+l) / f), which fits 32 bits for f <= 2^12)
+// encode constants of one symbol with frequency f and cumulative frequency
+// cum, for the state update x -> (x / f) * 4096 + x mod f + cum written as
+// x + bias + q * cmpl with q = floor(x / f), cmpl = 4096 - f, bias = cum.
+// q is the high word of x * rcp shifted right by shift: rcp = ceil(2^(31+l)
+// / f), shift = l - 1 with l = ceil(log2 f), exact for every x < 2^31
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, Thm 4.2, with N = 31).  For f = 1, rcp =
+// 2^32 - 1 and shift = 0 give q = x - 1, and bias = cum + 4095 restores
+// x * 4096 + cum.  x_max = f * 2^19 bounds the state before the update.
 struct AnsEnc {
-  uint32_t f, cum, m, l;
+  uint32_t x_max, rcp, bias, cmpl_shift;       // cmpl | shift << 16
 };
 struct AnsDec {
   uint16_t f, cum;
 };
+__device__ __forceinline__ AnsEnc ans_enc_entry(uint32_t f, uint32_t cum) {
+  if (f == 0) return AnsEnc{0, 0, 0, 0};
+  if (f == 1) return AnsEnc{1u << 19, 0xFFFFFFFFu, cum + kAnsM - 1, kAnsM - 1};
+  const uint32_t l = 32 - __clz(f - 1);
+  const uint32_t rcp = (uint32_t)((((uint64_t)1 << (31 + l)) + f - 1) / f);
+  return AnsEnc{f << 19, rcp, cum, (kAnsM - f) | ((l - 1) << 16)};
+}
+
+// LDS of the encode kernel (dynamic): the histograms -- the high byte plane
+// in kAnsHiCopies copies, the low in kAnsLoCopies, copy-minor so that lanes
+// counting one symbol in different copies hit different banks -- then, in
+// the same bytes, the encode constants of both planes followed by the image
+// of one coded plane (p.stage_bytes: its 16-byte header, model, lengths and
+// streams, at most n + 16 bytes).
+constexpr uint32_t kAnsHiCopies = 16, kAnsLoCopies = 4;
+constexpr uint32_t kAnsHistBytes = 4 * 256 * (kAnsHiCopies + kAnsLoCopies);
+constexpr uint32_t kAnsEncBytes = 2 * 256 * sizeof(AnsEnc);
+inline uint32_t ans_encode_lds(uint32_t stage_bytes) {
+  return kAnsHistBytes > kAnsEncBytes + stage_bytes ? kAnsHistBytes : kAnsEncBytes + stage_bytes;
+}
 
 // element offset (in the page) of canonical chunk c: 8 elements of one vector
 __device__ __forceinline__ uint32_t ans_chunk_off(const SegCtx& s, uint32_t c, uint32_t d) {
@@ -90,51 +113,67 @@ __device__ __forceinline__ uint32_t ans_model(const uint32_t (&c)[4], uint32_t n
   return k;
 }
 
-// one encode step: renormalise (at most two bytes), then x = C(s, x).
-// EMIT: emitted byte k lands at end - 1 - k, for k below lim (the count of
-// the sizing pass, so that a source changed between the passes cannot make
-// the writes leave the stream's bytes)
+// one encode step: renormalise, then x = C(s, x).  The state leaves k bytes,
+// low byte first: one when x >= x_max, a second when also x >= 256 x_max
+// (never a third: x < 2^31 and x_max >= 2^19).  EMIT: emitted byte number
+// cnt lands at out[end - 1 - cnt] for cnt below lim (the count of the sizing
+// pass, so that a source changed between the passes cannot make the writes
+// leave the stream's bytes).  q = floor(x / f) < 2^19 and cmpl < 2^12, so
+// their product is a 24-bit multiply.
 template <bool EMIT>
-__device__ __forceinline__ void ans_put(uint32_t& x, const AnsEnc& e, uint32_t& cnt, uint8_t* end, uint32_t lim) {
-  const uint32_t x_max = (kAnsL >> kAnsProbBits << 8) * e.f;
-#pragma unroll
-  for (int r = 0; r < 2; r++)
-    if (x >= x_max) {
-      if constexpr (EMIT)
-        if (cnt < lim) *(end - 1 - cnt) = (uint8_t)x;
-      cnt++;
-      x >>= 8;
-    }
-  const uint32_t q = (uint32_t)(((uint64_t)x * e.m) >> (31 + e.l));
-  x = q * kAnsM + (x - q * e.f) + e.cum;
+__device__ __forceinline__ void ans_put(uint32_t& x, const AnsEnc& e, uint32_t& cnt, uint8_t* out, uint32_t end,
+                                        uint32_t lim) {
+  const bool one = x >= e.x_max, two = e.x_max < (1u << 24) && x >= (e.x_max << 8);
+  if constexpr (EMIT) {
+    if (one && cnt < lim) out[end - 1 - cnt] = (uint8_t)x;
+    if (two && cnt + 1 < lim) out[end - 2 - cnt] = (uint8_t)(x >> 8);
+  }
+  const uint32_t k = (uint32_t)one + (uint32_t)two;
+  cnt += k;
+  x >>= 8 * k;
+  const uint32_t q = __umulhi(x, e.rcp) >> (e.cmpl_shift >> 16);
+  x = x + e.bias + __umul24(q, e.cmpl_shift & 0xFFFFu);
 }
 
-// encode both planes of lane j's stream in reverse element order; EMIT:
-// write the renormalisation bytes before end0 / end1
-template <int D, bool EMIT>
-__device__ __forceinline__ void ans_encode_streams(const SegCtx& s, uint32_t n, const AnsEnc (*enc)[256],
-                                                   const bool (&coded)[2], uint32_t (&x)[2], uint32_t (&cnt)[2],
-                                                   uint8_t* end0, uint8_t* end1, uint32_t lim0, uint32_t lim1) {
+// encode the planes in use (U0: low, U1: high) of lane j's stream in reverse
+// element order; EMIT: write the renormalisation bytes of plane pl before
+// out[end[pl]].  The next chunk's source is loaded while this one is coded,
+// and a chunk's encode constants are read before its first step.
+template <int D, bool EMIT, bool U0, bool U1>
+__device__ __forceinline__ void ans_encode_streams(const SegCtx& s, uint32_t n, const AnsEnc* enc,
+                                                   uint32_t (&x)[2], uint32_t (&cnt)[2], uint8_t* out,
+                                                   const uint32_t (&end)[2], const uint32_t (&lim)[2]) {
   const uint32_t j = threadIdx.x & 63, chunks = n / 8;
   x[0] = x[1] = kAnsL;
   cnt[0] = cnt[1] = 0;
   if (j >= chunks) return;
-  for (int c = (int)(j + (chunks - 1 - j) / kAnsStreams * kAnsStreams); c >= 0; c -= kAnsStreams) {
-    const uint4 w = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, (uint32_t)c, D)));
-    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+  int c = (int)(j + (chunks - 1 - j) / kAnsStreams * kAnsStreams);
+  uint4 nw = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, (uint32_t)c, D)));
+  for (; c >= 0; c -= kAnsStreams) {
+    const uint32_t a[4] = {nw.x, nw.y, nw.z, nw.w};
+    if (c >= (int)kAnsStreams) nw = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, (uint32_t)c - kAnsStreams, D)));
+    AnsEnc e0[8], e1[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const uint32_t v = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      if constexpr (U0) e0[e] = enc[v & 0xFF];
+      if constexpr (U1) e1[e] = enc[256 + (v >> 8)];
+    }
 #pragma unroll
     for (int e = 7; e >= 0; e--) {
-      const uint32_t v = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      if (coded[0]) ans_put<EMIT>(x[0], enc[0][v & 0xFF], cnt[0], end0, lim0);
-      if (coded[1]) ans_put<EMIT>(x[1], enc[1][v >> 8], cnt[1], end1, lim1);
+      if constexpr (U0) ans_put<EMIT>(x[0], e0[e], cnt[0], out, end[0], lim[0]);
+      if constexpr (U1) ans_put<EMIT>(x[1], e1[e], cnt[1], out, end[1], lim[1]);
     }
   }
 }
 
 template <int D, bool CRC>
 __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
-  __shared__ uint32_t s_hist[2][kAnsHistCopies][256];
-  __shared__ AnsEnc s_enc[2][256];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+  uint32_t* const s_hist_hi = reinterpret_cast<uint32_t*>(s_dyn);     // [256][kAnsHiCopies]
+  uint32_t* const s_hist_lo = s_hist_hi + 256 * kAnsHiCopies;         // [256][kAnsLoCopies]
+  AnsEnc* const s_enc = reinterpret_cast<AnsEnc*>(s_dyn);             // [2][256], after the histograms
+  uint8_t* const s_out = s_dyn + kAnsEncBytes;                        // one coded plane's image
   __shared__ unsigned long long s_off;
   CrcTables* const ct = crc_tables_lds<CRC>();
   const uint32_t seg = p.seg_base + blockIdx.x;
@@ -162,42 +201,50 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
   s.st = p.st32;
   s.sh = p.sh32;
   const uint32_t n = (uint32_t)s.n_vec * D, raw_bytes = 2 * n, chunks = n / 8;
+  if (n + 16 > p.stage_bytes) {                                  // the launch's LDS cannot hold a plane image
+    if (lane == 0) reinterpret_cast<uint4*>(desc)[1] = make_uint4(0, 0, (uint32_t)KVC_SEG_GUARD << 24, 0);
+    return;
+  }
   constexpr int crc_flag = CRC ? KVC_FLAG_CRC32 : 0;
   if constexpr (CRC) load_crc_tables<64>(ct, &p.tables->crc);
 
   // histograms of both planes
-  for (uint32_t u = lane; u < 2 * kAnsHistCopies * 256; u += 64) (&s_hist[0][0][0])[u] = 0;
+  for (uint32_t u = lane; u < kAnsHistBytes / 16; u += 64) reinterpret_cast<uint4*>(s_dyn)[u] = make_uint4(0, 0, 0, 0);
   __syncthreads();
+  uint4 nw = lane < chunks ? ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, lane, D))) : make_uint4(0, 0, 0, 0);
   for (uint32_t c = lane; c < chunks; c += kAnsStreams) {
-    const uint4 w = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, c, D)));
-    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t a[4] = {nw.x, nw.y, nw.z, nw.w};
+    if (c + kAnsStreams < chunks) nw = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, c + kAnsStreams, D)));
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const uint32_t v = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      atomicAdd(&s_hist[0][lane & (kAnsHistCopies - 1)][v & 0xFF], 1u);
-      atomicAdd(&s_hist[1][lane & (kAnsHistCopies - 1)][v >> 8], 1u);
+      atomicAdd(&s_hist_lo[(v & 0xFF) * kAnsLoCopies + (lane & (kAnsLoCopies - 1))], 1u);
+      atomicAdd(&s_hist_hi[(v >> 8) * kAnsHiCopies + (lane & (kAnsHiCopies - 1))], 1u);
     }
   }
   __syncthreads();
-  // models, encode constants, and pass 1: the stream lengths
+  // counts of symbols 4*lane .. 4*lane+3, then the models and encode constants
+  uint32_t cnts[2][4];
+  for (int r = 0; r < 4; r++) {
+    const uint32_t sy = 4 * lane + r;
+    uint32_t t = 0;
+    for (uint32_t q = 0; q < kAnsLoCopies; q++) t += s_hist_lo[sy * kAnsLoCopies + q];
+    cnts[0][r] = t;
+    t = 0;
+    for (uint32_t q = 0; q < kAnsHiCopies; q++) t += s_hist_hi[sy * kAnsHiCopies + q];
+    cnts[1][r] = t;
+  }
+  __syncthreads();                                               // the constants overwrite the histograms
   uint32_t f[2][4], cum[2][4], k[2];
   for (int pl = 0; pl < 2; pl++) {
-    uint32_t c[4];
-    for (int r = 0; r < 4; r++) {
-      c[r] = 0;
-      for (int q = 0; q < kAnsHistCopies; q++) c[r] += s_hist[pl][q][4 * lane + r];
-    }
-    k[pl] = ans_model(c, n, f[pl], cum[pl]);
-    for (int r = 0; r < 4; r++) {
-      const uint32_t d = f[pl][r], lg = d > 1 ? 32 - __clz(d - 1) : 0;
-      const uint32_t m = d ? (uint32_t)((((uint64_t)1 << (31 + lg)) + d - 1) / d) : 0;
-      s_enc[pl][4 * lane + r] = AnsEnc{d, cum[pl][r], m, lg};
-    }
+    k[pl] = ans_model(cnts[pl], n, f[pl], cum[pl]);
+    for (int r = 0; r < 4; r++) s_enc[256 * pl + 4 * lane + r] = ans_enc_entry(f[pl][r], cum[pl][r]);
   }
   __syncthreads();
-  const bool all[2] = {true, true};
+  // pass 1: the stream lengths
+  const uint32_t zero2[2] = {0, 0};
   uint32_t x[2], cnt[2];
-  ans_encode_streams<D, false>(s, n, s_enc, all, x, cnt, nullptr, nullptr, 0, 0);
+  ans_encode_streams<D, false, true, true>(s, n, s_enc, x, cnt, nullptr, zero2, zero2);
   uint32_t len[2], body[2], psize[2];
   bool coded[2];
   for (int pl = 0; pl < 2; pl++) {
@@ -231,49 +278,51 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
                         (int)p.dtype, comp, D, s.n_vec, raw_bytes, off, 0, cr);
     return;
   }
-  // pass 2: the payload
-  uint32_t base[2] = {0, psize[0]};
-  uint8_t* end[2] = {nullptr, nullptr};
+  // pass 2, a plane at a time: a raw plane goes straight to the spill region,
+  // a coded plane is assembled in LDS and written out in 16-byte units
+#pragma unroll
   for (int pl = 0; pl < 2; pl++) {
-    uint8_t* const P = heap + base[pl];
-    if (lane == 0) {
-      st_global16(P, make_uint4(coded[pl] ? 1u | (k[pl] << 16) : 0u, 0, 0, 0));
-      for (uint32_t b = 16 + (coded[pl] ? body[pl] : n); b < psize[pl]; b++) P[b] = 0;
-    }
+    uint8_t* const P = heap + (pl ? psize[0] : 0);
     if (!coded[pl]) {                                            // raw plane: byte pl of every value
+      if (lane == 0) st_global16(P, make_uint4(0, 0, 0, 0));
       for (uint32_t c = lane; c < chunks; c += kAnsStreams) {
         const uint4 w = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, c, D)));
         const uint32_t sel = pl ? 0x07050301u : 0x06040200u;    // bytes of the 8 values, in order
         *reinterpret_cast<uint2*>(P + 16 + 8 * c) =
             make_uint2(__builtin_amdgcn_perm(w.y, w.x, sel), __builtin_amdgcn_perm(w.w, w.z, sel));
       }
+      for (uint32_t b = 16 + n + lane; b < psize[pl]; b += 64) P[b] = 0;
       continue;
     }
-    // bitmap, frequencies of the present symbols, stream lengths
+    // header, bitmap, frequencies of the present symbols, stream lengths
+    if (lane == 0) *reinterpret_cast<uint4*>(s_out) = make_uint4(1u | (k[pl] << 16), 0, 0, 0);
     uint32_t nib = 0, present = 0;
     for (int r = 0; r < 4; r++) {
       nib |= (f[pl][r] != 0) << r;
       present += f[pl][r] != 0;
     }
     const uint32_t other = __shfl_xor(nib, 1, 64);
-    if (!(lane & 1)) P[16 + lane / 2] = (uint8_t)(nib | (other << 4));
+    if (!(lane & 1)) s_out[16 + lane / 2] = (uint8_t)(nib | (other << 4));
     uint32_t pos = wave_excl_scan(present);
     for (int r = 0; r < 4; r++)
-      if (f[pl][r]) *reinterpret_cast<uint16_t*>(P + 48 + 2 * pos++) = (uint16_t)f[pl][r];
-    uint8_t* const lens = P + 48 + 2 * k[pl];
-    *reinterpret_cast<uint16_t*>(lens + 2 * lane) = (uint16_t)len[pl];
-    uint8_t* const st = lens + 2 * kAnsStreams + wave_excl_scan(len[pl]);
-    end[pl] = st + len[pl];
+      if (f[pl][r]) *reinterpret_cast<uint16_t*>(s_out + 48 + 2 * pos++) = (uint16_t)f[pl][r];
+    const uint32_t lens = 48 + 2 * k[pl];
+    *reinterpret_cast<uint16_t*>(s_out + lens + 2 * lane) = (uint16_t)len[pl];
+    const uint32_t st = lens + 2 * kAnsStreams + wave_excl_scan(len[pl]);
+    for (uint32_t b = 16 + body[pl] + lane; b < psize[pl]; b += 64) s_out[b] = 0;
+    const uint32_t endv[2] = {st + len[pl], st + len[pl]};
+    const uint32_t limv[2] = {len[pl] - 4, len[pl] - 4};
+    if (pl == 0) ans_encode_streams<D, true, true, false>(s, n, s_enc, x, cnt, s_out, endv, limv);
+    else ans_encode_streams<D, true, false, true>(s, n, s_enc, x, cnt, s_out, endv, limv);
+    s_out[st] = (uint8_t)x[pl];                                  // final state, u32 little-endian
+    s_out[st + 1] = (uint8_t)(x[pl] >> 8);
+    s_out[st + 2] = (uint8_t)(x[pl] >> 16);
+    s_out[st + 3] = (uint8_t)(x[pl] >> 24);
+    __syncthreads();
+    for (uint32_t u = lane; u < psize[pl] / 16; u += 64)
+      st_global16(P + 16 * u, *reinterpret_cast<const uint4*>(s_out + 16 * u));
+    __syncthreads();                                             // the image is rebuilt for the next plane
   }
-  ans_encode_streams<D, true>(s, n, s_enc, coded, x, cnt, end[0], end[1], len[0] - 4, len[1] - 4);
-  for (int pl = 0; pl < 2; pl++)
-    if (coded[pl]) {
-      uint8_t* const st = end[pl] - len[pl];
-      st[0] = (uint8_t)x[pl];
-      st[1] = (uint8_t)(x[pl] >> 8);
-      st[2] = (uint8_t)(x[pl] >> 16);
-      st[3] = (uint8_t)(x[pl] >> 24);
-    }
   const uint32_t cr = CRC ? crc32_written(heap, payload, ct) : 0u;
   if (lane == 0) {
     __threadfence();                                             // payload before the header that points at it
@@ -282,22 +331,22 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
   }
 }
 
-// slot -> symbol table of a coded plane and its (f, cum) pairs; returns
-// false if the plane's model is malformed.  Lanes fill 64-slot blocks.
+// slot -> symbol table of a coded plane (payload bytes P in global memory)
+// and its (f, cum) pairs; returns false if the plane's model is malformed.
+// Lane j fills slots [64 j, 64 j + 64), four to a word.
 __device__ __forceinline__ bool ans_load_model(const uint8_t* P, uint32_t k, AnsDec* tab, uint8_t* lut) {
   const uint32_t lane = threadIdx.x & 63;
-  uint32_t fr[4], present = 0;
-  for (int r = 0; r < 4; r++) present += (P[16 + (4 * lane + r) / 8] >> ((4 * lane + r) & 7)) & 1;
+  const uint32_t bits = (P[16 + lane / 2] >> (4 * (lane & 1))) & 15u;   // symbols 4 lane .. 4 lane + 3
+  const uint32_t present = __popc(bits);
   uint32_t pos = wave_excl_scan(present);
   const bool ok_k = wave_sum(present) == k;
-  uint32_t tot = 0;
+  uint32_t fr[4], tot = 0;
   for (int r = 0; r < 4; r++) {
-    const uint32_t sy = 4 * lane + r;
-    fr[r] = ((P[16 + sy / 8] >> (sy & 7)) & 1) && pos < k ? *reinterpret_cast<const uint16_t*>(P + 48 + 2 * pos++) : 0;
+    fr[r] = (bits >> r) & 1 && pos < k ? *reinterpret_cast<const uint16_t*>(P + 48 + 2 * pos++) : 0;
     tot += fr[r];
   }
   bool ok = ok_k && wave_sum(tot) == kAnsM;
-  for (int r = 0; r < 4; r++) ok = ok && (((P[16 + (4 * lane + r) / 8] >> ((4 * lane + r) & 7)) & 1) == (fr[r] != 0));
+  for (int r = 0; r < 4; r++) ok = ok && (((bits >> r) & 1) == (fr[r] != 0));
   ok = __all(ok);
   uint32_t run = wave_excl_scan(tot);
   for (int r = 0; r < 4; r++) {
@@ -306,30 +355,153 @@ __device__ __forceinline__ bool ans_load_model(const uint8_t* P, uint32_t k, Ans
   }
   __syncthreads();
   if (!ok) return false;
-  // slots [64*lane, 64*lane + 64): the symbol of the first by binary search, then walk
+  // the symbol of slot 64 lane: the largest with cum <= 64 lane (it has f > 0,
+  // since a later symbol with f = 0 would share its cum), then walk
   const uint32_t s0 = 64 * lane;
-  uint32_t lo = 0, hi = 255;                                     // largest symbol with cum <= s0 and f > 0
+  uint32_t lo = 0, hi = 255;
   while (lo < hi) {
     const uint32_t mid = (lo + hi + 1) / 2;
     if (tab[mid].cum <= s0) lo = mid;
     else hi = mid - 1;
   }
-  uint32_t sy = lo;
-  while (sy > 0 && tab[sy].f == 0) sy--;
-  for (uint32_t sl = s0; sl < s0 + 64; sl++) {
-    while (sl >= (uint32_t)tab[sy].cum + tab[sy].f) sy++;
-    lut[sl] = (uint8_t)sy;
+  uint32_t sy = lo, lim = (uint32_t)tab[sy].cum + tab[sy].f;
+  for (uint32_t w = 0; w < 16; w++) {
+    uint32_t word = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < 4; b++) {
+      while (s0 + 4 * w + b >= lim) {                            // frequencies sum to 4096: ends by sy = 255
+        sy++;
+        lim = (uint32_t)tab[sy].cum + tab[sy].f;
+      }
+      word |= sy << (8 * b);
+    }
+    *reinterpret_cast<uint32_t*>(lut + s0 + 4 * w) = word;
   }
   __syncthreads();
   return true;
 }
 
+// 4 payload bytes at aligned offset a, or at the last aligned offset of the
+// checked span when a is past it (such bytes lie beyond every stream)
+__device__ __forceinline__ uint32_t ans_word(const uint8_t* heap, uint32_t a, uint32_t span) {
+  return ld_global4(heap + min(a, span - 4));
+}
+
+// the 16 payload bytes at block-aligned offset b, or the last block of the
+// checked span when b is past it (such bytes lie beyond every stream)
+__device__ __forceinline__ uint4 ans_block(const uint8_t* heap, uint32_t b, uint32_t span) {
+  return ld_global16(heap + min(b, span - 16));
+}
+
+// A lane's window on its stream of a coded plane: a ring of four 16-byte
+// blocks in LDS; word w of lane j at ring[64 w + j] (a bank per lane).  The
+// block at payload offset b (a multiple of 16) occupies words (b / 4) mod 16
+// to + 3.
+constexpr uint32_t kAnsRingWords = 16;
+__device__ __forceinline__ void ans_ring_put(uint32_t* ring, uint32_t b, uint4 v) {
+  const uint32_t j = threadIdx.x & 63, w = (b >> 2) & (kAnsRingWords - 1);
+  ring[64 * w + j] = v.x;
+  ring[64 * (w + 1) + j] = v.y;
+  ring[64 * (w + 2) + j] = v.z;
+  ring[64 * (w + 3) + j] = v.w;
+}
+__device__ __forceinline__ uint32_t ans_ring_byte(const uint32_t* ring, uint32_t q) {
+  const uint32_t j = threadIdx.x & 63;
+  return reinterpret_cast<const uint8_t*>(ring)[4 * (64 * ((q >> 2) & (kAnsRingWords - 1)) + j) + (q & 3)];
+}
+
+// Decode lane j's streams (chunks j, j + 64, ...) of both planes and write
+// each chunk of 8 values; C0 / C1: the low / high plane is coded (else raw).
+// Returns true when a stream is malformed: a state outside [2^23, 2^31) at
+// its start, more bytes consumed than it holds, or an end other than exactly
+// its last byte in state 2^23.
+//
+// A coded stream's bytes reach the lane through its ring: the ring holds
+// the blocks of pos and pos + 16 during a chunk (a chunk consumes at most 16
+// bytes: two per value), and the block two ahead is loaded while a chunk is
+// decoded and stored into the ring before the next one.  Raw planes' bytes
+// are likewise loaded a chunk ahead.  A state x >= 2^23 leaves a decode step
+// at or above 2^11, so one byte brings it back above 2^23 from [2^15, 2^23)
+// and two from [2^11, 2^15).
+template <int D, bool C0, bool C1>
+__device__ __forceinline__ bool ans_decode_lanes(const SegCtx& s, uint16_t* page_p, const uint8_t* heap, uint32_t span,
+                                                 uint32_t chunks, const uint32_t (&pbase)[2], const uint32_t (&sbeg)[2],
+                                                 const uint32_t (&send)[2], const AnsDec (*tab)[256],
+                                                 const uint8_t (*lut)[kAnsM], uint32_t (*ring)[64 * kAnsRingWords]) {
+  constexpr bool C[2] = {C0, C1};
+  const uint32_t lane = threadIdx.x & 63;
+  uint32_t x[2] = {kAnsL, kAnsL}, pos[2] = {0, 0}, nb[2] = {0, 0};
+  uint4 pend[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  uint2 rb[2] = {make_uint2(0, 0), make_uint2(0, 0)};
+  bool bad = false;
+#pragma unroll
+  for (int pl = 0; pl < 2; pl++) {
+    if constexpr (true) {
+      if (C[pl]) {
+        const uint32_t a = sbeg[pl] & ~3u;                       // final state, u32 little-endian
+        x[pl] = __builtin_amdgcn_alignbyte(ans_word(heap, a + 4, span), ans_word(heap, a, span), sbeg[pl] & 3);
+        bad |= x[pl] < kAnsL || x[pl] >= (kAnsL << 8);
+        pos[pl] = sbeg[pl] + 4;
+        const uint32_t b0 = pos[pl] & ~15u;
+        ans_ring_put(ring[pl], b0, ans_block(heap, b0, span));
+        ans_ring_put(ring[pl], b0 + 16, ans_block(heap, b0 + 16, span));
+        nb[pl] = b0 + 32;
+        pend[pl] = ans_block(heap, nb[pl], span);
+      } else if (lane < chunks) {
+        rb[pl] = ld_global8(heap + pbase[pl] + 16 + 8 * lane);
+      }
+    }
+  }
+  for (uint32_t c = lane; c < chunks; c += kAnsStreams) {
+    uint2 r[2];
+#pragma unroll
+    for (int pl = 0; pl < 2; pl++) {
+      if (C[pl]) {
+        ans_ring_put(ring[pl], nb[pl], pend[pl]);
+        nb[pl] = (pos[pl] & ~15u) + 32;
+        pend[pl] = ans_block(heap, nb[pl], span);
+      } else {
+        r[pl] = rb[pl];
+        if (c + kAnsStreams < chunks) rb[pl] = ld_global8(heap + pbase[pl] + 16 + 8 * (c + kAnsStreams));
+      }
+    }
+    uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      uint32_t b[2];
+#pragma unroll
+      for (int pl = 0; pl < 2; pl++) {
+        if (!C[pl]) {
+          b[pl] = ((e < 4 ? r[pl].x : r[pl].y) >> (8 * (e & 3))) & 0xFFu;
+          continue;
+        }
+        const uint32_t q0 = ans_ring_byte(ring[pl], pos[pl]), q1 = ans_ring_byte(ring[pl], pos[pl] + 1);
+        const uint32_t sl = x[pl] & (kAnsM - 1), sy = lut[pl][sl];
+        const AnsDec t = tab[pl][sy];
+        b[pl] = sy;
+        x[pl] = __umul24(t.f, x[pl] >> kAnsProbBits) + sl - t.cum;
+        const uint32_t k = (uint32_t)(x[pl] < kAnsL) + (uint32_t)(x[pl] < (kAnsL >> 8));
+        const uint32_t in = k == 2 ? (q0 << 8) | q1 : (k == 1 ? q0 : 0u);
+        x[pl] = (x[pl] << (8 * k)) | in;
+        bad |= pos[pl] + k > send[pl];
+        pos[pl] += k;
+      }
+      o[e >> 1] |= (b[0] | (b[1] << 8)) << (16 * (e & 1));
+    }
+    st_global16(byte_at(page_p, 2 * ans_chunk_off(s, c, D)), make_uint4(o[0], o[1], o[2], o[3]));
+  }
+#pragma unroll
+  for (int pl = 0; pl < 2; pl++)
+    if (C[pl]) bad |= pos[pl] != send[pl] || x[pl] != kAnsL;
+  return bad;
+}
+
 template <int D, bool CRC>
 __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   __shared__ AnsDec s_tab[2][256];
-  __shared__ uint8_t s_lut[2][kAnsM];
+  __shared__ __attribute__((aligned(16))) uint8_t s_lut[2][kAnsM];
+  __shared__ uint32_t s_ring[2][64 * kAnsRingWords];
   __shared__ uint32_t s_crc_ok;
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_img[];  // p.stage_bytes: the payload
   CrcTables* const ct = crc_tables_lds<CRC>();
   const uint32_t seg = p.seg_base + blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
@@ -367,10 +539,11 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   const uint64_t spill = (uint64_t)h1.x | ((uint64_t)h1.y << 32);
   const uint32_t stored = h0.w;
   if (raw_data) ok = ok && format == KVC_RAW && !(flags & KVC_FLAG_CAPACITY) && stored == raw_bytes;
-  else ok = ok && format == C_ANS && (flags & KVC_FLAG_HEAP) && stored >= 32 && stored <= p.stage_bytes;
-  // every read stays in the buffer: the stored bytes rounded up to 16
+  else ok = ok && format == C_ANS && (flags & KVC_FLAG_HEAP) && stored >= 32 && stored <= raw_bytes;
+  // every read stays in the buffer: the stored bytes rounded up to 16, from
+  // a 16-byte aligned offset
   const uint64_t span = ((uint64_t)stored + 15) & ~15ull;
-  ok = ok && spill >= p.slot_region && span <= p.buf_bytes && spill <= p.buf_bytes - span;
+  ok = ok && (spill & 15) == 0 && spill >= p.slot_region && span <= p.buf_bytes && spill <= p.buf_bytes - span;
   if (!ok) {
     if (report) p.seg_status[seg] = 1;
     return;
@@ -392,19 +565,16 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
     if (report) p.seg_status[seg] = 0;
     return;
   }
-  // stage the payload, parse both planes' headers and models
-  for (uint32_t u = lane; u < (stored + 15) / 16; u += 64)
-    *reinterpret_cast<uint4*>(s_img + 16 * u) = ld_global16(heap + 16 * u);
-  __syncthreads();
+  // parse both planes' headers and models
   uint32_t pbase[2], mode[2], kk[2], sbeg[2] = {0, 0}, send[2] = {0, 0};
   uint32_t at = 0;
   bool good = true;
   for (int pl = 0; pl < 2 && good; pl++) {
-    const uint8_t* const P = s_img + at;
+    const uint8_t* const P = heap + at;
     pbase[pl] = at;
     good = at + 16 <= stored;
     if (!good) break;
-    const uint4 hd = *reinterpret_cast<const uint4*>(P);
+    const uint4 hd = ld_global16(P);
     mode[pl] = hd.x & 0xFFFF;
     kk[pl] = hd.x >> 16;
     good = hd.y == 0 && hd.z == 0 && hd.w == 0 && mode[pl] <= 1 && kk[pl] <= 256;
@@ -417,7 +587,7 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
       const uint32_t lens_at = at + 48 + 2 * kk[pl];
       good = lens_at + 2 * kAnsStreams <= stored && kk[pl] >= 1;
       if (!good) break;
-      const uint32_t len = *reinterpret_cast<const uint16_t*>(s_img + lens_at + 2 * lane);
+      const uint32_t len = *reinterpret_cast<const uint16_t*>(heap + lens_at + 2 * lane);
       const uint32_t st0 = lens_at + 2 * kAnsStreams + wave_excl_scan(len);
       sbeg[pl] = st0;
       send[pl] = st0 + len;
@@ -427,7 +597,7 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
     }
     const uint32_t padded = (size + 15) & ~15u;
     good = good && at + padded <= stored;
-    if (good) good = __all(lane >= padded - size || s_img[at + size + lane] == 0);   // zero padding
+    if (good) good = __all(lane >= padded - size || heap[at + size + lane] == 0);   // zero padding
     at += padded;
   }
   good = good && at == stored;                                   // exact length of the payload
@@ -435,54 +605,20 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
     if (report) p.seg_status[seg] = 1;
     return;
   }
-  // decode lane j's streams of both planes, writing each chunk of 8 values
-  uint32_t x[2] = {kAnsL, kAnsL}, pos[2] = {sbeg[0], sbeg[1]};
-  for (int pl = 0; pl < 2; pl++)
-    if (mode[pl]) {                                              // final state, u32 little-endian
-      const uint8_t* q = s_img + pos[pl];
-      x[pl] = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
-      pos[pl] += 4;
-    }
-  bool bad = false;
-  for (uint32_t c = lane; c < chunks; c += kAnsStreams) {
-    uint32_t o[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const uint32_t i = 8 * c + e;
-      uint32_t b[2];
-#pragma unroll
-      for (int pl = 0; pl < 2; pl++) {
-        if (!mode[pl]) {
-          b[pl] = s_img[pbase[pl] + 16 + i];
-          continue;
-        }
-        const uint32_t sl = x[pl] & (kAnsM - 1), sy = s_lut[pl][sl];
-        const AnsDec t = s_tab[pl][sy];
-        b[pl] = sy;
-        x[pl] = t.f * (x[pl] >> kAnsProbBits) + sl - t.cum;
-#pragma unroll
-        for (int r = 0; r < 2; r++)
-          if (x[pl] < kAnsL) {
-            const bool in = pos[pl] < send[pl];
-            bad |= !in;
-            x[pl] = (x[pl] << 8) | (in ? s_img[pos[pl]] : 0u);
-            pos[pl] += in;
-          }
-      }
-      o[e >> 1] |= (b[0] | (b[1] << 8)) << (16 * (e & 1));
-    }
-    st_global16(byte_at(page_p, 2 * ans_chunk_off(s, c, D)), make_uint4(o[0], o[1], o[2], o[3]));
-  }
-  for (int pl = 0; pl < 2; pl++) bad |= mode[pl] && (pos[pl] != send[pl] || x[pl] != kAnsL);
+  bool bad;
+  if (mode[0]) bad = mode[1] ? ans_decode_lanes<D, true, true>(s, page_p, heap, (uint32_t)span, chunks, pbase, sbeg, send, s_tab, s_lut, s_ring)
+                             : ans_decode_lanes<D, true, false>(s, page_p, heap, (uint32_t)span, chunks, pbase, sbeg, send, s_tab, s_lut, s_ring);
+  else bad = mode[1] ? ans_decode_lanes<D, false, true>(s, page_p, heap, (uint32_t)span, chunks, pbase, sbeg, send, s_tab, s_lut, s_ring)
+                     : ans_decode_lanes<D, false, false>(s, page_p, heap, (uint32_t)span, chunks, pbase, sbeg, send, s_tab, s_lut, s_ring);
   bad = __any(bad);
   if (report) p.seg_status[seg] = bad ? 1 : 0;
 }
 
 template <int D, bool CRC>
 void launch_ans_encode_dc(const CallParams& p, uint64_t n, hipStream_t st) {
-  hipLaunchKernelGGL((ans_encode_kernel<D, CRC>), dim3((unsigned)n), dim3(64), 0, st, p);
+  hipLaunchKernelGGL((ans_encode_kernel<D, CRC>), dim3((unsigned)n), dim3(64), ans_encode_lds(p.stage_bytes), st, p);
 }
 template <int D, bool CRC>
 void launch_ans_decode_dc(const CallParams& p, uint64_t n, hipStream_t st) {
-  hipLaunchKernelGGL((ans_decode_kernel<D, CRC>), dim3((unsigned)n), dim3(64), p.stage_bytes, st, p);
+  hipLaunchKernelGGL((ans_decode_kernel<D, CRC>), dim3((unsigned)n), dim3(64), 0, st, p);
 }

@@ -22,6 +22,12 @@ __device__ __forceinline__ uint4 ld_global16(const void* p) {
   const u32x4 v = *(const g_u32x4*)p;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint32_t ld_global4(const void* p) { return *(const g_u32*)p; }
+__device__ __forceinline__ uint2 ld_global8(const void* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = *(const __attribute__((address_space(1))) u32x2*)p;
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void st_global16(void* p, uint4 v) {
   u32x4 w = {v.x, v.y, v.z, v.w};
   *(g_u32x4*)p = w;

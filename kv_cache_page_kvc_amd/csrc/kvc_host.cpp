@@ -504,21 +504,21 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
 
 // Encode / decode launches of a call: the fixed-size codecs' kernel, then,
 // when some component uses KVC_ANS16, the entropy stage's kernel over the
-// same segments (each skips the other's segments).  The entropy decode
-// stages a payload of at most 7/8 of the segment's source bytes in LDS.
+// same segments (each skips the other's segments).  The entropy encode
+// assembles one coded byte plane at a time in LDS: at most n + 16 bytes for
+// n values per segment.
 hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
   hipError_t e = launch_encode(P, L->head_dim, nseg, s);
-  if (e == hipSuccess && plan.ans) e = launch_ans_encode(P, L->head_dim, nseg, s);
+  if (e == hipSuccess && plan.ans) {
+    CallParams A = P;
+    A.stage_bytes = L->kv_heads * L->tokens_per_page * L->head_dim + 16;
+    e = launch_ans_encode(A, L->head_dim, nseg, s);
+  }
   return e;
 }
 hipError_t run_decode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
   hipError_t e = launch_decode(P, L->head_dim, nseg, s);
-  if (e == hipSuccess && plan.ans) {
-    CallParams A = P;
-    const uint32_t raw = L->kv_heads * L->tokens_per_page * L->head_dim * 2;
-    A.stage_bytes = (uint32_t)align_up(7ull * raw / 8, 16);
-    e = launch_ans_decode(A, L->head_dim, nseg, s);
-  }
+  if (e == hipSuccess && plan.ans) e = launch_ans_decode(P, L->head_dim, nseg, s);
   return e;
 }
 

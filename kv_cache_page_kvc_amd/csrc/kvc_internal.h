@@ -129,8 +129,8 @@ hipError_t launch_encode(const CallParams& p, uint32_t head_dim, uint64_t n_segm
 hipError_t launch_decode(const CallParams& p, uint32_t head_dim, uint64_t n_segments,
                          hipStream_t stream);
 // The entropy stage (KVC_ANS16 segments; the kernels above skip them), one
-// wave per segment, over the same segments.  Decode: p.stage_bytes of
-// dynamic LDS hold a segment's payload.
+// wave per segment, over the same segments.  Encode: p.stage_bytes (at
+// least n + 16 for n values per segment) of LDS hold one coded byte plane.
 hipError_t launch_ans_encode(const CallParams& p, uint32_t head_dim, uint64_t n_segments, hipStream_t stream);
 hipError_t launch_ans_decode(const CallParams& p, uint32_t head_dim, uint64_t n_segments, hipStream_t stream);
 // ANS16 applies to segments of this many source bytes (others stay raw)

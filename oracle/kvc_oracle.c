@@ -639,9 +639,10 @@ size_t kvo_ans_encode_plane(const uint8_t *sym, size_t n, uint8_t *out) {
 
 /* Decode n symbols from `in` (avail bytes).  Returns the bytes consumed, or
  * 0 on any inconsistency: an unknown mode, a bitmap not holding K symbols,
- * frequencies not summing to 2^12, a stream running past its length or not
- * ending exactly at its length in the initial state (the exact-length
- * check), nonzero padding. */
+ * frequencies not summing to 2^12, a stream whose starting state lies outside
+ * the coder's state interval [2^23, 2^31) (every final state of the encoder
+ * lies in it), a stream running past its length or not ending exactly at its
+ * length in the initial state (the exact-length check), nonzero padding. */
 size_t kvo_ans_decode_plane(const uint8_t *in, size_t avail, size_t n, uint8_t *sym) {
   if (avail < 16) return 0;
   const uint32_t mode = get_u16(in), k = get_u16(in + 2);
@@ -679,6 +680,7 @@ size_t kvo_ans_decode_plane(const uint8_t *in, size_t avail, size_t n, uint8_t *
       if (len < 4 || off + len > avail) return 0;
       const uint8_t *st = in + off;
       uint32_t x = get_u32(st);
+      if (x < ANS_L || x >= (ANS_L << 8)) return 0;
       size_t pos = 4;
       for (size_t c = j; 8 * c < n; c += ANS_STREAMS)
         for (size_t e = 0; e < 8 && 8 * c + e < n; e++) {

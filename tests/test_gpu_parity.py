@@ -402,6 +402,47 @@ def test_ans16_llama3_full_size(ctx):
     assert all(int(ora_st[s]) == O.SEG_ENCODED for s in segs)
 
 
+def _bf16_planes(hi, lo):
+    """BF16 tensor from byte planes (int64 tensors of the same shape)."""
+    b = (hi << 8) | lo
+    return (b - (b >= 32768).to(b.dtype) * 65536).to(torch.int16).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("crc", [False, True])
+def test_ans16_plane_modes(ctx, crc):
+    """ANS16 with each kind of payload the decoder distinguishes, 8 heads x
+    D128 BF16 (32 KiB segments), 2 layers x 4 of 9 blocks: both byte planes
+    coded (small integers), only the low plane coded (random high bytes,
+    low bytes from 4 values), only the high plane coded (Gaussian data), and
+    neither (uniform bits: stored raw).  The plane modes are checked on the
+    oracle's own coding of the planes; every segment is compared."""
+    print(f"[case] ans16 plane modes crc={crc}", flush=True)
+    wl = G.Workload(2, 8, 128, 16, 9, "bf16", "separate", seed=21)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    shape = wl.k[0].shape
+    wl.k[0].copy_((torch.randn(shape, generator=g, device="cuda") * 3).round().clamp(-8, 8).to(torch.bfloat16))
+
+    def finite_hi():                                      # high bytes except 0x7F and 0xFF (Inf/NaN exponents)
+        r = torch.randint(0, 254, shape, generator=g, device="cuda")
+        return r + (r >= 127).to(r.dtype)
+
+    wl.k[1].copy_(_bf16_planes(finite_hi(), torch.randint(0, 4, shape, generator=g, device="cuda") * 64))
+    wl.v[1].copy_(_bf16_planes(finite_hi(), torch.randint(0, 256, shape, generator=g, device="cuda")))
+    ids = inputs.random_page_ids(9, 4, seed=3)
+    expect = {(0, 0): (1, 1), (0, 1): (0, 1), (1, 0): (1, 0)}       # (layer, comp) -> (low, high) plane mode
+    for (l, c), modes in expect.items():
+        t = (wl.k if c == 0 else wl.v)[l][int(ids[0])]
+        bits = t.contiguous().view(torch.int16).cpu().numpy().astype(np.uint16).reshape(-1)
+        got = tuple(int(O.ans_encode_plane((bits >> (8 * pl)) & 0xFF)[0]) for pl in (0, 1))
+        assert got == modes, f"layer {l} comp {c}: plane modes {got}"
+    ora_st, _ = _roundtrip_case(ctx, wl, "ANS16", "ANS16", 0, ids, dst_ids=inputs.random_page_ids(9, 4, seed=4),
+                                crc=crc)
+    seglist = G.segments_of(wl.L, len(ids))
+    for sidx, (l, i, c) in enumerate(seglist):
+        want = O.SEG_RAW_DATA if (l, c) == (1, 1) else O.SEG_ENCODED
+        assert int(ora_st[sidx]) == want, f"segment {sidx}: status {ora_st[sidx]}"
+
+
 def test_k8v8_packed_full_size(ctx):
     """K8/V8 with per-token/head FP8 scales on the vLLM packed FP16 Qwen3-8B
     layout [2048 blocks, 8 heads, 16 tokens, 256], 36 layers: full-size

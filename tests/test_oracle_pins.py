@@ -866,6 +866,11 @@ def test_ans_exact_length_check(oracle):
     table = enc.copy()
     table[48:50] = (table[48:50].view(np.uint16) + 1).view(np.uint8)                    # frequencies sum to 4097
     assert oracle.ans_decode_plane(table, n)[1] == 0
+    # a starting state outside the state interval [2^23, 2^31) is malformed
+    for state in (0, (1 << 23) - 1, 1 << 31, 0xFFFFFFFF):
+        st = enc.copy()
+        st[first:first + 4] = np.array([state], np.uint32).view(np.uint8)
+        assert oracle.ans_decode_plane(st, n)[1] == 0
 
 
 def _kv_bits(rng, n_vec, d, dtype, scale=None):
