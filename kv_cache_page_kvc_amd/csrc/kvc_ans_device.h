@@ -36,12 +36,11 @@ struct AnsEnc {
 struct AnsDec {
   uint16_t f, cum;
 };
-__device__ __forceinline__ AnsEnc ans_enc_entry(uint32_t f, uint32_t cum) {
+__device__ __forceinline__ AnsEnc ans_enc_entry(uint32_t f, uint32_t cum, const uint32_t* rcp_tab) {
   if (f == 0) return AnsEnc{0, 0, 0, 0};
   if (f == 1) return AnsEnc{1u << 19, 0xFFFFFFFFu, cum + kAnsM - 1, kAnsM - 1};
   const uint32_t l = 32 - __clz(f - 1);
-  const uint32_t rcp = (uint32_t)((((uint64_t)1 << (31 + l)) + f - 1) / f);
-  return AnsEnc{f << 19, rcp, cum, (kAnsM - f) | ((l - 1) << 16)};
+  return AnsEnc{f << 19, rcp_tab[f], cum, (kAnsM - f) | ((l - 1) << 16)};
 }
 
 // LDS of the encode kernel (dynamic): the histograms -- the high byte plane
@@ -137,12 +136,15 @@ __device__ __forceinline__ void ans_put(uint32_t& x, const AnsEnc& e, uint32_t& 
 
 // encode the planes in use (U0: low, U1: high) of lane j's stream in reverse
 // element order; EMIT: write the renormalisation bytes of plane pl before
-// out[end[pl]].  The next chunk's source is loaded while this one is coded,
-// and a chunk's encode constants are read before its first step.
-template <int D, bool EMIT, bool U0, bool U1>
+// out[end[pl]].  RAW = 0 / 1: also store byte plane RAW of each chunk, in
+// order, at raw[8 c] (the raw plane of the payload).  The next chunk's
+// source is loaded while this one is coded, and a chunk's encode constants
+// are read before its first step.
+template <int D, bool EMIT, bool U0, bool U1, int RAW = -1>
 __device__ __forceinline__ void ans_encode_streams(const SegCtx& s, uint32_t n, const AnsEnc* enc,
                                                    uint32_t (&x)[2], uint32_t (&cnt)[2], uint8_t* out,
-                                                   const uint32_t (&end)[2], const uint32_t (&lim)[2]) {
+                                                   const uint32_t (&end)[2], const uint32_t (&lim)[2],
+                                                   uint8_t* raw = nullptr) {
   const uint32_t j = threadIdx.x & 63, chunks = n / 8;
   x[0] = x[1] = kAnsL;
   cnt[0] = cnt[1] = 0;
@@ -152,6 +154,10 @@ __device__ __forceinline__ void ans_encode_streams(const SegCtx& s, uint32_t n, 
   for (; c >= 0; c -= kAnsStreams) {
     const uint32_t a[4] = {nw.x, nw.y, nw.z, nw.w};
     if (c >= (int)kAnsStreams) nw = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, (uint32_t)c - kAnsStreams, D)));
+    if constexpr (RAW >= 0) {
+      constexpr uint32_t sel = RAW ? 0x07050301u : 0x06040200u;  // byte RAW of the 8 values, in order
+      st_global8(raw + 8 * c, make_uint2(__builtin_amdgcn_perm(a[1], a[0], sel), __builtin_amdgcn_perm(a[3], a[2], sel)));
+    }
     AnsEnc e0[8], e1[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) {
@@ -165,6 +171,26 @@ __device__ __forceinline__ void ans_encode_streams(const SegCtx& s, uint32_t n, 
       if constexpr (U1) ans_put<EMIT>(x[1], e1[e], cnt[1], out, end[1], lim[1]);
     }
   }
+}
+
+// True when a plane's coded body (32-byte bitmap, 2K bytes of frequencies,
+// 128 of stream lengths, the 64 streams: 4 state bytes each plus B_j
+// renormalisation bytes) cannot be below n bytes, so the plane is stored raw
+// without a sizing pass.  A coding step from a state x in [2^23, 2^31) that
+// emits b bytes gives a state above x 2^(-8b) (4096 / f) (1 - 2^-11)^2
+// (floor(x / f) > x / f - 1 with x 2^(-8b) >= 2^11 f, and the same for the
+// shift), so over a stream from 2^23 to a final state below 2^31,
+// 8 B_j > (bits of its symbols) - 8 - 0.00141 m_j, and over the plane
+// 8 sum B_j > H - 512 - 0.00141 n with H = sum of count(s) log2(4096 / f(s)).
+// H is evaluated in binary32 to well within the 2^-10 relative margin taken.
+__device__ __forceinline__ bool ans_raw_certain(const uint32_t (&c)[4], const uint32_t (&f)[4], uint32_t k,
+                                                uint32_t n) {
+  float h = 0.0f;
+  for (int r = 0; r < 4; r++)
+    if (f[r]) h += (float)c[r] * (12.0f - log2f((float)f[r]));
+  for (int m = 32; m >= 1; m >>= 1) h += __shfl_xor(h, m, 64);
+  const float bits = h * (1.0f - 1.0f / 1024.0f) - 512.0f - 0.002f * (float)n;
+  return 416.0f + 2.0f * (float)k + bits / 8.0f >= (float)n + 1.0f;
 }
 
 template <int D, bool CRC>
@@ -238,19 +264,22 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
   uint32_t f[2][4], cum[2][4], k[2];
   for (int pl = 0; pl < 2; pl++) {
     k[pl] = ans_model(cnts[pl], n, f[pl], cum[pl]);
-    for (int r = 0; r < 4; r++) s_enc[256 * pl + 4 * lane + r] = ans_enc_entry(f[pl][r], cum[pl][r]);
+    for (int r = 0; r < 4; r++) s_enc[256 * pl + 4 * lane + r] = ans_enc_entry(f[pl][r], cum[pl][r], p.tables->ans_rcp);
   }
   __syncthreads();
-  // pass 1: the stream lengths
+  // pass 1: the stream lengths of the planes that may code below raw size
+  const bool sure_raw[2] = {ans_raw_certain(cnts[0], f[0], k[0], n), ans_raw_certain(cnts[1], f[1], k[1], n)};
   const uint32_t zero2[2] = {0, 0};
-  uint32_t x[2], cnt[2];
-  ans_encode_streams<D, false, true, true>(s, n, s_enc, x, cnt, nullptr, zero2, zero2);
+  uint32_t x[2] = {kAnsL, kAnsL}, cnt[2] = {0, 0};
+  if (!sure_raw[0] && !sure_raw[1]) ans_encode_streams<D, false, true, true>(s, n, s_enc, x, cnt, nullptr, zero2, zero2);
+  else if (!sure_raw[0]) ans_encode_streams<D, false, true, false>(s, n, s_enc, x, cnt, nullptr, zero2, zero2);
+  else if (!sure_raw[1]) ans_encode_streams<D, false, false, true>(s, n, s_enc, x, cnt, nullptr, zero2, zero2);
   uint32_t len[2], body[2], psize[2];
   bool coded[2];
   for (int pl = 0; pl < 2; pl++) {
     len[pl] = 4 + cnt[pl];
     body[pl] = 32 + 2 * k[pl] + 2 * kAnsStreams + wave_sum(len[pl]);
-    coded[pl] = body[pl] < n;
+    coded[pl] = !sure_raw[pl] && body[pl] < n;
     psize[pl] = (16 + (coded[pl] ? body[pl] : n) + 15) & ~15u;
   }
   const uint32_t payload = psize[0] + psize[1];
@@ -270,30 +299,33 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
     return;
   }
   if (!keep) {                                                   // incompressible: raw bytes in the spill
-    for (uint32_t c = lane; c < chunks; c += kAnsStreams)
-      st_global16(heap + 16 * c, ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, c, D))));
+    for (uint32_t c0 = lane; c0 < chunks; c0 += 4 * kAnsStreams) {
+      uint4 w[4];
+#pragma unroll
+      for (uint32_t u = 0; u < 4; u++)
+        if (c0 + u * kAnsStreams < chunks) w[u] = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, c0 + u * kAnsStreams, D)));
+#pragma unroll
+      for (uint32_t u = 0; u < 4; u++)
+        if (c0 + u * kAnsStreams < chunks) st_global16(heap + 16 * (c0 + u * kAnsStreams), w[u]);
+    }
     const uint32_t cr = CRC ? crc32_written(heap, raw_bytes, ct) : 0u;
     if (lane == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | crc_flag, KVC_SEG_RAW_DATA,
                         (int)p.dtype, comp, D, s.n_vec, raw_bytes, off, 0, cr);
     return;
   }
-  // pass 2, a plane at a time: a raw plane goes straight to the spill region,
-  // a coded plane is assembled in LDS and written out in 16-byte units
+  // pass 2, a coded plane at a time, assembled in LDS and written out in
+  // 16-byte units; a raw plane (at most one: two raw planes fail the keep
+  // rule) is written during the coded plane's pass.  16 + n is a multiple of
+  // 16, so a raw plane has no padding.
+  uint8_t* const P0 = heap;
+  uint8_t* const P1 = heap + psize[0];
+  const int rawpl = coded[0] ? (coded[1] ? -1 : 1) : 0;
+  if (rawpl >= 0 && lane == 0) st_global16(rawpl ? P1 : P0, make_uint4(0, 0, 0, 0));   // mode 0, K = 0
 #pragma unroll
   for (int pl = 0; pl < 2; pl++) {
-    uint8_t* const P = heap + (pl ? psize[0] : 0);
-    if (!coded[pl]) {                                            // raw plane: byte pl of every value
-      if (lane == 0) st_global16(P, make_uint4(0, 0, 0, 0));
-      for (uint32_t c = lane; c < chunks; c += kAnsStreams) {
-        const uint4 w = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, c, D)));
-        const uint32_t sel = pl ? 0x07050301u : 0x06040200u;    // bytes of the 8 values, in order
-        *reinterpret_cast<uint2*>(P + 16 + 8 * c) =
-            make_uint2(__builtin_amdgcn_perm(w.y, w.x, sel), __builtin_amdgcn_perm(w.w, w.z, sel));
-      }
-      for (uint32_t b = 16 + n + lane; b < psize[pl]; b += 64) P[b] = 0;
-      continue;
-    }
+    uint8_t* const P = pl ? P1 : P0;
+    if (!coded[pl]) continue;
     // header, bitmap, frequencies of the present symbols, stream lengths
     if (lane == 0) *reinterpret_cast<uint4*>(s_out) = make_uint4(1u | (k[pl] << 16), 0, 0, 0);
     uint32_t nib = 0, present = 0;
@@ -312,8 +344,13 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
     for (uint32_t b = 16 + body[pl] + lane; b < psize[pl]; b += 64) s_out[b] = 0;
     const uint32_t endv[2] = {st + len[pl], st + len[pl]};
     const uint32_t limv[2] = {len[pl] - 4, len[pl] - 4};
-    if (pl == 0) ans_encode_streams<D, true, true, false>(s, n, s_enc, x, cnt, s_out, endv, limv);
-    else ans_encode_streams<D, true, false, true>(s, n, s_enc, x, cnt, s_out, endv, limv);
+    if (pl == 0) {
+      if (rawpl == 1) ans_encode_streams<D, true, true, false, 1>(s, n, s_enc, x, cnt, s_out, endv, limv, P1 + 16);
+      else ans_encode_streams<D, true, true, false>(s, n, s_enc, x, cnt, s_out, endv, limv);
+    } else {
+      if (rawpl == 0) ans_encode_streams<D, true, false, true, 0>(s, n, s_enc, x, cnt, s_out, endv, limv, P0 + 16);
+      else ans_encode_streams<D, true, false, true>(s, n, s_enc, x, cnt, s_out, endv, limv);
+    }
     s_out[st] = (uint8_t)x[pl];                                  // final state, u32 little-endian
     s_out[st + 1] = (uint8_t)(x[pl] >> 8);
     s_out[st + 2] = (uint8_t)(x[pl] >> 16);
@@ -331,30 +368,43 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
   }
 }
 
-// slot -> symbol table of a coded plane (payload bytes P in global memory)
-// and its (f, cum) pairs; returns false if the plane's model is malformed.
-// Lane j fills slots [64 j, 64 j + 64), four to a word.
-__device__ __forceinline__ bool ans_load_model(const uint8_t* P, uint32_t k, AnsDec* tab, uint8_t* lut) {
+// Whether a coded plane's model (payload bytes P in global memory) is well
+// formed: the bitmap holds K symbols, each with a nonzero frequency, and the
+// frequencies sum to 4096.
+__device__ __forceinline__ bool ans_model_ok(const uint8_t* P, uint32_t k) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t bits = (P[16 + lane / 2] >> (4 * (lane & 1))) & 15u;   // symbols 4 lane .. 4 lane + 3
   const uint32_t present = __popc(bits);
   uint32_t pos = wave_excl_scan(present);
   const bool ok_k = wave_sum(present) == k;
+  uint32_t tot = 0;
+  bool ok = true;
+  for (int r = 0; r < 4; r++)
+    if ((bits >> r) & 1) {
+      const uint32_t fr = pos < k ? *reinterpret_cast<const uint16_t*>(P + 48 + 2 * pos++) : 0;
+      ok = ok && fr != 0;
+      tot += fr;
+    }
+  return __all(ok) && ok_k && wave_sum(tot) == kAnsM;
+}
+
+// slot -> symbol table of a well-formed coded plane and its (f, cum) pairs.
+// Lane j fills slots [64 j, 64 j + 64), four to a word.
+__device__ __forceinline__ void ans_build_tables(const uint8_t* P, uint32_t k, AnsDec* tab, uint8_t* lut) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t bits = (P[16 + lane / 2] >> (4 * (lane & 1))) & 15u;
+  uint32_t pos = wave_excl_scan((uint32_t)__popc(bits));
   uint32_t fr[4], tot = 0;
   for (int r = 0; r < 4; r++) {
     fr[r] = (bits >> r) & 1 && pos < k ? *reinterpret_cast<const uint16_t*>(P + 48 + 2 * pos++) : 0;
     tot += fr[r];
   }
-  bool ok = ok_k && wave_sum(tot) == kAnsM;
-  for (int r = 0; r < 4; r++) ok = ok && (((bits >> r) & 1) == (fr[r] != 0));
-  ok = __all(ok);
   uint32_t run = wave_excl_scan(tot);
   for (int r = 0; r < 4; r++) {
     tab[4 * lane + r] = AnsDec{(uint16_t)fr[r], (uint16_t)run};
     run += fr[r];
   }
   __syncthreads();
-  if (!ok) return false;
   // the symbol of slot 64 lane: the largest with cum <= 64 lane (it has f > 0,
   // since a later symbol with f = 0 would share its cum), then walk
   const uint32_t s0 = 64 * lane;
@@ -378,7 +428,6 @@ __device__ __forceinline__ bool ans_load_model(const uint8_t* P, uint32_t k, Ans
     *reinterpret_cast<uint32_t*>(lut + s0 + 4 * w) = word;
   }
   __syncthreads();
-  return true;
 }
 
 // 4 payload bytes at aligned offset a, or at the last aligned offset of the
@@ -386,14 +435,12 @@ __device__ __forceinline__ bool ans_load_model(const uint8_t* P, uint32_t k, Ans
 __device__ __forceinline__ uint32_t ans_word(const uint8_t* heap, uint32_t a, uint32_t span) {
   return ld_global4(heap + min(a, span - 4));
 }
-
-// the 16 payload bytes at block-aligned offset b, or the last block of the
-// checked span when b is past it (such bytes lie beyond every stream)
+// the 16 payload bytes at block-aligned offset b, likewise
 __device__ __forceinline__ uint4 ans_block(const uint8_t* heap, uint32_t b, uint32_t span) {
   return ld_global16(heap + min(b, span - 16));
 }
 
-// A lane's window on its stream of a coded plane: a ring of four 16-byte
+// A lane's window on its stream of the coded plane: a ring of four 16-byte
 // blocks in LDS; word w of lane j at ring[64 w + j] (a bank per lane).  The
 // block at payload offset b (a multiple of 16) occupies words (b / 4) mod 16
 // to + 3.
@@ -410,97 +457,88 @@ __device__ __forceinline__ uint32_t ans_ring_byte(const uint32_t* ring, uint32_t
   return reinterpret_cast<const uint8_t*>(ring)[4 * (64 * ((q >> 2) & (kAnsRingWords - 1)) + j) + (q & 3)];
 }
 
-// Decode lane j's streams (chunks j, j + 64, ...) of both planes and write
-// each chunk of 8 values; C0 / C1: the low / high plane is coded (else raw).
-// Returns true when a stream is malformed: a state outside [2^23, 2^31) at
-// its start, more bytes consumed than it holds, or an end other than exactly
-// its last byte in state 2^23.
+// Where the byte of the plane not being decoded comes from
+enum AnsOther { kOtherRaw = 0, kOtherZero = 1, kOtherPage = 2 };
+
+// Decode lane j's stream (chunks j, j + 64, ...) of coded plane CP and write
+// each chunk of 8 values; the other plane's byte comes from its raw bytes at
+// payload offset other + 16 (kOtherRaw), is zero (kOtherZero), or is the
+// byte already in the destination page (kOtherPage: written by this lane's
+// kOtherZero pass over the other plane).  Returns true when the stream is
+// malformed: a state outside [2^23, 2^31) at its start, more bytes consumed
+// than it holds, or an end other than exactly its last byte in state 2^23.
 //
-// A coded stream's bytes reach the lane through its ring: the ring holds
-// the blocks of pos and pos + 16 during a chunk (a chunk consumes at most 16
+// The stream's bytes reach the lane through its ring: the ring holds the
+// blocks of pos and pos + 16 during a chunk (a chunk consumes at most 16
 // bytes: two per value), and the block two ahead is loaded while a chunk is
-// decoded and stored into the ring before the next one.  Raw planes' bytes
-// are likewise loaded a chunk ahead.  A state x >= 2^23 leaves a decode step
-// at or above 2^11, so one byte brings it back above 2^23 from [2^15, 2^23)
-// and two from [2^11, 2^15).
-template <int D, bool C0, bool C1>
+// decoded and stored into the ring before the next one.  The other plane's
+// bytes are likewise loaded a chunk ahead.  A state x >= 2^23 leaves a
+// decode step at or above 2^11, so one byte brings it back above 2^23 from
+// [2^15, 2^23) and two from [2^11, 2^15).
+template <int D, int CP, int OTHER>
 __device__ __forceinline__ bool ans_decode_lanes(const SegCtx& s, uint16_t* page_p, const uint8_t* heap, uint32_t span,
-                                                 uint32_t chunks, const uint32_t (&pbase)[2], const uint32_t (&sbeg)[2],
-                                                 const uint32_t (&send)[2], const AnsDec (*tab)[256],
-                                                 const uint8_t (*lut)[kAnsM], uint32_t (*ring)[64 * kAnsRingWords]) {
-  constexpr bool C[2] = {C0, C1};
+                                                 uint32_t chunks, uint32_t other, uint32_t sbeg, uint32_t send,
+                                                 const AnsDec* tab, const uint8_t* lut, uint32_t* ring) {
   const uint32_t lane = threadIdx.x & 63;
-  uint32_t x[2] = {kAnsL, kAnsL}, pos[2] = {0, 0}, nb[2] = {0, 0};
-  uint4 pend[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-  uint2 rb[2] = {make_uint2(0, 0), make_uint2(0, 0)};
-  bool bad = false;
-#pragma unroll
-  for (int pl = 0; pl < 2; pl++) {
-    if constexpr (true) {
-      if (C[pl]) {
-        const uint32_t a = sbeg[pl] & ~3u;                       // final state, u32 little-endian
-        x[pl] = __builtin_amdgcn_alignbyte(ans_word(heap, a + 4, span), ans_word(heap, a, span), sbeg[pl] & 3);
-        bad |= x[pl] < kAnsL || x[pl] >= (kAnsL << 8);
-        pos[pl] = sbeg[pl] + 4;
-        const uint32_t b0 = pos[pl] & ~15u;
-        ans_ring_put(ring[pl], b0, ans_block(heap, b0, span));
-        ans_ring_put(ring[pl], b0 + 16, ans_block(heap, b0 + 16, span));
-        nb[pl] = b0 + 32;
-        pend[pl] = ans_block(heap, nb[pl], span);
-      } else if (lane < chunks) {
-        rb[pl] = ld_global8(heap + pbase[pl] + 16 + 8 * lane);
-      }
-    }
-  }
+  const uint32_t a = sbeg & ~3u;                                 // final state, u32 little-endian
+  uint32_t x = __builtin_amdgcn_alignbyte(ans_word(heap, a + 4, span), ans_word(heap, a, span), sbeg & 3);
+  bool bad = x < kAnsL || x >= (kAnsL << 8);
+  uint32_t pos = sbeg + 4;
+  const uint32_t b0 = pos & ~15u;
+  ans_ring_put(ring, b0, ans_block(heap, b0, span));
+  ans_ring_put(ring, b0 + 16, ans_block(heap, b0 + 16, span));
+  uint32_t nb = b0 + 32;
+  uint4 pend = ans_block(heap, nb, span);
+  uint2 rb = make_uint2(0, 0);
+  uint4 pg = make_uint4(0, 0, 0, 0);
+  if constexpr (OTHER == kOtherRaw)
+    if (lane < chunks) rb = ld_global8(heap + other + 16 + 8 * lane);
+  if constexpr (OTHER == kOtherPage)
+    if (lane < chunks) pg = ld_global16(byte_at(page_p, 2 * ans_chunk_off(s, lane, D)));
   for (uint32_t c = lane; c < chunks; c += kAnsStreams) {
-    uint2 r[2];
+    ans_ring_put(ring, nb, pend);
+    nb = (pos & ~15u) + 32;
+    pend = ans_block(heap, nb, span);
+    uint32_t ob[8];                                              // the other plane's bytes of this chunk
+    if constexpr (OTHER == kOtherRaw) {
+      const uint2 r = rb;
+      if (c + kAnsStreams < chunks) rb = ld_global8(heap + other + 16 + 8 * (c + kAnsStreams));
 #pragma unroll
-    for (int pl = 0; pl < 2; pl++) {
-      if (C[pl]) {
-        ans_ring_put(ring[pl], nb[pl], pend[pl]);
-        nb[pl] = (pos[pl] & ~15u) + 32;
-        pend[pl] = ans_block(heap, nb[pl], span);
-      } else {
-        r[pl] = rb[pl];
-        if (c + kAnsStreams < chunks) rb[pl] = ld_global8(heap + pbase[pl] + 16 + 8 * (c + kAnsStreams));
-      }
+      for (int e = 0; e < 8; e++) ob[e] = ((e < 4 ? r.x : r.y) >> (8 * (e & 3))) & 0xFFu;
+    } else if constexpr (OTHER == kOtherPage) {
+      const uint32_t w[4] = {pg.x, pg.y, pg.z, pg.w};
+      if (c + kAnsStreams < chunks) pg = ld_global16(byte_at(page_p, 2 * ans_chunk_off(s, c + kAnsStreams, D)));
+#pragma unroll
+      for (int e = 0; e < 8; e++) ob[e] = (w[e >> 1] >> (16 * (e & 1) + 8 * (1 - CP))) & 0xFFu;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) ob[e] = 0;
     }
     uint32_t o[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      uint32_t b[2];
-#pragma unroll
-      for (int pl = 0; pl < 2; pl++) {
-        if (!C[pl]) {
-          b[pl] = ((e < 4 ? r[pl].x : r[pl].y) >> (8 * (e & 3))) & 0xFFu;
-          continue;
-        }
-        const uint32_t q0 = ans_ring_byte(ring[pl], pos[pl]), q1 = ans_ring_byte(ring[pl], pos[pl] + 1);
-        const uint32_t sl = x[pl] & (kAnsM - 1), sy = lut[pl][sl];
-        const AnsDec t = tab[pl][sy];
-        b[pl] = sy;
-        x[pl] = __umul24(t.f, x[pl] >> kAnsProbBits) + sl - t.cum;
-        const uint32_t k = (uint32_t)(x[pl] < kAnsL) + (uint32_t)(x[pl] < (kAnsL >> 8));
-        const uint32_t in = k == 2 ? (q0 << 8) | q1 : (k == 1 ? q0 : 0u);
-        x[pl] = (x[pl] << (8 * k)) | in;
-        bad |= pos[pl] + k > send[pl];
-        pos[pl] += k;
-      }
-      o[e >> 1] |= (b[0] | (b[1] << 8)) << (16 * (e & 1));
+      const uint32_t q0 = ans_ring_byte(ring, pos), q1 = ans_ring_byte(ring, pos + 1);
+      const uint32_t sl = x & (kAnsM - 1), sy = lut[sl];
+      const AnsDec t = tab[sy];
+      x = __umul24(t.f, x >> kAnsProbBits) + sl - t.cum;
+      const uint32_t k = (uint32_t)(x < kAnsL) + (uint32_t)(x < (kAnsL >> 8));
+      const uint32_t in = k == 2 ? (q0 << 8) | q1 : (k == 1 ? q0 : 0u);
+      x = (x << (8 * k)) | in;
+      bad |= pos + k > send;
+      pos += k;
+      const uint32_t v = CP ? (sy << 8) | ob[e] : (ob[e] << 8) | sy;
+      o[e >> 1] |= v << (16 * (e & 1));
     }
     st_global16(byte_at(page_p, 2 * ans_chunk_off(s, c, D)), make_uint4(o[0], o[1], o[2], o[3]));
   }
-#pragma unroll
-  for (int pl = 0; pl < 2; pl++)
-    if (C[pl]) bad |= pos[pl] != send[pl] || x[pl] != kAnsL;
-  return bad;
+  return bad || pos != send || x != kAnsL;
 }
 
 template <int D, bool CRC>
 __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
-  __shared__ AnsDec s_tab[2][256];
-  __shared__ __attribute__((aligned(16))) uint8_t s_lut[2][kAnsM];
-  __shared__ uint32_t s_ring[2][64 * kAnsRingWords];
+  __shared__ AnsDec s_tab[256];
+  __shared__ __attribute__((aligned(16))) uint8_t s_lut[kAnsM];
+  __shared__ uint32_t s_ring[64 * kAnsRingWords];
   __shared__ uint32_t s_crc_ok;
   CrcTables* const ct = crc_tables_lds<CRC>();
   const uint32_t seg = p.seg_base + blockIdx.x;
@@ -565,7 +603,7 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
     if (report) p.seg_status[seg] = 0;
     return;
   }
-  // parse both planes' headers and models
+  // parse both planes' headers, check their models, lengths and padding
   uint32_t pbase[2], mode[2], kk[2], sbeg[2] = {0, 0}, send[2] = {0, 0};
   uint32_t at = 0;
   bool good = true;
@@ -593,7 +631,7 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
       send[pl] = st0 + len;
       good = __all(len >= 4) && wave_max(st0 + len) <= stored;
       size = 48 + 2 * kk[pl] + 2 * kAnsStreams + wave_sum(len);
-      if (good) good = ans_load_model(P, kk[pl], s_tab[pl], s_lut[pl]);
+      if (good) good = ans_model_ok(P, kk[pl]);
     }
     const uint32_t padded = (size + 15) & ~15u;
     good = good && at + padded <= stored;
@@ -605,11 +643,29 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
     if (report) p.seg_status[seg] = 1;
     return;
   }
-  bool bad;
-  if (mode[0]) bad = mode[1] ? ans_decode_lanes<D, true, true>(s, page_p, heap, (uint32_t)span, chunks, pbase, sbeg, send, s_tab, s_lut, s_ring)
-                             : ans_decode_lanes<D, true, false>(s, page_p, heap, (uint32_t)span, chunks, pbase, sbeg, send, s_tab, s_lut, s_ring);
-  else bad = mode[1] ? ans_decode_lanes<D, false, true>(s, page_p, heap, (uint32_t)span, chunks, pbase, sbeg, send, s_tab, s_lut, s_ring)
-                     : ans_decode_lanes<D, false, false>(s, page_p, heap, (uint32_t)span, chunks, pbase, sbeg, send, s_tab, s_lut, s_ring);
+  // one coded plane at a time: its tables and ring in LDS
+  const uint32_t span32 = (uint32_t)span;
+  bool bad = false;
+  if (mode[0] && mode[1]) {                                      // low plane first, then the high merged in
+    ans_build_tables(heap + pbase[0], kk[0], s_tab, s_lut);
+    bad = ans_decode_lanes<D, 0, kOtherZero>(s, page_p, heap, span32, chunks, 0, sbeg[0], send[0], s_tab, s_lut, s_ring);
+    __syncthreads();
+    ans_build_tables(heap + pbase[1], kk[1], s_tab, s_lut);
+    bad |= ans_decode_lanes<D, 1, kOtherPage>(s, page_p, heap, span32, chunks, 0, sbeg[1], send[1], s_tab, s_lut, s_ring);
+  } else if (mode[0]) {
+    ans_build_tables(heap + pbase[0], kk[0], s_tab, s_lut);
+    bad = ans_decode_lanes<D, 0, kOtherRaw>(s, page_p, heap, span32, chunks, pbase[1], sbeg[0], send[0], s_tab, s_lut, s_ring);
+  } else if (mode[1]) {
+    ans_build_tables(heap + pbase[1], kk[1], s_tab, s_lut);
+    bad = ans_decode_lanes<D, 1, kOtherRaw>(s, page_p, heap, span32, chunks, pbase[0], sbeg[1], send[1], s_tab, s_lut, s_ring);
+  } else {                                                       // two raw planes
+    for (uint32_t c = lane; c < chunks; c += kAnsStreams) {
+      const uint2 lo = ld_global8(heap + pbase[0] + 16 + 8 * c), hi = ld_global8(heap + pbase[1] + 16 + 8 * c);
+      const uint4 o = make_uint4(__builtin_amdgcn_perm(hi.x, lo.x, 0x05010400u), __builtin_amdgcn_perm(hi.x, lo.x, 0x07030602u),
+                                 __builtin_amdgcn_perm(hi.y, lo.y, 0x05010400u), __builtin_amdgcn_perm(hi.y, lo.y, 0x07030602u));
+      st_global16(byte_at(page_p, 2 * ans_chunk_off(s, c, D)), o);
+    }
+  }
   bad = __any(bad);
   if (report) p.seg_status[seg] = bad ? 1 : 0;
 }

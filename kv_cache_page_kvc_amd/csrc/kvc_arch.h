@@ -28,6 +28,11 @@ __device__ __forceinline__ uint2 ld_global8(const void* p) {
   const u32x2 v = *(const __attribute__((address_space(1))) u32x2*)p;
   return make_uint2(v.x, v.y);
 }
+__device__ __forceinline__ void st_global8(void* p, uint2 v) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 w = {v.x, v.y};
+  *(__attribute__((address_space(1))) u32x2*)p = w;
+}
 __device__ __forceinline__ void st_global16(void* p, uint4 v) {
   u32x4 w = {v.x, v.y, v.z, v.w};
   *(g_u32x4*)p = w;

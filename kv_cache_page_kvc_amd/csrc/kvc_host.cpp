@@ -171,6 +171,13 @@ void build_crc_tables(CrcTables& c) {
 
 void build_tables(Tables& t) {
   build_crc_tables(t.crc);
+  std::memset(t.ans_rcp, 0, sizeof(t.ans_rcp));
+  t.ans_rcp[1] = 0xFFFFFFFFu;
+  for (uint32_t f = 2; f <= 4096; f++) {
+    uint32_t l = 0;
+    while ((1u << l) < f) l++;
+    t.ans_rcp[f] = (uint32_t)((((uint64_t)1 << (31 + l)) + f - 1) / f);
+  }
   for (int which = 0; which < 2; which++) {
     const int bits = which ? 4 : 3, n = 1 << bits;
     std::vector<double> lev;

@@ -65,11 +65,18 @@ struct CrcTables {
 };
 static_assert(sizeof(CrcTables) % 16 == 0, "CRC tables are copied in 16-byte units");
 
+// Reciprocals of the rANS encoder (KVC_ANS16), indexed by the frequency f in
+// [1, 4096]: ceil(2^(31+l) / f) with l = ceil(log2 f) for f >= 2, so that
+// floor(x / f) = (x * rcp) >> (31 + l) for every x < 2^31 (Granlund and
+// Montgomery, PLDI 1994, Thm 4.2); 2^32 - 1 for f = 1.
+constexpr uint32_t kAnsRcpEntries = 4100;
+
 // Per-ctx constant tables (device, in the arena).
 struct Tables {
   CellEntry cells[2][kCells];                 // [0]: 3-bit, [1]: 4-bit
   float centroids[2][16];
   alignas(16) CrcTables crc;
+  uint32_t ans_rcp[kAnsRcpEntries];
 };
 
 // Per-(layer, component) entry of a call (device, in the arena), indexed by

@@ -616,6 +616,18 @@ static size_t ans_rans_body(const uint8_t *sym, size_t n, uint8_t *out, uint32_t
   return (size_t)(dst - out);
 }
 
+/* Size of the rANS body (bitmap, frequencies, stream lengths, streams) of n
+ * symbols, n <= 16384, whether or not it is shorter than n. */
+size_t kvo_ans_coded_body(const uint8_t *sym, size_t n) {
+  if (n > 16384) return 0;
+  uint8_t *buf = (uint8_t *)malloc(1024 + 2 * n);
+  if (!buf) return 0;
+  uint32_t k = 0;
+  const size_t body = ans_rans_body(sym, n, buf, &k);
+  free(buf);
+  return body;
+}
+
 /* Encode n symbols (n <= 2^20); returns the serialised size, a multiple of
  * 16 (out must hold 16 + 32 + 512 + 128 + 4 * 64 + 2 * n + 15 bytes: a
  * symbol emits at most two bytes). */

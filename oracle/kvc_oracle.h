@@ -67,6 +67,8 @@ void   kvo_ans_normalize(const uint32_t *count, uint32_t n, uint16_t *freq);
  * bytes when that is shorter; returns the serialised size (a multiple of
  * 16).  out: at least 1024 + 2n bytes. */
 size_t kvo_ans_encode_plane(const uint8_t *sym, size_t n, uint8_t *out);
+/* Size of the rANS body of n <= 16384 symbols (0 beyond), coded or not. */
+size_t kvo_ans_coded_body(const uint8_t *sym, size_t n);
 /* Inverse; returns the bytes consumed, 0 on any inconsistency (bad table,
  * stream overrun, a stream not ending exactly at its length in the initial
  * state). */

@@ -102,6 +102,8 @@ def lib():
         L.kvo_ans_normalize.argtypes = [P, ctypes.c_uint32, P]
         L.kvo_ans_encode_plane.restype = ctypes.c_size_t
         L.kvo_ans_encode_plane.argtypes = [P, ctypes.c_size_t, P]
+        L.kvo_ans_coded_body.restype = ctypes.c_size_t
+        L.kvo_ans_coded_body.argtypes = [P, ctypes.c_size_t]
         L.kvo_ans_decode_plane.restype = ctypes.c_size_t
         L.kvo_ans_decode_plane.argtypes = [P, ctypes.c_size_t, ctypes.c_size_t, P]
         L.kvo_crc32.restype = ctypes.c_uint32
@@ -428,6 +430,12 @@ def ans_encode_plane(sym) -> np.ndarray:
     out = np.zeros(1024 + 2 * sym.size, np.uint8)
     n = lib().kvo_ans_encode_plane(_ptr(sym), sym.size, _ptr(out))
     return out[:n].copy()
+
+
+def ans_coded_body(sym) -> int:
+    """Bytes of the rANS body of a plane (bitmap on), coded or not."""
+    sym = np.ascontiguousarray(sym, dtype=np.uint8)
+    return int(lib().kvo_ans_coded_body(_ptr(sym), sym.size))
 
 
 def ans_decode_plane(data, n):

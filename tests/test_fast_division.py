@@ -71,10 +71,12 @@ def test_scaled_division_gives_identical_codes(scaled, codec, src):
 
 
 def test_rans_reciprocal_division_exact():
-    """The rANS encoder's floor(x / f) through a 32-bit reciprocal, for every
+    """The rANS encoder's state update x + bias + q * (4096 - f), q = floor(x
+    / f) through a 32-bit reciprocal (f = 1 through 2^32 - 1 and a bias of
+    cum + 4095), equals floor(x / f) * 4096 + x mod f + cum for every
     frequency f of a 12-bit model (checked over small x, the top of the
-    encoder's state range and random x; exact for all x < 2^31 by
-    Granlund-Montgomery)."""
+    encoder's state range and random x; the division is exact for all
+    x < 2^31 by Granlund-Montgomery)."""
     gcc = shutil.which("gcc")
     if gcc is None:
         pytest.skip("gcc not available")

@@ -838,6 +838,32 @@ def test_ans_size_tracks_model_entropy(oracle, kind):
     assert bits / 8 - 4 * 64 <= renorm <= bits / 8 * (1 + 1e-5) + 64
 
 
+def test_ans_coded_size_lower_bound(oracle):
+    """A coding step from a state in [2^23, 2^31) that emits b bytes leaves a
+    state above x 2^(-8b) (4096 / f) (1 - 2^-11)^2, so a plane's 64 streams
+    emit more than (H - 512 - 0.00141 n) / 8 renormalisation bytes, H the
+    sum of log2(4096 / f(s)) over its symbols; its body is then at least
+    416 + 2K + that.  The encoder skips the sizing pass of a plane whose
+    bound reaches n.  Checked against the coded size on planes from uniform
+    to skewed, including the low bytes of BF16 Gaussian data, which the
+    bound declares raw."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(16384).astype(np.float32)
+    bf_lo = (_bits(x, oracle.BF16) & 0xFF).astype(np.uint8)
+    planes = [_plane(k, n, rng) for k in ("uniform", "geometric", "two") for n in (2048, 8192, 16384)]
+    planes += [bf_lo, (_bits(x, oracle.FP16) & 0xFF).astype(np.uint8), rng.integers(0, 200, 16384).astype(np.uint8)]
+    for sym in planes:
+        n = sym.size
+        f = oracle.ans_normalize(np.bincount(sym, minlength=256)).astype(np.float64)
+        k = int((f > 0).sum())
+        h = np.log2(4096.0 / f[sym]).sum()
+        body = oracle.ans_coded_body(sym)
+        assert body >= 416 + 2 * k + (h - 512 - 0.00141 * n) / 8
+    f = oracle.ans_normalize(np.bincount(bf_lo, minlength=256)).astype(np.float64)
+    h = np.log2(4096.0 / f[bf_lo]).sum()
+    assert 416 + 2 * int((f > 0).sum()) + (h * (1 - 2.0 ** -10) - 512 - 0.002 * 16384) / 8 >= 16384 + 1
+
+
 def test_ans_exact_length_check(oracle):
     """A stream that ends early, runs long, or is corrupted is rejected, as is
     a frequency table that does not sum to 4096: the decoder must consume
