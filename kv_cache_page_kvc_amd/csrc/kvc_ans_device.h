@@ -361,8 +361,9 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
     __syncthreads();                                             // the image is rebuilt for the next plane
   }
   const uint32_t cr = CRC ? crc32_written(heap, payload, ct) : 0u;
+  // no fence before the header: nothing reads the payload during this
+  // launch, and its completion makes every write visible to later work
   if (lane == 0) {
-    __threadfence();                                             // payload before the header that points at it
     write_header_desc(s.slot, desc, slot_off, C_ANS, KVC_FLAG_HEAP | crc_flag, KVC_SEG_ENCODED, (int)p.dtype,
                       comp, D, s.n_vec, payload, off, 0, cr);
   }
@@ -443,7 +444,8 @@ __device__ __forceinline__ uint4 ans_block(const uint8_t* heap, uint32_t b, uint
 // A lane's window on its stream of the coded plane: a ring of four 16-byte
 // blocks in LDS; word w of lane j at ring[64 w + j] (a bank per lane).  The
 // block at payload offset b (a multiple of 16) occupies words (b / 4) mod 16
-// to + 3.
+// to + 3; word 16 repeats word 0, so that the word after any word w < 16 is
+// ring[64 (w + 1) + j].
 constexpr uint32_t kAnsRingWords = 16;
 __device__ __forceinline__ void ans_ring_put(uint32_t* ring, uint32_t b, uint4 v) {
   const uint32_t j = threadIdx.x & 63, w = (b >> 2) & (kAnsRingWords - 1);
@@ -451,10 +453,12 @@ __device__ __forceinline__ void ans_ring_put(uint32_t* ring, uint32_t b, uint4 v
   ring[64 * (w + 1) + j] = v.y;
   ring[64 * (w + 2) + j] = v.z;
   ring[64 * (w + 3) + j] = v.w;
+  if (w == 0) ring[64 * kAnsRingWords + j] = v.x;
 }
-__device__ __forceinline__ uint32_t ans_ring_byte(const uint32_t* ring, uint32_t q) {
-  const uint32_t j = threadIdx.x & 63;
-  return reinterpret_cast<const uint8_t*>(ring)[4 * (64 * ((q >> 2) & (kAnsRingWords - 1)) + j) + (q & 3)];
+// the 4 stream bytes from payload offset q, the first in the low byte
+__device__ __forceinline__ uint32_t ans_ring_bytes(const uint32_t* ring, uint32_t q) {
+  const uint32_t* const r = ring + 64 * ((q >> 2) & (kAnsRingWords - 1)) + (threadIdx.x & 63);
+  return __builtin_amdgcn_alignbyte(r[64], r[0], q & 3);
 }
 
 // Where the byte of the plane not being decoded comes from
@@ -517,12 +521,12 @@ __device__ __forceinline__ bool ans_decode_lanes(const SegCtx& s, uint16_t* page
     uint32_t o[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      const uint32_t q0 = ans_ring_byte(ring, pos), q1 = ans_ring_byte(ring, pos + 1);
+      const uint32_t q = ans_ring_bytes(ring, pos);             // the next stream bytes b0, b1 in bits 0..15
       const uint32_t sl = x & (kAnsM - 1), sy = lut[sl];
       const AnsDec t = tab[sy];
       x = __umul24(t.f, x >> kAnsProbBits) + sl - t.cum;
       const uint32_t k = (uint32_t)(x < kAnsL) + (uint32_t)(x < (kAnsL >> 8));
-      const uint32_t in = k == 2 ? (q0 << 8) | q1 : (k == 1 ? q0 : 0u);
+      const uint32_t in = k == 2 ? __builtin_amdgcn_perm(0u, q, 0x0C0C0001u) : (k == 1 ? q & 0xFFu : 0u);   // b0 b1 / b0
       x = (x << (8 * k)) | in;
       bad |= pos + k > send;
       pos += k;
@@ -538,7 +542,7 @@ template <int D, bool CRC>
 __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   __shared__ AnsDec s_tab[256];
   __shared__ __attribute__((aligned(16))) uint8_t s_lut[kAnsM];
-  __shared__ uint32_t s_ring[64 * kAnsRingWords];
+  __shared__ uint32_t s_ring[64 * (kAnsRingWords + 1)];
   __shared__ uint32_t s_crc_ok;
   CrcTables* const ct = crc_tables_lds<CRC>();
   const uint32_t seg = p.seg_base + blockIdx.x;
