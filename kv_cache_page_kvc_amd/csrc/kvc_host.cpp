@@ -509,13 +509,16 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   return KVC_OK;
 }
 
-// Encode / decode launches of a call: the fixed-size codecs' kernel, then,
-// when some component uses KVC_ANS16, the entropy stage's kernel over the
-// same segments (each skips the other's segments).  The entropy encode
-// assembles one coded byte plane at a time in LDS: at most n + 16 bytes for
-// n values per segment.
+// Encode / decode launches of a call: the fixed-size codecs' kernel (not
+// when every segment is KVC_ANS16), then, when some component uses
+// KVC_ANS16, the entropy stage's kernel over the same segments (each skips
+// the other's segments).  The entropy encode assembles one coded byte plane
+// at a time in LDS: at most n + 16 bytes for n values per segment.
+bool all_ans(const kvc_layout* L, const Plan& plan, const CallParams& P) {
+  return plan.ans == 2ull * L->layers * P.n_pages;
+}
 hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
-  hipError_t e = launch_encode(P, L->head_dim, nseg, s);
+  hipError_t e = all_ans(L, plan, P) ? hipSuccess : launch_encode(P, L->head_dim, nseg, s);
   if (e == hipSuccess && plan.ans) {
     CallParams A = P;
     A.stage_bytes = L->kv_heads * L->tokens_per_page * L->head_dim + 16;
@@ -524,7 +527,7 @@ hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan
   return e;
 }
 hipError_t run_decode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
-  hipError_t e = launch_decode(P, L->head_dim, nseg, s);
+  hipError_t e = all_ans(L, plan, P) ? hipSuccess : launch_decode(P, L->head_dim, nseg, s);
   if (e == hipSuccess && plan.ans) e = launch_ans_decode(P, L->head_dim, nseg, s);
   return e;
 }
