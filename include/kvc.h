@@ -254,7 +254,12 @@ kvc_status kvc_encode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_co
  * (KVC_SEG_CAPACITY), 2 when the kernel's range check on its staged
  * descriptor failed, or 3 when the stored bytes do not match the header's
  * CRC32 (KVC_CODEC_CRC32 only); in cases 1-3 the destination page is left
- * unchanged.  Enqueued on `stream`. */
+ * unchanged, with one exception: a KVC_ANS16 payload whose headers, model,
+ * stream lengths, padding and exact length all check out but one of whose
+ * streams does not decode to exactly its length in the initial state (or
+ * starts outside the state interval) reports 1 after its page has been
+ * written -- KVC_CODEC_CRC32 rejects such corrupted bytes before any write.
+ * Enqueued on `stream`. */
 kvc_status kvc_decode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
                             const void *in, size_t in_bytes,
                             const int32_t *dst_page_ids, uint32_t n_pages,
