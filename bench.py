@@ -115,6 +115,9 @@ WORKLOADS = {
     "tq4_u4_llama3": "TurboQuant-4 K + uniform-4 V, Llama-3-8B shape: 32 layers, 8 KV heads, D=128, BF16, "
                      "separate K/V, 16-token pages, 4096 random pages of an 8192-block pool (64K tokens), "
                      "layers 0,1,30,31 raw",
+    "tq4_u4_llama3_tp8": "one 8-way tensor-parallel shard of the TurboQuant-4 K + uniform-4 V Llama-3-8B workload: "
+                         "32 layers, 1 KV head, D=128, BF16, separate K/V, 16-token pages (4 KiB segments), "
+                         "4096 random pages of an 8192-block pool, layers 0,1,30,31 raw",
     "fp8_dynamic_small": "FP8 E4M3FN dynamic per-token/head K and V: 2 layers, 8 KV heads, D=128, BF16, "
                          "separate K/V, 64 pages of 16 tokens",
     "k16v8_packed": "K raw, V FP8 ({vcodec}), Qwen3-8B shape: 36 layers, 8 KV heads, D=128, FP16, vLLM packed "

@@ -581,9 +581,10 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   const uint64_t spill = (uint64_t)h1.x | ((uint64_t)h1.y << 32);
   const uint32_t stored = h0.w;
   if (raw_data) ok = ok && format == KVC_RAW && !(flags & KVC_FLAG_CAPACITY) && stored == raw_bytes;
-  else ok = ok && format == C_ANS && (flags & KVC_FLAG_HEAP) && stored >= 32 && stored <= raw_bytes;
+  else ok = ok && format == C_ANS && (flags & KVC_FLAG_HEAP) && stored >= 32 && stored <= (1u << 30);
   // every read stays in the buffer: the stored bytes rounded up to 16, from
-  // a 16-byte aligned offset
+  // a 16-byte aligned offset (payload offsets are 32-bit: stored <= 2^30 is
+  // far above any payload of a segment of at most 32 KiB)
   const uint64_t span = ((uint64_t)stored + 15) & ~15ull;
   ok = ok && (spill & 15) == 0 && spill >= p.slot_region && span <= p.buf_bytes && spill <= p.buf_bytes - span;
   if (!ok) {

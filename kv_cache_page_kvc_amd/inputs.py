@@ -135,6 +135,11 @@ CONFIGS = {
     # tokens, about the 54,254 BF16 tokens an 8 GB host budget holds
     "int8_records_qwen3": dict(layers=36, heads=8, dim=128, dtype="bf16", layout="separate", tokens=16,
                                pool=4096, pages=3392, k="INT8_ROWS", v="INT8_ROWS", random_pages=True),
+    # one tensor-parallel shard (8-way) of tq4_u4_llama3: one KV head per GPU,
+    # 4 KiB segments
+    "tq4_u4_llama3_tp8": dict(layers=32, heads=1, dim=128, dtype="bf16", layout="separate", tokens=16,
+                              pool=8192, pages=4096, k="TQ4", v="UNIFORM4", protected=(0, 1, 30, 31),
+                              random_pages=True),
     # the lossless entropy stage on the Llama-3-8B shape
     "ans16_llama3": dict(layers=32, heads=8, dim=128, dtype="bf16", layout="separate", tokens=16,
                          pool=8192, pages=4096, k="ANS16", v="ANS16", random_pages=True),

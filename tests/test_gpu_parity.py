@@ -342,6 +342,20 @@ def test_tq4_u4_llama3_full_size(ctx):
                     decode_from_oracle=False)
 
 
+def test_tq4_u4_llama3_tp8_full_size(ctx):
+    """One 8-way tensor-parallel shard of the TurboQuant-4 / uniform-4
+    workload: 1 KV head, 4 KiB segments (one-wave workgroups), 4096 of 8192
+    blocks, protected layers 0, 1, 30, 31; full-size launch, sampled
+    segments."""
+    cfg = inputs.CONFIGS["tq4_u4_llama3_tp8"]
+    print("[case] tq4_u4_llama3 tp8 shard full size", flush=True)
+    wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
+    ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
+    segs = _sample_segments(cfg["layers"], cfg["pages"], 96, 4, layers=[0, 31])
+    _roundtrip_case(ctx, wl, "TQ4", "UNIFORM4", 0, ids, protected=list(cfg["protected"]), segments=segs,
+                    decode_from_oracle=False)
+
+
 @pytest.mark.parametrize("dim", [32, 64, 256])
 def test_tq3_u3_dsweep_full_size(ctx, dim):
     """TurboQuant-3 K (outlier channels) + uniform-3 V, 28 layers x 4 heads,
@@ -441,6 +455,45 @@ def test_ans16_plane_modes(ctx, crc):
     for sidx, (l, i, c) in enumerate(seglist):
         want = O.SEG_RAW_DATA if (l, c) == (1, 1) else O.SEG_ENCODED
         assert int(ora_st[sidx]) == want, f"segment {sidx}: status {ora_st[sidx]}"
+
+
+def test_ans16_two_raw_planes_payload(ctx):
+    """A payload whose two byte planes are both stored raw (mode 0, 2n + 32
+    bytes) is valid for the format though the encoder never writes one (its
+    keep rule stores such a segment as raw data): written by hand over a
+    GPU-encoded segment, it decodes on the GPU to the oracle's decode of the
+    same buffer, the source values; the other segments are unaffected."""
+    print("[case] ans16 two raw planes", flush=True)
+    wl = G.Workload(1, 8, 128, 16, 4, "bf16", "separate", seed=5)
+    ids = np.array([2, 0], np.int32)
+    kc = vc = kvc.CODECS["ANS16"]
+    codec = kvc.Codec(kc, vc, seed=0, layers=wl.L)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids)
+    torch.cuda.synchronize()
+    gdesc = G.desc_np(desc)
+    assert all(int(d["status"]) == O.SEG_ENCODED for d in gdesc)
+    buf = out.cpu().numpy()
+    src = G.gpu_segment_vectors(wl, 0, 0, int(ids[0])).reshape(-1)      # segment 0: layer 0, page ids[0], K
+    n = src.size
+    payload = np.zeros(2 * n + 32, np.uint8)
+    payload[16:16 + n] = (src & 0xFF).astype(np.uint8)
+    payload[32 + n:] = (src >> 8).astype(np.uint8)
+    at = (buf.size + 255) // 256 * 256
+    crafted = np.zeros(at + payload.size, np.uint8)
+    crafted[:buf.size] = buf
+    crafted[at:] = payload
+    so = int(gdesc[0]["offset"])
+    crafted[so + 12:so + 16] = np.array([payload.size], np.uint32).view(np.uint8)    # stored_len
+    crafted[so + 16:so + 24] = np.array([at], np.uint64).view(np.uint8)              # spill offset
+    ora = G.oracle_decode_segments(crafted, wl, kc, vc, 0, len(ids), None, [0, 1, 2, 3])
+    assert np.array_equal(ora[0].reshape(-1), src)
+    dst = wl.empty_like(fill_bits=0x7FC1)
+    st = G.gpu_decode(ctx, dst, codec, torch.from_numpy(crafted).cuda(), crafted.size, ids)
+    torch.cuda.synchronize()
+    assert st.cpu().numpy().tolist() == [0, 0, 0, 0]
+    for sidx, (l, i, c) in enumerate(G.segments_of(wl.L, len(ids))):
+        got = G.gpu_segment_vectors(dst, l, c, int(ids[i]))
+        assert np.array_equal(got, ora[sidx]), f"segment {sidx}"
 
 
 def test_k8v8_packed_full_size(ctx):
