@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_tq4_u4_llama3.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_page_kvc_amd", "csrc", f)
-                  for f in ("kvc_kernels.hip", "kvc_ans_device.h", "kvc_arch.h", "kvc_internal.h")]
+                  for f in ("kvc_kernels.hip", "kvc_arch.h", "kvc_internal.h")]
 
 
 def kernel_source_hash():
