@@ -690,6 +690,41 @@ def test_crc_spill_capacity(ctx):
     assert np.all(st[cap] == 1) and np.all(np.delete(st, cap) == 0)
 
 
+def test_ans16_spill_capacity(ctx):
+    """ANS16 payloads live in the spill region: sized for about ten of the
+    32 payloads, the segments that found room hold the oracle's payload bytes
+    and decode losslessly; the others report KVC_SEG_CAPACITY, are not
+    stored, decode with status 1 and leave their pages untouched."""
+    print("[case] ans16 spill capacity", flush=True)
+    L, H, D, T, pool = 2, 8, 128, 16, 8
+    wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 14)
+    ids = np.arange(pool, dtype=np.int32)
+    codec = kvc.Codec(kvc.KVC_ANS16, kvc.KVC_ANS16, seed=0, layers=L)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids, spill_bytes=10 * 24 * 1024)
+    torch.cuda.synchronize()
+    d = G.desc_np(desc)
+    buf = out.cpu().numpy()
+    enc = np.nonzero(d["status"] == kvc.KVC_SEG_ENCODED)[0]
+    cap = np.nonzero(d["status"] == kvc.KVC_SEG_CAPACITY)[0]
+    assert len(enc) + len(cap) == L * pool * 2 and 8 <= len(enc) <= 10 and len(cap) > 0
+    seglist = G.segments_of(L, pool)
+    for sidx in enc:
+        l, i, c = seglist[sidx]
+        src = G.gpu_segment_vectors(wl, l, c, int(ids[i]))
+        _, ost, payload = O.encode_segment(src, wl.dt, kvc.KVC_ANS16, component=c, heads=H)
+        so, nb = int(d[sidx]["spill_offset"]), int(d[sidx]["stored_len"])
+        assert ost == O.SEG_ENCODED and nb == payload.size and slot <= so and so + nb <= total
+        assert np.array_equal(buf[so:so + nb], payload), f"segment {sidx}: payload differs"
+    dst = wl.empty_like(fill_bits=0x1234)
+    st = G.gpu_decode(ctx, dst, codec, out, total, ids).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.all(st[cap] == 1) and np.all(st[enc] == 0)
+    for sidx, (l, i, c) in enumerate(seglist):
+        got = G.gpu_segment_vectors(dst, l, c, int(ids[i]))
+        want = G.gpu_segment_vectors(wl, l, c, int(ids[i])) if sidx in enc else np.full_like(got, 0x1234)
+        assert np.array_equal(got, want), f"segment {sidx}"
+
+
 def test_tq4_u4_llama3_full_size_crc(ctx):
     """The TurboQuant-4 / uniform-4 Llama-3-8B workload with the CRC option:
     one full-size launch each way, sampled segments bit-exact (CRCs
