@@ -90,6 +90,8 @@ CASES = {
     "int8-fp8dyn-spill-crc": dict(ck="INT8", cv="FP8_DYNAMIC", inject=True, crc=True),
     "tq3-u3-d256-packed-fp16": dict(ck="TQ3", cv="UNIFORM3", D=256, H=4, layout="packed", dtype="fp16"),
     "int8rows-u4-crc": dict(ck="INT8_ROWS", cv="UNIFORM4", crc=True),
+    "ans16-fp8dyn-crc": dict(ck="ANS16", cv="FP8_DYNAMIC", crc=True),
+    "ans16-ans16-prot": dict(ck="ANS16", cv="ANS16", protected=[1]),
 }
 
 
