@@ -489,15 +489,13 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   // exact for every vector index v < 2^16 because heads <= 2^16 (v * heads < 2^32)
   P->heads_magic = ((1ull << 32) + L->kv_heads - 1) / L->kv_heads;
   {
-    const uint32_t seg_bytes = L->kv_heads * L->tokens_per_page * L->head_dim * 2;
-    P->threads = seg_bytes <= kSmallSegmentBytes ? kThreadsSmall : kThreads;
-    const uint32_t H = L->kv_heads, gw = (uint32_t)groups_per_workgroup((int)L->head_dim, (int)P->threads);
+    const uint32_t H = L->kv_heads;
     const uint32_t st = (uint32_t)L->stride_token, sh = (uint32_t)L->stride_head;   // < 2^31 (check_layout)
     P->st32 = st;
     P->sh32 = sh;
-    P->walk_dh = gw % H;
-    P->walk_step = (gw / H) * st + (gw % H) * sh;      // modulo 2^32
     P->walk_wrap = st - H * sh;                         // modulo 2^32
+    // the workgroup size and its walk constants are set per launch (with_threads)
+    P->threads = 0;
   }
   P->tokens = L->tokens_per_page;
   P->row_bytes = row_bytes(L->head_dim, L->kv_heads);
@@ -517,8 +515,26 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
 bool all_ans(const kvc_layout* L, const Plan& plan, const CallParams& P) {
   return plan.ans == 2ull * L->layers * P.n_pages;
 }
+// P for workgroups of nt threads: a lane walks from vector v to v + GW with
+// GW = groups_per_workgroup(D, nt): head + walk_dh (minus H on wrap), element
+// offset + walk_step (+ walk_wrap on wrap), all modulo 2^32
+CallParams with_threads(const CallParams& P, const kvc_layout* L, uint32_t nt) {
+  CallParams W = P;
+  const uint32_t H = L->kv_heads, gw = (uint32_t)groups_per_workgroup((int)L->head_dim, (int)nt);
+  W.threads = nt;
+  W.walk_dh = gw % H;
+  W.walk_step = (gw / H) * P.st32 + (gw % H) * P.sh32;
+  return W;
+}
+// one wave for small segments, else the direction's workgroup size
+uint32_t workgroup_threads(const kvc_layout* L, uint32_t big) {
+  const uint32_t seg_bytes = L->kv_heads * L->tokens_per_page * L->head_dim * 2;
+  return seg_bytes <= kSmallSegmentBytes ? (uint32_t)kThreadsSmall : big;
+}
 hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
-  hipError_t e = all_ans(L, plan, P) ? hipSuccess : launch_encode(P, L->head_dim, nseg, s);
+  hipError_t e = all_ans(L, plan, P) ? hipSuccess
+                                     : launch_encode(with_threads(P, L, workgroup_threads(L, kEncodeThreads)),
+                                                     L->head_dim, nseg, s);
   if (e == hipSuccess && plan.ans) {
     CallParams A = P;
     A.stage_bytes = L->kv_heads * L->tokens_per_page * L->head_dim + 16;
@@ -527,7 +543,9 @@ hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan
   return e;
 }
 hipError_t run_decode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
-  hipError_t e = all_ans(L, plan, P) ? hipSuccess : launch_decode(P, L->head_dim, nseg, s);
+  hipError_t e = all_ans(L, plan, P) ? hipSuccess
+                                     : launch_decode(with_threads(P, L, workgroup_threads(L, kDecodeThreads)),
+                                                     L->head_dim, nseg, s);
   if (e == hipSuccess && plan.ans) e = launch_ans_decode(P, L->head_dim, nseg, s);
   return e;
 }

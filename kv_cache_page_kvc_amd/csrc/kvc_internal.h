@@ -10,11 +10,14 @@
 
 namespace kvc {
 
-// One workgroup per segment: 256 threads, or one wave (64 threads) for
-// segments of at most kSmallSegmentBytes source bytes -- a small segment
-// would leave a 256-thread workgroup with little data in flight per wave,
-// while one-wave workgroups keep up to 32 segments in flight per CU.
-constexpr int kThreads = 256;
+// One workgroup per segment: one wave (64 threads) for segments of at most
+// kSmallSegmentBytes source bytes -- a small segment would leave a larger
+// workgroup with little data in flight per wave, while one-wave workgroups
+// keep up to 32 segments in flight per CU -- else kEncodeThreads for encode
+// (two waves: the compute-heavy TurboQuant encode keeps more vectors in
+// flight per wave) and kDecodeThreads for decode (four waves).
+constexpr int kEncodeThreads = 128;
+constexpr int kDecodeThreads = 256;
 constexpr int kThreadsSmall = 64;
 constexpr uint32_t kSmallSegmentBytes = 16384;
 
@@ -105,7 +108,7 @@ struct CallParams {
   uint64_t base_lo, base_hi;                  // range of every layer base pointer (guard)
   int64_t sb, st, sh;                         // element strides
   uint64_t heads_magic;                       // ceil(2^32 / heads): t = (v * magic) >> 32 = v / heads
-  uint32_t threads;                           // threads per workgroup: kThreads or kThreadsSmall
+  uint32_t threads;                           // threads per workgroup (see with_threads in the host)
   // Walking a lane from vector v to v + GW (GW = groups_per_workgroup(D, threads)):
   // head h -> h + walk_dh (minus heads on wrap), element offset within the
   // page -> + walk_step (+ walk_wrap on wrap); all modulo 2^32.  A page spans

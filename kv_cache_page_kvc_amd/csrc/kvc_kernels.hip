@@ -40,7 +40,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ geometry
-template <int D, int NT = kThreads>
+template <int D, int NT = kThreadsSmall>
 struct Geo {
   static constexpr int P = lanes_per_vector(D);               // lanes per vector
   static constexpr int LOGP = P == 2 ? 1 : (P == 4 ? 2 : (P == 8 ? 3 : 4));
@@ -1342,26 +1342,28 @@ struct DecodeLaunch {
     hipLaunchKernelGGL((decode_kernel<D, DT, NT, CRC>), dim3((unsigned)n), dim3(NT), dynamic_lds(p), st, p);
   }
 };
-// instantiation for the call's dtype, workgroup size and CRC option
-template <int D, template <int, int, int, bool> class F>
+// instantiation for the call's dtype, workgroup size (one wave, or BIG
+// threads) and CRC option; a launch with another size is refused
+template <int D, int BIG, template <int, int, int, bool> class F>
 hipError_t dispatch(const CallParams& p, uint64_t nseg, hipStream_t st) {
   const bool bf = p.dtype == KVC_BF16, small = p.threads == kThreadsSmall, crc = p.crc != 0;
+  if (!small && p.threads != (uint32_t)BIG) return hipErrorInvalidConfiguration;
   if (bf) {
     if (small) crc ? F<D, KVC_BF16, kThreadsSmall, true>::run(p, nseg, st) : F<D, KVC_BF16, kThreadsSmall, false>::run(p, nseg, st);
-    else crc ? F<D, KVC_BF16, kThreads, true>::run(p, nseg, st) : F<D, KVC_BF16, kThreads, false>::run(p, nseg, st);
+    else crc ? F<D, KVC_BF16, BIG, true>::run(p, nseg, st) : F<D, KVC_BF16, BIG, false>::run(p, nseg, st);
   } else {
     if (small) crc ? F<D, KVC_FP16, kThreadsSmall, true>::run(p, nseg, st) : F<D, KVC_FP16, kThreadsSmall, false>::run(p, nseg, st);
-    else crc ? F<D, KVC_FP16, kThreads, true>::run(p, nseg, st) : F<D, KVC_FP16, kThreads, false>::run(p, nseg, st);
+    else crc ? F<D, KVC_FP16, BIG, true>::run(p, nseg, st) : F<D, KVC_FP16, BIG, false>::run(p, nseg, st);
   }
   return hipGetLastError();
 }
 template <int D>
 hipError_t launch_encode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
-  return dispatch<D, EncodeLaunch>(p, nseg, st);
+  return dispatch<D, kEncodeThreads, EncodeLaunch>(p, nseg, st);
 }
 template <int D>
 hipError_t launch_decode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
-  return dispatch<D, DecodeLaunch>(p, nseg, st);
+  return dispatch<D, kDecodeThreads, DecodeLaunch>(p, nseg, st);
 }
 
 }  // namespace
