@@ -274,6 +274,8 @@ struct Plan {
   uint64_t per_page = 0;      // slot bytes of one page over all layers
   uint64_t encodable = 0;     // segments not raw by policy
   uint64_t ans = 0;           // of which KVC_ANS16 (payload in the spill region)
+  bool light = true;          // every component raw, FP8 direct, FP8 dynamic or ANS16 (no
+                              // per-element divide or TurboQuant/uniform arithmetic in encode)
 };
 
 Plan make_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages) {
@@ -293,6 +295,7 @@ Plan make_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages) {
       p.slot[comp][l] = (uint32_t)slot_size(e, L->head_dim, n_vec, L->kv_heads);
       if (e != KVC_RAW) p.encodable += n_pages;
       if (e == KVC_ANS16) p.ans += n_pages;
+      if (e != KVC_RAW && e != KVC_FP8_DIRECT && e != KVC_FP8_DYNAMIC && e != KVC_ANS16) p.light = false;
     }
     p.layer_off[l] = off;
     const uint64_t page = (uint64_t)p.slot[0][l] + p.slot[1][l];
@@ -531,10 +534,16 @@ uint32_t workgroup_threads(const kvc_layout* L, uint32_t big) {
   const uint32_t seg_bytes = L->kv_heads * L->tokens_per_page * L->head_dim * 2;
   return seg_bytes <= kSmallSegmentBytes ? (uint32_t)kThreadsSmall : big;
 }
+// Encode: a call whose components all encode with little arithmetic per
+// element (raw, FP8 direct, FP8 dynamic) runs one wave per segment at every
+// size when it has segments enough to keep 32 in flight on each of 256 CUs
+// -- more segments in flight per CU; the others run two waves above
+// kSmallSegmentBytes.
+constexpr uint64_t kLightOneWaveSegments = 32 * 256;
 hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
-  hipError_t e = all_ans(L, plan, P) ? hipSuccess
-                                     : launch_encode(with_threads(P, L, workgroup_threads(L, kEncodeThreads)),
-                                                     L->head_dim, nseg, s);
+  const uint32_t nt = plan.light && nseg >= kLightOneWaveSegments ? (uint32_t)kThreadsSmall
+                                                                   : workgroup_threads(L, kEncodeThreads);
+  hipError_t e = all_ans(L, plan, P) ? hipSuccess : launch_encode(with_threads(P, L, nt), L->head_dim, nseg, s);
   if (e == hipSuccess && plan.ans) {
     CallParams A = P;
     A.stage_bytes = L->kv_heads * L->tokens_per_page * L->head_dim + 16;

@@ -15,7 +15,8 @@ namespace kvc {
 // workgroup with little data in flight per wave, while one-wave workgroups
 // keep up to 32 segments in flight per CU -- else kEncodeThreads for encode
 // (two waves: the compute-heavy TurboQuant encode keeps more vectors in
-// flight per wave) and kDecodeThreads for decode (four waves).
+// flight per wave; a large call whose components all encode raw, FP8 direct
+// or FP8 dynamic keeps one wave) and kDecodeThreads for decode (four waves).
 constexpr int kEncodeThreads = 128;
 constexpr int kDecodeThreads = 256;
 constexpr int kThreadsSmall = 64;
