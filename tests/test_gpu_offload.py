@@ -116,13 +116,15 @@ def test_offload_then_restore(ctx, name):
     cs.check_decoded(dst, set(range(cs.wl.L)))
 
 
-def test_restore_layer_ranges_signal_each_layer(ctx):
+@pytest.mark.parametrize("pair", [("TQ4", "UNIFORM4"), ("ANS16", "ANS16")], ids=lambda p: f"{p[0]}-{p[1]}")
+def test_restore_layer_ranges_signal_each_layer(ctx, pair):
     """Three restores over [0,1), [1,3), [3,4) into shuffled destination pages,
     each layer with its own event: a consumer stream that waits on a layer's
     event reads that layer fully restored; layers not yet restored keep the
-    poison."""
-    print("[case] restore by layer ranges", flush=True)
-    cs = Case("TQ4", "UNIFORM4", L=4, n=11, seed=9, protected=[3])
+    poison.  (ANS16 payloads sit in the spill region, which every restore
+    copies before its first layer.)"""
+    print(f"[case] restore by layer ranges {pair}", flush=True)
+    cs = Case(pair[0], pair[1], L=4, n=11, seed=9, protected=[3])
     host = pinned(cs.total)
     hdesc = pinned(cs.nseg * 32)
     kvc.kvc_offload_pages(ctx, cs.wl.layout, cs.codec, cs.ids, host.data_ptr(), cs.total, hdesc.data_ptr())
@@ -156,11 +158,12 @@ def test_restore_layer_ranges_signal_each_layer(ctx):
     assert np.all(st.cpu().numpy() == 0)
 
 
-def test_decode_layers_device_buffer(ctx):
+@pytest.mark.parametrize("pair", [("INT8", "FP8_DIRECT"), ("ANS16", "INT8")], ids=lambda p: f"{p[0]}-{p[1]}")
+def test_decode_layers_device_buffer(ctx, pair):
     """kvc_decode_layers over a device buffer: only the requested layers are
     written, and their pages equal the oracle's decode."""
-    print("[case] decode_layers", flush=True)
-    cs = Case("INT8", "FP8_DIRECT", L=5, n=9, seed=21)
+    print(f"[case] decode_layers {pair}", flush=True)
+    cs = Case(pair[0], pair[1], L=5, n=9, seed=21)
     out, desc, slot, total = G.gpu_encode(ctx, cs.wl, cs.codec, cs.ids)
     torch.cuda.synchronize()
     cs.check_encoded(out.cpu().numpy(), G.desc_np(desc))
