@@ -329,6 +329,22 @@ def _sample_segments(L, n_pages, count, seed, layers=None):
     return sorted(segs)
 
 
+@pytest.mark.parametrize("heads,codec_pair,raw", [(32, ("TQ4", "FP8_DYNAMIC"), False), (40, ("INT8", "UNIFORM4"), True)],
+                         ids=["16MiB-coded", "20MiB-raw"])
+def test_segment_size_limit(ctx, heads, codec_pair, raw):
+    """Segments at the size limit: 1024 tokens x `heads` heads x D256 BF16 is
+    16 MiB at 32 heads -- still coded, each in one workgroup writing its
+    codes straight out (the slot exceeds the LDS staging limit) -- and 20 MiB
+    at 40 heads, above the 16 MiB cap: stored raw by policy.  Every segment
+    compared with the oracle, both directions."""
+    print(f"[case] segment size limit heads={heads} {codec_pair}", flush=True)
+    wl = G.Workload(1, heads, 256, 1024, 3, "bf16", "separate", seed=heads)
+    ids = np.array([2, 0], np.int32)
+    ora_st, gdesc = _roundtrip_case(ctx, wl, codec_pair[0], codec_pair[1], 5, ids, dst_ids=np.array([1, 2], np.int32))
+    want = O.SEG_RAW_POLICY if raw else O.SEG_ENCODED
+    assert all(int(v) == want for v in ora_st) and all(int(v) == want for v in gdesc["status"])
+
+
 def test_tq4_u4_llama3_full_size(ctx):
     """TurboQuant-4 K + uniform-4 V, 32 layers x 8 heads x D128 BF16, 4096 of
     8192 blocks in random order, protected layers 0, 1, 30, 31: one full-size
