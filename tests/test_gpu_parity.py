@@ -741,6 +741,24 @@ def test_ans16_spill_capacity(ctx):
         assert np.array_equal(got, want), f"segment {sidx}"
 
 
+@pytest.mark.parametrize("crc", [False, True])
+def test_fp8_large_call_one_wave_encode(ctx, crc):
+    """A call of raw/FP8-direct/FP8-dynamic components with at least 32 x 256
+    segments encodes one wave per 32 KiB segment: 2 layers x 2048 pages x 8
+    heads x D128 BF16 (8192 segments), K FP8 dynamic, V FP8 direct, layer 1
+    protected, 1% of segments injected with values the FP8 gate keeps raw;
+    with and without CRC, sampled segments compared both ways."""
+    print(f"[case] fp8 large call one-wave encode crc={crc}", flush=True)
+    L, pages = 2, 2048
+    wl = G.Workload(L, 8, 128, 16, pages, "bf16", "separate", seed=31)
+    ids = inputs.random_page_ids(pages, pages, seed=32)
+    inputs.inject_specials(wl.k, wl.v, ids, frac=0.01, seed=33)
+    segs = _sample_segments(L, pages, 96, 34, layers=[1])
+    spill = L * pages * 2 // 20 * 32768                  # room for the injected segments
+    _roundtrip_case(ctx, wl, "FP8_DYNAMIC", "FP8_DIRECT", 0, ids, protected=[1], segments=segs,
+                    decode_from_oracle=False, crc=crc, spill_bytes=spill)
+
+
 def test_tq4_u4_llama3_full_size_crc(ctx):
     """The TurboQuant-4 / uniform-4 Llama-3-8B workload with the CRC option:
     one full-size launch each way, sampled segments bit-exact (CRCs
