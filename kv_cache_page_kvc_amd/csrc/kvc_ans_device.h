@@ -525,17 +525,18 @@ __device__ __forceinline__ bool ans_decode_lanes(const SegCtx& s, uint16_t* page
       const uint32_t sl = x & (kAnsM - 1), sy = lut[sl];
       const AnsDec t = tab[sy];
       x = __umul24(t.f, x >> kAnsProbBits) + sl - t.cum;
-      const uint32_t k = (uint32_t)(x < kAnsL) + (uint32_t)(x < (kAnsL >> 8));
-      const uint32_t in = k == 2 ? __builtin_amdgcn_perm(0u, q, 0x0C0C0001u) : (k == 1 ? q & 0xFFu : 0u);   // b0 b1 / b0
-      x = (x << (8 * k)) | in;
-      bad |= pos + k > send;
-      pos += k;
+      // x < 2^23 takes b0: (x << 8) | b0; x < 2^15 takes b0, b1: (x << 16) |
+      // (b0 << 8) | b1 -- byte permutes of x and q (the bytes they drop are 0)
+      const bool one = x < kAnsL, two = x < (kAnsL >> 8);
+      const uint32_t x1 = __builtin_amdgcn_perm(x, q, 0x06050400u), x2 = __builtin_amdgcn_perm(x, q, 0x05040001u);
+      x = two ? x2 : (one ? x1 : x);
+      pos += (uint32_t)one + (uint32_t)two;                      // a stream read past its end ends past it
       const uint32_t v = CP ? (sy << 8) | ob[e] : (ob[e] << 8) | sy;
       o[e >> 1] |= v << (16 * (e & 1));
     }
     st_global16(byte_at(page_p, 2 * ans_chunk_off(s, c, D)), make_uint4(o[0], o[1], o[2], o[3]));
   }
-  return bad || pos != send || x != kAnsL;
+  return bad || pos != send || x != kAnsL;                      // pos only grows: a read past send shows here
 }
 
 template <int D, bool CRC>
