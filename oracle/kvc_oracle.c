@@ -18,16 +18,16 @@
  *            payloads at D=128) and "Ownership, storage and GDS" (segment
  *            carries version, original length, format, stored length, CRC32;
  *            keep only when the aligned footprint saves >= 12.5%; sources up
- *            to 16 MiB are encoded).
+ *            to 16 MiB are encoded) and "GPU ANS" (lossless entropy coding
+ *            of typed 16-bit pages; decompression checks the exact output
+ *            length; incompressible pages stay raw; at least 4 KiB of
+ *            input).
  *   [HIQ]    "Building a quantized HiCache for SGLang": "Building the INT8
  *            codec" (symmetric per-head INT8: amax floor, scale = amax/127,
  *            FP32 quotient, round, clamp to +-127; all-zero head restores
  *            to exact zero) and "Why exactly 1,152 bytes?" (a token's K or
  *            V row: H x D INT8 codes, then H BF16 scales, padded to a
  *            multiple of 128 bytes).
- *            "GPU ANS" (lossless entropy coding of typed 16-bit pages;
- *            decompression checks the exact output length; incompressible
- *            pages stay raw; at least 4 KiB of input).
  *   [KNLP]   "Asymmetric KV: methods and results": "Precision and scaling
  *            reference" (FP32 amax clamped at 1e-12, times the rounded FP32
  *            reciprocal of 448, FP32 divide, clip to +-448, E4M3FN RNE;

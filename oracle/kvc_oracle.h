@@ -8,7 +8,8 @@
  *
  * Sources (the pages):
  *   [OKV-SF]  OrbitKV docs, "KV precision and storage encoding",
- *             sections "FP8 and TurboQuant" and "Ownership, storage and GDS".
+ *             sections "FP8 and TurboQuant", "Ownership, storage and GDS"
+ *             and "GPU ANS".
  *   [HIQ]     "Building a quantized HiCache for SGLang", sections
  *             "Building the INT8 codec" and "Why exactly 1,152 bytes?".
  *   [KNLP]    knlp, "Asymmetric KV: methods and results", section
@@ -26,7 +27,13 @@
  * tables, distortion and optimality conditions; SplitMix64's published
  * vector; the WHT against the Hadamard matrix and its involution; payload
  * sizes; closed-form TurboQuant codes of signed Hadamard rows; nearest-level
- * and nearest-centroid brute force; gate cases.
+ * and nearest-centroid brute force; gate cases; the INT8 record's sizes
+ * (tests/golden/int8_record_sizes.json), a worked token row, the closed form
+ * of power-of-two scales and its error bound; the ANS16 model normalisation
+ * invariants, lossless round trips, the closed form of a constant plane, the
+ * raw-plane rule, the coded size against the model's cross-entropy (both
+ * bounds) and the rejection of streams that end early, run long or start
+ * outside the state interval.
  *
  * Parity unpinned (by the pages): the exact bits of TurboQuant codes at
  * threshold boundaries and of TurboQuant decodes depend on the FP32
@@ -34,7 +41,11 @@
  * pairwise sum-of-squares tree, WHT stages in ascending span, decode
  * g = RN(n_h / RN(RN(sqrt(q)) * RN(sqrt(D))))); the pages fix only the
  * steps, so only the invariants above pin them.  Likewise the uniform
- * codec's single rounding of RN(x - m_h) * RN(1/sigma_h).
+ * codec's single rounding of RN(x - m_h) * RN(1/sigma_h).  The ANS16
+ * payload bytes follow this library's own format (the pages name nvCOMP's
+ * ANS without giving its format): its pins fix what any such coder must
+ * satisfy (lossless, sizes near the entropy, exact-length checks), not the
+ * byte layout itself.
  */
 #ifndef KVC_ORACLE_H
 #define KVC_ORACLE_H
