@@ -706,6 +706,52 @@ def test_crc_spill_capacity(ctx):
     assert np.all(st[cap] == 1) and np.all(np.delete(st, cap) == 0)
 
 
+def test_ans16_corrupted_payloads_match_oracle(ctx):
+    """Bytes of an ANS16 payload changed at random (plane headers, bitmap,
+    frequencies, stream lengths, streams, padding; no CRC): the GPU accepts
+    exactly the payloads the oracle accepts (status 0 or 1) and then decodes
+    the same values.  200 trials over the 4 segments of a small call."""
+    print("[case] ans16 corrupted payloads", flush=True)
+    wl = G.Workload(1, 8, 128, 16, 3, "bf16", "separate", seed=41)
+    ids = np.array([2, 0], np.int32)
+    kc = vc = kvc.CODECS["ANS16"]
+    codec = kvc.Codec(kc, vc, seed=0, layers=wl.L)
+    out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids)
+    torch.cuda.synchronize()
+    gdesc = G.desc_np(desc)
+    assert all(int(d["status"]) == O.SEG_ENCODED for d in gdesc)
+    buf = out.cpu().numpy()
+    rng = np.random.default_rng(42)
+    dev = torch.empty(total, dtype=torch.uint8, device="cuda")
+    seglist = G.segments_of(wl.L, len(ids))
+    accepted = 0
+    for trial in range(200):
+        s_ = int(rng.integers(4))
+        so, nb = int(gdesc[s_]["spill_offset"]), int(gdesc[s_]["stored_len"])
+        bad = buf.copy()
+        for _ in range(int(rng.integers(1, 4))):
+            if rng.random() < 0.5:                          # the plane headers, bitmap, frequencies and lengths
+                pos = so + int(rng.integers(min(nb, 800)))
+            else:
+                pos = so + int(rng.integers(nb))
+            bad[pos] ^= np.uint8(1 << int(rng.integers(8)))
+        try:
+            ora = G.oracle_decode_segments(bad, wl, kc, vc, 0, len(ids), None, [s_])[s_]
+        except ValueError:
+            ora = None
+        dev.copy_(torch.from_numpy(bad))
+        dst = wl.empty_like(fill_bits=0x7FC1)
+        st = G.gpu_decode(ctx, dst, codec, dev, total, ids).cpu().numpy()
+        torch.cuda.synchronize()
+        assert int(st[s_]) == (1 if ora is None else 0), f"trial {trial}: segment {s_} status {st[s_]}"
+        assert all(int(st[t]) == 0 for t in range(4) if t != s_)
+        if ora is not None:
+            accepted += 1
+            l, i, c = seglist[s_]
+            assert np.array_equal(G.gpu_segment_vectors(dst, l, c, int(ids[i])), ora), f"trial {trial}"
+    assert accepted < 200
+
+
 def test_ans16_spill_capacity(ctx):
     """ANS16 payloads live in the spill region: sized for about ten of the
     32 payloads, the segments that found room hold the oracle's payload bytes
