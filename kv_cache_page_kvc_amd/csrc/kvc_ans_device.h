@@ -201,7 +201,7 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
   AnsEnc* const s_enc = reinterpret_cast<AnsEnc*>(s_dyn);             // [2][256], after the histograms
   uint8_t* const s_out = s_dyn + kAnsEncBytes;                        // one coded plane's image
   __shared__ unsigned long long s_off;
-  CrcTables* const ct = crc_tables_lds<CRC>();
+  CrcLds* const ct = crc_tables_lds<CRC>();
   const uint32_t seg = p.seg_base + blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
       for (uint32_t u = 0; u < 4; u++)
         if (c0 + u * kAnsStreams < chunks) st_global16(heap + 16 * (c0 + u * kAnsStreams), w[u]);
     }
-    const uint32_t cr = CRC ? crc32_written(heap, raw_bytes, ct) : 0u;
+    const uint32_t cr = CRC ? crc32_written<64>(heap, raw_bytes, ct) : 0u;
     if (lane == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | crc_flag, KVC_SEG_RAW_DATA,
                         (int)p.dtype, comp, D, s.n_vec, raw_bytes, off, 0, cr);
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
       st_global16(P + 16 * u, *reinterpret_cast<const uint4*>(s_out + 16 * u));
     __syncthreads();                                             // the image is rebuilt for the next plane
   }
-  const uint32_t cr = CRC ? crc32_written(heap, payload, ct) : 0u;
+  const uint32_t cr = CRC ? crc32_written<64>(heap, payload, ct) : 0u;
   // no fence before the header: nothing reads the payload during this
   // launch, and its completion makes every write visible to later work
   if (lane == 0) {
@@ -544,8 +544,7 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   __shared__ AnsDec s_tab[256];
   __shared__ __attribute__((aligned(16))) uint8_t s_lut[kAnsM];
   __shared__ uint32_t s_ring[64 * (kAnsRingWords + 1)];
-  __shared__ uint32_t s_crc_ok;
-  CrcTables* const ct = crc_tables_lds<CRC>();
+  CrcLds* const ct = crc_tables_lds<CRC>();
   const uint32_t seg = p.seg_base + blockIdx.x;
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
@@ -594,11 +593,8 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   }
   const uint8_t* const heap = p.buf + spill;
   if constexpr (CRC) {
-    __syncthreads();
-    const uint32_t c = crc32_wave(GlobalBytes{heap}, stored, ct);
-    if (lane == 0) s_crc_ok = c == h1.z;
-    __syncthreads();
-    if (!s_crc_ok) {
+    __syncthreads();                                             // CRC tables in LDS
+    if (crc32_lanes<64>(GlobalBytes{heap}, stored, ct) != h1.z) {
       if (report) p.seg_status[seg] = 3;
       return;
     }

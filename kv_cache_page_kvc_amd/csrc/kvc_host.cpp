@@ -154,13 +154,16 @@ void build_crc_tables(CrcTables& c) {
   auto zero_byte = [&c](uint32_t r) { return (r >> 8) ^ c.t[0][r & 0xFF]; };
   for (int k = 1; k < 4; k++)
     for (int b = 0; b < 256; b++) c.t[k][b] = zero_byte(c.t[k - 1][b]);
-  for (int k = 0; k < 4; k++)
-    for (int b = 0; b < 256; b++) {
-      uint32_t r = c.t[k][b];
-      for (uint32_t i = 0; i < kCrcGapBytes; i++) r = zero_byte(r);
-      c.tg[k][b] = r;
-    }
-  for (int lvl = 0; lvl < 6; lvl++)
+  for (int w = 0; w < kCrcLaneSets; w++) {
+    const uint32_t gap = 16u * ((uint32_t)kCrcLanes * (1u << w) - 1u);
+    for (int k = 0; k < 4; k++)
+      for (int b = 0; b < 256; b++) {
+        uint32_t r = c.t[k][b];
+        for (uint32_t i = 0; i < gap; i++) r = zero_byte(r);
+        c.tg[w][k][b] = r;
+      }
+  }
+  for (int lvl = 0; lvl < kCrcShiftLevels; lvl++)
     for (int i = 0; i < 8; i++)
       for (uint32_t v = 0; v < 16; v++) {
         uint32_t r = v << (4 * i);

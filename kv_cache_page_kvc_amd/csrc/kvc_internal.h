@@ -53,21 +53,29 @@ struct CellEntry {
   uint32_t base;
 };
 
-// CRC-32 tables (reflected polynomial 0xEDB88320) for the one-wave CRC of a
-// byte range: lane j takes 16-byte units j, j + 64, j + 128, ... and runs
-// the slice-by-4 table step over each; the last word of a unit that has a
-// successor in the same lane uses tg, which also carries the register over
-// the kCrcGapBytes that the other 63 lanes take in between.  Each lane then
-// carries its register over the (63 - j) units after its last one with the
-// nibble tables sh, and the wave xors the registers.
-constexpr int kCrcLanes = 64;
-constexpr uint32_t kCrcGapBytes = 16 * (kCrcLanes - 1);
+// CRC-32 tables (reflected polynomial 0xEDB88320) for the CRC of a byte
+// range computed by all N = 64 * 2^w lanes of a workgroup (w = 0, 1, 2 for
+// 64, 128, 256 threads): lane j takes 16-byte units j, j + N, j + 2N, ...
+// and runs the slice-by-4 table step over each; the last word of a unit that
+// has a successor in the same lane uses tg[w], which also carries the
+// register over the 16 (N - 1) bytes that the other lanes take in between.
+// Each lane then carries its register over the (N - 1 - j) units after its
+// last one with the nibble tables sh, and the lanes' registers are xored.
+constexpr int kCrcLanes = 64;               // lanes of a wave
+constexpr int kCrcLaneSets = 3;             // N = 64, 128, 256
+constexpr int kCrcShiftLevels = 8;          // shifts of 16 << lvl bytes, lvl < 8: up to N - 1 = 255 units
 struct CrcTables {
-  uint32_t t[4][256];    // register after byte b followed by k zero bytes, from a zero register
-  uint32_t tg[4][256];   // t[k][b] carried over kCrcGapBytes more zero bytes
-  uint32_t sh[6][8][16]; // register whose nibble i is v (others 0) carried over 16 << lvl zero bytes
+  uint32_t t[4][256];                       // register after byte b followed by k zero bytes, from a zero register
+  uint32_t tg[kCrcLaneSets][4][256];        // t[k][b] carried over 16 (64 * 2^w - 1) more zero bytes
+  uint32_t sh[kCrcShiftLevels][8][16];      // register whose nibble i is v (others 0) over 16 << lvl zero bytes
 };
 static_assert(sizeof(CrcTables) % 16 == 0, "CRC tables are copied in 16-byte units");
+// the part of CrcTables one kernel keeps in LDS: t, its lane count's tg, sh
+struct CrcLds {
+  uint32_t t[4][256];
+  uint32_t tg[4][256];
+  uint32_t sh[kCrcShiftLevels][8][16];
+};
 
 // Reciprocals of the rANS encoder (KVC_ANS16), indexed by the frequency f in
 // [1, 4096]: ceil(2^(31+l) / f) with l = ceil(log2 f) for f >= 2, so that

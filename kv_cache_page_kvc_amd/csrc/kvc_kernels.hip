@@ -755,10 +755,10 @@ __device__ __forceinline__ uint32_t payload_bytes(int codec, int d, uint32_t n_v
 
 // ------------------------------------------------------------------ CRC-32
 // CRC-32 of zlib over a byte range [OKV-SF "Ownership, storage and GDS":
-// every stored segment carries a CRC32], computed by one wave from the
-// tables in CrcTables (see there for the lane schedule).  The register is
-// preset to 0xFFFFFFFF by complementing the first word and the result is
-// complemented at the end.
+// every stored segment carries a CRC32], computed by all lanes of the
+// workgroup from the tables in CrcTables (see there for the lane schedule).
+// The register is preset to 0xFFFFFFFF by complementing the first word and
+// the result is complemented at the end.
 
 // register after the four bytes of x (x = register ^ next little-endian word)
 __device__ __forceinline__ uint32_t crc_word(uint32_t x, const uint32_t (*t)[256]) {
@@ -773,42 +773,56 @@ __device__ __forceinline__ uint32_t crc_zeros(uint32_t r, const uint32_t (*sh)[1
 }
 
 // The CRC tables in LDS: a static allocation that only the kernels built
-// with CRC reference (so the others do not pay for its 11 KiB), at an
+// with CRC reference (so the others do not pay for its 12 KiB), at an
 // address the compiler knows, so table offsets fold into the LDS loads.
 template <bool CRC>
-__device__ __forceinline__ CrcTables* crc_tables_lds() {
+__device__ __forceinline__ CrcLds* crc_tables_lds() {
   if constexpr (CRC) {
-    __shared__ CrcTables s_crc_tables;
+    __shared__ CrcLds s_crc_tables;
     return &s_crc_tables;
   } else {
     return nullptr;
   }
 }
 
-// Copy the CRC tables into LDS (all threads of the workgroup; the caller
-// synchronises before the first use).
+// log2 of a workgroup's wave count: its lane set in CrcTables::tg
 template <int NT>
-__device__ __forceinline__ void load_crc_tables(CrcTables* dst, const CrcTables* src) {
-  constexpr uint32_t kUnits = sizeof(CrcTables) / 16;
-  for (uint32_t u = threadIdx.x; u < kUnits; u += NT)
-    reinterpret_cast<uint4*>(dst)[u] = ld_global16(reinterpret_cast<const uint8_t*>(src) + 16 * u);
+constexpr int crc_lane_set() {
+  static_assert(NT == 64 || NT == 128 || NT == 256, "CRC lane sets cover 1, 2 or 4 waves");
+  return NT == 64 ? 0 : (NT == 128 ? 1 : 2);
+}
+
+// Copy the tables for NT lanes into LDS (all threads of the workgroup; the
+// caller synchronises before the first use).
+template <int NT>
+__device__ __forceinline__ void load_crc_tables(CrcLds* dst, const CrcTables* src) {
+  const uint4* t = reinterpret_cast<const uint4*>(src->t);
+  const uint4* tg = reinterpret_cast<const uint4*>(src->tg[crc_lane_set<NT>()]);
+  const uint4* sh = reinterpret_cast<const uint4*>(src->sh);
+  constexpr uint32_t kT = sizeof(src->t) / 16, kTg = sizeof(src->tg[0]) / 16, kSh = sizeof(src->sh) / 16;
+  for (uint32_t u = threadIdx.x; u < kT + kTg + kSh; u += NT) {
+    const uint4* from = u < kT ? t + u : (u < kT + kTg ? tg + (u - kT) : sh + (u - kT - kTg));
+    reinterpret_cast<uint4*>(dst)[u] = ld_global16(from);
+  }
 }
 
 // CRC32 of n bytes; load(o) returns the 16 bytes at offset o of the range
 // (o a multiple of 16).  When n is not a multiple of 16 the 16-byte unit
-// holding the last bytes must be readable as a whole.  Called by all 64
-// lanes of one wave; every lane returns the CRC.
-template <class Load>
-__device__ __forceinline__ uint32_t crc32_wave(const Load& load, uint32_t n, const CrcTables* ct) {
-  const uint32_t lane = threadIdx.x & (kCrcLanes - 1);
+// holding the last bytes must be readable as a whole.  Called by all NT
+// threads of the workgroup (with NT > 64 it synchronises them); every thread
+// returns the CRC.
+template <int NT, class Load>
+__device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, const CrcLds* ct) {
+  constexpr int LEVELS = 6 + crc_lane_set<NT>();              // NT - 1 < 2^LEVELS units
+  const uint32_t lane = threadIdx.x;
   const uint32_t units = n >> 4;
-  // virtual zero units in front make the unit count a multiple of 64 (a zero
-  // register stays zero over zero bytes), so lane 63 holds the last unit
-  const uint32_t pad = (kCrcLanes - (units & (kCrcLanes - 1))) & (kCrcLanes - 1);
-  const uint32_t rounds = (units + pad) / kCrcLanes;
+  // virtual zero units in front make the unit count a multiple of NT (a zero
+  // register stays zero over zero bytes), so lane NT - 1 holds the last unit
+  const uint32_t pad = (NT - (units & (NT - 1))) & (NT - 1);
+  const uint32_t rounds = (units + pad) / NT;
   uint32_t r = 0;
   for (uint32_t k = 0; k < rounds; k++) {
-    const int32_t q = (int32_t)(k * kCrcLanes + lane) - (int32_t)pad;
+    const int32_t q = (int32_t)(k * NT + lane) - (int32_t)pad;
     uint4 w = make_uint4(0, 0, 0, 0);
     if (q >= 0) w = load(16u * (uint32_t)q);
     if (q == 0) w.x = ~w.x;
@@ -817,15 +831,24 @@ __device__ __forceinline__ uint32_t crc32_wave(const Load& load, uint32_t n, con
     r = crc_word(r ^ w.z, ct->t);
     r = crc_word(r ^ w.w, k + 1 < rounds ? ct->tg : ct->t);
   }
-  // carry each register over the units after its last one: 63 - lane
-  const uint32_t after = (kCrcLanes - 1) - lane;
+  // carry each register over the units after its last one: NT - 1 - lane
+  const uint32_t after = (NT - 1) - lane;
 #pragma unroll
-  for (int lvl = 0; lvl < 6; lvl++) {
+  for (int lvl = 0; lvl < LEVELS; lvl++) {
     const uint32_t y = crc_zeros(r, ct->sh[lvl]);
     r = (after >> lvl) & 1 ? y : r;
   }
 #pragma unroll
   for (int m = kCrcLanes / 2; m >= 1; m >>= 1) r ^= __shfl_xor(r, m, kCrcLanes);
+  if constexpr (NT > kCrcLanes) {                                // xor the waves' registers
+    __shared__ uint32_t s_part[NT / kCrcLanes];
+    if ((lane & (kCrcLanes - 1)) == 0) s_part[lane / kCrcLanes] = r;
+    __syncthreads();
+    r = 0;
+#pragma unroll
+    for (int v = 0; v < NT / kCrcLanes; v++) r ^= s_part[v];
+    __syncthreads();                                             // s_part is reused by the next call
+  }
   // the ragged end (n mod 16 bytes), the same in every lane
   if (!units) r = 0xFFFFFFFFu;
   const uint32_t tail = n & 15;
@@ -868,11 +891,12 @@ __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const La
 }
 
 // CRC32 of bytes the workgroup has just written to global memory: the
-// barrier orders every wave's stores before wave 0 reads them back; wave 0
-// returns the CRC, the other waves 0.  Called by all threads.
-__device__ __forceinline__ uint32_t crc32_written(const uint8_t* b, uint32_t n, const CrcTables* ct) {
+// barrier orders every wave's stores before they are read back.  Called by
+// all threads; every thread returns the CRC.
+template <int NT>
+__device__ __forceinline__ uint32_t crc32_written(const uint8_t* b, uint32_t n, const CrcLds* ct) {
   __syncthreads();
-  return threadIdx.x < kCrcLanes ? crc32_wave(GlobalBytes{b}, n, ct) : 0u;
+  return crc32_lanes<NT>(GlobalBytes{b}, n, ct);
 }
 
 // ------------------------------------------------------------------ encode kernel
@@ -880,9 +904,8 @@ template <int D, int DT, int NT, bool CRC>
 __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   __shared__ CellEntry s_cells[kCells];
   __shared__ unsigned long long s_spill;
-  __shared__ uint32_t s_crc;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
-  CrcTables* const ct = crc_tables_lds<CRC>();
+  CrcLds* const ct = crc_tables_lds<CRC>();
 
   const uint32_t seg = p.seg_base + blockIdx.x;       // segments [seg_base, seg_base + grid)
   const uint32_t two_n = 2u * p.n_pages;
@@ -928,7 +951,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   if (codec == C_RAW) {                                        // raw by policy
     copy_out_raw<D, NT, false>(s, ln, s.slot + kHeaderBytes);
     zero_pad<NT>(s.slot, kHeaderBytes + raw_bytes, slot_bytes);
-    const uint32_t c = crc ? crc32_written(s.slot + kHeaderBytes, raw_bytes, ct) : 0u;
+    const uint32_t c = crc ? crc32_written<NT>(s.slot + kHeaderBytes, raw_bytes, ct) : 0u;
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY | crc_flag, KVC_SEG_RAW_POLICY, DT,
                         comp, D, s.n_vec, raw_bytes, 0, 0, c);
@@ -966,15 +989,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const int any_bad = __syncthreads_or(bad);
   const uint32_t aux = codec == C_FP8F ? __float_as_uint(fixed) : 0u;
   if (staged && !any_bad) {
-    uint32_t c = 0;
-    if (crc) {
-      if (threadIdx.x < kCrcLanes) {
-        c = crc32_wave(LdsBytes{s_stage + stored_at}, payload, ct);
-        if (threadIdx.x == 0) s_crc = c;
-      }
-      __syncthreads();
-      c = s_crc;
-    }
+    const uint32_t c = crc ? crc32_lanes<NT>(LdsBytes{s_stage + stored_at}, payload, ct) : 0u;
     // header + body from unit 0, so every wave store covers whole lines
     const Header h = make_header(codec, crc_flag, DT, comp, D, s.n_vec, payload, 0, aux, c);
     for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT) {
@@ -990,7 +1005,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
     for (uint32_t u = 2 + threadIdx.x; u < slot_bytes / 16; u += NT)
       st_stream16(s.slot + 16 * u, *reinterpret_cast<const uint4*>(s_stage + 16 * u));
   if (!any_bad) {
-    const uint32_t c = crc ? crc32_written(s.slot + stored_at, payload, ct) : 0u;
+    const uint32_t c = crc ? crc32_written<NT>(s.slot + stored_at, payload, ct) : 0u;
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, codec, crc_flag, KVC_SEG_ENCODED, DT, comp, D, s.n_vec, payload, 0,
                         aux, c);
@@ -1004,7 +1019,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
   if (fits) copy_out_raw<D, NT, true>(s, ln, p.buf + p.slot_region + off);
   // a segment that was not stored (no spill space) carries no CRC
-  const uint32_t c = crc && fits ? crc32_written(p.buf + p.slot_region + off, raw_bytes, ct) : 0u;
+  const uint32_t c = crc && fits ? crc32_written<NT>(p.buf + p.slot_region + off, raw_bytes, ct) : 0u;
   if (threadIdx.x == 0) {
     if (fits)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | crc_flag, KVC_SEG_RAW_DATA, DT, comp,
@@ -1218,9 +1233,8 @@ __device__ __forceinline__ void decode_codec(int codec, const SegCtx& s, const L
 template <int D, int DT, int NT, bool CRC>
 __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   __shared__ float s_cent[32];
-  __shared__ uint32_t s_crc_ok;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
-  CrcTables* const ct = crc_tables_lds<CRC>();
+  CrcLds* const ct = crc_tables_lds<CRC>();
   const uint32_t seg = p.seg_base + blockIdx.x;       // segments [seg_base, seg_base + grid)
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
@@ -1286,14 +1300,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   // the stored bytes must match the header's CRC32 before the page is written
   if constexpr (CRC) {
     __syncthreads();                                      // CRC tables in LDS
-    if (threadIdx.x < kCrcLanes) {
-      const uint32_t c = raw_data ? crc32_wave(GlobalBytes{p.buf + spill}, stored, ct)
-                         : staged ? crc32_wave(LdsBytes{s_stage + stored_at}, stored, ct)
-                                  : crc32_wave(GlobalBytes{s.slot + stored_at}, stored, ct);
-      if (threadIdx.x == 0) s_crc_ok = c == h1.z;
-    }
-    __syncthreads();
-    if (!s_crc_ok) {
+    const uint32_t c = raw_data ? crc32_lanes<NT>(GlobalBytes{p.buf + spill}, stored, ct)
+                       : staged ? crc32_lanes<NT>(LdsBytes{s_stage + stored_at}, stored, ct)
+                                : crc32_lanes<NT>(GlobalBytes{s.slot + stored_at}, stored, ct);
+    if (c != h1.z) {
       if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 3;
       return;
     }
