@@ -544,8 +544,9 @@ uint32_t workgroup_threads(const kvc_layout* L, uint32_t big) {
 // kSmallSegmentBytes.
 constexpr uint64_t kLightOneWaveSegments = 32 * 256;
 hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
-  const uint32_t nt = plan.light && nseg >= kLightOneWaveSegments ? (uint32_t)kThreadsSmall
-                                                                   : workgroup_threads(L, kEncodeThreads);
+  const uint32_t nt = plan.light && nseg >= kLightOneWaveSegments
+                          ? (uint32_t)kThreadsSmall
+                          : workgroup_threads(L, P.crc ? kEncodeThreadsCrc : kEncodeThreads);
   hipError_t e = all_ans(L, plan, P) ? hipSuccess : launch_encode(with_threads(P, L, nt), L->head_dim, nseg, s);
   if (e == hipSuccess && plan.ans) {
     CallParams A = P;

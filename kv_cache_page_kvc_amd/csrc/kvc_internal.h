@@ -18,6 +18,9 @@ namespace kvc {
 // flight per wave; a large call whose components all encode raw, FP8 direct
 // or FP8 dynamic keeps one wave) and kDecodeThreads for decode (four waves).
 constexpr int kEncodeThreads = 128;
+// encode with the CRC option: the CRC tables' LDS halves the workgroups a CU
+// holds, so four waves per workgroup keep as many waves in flight
+constexpr int kEncodeThreadsCrc = 256;
 constexpr int kDecodeThreads = 256;
 constexpr int kThreadsSmall = 64;
 constexpr uint32_t kSmallSegmentBytes = 16384;

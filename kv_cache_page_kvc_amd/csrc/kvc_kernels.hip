@@ -1353,27 +1353,28 @@ struct DecodeLaunch {
   }
 };
 // instantiation for the call's dtype, workgroup size (one wave, or BIG
-// threads) and CRC option; a launch with another size is refused
-template <int D, int BIG, template <int, int, int, bool> class F>
+// threads; BIGC with the CRC option) and CRC option; a launch with another
+// size is refused
+template <int D, int BIG, int BIGC, template <int, int, int, bool> class F>
 hipError_t dispatch(const CallParams& p, uint64_t nseg, hipStream_t st) {
   const bool bf = p.dtype == KVC_BF16, small = p.threads == kThreadsSmall, crc = p.crc != 0;
-  if (!small && p.threads != (uint32_t)BIG) return hipErrorInvalidConfiguration;
+  if (!small && p.threads != (uint32_t)(crc ? BIGC : BIG)) return hipErrorInvalidConfiguration;
   if (bf) {
     if (small) crc ? F<D, KVC_BF16, kThreadsSmall, true>::run(p, nseg, st) : F<D, KVC_BF16, kThreadsSmall, false>::run(p, nseg, st);
-    else crc ? F<D, KVC_BF16, BIG, true>::run(p, nseg, st) : F<D, KVC_BF16, BIG, false>::run(p, nseg, st);
+    else crc ? F<D, KVC_BF16, BIGC, true>::run(p, nseg, st) : F<D, KVC_BF16, BIG, false>::run(p, nseg, st);
   } else {
     if (small) crc ? F<D, KVC_FP16, kThreadsSmall, true>::run(p, nseg, st) : F<D, KVC_FP16, kThreadsSmall, false>::run(p, nseg, st);
-    else crc ? F<D, KVC_FP16, BIG, true>::run(p, nseg, st) : F<D, KVC_FP16, BIG, false>::run(p, nseg, st);
+    else crc ? F<D, KVC_FP16, BIGC, true>::run(p, nseg, st) : F<D, KVC_FP16, BIG, false>::run(p, nseg, st);
   }
   return hipGetLastError();
 }
 template <int D>
 hipError_t launch_encode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
-  return dispatch<D, kEncodeThreads, EncodeLaunch>(p, nseg, st);
+  return dispatch<D, kEncodeThreads, kEncodeThreadsCrc, EncodeLaunch>(p, nseg, st);
 }
 template <int D>
 hipError_t launch_decode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
-  return dispatch<D, kDecodeThreads, DecodeLaunch>(p, nseg, st);
+  return dispatch<D, kDecodeThreads, kDecodeThreads, DecodeLaunch>(p, nseg, st);
 }
 
 }  // namespace
