@@ -31,6 +31,9 @@
  *    caller owns the KV tensors, the page-id arrays, the encoded buffer and
  *    the descriptor array; the library owns only its arena.
  *  - A context may be used from one host thread at a time.
+ *  - No C++ exception leaves the library: a failed host allocation returns
+ *    KVC_E_NOMEM, from the call's checks and set-up, before it enqueues
+ *    anything.
  *
  * Encoded format (version 1)
  *  Segment = (page, layer, component K or V) = T*H vectors of D elements, in
@@ -107,7 +110,8 @@ typedef enum {
   KVC_E_DUP_DST = 4,      /* the same destination page twice in one decode */
   KVC_E_CAPACITY = 5,     /* output/input buffer smaller than the plan */
   KVC_E_BUDGET = 6,       /* per-call metadata exceeds the workspace budget */
-  KVC_E_HIP = 7           /* a HIP runtime call failed */
+  KVC_E_HIP = 7,          /* a HIP runtime call failed */
+  KVC_E_NOMEM = 8         /* host memory for the call's bookkeeping ran out */
 } kvc_status;
 
 typedef enum { KVC_BF16 = 1, KVC_FP16 = 2 } kvc_dtype;

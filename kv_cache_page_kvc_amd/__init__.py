@@ -22,7 +22,7 @@ KVC_DEFAULT_WORKSPACE = 64 << 20
 
 # kvc_status
 KVC_OK, KVC_E_ARG, KVC_E_UNSUPPORTED, KVC_E_PAGE_RANGE, KVC_E_DUP_DST, KVC_E_CAPACITY, \
-    KVC_E_BUDGET, KVC_E_HIP = range(8)
+    KVC_E_BUDGET, KVC_E_HIP, KVC_E_NOMEM = range(9)
 # kvc_dtype / kvc_layout_kind
 KVC_BF16, KVC_FP16 = 1, 2
 KVC_SEPARATE_NHD, KVC_PACKED_HT2D = 1, 2

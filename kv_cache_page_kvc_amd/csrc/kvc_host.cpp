@@ -23,6 +23,7 @@
 #include <cmath>
 #include <cstring>
 #include <limits>
+#include <memory>
 #include <vector>
 
 #include "kvc.h"
@@ -350,6 +351,10 @@ struct DeviceGuard {
 // occupies the bytes about to be reused
 kvc_status ring_alloc(kvc_ctx* ctx, size_t size, size_t* off) {
   if (size > ctx->ring_end - ctx->ring_begin) return KVC_E_BUDGET;
+  // room for every event this call may retire and for ring_commit's entry,
+  // so that no container grows (or throws) once work is enqueued
+  ctx->free_events.reserve(ctx->free_events.size() + ctx->inflight.size());
+  ctx->inflight.reserve(ctx->inflight.size() + 1);
   // retire finished calls
   for (size_t i = 0; i < ctx->inflight.size();) {
     if (hipEventQuery(ctx->inflight[i].ev) == hipSuccess) {
@@ -418,6 +423,7 @@ kvc_status lane_reserve(kvc_ctx* ctx, int dir, size_t bytes) {
   auto& st = ctx->lane[dir];
   if (st.cap >= bytes) return KVC_OK;
   const size_t cap = align_up(std::max(bytes, st.cap + st.cap / 4), 1u << 20);
+  ctx->retired.reserve(ctx->retired.size() + 1);      // before the buffer exists
   uint8_t* p = nullptr;
   if (hipMalloc(&p, cap) != hipSuccess) return KVC_E_HIP;
   if (st.ptr) ctx->retired.push_back({st.ptr, st.last});
@@ -563,6 +569,16 @@ hipError_t run_decode(const CallParams& P, const kvc_layout* L, const Plan& plan
   return e;
 }
 
+// Host containers can throw std::bad_alloc; no exception crosses the C ABI.
+template <class F>
+kvc_status no_throw(F&& f) noexcept {
+  try {
+    return f();
+  } catch (...) {
+    return KVC_E_NOMEM;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -577,279 +593,301 @@ const char* kvc_status_string(kvc_status s) {
     case KVC_E_CAPACITY: return "buffer smaller than the plan";
     case KVC_E_BUDGET: return "workspace budget exceeded";
     case KVC_E_HIP: return "HIP runtime error";
+    case KVC_E_NOMEM: return "host memory exhausted";
   }
   return "unknown status";
 }
 
 kvc_status kvc_plan(const kvc_layout* layout, const kvc_codec* codec, uint32_t n_pages, size_t* slot_bytes,
                     size_t* spill_bytes_suggested, size_t* bytes_per_token) {
-  kvc_status st = check_layout(layout);
-  if (st == KVC_OK) st = check_codec(layout, codec);
-  if (st != KVC_OK) return st;
-  const Plan p = make_plan(layout, codec, n_pages);
-  const uint64_t raw_seg = align_up((uint64_t)layout->kv_heads * layout->tokens_per_page * layout->head_dim * 2,
-                                    KVC_SLOT_ALIGN);
-  if (slot_bytes) *slot_bytes = p.total;
-  // ~3% of the fixed-size segments may fall back to raw, and every KVC_ANS16
-  // segment needs its payload -- at most its raw size -- in the spill region
-  if (spill_bytes_suggested)
-    *spill_bytes_suggested = raw_seg * (std::max<uint64_t>(1, (p.encodable - p.ans + 31) / 32) + p.ans);
-  if (bytes_per_token) *bytes_per_token = (p.per_page + layout->tokens_per_page - 1) / layout->tokens_per_page;
-  return KVC_OK;
+  return no_throw([&]() -> kvc_status {
+    kvc_status st = check_layout(layout);
+    if (st == KVC_OK) st = check_codec(layout, codec);
+    if (st != KVC_OK) return st;
+    const Plan p = make_plan(layout, codec, n_pages);
+    const uint64_t raw_seg = align_up((uint64_t)layout->kv_heads * layout->tokens_per_page * layout->head_dim * 2,
+                                      KVC_SLOT_ALIGN);
+    if (slot_bytes) *slot_bytes = p.total;
+    // ~3% of the fixed-size segments may fall back to raw, and every KVC_ANS16
+    // segment needs its payload -- at most its raw size -- in the spill region
+    if (spill_bytes_suggested)
+      *spill_bytes_suggested = raw_seg * (std::max<uint64_t>(1, (p.encodable - p.ans + 31) / 32) + p.ans);
+    if (bytes_per_token) *bytes_per_token = (p.per_page + layout->tokens_per_page - 1) / layout->tokens_per_page;
+    return KVC_OK;
+  });
 }
 
 kvc_status kvc_validate_encode(const kvc_layout* layout, const kvc_codec* codec, const int32_t* page_ids,
                                uint32_t n_pages, size_t out_bytes) {
-  kvc_status st = check_layout(layout);
-  if (st == KVC_OK) st = check_codec(layout, codec);
-  if (st == KVC_OK) st = check_grid(layout, n_pages);
-  if (st == KVC_OK) st = check_pages(layout, page_ids, n_pages, false);
-  if (st != KVC_OK) return st;
-  if (make_plan(layout, codec, n_pages).total > out_bytes) return KVC_E_CAPACITY;
-  return KVC_OK;
+  return no_throw([&]() -> kvc_status {
+    kvc_status st = check_layout(layout);
+    if (st == KVC_OK) st = check_codec(layout, codec);
+    if (st == KVC_OK) st = check_grid(layout, n_pages);
+    if (st == KVC_OK) st = check_pages(layout, page_ids, n_pages, false);
+    if (st != KVC_OK) return st;
+    if (make_plan(layout, codec, n_pages).total > out_bytes) return KVC_E_CAPACITY;
+    return KVC_OK;
+  });
 }
 
 kvc_status kvc_validate_decode(const kvc_layout* layout, const kvc_codec* codec, const int32_t* dst_page_ids,
                                uint32_t n_pages, size_t in_bytes) {
-  kvc_status st = check_layout(layout);
-  if (st == KVC_OK) st = check_codec(layout, codec);
-  if (st == KVC_OK) st = check_grid(layout, n_pages);
-  if (st == KVC_OK) st = check_pages(layout, dst_page_ids, n_pages, true);
-  if (st != KVC_OK) return st;
-  if (make_plan(layout, codec, n_pages).total > in_bytes) return KVC_E_CAPACITY;
-  return KVC_OK;
+  return no_throw([&]() -> kvc_status {
+    kvc_status st = check_layout(layout);
+    if (st == KVC_OK) st = check_codec(layout, codec);
+    if (st == KVC_OK) st = check_grid(layout, n_pages);
+    if (st == KVC_OK) st = check_pages(layout, dst_page_ids, n_pages, true);
+    if (st != KVC_OK) return st;
+    if (make_plan(layout, codec, n_pages).total > in_bytes) return KVC_E_CAPACITY;
+    return KVC_OK;
+  });
 }
 
 kvc_status kvc_create(kvc_ctx** out, int hip_device, size_t workspace_budget) {
-  if (!out) return KVC_E_ARG;
-  *out = nullptr;
-  if (workspace_budget == 0) workspace_budget = KVC_DEFAULT_WORKSPACE;
-  const size_t tb = tables_bytes();
-  if (workspace_budget < tb + 4 * kAlign) return KVC_E_BUDGET;
-  DeviceGuard g(hip_device);
-  if (!g.ok) return KVC_E_HIP;
-  kvc_ctx* ctx = new kvc_ctx();
-  ctx->device = hip_device;
-  ctx->budget = workspace_budget;
-  ctx->ring_begin = tb;
-  ctx->ring_end = workspace_budget / kAlign * kAlign;
-  ctx->head = ctx->ring_begin;
-  Tables* t = new Tables();
-  build_tables(*t);
-  bool ok = hipMalloc(&ctx->arena, workspace_budget) == hipSuccess &&
-            hipHostMalloc(&ctx->staging, ctx->ring_end, hipHostMallocDefault) == hipSuccess &&
-            hipMemcpy(ctx->arena, t, sizeof(Tables), hipMemcpyHostToDevice) == hipSuccess;
-  delete t;
-  if (!ok) {
-    kvc_destroy(ctx);
-    return KVC_E_HIP;
-  }
-  *out = ctx;
-  return KVC_OK;
+  return no_throw([&]() -> kvc_status {
+    if (!out) return KVC_E_ARG;
+    *out = nullptr;
+    if (workspace_budget == 0) workspace_budget = KVC_DEFAULT_WORKSPACE;
+    const size_t tb = tables_bytes();
+    if (workspace_budget < tb + 4 * kAlign) return KVC_E_BUDGET;
+    DeviceGuard g(hip_device);
+    if (!g.ok) return KVC_E_HIP;
+    // every host allocation that may throw comes before the device memory
+    std::unique_ptr<Tables> t(new Tables());
+    build_tables(*t);
+    kvc_ctx* ctx = new kvc_ctx();
+    ctx->device = hip_device;
+    ctx->budget = workspace_budget;
+    ctx->ring_begin = tb;
+    ctx->ring_end = workspace_budget / kAlign * kAlign;
+    ctx->head = ctx->ring_begin;
+    bool ok = hipMalloc(&ctx->arena, workspace_budget) == hipSuccess &&
+              hipHostMalloc(&ctx->staging, ctx->ring_end, hipHostMallocDefault) == hipSuccess &&
+              hipMemcpy(ctx->arena, t.get(), sizeof(Tables), hipMemcpyHostToDevice) == hipSuccess;
+    if (!ok) {
+      kvc_destroy(ctx);
+      return KVC_E_HIP;
+    }
+    *out = ctx;
+    return KVC_OK;
+  });
 }
 
 kvc_status kvc_destroy(kvc_ctx* ctx) {
-  if (!ctx) return KVC_OK;
-  kvc_status st = KVC_OK;
-  {
-    DeviceGuard g(ctx->device);
-    for (auto& f : ctx->inflight) {
-      if (hipEventSynchronize(f.ev) != hipSuccess) st = KVC_E_HIP;
-      (void)hipEventDestroy(f.ev);
+  return no_throw([&]() -> kvc_status {
+    if (!ctx) return KVC_OK;
+    kvc_status st = KVC_OK;
+    {
+      DeviceGuard g(ctx->device);
+      for (auto& f : ctx->inflight) {
+        if (hipEventSynchronize(f.ev) != hipSuccess) st = KVC_E_HIP;
+        (void)hipEventDestroy(f.ev);
+      }
+      for (auto e : ctx->free_events) (void)hipEventDestroy(e);
+      for (auto& ln : ctx->lane) {
+        if (ln.last && hipEventSynchronize(ln.last) != hipSuccess) st = KVC_E_HIP;
+        if (ln.ptr) (void)hipFree(ln.ptr);
+        if (ln.last) (void)hipEventDestroy(ln.last);
+      }
+      reap_retired(ctx, true);
+      if (ctx->copy_stream && hipStreamSynchronize(ctx->copy_stream) != hipSuccess) st = KVC_E_HIP;
+      for (auto e : ctx->layer_copied) (void)hipEventDestroy(e);
+      if (ctx->fork) (void)hipEventDestroy(ctx->fork);
+      if (ctx->copy_stream) (void)hipStreamDestroy(ctx->copy_stream);
+      if (ctx->arena) (void)hipFree(ctx->arena);
+      if (ctx->staging) (void)hipHostFree(ctx->staging);
     }
-    for (auto e : ctx->free_events) (void)hipEventDestroy(e);
-    for (auto& ln : ctx->lane) {
-      if (ln.last && hipEventSynchronize(ln.last) != hipSuccess) st = KVC_E_HIP;
-      if (ln.ptr) (void)hipFree(ln.ptr);
-      if (ln.last) (void)hipEventDestroy(ln.last);
-    }
-    reap_retired(ctx, true);
-    if (ctx->copy_stream && hipStreamSynchronize(ctx->copy_stream) != hipSuccess) st = KVC_E_HIP;
-    for (auto e : ctx->layer_copied) (void)hipEventDestroy(e);
-    if (ctx->fork) (void)hipEventDestroy(ctx->fork);
-    if (ctx->copy_stream) (void)hipStreamDestroy(ctx->copy_stream);
-    if (ctx->arena) (void)hipFree(ctx->arena);
-    if (ctx->staging) (void)hipHostFree(ctx->staging);
-  }
-  delete ctx;
-  return st;
+    delete ctx;
+    return st;
+  });
 }
 
 kvc_status kvc_encode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec,
                             const int32_t* page_ids, uint32_t n_pages, void* out, size_t out_bytes,
                             kvc_segment_desc* desc, void* stream) {
-  if (!ctx) return KVC_E_ARG;
-  kvc_status st = kvc_validate_encode(layout, codec, page_ids, n_pages, out_bytes);
-  if (st != KVC_OK) return st;
-  if (n_pages == 0) return KVC_OK;
-  if (!out || !desc || ((uintptr_t)out & 255) || ((uintptr_t)desc & 15)) return KVC_E_ARG;
-  DeviceGuard g(ctx->device);
-  if (!g.ok) return KVC_E_HIP;
-  const Plan plan = make_plan(layout, codec, n_pages);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  CallParams P{};
-  size_t roff = 0, rsize = 0;
-  st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize);
-  if (st != KVC_OK) return st;
-  P.buf = static_cast<uint8_t*>(out);
-  P.buf_bytes = out_bytes;
-  P.slot_region = plan.total;
-  P.desc = desc;
-  P.seg_status = nullptr;
-  const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
-  if (run_encode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
-  return ring_commit(ctx, roff, rsize, s);
+  return no_throw([&]() -> kvc_status {
+    if (!ctx) return KVC_E_ARG;
+    kvc_status st = kvc_validate_encode(layout, codec, page_ids, n_pages, out_bytes);
+    if (st != KVC_OK) return st;
+    if (n_pages == 0) return KVC_OK;
+    if (!out || !desc || ((uintptr_t)out & 255) || ((uintptr_t)desc & 15)) return KVC_E_ARG;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVC_E_HIP;
+    const Plan plan = make_plan(layout, codec, n_pages);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CallParams P{};
+    size_t roff = 0, rsize = 0;
+    st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize);
+    if (st != KVC_OK) return st;
+    P.buf = static_cast<uint8_t*>(out);
+    P.buf_bytes = out_bytes;
+    P.slot_region = plan.total;
+    P.desc = desc;
+    P.seg_status = nullptr;
+    const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
+    if (run_encode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
+    return ring_commit(ctx, roff, rsize, s);
+  });
 }
 
 kvc_status kvc_decode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec, const void* in,
                             size_t in_bytes, const int32_t* dst_page_ids, uint32_t n_pages, uint8_t* seg_status,
                             void* stream) {
-  if (!ctx) return KVC_E_ARG;
-  kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
-  if (st != KVC_OK) return st;
-  if (n_pages == 0) return KVC_OK;
-  if (!in || ((uintptr_t)in & 255)) return KVC_E_ARG;
-  DeviceGuard g(ctx->device);
-  if (!g.ok) return KVC_E_HIP;
-  const Plan plan = make_plan(layout, codec, n_pages);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  CallParams P{};
-  size_t roff = 0, rsize = 0;
-  st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
-  if (st != KVC_OK) return st;
-  P.buf = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
-  P.buf_bytes = in_bytes;
-  P.slot_region = plan.total;
-  P.desc = nullptr;
-  P.seg_status = seg_status;
-  const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
-  if (run_decode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
-  return ring_commit(ctx, roff, rsize, s);
+  return no_throw([&]() -> kvc_status {
+    if (!ctx) return KVC_E_ARG;
+    kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
+    if (st != KVC_OK) return st;
+    if (n_pages == 0) return KVC_OK;
+    if (!in || ((uintptr_t)in & 255)) return KVC_E_ARG;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVC_E_HIP;
+    const Plan plan = make_plan(layout, codec, n_pages);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CallParams P{};
+    size_t roff = 0, rsize = 0;
+    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+    if (st != KVC_OK) return st;
+    P.buf = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
+    P.buf_bytes = in_bytes;
+    P.slot_region = plan.total;
+    P.desc = nullptr;
+    P.seg_status = seg_status;
+    const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
+    if (run_decode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
+    return ring_commit(ctx, roff, rsize, s);
+  });
 }
 
 kvc_status kvc_decode_layers(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec, const void* in,
                              size_t in_bytes, const int32_t* dst_page_ids, uint32_t n_pages, uint32_t layer_begin,
                              uint32_t layer_end, uint8_t* seg_status, void* stream) {
-  if (!ctx) return KVC_E_ARG;
-  kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
-  if (st != KVC_OK) return st;
-  if (layer_begin > layer_end || layer_end > layout->layers) return KVC_E_ARG;
-  if (n_pages == 0 || layer_begin == layer_end) return KVC_OK;
-  if (!in || ((uintptr_t)in & 255)) return KVC_E_ARG;
-  DeviceGuard g(ctx->device);
-  if (!g.ok) return KVC_E_HIP;
-  const Plan plan = make_plan(layout, codec, n_pages);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  CallParams P{};
-  size_t roff = 0, rsize = 0;
-  st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
-  if (st != KVC_OK) return st;
-  P.buf = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
-  P.buf_bytes = in_bytes;
-  P.slot_region = plan.total;
-  P.seg_status = seg_status;
-  P.seg_base = layer_begin * n_pages * 2;
-  if (run_decode(P, layout, plan, (uint64_t)(layer_end - layer_begin) * n_pages * 2, s) != hipSuccess)
-    return KVC_E_HIP;
-  return ring_commit(ctx, roff, rsize, s);
+  return no_throw([&]() -> kvc_status {
+    if (!ctx) return KVC_E_ARG;
+    kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
+    if (st != KVC_OK) return st;
+    if (layer_begin > layer_end || layer_end > layout->layers) return KVC_E_ARG;
+    if (n_pages == 0 || layer_begin == layer_end) return KVC_OK;
+    if (!in || ((uintptr_t)in & 255)) return KVC_E_ARG;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVC_E_HIP;
+    const Plan plan = make_plan(layout, codec, n_pages);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CallParams P{};
+    size_t roff = 0, rsize = 0;
+    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+    if (st != KVC_OK) return st;
+    P.buf = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
+    P.buf_bytes = in_bytes;
+    P.slot_region = plan.total;
+    P.seg_status = seg_status;
+    P.seg_base = layer_begin * n_pages * 2;
+    if (run_decode(P, layout, plan, (uint64_t)(layer_end - layer_begin) * n_pages * 2, s) != hipSuccess)
+      return KVC_E_HIP;
+    return ring_commit(ctx, roff, rsize, s);
+  });
 }
 
 kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec,
                              const int32_t* page_ids, uint32_t n_pages, void* host_out, size_t host_bytes,
                              kvc_segment_desc* host_desc, void* stream) {
-  if (!ctx) return KVC_E_ARG;
-  kvc_status st = kvc_validate_encode(layout, codec, page_ids, n_pages, host_bytes);
-  if (st != KVC_OK) return st;
-  if (n_pages == 0) return KVC_OK;
-  const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
-  const size_t desc_bytes = nseg * sizeof(kvc_segment_desc);
-  if (!pinned_range(host_out, host_bytes) || !pinned_range(host_desc, desc_bytes)) return KVC_E_ARG;
-  DeviceGuard g(ctx->device);
-  if (!g.ok) return KVC_E_HIP;
-  const Plan plan = make_plan(layout, codec, n_pages);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t buf_bytes = align_up(host_bytes, kAlign);
-  st = lane_reserve(ctx, 0, buf_bytes + desc_bytes);
-  if (st != KVC_OK) return st;
-  auto& lane = ctx->lane[0];
-  if (hipStreamWaitEvent(s, lane.last, 0) != hipSuccess) return KVC_E_HIP;   // the previous offload's copies
-  CallParams P{};
-  size_t roff = 0, rsize = 0;
-  st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize);
-  if (st != KVC_OK) return st;
-  P.buf = lane.ptr;
-  P.buf_bytes = host_bytes;
-  P.slot_region = plan.total;
-  P.desc = reinterpret_cast<kvc_segment_desc*>(lane.ptr + buf_bytes);
-  if (run_encode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
-  if (hipMemcpyAsync(host_out, lane.ptr, host_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
-      hipMemcpyAsync(host_desc, P.desc, desc_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
-      hipEventRecord(lane.last, s) != hipSuccess)
-    return KVC_E_HIP;
-  return ring_commit(ctx, roff, rsize, s);
+  return no_throw([&]() -> kvc_status {
+    if (!ctx) return KVC_E_ARG;
+    kvc_status st = kvc_validate_encode(layout, codec, page_ids, n_pages, host_bytes);
+    if (st != KVC_OK) return st;
+    if (n_pages == 0) return KVC_OK;
+    const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
+    const size_t desc_bytes = nseg * sizeof(kvc_segment_desc);
+    if (!pinned_range(host_out, host_bytes) || !pinned_range(host_desc, desc_bytes)) return KVC_E_ARG;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVC_E_HIP;
+    const Plan plan = make_plan(layout, codec, n_pages);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t buf_bytes = align_up(host_bytes, kAlign);
+    st = lane_reserve(ctx, 0, buf_bytes + desc_bytes);
+    if (st != KVC_OK) return st;
+    auto& lane = ctx->lane[0];
+    if (hipStreamWaitEvent(s, lane.last, 0) != hipSuccess) return KVC_E_HIP;   // the previous offload's copies
+    CallParams P{};
+    size_t roff = 0, rsize = 0;
+    st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize);
+    if (st != KVC_OK) return st;
+    P.buf = lane.ptr;
+    P.buf_bytes = host_bytes;
+    P.slot_region = plan.total;
+    P.desc = reinterpret_cast<kvc_segment_desc*>(lane.ptr + buf_bytes);
+    if (run_encode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
+    if (hipMemcpyAsync(host_out, lane.ptr, host_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(host_desc, P.desc, desc_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipEventRecord(lane.last, s) != hipSuccess)
+      return KVC_E_HIP;
+    return ring_commit(ctx, roff, rsize, s);
+  });
 }
 
 kvc_status kvc_restore_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec, const void* host_in,
                              size_t in_bytes, const int32_t* dst_page_ids, uint32_t n_pages, uint32_t layer_begin,
                              uint32_t layer_end, uint8_t* seg_status, void* const* layer_ready, void* stream) {
-  if (!ctx) return KVC_E_ARG;
-  kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
-  if (st != KVC_OK) return st;
-  if (layer_begin > layer_end || layer_end > layout->layers) return KVC_E_ARG;
-  if (n_pages == 0 || layer_begin == layer_end) return KVC_OK;
-  if (!pinned_range(host_in, in_bytes)) return KVC_E_ARG;
-  DeviceGuard g(ctx->device);
-  if (!g.ok) return KVC_E_HIP;
-  const Plan plan = make_plan(layout, codec, n_pages);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint32_t nl = layer_end - layer_begin;
-  // lazily created: the copy stream (default priority), the fork event and
-  // one copy-done event per layer of the widest restore so far
-  if (!ctx->copy_stream && hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking) != hipSuccess)
-    return KVC_E_HIP;
-  if (!ctx->fork && !(ctx->fork = new_event())) return KVC_E_HIP;
-  while (ctx->layer_copied.size() < nl) {
-    hipEvent_t e = new_event();
-    if (!e) return KVC_E_HIP;
-    ctx->layer_copied.push_back(e);
-  }
-  st = lane_reserve(ctx, 1, align_up(in_bytes, kAlign));
-  if (st != KVC_OK) return st;
-  auto& lane = ctx->lane[1];
-  CallParams P{};
-  size_t roff = 0, rsize = 0;
-  st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
-  if (st != KVC_OK) return st;
-  P.buf = lane.ptr;
-  P.buf_bytes = in_bytes;
-  P.slot_region = plan.total;
-  P.seg_status = seg_status;
-  // The copy stream starts after the caller's earlier work (which may have
-  // produced host_in) and after the previous restore's decodes have read the
-  // staging buffer.
-  const hipStream_t cs = ctx->copy_stream;
-  const uint8_t* hin = static_cast<const uint8_t*>(host_in);
-  if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(cs, ctx->fork, 0) != hipSuccess ||
-      hipStreamWaitEvent(cs, lane.last, 0) != hipSuccess)
-    return KVC_E_HIP;
-  if (in_bytes > plan.total &&
-      hipMemcpyAsync(lane.ptr + plan.total, hin + plan.total, in_bytes - plan.total, hipMemcpyHostToDevice, cs) !=
-          hipSuccess)
-    return KVC_E_HIP;
-  for (uint32_t l = layer_begin; l < layer_end; l++) {
-    const uint64_t a = plan.layer_off[l], b = l + 1 < layout->layers ? plan.layer_off[l + 1] : plan.total;
-    hipEvent_t copied = ctx->layer_copied[l - layer_begin];
-    if ((b > a && hipMemcpyAsync(lane.ptr + a, hin + a, b - a, hipMemcpyHostToDevice, cs) != hipSuccess) ||
-        hipEventRecord(copied, cs) != hipSuccess || hipStreamWaitEvent(s, copied, 0) != hipSuccess)
+  return no_throw([&]() -> kvc_status {
+    if (!ctx) return KVC_E_ARG;
+    kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
+    if (st != KVC_OK) return st;
+    if (layer_begin > layer_end || layer_end > layout->layers) return KVC_E_ARG;
+    if (n_pages == 0 || layer_begin == layer_end) return KVC_OK;
+    if (!pinned_range(host_in, in_bytes)) return KVC_E_ARG;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVC_E_HIP;
+    const Plan plan = make_plan(layout, codec, n_pages);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint32_t nl = layer_end - layer_begin;
+    // lazily created: the copy stream (default priority), the fork event and
+    // one copy-done event per layer of the widest restore so far
+    if (!ctx->copy_stream && hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking) != hipSuccess)
       return KVC_E_HIP;
-    P.seg_base = l * n_pages * 2;
-    if (run_decode(P, layout, plan, (uint64_t)n_pages * 2, s) != hipSuccess) return KVC_E_HIP;
-    if (layer_ready && layer_ready[l - layer_begin] &&
-        hipEventRecord(static_cast<hipEvent_t>(layer_ready[l - layer_begin]), s) != hipSuccess)
+    if (!ctx->fork && !(ctx->fork = new_event())) return KVC_E_HIP;
+    ctx->layer_copied.reserve(nl);
+    while (ctx->layer_copied.size() < nl) {
+      hipEvent_t e = new_event();
+      if (!e) return KVC_E_HIP;
+      ctx->layer_copied.push_back(e);
+    }
+    st = lane_reserve(ctx, 1, align_up(in_bytes, kAlign));
+    if (st != KVC_OK) return st;
+    auto& lane = ctx->lane[1];
+    CallParams P{};
+    size_t roff = 0, rsize = 0;
+    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+    if (st != KVC_OK) return st;
+    P.buf = lane.ptr;
+    P.buf_bytes = in_bytes;
+    P.slot_region = plan.total;
+    P.seg_status = seg_status;
+    // The copy stream starts after the caller's earlier work (which may have
+    // produced host_in) and after the previous restore's decodes have read the
+    // staging buffer.
+    const hipStream_t cs = ctx->copy_stream;
+    const uint8_t* hin = static_cast<const uint8_t*>(host_in);
+    if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(cs, ctx->fork, 0) != hipSuccess ||
+        hipStreamWaitEvent(cs, lane.last, 0) != hipSuccess)
       return KVC_E_HIP;
-  }
-  if (hipEventRecord(lane.last, s) != hipSuccess) return KVC_E_HIP;
-  return ring_commit(ctx, roff, rsize, s);
+    if (in_bytes > plan.total &&
+        hipMemcpyAsync(lane.ptr + plan.total, hin + plan.total, in_bytes - plan.total, hipMemcpyHostToDevice, cs) !=
+            hipSuccess)
+      return KVC_E_HIP;
+    for (uint32_t l = layer_begin; l < layer_end; l++) {
+      const uint64_t a = plan.layer_off[l], b = l + 1 < layout->layers ? plan.layer_off[l + 1] : plan.total;
+      hipEvent_t copied = ctx->layer_copied[l - layer_begin];
+      if ((b > a && hipMemcpyAsync(lane.ptr + a, hin + a, b - a, hipMemcpyHostToDevice, cs) != hipSuccess) ||
+          hipEventRecord(copied, cs) != hipSuccess || hipStreamWaitEvent(s, copied, 0) != hipSuccess)
+        return KVC_E_HIP;
+      P.seg_base = l * n_pages * 2;
+      if (run_decode(P, layout, plan, (uint64_t)n_pages * 2, s) != hipSuccess) return KVC_E_HIP;
+      if (layer_ready && layer_ready[l - layer_begin] &&
+          hipEventRecord(static_cast<hipEvent_t>(layer_ready[l - layer_begin]), s) != hipSuccess)
+        return KVC_E_HIP;
+    }
+    if (hipEventRecord(lane.last, s) != hipSuccess) return KVC_E_HIP;
+    return ring_commit(ctx, roff, rsize, s);
+  });
 }
 
 }  // extern "C"

@@ -40,6 +40,19 @@ def test_header_constants_match_binding():
     assert int(re.search(r"KVC_FLAG_CRC32 = (\d+)", hdr).group(1)) == kvc.KVC_FLAG_CRC32 == O.FLAG_CRC32
 
 
+def test_status_codes_match_header():
+    """Every kvc_status value of the header is the binding's, with its own
+    message; KVC_E_NOMEM is what a failed host allocation returns instead of
+    an exception crossing the C ABI."""
+    hdr = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    enum = hdr[hdr.index("typedef enum {\n  KVC_OK"):hdr.index("} kvc_status;")]
+    values = {k: int(v) for k, v in re.findall(r"(KVC_[A-Z_]+) = (\d+)", enum)}
+    assert values == {k: getattr(kvc, k) for k in values} and len(values) == 9
+    msgs = {kvc.status_string(v) for v in values.values()}
+    assert len(msgs) == 9 and "unknown status" not in msgs
+    assert kvc.status_string(kvc.KVC_E_NOMEM) == "host memory exhausted"
+
+
 FAKE = 1 << 40          # aligned fake device addresses: validation never dereferences them
 
 
