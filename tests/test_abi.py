@@ -193,3 +193,14 @@ def test_plan_int8_records_qwen3_row():
     slot, _, bpt = kvc.kvc_plan(lay, kvc.Codec("INT8_ROWS", "INT8_ROWS"), 1)
     assert slot == 2 * ((128 + 16 * 1152 + 255) // 256 * 256)
     assert bpt == -(-slot // 16)
+
+
+def test_create_checks_before_touching_a_device():
+    """kvc_create rejects a missing out pointer and a workspace budget too
+    small for its tables before any HIP call; kvc_destroy(NULL) is a no-op."""
+    L = kvc.lib()
+    h = ctypes.c_void_p(1)
+    assert L.kvc_create(None, 0, 0) == kvc.KVC_E_ARG
+    assert L.kvc_create(ctypes.byref(h), 0, 4096) == kvc.KVC_E_BUDGET
+    assert h.value is None                              # *out cleared on failure
+    assert L.kvc_destroy(None) == kvc.KVC_OK
