@@ -50,6 +50,7 @@ __device__ __forceinline__ AnsEnc ans_enc_entry(uint32_t f, uint32_t cum, const 
 // of one coded plane (p.stage_bytes: its 16-byte header, model, lengths and
 // streams, at most n + 16 bytes).
 constexpr uint32_t kAnsHiCopies = 16, kAnsLoCopies = 4;
+constexpr uint32_t kAnsHistAhead = 8;                    // histogram pass: source chunks in flight per lane
 constexpr uint32_t kAnsHistBytes = 4 * 256 * (kAnsHiCopies + kAnsLoCopies);
 constexpr uint32_t kAnsEncBytes = 2 * 256 * sizeof(AnsEnc);
 inline uint32_t ans_encode_lds(uint32_t stage_bytes) {
@@ -237,15 +238,28 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
   // histograms of both planes
   for (uint32_t u = lane; u < kAnsHistBytes / 16; u += 64) reinterpret_cast<uint4*>(s_dyn)[u] = make_uint4(0, 0, 0, 0);
   __syncthreads();
-  uint4 nw = lane < chunks ? ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, lane, D))) : make_uint4(0, 0, 0, 0);
-  for (uint32_t c = lane; c < chunks; c += kAnsStreams) {
-    const uint32_t a[4] = {nw.x, nw.y, nw.z, nw.w};
-    if (c + kAnsStreams < chunks) nw = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, c + kAnsStreams, D)));
+  // kAnsHistAhead chunks per lane in flight: with one wave per segment and
+  // few waves per CU, a single outstanding load per lane leaves this phase
+  // bound by load latency
+  uint4 nw[kAnsHistAhead];
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const uint32_t v = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      atomicAdd(&s_hist_lo[(v & 0xFF) * kAnsLoCopies + (lane & (kAnsLoCopies - 1))], 1u);
-      atomicAdd(&s_hist_hi[(v >> 8) * kAnsHiCopies + (lane & (kAnsHiCopies - 1))], 1u);
+  for (uint32_t q = 0; q < kAnsHistAhead; q++) {
+    const uint32_t c = lane + q * kAnsStreams;
+    nw[q] = c < chunks ? ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, c, D))) : make_uint4(0, 0, 0, 0);
+  }
+  for (uint32_t c0 = lane; c0 < chunks; c0 += kAnsHistAhead * kAnsStreams) {
+#pragma unroll
+    for (uint32_t q = 0; q < kAnsHistAhead; q++) {
+      const uint32_t c = c0 + q * kAnsStreams, cn = c + kAnsHistAhead * kAnsStreams;
+      if (c >= chunks) break;
+      const uint32_t a[4] = {nw[q].x, nw[q].y, nw[q].z, nw[q].w};
+      if (cn < chunks) nw[q] = ld_global16(byte_at(s.src, 2 * ans_chunk_off(s, cn, D)));
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const uint32_t v = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        atomicAdd(&s_hist_lo[(v & 0xFF) * kAnsLoCopies + (lane & (kAnsLoCopies - 1))], 1u);
+        atomicAdd(&s_hist_hi[(v >> 8) * kAnsHiCopies + (lane & (kAnsHiCopies - 1))], 1u);
+      }
     }
   }
   __syncthreads();
