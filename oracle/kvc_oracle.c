@@ -417,11 +417,12 @@ static void enc_int8(const float *x, int d, float s, uint8_t *codes) {
 }
 
 /* [OKV-SF "FP8 and TurboQuant"] V: per-vector uniform b-bit quantization with
- * FP16 minimum and scale.  sigma = RN(RN(max - min) / (2^b - 1)); both are
- * stored as FP16 and the codes are taken against the stored values:
- * code = clamp(RNE(RN(x - m_h) * (1/sigma_h)), 0, 2^b - 1), where the product
- * uses the FP32 reciprocal RN(1/sigma_h) and is rounded once, to an integer.
- * sigma_h == 0 gives all-zero codes. */
+ * an FP16 minimum and an FP16 scale.  sigma = RN(RN(max - min) / (2^b - 1));
+ * both are stored as FP16, and the codes are taken against the stored values
+ * so that encoder and decoder agree:
+ *   code = clamp(RNE(RN(RN(x - m_h) / sigma_h)), 0, 2^b - 1),
+ * the binary32 quotient rounded once to binary32 and then to the nearest
+ * integer, ties to even.  sigma_h == 0 gives all-zero codes. */
 static int enc_uniform(const float *x, int d, int bits, uint8_t *codes, uint8_t *meta) {
   int top = (1 << bits) - 1;
   float mn = x[0], mx = x[0];
@@ -441,13 +442,12 @@ static int enc_uniform(const float *x, int d, int bits, uint8_t *codes, uint8_t 
   if (!isfinite(mhf) || !isfinite(shf)) return 1;
   memset(codes, 0, (size_t)(bits * d / 8));
   if (shf == 0.0f) return 0;
-  float y = 1.0f / shf;
   for (int i = 0; i < d; i++) {
     float dd = x[i] - mhf;
-    double p = (double)dd * (double)y;        /* exact: 24 x 24 bits */
-    double c = rint(p);
-    if (c < 0.0) c = 0.0;
-    if (c > (double)top) c = (double)top;
+    float q = dd / shf;
+    float c = rintf(q);
+    if (c < 0.0f) c = 0.0f;
+    if (c > (float)top) c = (float)top;
     put_code(codes, i, bits, (unsigned)c);
   }
   return 0;

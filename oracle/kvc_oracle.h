@@ -40,8 +40,10 @@
  * operation order chosen here (normalise by RN(1/n) with the FP32 norm,
  * pairwise sum-of-squares tree, WHT stages in ascending span, decode
  * g = RN(n_h / RN(RN(sqrt(q)) * RN(sqrt(D))))); the pages fix only the
- * steps, so only the invariants above pin them.  Likewise the uniform
- * codec's single rounding of RN(x - m_h) * RN(1/sigma_h).  The ANS16
+ * steps, so only the invariants above pin them.  The uniform codec's
+ * codes are the plain binary32 quotient RN(RN(x - m_h) / sigma_h) rounded
+ * to the nearest integer, pinned against an exact-rational construction of
+ * that definition and the tie cases it decides.  The ANS16
  * payload bytes follow this library's own format (the pages name nvCOMP's
  * ANS without giving its format): its pins fix what any such coder must
  * satisfy (lossless, sizes near the entropy, exact-length checks), not the

@@ -326,6 +326,84 @@ def test_segment_gate(oracle, codec):
             np.testing.assert_array_equal(oracle.decode_segment(slot, buf, oracle.BF16, 128, 16), v)
 
 
+# The FP16 metadata rule [OKV-SF "FP8 and TurboQuant": the TurboQuant norm,
+# the uniform minimum and the uniform scale are stored as FP16;
+# "Ownership, storage and GDS": a segment the codec cannot represent stays
+# raw]: a norm, minimum or scale that rounds past the FP16 range (|v| >=
+# 65520 rounds to infinity) sends the segment raw, bit-exactly.
+# BF16 vectors with exactly computed squared norms: every square and partial
+# sum below is a multiple of 256 under 2^32, so any summation order is exact.
+OVERFLOW_TQ_BF16 = {
+    # squared norm 65520^2: RN(sqrt) = 65520, FP16 -> inf: raw
+    "norm_65520": ([65280.0, 5600.0, 160.0, 80.0], True),
+    # 65520^2 - 256: sqrt = 65519.99805 rounds (just below the binary32
+    # midpoint) to 65519.996, FP16 65504: coded
+    "norm_65520_minus_256": ([65280.0, 5600.0, 160.0, 64.0, 32.0, 32.0], False),
+    # a norm of about 65522.5: raw; about 65519.8: coded
+    "norm_65522": ([65280.0, 5632.0], True),
+    "norm_65519": ([65280.0, 5600.0], False),
+}
+
+
+def _raw_roundtrip(oracle, vec, dtype, codec, raw):
+    n_vec, d = vec.shape
+    slot, st, spill = oracle.encode_segment(vec, dtype, codec, spill_offset=1 << 16)
+    assert (st == oracle.SEG_RAW_DATA) == raw
+    if raw:
+        assert slot[1] == oracle.RAW and slot[2] == 2
+        np.testing.assert_array_equal(spill.view(np.uint16), vec.ravel())
+        buf = np.zeros((1 << 16) + spill.size, np.uint8)
+        buf[1 << 16:] = spill
+        np.testing.assert_array_equal(oracle.decode_segment(slot, buf, dtype, d, n_vec), vec)
+    return slot
+
+
+@pytest.mark.parametrize("case", sorted(OVERFLOW_TQ_BF16))
+@pytest.mark.parametrize("codec", ["TQ3", "TQ4"])
+def test_tq_norm_fp16_overflow_goes_raw(oracle, case, codec):
+    vals, raw = OVERFLOW_TQ_BF16[case]
+    vec = np.zeros((16, 128), np.uint16)
+    vec[7, :len(vals)] = _bits(vals, oracle.BF16)
+    slot = _raw_roundtrip(oracle, vec, oracle.BF16, getattr(oracle, codec), raw)
+    if not raw:
+        bits = 3 if codec == "TQ3" else 4
+        meta = slot[32 + 16 * bits * 16:32 + 16 * (bits * 16 + 2)].view(np.uint16)
+        assert meta[7] == 0x7BFF                         # FP16 65504
+
+
+def test_tq_norm_fp16_overflow_fp16_source(oracle):
+    """Two FP16 maxima give a norm of 92,636: raw; one gives 65,504: coded."""
+    vec = np.zeros((16, 64), np.uint16)
+    vec[3, 5] = 0x7BFF
+    _raw_roundtrip(oracle, vec, oracle.FP16, oracle.TQ4, False)
+    vec[3, 9] = 0xFBFF
+    _raw_roundtrip(oracle, vec, oracle.FP16, oracle.TQ4, True)
+
+
+@pytest.mark.parametrize("codec", ["UNIFORM3", "UNIFORM4"])
+def test_uniform_fp16_metadata_overflow_goes_raw(oracle, codec):
+    """BF16 sources: a minimum of -65536 (FP16 -inf) or a scale of
+    983040/(2^b - 1) >= 65520 sends the segment raw; a minimum of -65280 and
+    a scale of 974848/15 = 64989.9 (FP16 64992) stay coded.  The scale case
+    applies to 4-bit codes: 3-bit ones divide by 7, so both spans overflow."""
+    c = getattr(oracle, codec)
+    top = 7 if codec == "UNIFORM3" else 15
+    base = np.zeros((16, 32), np.uint16)
+    for lo, raw in ((-65280.0, False), (-65536.0, True)):
+        vec = base.copy()
+        vec[2, 3] = _bits([lo], oracle.BF16)[0]
+        _raw_roundtrip(oracle, vec, oracle.BF16, c, raw)
+    for hi in (974848.0, 983040.0):
+        vec = base.copy()
+        vec[9, 30] = _bits([hi], oracle.BF16)[0]
+        raw = float(np.float32(hi) / np.float32(top)) >= 65520
+        assert raw == (hi == 983040.0 or top == 7)
+        slot = _raw_roundtrip(oracle, vec, oracle.BF16, c, raw)
+        if not raw:
+            meta = slot[32 + 16 * 16:32 + 16 * 20].view(np.uint16).reshape(16, 2)
+            assert meta[9, 1] == np.float16(64992.0).view(np.uint16)
+
+
 def test_fp8_direct_roundtrip_exact_on_representable(oracle):
     codes = np.arange(256, dtype=np.uint8)
     vals = oracle.e4m3_to_f32(codes)
@@ -337,39 +415,156 @@ def test_fp8_direct_roundtrip_exact_on_representable(oracle):
 
 
 # ------------------------------------------------------------ uniform
+def _rn32(q):
+    """binary32 round-to-nearest-even of a rational (exact; no overflow)."""
+    from fractions import Fraction
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                   # now 2^e <= a < 2^(e+1)
+    ulp = Fraction(2) ** (max(e, -126) - 23)
+    n, r = divmod(a, ulp)
+    if r * 2 > ulp or (r * 2 == ulp and n % 2 == 1):
+        n += 1
+    return (n * ulp) if q > 0 else -(n * ulp)
+
+
+def _rne_int(q):
+    """nearest integer to a rational, ties to even"""
+    import math as _m
+    n = _m.floor(q)
+    r = q - n
+    return n + 1 if r * 2 > 1 or (r * 2 == 1 and n % 2 == 1) else n
+
+
+def _uniform_reference_codes(xs, bits):
+    """The uniform codec's codes written from its definition with exact
+    rationals: m = min, M = max (values, a zero extreme +0),
+    sigma = RN(RN(M - m) / (2^b - 1)), m_h = FP16(m), sigma_h = FP16(sigma),
+    code = clamp(RNE(RN(RN(x - m_h) / sigma_h)), 0, 2^b - 1)."""
+    from fractions import Fraction
+    top = (1 << bits) - 1
+    m, M = Fraction(float(xs.min())), Fraction(float(xs.max()))
+    sigma = _rn32(_rn32(M - m) / top)
+    mh = Fraction(float(np.float16(float(m))))             # numpy: RNE to FP16
+    sh = Fraction(float(np.float16(float(sigma))))
+    codes = []
+    for x in xs:
+        if sh == 0:
+            codes.append(0)
+            continue
+        d = _rn32(Fraction(float(x)) - mh)
+        codes.append(min(max(_rne_int(_rn32(d / sh)), 0), top))
+    return codes, mh, sh
+
+
+def _uniform_slot_codes(slot, v, d, bits, n_vec):
+    cb = bits * d // 8
+    blk = slot[32 + v * cb:32 + (v + 1) * cb]
+    stream = np.unpackbits(blk, bitorder="little")
+    return [int(sum(int(stream[bits * i + k]) << k for k in range(bits))) for i in range(d)]
+
+
 @pytest.mark.parametrize("bits", [3, 4])
-def test_uniform_nearest_level(oracle, bits):
-    """Brute force: every code is the nearest level m_h + k*sigma_h of the
-    stored FP16 grid (clamped to the code range), ties to even k."""
+def test_uniform_codes_are_the_rounded_quotient(oracle, bits):
+    """Every code against the definition built with exact rationals: the
+    FP16 minimum and scale, the binary32 quotient RN(RN(x - m_h)/sigma_h)
+    and its nearest integer, ties to even; the decode lies within half a step
+    of the source."""
     rng = np.random.default_rng(8)
     codec = oracle.UNIFORM3 if bits == 3 else oracle.UNIFORM4
+    top = (1 << bits) - 1
     x = rng.standard_normal((16, 32)).astype(np.float32) * 3
     vec = _bits(x, oracle.BF16)
     xs = oracle.src_to_f32(vec, oracle.BF16)
     slot, st, _ = oracle.encode_segment(vec, oracle.BF16, codec)
     assert st == oracle.SEG_ENCODED
     cb = bits * 32 // 8
-    top = (1 << bits) - 1
     meta = slot[32 + 16 * cb:32 + 16 * (cb + 4)].view(np.uint16).reshape(16, 2)
     for v in range(16):
-        m = float(oracle.f16_to_f32(meta[v, 0]))
-        sg = float(oracle.f16_to_f32(meta[v, 1]))
-        # FP16 min and scale: sigma = RN(RN(max - min) / (2^b - 1))
-        assert meta[v, 0] == oracle.f32_to_f16(xs[v].min())
-        assert meta[v, 1] == oracle.f32_to_f16((xs[v].max() - xs[v].min()) / np.float32(top))
-        blk = slot[32 + v * cb:32 + (v + 1) * cb]
-        stream = np.unpackbits(blk, bitorder="little")
-        codes = [int(sum(stream[bits * i + k] << k for k in range(bits))) for i in range(32)]
-        y = np.float32(1) / np.float32(sg)
-        for i in range(32):
-            t = float(np.float32(xs[v, i] - np.float32(m))) * float(y)   # exact in double
-            dist = [abs(t - k) for k in range(top + 1)]
-            best = min(dist)
-            cands = [k for k in range(top + 1) if dist[k] == best]
-            assert codes[i] in cands and (len(cands) == 1 or codes[i] % 2 == 0)
+        ref, mh, sh = _uniform_reference_codes(xs[v], bits)
+        assert float(np.ravel(oracle.f16_to_f32(meta[v, 0]))[0]) == float(mh)
+        assert float(np.ravel(oracle.f16_to_f32(meta[v, 1]))[0]) == float(sh)
+        assert _uniform_slot_codes(slot, v, 32, bits, 16) == ref
         dec = oracle.src_to_f32(oracle.decode_segment(slot, None, oracle.BF16, 32, 16)[v], oracle.BF16)
-        assert np.all(np.abs(dec - xs[v]) <= sg / 2 * 1.001 + abs(m - xs[v].min()) +
+        assert np.all(np.abs(dec - xs[v]) <= float(sh) / 2 * 1.001 + abs(float(mh) - xs[v].min()) +
                       np.abs(dec) * 2.0 ** -8)
+    assert top in (7, 15)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_uniform_quotient_ties_go_to_even(oracle, bits):
+    """Half-integer quotients decide the tie rule and the division: with
+    minimum 0 and maximum 3*(2^b - 1), sigma_h = 3, and x = 1.5, 4.5, 7.5, ...
+    give the exact quotients 0.5, 1.5, 2.5, ..., whose codes are the even
+    neighbours 0, 2, 2, 4, 4, ...  Multiplying by the rounded reciprocal
+    RN(1/3) > 1/3 instead would push every such quotient above the tie
+    (codes 1, 2, 3, 4, 5, ...).  Both orders of x near the ties are also
+    checked against the exact-rational definition."""
+    codec = oracle.UNIFORM3 if bits == 3 else oracle.UNIFORM4
+    top = (1 << bits) - 1
+    xs = np.zeros(32, np.float32)
+    xs[1] = 3.0 * top
+    ties = [1.5 + 3.0 * k for k in range(top)]
+    xs[2:2 + top] = ties
+    # neighbours of the ties, one BF16 step either side
+    nb = []
+    for t in ties[:7]:
+        b = int(np.float32(t).view(np.uint32)) >> 16
+        nb += [float(np.uint32((b + 1) << 16).view(np.float32)), float(np.uint32((b - 1) << 16).view(np.float32))]
+    xs[2 + top:2 + top + len(nb)] = nb[:32 - 2 - top]
+    vec = np.tile(_bits(xs[None, :], oracle.BF16), (16, 1))
+    xs = oracle.src_to_f32(vec, oracle.BF16)[0]
+    slot, st, _ = oracle.encode_segment(vec, oracle.BF16, codec)
+    assert st == oracle.SEG_ENCODED
+    codes = _uniform_slot_codes(slot, 0, 32, bits, 16)
+    ref, mh, sh = _uniform_reference_codes(xs, bits)
+    assert float(mh) == 0.0 and float(sh) == 3.0
+    assert codes == ref
+    assert codes[2:2 + top] == [k + (k & 1) for k in range(top)]   # 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, ...
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_uniform_codes_random_scales_near_ties(oracle, bits):
+    """FP16 vectors over many scales whose elements include every source
+    value (up to a cap) at which the quotient rule differs from the two
+    reciprocal readings -- RNE(RN(d * RN(1/sigma_h))) and the exact product
+    d * RN(1/sigma_h) rounded once -- plus values next to the tie points
+    m_h + (k + 1/2) sigma_h: every code against the exact-rational
+    definition."""
+    rng = np.random.default_rng(21)
+    codec = oracle.UNIFORM3 if bits == 3 else oracle.UNIFORM4
+    top = (1 << bits) - 1
+    all_h = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    all_h = np.concatenate([-all_h[1:], all_h])
+    vecs, separating = [], 0
+    for v in range(16):
+        lo = np.float32(np.float16(rng.uniform(-4, 4)))
+        hi = np.float32(np.float16(lo + rng.uniform(0.05, 60)))
+        mh = np.float32(np.float16(lo))
+        sig = np.float32(np.float16((hi - lo) / np.float32(top)))
+        y = np.float32(1) / sig
+        xs = all_h[(all_h > lo) & (all_h < hi)]
+        d = (xs - mh).astype(np.float32)
+        q = np.rint(d / sig)
+        other = (q != np.rint((d * y).astype(np.float32))) | (q != np.rint(d.astype(np.float64) * float(y)))
+        pick = list(xs[other][:40])
+        separating += len(pick)
+        while len(pick) < 62:
+            k = int(rng.integers(0, top))
+            t = np.float16(mh + (k + 0.5) * sig)
+            pick.append(np.float32(np.uint16(int(t.view(np.uint16)) + int(rng.integers(-2, 3))).view(np.float16)))
+        vecs.append(np.clip(np.array([lo, hi] + pick[:62], np.float32), lo, hi))
+    assert separating >= 8                       # the readings are told apart
+    vec = np.stack(vecs).astype(np.float16).view(np.uint16)
+    xs = oracle.src_to_f32(vec, oracle.FP16)
+    slot, st, _ = oracle.encode_segment(vec, oracle.FP16, codec)
+    assert st == oracle.SEG_ENCODED
+    for v in range(16):
+        ref, _, _ = _uniform_reference_codes(xs[v], bits)
+        assert _uniform_slot_codes(slot, v, 64, bits, 16) == ref
 
 
 def test_uniform_sigma_rounds_to_binary32_then_fp16(oracle):
