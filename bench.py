@@ -78,36 +78,106 @@ def algorithmic_bytes(desc):
                desc["stored_len"].astype(np.int64).sum())
 
 
-def cpu_baseline(ks, vs, ids, H, T, D, prot, seed, pages_sample, threads):
-    """The CPU oracle on a bounded sample (pages_sample pages, all layers)."""
-    import numpy as np
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """Worker threads for the oracle's parallel leg: the CPUs this process
+    may run on, at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(w, out_gpu, threads, pages_parallel, pages_single):
+    """The CPU oracle, as it stands, on bounded samples of the workload's
+    pages (all layers, K and V, encode then decode): once on `threads`
+    threads over the first `pages_parallel` pages and once on one thread over
+    the first `pages_single`.  Outside any timed region, the parallel leg's
+    slots and decoded pages are compared with the GPU's (`out_gpu`: the GPU's
+    encoded buffer; w["dst"]: the pages the GPU decoded it into), segment by
+    segment: slot bytes identical, decoded values bit-identical (TurboQuant:
+    up to the sign of a zero)."""
     import torch
 
     from oracle import kvc_oracle as O
-    L = len(ks)
-    sample = ids[:pages_sample]
-    idx = torch.tensor(sorted(set(int(p) for p in sample)), dtype=torch.long, device=ks[0].device)
-    remap = {int(b): j for j, b in enumerate(idx.tolist())}
+    ks, vs, ids, H, T, D = w["ks"], w["vs"], w["ids"], w["H"], w["T"], w["D"]
+    L, prot, seed = len(ks), w["protected"], w["seed"]
+    protl = [1 if l in prot else 0 for l in range(L)]
 
     def u16(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
 
-    host = O.HostLayout(O.BF16, L, H, D, T, len(remap), T * H * D, H * D, D,
-                        [u16(t.index_select(0, idx)) for t in ks], [u16(t.index_select(0, idx)) for t in vs])
-    mapped = np.array([remap[int(p)] for p in sample], np.int32)
-    protl = [1 if l in prot else 0 for l in range(L)]
-    t0 = time.perf_counter()
-    buf, st, offs, total = O.encode_pages(host, O.TQ4, O.UNIFORM4, seed, mapped, protected=protl,
-                                          threads=threads)
-    t1 = time.perf_counter()
-    out = O.HostLayout(O.BF16, L, H, D, T, len(remap), T * H * D, H * D, D,
-                       [np.zeros_like(a) for a in host.k], [np.zeros_like(a) for a in host.v])
-    O.decode_pages(buf, out, O.TQ4, O.UNIFORM4, seed, mapped, protected=protl, threads=threads)
-    t2 = time.perf_counter()
-    orig = L * len(sample) * 2 * T * H * D * 2
-    return {"value": round(orig / (t2 - t0) / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(sample)} pages x {L} layers x K,V ({orig / 2**20:.0f} MiB of original KV), "
-                      f"encode {t1 - t0:.2f} s + decode {t2 - t1:.2f} s wall"}
+    def run(n_pages, nthreads):
+        sample = ids[:n_pages]
+        idx = torch.tensor(sorted(set(int(p) for p in sample)), dtype=torch.long, device=ks[0].device)
+        remap = {int(b): j for j, b in enumerate(idx.tolist())}
+        host = O.HostLayout(O.BF16, L, H, D, T, len(remap), T * H * D, H * D, D,
+                            [u16(t.index_select(0, idx)) for t in ks], [u16(t.index_select(0, idx)) for t in vs])
+        mapped = np.array([remap[int(p)] for p in sample], np.int32)
+        t0 = time.perf_counter()
+        buf, st, offs, total = O.encode_pages(host, O.TQ4, O.UNIFORM4, seed, mapped, protected=protl,
+                                              threads=nthreads)
+        t1 = time.perf_counter()
+        out = O.HostLayout(O.BF16, L, H, D, T, len(remap), T * H * D, H * D, D,
+                           [np.zeros_like(a) for a in host.k], [np.zeros_like(a) for a in host.v])
+        O.decode_pages(buf, out, O.TQ4, O.UNIFORM4, seed, mapped, protected=protl, threads=nthreads)
+        t2 = time.perf_counter()
+        orig = L * len(sample) * 2 * T * H * D * 2
+        return {"orig": orig, "enc_s": t1 - t0, "dec_s": t2 - t1, "buf": buf, "offs": offs, "out": out,
+                "idx": idx, "remap": remap, "sample": sample}
+
+    par = run(pages_parallel, threads)
+    one = run(pages_single, 1)
+
+    # parity of the parallel sample against the GPU's bytes and pages
+    n_all = len(ids)
+    offs_gpu, sizes, effs, _ = O.plan(L, H, D, T, O.TQ4, O.UNIFORM4, protl, n_all)
+    gbuf = out_gpu.cpu().numpy()
+    seg_all, seg_s = O.segment_list(L, n_all), O.segment_list(L, pages_parallel)
+    pos = {key: s for s, key in enumerate(seg_all)}
+    mism = 0
+    checked = 0
+    for s, (l, i, c) in enumerate(seg_s):
+        g = pos[(l, i, c)]
+        a = gbuf[offs_gpu[g]:offs_gpu[g] + sizes[g]]
+        b = par["buf"][par["offs"][s]:par["offs"][s] + sizes[g]]
+        bad = not np.array_equal(a, b)
+        checked += 1
+        mism += int(bad)
+    dst_k, dst_v = w["dst"]
+    idx = par["idx"]
+    for l in range(L):
+        for c, (gl, hl) in enumerate(((dst_k, par["out"].k), (dst_v, par["out"].v))):
+            got = u16(gl[l].index_select(0, idx)).reshape(len(idx), T * H, D)
+            want = hl[l].reshape(len(idx), T * H, D)
+            tq = c == 0 and not protl[l]
+            same = got == want
+            if tq:
+                same |= ((got & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)
+            mism += int((~same.reshape(len(idx), -1).all(1)).sum())
+    def rate(r):
+        return round(r["orig"] / (r["enc_s"] + r["dec_s"]) / 1e9, 4)
+    return {"value": rate(par), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{pages_parallel} pages x {L} layers x K,V ({par['orig'] / 2**20:.0f} MiB of original KV), "
+                      f"encode {par['enc_s']:.2f} s + decode {par['dec_s']:.2f} s wall on {threads} threads",
+            "single_thread": {"value": rate(one), "unit": "GB/s", "cores": 1,
+                              "sample": f"{pages_single} pages x {L} layers x K,V "
+                                        f"({one['orig'] / 2**20:.0f} MiB), encode {one['enc_s']:.2f} s + "
+                                        f"decode {one['dec_s']:.2f} s wall"},
+            "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+            "parity": {"segments": checked, "mismatches": mism,
+                       "checked": "slot bytes of every sampled segment and its decoded page, GPU vs oracle"}}
 
 
 DEFAULT_WORKLOAD = "tq4_u4_llama3"
@@ -239,7 +309,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-pages", type=int, default=1024)
+    ap.add_argument("--cpu-sample-pages", type=int, default=512,
+                    help="pages of the oracle's multi-threaded leg (all layers, K and V)")
+    ap.add_argument("--cpu-single-pages", type=int, default=256,
+                    help="pages of the oracle's single-thread leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="GIB",
                     help="only run a plain GIB-GiB device copy (byte-counter calibration)")
@@ -316,8 +389,9 @@ def main():
         step(k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    enc_all = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_all = [e[1].elapsed_time(e[2]) for e in evs]
+    enc_ms, dec_ms = float(np.mean(enc_all)), float(np.mean(dec_all))
     ms_per_step = wall * 1e3 / args.steps
 
     orig = L * n * 2 * T * H * D * 2
@@ -339,6 +413,10 @@ def main():
                    "pages": n, "pool_blocks": w["pool"], "original_bytes": orig, "crc32": bool(args.crc),
                    "replicas": len(reps), "parallelism": "none"},
         "encode_ms": round(enc_ms, 4), "decode_ms": round(dec_ms, 4),
+        "encode_ms_median": round(float(np.median(enc_all)), 4),
+        "decode_ms_median": round(float(np.median(dec_all)), 4),
+        "timing": "HIP events recorded on the launch stream around each launch; means (and medians) over "
+                  "the timed steps; rocprofv3 kernel-trace averages of the same launches are in profiles/",
         "encode_GBps_original": round(orig / enc_ms / 1e6, 1),
         "decode_GBps_original": round(orig / dec_ms / 1e6, 1),
         "encode_hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
@@ -353,10 +431,11 @@ def main():
         result["metric"] = "encode+decode GB/s of original KV and % of HBM peak"
     kvc.kvc_destroy(ctx)
     if default and not args.no_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
-        print(f"[bench] cpu baseline ({threads} threads)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w["ks"], w["vs"], w["ids"], H, T, D, w["protected"], w["seed"],
-                                              args.cpu_sample_pages, threads)
+        threads = host_threads()
+        print(f"[bench] cpu baseline ({threads} threads, then 1)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, w["out"], threads, args.cpu_sample_pages,
+                                              args.cpu_single_pages)
+        result["parity"] = result["cpu_baseline"]["parity"]
     print(json.dumps(result), flush=True)
 
 

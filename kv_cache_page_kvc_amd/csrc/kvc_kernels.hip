@@ -25,8 +25,7 @@
 // fmaf is used only where the fused single rounding is the defined result.
 // Data-dependent raw segments: codes are written speculatively, then the
 // workgroup OR-reduces the per-vector gate; a raw segment gets a header with
-// RAW_DATA and its bytes in the spill region (the encoded codes left in its
-// slot are ignored by decode).
+// RAW_DATA, a zeroed slot body and its bytes in the spill region.
 #include <hip/hip_runtime.h>
 
 #include "kvc_arch.h"
@@ -229,6 +228,20 @@ __device__ __forceinline__ float div_scaled(float x, float s, float r) {
 __device__ __forceinline__ float recip_f16val(float h) {
   const float y0 = __builtin_amdgcn_rcpf(h);
   return fmaf(fmaf(-h, y0, 1.0f), y0, y0);
+}
+
+// Uniform code of d = RN(x - m_h) against the FP16 scale s = sigma_h, as
+// the bits of RN(q + 1.5*2^23) with q = RN(d / s): for |q| < 2^22 these are
+// 0x4B400000 + RNE(q), and clamping them as integers to [0x4B400000,
+// 0x4B400000 + 2^b - 1] gives clamp(RNE(q), 0, 2^b - 1) for every q.  The
+// quotient comes from y = RN(1/s): q0 = RN(d*y), then one FMA residual step
+// RN(q0 + RN(d - q0*s)*y), which equals RN(d / s) for every positive finite
+// FP16 s and every d >= s/4 (checked over every pair of significands; for
+// smaller d both codes are 0).  With s == 0 (y == 0) q is 0 for finite d.
+__device__ __forceinline__ int uniform_code_bits(float d, float s, float y) {
+  const float q0 = d * y;
+  const float q = fmaf(fmaf(-q0, s, d), y, q0);
+  return __float_as_int(q + 12582912.0f);
 }
 
 // ------------------------------------------------------------------ addressing
@@ -548,17 +561,16 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
       uint32_t acc = 0;                  // sum over j of (MAGIC + code_j) << BITS*j
 #pragma unroll
       for (int j = 7; j >= 0; j--) {
-        // RN(d*y + 1.5*2^23) = 1.5*2^23 + RNE(d*y) while |d*y| < 2^22; the
-        // integer clamp maps every out-of-range result to 0 or TOP
-        const int t = __float_as_int(fmaf(x[8 * k + j] - mh, y, 12582912.0f));
+        const int t = uniform_code_bits(x[8 * k + j] - mh, sh, y);
         tor |= (uint32_t)t;
         acc = (acc << BITS) + (uint32_t)min(max(t, MAGIC), MAGIC + TOP);
       }
       store_codes<D, BITS>(slot, cv, k, ln.p, acc - magic_sum<BITS>(), 0);
     }
-    // For finite inputs every t lies in (2^22, 2^41) in magnitude (|d*y| is
-    // bounded by the FP16 range of d and by y <= 2^24), so bit 29 (exponent
-    // bit 6) of t is clear; a NaN source value makes t NaN, which sets it.
+    // For finite inputs every t lies in (2^22, 2^45) in magnitude (d is
+    // bounded by the FP16 range of the metadata and 1/sigma_h by 2^24), so
+    // bit 29 (exponent bit 6) of t is clear; a NaN source value makes t NaN,
+    // which sets it.
     bad |= (int)((group_or<LOGP>(tor) >> 29) & 1u);
     if (ln.p == 0) *byte_at(reinterpret_cast<uint32_t*>(slot), mv) = f16_bits(mh) | (f16_bits(sh) << 16);
   }
@@ -1001,9 +1013,18 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
     if (threadIdx.x == 0) write_desc(desc, slot_off, codec, crc_flag, KVC_SEG_ENCODED, D, s.n_vec, payload, 0, c);
     return;
   }
-  if (staged)
+  // the slot body: the staged image of a coded segment; a segment raw
+  // because of its data keeps only its header in the slot, and the rest of
+  // the slot is zero.  Codes written straight to an unstaged slot before the
+  // gate are overwritten: each wave first waits for its own stores to
+  // complete, and a barrier orders them before the zeroing stores.
+  if (any_bad && !staged) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (staged || any_bad)
     for (uint32_t u = 2 + threadIdx.x; u < slot_bytes / 16; u += NT)
-      st_stream16(s.slot + 16 * u, *reinterpret_cast<const uint4*>(s_stage + 16 * u));
+      st_stream16(s.slot + 16 * u, any_bad ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(s_stage + 16 * u));
   if (!any_bad) {
     const uint32_t c = crc ? crc32_written<NT>(s.slot + stored_at, payload, ct) : 0u;
     if (threadIdx.x == 0)

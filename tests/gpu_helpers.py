@@ -116,8 +116,8 @@ def oracle_encode(wl: Workload, codec_k, codec_v, seed, page_ids, fixed=None, pr
 def compare_encoded(gpu_buf: np.ndarray, gpu_desc, ora_buf, ora_status, offs, total, segments):
     """Per segment: status equal; slot bytes identical for encoded and
     policy-raw segments; for data-raw segments the header equal except the
-    spill offset, and the spilled bytes equal the source (from the oracle's
-    own spill copy).  The descriptor's flags and crc32 equal the header's."""
+    spill offset, the rest of the slot zero, and the spilled bytes equal the
+    source (from the oracle's own spill copy).  The descriptor's flags and crc32 equal the header's."""
     bad = []
     for s in segments:
         st = int(ora_status[s])
@@ -137,8 +137,8 @@ def compare_encoded(gpu_buf: np.ndarray, gpu_desc, ora_buf, ora_status, offs, to
                 bad.append((s, "spilled segment header"))
                 continue
             size = (offs[s + 1] if s + 1 < len(offs) else total) - o
-            if hdr_o[2] & O.FLAG_HEAP and gpu_buf[o + 32:o + size].any():
-                bad.append((s, "slot padding"))      # a header-only slot is zero after the header
+            if gpu_buf[o + 32:o + size].any():
+                bad.append((s, "slot body"))         # a header-only slot is zero after the header
             so_g = int(hdr_g[16:24].view(np.uint64)[0])
             so_o = int(hdr_o[16:24].view(np.uint64)[0])
             n = int(hdr_o[12:16].view(np.uint32)[0])

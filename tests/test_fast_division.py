@@ -87,3 +87,28 @@ def test_rans_reciprocal_division_exact():
         bad, cases = (int(v) for v in subprocess.run([exe], check=True, capture_output=True, text=True,
                                                      timeout=300).stdout.split())
     assert cases > 4096 * 65536 and bad == 0
+
+
+def test_uniform_quotient_code_exact():
+    """The uniform encoder's quotient RN(RN(x - m_h) / sigma_h) through
+    RN(1/sigma_h) and one FMA correction, then rounded to the nearest integer
+    through the bits of RN(q + 1.5 * 2^23) and clamped: identical to the
+    correctly rounded quotient over every pair of significands (which, by
+    scaling, covers every positive finite FP16 sigma_h and every d >= s/4),
+    and the full code identical to the definition for every FP16 sigma_h
+    around every half-integer tie point and the clamp, and zero below s/4."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        exe = os.path.join(d, "check")
+        subprocess.run([gcc, "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-o", exe,
+                        os.path.join(HERE, "uniform_quotient_check.c"), "-lm"], check=True)
+        env = dict(os.environ, OMP_NUM_THREADS=str(min(16, os.cpu_count() or 1)))
+        out = subprocess.run([exe], check=True, capture_output=True, text=True, env=env, timeout=600).stdout
+    res = {ln.split()[0]: (int(ln.split()[1]), int(ln.split()[2])) for ln in out.splitlines()}
+    assert res["pairs"] == (0, 1 << 33)
+    assert res["ties_7"][0] == 0 and res["ties_7"][1] == (0x7C00 - 1) * 8 * 2050
+    assert res["ties_15"][0] == 0 and res["ties_15"][1] == (0x7C00 - 1) * 16 * 2050
+    assert res["small"] == (0, 3 * ((1 << 23) + (1 << 20)))

@@ -2,8 +2,8 @@
 
 Bar: encoded bytes (codes, metadata, headers, padding) and segment statuses
 bit-exact for every codec; decoded values bit-exact for FP8, INT8, uniform
-and raw; TurboQuant decodes within 1e-3 absolute (and reported bit-equal up
-to the sign of zero).  Small cases cover every codec, head dim, dtype and
+and raw; TurboQuant decodes within 1e-3 absolute and bit-equal up to the
+sign of zero.  Small cases cover every codec, head dim, dtype and
 layout over several tiles and a ragged page count; the workload-sized cases
 run at full size in the launch configuration the benchmark times, checked
 on sampled segments.
@@ -45,10 +45,14 @@ def _check_decoded(dec_gpu: np.ndarray, dec_ora: np.ndarray, dt, lossy_tq: bool,
     if not lossy_tq:
         assert np.array_equal(dec_gpu, dec_ora), f"decode bits differ {where}"
         return
+    # TurboQuant: within the 1e-3 bound, and bit-equal -- both sides fix the
+    # same binary32 operation order -- except that a zero may carry either sign
     a = G.bits_to_f32(dec_gpu, dt).astype(np.float64)
     b = G.bits_to_f32(dec_ora, dt).astype(np.float64)
     err = np.abs(a - b).max()
     assert err <= TQ_TOL, f"TurboQuant decode error {err} {where}"
+    same = (dec_gpu == dec_ora) | (((dec_gpu & 0x7FFF) == 0) & ((dec_ora & 0x7FFF) == 0))
+    assert same.all(), f"TurboQuant decode bits differ at {int((~same).sum())} elements {where}"
 
 
 def _roundtrip_case(ctx, wl, ck, cv, seed, page_ids, protected=None, fixed=None, segments=None,
@@ -262,6 +266,90 @@ def test_gate_small(ctx):
             k = kind.get((l, i, c))
             expect_raw = k is not None and (fp8 or k in ("nan", "+inf", "-inf"))
             assert (gdesc[s]["status"] == kvc.KVC_SEG_RAW_DATA) == expect_raw, (s, codec, k)
+
+
+def _bf16_row(vals):
+    x = np.zeros(128, np.float32)
+    x[:len(vals)] = vals
+    return torch.from_numpy(O.f32_to_bf16(x).view(np.int16))
+
+
+def test_fp16_metadata_overflow_goes_raw(ctx):
+    """The FP16 metadata rule: a TurboQuant norm of exactly 65520 (FP16 inf)
+    or above, a uniform minimum of -65536 or a uniform scale >= 65520 sends
+    the segment raw; norms of 65519.996 and 65519.8, a minimum of -65280 and a
+    scale of 64989.9 stay coded.  The exact set of data-raw segments, every
+    slot byte and a bit-exact raw round trip against the oracle."""
+    print("[case] FP16 metadata overflow", flush=True)
+    L, H, D, T, pool = 2, 8, 128, 16, 10
+    for ck, cv in (("TQ4", "UNIFORM4"), ("TQ3", "UNIFORM4")):
+        wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 31)
+        k_cases = [([65280.0, 5600.0, 160.0, 80.0], True), ([65280.0, 5600.0, 160.0, 64.0, 32.0, 32.0], False),
+                   ([65280.0, 5632.0], True), ([65280.0, 5600.0], False)]
+        v_cases = [({3: -65280.0}, False), ({3: -65536.0}, True), ({100: 974848.0}, False),
+                   ({100: 983040.0}, True)]
+        expect = {}
+        for j, (vals, raw) in enumerate(k_cases):
+            wl.k[j % L][j + 1, 5, 3] = _bf16_row(vals).cuda().view(torch.bfloat16)
+            expect[(j % L, j + 1, 0)] = raw
+        for j, (pos, raw) in enumerate(v_cases):
+            row = O.src_to_f32(G.u16(wl.v[j % L][j + 5, 9, 1]), O.BF16).copy()
+            for i, val in pos.items():
+                row[i] = val
+            wl.v[j % L][j + 5, 9, 1] = torch.from_numpy(O.f32_to_bf16(row).view(np.int16)).cuda().view(torch.bfloat16)
+            expect[(j % L, j + 5, 1)] = raw
+        ids = np.arange(pool, dtype=np.int32)
+        ora_st, gdesc = _roundtrip_case(ctx, wl, ck, cv, 3, ids, dst_ids=inputs.permutation(pool, 2),
+                                        spill_bytes=L * pool * 2 * (H * T * D * 2))
+        for s, (l, i, c) in enumerate(G.segments_of(L, pool)):
+            raw = expect.get((l, int(ids[i]), c), False)
+            assert (gdesc[s]["status"] == kvc.KVC_SEG_RAW_DATA) == raw, (s, l, i, c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_uniform_quotient_ties(ctx, dtype):
+    """Uniform codes at the tie points of the quotient rule: vectors with
+    minimum 0 and maximum 3 * (2^b - 1) (sigma_h = 3) whose elements are the
+    half-integer multiples 1.5, 4.5, ... of the scale and their neighbours,
+    so that the quotient RN(d / sigma_h) decides each code (the rounded
+    reciprocal would give other codes); every slot byte against the oracle."""
+    print(f"[case] uniform quotient ties {dtype}", flush=True)
+    L, H, D, T, pool = 1, 4, 32, 16, 4
+    for bits in (3, 4):
+        codec = "UNIFORM3" if bits == 3 else "UNIFORM4"
+        top = (1 << bits) - 1
+        wl = G.Workload(L, H, D, T, pool, dtype, "separate", 40 + bits)
+        conv = O.f32_to_bf16 if dtype == "bf16" else O.f32_to_f16
+        dt = O.BF16 if dtype == "bf16" else O.FP16
+        for b in range(pool):
+            x = np.zeros((T, H, D), np.float32)
+            x[..., 1] = 3.0 * top
+            ties = np.array([1.5 + 3.0 * k for k in range(top)], np.float32)
+            tb = conv(ties).astype(np.int32)
+            step = (0, 1, -1, 2)[b]                       # units in the last place off the ties
+            x[..., 2:2 + top] = O.src_to_f32((tb + step).astype(np.uint16), dt)
+            for t in (wl.k[0], wl.v[0]):
+                t[b] = torch.from_numpy(conv(x.ravel()).view(np.int16).reshape(T, H, D)).cuda().view(t.dtype)
+        ids = np.arange(pool, dtype=np.int32)
+        _roundtrip_case(ctx, wl, codec, codec, 0, ids)
+
+
+def test_raw_data_unstaged_slot(ctx):
+    """Segments of 40 heads (160 KiB, slots written straight to memory, not
+    staged in LDS) that fall back to raw: the slot keeps only its header and
+    is zero after it, the bytes go to the spill region, as in the oracle."""
+    print("[case] raw data unstaged slot", flush=True)
+    L, H, D, T, pool = 2, 40, 128, 16, 4
+    wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 17)
+    wl.k[0][1, 3, 7, 9] = float("nan")
+    wl.v[1][2, 15, 39, 127] = float("inf")
+    wl.v[0][3, 0, 0, 0] = 1000.0
+    ids = np.arange(pool, dtype=np.int32)
+    for ck, cv in (("TQ4", "UNIFORM4"), ("INT8", "FP8_DYNAMIC")):
+        ora_st, gdesc = _roundtrip_case(ctx, wl, ck, cv, 5, ids, spill_bytes=4 * (H * T * D * 2))
+        raw = {(0, 1, 0), (1, 2, 1)} | ({(0, 3, 1)} if cv == "FP8_DYNAMIC" else set())
+        for s, (l, i, c) in enumerate(G.segments_of(L, pool)):
+            assert (gdesc[s]["status"] == kvc.KVC_SEG_RAW_DATA) == ((l, i, c) in raw), (s, l, i, c)
 
 
 def test_spill_capacity_exhausted(ctx):
