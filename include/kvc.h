@@ -322,6 +322,31 @@ kvc_status kvc_restore_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_c
                              uint32_t layer_begin, uint32_t layer_end,
                              uint8_t *seg_status, void *const *layer_ready, void *stream);
 
+/* Allocation-free variant of kvc_encode_pages, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  No context: the per-call side table,
+ * page ids and spill cursor live in a fixed device array of this library,
+ * one copy per GPU held until the process ends (about 320 KiB: the codec
+ * tables, a 256-byte cursor, 2 x 256 side-table entries of 32 bytes and
+ * 65,536 page ids).  The call allocates nothing: no hipMalloc, hipFree, host
+ * heap or pinned memory.  The first call on a device looks the array up and
+ * copies the codec tables into it (a synchronous copy): make that call
+ * outside any graph capture.
+ * Arguments, output bytes, descriptors and errors are those of
+ * kvc_encode_pages on the current HIP device, plus KVC_E_BUDGET when
+ * layout->layers > 256 or n_pages > 65536.  The side table and the zeroed
+ * spill cursor are copied from the call's stack with a pageable copy, which
+ * HIP completes before returning (it may wait for earlier work on the
+ * stream); page_ids (host) is copied the same way when it is pageable, and
+ * must stay unchanged until the stream passes this call when it is pinned.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams, or from several host threads) race and give
+ * undefined results; calls ordered on one stream are safe. */
+kvc_status kvc_encode_pages_noalloc(const kvc_layout *layout, const kvc_codec *codec,
+                                    const int32_t *page_ids, uint32_t n_pages,
+                                    void *out, size_t out_bytes, kvc_segment_desc *desc,
+                                    void *stream);
+
 /* Short text for a status code (static storage). */
 const char *kvc_status_string(kvc_status s);
 

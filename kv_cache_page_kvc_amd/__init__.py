@@ -79,7 +79,7 @@ assert DESC_DTYPE.itemsize == ctypes.sizeof(kvc_segment_desc) == 32
 
 EXPORTS = ["kvc_create", "kvc_destroy", "kvc_plan", "kvc_validate_encode", "kvc_validate_decode",
            "kvc_encode_pages", "kvc_decode_pages", "kvc_decode_layers", "kvc_offload_pages",
-           "kvc_restore_pages", "kvc_status_string"]
+           "kvc_restore_pages", "kvc_encode_pages_noalloc", "kvc_status_string"]
 
 _lib = None
 
@@ -122,6 +122,9 @@ def lib():
         L.kvc_restore_pages.argtypes = [P, ctypes.POINTER(kvc_layout), ctypes.POINTER(kvc_codec), P,
                                         ctypes.c_size_t, P, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                         P, P, P]
+        L.kvc_encode_pages_noalloc.restype = st
+        L.kvc_encode_pages_noalloc.argtypes = [ctypes.POINTER(kvc_layout), ctypes.POINTER(kvc_codec), P,
+                                               ctypes.c_uint32, P, ctypes.c_size_t, P, P]
         L.kvc_status_string.restype = ctypes.c_char_p
         L.kvc_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -246,6 +249,14 @@ def kvc_encode_pages(ctx, layout: Layout, codec: Codec, page_ids, out_ptr: int, 
     arr, ptr = _pages(page_ids)
     _check(lib().kvc_encode_pages(ctx, ctypes.byref(layout.c), ctypes.byref(codec.c), ptr, arr.size,
                                   out_ptr, out_bytes, desc_ptr, stream or None), "kvc_encode_pages")
+
+
+def kvc_encode_pages_noalloc(layout: Layout, codec: Codec, page_ids, out_ptr: int, out_bytes: int,
+                             desc_ptr: int, stream: int = 0):
+    arr, ptr = _pages(page_ids)
+    _check(lib().kvc_encode_pages_noalloc(ctypes.byref(layout.c), ctypes.byref(codec.c), ptr, arr.size,
+                                          out_ptr, out_bytes, desc_ptr, stream or None),
+           "kvc_encode_pages_noalloc")
 
 
 def kvc_decode_pages(ctx, layout: Layout, codec: Codec, in_ptr: int, in_bytes: int, dst_page_ids,

@@ -24,6 +24,7 @@
 #include <cstring>
 #include <limits>
 #include <memory>
+#include <mutex>
 #include <vector>
 
 #include "kvc.h"
@@ -120,10 +121,10 @@ double cell_mass(double lo, double hi) {
   if (hi <= 0) return upper(-hi) - upper(-lo);
   return 1.0 - upper(hi) - upper(-lo);
 }
-void lloyd_max(int n, std::vector<double>& lev) {
-  lev.resize(n);
+constexpr int kMaxLevels = 16;
+void lloyd_max(int n, double* lev) {           // n <= kMaxLevels
   for (int k = 0; k < n; k++) lev[k] = -3.0 + 6.0 * (k + 0.5) / n;
-  std::vector<double> b(n + 1);
+  double b[kMaxLevels + 1];
   for (int it = 0; it < 4000000; it++) {
     b[0] = -INFINITY;
     b[n] = INFINITY;
@@ -184,7 +185,7 @@ void build_tables(Tables& t) {
   }
   for (int which = 0; which < 2; which++) {
     const int bits = which ? 4 : 3, n = 1 << bits;
-    std::vector<double> lev;
+    double lev[kMaxLevels];
     lloyd_max(n, lev);
     float thr[15];
     for (int k = 0; k < n; k++) t.centroids[which][k] = (float)lev[k];
@@ -270,10 +271,14 @@ kvc_status check_codec(const kvc_layout* L, const kvc_codec* c) {
   return KVC_OK;
 }
 
+// The slot plan of a call: per layer its slot offset and, per component,
+// its slot size and effective codec.  The per-layer arrays live in storage
+// the caller provides (HeapPlan: vectors; the allocation-free entry point:
+// fixed arrays on its stack).
 struct Plan {
-  std::vector<uint64_t> layer_off;
-  std::vector<uint32_t> slot[2];
-  std::vector<uint8_t> eff[2];
+  uint64_t* layer_off = nullptr;
+  uint32_t* slot[2] = {nullptr, nullptr};
+  uint8_t* eff[2] = {nullptr, nullptr};
   uint64_t total = 0;
   uint64_t per_page = 0;      // slot bytes of one page over all layers
   uint64_t encodable = 0;     // segments not raw by policy
@@ -282,31 +287,56 @@ struct Plan {
                               // per-element divide or TurboQuant/uniform arithmetic in encode)
 };
 
-Plan make_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages) {
-  Plan p;
+// Fill p (whose arrays hold at least L->layers entries).
+void fill_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages, Plan& p) {
   const uint32_t n_vec = L->kv_heads * L->tokens_per_page;
-  p.layer_off.resize(L->layers);
-  for (int comp = 0; comp < 2; comp++) {
-    p.slot[comp].resize(L->layers);
-    p.eff[comp].resize(L->layers);
-  }
+  p.total = p.per_page = p.encodable = p.ans = 0;
+  p.light = true;
   uint64_t off = 0;
   for (uint32_t l = 0; l < L->layers; l++) {
     const bool prot = is_protected(c, l);
+    uint64_t page = 0;
     for (int comp = 0; comp < 2; comp++) {
       const int e = effective_codec(comp ? c->v : c->k, L->head_dim, n_vec, L->kv_heads, prot);
-      p.eff[comp][l] = (uint8_t)e;
-      p.slot[comp][l] = (uint32_t)slot_size(e, L->head_dim, n_vec, L->kv_heads);
+      const uint32_t sz = (uint32_t)slot_size(e, L->head_dim, n_vec, L->kv_heads);
+      if (p.eff[comp]) p.eff[comp][l] = (uint8_t)e;
+      if (p.slot[comp]) p.slot[comp][l] = sz;
+      page += sz;
       if (e != KVC_RAW) p.encodable += n_pages;
       if (e == KVC_ANS16) p.ans += n_pages;
       if (e != KVC_RAW && e != KVC_FP8_DIRECT && e != KVC_FP8_DYNAMIC && e != KVC_ANS16) p.light = false;
     }
-    p.layer_off[l] = off;
-    const uint64_t page = (uint64_t)p.slot[0][l] + p.slot[1][l];
+    if (p.layer_off) p.layer_off[l] = off;
     p.per_page += page;
     off += page * n_pages;
   }
   p.total = off;
+}
+
+// A plan with the per-layer arrays on the heap (not copyable: the pointers
+// refer to its own vectors).
+struct HeapPlan : Plan {
+  std::vector<uint64_t> lo;
+  std::vector<uint32_t> sz[2];
+  std::vector<uint8_t> ef[2];
+  HeapPlan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages)
+      : lo(L->layers), sz{std::vector<uint32_t>(L->layers), std::vector<uint32_t>(L->layers)},
+        ef{std::vector<uint8_t>(L->layers), std::vector<uint8_t>(L->layers)} {
+    layer_off = lo.data();
+    for (int comp = 0; comp < 2; comp++) {
+      slot[comp] = sz[comp].data();
+      eff[comp] = ef[comp].data();
+    }
+    fill_plan(L, c, n_pages, *this);
+  }
+  HeapPlan(const HeapPlan&) = delete;
+  HeapPlan& operator=(const HeapPlan&) = delete;
+};
+
+// the plan's totals only (no per-layer arrays)
+Plan plan_totals(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages) {
+  Plan p;
+  fill_plan(L, c, n_pages, p);
   return p;
 }
 
@@ -447,16 +477,10 @@ bool pinned_range(const void* p, size_t n) {
   return ok;
 }
 
-// stage layer table + page ids + zeroed spill cursor, upload, fill params
-kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, const Plan& plan,
-                      const int32_t* pages, uint32_t n, hipStream_t stream, CallParams* P, size_t* ring_off,
-                      size_t* ring_size) {
-  const size_t need = call_bytes(L->layers, n);
-  size_t off = 0;
-  kvc_status st = ring_alloc(ctx, need, &off);
-  if (st != KVC_OK) return st;
-  uint8_t* h = ctx->staging + off;
-  SideEntry* se = reinterpret_cast<SideEntry*>(h);
+// The call's side table (into se, 2 * layers entries) and every field of P
+// but the device pointers (sides, pages, spill_cursor, tables, buf, desc,
+// seg_status) and the buffer sizes.
+void fill_call(const kvc_layout* L, const kvc_codec* c, const Plan& plan, uint32_t n, SideEntry* se, CallParams* P) {
   uint64_t lo = ~0ull, hi = 0;
   uint32_t stage = 0;
   for (uint32_t l = 0; l < L->layers; l++) {
@@ -482,16 +506,6 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   P->base_hi = hi;
   P->stage_bytes = stage <= kMaxStageBytes ? stage : 0;   // slot sizes are multiples of 256
   P->num_blocks = (uint32_t)L->num_blocks;
-  const size_t pages_off = align_up(sizeof(SideEntry) * 2 * L->layers, kAlign);
-  std::memcpy(h + pages_off, pages, sizeof(int32_t) * (size_t)n);
-  const size_t cur_off = pages_off + align_up(sizeof(int32_t) * (size_t)n, kAlign);
-  std::memset(h + cur_off, 0, kAlign);
-  if (hipMemcpyAsync(ctx->arena + off, h, need, hipMemcpyHostToDevice, stream) != hipSuccess) return KVC_E_HIP;
-  uint8_t* d = ctx->arena + off;
-  P->sides = reinterpret_cast<const SideEntry*>(d);
-  P->pages = reinterpret_cast<const int32_t*>(d + pages_off);
-  P->spill_cursor = reinterpret_cast<unsigned long long*>(d + cur_off);
-  P->tables = reinterpret_cast<const Tables*>(ctx->arena);
   P->sb = L->stride_block;
   P->st = L->stride_token;
   P->sh = L->stride_head;
@@ -514,6 +528,29 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   P->dtype = L->dtype;
   P->crc = (c->flags & KVC_CODEC_CRC32) ? 1u : 0u;
   sign_mask(c->seed, L->head_dim, P->sign_mask);
+}
+
+// stage layer table + page ids + zeroed spill cursor in the context's ring,
+// upload, fill params
+kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, const Plan& plan,
+                      const int32_t* pages, uint32_t n, hipStream_t stream, CallParams* P, size_t* ring_off,
+                      size_t* ring_size) {
+  const size_t need = call_bytes(L->layers, n);
+  size_t off = 0;
+  kvc_status st = ring_alloc(ctx, need, &off);
+  if (st != KVC_OK) return st;
+  uint8_t* h = ctx->staging + off;
+  fill_call(L, c, plan, n, reinterpret_cast<SideEntry*>(h), P);
+  const size_t pages_off = align_up(sizeof(SideEntry) * 2 * L->layers, kAlign);
+  std::memcpy(h + pages_off, pages, sizeof(int32_t) * (size_t)n);
+  const size_t cur_off = pages_off + align_up(sizeof(int32_t) * (size_t)n, kAlign);
+  std::memset(h + cur_off, 0, kAlign);
+  if (hipMemcpyAsync(ctx->arena + off, h, need, hipMemcpyHostToDevice, stream) != hipSuccess) return KVC_E_HIP;
+  uint8_t* d = ctx->arena + off;
+  P->sides = reinterpret_cast<const SideEntry*>(d);
+  P->pages = reinterpret_cast<const int32_t*>(d + pages_off);
+  P->spill_cursor = reinterpret_cast<unsigned long long*>(d + cur_off);
+  P->tables = reinterpret_cast<const Tables*>(ctx->arena);
   *ring_off = off;
   *ring_size = need;
   return KVC_OK;
@@ -579,6 +616,15 @@ kvc_status no_throw(F&& f) noexcept {
   }
 }
 
+// Tables for the allocation-free entry point, built once per process into
+// static storage (no heap).
+const Tables* static_tables() {
+  static Tables t;
+  static std::once_flag once;
+  std::call_once(once, [] { build_tables(t); });
+  return &t;
+}
+
 }  // namespace
 
 extern "C" {
@@ -604,7 +650,7 @@ kvc_status kvc_plan(const kvc_layout* layout, const kvc_codec* codec, uint32_t n
     kvc_status st = check_layout(layout);
     if (st == KVC_OK) st = check_codec(layout, codec);
     if (st != KVC_OK) return st;
-    const Plan p = make_plan(layout, codec, n_pages);
+    const Plan p = plan_totals(layout, codec, n_pages);
     const uint64_t raw_seg = align_up((uint64_t)layout->kv_heads * layout->tokens_per_page * layout->head_dim * 2,
                                       KVC_SLOT_ALIGN);
     if (slot_bytes) *slot_bytes = p.total;
@@ -625,7 +671,7 @@ kvc_status kvc_validate_encode(const kvc_layout* layout, const kvc_codec* codec,
     if (st == KVC_OK) st = check_grid(layout, n_pages);
     if (st == KVC_OK) st = check_pages(layout, page_ids, n_pages, false);
     if (st != KVC_OK) return st;
-    if (make_plan(layout, codec, n_pages).total > out_bytes) return KVC_E_CAPACITY;
+    if (plan_totals(layout, codec, n_pages).total > out_bytes) return KVC_E_CAPACITY;
     return KVC_OK;
   });
 }
@@ -638,7 +684,7 @@ kvc_status kvc_validate_decode(const kvc_layout* layout, const kvc_codec* codec,
     if (st == KVC_OK) st = check_grid(layout, n_pages);
     if (st == KVC_OK) st = check_pages(layout, dst_page_ids, n_pages, true);
     if (st != KVC_OK) return st;
-    if (make_plan(layout, codec, n_pages).total > in_bytes) return KVC_E_CAPACITY;
+    if (plan_totals(layout, codec, n_pages).total > in_bytes) return KVC_E_CAPACITY;
     return KVC_OK;
   });
 }
@@ -713,7 +759,7 @@ kvc_status kvc_encode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_co
     if (!out || !desc || ((uintptr_t)out & 255) || ((uintptr_t)desc & 15)) return KVC_E_ARG;
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVC_E_HIP;
-    const Plan plan = make_plan(layout, codec, n_pages);
+    const HeapPlan plan(layout, codec, n_pages);
     hipStream_t s = static_cast<hipStream_t>(stream);
     CallParams P{};
     size_t roff = 0, rsize = 0;
@@ -741,7 +787,7 @@ kvc_status kvc_decode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_co
     if (!in || ((uintptr_t)in & 255)) return KVC_E_ARG;
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVC_E_HIP;
-    const Plan plan = make_plan(layout, codec, n_pages);
+    const HeapPlan plan(layout, codec, n_pages);
     hipStream_t s = static_cast<hipStream_t>(stream);
     CallParams P{};
     size_t roff = 0, rsize = 0;
@@ -770,7 +816,7 @@ kvc_status kvc_decode_layers(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     if (!in || ((uintptr_t)in & 255)) return KVC_E_ARG;
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVC_E_HIP;
-    const Plan plan = make_plan(layout, codec, n_pages);
+    const HeapPlan plan(layout, codec, n_pages);
     hipStream_t s = static_cast<hipStream_t>(stream);
     CallParams P{};
     size_t roff = 0, rsize = 0;
@@ -800,7 +846,7 @@ kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     if (!pinned_range(host_out, host_bytes) || !pinned_range(host_desc, desc_bytes)) return KVC_E_ARG;
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVC_E_HIP;
-    const Plan plan = make_plan(layout, codec, n_pages);
+    const HeapPlan plan(layout, codec, n_pages);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t buf_bytes = align_up(host_bytes, kAlign);
     st = lane_reserve(ctx, 0, buf_bytes + desc_bytes);
@@ -836,7 +882,7 @@ kvc_status kvc_restore_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     if (!pinned_range(host_in, in_bytes)) return KVC_E_ARG;
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVC_E_HIP;
-    const Plan plan = make_plan(layout, codec, n_pages);
+    const HeapPlan plan(layout, codec, n_pages);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint32_t nl = layer_end - layer_begin;
     // lazily created: the copy stream (default priority), the fork event and
@@ -887,6 +933,61 @@ kvc_status kvc_restore_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     }
     if (hipEventRecord(lane.last, s) != hipSuccess) return KVC_E_HIP;
     return ring_commit(ctx, roff, rsize, s);
+  });
+}
+
+kvc_status kvc_encode_pages_noalloc(const kvc_layout* layout, const kvc_codec* codec, const int32_t* page_ids,
+                                    uint32_t n_pages, void* out, size_t out_bytes, kvc_segment_desc* desc,
+                                    void* stream) {
+  return no_throw([&]() -> kvc_status {
+    kvc_status st = check_layout(layout);
+    if (st == KVC_OK) st = check_codec(layout, codec);
+    if (st == KVC_OK) st = check_grid(layout, n_pages);
+    if (st == KVC_OK) st = check_pages(layout, page_ids, n_pages, false);
+    if (st != KVC_OK) return st;
+    if (layout->layers > kNoAllocMaxLayers || n_pages > kNoAllocMaxPages) return KVC_E_BUDGET;
+    // the plan in fixed arrays on the stack
+    uint64_t layer_off[kNoAllocMaxLayers];
+    uint32_t slot_k[kNoAllocMaxLayers], slot_v[kNoAllocMaxLayers];
+    uint8_t eff_k[kNoAllocMaxLayers], eff_v[kNoAllocMaxLayers];
+    Plan plan;
+    plan.layer_off = layer_off;
+    plan.slot[0] = slot_k;
+    plan.slot[1] = slot_v;
+    plan.eff[0] = eff_k;
+    plan.eff[1] = eff_v;
+    fill_plan(layout, codec, n_pages, plan);
+    if (plan.total > out_bytes) return KVC_E_CAPACITY;
+    if (n_pages == 0) return KVC_OK;
+    if (!out || !desc || ((uintptr_t)out & 255) || ((uintptr_t)desc & 15)) return KVC_E_ARG;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KVC_E_HIP;
+    uint8_t* scr = nullptr;
+    if (noalloc_scratch(dev, static_tables(), &scr) != hipSuccess) return KVC_E_HIP;
+    // host image of [spill cursor = 0 | side table], copied into the scratch
+    // in one pageable copy (complete when the call returns)
+    alignas(16) uint8_t img[kNoAllocSidesOff - kNoAllocCursorOff + sizeof(SideEntry) * 2 * kNoAllocMaxLayers];
+    std::memset(img, 0, kNoAllocSidesOff - kNoAllocCursorOff);
+    CallParams P{};
+    fill_call(layout, codec, plan, n_pages, reinterpret_cast<SideEntry*>(img + (kNoAllocSidesOff - kNoAllocCursorOff)),
+              &P);
+    const size_t img_bytes = kNoAllocSidesOff - kNoAllocCursorOff + sizeof(SideEntry) * 2 * layout->layers;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(scr + kNoAllocCursorOff, img, img_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(scr + kNoAllocPagesOff, page_ids, sizeof(int32_t) * (size_t)n_pages, hipMemcpyHostToDevice,
+                       s) != hipSuccess)
+      return KVC_E_HIP;
+    P.tables = reinterpret_cast<const Tables*>(scr);
+    P.spill_cursor = reinterpret_cast<unsigned long long*>(scr + kNoAllocCursorOff);
+    P.sides = reinterpret_cast<const SideEntry*>(scr + kNoAllocSidesOff);
+    P.pages = reinterpret_cast<const int32_t*>(scr + kNoAllocPagesOff);
+    P.buf = static_cast<uint8_t*>(out);
+    P.buf_bytes = out_bytes;
+    P.slot_region = plan.total;
+    P.desc = desc;
+    P.seg_status = nullptr;
+    const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
+    return run_encode(P, layout, plan, nseg, s) == hipSuccess ? KVC_OK : KVC_E_HIP;
   });
 }
 

@@ -144,6 +144,22 @@ struct CallParams {
   uint32_t sign_mask[8];                      // TurboQuant signs, bit i = (sigma_i < 0)
 };
 
+// Allocation-free encode (kvc_encode_pages_noalloc): every call on a GPU
+// uses that GPU's copy of one file-scope device array (kvc_kernels.hip),
+// laid out as [Tables | spill cursor (256 B) | side table | page ids], for
+// calls of at most kNoAllocMaxLayers layers and kNoAllocMaxPages pages.
+constexpr uint32_t kNoAllocMaxLayers = 256;
+constexpr uint32_t kNoAllocMaxPages = 65536;
+constexpr size_t kNoAllocCursorOff = (sizeof(Tables) + 255) / 256 * 256;
+constexpr size_t kNoAllocSidesOff = kNoAllocCursorOff + 256;
+constexpr size_t kNoAllocPagesOff = kNoAllocSidesOff + sizeof(SideEntry) * 2 * kNoAllocMaxLayers;
+constexpr size_t kNoAllocScratchBytes = kNoAllocPagesOff + sizeof(int32_t) * kNoAllocMaxPages;
+constexpr int kNoAllocMaxDevices = 64;
+// Device address of the current device's scratch array (`device` must be
+// current).  The first call for a device looks the address up and copies
+// host_tables into its head; later calls return the kept address.
+hipError_t noalloc_scratch(int device, const Tables* host_tables, uint8_t** ptr);
+
 // Launchers (kvc_kernels.hip): segments [p.seg_base, p.seg_base +
 // n_segments).  Return hipSuccess or the launch error.
 hipError_t launch_encode(const CallParams& p, uint32_t head_dim, uint64_t n_segments,

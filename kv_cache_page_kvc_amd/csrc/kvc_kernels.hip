@@ -28,6 +28,8 @@
 // RAW_DATA, a zeroed slot body and its bytes in the spill region.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kvc_arch.h"
 #include "kvc_internal.h"
 
@@ -1358,6 +1360,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
 // ------------------------------------------------------------------ entropy stage
 #include "kvc_ans_device.h"
 
+// ------------------------------------------------------------------ allocation-free scratch
+// The scratch of kvc_encode_pages_noalloc, one copy per GPU for the life of
+// the process.  In host code `scratch` names a host-side stand-in, never the
+// device array: only the address from hipGetSymbolAddress is used.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 // dynamic LDS of a launch: the slot staging
 inline uint32_t dynamic_lds(const CallParams& p) { return p.stage_bytes; }
 
@@ -1399,6 +1407,23 @@ hipError_t launch_decode_d(const CallParams& p, uint64_t nseg, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t noalloc_scratch(int device, const Tables* host_tables, uint8_t** ptr) {
+  static std::mutex mu;
+  static uint8_t* addr[kNoAllocMaxDevices] = {};
+  if (device < 0 || device >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    e = hipMemcpy(p, host_tables, sizeof(Tables), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return e;
+    addr[device] = static_cast<uint8_t*>(p);
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 hipError_t launch_encode(const CallParams& p, uint32_t head_dim, uint64_t nseg, hipStream_t st) {
   switch (head_dim) {

@@ -204,3 +204,33 @@ def test_create_checks_before_touching_a_device():
     assert L.kvc_create(ctypes.byref(h), 0, 4096) == kvc.KVC_E_BUDGET
     assert h.value is None                              # *out cleared on failure
     assert L.kvc_destroy(None) == kvc.KVC_OK
+
+
+def test_noalloc_encode_validates_before_the_device():
+    """kvc_encode_pages_noalloc checks its arguments on the host like
+    kvc_encode_pages, and rejects calls beyond its fixed scratch (more than
+    256 layers or 65,536 pages) with KVC_E_BUDGET, before any GPU call (the
+    fake tensor pointers below are never dereferenced)."""
+    codec = kvc.Codec("TQ4", "UNIFORM4")
+    L = kvc.lib()
+    lay = layout()
+    cc = ctypes.byref(codec.c)
+    big = np.zeros(65537, np.int32)
+    bp = big.ctypes.data_as(ctypes.c_void_p)
+    assert L.kvc_encode_pages_noalloc(ctypes.byref(lay.c), cc, bp, 65537, None, 1 << 40, None, None) == \
+        kvc.KVC_E_BUDGET
+    deep = layout(L=257)
+    ids = np.arange(3, dtype=np.int32)
+    ip = ids.ctypes.data_as(ctypes.c_void_p)
+    assert L.kvc_encode_pages_noalloc(ctypes.byref(deep.c), cc, ip, 3, None, 1 << 40, None, None) == \
+        kvc.KVC_E_BUDGET
+    slot, _, _ = kvc.kvc_plan(lay, codec, 3)
+    assert L.kvc_encode_pages_noalloc(ctypes.byref(lay.c), cc, ip, 3, None, slot - 1, None, None) == \
+        kvc.KVC_E_CAPACITY
+    assert L.kvc_encode_pages_noalloc(ctypes.byref(layout(D=96).c), cc, ip, 3, None, slot, None, None) == \
+        kvc.KVC_E_UNSUPPORTED
+    bad = np.array([0, 100], np.int32)
+    assert L.kvc_encode_pages_noalloc(ctypes.byref(lay.c), cc, bad.ctypes.data_as(ctypes.c_void_p), 2, None,
+                                      1 << 40, None, None) == kvc.KVC_E_PAGE_RANGE
+    # output and descriptor pointers are checked after the plan, still on the host
+    assert L.kvc_encode_pages_noalloc(ctypes.byref(lay.c), cc, ip, 3, None, slot, None, None) == kvc.KVC_E_ARG
