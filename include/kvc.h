@@ -162,9 +162,9 @@ typedef enum {
 /* Codec choice per component.  fixed_scales: host array [layers][2] (K, V)
  * of FP32 scales, required iff a component uses KVC_FP8_FIXED (each must be
  * finite and in [2^-100, 2^100]).  protected_layers: host bitmap
- * [ceil(layers/8)] (bit l%8 of byte l/8), or NULL; protected layers stay
- * exact [OKV-SF "FP8 and TurboQuant": the first and last two layers of each
- * pipeline stage remain exact -- the caller marks them].  seed: rotation
+ * [ceil(layers/8)] (bit l%8 of byte l/8), or NULL; protected layers are
+ * stored raw [OKV-SF "FP8 and TurboQuant": some layers at the ends of each
+ * pipeline stage are kept lossless; which ones is the caller's choice].  seed: rotation
  * seed of the TurboQuant sign generator (SplitMix64, version 1).  flags:
  * KVC_CODEC_CRC32 makes encode store each segment's CRC32 (KVC_FLAG_CRC32)
  * and makes decode verify it before it writes the page; other bits and

@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
       for (uint32_t u = 0; u < 4; u++)
         if (c0 + u * kAnsStreams < chunks) st_global16(heap + 16 * (c0 + u * kAnsStreams), w[u]);
     }
-    const uint32_t cr = CRC ? crc32_written<64>(heap, raw_bytes, ct) : 0u;
+    const uint32_t cr = CRC ? crc32_written<64>(heap, raw_bytes, ct, p.tables) : 0u;
     if (lane == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | crc_flag, KVC_SEG_RAW_DATA,
                         (int)p.dtype, comp, D, s.n_vec, raw_bytes, off, 0, cr);
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
       st_global16(P + 16 * u, *reinterpret_cast<const uint4*>(s_out + 16 * u));
     __syncthreads();                                             // the image is rebuilt for the next plane
   }
-  const uint32_t cr = CRC ? crc32_written<64>(heap, payload, ct) : 0u;
+  const uint32_t cr = CRC ? crc32_written<64>(heap, payload, ct, p.tables) : 0u;
   // no fence before the header: nothing reads the payload during this
   // launch, and its completion makes every write visible to later work
   if (lane == 0) {
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   const uint8_t* const heap = p.buf + spill;
   if constexpr (CRC) {
     __syncthreads();                                             // CRC tables in LDS
-    if (crc32_lanes<64>(GlobalBytes{heap}, stored, ct) != h1.z) {
+    if (crc32_lanes<64>(GlobalBytes{heap}, stored, ct, p.tables) != h1.z) {
       if (report) p.seg_status[seg] = 3;
       return;
     }

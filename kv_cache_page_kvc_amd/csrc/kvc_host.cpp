@@ -148,30 +148,35 @@ void lloyd_max(int n, double* lev) {           // n <= kMaxLevels
 // CRC-32 tables (zlib's CRC: reflected polynomial 0xEDB88320), built from
 // the bitwise definition; see CrcTables for how the kernels use them.
 void build_crc_tables(CrcTables& c) {
+  uint32_t byte_tab[256];
   for (uint32_t b = 0; b < 256; b++) {
     uint32_t r = b;
     for (int i = 0; i < 8; i++) r = (r >> 1) ^ (0xEDB88320u & (0u - (r & 1u)));
-    c.t[0][b] = r;
+    byte_tab[b] = r;
   }
-  auto zero_byte = [&c](uint32_t r) { return (r >> 8) ^ c.t[0][r & 0xFF]; };
-  for (int k = 1; k < 4; k++)
-    for (int b = 0; b < 256; b++) c.t[k][b] = zero_byte(c.t[k - 1][b]);
+  auto zero_byte = [&byte_tab](uint32_t r) { return (r >> 8) ^ byte_tab[r & 0xFF]; };
+  // register after the four bytes of x from a zero register, then `zeros` zero bytes
+  auto word_then_zeros = [&](uint32_t x, uint32_t zeros) {
+    uint32_t r = x;
+    for (int b = 0; b < 4; b++) r = zero_byte(r);
+    for (uint32_t i = 0; i < zeros; i++) r = zero_byte(r);
+    return r;
+  };
+  for (int k = 0; k < 8; k++)
+    for (uint32_t v = 0; v < 16; v++) c.t[k][v] = word_then_zeros(v << (4 * k), 0);
   for (int w = 0; w < kCrcLaneSets; w++) {
-    const uint32_t gap = 16u * ((uint32_t)kCrcLanes * (1u << w) - 1u);
-    for (int k = 0; k < 4; k++)
-      for (int b = 0; b < 256; b++) {
-        uint32_t r = c.t[k][b];
-        for (uint32_t i = 0; i < gap; i++) r = zero_byte(r);
-        c.tg[w][k][b] = r;
+    const uint32_t lanes = (uint32_t)kCrcLanes << w;
+    for (int k = 0; k < 8; k++)
+      for (uint32_t v = 0; v < 16; v++) c.tj[w][k][v] = word_then_zeros(v << (4 * k), 16u * (lanes - 1));
+    for (uint32_t j = 0; j < 256; j++) {
+      uint32_t r = 0;
+      if (j < lanes) {
+        r = 0x80000000u;                       // x^0
+        for (uint32_t i = 0; i < 16u * (lanes - 1 - j); i++) r = zero_byte(r);
       }
+      c.shift[w][j] = r;
+    }
   }
-  for (int lvl = 0; lvl < kCrcShiftLevels; lvl++)
-    for (int i = 0; i < 8; i++)
-      for (uint32_t v = 0; v < 16; v++) {
-        uint32_t r = v << (4 * i);
-        for (int n = 0; n < (16 << lvl); n++) r = zero_byte(r);
-        c.sh[lvl][i][v] = r;
-      }
 }
 
 void build_tables(Tables& t) {

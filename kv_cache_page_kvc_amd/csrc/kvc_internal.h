@@ -20,7 +20,7 @@ namespace kvc {
 constexpr int kEncodeThreads = 128;
 // encode with the CRC option: the CRC tables' LDS halves the workgroups a CU
 // holds, so four waves per workgroup keep as many waves in flight
-constexpr int kEncodeThreadsCrc = 256;
+constexpr int kEncodeThreadsCrc = 128;
 constexpr int kDecodeThreads = 256;
 constexpr int kThreadsSmall = 64;
 constexpr uint32_t kSmallSegmentBytes = 16384;
@@ -59,25 +59,27 @@ struct CellEntry {
 // CRC-32 tables (reflected polynomial 0xEDB88320) for the CRC of a byte
 // range computed by all N = 64 * 2^w lanes of a workgroup (w = 0, 1, 2 for
 // 64, 128, 256 threads): lane j takes 16-byte units j, j + N, j + 2N, ...
-// and runs the slice-by-4 table step over each; the last word of a unit that
-// has a successor in the same lane uses tg[w], which also carries the
-// register over the 16 (N - 1) bytes that the other lanes take in between.
-// Each lane then carries its register over the (N - 1 - j) units after its
-// last one with the nibble tables sh, and the lanes' registers are xored.
+// and steps its register over each 4-byte word with nibble tables (eight
+// lookups of 16 entries per word, by linearity of the CRC register update);
+// the last word of a unit that has a successor in the same lane uses tj[w],
+// which also carries the register over the 16 (N - 1) bytes that the other
+// lanes take in between.  Each lane then carries its register over the
+// 16 (N - 1 - j) bytes after its last unit by one carry-less multiplication
+// modulo the polynomial with shift[w][j] = x^(8 * 16 (N - 1 - j)), and the
+// lanes' registers are xored.  Registers are in the reflected order: bit 31
+// holds the coefficient of x^0.
 constexpr int kCrcLanes = 64;               // lanes of a wave
 constexpr int kCrcLaneSets = 3;             // N = 64, 128, 256
-constexpr int kCrcShiftLevels = 8;          // shifts of 16 << lvl bytes, lvl < 8: up to N - 1 = 255 units
 struct CrcTables {
-  uint32_t t[4][256];                       // register after byte b followed by k zero bytes, from a zero register
-  uint32_t tg[kCrcLaneSets][4][256];        // t[k][b] carried over 16 (64 * 2^w - 1) more zero bytes
-  uint32_t sh[kCrcShiftLevels][8][16];      // register whose nibble i is v (others 0) over 16 << lvl zero bytes
+  uint32_t t[8][16];                        // register after a word whose only nonzero nibble k is v, from a zero register
+  uint32_t tj[kCrcLaneSets][8][16];         // t[k][v] carried over 16 (64 * 2^w - 1) more zero bytes
+  uint32_t shift[kCrcLaneSets][256];        // x^(128 (64 * 2^w - 1 - j)) mod P for lane j (0 beyond the lane count)
 };
 static_assert(sizeof(CrcTables) % 16 == 0, "CRC tables are copied in 16-byte units");
-// the part of CrcTables one kernel keeps in LDS: t, its lane count's tg, sh
+// the part of CrcTables one kernel keeps in LDS: t and its lane count's tj
 struct CrcLds {
-  uint32_t t[4][256];
-  uint32_t tg[4][256];
-  uint32_t sh[kCrcShiftLevels][8][16];
+  uint32_t t[8][16];
+  uint32_t tj[8][16];
 };
 
 // Reciprocals of the rANS encoder (KVC_ANS16), indexed by the frequency f in

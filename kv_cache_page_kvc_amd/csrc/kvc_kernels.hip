@@ -774,21 +774,28 @@ __device__ __forceinline__ uint32_t payload_bytes(int codec, int d, uint32_t n_v
 // The register is preset to 0xFFFFFFFF by complementing the first word and
 // the result is complemented at the end.
 
-// register after the four bytes of x (x = register ^ next little-endian word)
-__device__ __forceinline__ uint32_t crc_word(uint32_t x, const uint32_t (*t)[256]) {
-  return t[3][x & 0xFF] ^ t[2][(x >> 8) & 0xFF] ^ t[1][(x >> 16) & 0xFF] ^ t[0][x >> 24];
+// register after the four bytes of x (x = register ^ next little-endian word),
+// from the nibble tables t[k][v] (eight lookups: the update is linear)
+__device__ __forceinline__ uint32_t crc_word(uint32_t x, const uint32_t (*t)[16]) {
+  return t[0][x & 15] ^ t[1][(x >> 4) & 15] ^ t[2][(x >> 8) & 15] ^ t[3][(x >> 12) & 15] ^ t[4][(x >> 16) & 15] ^
+         t[5][(x >> 20) & 15] ^ t[6][(x >> 24) & 15] ^ t[7][x >> 28];
 }
-// register r carried over 16 << lvl zero bytes
-__device__ __forceinline__ uint32_t crc_zeros(uint32_t r, const uint32_t (*sh)[16]) {
-  uint32_t y = 0;
+// a * b modulo the CRC polynomial, both in the register's reflected order
+// (bit 31 = coefficient of x^0): b is multiplied by x once per coefficient
+// of a, low degree first, and added where that coefficient is 1
+__device__ __forceinline__ uint32_t crc_mulmod(uint32_t a, uint32_t b) {
+  uint32_t p = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) y ^= sh[i][(r >> (4 * i)) & 15];
-  return y;
+  for (int i = 0; i < 32; i++) {
+    p ^= b & (0u - ((a >> (31 - i)) & 1u));
+    b = (b >> 1) ^ (0xEDB88320u & (0u - (b & 1u)));
+  }
+  return p;
 }
 
 // The CRC tables in LDS: a static allocation that only the kernels built
-// with CRC reference (so the others do not pay for its 12 KiB), at an
-// address the compiler knows, so table offsets fold into the LDS loads.
+// with CRC reference, at an address the compiler knows, so table offsets
+// fold into the LDS loads.
 template <bool CRC>
 __device__ __forceinline__ CrcLds* crc_tables_lds() {
   if constexpr (CRC) {
@@ -799,7 +806,7 @@ __device__ __forceinline__ CrcLds* crc_tables_lds() {
   }
 }
 
-// log2 of a workgroup's wave count: its lane set in CrcTables::tg
+// log2 of a workgroup's wave count: its lane set in CrcTables::tj
 template <int NT>
 constexpr int crc_lane_set() {
   static_assert(NT == 64 || NT == 128 || NT == 256, "CRC lane sets cover 1, 2 or 4 waves");
@@ -810,12 +817,12 @@ constexpr int crc_lane_set() {
 // caller synchronises before the first use).
 template <int NT>
 __device__ __forceinline__ void load_crc_tables(CrcLds* dst, const CrcTables* src) {
-  const uint4* t = reinterpret_cast<const uint4*>(src->t);
-  const uint4* tg = reinterpret_cast<const uint4*>(src->tg[crc_lane_set<NT>()]);
-  const uint4* sh = reinterpret_cast<const uint4*>(src->sh);
-  constexpr uint32_t kT = sizeof(src->t) / 16, kTg = sizeof(src->tg[0]) / 16, kSh = sizeof(src->sh) / 16;
-  for (uint32_t u = threadIdx.x; u < kT + kTg + kSh; u += NT) {
-    const uint4* from = u < kT ? t + u : (u < kT + kTg ? tg + (u - kT) : sh + (u - kT - kTg));
+  constexpr uint32_t kT = sizeof(src->t) / 16, kTj = sizeof(src->tj[0]) / 16;
+  static_assert(kT + kTj <= NT, "one 16-byte unit per thread");
+  const uint32_t u = threadIdx.x;
+  if (u < kT + kTj) {
+    const uint4* from = u < kT ? reinterpret_cast<const uint4*>(src->t) + u
+                               : reinterpret_cast<const uint4*>(src->tj[crc_lane_set<NT>()]) + (u - kT);
     reinterpret_cast<uint4*>(dst)[u] = ld_global16(from);
   }
 }
@@ -824,34 +831,29 @@ __device__ __forceinline__ void load_crc_tables(CrcLds* dst, const CrcTables* sr
 // (o a multiple of 16).  When n is not a multiple of 16 the 16-byte unit
 // holding the last bytes must be readable as a whole.  Called by all NT
 // threads of the workgroup (with NT > 64 it synchronises them); every thread
-// returns the CRC.
+// returns the CRC.  tables: the call's tables (the lane's carry constant).
 template <int NT, class Load>
-__device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, const CrcLds* ct) {
-  constexpr int LEVELS = 6 + crc_lane_set<NT>();              // NT - 1 < 2^LEVELS units
+__device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, const CrcLds* ct, const Tables* tables) {
   const uint32_t lane = threadIdx.x;
   const uint32_t units = n >> 4;
   // virtual zero units in front make the unit count a multiple of NT (a zero
   // register stays zero over zero bytes), so lane NT - 1 holds the last unit
   const uint32_t pad = (NT - (units & (NT - 1))) & (NT - 1);
   const uint32_t rounds = (units + pad) / NT;
+  const uint32_t carry = tables->crc.shift[crc_lane_set<NT>()][lane];   // x^(128 (NT - 1 - lane))
   uint32_t r = 0;
   for (uint32_t k = 0; k < rounds; k++) {
     const int32_t q = (int32_t)(k * NT + lane) - (int32_t)pad;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (q >= 0) w = load(16u * (uint32_t)q);
+    if (q < 0) continue;                    // a zero unit in front: the register stays zero
+    uint4 w = load(16u * (uint32_t)q);
     if (q == 0) w.x = ~w.x;
     r = crc_word(r ^ w.x, ct->t);
     r = crc_word(r ^ w.y, ct->t);
     r = crc_word(r ^ w.z, ct->t);
-    r = crc_word(r ^ w.w, k + 1 < rounds ? ct->tg : ct->t);
+    r = crc_word(r ^ w.w, k + 1 < rounds ? ct->tj : ct->t);
   }
   // carry each register over the units after its last one: NT - 1 - lane
-  const uint32_t after = (NT - 1) - lane;
-#pragma unroll
-  for (int lvl = 0; lvl < LEVELS; lvl++) {
-    const uint32_t y = crc_zeros(r, ct->sh[lvl]);
-    r = (after >> lvl) & 1 ? y : r;
-  }
+  r = crc_mulmod(r, carry);
 #pragma unroll
   for (int m = kCrcLanes / 2; m >= 1; m >>= 1) r ^= __shfl_xor(r, m, kCrcLanes);
   if constexpr (NT > kCrcLanes) {                                // xor the waves' registers
@@ -863,7 +865,8 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
     for (int v = 0; v < NT / kCrcLanes; v++) r ^= s_part[v];
     __syncthreads();                                             // s_part is reused by the next call
   }
-  // the ragged end (n mod 16 bytes), the same in every lane
+  // the ragged end (n mod 16 bytes), the same in every lane: whole words
+  // through the tables, the last bytes bit by bit
   if (!units) r = 0xFFFFFFFFu;
   const uint32_t tail = n & 15;
   if (tail) {
@@ -873,7 +876,10 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
     if (tail >= 12) r = crc_word(r ^ w.z, ct->t);
     const uint32_t q = tail >> 2;
     uint32_t last = q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w));
-    for (uint32_t b = 0; b < (tail & 3); b++, last >>= 8) r = (r >> 8) ^ ct->t[0][(r ^ last) & 0xFF];
+    for (uint32_t b = 0; b < (tail & 3); b++, last >>= 8) {
+      r ^= last & 0xFFu;
+      for (int i = 0; i < 8; i++) r = (r >> 1) ^ (0xEDB88320u & (0u - (r & 1u)));
+    }
   }
   return ~r;
 }
@@ -908,9 +914,9 @@ __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const La
 // barrier orders every wave's stores before they are read back.  Called by
 // all threads; every thread returns the CRC.
 template <int NT>
-__device__ __forceinline__ uint32_t crc32_written(const uint8_t* b, uint32_t n, const CrcLds* ct) {
+__device__ __forceinline__ uint32_t crc32_written(const uint8_t* b, uint32_t n, const CrcLds* ct, const Tables* tables) {
   __syncthreads();
-  return crc32_lanes<NT>(GlobalBytes{b}, n, ct);
+  return crc32_lanes<NT>(GlobalBytes{b}, n, ct, tables);
 }
 
 // ------------------------------------------------------------------ encode kernel
@@ -965,7 +971,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   if (codec == C_RAW) {                                        // raw by policy
     copy_out_raw<D, NT, false>(s, ln, s.slot + kHeaderBytes);
     zero_pad<NT>(s.slot, kHeaderBytes + raw_bytes, slot_bytes);
-    const uint32_t c = crc ? crc32_written<NT>(s.slot + kHeaderBytes, raw_bytes, ct) : 0u;
+    const uint32_t c = crc ? crc32_written<NT>(s.slot + kHeaderBytes, raw_bytes, ct, p.tables) : 0u;
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY | crc_flag, KVC_SEG_RAW_POLICY, DT,
                         comp, D, s.n_vec, raw_bytes, 0, 0, c);
@@ -1003,7 +1009,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const int any_bad = __syncthreads_or(bad);
   const uint32_t aux = codec == C_FP8F ? __float_as_uint(fixed) : 0u;
   if (staged && !any_bad) {
-    const uint32_t c = crc ? crc32_lanes<NT>(LdsBytes{s_stage + stored_at}, payload, ct) : 0u;
+    const uint32_t c = crc ? crc32_lanes<NT>(LdsBytes{s_stage + stored_at}, payload, ct, p.tables) : 0u;
     // header + body from unit 0, so every wave store covers whole lines
     const Header h = make_header(codec, crc_flag, DT, comp, D, s.n_vec, payload, 0, aux, c);
     for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT) {
@@ -1028,7 +1034,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
     for (uint32_t u = 2 + threadIdx.x; u < slot_bytes / 16; u += NT)
       st_stream16(s.slot + 16 * u, any_bad ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(s_stage + 16 * u));
   if (!any_bad) {
-    const uint32_t c = crc ? crc32_written<NT>(s.slot + stored_at, payload, ct) : 0u;
+    const uint32_t c = crc ? crc32_written<NT>(s.slot + stored_at, payload, ct, p.tables) : 0u;
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, codec, crc_flag, KVC_SEG_ENCODED, DT, comp, D, s.n_vec, payload, 0,
                         aux, c);
@@ -1042,7 +1048,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
   if (fits) copy_out_raw<D, NT, true>(s, ln, p.buf + p.slot_region + off);
   // a segment that was not stored (no spill space) carries no CRC
-  const uint32_t c = crc && fits ? crc32_written<NT>(p.buf + p.slot_region + off, raw_bytes, ct) : 0u;
+  const uint32_t c = crc && fits ? crc32_written<NT>(p.buf + p.slot_region + off, raw_bytes, ct, p.tables) : 0u;
   if (threadIdx.x == 0) {
     if (fits)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | crc_flag, KVC_SEG_RAW_DATA, DT, comp,
@@ -1323,9 +1329,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   // the stored bytes must match the header's CRC32 before the page is written
   if constexpr (CRC) {
     __syncthreads();                                      // CRC tables in LDS
-    const uint32_t c = raw_data ? crc32_lanes<NT>(GlobalBytes{p.buf + spill}, stored, ct)
-                       : staged ? crc32_lanes<NT>(LdsBytes{s_stage + stored_at}, stored, ct)
-                                : crc32_lanes<NT>(GlobalBytes{s.slot + stored_at}, stored, ct);
+    const uint32_t c = raw_data ? crc32_lanes<NT>(GlobalBytes{p.buf + spill}, stored, ct, p.tables)
+                       : staged ? crc32_lanes<NT>(LdsBytes{s_stage + stored_at}, stored, ct, p.tables)
+                                : crc32_lanes<NT>(GlobalBytes{s.slot + stored_at}, stored, ct, p.tables);
     if (c != h1.z) {
       if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 3;
       return;

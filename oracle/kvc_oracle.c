@@ -13,7 +13,7 @@
  *            subnormals; nonfinite or |x|>448 segments stay raw; TurboQuant K
  *            = normalize, deterministic random signs, orthonormal WHT,
  *            Gaussian Lloyd-Max centroids, norm-corrected inverse with the
- *            original FP16 norm; V = per-vector uniform quantization with FP16
+ *            original FP16 norm; V = b-bit codes per vector against an FP16
  *            minimum and scale; D in {32,64,128,256}; 66/68 and 50/52 byte
  *            payloads at D=128) and "Ownership, storage and GDS" (segment
  *            carries version, original length, format, stored length, CRC32;
