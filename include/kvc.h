@@ -167,7 +167,9 @@ typedef enum {
  * pipeline stage are kept lossless; which ones is the caller's choice].  seed: rotation
  * seed of the TurboQuant sign generator (SplitMix64, version 1).  flags:
  * KVC_CODEC_CRC32 makes encode store each segment's CRC32 (KVC_FLAG_CRC32)
- * and makes decode verify it before it writes the page; other bits and
+ * and makes decode verify it before it writes the page; a codec with a
+ * KVC_ANS16 component requires it (else KVC_E_ARG), since a corrupted
+ * entropy-coded stream shows only once it has been decoded; other bits and
  * `reserved` must be 0 (else KVC_E_ARG). */
 #define KVC_CODEC_CRC32 1u
 typedef struct {
@@ -258,11 +260,11 @@ kvc_status kvc_encode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_co
  * (KVC_SEG_CAPACITY), 2 when the kernel's range check on its staged
  * descriptor failed, or 3 when the stored bytes do not match the header's
  * CRC32 (KVC_CODEC_CRC32 only); in cases 1-3 the destination page is left
- * unchanged, with one exception: a KVC_ANS16 payload whose headers, model,
- * stream lengths, padding and exact length all check out but one of whose
- * streams does not decode to exactly its length in the initial state (or
- * starts outside the state interval) reports 1 after its page has been
- * written -- KVC_CODEC_CRC32 rejects such corrupted bytes before any write.
+ * unchanged, with one exception: a KVC_ANS16 payload that matches its CRC32
+ * and whose headers, model, stream lengths, padding and exact length all
+ * check out, but one of whose streams does not decode to exactly its length
+ * in the initial state (or starts outside the state interval) -- bytes the
+ * encoder never writes -- reports 1 after its page has been written.
  * Enqueued on `stream`. */
 kvc_status kvc_decode_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
                             const void *in, size_t in_bytes,
@@ -285,13 +287,21 @@ kvc_status kvc_decode_layers(kvc_ctx *ctx, const kvc_layout *layout, const kvc_c
  * buffers, separate for backup and restoration, grown when necessary and
  * never replaced while a stream still uses them].
  * Encode the pages page_ids of every layer into the context's offload
- * staging buffer, then copy the encoded buffer (host_bytes bytes: slot
- * region, then spill region) to host_out and the layers*n_pages*2
- * descriptors to host_desc, all enqueued on `stream`.  host_out and
- * host_desc must be pinned host memory (hipHostMalloc, or a pinned torch
- * tensor); they are written when the stream reaches this call and must stay
- * allocated until then.  The bytes in host_out are exactly what
- * kvc_encode_pages writes to a device buffer of host_bytes bytes.
+ * staging buffer, always with a CRC32 per segment (KVC_CODEC_CRC32 is added
+ * to codec->flags) [OKV-SF "Ownership, storage and GDS": every stored
+ * segment carries a CRC32 that is checked before decode], then copy the
+ * slot region and the layers*n_pages*2 descriptors to host_out and
+ * host_desc, and of the spill region (the rest of host_bytes) only the bytes
+ * the encode used, all enqueued on `stream`.  The used size is read back
+ * from the device once per call [OKV-SF "Ownership, storage and GDS": sizes
+ * are collected once per batch]: the call waits for the encode to finish
+ * (not for the copies) and stores in *host_used (may be NULL) the bytes of
+ * host_out that hold the encoding -- the slot region plus the used spill
+ * bytes; a restore needs only those.  host_out and host_desc must be pinned
+ * host memory (hipHostMalloc, or a pinned torch tensor); they are written
+ * when the stream reaches the copies and must stay allocated until then.
+ * The bytes in host_out[0, *host_used) are what kvc_encode_pages with
+ * KVC_CODEC_CRC32 writes to a device buffer of host_bytes bytes.
  * Errors as kvc_validate_encode (host_bytes in place of out_bytes), and
  * KVC_E_ARG for memory that is not pinned host memory.  The staging buffer
  * grows to host_bytes + the descriptors; a buffer it replaces is freed once
@@ -299,11 +309,13 @@ kvc_status kvc_decode_layers(kvc_ctx *ctx, const kvc_layout *layout, const kvc_c
 kvc_status kvc_offload_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_codec *codec,
                              const int32_t *page_ids, uint32_t n_pages,
                              void *host_out, size_t host_bytes, kvc_segment_desc *host_desc,
-                             void *stream);
+                             size_t *host_used, void *stream);
 
 /* Offload lane, host to device: restore layers [layer_begin, layer_end) of
  * an encoded buffer held in pinned host memory (host_in, in_bytes: what
- * kvc_offload_pages wrote, or any kvc_encode_pages output copied to host)
+ * kvc_offload_pages wrote -- in_bytes may be its *host_used -- or any
+ * kvc_encode_pages output made with KVC_CODEC_CRC32 and copied to host;
+ * the lane always checks the CRC32, as if codec->flags held KVC_CODEC_CRC32)
  * into the destination pages dst_page_ids (host [n_pages], distinct, all
  * validated before anything is enqueued).  The context's restore staging
  * buffer receives the spill region, then each layer's slots, on an internal
@@ -326,7 +338,7 @@ kvc_status kvc_restore_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_c
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  No context: the per-call side table,
  * page ids and spill cursor live in a fixed device array of this library,
- * one copy per GPU held until the process ends (about 320 KiB: the codec
+ * one copy per GPU held until the process ends (about 300 KiB: the codec
  * tables, a 256-byte cursor, 2 x 256 side-table entries of 32 bytes and
  * 65,536 page ids).  The call allocates nothing: no hipMalloc, hipFree, host
  * heap or pinned memory.  The first call on a device looks the array up and

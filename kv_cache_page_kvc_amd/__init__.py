@@ -117,7 +117,7 @@ def lib():
                                         P, P]
         L.kvc_offload_pages.restype = st
         L.kvc_offload_pages.argtypes = [P, ctypes.POINTER(kvc_layout), ctypes.POINTER(kvc_codec), P,
-                                        ctypes.c_uint32, P, ctypes.c_size_t, P, P]
+                                        ctypes.c_uint32, P, ctypes.c_size_t, P, ctypes.POINTER(ctypes.c_size_t), P]
         L.kvc_restore_pages.restype = st
         L.kvc_restore_pages.argtypes = [P, ctypes.POINTER(kvc_layout), ctypes.POINTER(kvc_codec), P,
                                         ctypes.c_size_t, P, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
@@ -276,11 +276,15 @@ def kvc_decode_layers(ctx, layout: Layout, codec: Codec, in_ptr: int, in_bytes: 
 
 
 def kvc_offload_pages(ctx, layout: Layout, codec: Codec, page_ids, host_ptr: int, host_bytes: int,
-                      host_desc_ptr: int, stream: int = 0):
-    """host_ptr / host_desc_ptr: pinned host memory (e.g. torch pin_memory tensors)."""
+                      host_desc_ptr: int, stream: int = 0) -> int:
+    """host_ptr / host_desc_ptr: pinned host memory (e.g. torch pin_memory
+    tensors).  Returns the bytes of host_ptr that hold the encoding."""
     arr, ptr = _pages(page_ids)
+    used = ctypes.c_size_t(0)
     _check(lib().kvc_offload_pages(ctx, ctypes.byref(layout.c), ctypes.byref(codec.c), ptr, arr.size,
-                                   host_ptr, host_bytes, host_desc_ptr, stream or None), "kvc_offload_pages")
+                                   host_ptr, host_bytes, host_desc_ptr, ctypes.byref(used), stream or None),
+           "kvc_offload_pages")
+    return used.value
 
 
 def kvc_restore_pages(ctx, layout: Layout, codec: Codec, host_ptr: int, host_bytes: int, dst_page_ids,

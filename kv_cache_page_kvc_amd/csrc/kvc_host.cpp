@@ -264,6 +264,9 @@ kvc_status check_layout(const kvc_layout* L) {
 kvc_status check_codec(const kvc_layout* L, const kvc_codec* c) {
   if (!c || c->k > KVC_ANS16 || c->v > KVC_ANS16) return KVC_E_ARG;
   if ((c->flags & ~KVC_CODEC_CRC32) || c->reserved) return KVC_E_ARG;
+  // the entropy decoder can tell a corrupted stream only once it has
+  // written the page: the segment CRC32 rejects it before
+  if ((c->k == KVC_ANS16 || c->v == KVC_ANS16) && !(c->flags & KVC_CODEC_CRC32)) return KVC_E_ARG;
   if (c->k == KVC_FP8_FIXED || c->v == KVC_FP8_FIXED) {
     if (!c->fixed_scales) return KVC_E_ARG;
     for (uint32_t l = 0; l < L->layers; l++)
@@ -838,13 +841,17 @@ kvc_status kvc_decode_layers(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
   });
 }
 
-kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec,
+kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec_in,
                              const int32_t* page_ids, uint32_t n_pages, void* host_out, size_t host_bytes,
-                             kvc_segment_desc* host_desc, void* stream) {
+                             kvc_segment_desc* host_desc, size_t* host_used, void* stream) {
   return no_throw([&]() -> kvc_status {
-    if (!ctx) return KVC_E_ARG;
+    if (!ctx || !codec_in) return KVC_E_ARG;
+    kvc_codec codec_crc = *codec_in;                 // the lane always stores a CRC32 per segment
+    codec_crc.flags |= KVC_CODEC_CRC32;
+    const kvc_codec* codec = &codec_crc;
     kvc_status st = kvc_validate_encode(layout, codec, page_ids, n_pages, host_bytes);
     if (st != KVC_OK) return st;
+    if (host_used) *host_used = 0;
     if (n_pages == 0) return KVC_OK;
     const uint64_t nseg = (uint64_t)layout->layers * n_pages * 2;
     const size_t desc_bytes = nseg * sizeof(kvc_segment_desc);
@@ -867,19 +874,36 @@ kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     P.slot_region = plan.total;
     P.desc = reinterpret_cast<kvc_segment_desc*>(lane.ptr + buf_bytes);
     if (run_encode(P, layout, plan, nseg, s) != hipSuccess) return KVC_E_HIP;
-    if (hipMemcpyAsync(host_out, lane.ptr, host_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
+    // The spill bytes used are known only on the device: read the cursor
+    // back once for the batch (into the host mirror of the call's own ring
+    // bytes), start the slot and descriptor copies, then wait for the
+    // encode and copy exactly the used spill bytes.
+    unsigned long long* h_cursor = reinterpret_cast<unsigned long long*>(
+        ctx->staging + roff + (reinterpret_cast<uint8_t*>(P.spill_cursor) - (ctx->arena + roff)));
+    if (hipMemcpyAsync(h_cursor, P.spill_cursor, sizeof(*h_cursor), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipEventRecord(lane.last, s) != hipSuccess ||
+        hipMemcpyAsync(host_out, lane.ptr, plan.total, hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipMemcpyAsync(host_desc, P.desc, desc_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipEventSynchronize(lane.last) != hipSuccess)
+      return KVC_E_HIP;
+    const size_t used = std::min<size_t>((size_t)*h_cursor, host_bytes - plan.total);
+    if ((used && hipMemcpyAsync(static_cast<uint8_t*>(host_out) + plan.total, lane.ptr + plan.total, used,
+                                hipMemcpyDeviceToHost, s) != hipSuccess) ||
         hipEventRecord(lane.last, s) != hipSuccess)
       return KVC_E_HIP;
+    if (host_used) *host_used = plan.total + used;
     return ring_commit(ctx, roff, rsize, s);
   });
 }
 
-kvc_status kvc_restore_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec, const void* host_in,
+kvc_status kvc_restore_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_codec* codec_in, const void* host_in,
                              size_t in_bytes, const int32_t* dst_page_ids, uint32_t n_pages, uint32_t layer_begin,
                              uint32_t layer_end, uint8_t* seg_status, void* const* layer_ready, void* stream) {
   return no_throw([&]() -> kvc_status {
-    if (!ctx) return KVC_E_ARG;
+    if (!ctx || !codec_in) return KVC_E_ARG;
+    kvc_codec codec_crc = *codec_in;                 // the lane always checks the segments' CRC32
+    codec_crc.flags |= KVC_CODEC_CRC32;
+    const kvc_codec* codec = &codec_crc;
     kvc_status st = kvc_validate_decode(layout, codec, dst_page_ids, n_pages, in_bytes);
     if (st != KVC_OK) return st;
     if (layer_begin > layer_end || layer_end > layout->layers) return KVC_E_ARG;

@@ -138,6 +138,11 @@ def test_validation_errors():
     assert V(ok, c, ids, 1 << 40) == kvc.KVC_E_ARG
     c.c.flags, c.c.reserved = kvc.KVC_CODEC_CRC32, 1
     assert V(ok, c, ids, 1 << 40) == kvc.KVC_E_ARG
+    # the entropy stage needs the segment CRC32 (a corrupted stream shows only after decoding)
+    for pair in (("ANS16", "INT8"), ("TQ4", "ANS16"), ("ANS16", "ANS16")):
+        assert V(ok, kvc.Codec(*pair), ids, 1 << 40) == kvc.KVC_E_ARG
+        assert V(ok, kvc.Codec(*pair, crc=True), ids, 1 << 40) == kvc.KVC_OK
+        assert kvc.kvc_validate_decode(ok, kvc.Codec(*pair), ids, 1 << 40) == kvc.KVC_E_ARG
     lay_old = layout()
     lay_old.c.abi = 1                                   # callers built against the previous ABI
     assert V(lay_old, kvc.Codec("TQ4", "UNIFORM4"), ids, 1 << 40) == kvc.KVC_E_ARG
@@ -171,7 +176,7 @@ def test_lane_and_layer_entry_points_validate_first():
     slot, _, _ = kvc.kvc_plan(lay, codec, 3)
     L = kvc.lib()
     lc, cc = ctypes.byref(lay.c), ctypes.byref(codec.c)
-    assert L.kvc_offload_pages(None, lc, cc, idp, 3, None, slot, None, None) == kvc.KVC_E_ARG
+    assert L.kvc_offload_pages(None, lc, cc, idp, 3, None, slot, None, None, None) == kvc.KVC_E_ARG
     assert L.kvc_restore_pages(None, lc, cc, None, slot, idp, 3, 0, 4, None, None, None) == kvc.KVC_E_ARG
     assert L.kvc_decode_layers(None, lc, cc, None, slot, idp, 3, 0, 4, None, None) == kvc.KVC_E_ARG
     fake = ctypes.c_void_p(16)

@@ -37,9 +37,10 @@ def pinned(nbytes):
 
 
 class Case:
-    """A small call: workload, codec, page ids, and the oracle's encode."""
+    """A small call: workload, codec, page ids, and the oracle's encode (with
+    a CRC32 per segment by default: the lane always stores one)."""
 
-    def __init__(self, ck, cv, L=4, H=8, D=128, T=16, pool=40, n=13, seed=5, protected=None, crc=False,
+    def __init__(self, ck, cv, L=4, H=8, D=128, T=16, pool=40, n=13, seed=5, protected=None, crc=True,
                  inject=False, layout="separate", dtype="bf16"):
         self.wl = G.Workload(L, H, D, T, pool, dtype, layout, seed)
         self.ids = inputs.random_page_ids(pool, n, seed=seed + 1)
@@ -87,30 +88,48 @@ class Case:
 
 CASES = {
     "tq4-u4-prot": dict(ck="TQ4", cv="UNIFORM4", protected=[0]),
-    "int8-fp8dyn-spill-crc": dict(ck="INT8", cv="FP8_DYNAMIC", inject=True, crc=True),
+    "int8-fp8dyn-spill": dict(ck="INT8", cv="FP8_DYNAMIC", inject=True),
     "tq3-u3-d256-packed-fp16": dict(ck="TQ3", cv="UNIFORM3", D=256, H=4, layout="packed", dtype="fp16"),
-    "int8rows-u4-crc": dict(ck="INT8_ROWS", cv="UNIFORM4", crc=True),
-    "ans16-fp8dyn-crc": dict(ck="ANS16", cv="FP8_DYNAMIC", crc=True),
+    "int8rows-u4": dict(ck="INT8_ROWS", cv="UNIFORM4"),
+    "ans16-fp8dyn": dict(ck="ANS16", cv="FP8_DYNAMIC"),
     "ans16-ans16-prot": dict(ck="ANS16", cv="ANS16", protected=[1]),
+    "tq4-u4-nocrc-codec": dict(ck="TQ4", cv="UNIFORM4", crc=False),
 }
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_offload_then_restore(ctx, name):
-    """Offload to pinned host memory equals the oracle's encode; a restore of
-    all layers from it equals the oracle's decode, statuses 0."""
+    """Offload to pinned host memory equals the oracle's encode with a CRC32
+    per segment (the lane adds it to a codec without one); only the slot
+    region and the spill bytes the encode used are copied -- the rest of
+    the host buffer keeps its previous bytes -- and the size returned
+    counts exactly those.  A restore of all layers from those bytes equals
+    the oracle's decode, statuses 0."""
     print(f"[case] offload/restore {name}", flush=True)
     cs = Case(**CASES[name])
+    if not cs.crc:                      # the lane's own CRC: compare with the oracle's CRC encode
+        cs = Case(**dict(CASES[name], crc=True))
+        codec = kvc.Codec(CASES[name]["ck"], CASES[name]["cv"], seed=cs.seed, protected_layers=cs.protected,
+                          layers=cs.wl.L, crc=False)
+    else:
+        codec = cs.codec
     host = pinned(cs.total)
+    host.fill_(0xA7)
     hdesc = pinned(cs.nseg * 32)
-    kvc.kvc_offload_pages(ctx, cs.wl.layout, cs.codec, cs.ids, host.data_ptr(), cs.total, hdesc.data_ptr())
+    used = kvc.kvc_offload_pages(ctx, cs.wl.layout, codec, cs.ids, host.data_ptr(), cs.total, hdesc.data_ptr())
     torch.cuda.synchronize()
-    cs.check_encoded(host.numpy(), hdesc.numpy().view(kvc.DESC_DTYPE))
+    hb = host.numpy()
+    d = hdesc.numpy().view(kvc.DESC_DTYPE)
+    spilled = (d["flags"] & (kvc.KVC_FLAG_RAW_DATA | kvc.KVC_FLAG_HEAP)) != 0
+    spilled &= d["status"] != kvc.KVC_SEG_CAPACITY
+    expect = cs.slot + int(((d["stored_len"][spilled].astype(np.int64) + 255) // 256 * 256).sum())
+    assert used == expect, (used, expect)
+    assert np.all(hb[used:] == 0xA7), "bytes beyond the used spill region were copied"
+    cs.check_encoded(hb, d)
 
     dst = cs.wl.empty_like(fill_bits=POISON)
     st = torch.full((cs.nseg,), 255, dtype=torch.uint8, device="cuda")
-    kvc.kvc_restore_pages(ctx, dst.layout, cs.codec, host.data_ptr(), cs.total, cs.ids, 0, cs.wl.L,
-                          st.data_ptr())
+    kvc.kvc_restore_pages(ctx, dst.layout, codec, host.data_ptr(), used, cs.ids, 0, cs.wl.L, st.data_ptr())
     torch.cuda.synchronize()
     assert np.all(st.cpu().numpy() == 0)
     cs.check_decoded(dst, set(range(cs.wl.L)))

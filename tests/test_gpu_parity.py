@@ -114,7 +114,7 @@ def test_small_grid(ctx, pair, dim, dtype, layout):
     fixed = _fixed_scales(L) if "FP8_FIXED" in pair else None
     dst = inputs.random_page_ids(pool, 5, seed=dim + 1)
     _roundtrip_case(ctx, wl, pair[0], pair[1], seed=1234 + dim, page_ids=ids, protected=[1], fixed=fixed,
-                    dst_ids=dst)
+                    dst_ids=dst, crc="ANS16" in pair)
 
 
 @pytest.mark.parametrize("layout", ["separate", "packed"])
@@ -132,7 +132,7 @@ def test_wide_grid(ctx, pair, dim, layout):
     fixed = _fixed_scales(2) if "FP8_FIXED" in pair else None
     dst = inputs.random_page_ids(6, 3, seed=dim + 6)
     _roundtrip_case(ctx, wl, pair[0], pair[1], seed=99 + dim, page_ids=ids, protected=[0], fixed=fixed,
-                    dst_ids=dst)
+                    dst_ids=dst, crc="ANS16" in pair)
 
 
 @pytest.mark.parametrize("heads", [3, 12, 40])
@@ -516,7 +516,8 @@ def test_ans16_llama3_full_size(ctx):
     wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
     ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
     segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 13)
-    ora_st, gdesc = _roundtrip_case(ctx, wl, "ANS16", "ANS16", 0, ids, segments=segs, decode_from_oracle=False)
+    ora_st, gdesc = _roundtrip_case(ctx, wl, "ANS16", "ANS16", 0, ids, segments=segs, decode_from_oracle=False,
+                                    crc=True)
     assert all(int(ora_st[s]) == O.SEG_ENCODED for s in segs)
 
 
@@ -526,15 +527,14 @@ def _bf16_planes(hi, lo):
     return (b - (b >= 32768).to(b.dtype) * 65536).to(torch.int16).view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("crc", [False, True])
-def test_ans16_plane_modes(ctx, crc):
+def test_ans16_plane_modes(ctx):
     """ANS16 with each kind of payload the decoder distinguishes, 8 heads x
     D128 BF16 (32 KiB segments), 2 layers x 4 of 9 blocks: both byte planes
     coded (small integers), only the low plane coded (random high bytes,
     low bytes from 4 values), only the high plane coded (Gaussian data), and
     neither (uniform bits: stored raw).  The plane modes are checked on the
     oracle's own coding of the planes; every segment is compared."""
-    print(f"[case] ans16 plane modes crc={crc}", flush=True)
+    print("[case] ans16 plane modes", flush=True)
     wl = G.Workload(2, 8, 128, 16, 9, "bf16", "separate", seed=21)
     g = torch.Generator(device="cuda").manual_seed(77)
     shape = wl.k[0].shape
@@ -554,7 +554,7 @@ def test_ans16_plane_modes(ctx, crc):
         got = tuple(int(O.ans_encode_plane((bits >> (8 * pl)) & 0xFF)[0]) for pl in (0, 1))
         assert got == modes, f"layer {l} comp {c}: plane modes {got}"
     ora_st, _ = _roundtrip_case(ctx, wl, "ANS16", "ANS16", 0, ids, dst_ids=inputs.random_page_ids(9, 4, seed=4),
-                                crc=crc)
+                                crc=True)
     seglist = G.segments_of(wl.L, len(ids))
     for sidx, (l, i, c) in enumerate(seglist):
         want = O.SEG_RAW_DATA if (l, c) == (1, 1) else O.SEG_ENCODED
@@ -571,7 +571,7 @@ def test_ans16_two_raw_planes_payload(ctx):
     wl = G.Workload(1, 8, 128, 16, 4, "bf16", "separate", seed=5)
     ids = np.array([2, 0], np.int32)
     kc = vc = kvc.CODECS["ANS16"]
-    codec = kvc.Codec(kc, vc, seed=0, layers=wl.L)
+    codec = kvc.Codec(kc, vc, seed=0, layers=wl.L, crc=True)
     out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids)
     torch.cuda.synchronize()
     gdesc = G.desc_np(desc)
@@ -589,6 +589,7 @@ def test_ans16_two_raw_planes_payload(ctx):
     so = int(gdesc[0]["offset"])
     crafted[so + 12:so + 16] = np.array([payload.size], np.uint32).view(np.uint8)    # stored_len
     crafted[so + 16:so + 24] = np.array([at], np.uint64).view(np.uint8)              # spill offset
+    crafted[so + 24:so + 28] = np.array([O.crc32(payload)], np.uint32).view(np.uint8)  # its CRC32
     ora = G.oracle_decode_segments(crafted, wl, kc, vc, 0, len(ids), None, [0, 1, 2, 3])
     assert np.array_equal(ora[0].reshape(-1), src)
     dst = wl.empty_like(fill_bits=0x7FC1)
@@ -796,14 +797,17 @@ def test_crc_spill_capacity(ctx):
 
 def test_ans16_corrupted_payloads_match_oracle(ctx):
     """Bytes of an ANS16 payload changed at random (plane headers, bitmap,
-    frequencies, stream lengths, streams, padding; no CRC): the GPU accepts
-    exactly the payloads the oracle accepts (status 0 or 1) and then decodes
-    the same values.  200 trials over the 4 segments of a small call."""
+    frequencies, stream lengths, streams, padding).  As stored, every such
+    payload fails its CRC32: status 3, the page untouched, as the oracle
+    rejects it.  With the header's CRC32 recomputed over the changed bytes,
+    the structural checks decide: the GPU accepts exactly the payloads the
+    oracle accepts (status 0 or 1) and then decodes the same values.  200
+    trials over the 4 segments of a small call."""
     print("[case] ans16 corrupted payloads", flush=True)
     wl = G.Workload(1, 8, 128, 16, 3, "bf16", "separate", seed=41)
     ids = np.array([2, 0], np.int32)
     kc = vc = kvc.CODECS["ANS16"]
-    codec = kvc.Codec(kc, vc, seed=0, layers=wl.L)
+    codec = kvc.Codec(kc, vc, seed=0, layers=wl.L, crc=True)
     out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids)
     torch.cuda.synchronize()
     gdesc = G.desc_np(desc)
@@ -815,28 +819,41 @@ def test_ans16_corrupted_payloads_match_oracle(ctx):
     accepted = 0
     for trial in range(200):
         s_ = int(rng.integers(4))
-        so, nb = int(gdesc[s_]["spill_offset"]), int(gdesc[s_]["stored_len"])
+        so, nb, off = int(gdesc[s_]["spill_offset"]), int(gdesc[s_]["stored_len"]), int(gdesc[s_]["offset"])
         bad = buf.copy()
+        flips = set()
         for _ in range(int(rng.integers(1, 4))):
             if rng.random() < 0.5:                          # the plane headers, bitmap, frequencies and lengths
                 pos = so + int(rng.integers(min(nb, 800)))
             else:
                 pos = so + int(rng.integers(nb))
-            bad[pos] ^= np.uint8(1 << int(rng.integers(8)))
-        try:
-            ora = G.oracle_decode_segments(bad, wl, kc, vc, 0, len(ids), None, [s_])[s_]
-        except ValueError:
-            ora = None
-        dev.copy_(torch.from_numpy(bad))
-        dst = wl.empty_like(fill_bits=0x7FC1)
-        st = G.gpu_decode(ctx, dst, codec, dev, total, ids).cpu().numpy()
-        torch.cuda.synchronize()
-        assert int(st[s_]) == (1 if ora is None else 0), f"trial {trial}: segment {s_} status {st[s_]}"
-        assert all(int(st[t]) == 0 for t in range(4) if t != s_)
-        if ora is not None:
-            accepted += 1
-            l, i, c = seglist[s_]
-            assert np.array_equal(G.gpu_segment_vectors(dst, l, c, int(ids[i])), ora), f"trial {trial}"
+            flips.add((pos, int(rng.integers(8))))         # distinct bits: the bytes always change
+        for pos, bit in flips:
+            bad[pos] ^= np.uint8(1 << bit)
+        l, i, c = seglist[s_]
+        for patched in (False, True):
+            if patched:
+                bad[off + 24:off + 28] = np.array([O.crc32(bad[so:so + nb])], np.uint32).view(np.uint8)
+            try:
+                ora = G.oracle_decode_segments(bad, wl, kc, vc, 0, len(ids), None, [s_])[s_]
+                ora_st = 0
+            except O.ChecksumError:
+                ora, ora_st = None, 3
+            except ValueError:
+                ora, ora_st = None, 1
+            dev.copy_(torch.from_numpy(bad))
+            dst = wl.empty_like(fill_bits=0x7FC1)
+            st = G.gpu_decode(ctx, dst, codec, dev, total, ids).cpu().numpy()
+            torch.cuda.synchronize()
+            assert int(st[s_]) == ora_st, f"trial {trial} patched={patched}: segment {s_} status {st[s_]}"
+            assert patched or ora_st == 3
+            assert all(int(st[t]) == 0 for t in range(4) if t != s_)
+            got = G.gpu_segment_vectors(dst, l, c, int(ids[i]))
+            if ora is not None:
+                accepted += 1
+                assert np.array_equal(got, ora), f"trial {trial}"
+            elif ora_st == 3:
+                assert np.all(got == 0x7FC1), f"trial {trial}: a page written despite a CRC mismatch"
     assert accepted < 200
 
 
@@ -849,7 +866,7 @@ def test_ans16_spill_capacity(ctx):
     L, H, D, T, pool = 2, 8, 128, 16, 8
     wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 14)
     ids = np.arange(pool, dtype=np.int32)
-    codec = kvc.Codec(kvc.KVC_ANS16, kvc.KVC_ANS16, seed=0, layers=L)
+    codec = kvc.Codec(kvc.KVC_ANS16, kvc.KVC_ANS16, seed=0, layers=L, crc=True)
     out, desc, slot, total = G.gpu_encode(ctx, wl, codec, ids, spill_bytes=10 * 24 * 1024)
     torch.cuda.synchronize()
     d = G.desc_np(desc)
@@ -861,7 +878,7 @@ def test_ans16_spill_capacity(ctx):
     for sidx in enc:
         l, i, c = seglist[sidx]
         src = G.gpu_segment_vectors(wl, l, c, int(ids[i]))
-        _, ost, payload = O.encode_segment(src, wl.dt, kvc.KVC_ANS16, component=c, heads=H)
+        _, ost, payload = O.encode_segment(src, wl.dt, kvc.KVC_ANS16, component=c, heads=H, crc=True)
         so, nb = int(d[sidx]["spill_offset"]), int(d[sidx]["stored_len"])
         assert ost == O.SEG_ENCODED and nb == payload.size and slot <= so and so + nb <= total
         assert np.array_equal(buf[so:so + nb], payload), f"segment {sidx}: payload differs"
