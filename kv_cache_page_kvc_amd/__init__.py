@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvc.so")
+# KVC_LIB: another build of the same sources (the host sanitizer build)
+LIB_PATH = os.environ.get("KVC_LIB") or os.path.join(HERE, "libkvc.so")
 
 KVC_ABI_VERSION = 2
 KVC_SLOT_ALIGN = 256

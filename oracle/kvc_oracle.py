@@ -21,7 +21,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
-_LIB = os.path.join(_HERE, "libkvc_oracle.so")
+# KVC_ORACLE_LIB: another build of the same source (the sanitizer test)
+_LIB = os.environ.get("KVC_ORACLE_LIB") or os.path.join(_HERE, "libkvc_oracle.so")
 
 RAW, FP8_DIRECT, FP8_FIXED, FP8_DYNAMIC, INT8, UNIFORM3, UNIFORM4, TQ3, TQ4, INT8_ROWS, ANS16 = range(11)
 CODEC_NAMES = ["RAW", "FP8_DIRECT", "FP8_FIXED", "FP8_DYNAMIC", "INT8",
