@@ -208,10 +208,10 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
   const uint32_t l = seg / two_n;
   const uint32_t rem = seg - l * two_n;
   const uint32_t pi = rem >> 1, comp = rem & 1;
-  const SideEntry& E = p.sides[2 * l + comp];
+  const SideEntry E = side_entry(p, 2 * l + comp);
   if (E.codec != C_ANS) return;
   const uint64_t slot_off = E.slot_base + (uint64_t)pi * E.page_stride;
-  const int32_t page = p.pages[pi];
+  const int32_t page = page_id(p, pi);
   kvc_segment_desc* desc = p.desc + seg;
   const uint32_t lane = threadIdx.x;
   if ((uint64_t)(uintptr_t)E.base < p.base_lo || (uint64_t)(uintptr_t)E.base > p.base_hi || page < 0 ||
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64) void ans_encode_kernel(CallParams p) {
   const uint32_t payload = psize[0] + psize[1];
   const bool keep = 8 * (E.slot_bytes + ((payload + 255) & ~255u)) <= 7 * raw_bytes;
   const uint32_t need = keep ? ((payload + 255) & ~255u) : ((raw_bytes + 255) & ~255u);
-  if (lane == 0) s_off = atomicAdd(p.spill_cursor, (unsigned long long)need);
+  if (lane == 0) s_off = spill_reserve(p, need);
   __syncthreads();
   const uint64_t off = p.slot_region + s_off;
   const bool fits = off + need <= p.buf_bytes;
@@ -564,10 +564,10 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   const uint32_t l = seg / two_n;
   const uint32_t rem = seg - l * two_n;
   const uint32_t pi = rem >> 1, comp = rem & 1;
-  const SideEntry& E = p.sides[2 * l + comp];
+  const SideEntry E = side_entry(p, 2 * l + comp);
   if (E.codec != C_ANS) return;
   const uint64_t slot_off = E.slot_base + (uint64_t)pi * E.page_stride;
-  const int32_t page = p.pages[pi];
+  const int32_t page = page_id(p, pi);
   const uint32_t lane = threadIdx.x;
   const bool report = p.seg_status && lane == 0;
   if ((uint64_t)(uintptr_t)E.base < p.base_lo || (uint64_t)(uintptr_t)E.base > p.base_hi || page < 0 ||

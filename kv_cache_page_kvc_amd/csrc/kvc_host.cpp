@@ -38,6 +38,7 @@ struct kvc_ctx {
   uint8_t* arena = nullptr;          // device: [Tables | ring]
   uint8_t* staging = nullptr;        // pinned host mirror of the ring
   size_t ring_begin = 0, ring_end = 0, head = 0;
+  uint64_t small_encodes = 0;        // encode calls whose spill cursor is a pool slot
   struct InFlight {
     size_t off, size;
     hipEvent_t ev;
@@ -372,6 +373,9 @@ size_t call_bytes(uint32_t layers, uint32_t n) {
 }
 
 size_t tables_bytes() { return align_up(sizeof(Tables), kAlign); }
+// arena: [Tables | spill-cursor pool of small encode calls | ring]
+size_t cursor_pool_offset() { return tables_bytes(); }
+size_t cursor_pool_bytes() { return align_up(sizeof(unsigned long long) * kCursorSlots, kAlign); }
 
 struct DeviceGuard {
   int old = -1;
@@ -420,6 +424,7 @@ kvc_status ring_alloc(kvc_ctx* ctx, size_t size, size_t* off) {
 }
 
 kvc_status ring_commit(kvc_ctx* ctx, size_t off, size_t size, hipStream_t stream) {
+  if (size == 0) return KVC_OK;                 // the call took no ring bytes
   hipEvent_t ev;
   if (!ctx->free_events.empty()) {
     ev = ctx->free_events.back();
@@ -538,17 +543,40 @@ void fill_call(const kvc_layout* L, const kvc_codec* c, const Plan& plan, uint32
   sign_mask(c->seed, L->head_dim, P->sign_mask);
 }
 
-// stage layer table + page ids + zeroed spill cursor in the context's ring,
-// upload, fill params
+// Stage the call's layer table, page ids and zeroed spill cursor (encode
+// only: cursor = true), fill params.  A small call (at most kInlineSides
+// side entries and kInlinePages pages) carries its table and page ids in the
+// kernel arguments; only an encode's cursor then takes ring bytes, zeroed by
+// a one-thread kernel.  Larger calls stage everything in the context's ring
+// and upload it in one copy.  ring_size is 0 when no ring bytes were taken.
 kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, const Plan& plan,
                       const int32_t* pages, uint32_t n, hipStream_t stream, CallParams* P, size_t* ring_off,
-                      size_t* ring_size) {
+                      size_t* ring_size, bool cursor) {
+  *ring_off = 0;
+  *ring_size = 0;
+  P->tables = reinterpret_cast<const Tables*>(ctx->arena);
+  if (2 * L->layers <= kInlineSides && n <= kInlinePages) {
+    fill_call(L, c, plan, n, P->sides_inline, P);
+    std::memcpy(P->pages_inline, pages, sizeof(int32_t) * (size_t)n);
+    P->inline_tables = 1;
+    P->sides = nullptr;
+    P->pages = nullptr;
+    P->spill_cursor = nullptr;
+    P->cursor_lap = 0;
+    if (!cursor) return KVC_OK;
+    // a pool slot tagged with this call's lap: no upload, no clearing launch
+    const uint64_t k = ctx->small_encodes++;
+    P->spill_cursor = reinterpret_cast<unsigned long long*>(ctx->arena + cursor_pool_offset()) + k % kCursorSlots;
+    P->cursor_lap = (uint32_t)((k / kCursorSlots) % ((1u << (64 - kCursorLapShift)) - 1u)) + 1u;
+    return KVC_OK;
+  }
   const size_t need = call_bytes(L->layers, n);
   size_t off = 0;
   kvc_status st = ring_alloc(ctx, need, &off);
   if (st != KVC_OK) return st;
   uint8_t* h = ctx->staging + off;
   fill_call(L, c, plan, n, reinterpret_cast<SideEntry*>(h), P);
+  P->inline_tables = 0;
   const size_t pages_off = align_up(sizeof(SideEntry) * 2 * L->layers, kAlign);
   std::memcpy(h + pages_off, pages, sizeof(int32_t) * (size_t)n);
   const size_t cur_off = pages_off + align_up(sizeof(int32_t) * (size_t)n, kAlign);
@@ -558,7 +586,6 @@ kvc_status stage_call(kvc_ctx* ctx, const kvc_layout* L, const kvc_codec* c, con
   P->sides = reinterpret_cast<const SideEntry*>(d);
   P->pages = reinterpret_cast<const int32_t*>(d + pages_off);
   P->spill_cursor = reinterpret_cast<unsigned long long*>(d + cur_off);
-  P->tables = reinterpret_cast<const Tables*>(ctx->arena);
   *ring_off = off;
   *ring_size = need;
   return KVC_OK;
@@ -702,7 +729,7 @@ kvc_status kvc_create(kvc_ctx** out, int hip_device, size_t workspace_budget) {
     if (!out) return KVC_E_ARG;
     *out = nullptr;
     if (workspace_budget == 0) workspace_budget = KVC_DEFAULT_WORKSPACE;
-    const size_t tb = tables_bytes();
+    const size_t tb = tables_bytes() + cursor_pool_bytes();
     if (workspace_budget < tb + 4 * kAlign) return KVC_E_BUDGET;
     DeviceGuard g(hip_device);
     if (!g.ok) return KVC_E_HIP;
@@ -717,7 +744,9 @@ kvc_status kvc_create(kvc_ctx** out, int hip_device, size_t workspace_budget) {
     ctx->head = ctx->ring_begin;
     bool ok = hipMalloc(&ctx->arena, workspace_budget) == hipSuccess &&
               hipHostMalloc(&ctx->staging, ctx->ring_end, hipHostMallocDefault) == hipSuccess &&
-              hipMemcpy(ctx->arena, t.get(), sizeof(Tables), hipMemcpyHostToDevice) == hipSuccess;
+              hipMemcpy(ctx->arena, t.get(), sizeof(Tables), hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemset(ctx->arena + cursor_pool_offset(), 0, cursor_pool_bytes()) == hipSuccess &&
+              hipDeviceSynchronize() == hipSuccess;
     if (!ok) {
       kvc_destroy(ctx);
       return KVC_E_HIP;
@@ -771,7 +800,7 @@ kvc_status kvc_encode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_co
     hipStream_t s = static_cast<hipStream_t>(stream);
     CallParams P{};
     size_t roff = 0, rsize = 0;
-    st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize);
+    st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize, true);
     if (st != KVC_OK) return st;
     P.buf = static_cast<uint8_t*>(out);
     P.buf_bytes = out_bytes;
@@ -799,7 +828,7 @@ kvc_status kvc_decode_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_co
     hipStream_t s = static_cast<hipStream_t>(stream);
     CallParams P{};
     size_t roff = 0, rsize = 0;
-    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize, false);
     if (st != KVC_OK) return st;
     P.buf = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
     P.buf_bytes = in_bytes;
@@ -828,7 +857,7 @@ kvc_status kvc_decode_layers(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     hipStream_t s = static_cast<hipStream_t>(stream);
     CallParams P{};
     size_t roff = 0, rsize = 0;
-    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize, false);
     if (st != KVC_OK) return st;
     P.buf = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
     P.buf_bytes = in_bytes;
@@ -867,7 +896,7 @@ kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     if (hipStreamWaitEvent(s, lane.last, 0) != hipSuccess) return KVC_E_HIP;   // the previous offload's copies
     CallParams P{};
     size_t roff = 0, rsize = 0;
-    st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize);
+    st = stage_call(ctx, layout, codec, plan, page_ids, n_pages, s, &P, &roff, &rsize, true);
     if (st != KVC_OK) return st;
     P.buf = lane.ptr;
     P.buf_bytes = host_bytes;
@@ -879,14 +908,17 @@ kvc_status kvc_offload_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     // bytes), start the slot and descriptor copies, then wait for the
     // encode and copy exactly the used spill bytes.
     unsigned long long* h_cursor = reinterpret_cast<unsigned long long*>(
-        ctx->staging + roff + (reinterpret_cast<uint8_t*>(P.spill_cursor) - (ctx->arena + roff)));
+        ctx->staging + (reinterpret_cast<uint8_t*>(P.spill_cursor) - ctx->arena));
     if (hipMemcpyAsync(h_cursor, P.spill_cursor, sizeof(*h_cursor), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipEventRecord(lane.last, s) != hipSuccess ||
         hipMemcpyAsync(host_out, lane.ptr, plan.total, hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipMemcpyAsync(host_desc, P.desc, desc_bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipEventSynchronize(lane.last) != hipSuccess)
       return KVC_E_HIP;
-    const size_t used = std::min<size_t>((size_t)*h_cursor, host_bytes - plan.total);
+    uint64_t cur = *h_cursor;
+    if (P.cursor_lap)                            // a pool slot: this call's bytes, or none if another lap's tag
+      cur = (cur >> kCursorLapShift) == P.cursor_lap ? cur & ((1ull << kCursorLapShift) - 1) : 0;
+    const size_t used = std::min<size_t>((size_t)cur, host_bytes - plan.total);
     if ((used && hipMemcpyAsync(static_cast<uint8_t*>(host_out) + plan.total, lane.ptr + plan.total, used,
                                 hipMemcpyDeviceToHost, s) != hipSuccess) ||
         hipEventRecord(lane.last, s) != hipSuccess)
@@ -930,7 +962,7 @@ kvc_status kvc_restore_pages(kvc_ctx* ctx, const kvc_layout* layout, const kvc_c
     auto& lane = ctx->lane[1];
     CallParams P{};
     size_t roff = 0, rsize = 0;
-    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize);
+    st = stage_call(ctx, layout, codec, plan, dst_page_ids, n_pages, s, &P, &roff, &rsize, false);
     if (st != KVC_OK) return st;
     P.buf = lane.ptr;
     P.buf_bytes = in_bytes;

@@ -109,6 +109,17 @@ struct SideEntry {
 };
 static_assert(sizeof(SideEntry) == 32, "SideEntry is a 32-byte record");
 
+// the largest call whose side table and page ids ride in the kernel arguments
+constexpr uint32_t kInlineSides = 16;         // 2 * layers
+constexpr uint32_t kInlinePages = 256;
+// Spill cursors of such calls: a pool of 8-byte slots in the context's
+// arena, zero when the context is created and never reset; call k uses slot
+// k mod kCursorSlots and tags its value with the lap k / kCursorSlots + 1
+// (bits 40..63), so the first reservation of a call starts from zero
+// whatever an earlier call left in the slot.  Offsets use bits 0..39.
+constexpr uint32_t kCursorSlots = 65536;
+constexpr int kCursorLapShift = 40;
+
 struct CallParams {
   const SideEntry* sides;                     // [2 * n_layers]
   const int32_t* pages;                       // source (encode) / destination (decode) block ids
@@ -119,6 +130,7 @@ struct CallParams {
   kvc_segment_desc* desc;                     // encode: descriptors (device)
   uint8_t* seg_status;                        // decode: statuses (device, may be null)
   unsigned long long* spill_cursor;           // encode: bytes used in the spill region
+  uint32_t cursor_lap;                        // 0: spill_cursor starts at zero; else its lap tag
   uint64_t base_lo, base_hi;                  // range of every layer base pointer (guard)
   int64_t sb, st, sh;                         // element strides
   uint64_t heads_magic;                       // ceil(2^32 / heads): t = (v * magic) >> 32 = v / heads
@@ -144,6 +156,11 @@ struct CallParams {
   uint32_t dtype;                             // kvc_dtype
   uint32_t num_blocks;                        // page ids must be below this (guard)
   uint32_t sign_mask[8];                      // TurboQuant signs, bit i = (sigma_i < 0)
+  // Small calls: the side table and the page ids travel in the kernel
+  // arguments (inline_tables = 1), so nothing is uploaded before the launch
+  uint32_t inline_tables;
+  SideEntry sides_inline[kInlineSides];
+  int32_t pages_inline[kInlinePages];
 };
 
 // Allocation-free encode (kvc_encode_pages_noalloc): every call on a GPU

@@ -292,6 +292,42 @@ __device__ __forceinline__ const T* byte_at(const T* base, uint32_t off) {
   return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
 }
 
+// The call's side-table entry idx and page id i: from the kernel arguments
+// for a small call, else from the table the host uploaded.  Both are read
+// through the constant address space, so the loads stay scalar.
+typedef const __attribute__((address_space(4))) uint64_t ConstU64;
+typedef const __attribute__((address_space(4))) int32_t ConstI32;
+__device__ __forceinline__ SideEntry side_entry(const CallParams& p, uint32_t idx) {
+  static_assert(sizeof(SideEntry) == 4 * sizeof(uint64_t), "a side entry is four 8-byte words");
+  ConstU64* t = p.inline_tables ? (ConstU64*)&p.sides_inline[0] : (ConstU64*)p.sides;
+  uint64_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) w[i] = t[4 * idx + i];
+  SideEntry e;
+  __builtin_memcpy(&e, w, sizeof(e));
+  return e;
+}
+__device__ __forceinline__ int32_t page_id(const CallParams& p, uint32_t i) {
+  ConstI32* t = p.inline_tables ? (ConstI32*)&p.pages_inline[0] : (ConstI32*)p.pages;
+  return t[i];
+}
+
+// Reserve `need` bytes of the spill region: the offset of the reservation.
+// A cursor with a lap tag holds the lap in its high bits; the call's first
+// reservation replaces a value from an earlier lap, the others add to it.
+__device__ __forceinline__ uint64_t spill_reserve(const CallParams& p, uint64_t need) {
+  if (p.cursor_lap == 0) return atomicAdd(p.spill_cursor, (unsigned long long)need);
+  const unsigned long long tag = (unsigned long long)p.cursor_lap << kCursorLapShift;
+  unsigned long long cur = *reinterpret_cast<volatile unsigned long long*>(p.spill_cursor);
+  for (;;) {
+    const bool mine = (cur >> kCursorLapShift) == p.cursor_lap;
+    const unsigned long long next = mine ? cur + need : tag + need;
+    const unsigned long long prev = atomicCAS(p.spill_cursor, cur, next);
+    if (prev == cur) return mine ? cur - tag : 0ull;
+    cur = prev;
+  }
+}
+
 // ------------------------------------------------------------------ encoders
 // Each returns 1 if this vector forces the segment raw.
 enum Codec { C_RAW = 0, C_FP8D = 1, C_FP8F = 2, C_FP8Y = 3, C_INT8 = 4, C_U3 = 5, C_U4 = 6, C_TQ3 = 7, C_TQ4 = 8,
@@ -932,11 +968,11 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const uint32_t l = seg / two_n;
   const uint32_t rem = seg - l * two_n;
   const uint32_t pi = rem >> 1, comp = rem & 1;
-  const SideEntry& E = p.sides[2 * l + comp];
+  const SideEntry E = side_entry(p, 2 * l + comp);
   const int codec = (int)E.codec;
   if (codec == C_ANS) return;                                   // the entropy stage's own kernel
   const uint64_t slot_off = E.slot_base + (uint64_t)pi * E.page_stride;
-  const int32_t page = p.pages[pi];
+  const int32_t page = page_id(p, pi);
   // guard: the side table and page list come from memory; never follow a
   // base pointer outside the caller's set or a page id outside the pool
   if ((uint64_t)(uintptr_t)E.base < p.base_lo || (uint64_t)(uintptr_t)E.base > p.base_hi || page < 0 ||
@@ -1042,7 +1078,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   }
   // raw because of its data: reserve spill space, copy the source bytes
   const uint64_t need = (raw_bytes + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
-  if (threadIdx.x == 0) s_spill = atomicAdd(p.spill_cursor, (unsigned long long)need);
+  if (threadIdx.x == 0) s_spill = spill_reserve(p, need);
   __syncthreads();
   const uint64_t off = s_spill;
   const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
@@ -1269,11 +1305,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   const uint32_t l = seg / two_n;
   const uint32_t rem = seg - l * two_n;
   const uint32_t pi = rem >> 1, comp = rem & 1;
-  const SideEntry& E = p.sides[2 * l + comp];
+  const SideEntry E = side_entry(p, 2 * l + comp);
   const int codec = (int)E.codec;
   if (codec == C_ANS) return;                                   // the entropy stage's own kernel
   const uint64_t slot_off = E.slot_base + (uint64_t)pi * E.page_stride;
-  const int32_t page = p.pages[pi];
+  const int32_t page = page_id(p, pi);
   if ((uint64_t)(uintptr_t)E.base < p.base_lo || (uint64_t)(uintptr_t)E.base > p.base_hi || page < 0 ||
       (uint32_t)page >= p.num_blocks || slot_off + E.slot_bytes > p.slot_region) {
     if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 2;

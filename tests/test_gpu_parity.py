@@ -352,6 +352,44 @@ def test_raw_data_unstaged_slot(ctx):
             assert (gdesc[s]["status"] == kvc.KVC_SEG_RAW_DATA) == ((l, i, c) in raw), (s, l, i, c)
 
 
+def test_small_call_spill_cursor_slots_wrap():
+    """Small encode calls take their spill cursor from a pool of 65,536 slots
+    that are never cleared: each call's first reservation must start at
+    offset 0 whatever an earlier call left in its slot.  65,539 calls in a
+    row on one context (every slot used once, then three slots again), each
+    with one data-raw segment: the raw bytes always land at the start of the
+    spill region, and the last call's output equals the oracle's."""
+    print("[case] small-call cursor slots wrap", flush=True)
+    ctx = kvc.kvc_create(0, 0)
+    try:
+        L, H, D, T, pool = 1, 1, 128, 16, 4
+        wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 23)
+        wl.k[0][1, 5, 0, 7] = float("nan")
+        ids = np.array([1, 3], np.int32)
+        codec = kvc.Codec("INT8", "INT8", seed=0, layers=L)
+        slot, _, _ = kvc.kvc_plan(wl.layout, codec, len(ids))
+        spill = 2 * H * T * D * 2
+        total = slot + spill
+        out = torch.zeros(total, dtype=torch.uint8, device="cuda")
+        desc = torch.zeros(L * len(ids) * 2 * 32, dtype=torch.uint8, device="cuda")
+        firsts = []
+        for k in range(65536 + 3):
+            kvc.kvc_encode_pages(ctx, wl.layout, codec, ids, out.data_ptr(), total, desc.data_ptr())
+            if k in (0, 1, 65535, 65536, 65537, 65538):
+                torch.cuda.synchronize()
+                d = G.desc_np(desc)
+                assert int(d[0]["status"]) == kvc.KVC_SEG_RAW_DATA and int(d[0]["spill_offset"]) == slot, (k, d[0])
+                firsts.append(k)
+        torch.cuda.synchronize()
+        assert len(firsts) == 6
+        ora_buf, ora_st, offs, ora_total = G.oracle_encode(wl, kvc.KVC_INT8, kvc.KVC_INT8, 0, ids)
+        bad = G.compare_encoded(out.cpu().numpy(), G.desc_np(desc), ora_buf, ora_st, offs, ora_total,
+                                range(L * len(ids) * 2))
+        assert not bad, bad[:5]
+    finally:
+        kvc.kvc_destroy(ctx)
+
+
 def test_spill_capacity_exhausted(ctx):
     """A spill region for only two raw segments: later raw segments report
     KVC_SEG_CAPACITY; their destination pages are left untouched and the
