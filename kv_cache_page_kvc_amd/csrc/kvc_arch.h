@@ -1,7 +1,9 @@
 // kvc_arch.h -- gfx950-specific helpers of libkvc's kernels: global-memory
 // access through address-space-1 pointers (global_load/global_store rather
-// than flat, which would also count against the LDS wait counter) and the
-// DPP-fused FMA used by the cross-lane WHT butterflies.
+// than flat, which would also count against the LDS wait counter), the
+// DPP-fused FMA used by the cross-lane WHT butterflies, and short correctly
+// rounded reciprocal and square-root sequences built on the hardware
+// estimates.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -104,6 +106,35 @@ __device__ __forceinline__ void group_minmax_dpp(float& mn, float& mx) {
         : "+v"(mn), "+v"(mx));
 }
 #undef KVC_MINMAX_STEP
+
+// RN(1/h) by one Newton step e = 1 - h*y0, y0 + e*y0 from the hardware
+// estimate y0 (accurate to one ulp), for
+//  - every positive finite h that is an FP16 value: every start within one
+//    ulp of 1/h gives the correctly rounded reciprocal (checked exhaustively
+//    on the CPU), so the estimate's own rounding does not matter;
+//  - every binary32 h in [2^-48, 2^16): the same holds for every start but
+//    one per binade (h = (2 - 2^-23) * 2^k started at 2^-(k+1), a fixed point
+//    of the step, as of every longer Newton sequence), and the device's own
+//    estimate followed by the step equals the IEEE quotient for every such h
+//    (checked exhaustively on the device).
+__device__ __forceinline__ float recip_newton(float h) {
+  const float y0 = __builtin_amdgcn_rcpf(h);
+  return fmaf(fmaf(-h, y0, 1.0f), y0, y0);
+}
+
+// Correctly rounded square root of a binary32 S in [2^-96, 2^31), without
+// the range scaling and special-value handling of the general sequence: the
+// hardware estimate s (accurate to one ulp) gives way to its lower or upper
+// neighbour s' when the sign of the residual S - s'*s shows the root past
+// the midpoint between them.  In that range a nonzero residual is at least
+// 2^-144 in magnitude, so its sign survives the FMA's rounding.  Exact for
+// every start within one ulp of the root (checked exhaustively on the CPU).
+__device__ __forceinline__ float sqrt_rn_normal(float S) {
+  const float s = __builtin_amdgcn_sqrtf(S);
+  const float sd = __uint_as_float(__float_as_uint(s) - 1u), su = __uint_as_float(__float_as_uint(s) + 1u);
+  const float t = fmaf(-sd, s, S) <= 0.0f ? sd : s;
+  return fmaf(-su, s, S) > 0.0f ? su : t;
+}
 
 template <int Q>
 __device__ __forceinline__ void fmac_xlane8(float* y, float c) {

@@ -196,7 +196,9 @@ void build_tables(Tables& t) {
     float thr[15];
     for (int k = 0; k < n; k++) t.centroids[which][k] = (float)lev[k];
     for (int k = 0; k < n - 1; k++) thr[k] = (float)(0.5 * (lev[k] + lev[k + 1]));
-    // cells: c = RNE(4 z) + 64, i.e. 4z in [c-64-0.5, c-64+0.5]
+    // cells: c = RNE(4 z) + 64, i.e. 4z in [c-64-0.5, c-64+0.5].  Every
+    // threshold lies well inside (-15.875, 15.875): the edge cells hold none,
+    // which lets the encoder clamp z to +-16 without changing a code.
     for (int c = 0; c < kCells; c++) {
       const double lo = (c - kCellOffset - 0.5) / kCellScale, hi = (c - kCellOffset + 0.5) / kCellScale;
       uint32_t below = 0;

@@ -222,16 +222,6 @@ __device__ __forceinline__ float div_scaled(float x, float s, float r) {
   return fmaf(fmaf(-q0, s, x), r, q0);
 }
 
-// RN(1/h) for a positive finite h that is an FP16 value: one Newton step
-// e = 1 - h*y0, y0 + e*y0 from the hardware estimate (within 1 ulp).  For
-// every such h, every start within 1 ulp of 1/h gives the correctly rounded
-// reciprocal (checked exhaustively), so the estimate's own rounding does not
-// matter.
-__device__ __forceinline__ float recip_f16val(float h) {
-  const float y0 = __builtin_amdgcn_rcpf(h);
-  return fmaf(fmaf(-h, y0, 1.0f), y0, y0);
-}
-
 // Uniform code of d = RN(x - m_h) against the FP16 scale s = sigma_h, as
 // the bits of RN(q + 1.5*2^23) with q = RN(d / s): for |q| < 2^22 these are
 // 0x4B400000 + RNE(q), and clamping them as integers to [0x4B400000,
@@ -502,6 +492,29 @@ __device__ __forceinline__ void vec_offsets(const SegCtx& s, int v, uint32_t met
   }
 }
 
+// TurboQuant codes of a lane's transformed values y: cell c = RNE(4z) + 64
+// of the threshold table, code = base(c) + (z > T(c)).  The caller keeps
+// |z| < 16.125, so c lies in [0, 128].
+template <int D, int BITS>
+__device__ __forceinline__ void tq_bucketize(const float* y, const CellEntry* cells, uint8_t* slot, uint32_t cv,
+                                             int p) {
+  constexpr int NCH = Geo<D>::NCH;
+  constexpr int LO = 0x4B400000 - kCellOffset;
+#pragma unroll
+  for (int k = 0; k < NCH; k++) {
+    uint32_t acc = 0;                    // element j ends up at bits [BITS*j, BITS*j + BITS)
+#pragma unroll
+    for (int j = 7; j >= 0; j--) {
+      const float z = y[8 * k + j];
+      const int t = __float_as_int(fmaf(z, kCellScale, 12582912.0f));
+      const int idx = t - LO;
+      const CellEntry ce = cells[idx];
+      acc = (acc << BITS) + ce.base + (z > ce.thr ? 1u : 0u);
+    }
+    store_codes<D, BITS>(slot, cv, k, p, acc, 0);
+  }
+}
+
 template <int D, int DT, int C>
 __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv, const Lane& ln, uint8_t* slot,
                                              float fixed, const LaneSigns<D>& ls, const CellEntry* cells) {
@@ -591,7 +604,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
     const float mh = f16_round(mn), sh = f16_round(sig);
     // +-Inf reach mn/mx and overflow the FP16 metadata; NaN is caught below
     bad = !__builtin_isfinite(mh) || !__builtin_isfinite(sh);
-    const float y = sh == 0.0f ? 0.0f : recip_f16val(sh);
+    const float y = sh == 0.0f ? 0.0f : recip_newton(sh);
     constexpr int MAGIC = 0x4B400000;   // bits of 1.5 * 2^23
     uint32_t tor = 0;
 #pragma unroll
@@ -614,11 +627,27 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
   }
 
   if constexpr (CodecInfo<C>::tq) {
-    // 1. norm (signs do not change the squares)
-    const float n = sqrtf(sumsq_tree<NCH, LOGP>(x));
+    // 1. norm (signs do not change the squares).  The common case is taken
+    // for the whole wave when every active lane's sum of squares S lies in
+    // [2^-96, 2^31): then RN(sqrt(S)) and RN(1/n) come from the short
+    // sequences (n >= 2^-48), n < 2^15.5 rounds to a finite FP16 value, and
+    // every transformed value satisfies |z| <= sqrt(D) (1 + 2^-20) < 16.125
+    // (the squares lost to underflow weigh at most 2^-46 of S, each rounding
+    // of the sum, the root, the reciprocal, the products and the butterflies
+    // at most 2^-24), so its cell index lies in the table without a clamp.
+    // Other vectors (zero, tiny, huge or non-finite) take the general path.
+    const float S = sumsq_tree<NCH, LOGP>(x);
+    const bool common = __builtin_amdgcn_ballot_w64(!(S >= 0x1p-96f && S < 0x1p31f)) == 0;
+    float n, r;
+    if (common) {
+      n = sqrt_rn_normal(S);
+      r = recip_newton(n);
+    } else {
+      n = sqrtf(S);
+      bad = !__builtin_isfinite(f16_round(n));
+      r = (n == 0.0f || bad) ? 0.0f : 1.0f / n;
+    }
     const float nh = f16_round(n);
-    bad = !__builtin_isfinite(nh);
-    const float r = (n == 0.0f || bad) ? 0.0f : 1.0f / n;
     // 2.-3. normalise the signed values
     float y[E];
 #pragma unroll
@@ -627,21 +656,16 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
     wht_inlane_low<NCH>(y);
     wht_cross<LOGP, E>(y, ln.p);
     wht_inlane_high<NCH>(y);
-    // 5. bucketize: code = #{B_k < z} = base(cell) + (z > T(cell))
-    constexpr int LO = 0x4B400000 - kCellOffset, HI = 0x4B400000 + kCellOffset;
+    // 5. bucketize: code = #{B_k < z} = base(cell) + (z > T(cell)).  Outside
+    // the common case |z| may exceed 16 (or z be NaN, in a vector that sends
+    // its segment raw); the edge cells hold no threshold, so clamping z to
+    // +-16 (NaN to -16) keeps every cell index in the table and leaves every
+    // code as it is.
+    if (!common) {
 #pragma unroll
-    for (int k = 0; k < NCH; k++) {
-      uint32_t acc = 0;                  // element j ends up at bits [BITS*j, BITS*j + BITS)
-#pragma unroll
-      for (int j = 7; j >= 0; j--) {
-        const float z = y[8 * k + j];
-        const int t = __float_as_int(fmaf(z, kCellScale, 12582912.0f));
-        const int idx = min(max(t, LO), HI) - LO;
-        const CellEntry ce = cells[idx];
-        acc = (acc << BITS) + ce.base + (z > ce.thr ? 1u : 0u);
-      }
-      store_codes<D, BITS>(slot, cv, k, ln.p, acc, 0);
+      for (int e = 0; e < E; e++) y[e] = fabsf(y[e]) <= 16.0f ? y[e] : (y[e] > 0.0f ? 16.0f : -16.0f);
     }
+    tq_bucketize<D, BITS>(y, cells, slot, cv, ln.p);
     if (ln.p == 0) *byte_at(reinterpret_cast<uint16_t*>(slot), mv) = (uint16_t)f16_bits(nh);
   }
   return bad;

@@ -9,7 +9,9 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-KERNELS = {"fp8_cvt_sweep.hip": "libkvc_test_fp8_sweep.so"}
+KERNELS = {"fp8_cvt_sweep.hip": "libkvc_test_fp8_sweep.so", "norm_sweep.hip": "libkvc_test_norm_sweep.so"}
+# the library's device helpers (kvc_arch.h) for the kernels that test them
+INCLUDES = ["-I", os.path.join(os.path.dirname(HERE), "kv_cache_page_kvc_amd", "csrc")]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -21,7 +23,7 @@ def lib_path(source: str) -> str:
 def build(verbose: bool = False) -> None:
     for src, so in KERNELS.items():
         tmp = os.path.join(HERE, so + ".tmp")
-        cmd = [HIPCC, *FLAGS, "-o", tmp, os.path.join(HERE, src)]
+        cmd = [HIPCC, *FLAGS, *INCLUDES, "-o", tmp, os.path.join(HERE, src)]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)

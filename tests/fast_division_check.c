@@ -1,6 +1,6 @@
 /*
  * Exhaustive checks of the two division shortcuts used by libkvc's kernels
- * (kvc_kernels.hip: div_const, recip_f16val), evaluated here with the same
+ * (kvc_kernels.hip: div_const; kvc_arch.h: recip_newton), evaluated here with the same
  * binary32 operations (C float with -ffp-contract=off, fmaf):
  *   1. RN(a / N) = q0 + e*r with r = RN(1/N), q0 = RN(a*r), e = fma(-q0, N, a),
  *      for every non-negative finite binary32 a and N in {7, 15, 127};

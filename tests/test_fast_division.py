@@ -1,4 +1,4 @@
-"""Exhaustive proofs of the kernels' division shortcuts (CPU only).
+"""Exhaustive proofs of the kernels' division and square-root shortcuts (CPU only).
 
 The encode kernel replaces IEEE divisions by shorter sequences: RN(a/N) for
 the constants N = 7, 15, 127 (uniform scale, INT8 scale), RN(1/h) for an
@@ -8,6 +8,8 @@ one FMA correction.  `fast_division_check.c` and
 `fast_division_scaled_check.c` run the same binary32 sequences over every
 input they can see and count results that differ from the correctly
 rounded quotient, or, for the scaled quotients, the stored codes that differ.
+`fast_norm_check.c` does the same for the TurboQuant norm and its
+reciprocal in the encoder's common case.
 """
 import os
 import shutil
@@ -112,3 +114,28 @@ def test_uniform_quotient_code_exact():
     assert res["ties_7"][0] == 0 and res["ties_7"][1] == (0x7C00 - 1) * 8 * 2050
     assert res["ties_15"][0] == 0 and res["ties_15"][1] == (0x7C00 - 1) * 16 * 2050
     assert res["small"] == (0, 3 * ((1 << 23) + (1 << 20)))
+
+
+def test_norm_sqrt_and_reciprocal_exact():
+    """TurboQuant encode, common case: RN(sqrt(S)) from the hardware estimate
+    and one neighbour test each way, for every binary32 S in [2^-96, 2^31)
+    and every start within one ulp; RN(1/n) from one Newton step for every
+    binary32 n in [2^-48, 2^16) and every start within one ulp but the one
+    fixed point per binade (n = (2 - 2^-23) 2^k from 2^-(k+1)), which
+    tests/test_gpu_norm_sweep.py rules out for the device's own estimate."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        exe = os.path.join(d, "check")
+        subprocess.run([gcc, "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-o", exe,
+                        os.path.join(HERE, "fast_norm_check.c"), "-lm"], check=True)
+        env = dict(os.environ, OMP_NUM_THREADS=str(min(16, os.cpu_count() or 1)))
+        out = subprocess.run([exe], check=True, capture_output=True, text=True, env=env, timeout=600).stdout
+    res = {ln.split()[0]: (int(ln.split()[1]), int(ln.split()[2])) for ln in out.splitlines()}
+    lo, hi = 0x0F800000, 0x4F000000          # bits of 2^-96 and 2^31
+    assert res["sqrt_normal"] == (0, 3 * (hi - lo))
+    bad, cases = res["recip_normal"]
+    assert bad == 0 and cases >= 2 * (0x47800000 - 0x27800000)   # at least two starts per n
+    assert res["recip_fixed_point"] == (64, 64)

@@ -4,7 +4,7 @@
  * operations (C float with -ffp-contract=off, fmaf).  The defined code is
  *     code = clamp(RNE(RN(d / s)), 0, top),  d = RN(x - m_h), s = sigma_h,
  * with s a positive finite FP16 value and top = 2^b - 1 (7 or 15).  The
- * kernel forms the quotient from y = RN(1/s) (recip_f16val, checked
+ * kernel forms the quotient from y = RN(1/s) (recip_newton, checked
  * separately):
  *     q0 = RN(d*y), q = RN(q0 + RN(d - q0*s)*y)   (two FMAs),
  * and the code from the bits of RN(q + 1.5*2^23), clamped as integers.
