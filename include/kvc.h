@@ -338,7 +338,7 @@ kvc_status kvc_restore_pages(kvc_ctx *ctx, const kvc_layout *layout, const kvc_c
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  No context: the per-call side table,
  * page ids and spill cursor live in a fixed device array of this library,
- * one copy per GPU held until the process ends (about 300 KiB: the codec
+ * one copy per GPU held until the process ends (about 350 KiB: the codec
  * tables, a 256-byte cursor, 2 x 256 side-table entries of 32 bytes and
  * 65,536 page ids).  The call allocates nothing: no hipMalloc, hipFree, host
  * heap or pinned memory.  The first call on a device looks the array up and

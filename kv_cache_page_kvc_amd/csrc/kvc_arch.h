@@ -107,6 +107,35 @@ __device__ __forceinline__ void group_minmax_dpp(float& mn, float& mx) {
 }
 #undef KVC_MINMAX_STEP
 
+// Bitwise helpers the compiler does not form by itself around LDS results:
+// byte B of x masked with 0x3C as one v_and_b32 with a byte-select source
+// operand, a ^ b ^ c and a ^ (b & c) as one v_bitop3_b32 each.
+template <int B>
+__device__ __forceinline__ uint32_t and3c_byte(uint32_t x) {
+  static_assert(B >= 1 && B <= 3, "byte 1, 2 or 3 (byte 0 is a plain AND)");
+  uint32_t r;
+  if constexpr (B == 1)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(0x3Cu), "v"(x));
+  else if constexpr (B == 2)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(0x3Cu), "v"(x));
+  else
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(0x3Cu), "v"(x));
+  return r;
+}
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t xor_and(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x78" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // RN(1/h) by one Newton step e = 1 - h*y0, y0 + e*y0 from the hardware
 // estimate y0 (accurate to one ulp), for
 //  - every positive finite h that is an FP16 value: every start within one

@@ -169,13 +169,15 @@ void build_crc_tables(CrcTables& c) {
     const uint32_t lanes = (uint32_t)kCrcLanes << w;
     for (int k = 0; k < 8; k++)
       for (uint32_t v = 0; v < 16; v++) c.tj[w][k][v] = word_then_zeros(v << (4 * k), 16u * (lanes - 1));
-    for (uint32_t j = 0; j < 256; j++) {
-      uint32_t r = 0;
-      if (j < lanes) {
-        r = 0x80000000u;                       // x^0
-        for (uint32_t i = 0; i < 16u * (lanes - 1 - j); i++) r = zero_byte(r);
+    uint32_t* pw = w == 0 ? &c.pw64[0][0][0] : (w == 1 ? &c.pw128[0][0][0] : &c.pw256[0][0][0]);
+    uint32_t s = 0x80000000u;                  // x^0: s_j for the last lane, then one unit more per lane
+    for (uint32_t j = lanes; j-- > 0;) {
+      uint32_t xi = s;                         // x^i * s_j
+      for (uint32_t i = 0; i < 32; i++) {
+        pw[((i / 4) * lanes + j) * 4 + i % 4] = xi;
+        xi = (xi >> 1) ^ (0xEDB88320u & (0u - (xi & 1u)));   // times x
       }
-      c.shift[w][j] = r;
+      for (int b = 0; b < 16; b++) s = zero_byte(s);
     }
   }
 }

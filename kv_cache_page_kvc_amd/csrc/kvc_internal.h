@@ -63,17 +63,22 @@ struct CellEntry {
 // lookups of 16 entries per word, by linearity of the CRC register update);
 // the last word of a unit that has a successor in the same lane uses tj[w],
 // which also carries the register over the 16 (N - 1) bytes that the other
-// lanes take in between.  Each lane then carries its register over the
-// 16 (N - 1 - j) bytes after its last unit by one carry-less multiplication
-// modulo the polynomial with shift[w][j] = x^(8 * 16 (N - 1 - j)), and the
-// lanes' registers are xored.  Registers are in the reflected order: bit 31
-// holds the coefficient of x^0.
+// lanes take in between.  Each lane then carries its register r over the
+// 16 (N - 1 - j) bytes after its last unit: the product r * s_j modulo the
+// polynomial with s_j = x^(8 * 16 (N - 1 - j)), formed as the xor of
+// x^i * s_j over the coefficients i set in r (the powers pw*, grouped four
+// to a 16-byte load: pw[i / 4][j][i % 4]; the decode kernels read only s_j
+// and multiply it by x between the steps), and the lanes' registers are
+// xored.  Registers are in the reflected order: bit 31 holds the
+// coefficient of x^0.
 constexpr int kCrcLanes = 64;               // lanes of a wave
 constexpr int kCrcLaneSets = 3;             // N = 64, 128, 256
 struct CrcTables {
   uint32_t t[8][16];                        // register after a word whose only nonzero nibble k is v, from a zero register
   uint32_t tj[kCrcLaneSets][8][16];         // t[k][v] carried over 16 (64 * 2^w - 1) more zero bytes
-  uint32_t shift[kCrcLaneSets][256];        // x^(128 (64 * 2^w - 1 - j)) mod P for lane j (0 beyond the lane count)
+  uint32_t pw64[8][64][4];                  // x^i * s_j mod P for N = 64, 128, 256
+  uint32_t pw128[8][128][4];
+  uint32_t pw256[8][256][4];
 };
 static_assert(sizeof(CrcTables) % 16 == 0, "CRC tables are copied in 16-byte units");
 // the part of CrcTables one kernel keeps in LDS: t and its lane count's tj

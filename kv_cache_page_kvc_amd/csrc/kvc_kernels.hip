@@ -835,22 +835,39 @@ __device__ __forceinline__ uint32_t payload_bytes(int codec, int d, uint32_t n_v
 // the result is complemented at the end.
 
 // register after the four bytes of x (x = register ^ next little-endian word),
-// from the nibble tables t[k][v] (eight lookups: the update is linear)
+// from the nibble tables t[k][v] (eight lookups: the update is linear).  The
+// byte offset 4v of nibble k is (x << 2 or x >> 2, shifted) & 0x3C; with
+// BYTESEL the three upper bytes of x << 2 and x >> 2 are masked in one
+// byte-select AND each.  BYTESEL measured faster in the encode kernels and
+// slower in the decode kernels, so each direction passes its own choice.
+template <bool BYTESEL>
 __device__ __forceinline__ uint32_t crc_word(uint32_t x, const uint32_t (*t)[16]) {
-  return t[0][x & 15] ^ t[1][(x >> 4) & 15] ^ t[2][(x >> 8) & 15] ^ t[3][(x >> 12) & 15] ^ t[4][(x >> 16) & 15] ^
-         t[5][(x >> 20) & 15] ^ t[6][(x >> 24) & 15] ^ t[7][x >> 28];
-}
-// a * b modulo the CRC polynomial, both in the register's reflected order
-// (bit 31 = coefficient of x^0): b is multiplied by x once per coefficient
-// of a, low degree first, and added where that coefficient is 1
-__device__ __forceinline__ uint32_t crc_mulmod(uint32_t a, uint32_t b) {
-  uint32_t p = 0;
+  const uint32_t ev = x << 2, od = x >> 2;
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(t);
+  auto at = [b](int k, uint32_t off) { return *reinterpret_cast<const uint32_t*>(b + 64 * k + off); };
+  uint32_t a[8];
+  a[0] = at(0, ev & 0x3Cu);
+  a[1] = at(1, od & 0x3Cu);
+  if constexpr (BYTESEL) {
+    a[2] = at(2, and3c_byte<1>(ev));
+    a[3] = at(3, and3c_byte<1>(od));
+    a[4] = at(4, and3c_byte<2>(ev));
+    a[5] = at(5, and3c_byte<2>(od));
+    a[6] = at(6, and3c_byte<3>(ev));
+    a[7] = at(7, and3c_byte<3>(od));
+  } else {
 #pragma unroll
-  for (int i = 0; i < 32; i++) {
-    p ^= b & (0u - ((a >> (31 - i)) & 1u));
-    b = (b >> 1) ^ (0xEDB88320u & (0u - (b & 1u)));
+    for (int k = 2; k < 8; k++) a[k] = at(k, (x >> (4 * k - 2)) & 0x3Cu);
   }
-  return p;
+  return xor3(xor3(a[0], a[1], a[2]), xor3(a[3], a[4], a[5]), a[6] ^ a[7]);
+}
+// x^i * s_lane mod P for the lanes of an NT-thread workgroup, as 16-byte
+// groups [i / 4][lane]
+template <int NT>
+__device__ __forceinline__ const uint4* crc_lane_powers(const Tables* tables) {
+  if constexpr (NT == 64) return reinterpret_cast<const uint4*>(tables->crc.pw64);
+  else if constexpr (NT == 128) return reinterpret_cast<const uint4*>(tables->crc.pw128);
+  else return reinterpret_cast<const uint4*>(tables->crc.pw256);
 }
 
 // The CRC tables in LDS: a static allocation that only the kernels built
@@ -891,8 +908,12 @@ __device__ __forceinline__ void load_crc_tables(CrcLds* dst, const CrcTables* sr
 // (o a multiple of 16).  When n is not a multiple of 16 the 16-byte unit
 // holding the last bytes must be readable as a whole.  Called by all NT
 // threads of the workgroup (with NT > 64 it synchronises them); every thread
-// returns the CRC.  tables: the call's tables (the lane's carry constant).
-template <int NT, class Load>
+// returns the CRC.  tables: the call's tables (the lanes' powers).  ENC
+// selects the encode kernels' form (byte-select masks; the final carry from
+// all 32 powers x^i * s_lane, eight 16-byte loads in flight during the
+// loop) or the decode kernels' (plain masks; the carry from s_lane alone,
+// multiplied by x between the 32 steps): each measured faster where used.
+template <int NT, bool ENC, class Load>
 __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, const CrcLds* ct, const Tables* tables) {
   const uint32_t lane = threadIdx.x;
   const uint32_t units = n >> 4;
@@ -900,20 +921,43 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
   // register stays zero over zero bytes), so lane NT - 1 holds the last unit
   const uint32_t pad = (NT - (units & (NT - 1))) & (NT - 1);
   const uint32_t rounds = (units + pad) / NT;
-  const uint32_t carry = tables->crc.shift[crc_lane_set<NT>()][lane];   // x^(128 (NT - 1 - lane))
+  // x^i * s_lane (s_lane = x^(128 (NT - 1 - lane))), as [i / 4][lane][i % 4]
+  const uint4* pws = crc_lane_powers<NT>(tables) + lane;
+  uint4 pw[ENC ? 8 : 1];
+#pragma unroll
+  for (int g = 0; g < (ENC ? 8 : 1); g++) pw[g] = ld_global16(pws + g * NT);
   uint32_t r = 0;
   for (uint32_t k = 0; k < rounds; k++) {
     const int32_t q = (int32_t)(k * NT + lane) - (int32_t)pad;
     if (q < 0) continue;                    // a zero unit in front: the register stays zero
     uint4 w = load(16u * (uint32_t)q);
     if (q == 0) w.x = ~w.x;
-    r = crc_word(r ^ w.x, ct->t);
-    r = crc_word(r ^ w.y, ct->t);
-    r = crc_word(r ^ w.z, ct->t);
-    r = crc_word(r ^ w.w, k + 1 < rounds ? ct->tj : ct->t);
+    r = crc_word<ENC>(r ^ w.x, ct->t);
+    r = crc_word<ENC>(r ^ w.y, ct->t);
+    r = crc_word<ENC>(r ^ w.z, ct->t);
+    r = crc_word<ENC>(r ^ w.w, k + 1 < rounds ? ct->tj : ct->t);
   }
-  // carry each register over the units after its last one: NT - 1 - lane
-  r = crc_mulmod(r, carry);
+  // carry each register over the units after its last one (NT - 1 - lane):
+  // r * s_lane, the xor of x^i * s_lane over the coefficients i set in r
+  // (coefficient i is bit 31 - i)
+  uint32_t c = 0;
+  if constexpr (ENC) {
+#pragma unroll
+    for (int g = 0; g < 8; g++) {
+      c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g)) >> 31), pw[g].x);
+      c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 1)) >> 31), pw[g].y);
+      c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 2)) >> 31), pw[g].z);
+      c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 3)) >> 31), pw[g].w);
+    }
+  } else {
+    uint32_t v = pw[0].x;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      c = xor_and(c, (uint32_t)((int32_t)(r << i) >> 31), v);
+      if (i < 31) v = xor_and(v >> 1, 0u - (v & 1u), 0xEDB88320u);   // v * x
+    }
+  }
+  r = c;
 #pragma unroll
   for (int m = kCrcLanes / 2; m >= 1; m >>= 1) r ^= __shfl_xor(r, m, kCrcLanes);
   if constexpr (NT > kCrcLanes) {                                // xor the waves' registers
@@ -931,9 +975,9 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
   const uint32_t tail = n & 15;
   if (tail) {
     const uint4 w = load(16u * units);
-    if (tail >= 4) r = crc_word(r ^ w.x, ct->t);
-    if (tail >= 8) r = crc_word(r ^ w.y, ct->t);
-    if (tail >= 12) r = crc_word(r ^ w.z, ct->t);
+    if (tail >= 4) r = crc_word<ENC>(r ^ w.x, ct->t);
+    if (tail >= 8) r = crc_word<ENC>(r ^ w.y, ct->t);
+    if (tail >= 12) r = crc_word<ENC>(r ^ w.z, ct->t);
     const uint32_t q = tail >> 2;
     uint32_t last = q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w));
     for (uint32_t b = 0; b < (tail & 3); b++, last >>= 8) {
@@ -976,7 +1020,7 @@ __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const La
 template <int NT>
 __device__ __forceinline__ uint32_t crc32_written(const uint8_t* b, uint32_t n, const CrcLds* ct, const Tables* tables) {
   __syncthreads();
-  return crc32_lanes<NT>(GlobalBytes{b}, n, ct, tables);
+  return crc32_lanes<NT, true>(GlobalBytes{b}, n, ct, tables);
 }
 
 // ------------------------------------------------------------------ encode kernel
@@ -1069,7 +1113,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const int any_bad = __syncthreads_or(bad);
   const uint32_t aux = codec == C_FP8F ? __float_as_uint(fixed) : 0u;
   if (staged && !any_bad) {
-    const uint32_t c = crc ? crc32_lanes<NT>(LdsBytes{s_stage + stored_at}, payload, ct, p.tables) : 0u;
+    const uint32_t c = crc ? crc32_lanes<NT, true>(LdsBytes{s_stage + stored_at}, payload, ct, p.tables) : 0u;
     // header + body from unit 0, so every wave store covers whole lines
     const Header h = make_header(codec, crc_flag, DT, comp, D, s.n_vec, payload, 0, aux, c);
     for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT) {
@@ -1389,9 +1433,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   // the stored bytes must match the header's CRC32 before the page is written
   if constexpr (CRC) {
     __syncthreads();                                      // CRC tables in LDS
-    const uint32_t c = raw_data ? crc32_lanes<NT>(GlobalBytes{p.buf + spill}, stored, ct, p.tables)
-                       : staged ? crc32_lanes<NT>(LdsBytes{s_stage + stored_at}, stored, ct, p.tables)
-                                : crc32_lanes<NT>(GlobalBytes{s.slot + stored_at}, stored, ct, p.tables);
+    const uint32_t c = raw_data ? crc32_lanes<NT, false>(GlobalBytes{p.buf + spill}, stored, ct, p.tables)
+                       : staged ? crc32_lanes<NT, false>(LdsBytes{s_stage + stored_at}, stored, ct, p.tables)
+                                : crc32_lanes<NT, false>(GlobalBytes{s.slot + stored_at}, stored, ct, p.tables);
     if (c != h1.z) {
       if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 3;
       return;
