@@ -612,6 +612,8 @@ CallParams with_threads(const CallParams& P, const kvc_layout* L, uint32_t nt) {
   W.threads = nt;
   W.walk_dh = gw % H;
   W.walk_step = (gw / H) * P.st32 + (gw % H) * P.sh32;
+  const uint32_t n_vec = H * L->tokens_per_page, batch = gw * (uint32_t)kBatchVectors;
+  W.linear_iters = P.sh32 == L->head_dim && P.st32 == H * L->head_dim && n_vec % batch == 0 ? n_vec / batch : 0;
   return W;
 }
 // one wave for small segments, else the direction's workgroup size

@@ -31,6 +31,8 @@ constexpr uint32_t kSmallSegmentBytes = 16384;
 // (GW = groups per workgroup).
 constexpr int lanes_per_vector(int d) { return d == 32 ? 2 : (d == 64 ? 4 : (d == 128 ? 8 : 16)); }
 constexpr int groups_per_workgroup(int d, int nt) { return nt / lanes_per_vector(d); }
+// vectors per group whose loads are in flight together (one batch)
+constexpr int kBatchVectors = 2;
 constexpr uint64_t kSlotAlign = KVC_SLOT_ALIGN;
 constexpr uint32_t kHeaderBytes = KVC_HEADER_BYTES;
 
@@ -146,6 +148,12 @@ struct CallParams {
   // fewer than 2^31 elements, so every offset actually used is exact.
   uint32_t st32, sh32;                        // stride_token, stride_head
   uint32_t walk_dh, walk_step, walk_wrap;
+  // Nonzero when vector v of a page starts at element v * D (stride_head = D,
+  // stride_token = heads * D) and the vectors fill whole batches of every
+  // group (heads * tokens a multiple of GW * kBatchVectors): the batches per
+  // group, which the fixed-size codec loops then walk without the head
+  // counter or per-vector bounds.  0 otherwise.
+  uint32_t linear_iters;
   // Encode: bytes of dynamic LDS in which each coded (non-raw) segment's slot
   // is assembled before it is written out with full-line stores; 0 when
   // some coded slot exceeds kMaxStageBytes (then codes go straight out).

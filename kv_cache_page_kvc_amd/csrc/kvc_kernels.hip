@@ -53,7 +53,7 @@ struct Geo {
   // vectors per group whose loads are in flight together: 2 keeps the encode
   // kernel at <= 80 VGPRs for D <= 128 (six waves per SIMD), and more vectors
   // per batch measured slower through the lost occupancy
-  static constexpr int U = 2;
+  static constexpr int U = kBatchVectors;
 };
 
 struct Lane {
@@ -245,6 +245,7 @@ struct SegCtx {
   uint64_t heads_magic;     // v / heads = (v * heads_magic) >> 32 for v < 2^16
   uint32_t st, sh;          // element strides of token and head
   uint32_t walk_dh, walk_step, walk_wrap;
+  uint32_t linear_iters;    // batches per group of a linear layout, else 0
   uint32_t row_bytes;       // record codec: bytes of one token row
 };
 
@@ -699,6 +700,32 @@ __device__ __forceinline__ int encode_segment_vectors(const SegCtx& s, const Lan
   const uint32_t meta_blk = kHeaderBytes + (uint32_t)s.n_vec * CB;   // byte offset in the slot
   int bad = 0;
   uint4 w[U][Geo<D>::NCH];
+  if (s.linear_iters) {
+    // vector v at element v * D, every batch full: a uniform trip count and
+    // one address step per batch
+    constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH;
+#pragma unroll 1
+    for (uint32_t it = 0; it < s.linear_iters; it++) {
+      const int v0 = ln.g + (int)it * (GW * U);
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const uint32_t b = 2u * ((uint32_t)(v0 + u * GW) * D + 8 * ln.p);
+#pragma unroll
+        for (int k = 0; k < NCH; k++) w[u][k] = ld_stream16(byte_at(s.src, b + 16 * P * k));
+      }
+      // (the bound always holds here; as a branch it keeps the vectors'
+      // arithmetic apart, which holds the register count of the general loop)
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        if (v0 + u * GW < s.n_vec) {
+          uint32_t cv, mv;
+          vec_offsets<D, C>(s, v0 + u * GW, meta_blk, cv, mv);
+          bad |= encode_vector<D, DT, C>(w[u], cv, mv, ln, image, fixed, ls, cells);
+        }
+      }
+    }
+    return bad;
+  }
   VecPos pos = vec_pos(s, ln.g);
   for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
     load_batch<D, NT>(s, ln, v0, pos, w);
@@ -1059,6 +1086,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   s.walk_dh = p.walk_dh;
   s.walk_step = p.walk_step;
   s.walk_wrap = p.walk_wrap;
+  s.linear_iters = p.linear_iters;
   s.row_bytes = p.row_bytes;
   const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
   const uint32_t slot_bytes = E.slot_bytes;
@@ -1299,6 +1327,24 @@ __device__ __forceinline__ void decode_segment_vectors(const SegCtx& s, const La
   constexpr int CB = CodecInfo<C>::bits * D / 8;
   const uint32_t meta_blk = kHeaderBytes + (uint32_t)s.n_vec * CB;
   uint16_t* page = const_cast<uint16_t*>(s.src);
+  if (s.linear_iters) {
+    // vector v at element v * D, every batch full (see encode_segment_vectors)
+#pragma unroll 1
+    for (uint32_t it = 0; it < s.linear_iters; it++) {
+      const int v0 = ln.g + (int)it * (GW * U);
+      VecCodes<D> vc[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        uint32_t cv, mv;
+        vec_offsets<D, C>(s, v0 + u * GW, meta_blk, cv, mv);
+        load_vec_codes<D, C>(image, cv, mv, ln, vc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)      // (always true: keeps the vectors apart, as in encode)
+        if (v0 + u * GW < s.n_vec) decode_vector<D, DT, C>(vc[u], ln, page, (uint32_t)(v0 + u * GW) * D, fixed, ls, cent);
+    }
+    return;
+  }
   VecPos pos = vec_pos(s, ln.g);
   for (int v0 = ln.g; v0 < s.n_vec; v0 += GW * U) {
     VecCodes<D> vc[U];
@@ -1394,6 +1440,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   s.walk_dh = p.walk_dh;
   s.walk_step = p.walk_step;
   s.walk_wrap = p.walk_wrap;
+  s.linear_iters = p.linear_iters;
   s.row_bytes = p.row_bytes;
   const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
 

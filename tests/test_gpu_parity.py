@@ -149,6 +149,21 @@ def test_odd_head_counts(ctx, pair, heads):
     _roundtrip_case(ctx, wl, pair[0], pair[1], seed=7 + heads, page_ids=ids, dst_ids=ids[::-1].copy())
 
 
+@pytest.mark.parametrize("shape", [(1, 8), (3, 5), (5, 7), (2, 24)], ids=lambda s: f"H{s[0]}-T{s[1]}")
+@pytest.mark.parametrize("dim", [32, 128])
+@pytest.mark.parametrize("pair", [("TQ4", "UNIFORM4"), ("INT8", "FP8_DYNAMIC"), ("TQ3", "INT8_ROWS")],
+                         ids=lambda p: f"{p[0]}-{p[1]}")
+def test_ragged_vector_counts(ctx, pair, dim, shape):
+    """Separate layouts whose heads x tokens is not a multiple of a
+    workgroup's batch of vectors (the general loop with a ragged last batch)
+    next to one that is (H2-T24 at D=32): every segment compared."""
+    H, T = shape
+    print(f"[case] ragged {pair} D={dim} H={H} T={T}", flush=True)
+    wl = G.Workload(2, H, dim, T, 5, "bf16", "separate", seed=H * 100 + T)
+    ids = inputs.random_page_ids(5, 3, seed=T)
+    _roundtrip_case(ctx, wl, pair[0], pair[1], seed=5 + H + T, page_ids=ids, dst_ids=ids[::-1].copy())
+
+
 def test_fp8_dynamic_small_full(ctx):
     """FP8 E4M3FN dynamic workload, 2 layers x 8 heads x D128 BF16, 64 pages:
     all 256 segments."""
