@@ -470,6 +470,14 @@ def _sample_segments(L, n_pages, count, seed, layers=None):
     return sorted(segs)
 
 
+def _sample_pages(L, n_pages, count, seed):
+    """Every segment (all layers, K and V) of `count` sampled positions in
+    the call's page list: the oracle then copies only those pages."""
+    rng = np.random.default_rng(seed)
+    pos = rng.choice(n_pages, size=count, replace=False)
+    return sorted(int((l * n_pages + int(i)) * 2 + c) for i in pos for l in range(L) for c in (0, 1))
+
+
 @pytest.mark.parametrize("heads,codec_pair,raw", [(32, ("TQ4", "FP8_DYNAMIC"), False), (40, ("INT8", "UNIFORM4"), True)],
                          ids=["16MiB-coded", "20MiB-raw"])
 def test_segment_size_limit(ctx, heads, codec_pair, raw):
@@ -489,12 +497,13 @@ def test_segment_size_limit(ctx, heads, codec_pair, raw):
 def test_tq4_u4_llama3_full_size(ctx):
     """TurboQuant-4 K + uniform-4 V, 32 layers x 8 heads x D128 BF16, 4096 of
     8192 blocks in random order, protected layers 0, 1, 30, 31: one full-size
-    launch each way (as timed by the benchmark), 96 sampled segments checked."""
+    launch each way (as timed by the benchmark); every segment of 64 sampled
+    pages (4096 segments, all layers) checked."""
     cfg = inputs.CONFIGS["tq4_u4_llama3"]
     print("[case] tq4_u4_llama3 full size", flush=True)
     wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
     ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
-    segs = _sample_segments(cfg["layers"], cfg["pages"], 96, 1, layers=[0, 31])
+    segs = _sample_pages(cfg["layers"], cfg["pages"], 64, 1)
     _roundtrip_case(ctx, wl, "TQ4", "UNIFORM4", 0, ids, protected=list(cfg["protected"]), segments=segs,
                     decode_from_oracle=False)
 
@@ -502,13 +511,13 @@ def test_tq4_u4_llama3_full_size(ctx):
 def test_tq4_u4_llama3_tp8_full_size(ctx):
     """One 8-way tensor-parallel shard of the TurboQuant-4 / uniform-4
     workload: 1 KV head, 4 KiB segments (one-wave workgroups), 4096 of 8192
-    blocks, protected layers 0, 1, 30, 31; full-size launch, sampled
-    segments."""
+    blocks, protected layers 0, 1, 30, 31; full-size launch, every segment
+    of 128 sampled pages (8192 segments)."""
     cfg = inputs.CONFIGS["tq4_u4_llama3_tp8"]
     print("[case] tq4_u4_llama3 tp8 shard full size", flush=True)
     wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
     ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
-    segs = _sample_segments(cfg["layers"], cfg["pages"], 96, 4, layers=[0, 31])
+    segs = _sample_pages(cfg["layers"], cfg["pages"], 128, 4)
     _roundtrip_case(ctx, wl, "TQ4", "UNIFORM4", 0, ids, protected=list(cfg["protected"]), segments=segs,
                     decode_from_oracle=False)
 
@@ -516,13 +525,14 @@ def test_tq4_u4_llama3_tp8_full_size(ctx):
 @pytest.mark.parametrize("dim", [32, 64, 256])
 def test_tq3_u3_dsweep_full_size(ctx, dim):
     """TurboQuant-3 K (outlier channels) + uniform-3 V, 28 layers x 4 heads,
-    2048 pages: full-size launch, sampled segments, 3-bit sizes."""
+    2048 pages: full-size launch, every segment of 32 sampled pages, 3-bit
+    sizes."""
     cfg = inputs.CONFIGS["tq3_u3_dsweep"]
     print(f"[case] tq3_u3 D={dim} full size", flush=True)
     wl = G.Workload(cfg["layers"], cfg["heads"], dim, cfg["tokens"], cfg["pool"], "bf16", "separate", 0,
                     k_kind="outliers")
     ids = np.arange(cfg["pages"], dtype=np.int32)
-    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, dim)
+    segs = _sample_pages(cfg["layers"], cfg["pages"], 32, dim)
     ora_st, gdesc = _roundtrip_case(ctx, wl, "TQ3", "UNIFORM3", 0, ids, segments=segs, decode_from_oracle=False)
     n_vec = cfg["heads"] * cfg["tokens"]
     assert set(gdesc["stored_len"][0::2]) == {n_vec * (3 * dim // 8 + 2)}
@@ -533,7 +543,7 @@ def test_tq3_u3_dsweep_full_size(ctx, dim):
 def test_k16v8_packed_full_size(ctx, vcodec):
     """vLLM packed FP16 [2048 blocks, 8 heads, 16 tokens, 256], 36 layers,
     K raw, V FP8 with a fixed per-layer scale (calibrated on sequence 0's V)
-    or per-vector scales: full-size launch, sampled segments."""
+    or per-vector scales: full-size launch, every segment of 16 sampled pages."""
     cfg = inputs.CONFIGS["k16v8_packed"]
     print(f"[case] k16v8 packed {vcodec}", flush=True)
     wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "fp16", "packed", 0)
@@ -542,33 +552,33 @@ def test_k16v8_packed_full_size(ctx, vcodec):
         amax = np.array([float(t[:512, :, :, cfg["dim"]:].abs().max()) for t in wl.k])
         fixed = np.stack([np.ones(cfg["layers"]), amax / 448.0], 1).astype(np.float32)
     ids = np.arange(cfg["pages"], dtype=np.int32)
-    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 3)
+    segs = _sample_pages(cfg["layers"], cfg["pages"], 16, 3)
     _roundtrip_case(ctx, wl, "RAW", vcodec, 0, ids, fixed=fixed, segments=segs, decode_from_oracle=False)
 
 
 def test_int8_records_qwen3_full_size(ctx):
     """INT8 host-pool records on the Qwen3-8B shape, 36 layers x 8 heads x
     D128 BF16, 3392 of 4096 blocks in random order: one full-size launch
-    each way, sampled segments checked bit-exactly (codes, BF16 scales, row
+    each way, every segment of 16 sampled pages checked bit-exactly (codes, BF16 scales, row
     padding, decode)."""
     cfg = inputs.CONFIGS["int8_records_qwen3"]
     print("[case] int8 records qwen3", flush=True)
     wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
     ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
-    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 11)
+    segs = _sample_pages(cfg["layers"], cfg["pages"], 16, 11)
     _roundtrip_case(ctx, wl, "INT8_ROWS", "INT8_ROWS", 0, ids, segments=segs, decode_from_oracle=False)
 
 
 def test_ans16_llama3_full_size(ctx):
     """The lossless entropy stage on the Llama-3-8B shape, 32 layers x 8 heads
     x D128 BF16, 4096 of 8192 blocks in random order: one full-size launch
-    each way; sampled segments' headers and payloads equal the oracle's and
+    each way; the headers and payloads of every segment of 16 sampled pages equal the oracle's and
     every sampled page decodes bit-exactly."""
     cfg = inputs.CONFIGS["ans16_llama3"]
     print("[case] ans16 llama3", flush=True)
     wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
     ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
-    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 13)
+    segs = _sample_pages(cfg["layers"], cfg["pages"], 16, 13)
     ora_st, gdesc = _roundtrip_case(ctx, wl, "ANS16", "ANS16", 0, ids, segments=segs, decode_from_oracle=False,
                                     crc=True)
     assert all(int(ora_st[s]) == O.SEG_ENCODED for s in segs)
@@ -657,12 +667,12 @@ def test_ans16_two_raw_planes_payload(ctx):
 def test_k8v8_packed_full_size(ctx):
     """K8/V8 with per-token/head FP8 scales on the vLLM packed FP16 Qwen3-8B
     layout [2048 blocks, 8 heads, 16 tokens, 256], 36 layers: full-size
-    launch, sampled segments."""
+    launch, every segment of 16 sampled pages."""
     cfg = inputs.CONFIGS["k8v8_packed"]
     print("[case] k8v8 packed", flush=True)
     wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "fp16", "packed", 0)
     ids = np.arange(cfg["pages"], dtype=np.int32)
-    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 5)
+    segs = _sample_pages(cfg["layers"], cfg["pages"], 16, 5)
     _roundtrip_case(ctx, wl, "FP8_DYNAMIC", "FP8_DYNAMIC", 0, ids, segments=segs, decode_from_oracle=False)
 
 
@@ -965,12 +975,12 @@ def test_fp8_large_call_one_wave_encode(ctx, crc):
 
 def test_tq4_u4_llama3_full_size_crc(ctx):
     """The TurboQuant-4 / uniform-4 Llama-3-8B workload with the CRC option:
-    one full-size launch each way, sampled segments bit-exact (CRCs
+    one full-size launch each way, every segment of 32 sampled pages bit-exact (CRCs
     included) and decoded with status 0 after the CRC check."""
     cfg = inputs.CONFIGS["tq4_u4_llama3"]
     print("[case] tq4_u4_llama3 full size crc", flush=True)
     wl = G.Workload(cfg["layers"], cfg["heads"], cfg["dim"], cfg["tokens"], cfg["pool"], "bf16", "separate", 0)
     ids = inputs.random_page_ids(cfg["pool"], cfg["pages"], seed=0)
-    segs = _sample_segments(cfg["layers"], cfg["pages"], 64, 2, layers=[0, 31])
+    segs = _sample_pages(cfg["layers"], cfg["pages"], 32, 2)
     _roundtrip_case(ctx, wl, "TQ4", "UNIFORM4", 0, ids, protected=list(cfg["protected"]), segments=segs,
                     decode_from_oracle=False, crc=True)
