@@ -6,7 +6,7 @@ and raw; TurboQuant decodes within 1e-3 absolute and bit-equal up to the
 sign of zero.  Small cases cover every codec, head dim, dtype and
 layout over several tiles and a ragged page count; the workload-sized cases
 run at full size in the launch configuration the benchmark times, checked
-on sampled segments.
+on every segment (all layers, K and V) of sampled pages.
 """
 import numpy as np
 import pytest
