@@ -954,15 +954,23 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
 #pragma unroll
   for (int g = 0; g < (ENC ? 8 : 1); g++) pw[g] = ld_global16(pws + g * NT);
   uint32_t r = 0;
+  // each round's unit is loaded one round ahead; only round 0 holds padding
+  // (q < 0: a zero unit in front, over which the register stays zero)
+  const int32_t q0 = (int32_t)lane - (int32_t)pad;
+  uint4 w = make_uint4(0, 0, 0, 0);
+  if (rounds && q0 >= 0) w = load(16u * (uint32_t)q0);
   for (uint32_t k = 0; k < rounds; k++) {
-    const int32_t q = (int32_t)(k * NT + lane) - (int32_t)pad;
-    if (q < 0) continue;                    // a zero unit in front: the register stays zero
-    uint4 w = load(16u * (uint32_t)q);
-    if (q == 0) w.x = ~w.x;
-    r = crc_word<ENC>(r ^ w.x, ct->t);
-    r = crc_word<ENC>(r ^ w.y, ct->t);
-    r = crc_word<ENC>(r ^ w.z, ct->t);
-    r = crc_word<ENC>(r ^ w.w, k + 1 < rounds ? ct->tj : ct->t);
+    const int32_t q = q0 + (int32_t)(k * NT);
+    uint4 wn = make_uint4(0, 0, 0, 0);
+    if (k + 1 < rounds) wn = load(16u * (uint32_t)(q + NT));
+    if (q >= 0) {
+      if (q == 0) w.x = ~w.x;
+      r = crc_word<ENC>(r ^ w.x, ct->t);
+      r = crc_word<ENC>(r ^ w.y, ct->t);
+      r = crc_word<ENC>(r ^ w.z, ct->t);
+      r = crc_word<ENC>(r ^ w.w, k + 1 < rounds ? ct->tj : ct->t);
+    }
+    w = wn;
   }
   // carry each register over the units after its last one (NT - 1 - lane):
   // r * s_lane, the xor of x^i * s_lane over the coefficients i set in r
