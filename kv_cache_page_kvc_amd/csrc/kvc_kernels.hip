@@ -56,6 +56,10 @@ struct Geo {
   static constexpr int U = kBatchVectors;
 };
 
+// 16-byte units each thread has in flight while it copies a slot or a table
+// into LDS: all its loads are issued before the first store
+constexpr int kStageRounds = 4;
+
 struct Lane {
   int p;        // lane index within the group
   int g;        // group index within the workgroup
@@ -349,14 +353,16 @@ struct LaneSigns {
 template <int D>
 __device__ __forceinline__ void make_lane_signs(const uint32_t* mask, int p, bool parity, LaneSigns<D>& ls) {
   constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH;
-  const uint32_t par = (parity && (__builtin_popcount(p) & 1)) ? 0x80008000u : 0u;
+  const uint32_t par = (parity && (__builtin_popcount(p) & 1)) ? 0xFFu : 0u;
 #pragma unroll
   for (int k = 0; k < NCH; k++) {
     const int e0 = k * 8 * P + 8 * p;            // multiple of 8: one byte of the mask
-    const uint32_t byte = (mask[e0 >> 5] >> (e0 & 31)) & 0xFFu;
+    const uint32_t byte = ((mask[e0 >> 5] >> (e0 & 31)) & 0xFFu) ^ par;
+    // spread holds bit j of the byte at bits j and j + 15; shifted left by
+    // 15 - 2m, bit 15 then holds bit 2m and bit 31 bit 2m + 1
+    const uint32_t spread = byte | (byte << 15);
 #pragma unroll
-    for (int m = 0; m < 4; m++)
-      ls.flip[4 * k + m] = ((((byte >> (2 * m)) & 1u) << 15) | (((byte >> (2 * m + 1)) & 1u) << 31)) ^ par;
+    for (int m = 0; m < 4; m++) ls.flip[4 * k + m] = (spread << (15 - 2 * m)) & 0x80008000u;
   }
 }
 
@@ -1120,8 +1126,17 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
 
   const bool tq = codec == C_TQ3 || codec == C_TQ4;
   if (tq) {
-    const CellEntry* src = p.tables->cells[codec == C_TQ4 ? 1 : 0];
-    for (int q = threadIdx.x; q < kCells; q += NT) s_cells[q] = src[q];
+    const uint2* src = reinterpret_cast<const uint2*>(p.tables->cells[codec == C_TQ4 ? 1 : 0]);
+    uint2* dst = reinterpret_cast<uint2*>(s_cells);
+    static_assert(sizeof(CellEntry) == sizeof(uint2), "one 8-byte word per cell");
+    constexpr int R = (kCells + NT - 1) / NT;
+    uint2 c[R];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+      c[r] = threadIdx.x + r * NT < kCells ? src[threadIdx.x + r * NT] : make_uint2(0, 0);
+#pragma unroll
+    for (int r = 0; r < R; r++)
+      if (threadIdx.x + r * NT < kCells) dst[threadIdx.x + r * NT] = c[r];
     __syncthreads();
   }
   LaneSigns<D> ls;
@@ -1151,13 +1166,15 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   if (staged && !any_bad) {
     const uint32_t c = crc ? crc32_lanes<NT, true>(LdsBytes{s_stage + stored_at}, payload, ct, p.tables) : 0u;
     // header + body from unit 0, so every wave store covers whole lines
-    const Header h = make_header(codec, crc_flag, DT, comp, D, s.n_vec, payload, 0, aux, c);
-    for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT) {
-      uint4 w = *reinterpret_cast<const uint4*>(s_stage + 16 * u);
-      if (u == 0) w = h.h0;
-      if (u == 1) w = h.h1;
-      st_stream16(s.slot + 16 * u, w);
+    // the header goes into the image's first 32 bytes; the threads that
+    // store them read them back below, in order after their own LDS stores
+    if (threadIdx.x < 2) {
+      const Header h = make_header(codec, crc_flag, DT, comp, D, s.n_vec, payload, 0, aux, c);
+      if (threadIdx.x == 0) *reinterpret_cast<uint4*>(s_stage) = h.h0;
+      if (threadIdx.x == 1) *reinterpret_cast<uint4*>(s_stage + 16) = h.h1;
     }
+    for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT)
+      st_stream16(s.slot + 16 * u, *reinterpret_cast<const uint4*>(s_stage + 16 * u));
     if (threadIdx.x == 0) write_desc(desc, slot_off, codec, crc_flag, KVC_SEG_ENCODED, D, s.n_vec, payload, 0, c);
     return;
   }
@@ -1457,14 +1474,40 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   const uint32_t slot_bytes = E.slot_bytes;
   const bool staged = codec != C_RAW && slot_bytes <= p.stage_bytes;
   if constexpr (CRC) load_crc_tables<NT>(ct, &p.tables->crc);
+  // TurboQuant centroids (negated in s_cent[16..31]) and the lane's signs.
+  // A one-wave workgroup, whose life is mostly memory latency, issues their
+  // loads with the slot's; larger ones load them once the slot is in LDS
+  // (measured faster there).
+  const bool tq = codec == C_TQ3 || codec == C_TQ4;
+  constexpr bool early = NT == 64;
+  const Lane ln = lane_info<D>();
+  float cent = 0.0f;
+  LaneSigns<D> ls;
+  if (early && tq) {
+    if (threadIdx.x < 32) cent = p.tables->centroids[codec == C_TQ4 ? 1 : 0][threadIdx.x & 15];
+    make_lane_signs<D>(p.sign_mask, ln.p, false, ls);
+  }
   uint4 h0, h1;
   if (staged) {
-    for (uint32_t u = threadIdx.x; u < slot_bytes / 16; u += NT)
-      *reinterpret_cast<uint4*>(s_stage + 16 * u) = ld_stream16(s.slot + 16 * u);
-    __syncthreads();
+    // kStageRounds units per thread are loaded before any is stored to LDS,
+    // so a wave waits for one memory latency per kStageRounds units, not one
+    // per unit
+    const uint32_t nu = slot_bytes / 16;
+    for (uint32_t u0 = threadIdx.x; u0 < nu; u0 += kStageRounds * NT) {
+      uint4 w[kStageRounds];
+#pragma unroll
+      for (int r = 0; r < kStageRounds; r++)
+        if (u0 + r * NT < nu) w[r] = ld_stream16(s.slot + 16 * (u0 + r * NT));
+#pragma unroll
+      for (int r = 0; r < kStageRounds; r++)
+        if (u0 + r * NT < nu) *reinterpret_cast<uint4*>(s_stage + 16 * (u0 + r * NT)) = w[r];
+    }
+    if (early && tq && threadIdx.x < 32) s_cent[threadIdx.x] = threadIdx.x < 16 ? cent : -cent;
+    __syncthreads();                                      // the slot image (and the centroids)
     h0 = *reinterpret_cast<const uint4*>(s_stage);
     h1 = *reinterpret_cast<const uint4*>(s_stage + 16);
   } else {
+    if (early && tq && threadIdx.x < 32) s_cent[threadIdx.x] = threadIdx.x < 16 ? cent : -cent;
     h0 = ld_global16(s.slot);
     h1 = ld_global16(s.slot + 16);
   }
@@ -1498,7 +1541,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   }
   if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 0;
 
-  const Lane ln = lane_info<D>();
   if (raw_data) {
     copy_in_raw<D, NT>(s, ln, p.buf + spill);
     return;
@@ -1507,16 +1549,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
     copy_in_raw<D, NT>(s, ln, s.slot + kHeaderBytes);
     return;
   }
-  const bool tq = codec == C_TQ3 || codec == C_TQ4;
-  if (tq) {
+  if (!early && tq) {
     if (threadIdx.x < 32) {
       const float c = p.tables->centroids[codec == C_TQ4 ? 1 : 0][threadIdx.x & 15];
       s_cent[threadIdx.x] = threadIdx.x < 16 ? c : -c;
     }
-    __syncthreads();
+    make_lane_signs<D>(p.sign_mask, ln.p, false, ls);
   }
-  LaneSigns<D> ls;
-  if (tq) make_lane_signs<D>(p.sign_mask, ln.p, false, ls);
+  if (tq && (!early || !staged)) __syncthreads();         // the centroids
   const float fixed = __uint_as_float(h1.w);
   if (staged) decode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cent, s_stage);
   else decode_codec<D, DT, NT>(codec, s, ln, fixed, ls, s_cent, s.slot);
