@@ -115,14 +115,6 @@ __device__ __forceinline__ float group_sum(float v) {   // sum over element bits
   return v;
 }
 template <int LOGP>
-__device__ __forceinline__ uint32_t group_or(uint32_t v) {
-  if constexpr (LOGP >= 1) v |= xlane_u<0>(v);
-  if constexpr (LOGP >= 2) v |= xlane_u<1>(v);
-  if constexpr (LOGP >= 3) v |= xlane_u<2>(v);
-  if constexpr (LOGP >= 4) v |= xlane_u<3>(v);
-  return v;
-}
-template <int LOGP>
 __device__ __forceinline__ uint32_t group_umax(uint32_t v) {
   if constexpr (LOGP >= 1) v = max(v, xlane_u<0>(v));
   if constexpr (LOGP >= 2) v = max(v, xlane_u<1>(v));
@@ -598,38 +590,35 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
 
   if constexpr (CodecInfo<C>::uni) {
     constexpr int TOP = (1 << BITS) - 1;
+    // the lane's extremes by IEEE minimum/maximum, which return NaN when
+    // any element is NaN; the group's by the hardware min/max, which skip a
+    // NaN partner (a lane's own NaN already sends the segment raw)
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int e = 1; e < E; e++) {
-      mn = fminf(mn, x[e]);
-      mx = fmaxf(mx, x[e]);
+      mn = __builtin_elementwise_minimum(mn, x[e]);
+      mx = __builtin_elementwise_maximum(mx, x[e]);
     }
+    const bool lane_nan = mn != mn;
     group_minmax_dpp<LOGP>(mn, mx);
     mn = mn + 0.0f;                      // a zero extreme is +0, whichever zeros the vector holds
     mx = mx + 0.0f;
     const float sig = materialize_f32(div_const<TOP>(mx - mn));   // RN to binary32, then to FP16
     const float mh = f16_round(mn), sh = f16_round(sig);
-    // +-Inf reach mn/mx and overflow the FP16 metadata; NaN is caught below
-    bad = !__builtin_isfinite(mh) || !__builtin_isfinite(sh);
+    // +-Inf reach mn/mx and overflow the FP16 metadata
+    bad = lane_nan || !__builtin_isfinite(mh) || !__builtin_isfinite(sh);
     const float y = sh == 0.0f ? 0.0f : recip_newton(sh);
     constexpr int MAGIC = 0x4B400000;   // bits of 1.5 * 2^23
-    uint32_t tor = 0;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
       uint32_t acc = 0;                  // sum over j of (MAGIC + code_j) << BITS*j
 #pragma unroll
       for (int j = 7; j >= 0; j--) {
         const int t = uniform_code_bits(x[8 * k + j] - mh, sh, y);
-        tor |= (uint32_t)t;
         acc = (acc << BITS) + (uint32_t)min(max(t, MAGIC), MAGIC + TOP);
       }
       store_codes<D, BITS>(slot, cv, k, ln.p, acc - magic_sum<BITS>(), 0);
     }
-    // For finite inputs every t lies in (2^22, 2^45) in magnitude (d is
-    // bounded by the FP16 range of the metadata and 1/sigma_h by 2^24), so
-    // bit 29 (exponent bit 6) of t is clear; a NaN source value makes t NaN,
-    // which sets it.
-    bad |= (int)((group_or<LOGP>(tor) >> 29) & 1u);
     if (ln.p == 0) *byte_at(reinterpret_cast<uint32_t*>(slot), mv) = f16_bits(mh) | (f16_bits(sh) << 16);
   }
 
