@@ -608,7 +608,7 @@ __global__ __launch_bounds__(64) void ans_decode_kernel(CallParams p) {
   const uint8_t* const heap = p.buf + spill;
   if constexpr (CRC) {
     __syncthreads();                                             // CRC tables in LDS
-    if (crc32_lanes<64, false>(GlobalBytes{heap}, stored, ct, p.tables) != h1.z) {
+    if (crc32_lanes<64, kCarryChain>(GlobalBytes{heap}, stored, ct, p.tables) != h1.z) {
       if (report) p.seg_status[seg] = 3;
       return;
     }

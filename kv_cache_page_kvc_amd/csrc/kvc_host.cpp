@@ -180,6 +180,13 @@ void build_crc_tables(CrcTables& c) {
       for (int b = 0; b < 16; b++) s = zero_byte(s);
     }
   }
+  for (int lvl = 0; lvl < kCrcLevels; lvl++)
+    for (int k = 0; k < 8; k++)
+      for (uint32_t v = 0; v < 16; v++) {
+        uint32_t r = v << (4 * k);
+        for (uint32_t i = 0; i < (16u << lvl); i++) r = zero_byte(r);
+        c.lv[lvl][k][v] = r;
+      }
 }
 
 void build_tables(Tables& t) {

@@ -75,12 +75,16 @@ struct CellEntry {
 // coefficient of x^0.
 constexpr int kCrcLanes = 64;               // lanes of a wave
 constexpr int kCrcLaneSets = 3;             // N = 64, 128, 256
+constexpr int kCrcLevels = 8;               // log2 of the largest N
 struct CrcTables {
   uint32_t t[8][16];                        // register after a word whose only nonzero nibble k is v, from a zero register
   uint32_t tj[kCrcLaneSets][8][16];         // t[k][v] carried over 16 (64 * 2^w - 1) more zero bytes
   uint32_t pw64[8][64][4];                  // x^i * s_j mod P for N = 64, 128, 256
   uint32_t pw128[8][128][4];
   uint32_t pw256[8][256][4];
+  // lv[b][k][v]: the register v << 4k carried over 16 * 2^b zero bytes, i.e.
+  // multiplied by x^(128 * 2^b) mod P (a pairwise combination of lanes)
+  uint32_t lv[kCrcLevels][8][16];
 };
 static_assert(sizeof(CrcTables) % 16 == 0, "CRC tables are copied in 16-byte units");
 // the part of CrcTables one kernel keeps in LDS: t and its lane count's tj

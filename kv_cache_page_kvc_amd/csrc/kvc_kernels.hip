@@ -926,17 +926,70 @@ __device__ __forceinline__ void load_crc_tables(CrcLds* dst, const CrcTables* sr
   }
 }
 
+// How crc32_lanes carries each lane's register over the units after its
+// last one (NT - 1 - lane of them):
+// - kCarryPowers: r * s_lane as the xor of the 32 powers x^i * s_lane
+//   selected by r's bits (eight 16-byte loads per lane, in flight during the
+//   loop), then an xor over the lanes; the encode kernels' form;
+// - kCarryChain: the same product from s_lane alone, multiplied by x
+//   between the 32 steps (one-wave decode, the entropy stage's decode);
+// - kCarryTree: no per-lane carry; lanes are combined in pairs, log2(NT)
+//   levels deep, level b multiplying the lower lane's register by
+//   x^(128 * 2^b) from nibble tables in LDS (multi-wave decode).
+enum { kCarryPowers = 0, kCarryChain = 1, kCarryTree = 2 };
+
+// Levels of the pairwise lane combination an NT-lane workgroup uses:
+// log2(NT), multipliers x^(128 * 2^b) for b < log2(NT)
+template <int NT>
+constexpr int crc_levels() { return NT == 64 ? 6 : (NT == 128 ? 7 : 8); }
+
+// The lane carry of the decode kernels: the level tables (3.5-4 KiB) pay
+// for themselves in multi-wave workgroups; a one-wave workgroup, whose slot
+// may be a single KiB, measured faster with the chain and no extra tables
+template <int NT>
+constexpr int decode_crc_carry() { return NT > 64 ? kCarryTree : kCarryChain; }
+
+// The level tables in LDS, for kernels built with CRC that combine lanes in
+// a tree (as crc_tables_lds)
+template <int NT, bool CRC>
+__device__ __forceinline__ uint32_t (*crc_levels_lds())[8][16] {
+  if constexpr (CRC && decode_crc_carry<NT>() == kCarryTree) {
+    __shared__ uint32_t s_crc_levels[crc_levels<NT>()][8][16];
+    return s_crc_levels;
+  } else {
+    return nullptr;
+  }
+}
+
+// Copy the level tables into LDS: every thread issues its loads before its
+// first store (the caller synchronises before the first use)
+template <int NT>
+__device__ __forceinline__ void load_crc_levels(uint32_t (*dst)[8][16], const CrcTables* src) {
+  constexpr uint32_t kUnits = crc_levels<NT>() * sizeof(src->lv[0]) / 16;
+  constexpr int R = (kUnits + NT - 1) / NT;
+  const uint4* from = reinterpret_cast<const uint4*>(src->lv);
+  uint4 w[R];
+#pragma unroll
+  for (int r = 0; r < R; r++)
+    w[r] = threadIdx.x + r * NT < kUnits ? ld_global16(from + threadIdx.x + r * NT) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < R; r++)
+    if (threadIdx.x + r * NT < kUnits) reinterpret_cast<uint4*>(dst)[threadIdx.x + r * NT] = w[r];
+}
+
 // CRC32 of n bytes; load(o) returns the 16 bytes at offset o of the range
 // (o a multiple of 16).  When n is not a multiple of 16 the 16-byte unit
 // holding the last bytes must be readable as a whole.  Called by all NT
 // threads of the workgroup (with NT > 64 it synchronises them); every thread
-// returns the CRC.  tables: the call's tables (the lanes' powers).  ENC
-// selects the encode kernels' form (byte-select masks; the final carry from
-// all 32 powers x^i * s_lane, eight 16-byte loads in flight during the
-// loop) or the decode kernels' (plain masks; the carry from s_lane alone,
-// multiplied by x between the 32 steps): each measured faster where used.
-template <int NT, bool ENC, class Load>
-__device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, const CrcLds* ct, const Tables* tables) {
+// returns the CRC.  tables: the call's tables (the lanes' powers); lv: the
+// level tables in LDS (kCarryTree only).  CARRY picks the lane carry (see
+// above); the encode form also masks nibbles with byte-select ANDs.  Each
+// form measured faster where it is used.
+template <int NT, int CARRY, class Load>
+__device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, const CrcLds* ct, const Tables* tables,
+                                                const uint32_t (*lv)[8][16] = nullptr) {
+  constexpr bool ENC = CARRY == kCarryPowers;
+  constexpr int NPW = CARRY == kCarryPowers ? 8 : (CARRY == kCarryChain ? 1 : 0);
   const uint32_t lane = threadIdx.x;
   const uint32_t units = n >> 4;
   // virtual zero units in front make the unit count a multiple of NT (a zero
@@ -944,10 +997,12 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
   const uint32_t pad = (NT - (units & (NT - 1))) & (NT - 1);
   const uint32_t rounds = (units + pad) / NT;
   // x^i * s_lane (s_lane = x^(128 (NT - 1 - lane))), as [i / 4][lane][i % 4]
-  const uint4* pws = crc_lane_powers<NT>(tables) + lane;
-  uint4 pw[ENC ? 8 : 1];
+  uint4 pw[NPW > 0 ? NPW : 1];
+  if constexpr (NPW > 0) {
+    const uint4* pws = crc_lane_powers<NT>(tables) + lane;
 #pragma unroll
-  for (int g = 0; g < (ENC ? 8 : 1); g++) pw[g] = ld_global16(pws + g * NT);
+    for (int g = 0; g < NPW; g++) pw[g] = ld_global16(pws + g * NT);
+  }
   uint32_t r = 0;
   // each round's unit is loaded one round ahead; only round 0 holds padding
   // (q < 0: a zero unit in front, over which the register stays zero)
@@ -967,29 +1022,47 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
     }
     w = wn;
   }
-  // carry each register over the units after its last one (NT - 1 - lane):
-  // r * s_lane, the xor of x^i * s_lane over the coefficients i set in r
-  // (coefficient i is bit 31 - i)
-  uint32_t c = 0;
-  if constexpr (ENC) {
+  if constexpr (CARRY == kCarryTree) {
+    // after level b, lane j (a multiple of 2^(b+1)) holds the register of
+    // lanes j .. j + 2^(b+1) - 1 carried to the end of the last one's unit:
+    // lane j's level-(b-1) register times x^(128 * 2^b), xor lane j + 2^b's
 #pragma unroll
-    for (int g = 0; g < 8; g++) {
-      c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g)) >> 31), pw[g].x);
-      c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 1)) >> 31), pw[g].y);
-      c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 2)) >> 31), pw[g].z);
-      c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 3)) >> 31), pw[g].w);
+    for (int b = 0; b < 6; b++) r = crc_word<false>(r, lv[b]) ^ __shfl_down(r, 1 << b, kCrcLanes);
+    if constexpr (NT == kCrcLanes) {
+      r = __builtin_amdgcn_readfirstlane(r);
+    } else {
+      // wave w's register (its lane 0), carried over the 64 units per round
+      // of each later wave: times x^(128 * 64 * (NT / 64 - 1 - w))
+      const uint32_t later = NT / kCrcLanes - 1 - lane / kCrcLanes;
+      if (later & 1) r = crc_word<false>(r, lv[6]);
+      if constexpr (NT > 2 * kCrcLanes)
+        if (later & 2) r = crc_word<false>(r, lv[7]);
     }
   } else {
-    uint32_t v = pw[0].x;
+    // carry each register over the units after its last one (NT - 1 - lane):
+    // r * s_lane, the xor of x^i * s_lane over the coefficients i set in r
+    // (coefficient i is bit 31 - i)
+    uint32_t c = 0;
+    if constexpr (CARRY == kCarryPowers) {
 #pragma unroll
-    for (int i = 0; i < 32; i++) {
-      c = xor_and(c, (uint32_t)((int32_t)(r << i) >> 31), v);
-      if (i < 31) v = xor_and(v >> 1, 0u - (v & 1u), 0xEDB88320u);   // v * x
+      for (int g = 0; g < 8; g++) {
+        c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g)) >> 31), pw[g].x);
+        c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 1)) >> 31), pw[g].y);
+        c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 2)) >> 31), pw[g].z);
+        c = xor_and(c, (uint32_t)((int32_t)(r << (4 * g + 3)) >> 31), pw[g].w);
+      }
+    } else {
+      uint32_t v = pw[0].x;
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        c = xor_and(c, (uint32_t)((int32_t)(r << i) >> 31), v);
+        if (i < 31) v = xor_and(v >> 1, 0u - (v & 1u), 0xEDB88320u);   // v * x
+      }
     }
-  }
-  r = c;
+    r = c;
 #pragma unroll
-  for (int m = kCrcLanes / 2; m >= 1; m >>= 1) r ^= __shfl_xor(r, m, kCrcLanes);
+    for (int m = kCrcLanes / 2; m >= 1; m >>= 1) r ^= __shfl_xor(r, m, kCrcLanes);
+  }
   if constexpr (NT > kCrcLanes) {                                // xor the waves' registers
     __shared__ uint32_t s_part[NT / kCrcLanes];
     if ((lane & (kCrcLanes - 1)) == 0) s_part[lane / kCrcLanes] = r;
@@ -1050,7 +1123,7 @@ __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const La
 template <int NT>
 __device__ __forceinline__ uint32_t crc32_written(const uint8_t* b, uint32_t n, const CrcLds* ct, const Tables* tables) {
   __syncthreads();
-  return crc32_lanes<NT, true>(GlobalBytes{b}, n, ct, tables);
+  return crc32_lanes<NT, kCarryPowers>(GlobalBytes{b}, n, ct, tables);
 }
 
 // ------------------------------------------------------------------ encode kernel
@@ -1153,7 +1226,7 @@ __global__ __launch_bounds__(NT) void encode_kernel(CallParams p) {
   const int any_bad = __syncthreads_or(bad);
   const uint32_t aux = codec == C_FP8F ? __float_as_uint(fixed) : 0u;
   if (staged && !any_bad) {
-    const uint32_t c = crc ? crc32_lanes<NT, true>(LdsBytes{s_stage + stored_at}, payload, ct, p.tables) : 0u;
+    const uint32_t c = crc ? crc32_lanes<NT, kCarryPowers>(LdsBytes{s_stage + stored_at}, payload, ct, p.tables) : 0u;
     // header + body from unit 0, so every wave store covers whole lines
     // the header goes into the image's first 32 bytes; the threads that
     // store them read them back below, in order after their own LDS stores
@@ -1428,6 +1501,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   __shared__ float s_cent[32];
   extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];   // p.stage_bytes
   CrcLds* const ct = crc_tables_lds<CRC>();
+  uint32_t (*const lvs)[8][16] = crc_levels_lds<NT, CRC>();
   const uint32_t seg = p.seg_base + blockIdx.x;       // segments [seg_base, seg_base + grid)
   const uint32_t two_n = 2u * p.n_pages;
   const uint32_t l = seg / two_n;
@@ -1462,7 +1536,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   // loads (header and codes together); otherwise the header is read first.
   const uint32_t slot_bytes = E.slot_bytes;
   const bool staged = codec != C_RAW && slot_bytes <= p.stage_bytes;
-  if constexpr (CRC) load_crc_tables<NT>(ct, &p.tables->crc);
+  if constexpr (CRC) {
+    load_crc_tables<NT>(ct, &p.tables->crc);
+    if constexpr (decode_crc_carry<NT>() == kCarryTree) load_crc_levels<NT>(lvs, &p.tables->crc);
+  }
   // TurboQuant centroids (negated in s_cent[16..31]) and the lane's signs.
   // A one-wave workgroup, whose life is mostly memory latency, issues their
   // loads with the slot's; larger ones load them once the slot is in LDS
@@ -1520,9 +1597,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   // the stored bytes must match the header's CRC32 before the page is written
   if constexpr (CRC) {
     __syncthreads();                                      // CRC tables in LDS
-    const uint32_t c = raw_data ? crc32_lanes<NT, false>(GlobalBytes{p.buf + spill}, stored, ct, p.tables)
-                       : staged ? crc32_lanes<NT, false>(LdsBytes{s_stage + stored_at}, stored, ct, p.tables)
-                                : crc32_lanes<NT, false>(GlobalBytes{s.slot + stored_at}, stored, ct, p.tables);
+    const uint32_t c =
+        raw_data ? crc32_lanes<NT, decode_crc_carry<NT>()>(GlobalBytes{p.buf + spill}, stored, ct, p.tables, lvs)
+        : staged ? crc32_lanes<NT, decode_crc_carry<NT>()>(LdsBytes{s_stage + stored_at}, stored, ct, p.tables, lvs)
+                 : crc32_lanes<NT, decode_crc_carry<NT>()>(GlobalBytes{s.slot + stored_at}, stored, ct, p.tables, lvs);
     if (c != h1.z) {
       if (p.seg_status && threadIdx.x == 0) p.seg_status[seg] = 3;
       return;
