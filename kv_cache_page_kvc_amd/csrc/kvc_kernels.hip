@@ -1004,23 +1004,27 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
     for (int g = 0; g < NPW; g++) pw[g] = ld_global16(pws + g * NT);
   }
   uint32_t r = 0;
-  // each round's unit is loaded one round ahead; only round 0 holds padding
-  // (q < 0: a zero unit in front, over which the register stays zero)
+  // each round's unit is loaded one round ahead.  Only round 0 holds
+  // padding (q < 0): a zero unit, over which the register stays zero.  The
+  // initial register 0xFFFFFFFF is the inverted first word of unit 0.  Every
+  // round but the last ends in the jump tables, the last in the plain ones.
   const int32_t q0 = (int32_t)lane - (int32_t)pad;
   uint4 w = make_uint4(0, 0, 0, 0);
   if (rounds && q0 >= 0) w = load(16u * (uint32_t)q0);
-  for (uint32_t k = 0; k < rounds; k++) {
-    const int32_t q = q0 + (int32_t)(k * NT);
-    uint4 wn = make_uint4(0, 0, 0, 0);
-    if (k + 1 < rounds) wn = load(16u * (uint32_t)(q + NT));
-    if (q >= 0) {
-      if (q == 0) w.x = ~w.x;
-      r = crc_word<ENC>(r ^ w.x, ct->t);
-      r = crc_word<ENC>(r ^ w.y, ct->t);
-      r = crc_word<ENC>(r ^ w.z, ct->t);
-      r = crc_word<ENC>(r ^ w.w, k + 1 < rounds ? ct->tj : ct->t);
-    }
+  if (q0 == 0) w.x = ~w.x;
+  for (uint32_t k = 0; k + 1 < rounds; k++) {
+    const uint4 wn = load(16u * (uint32_t)(q0 + (int32_t)((k + 1) * NT)));   // q0 + NT > 0
+    r = crc_word<ENC>(r ^ w.x, ct->t);
+    r = crc_word<ENC>(r ^ w.y, ct->t);
+    r = crc_word<ENC>(r ^ w.z, ct->t);
+    r = crc_word<ENC>(r ^ w.w, ct->tj);
     w = wn;
+  }
+  if (rounds) {
+    r = crc_word<ENC>(r ^ w.x, ct->t);
+    r = crc_word<ENC>(r ^ w.y, ct->t);
+    r = crc_word<ENC>(r ^ w.z, ct->t);
+    r = crc_word<ENC>(r ^ w.w, ct->t);
   }
   if constexpr (CARRY == kCarryTree) {
     // after level b, lane j (a multiple of 2^(b+1)) holds the register of
