@@ -1008,11 +1008,14 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
   // padding (q < 0): a zero unit, over which the register stays zero.  The
   // initial register 0xFFFFFFFF is the inverted first word of unit 0.  Every
   // round but the last ends in the jump tables, the last in the plain ones.
+  // A wave whose lanes all hold padding in round 0 starts at round 1.
   const int32_t q0 = (int32_t)lane - (int32_t)pad;
+  const uint32_t k0 = __builtin_amdgcn_readfirstlane(rounds && (int32_t)(lane | (kCrcLanes - 1)) < (int32_t)pad);
   uint4 w = make_uint4(0, 0, 0, 0);
-  if (rounds && q0 >= 0) w = load(16u * (uint32_t)q0);
-  if (q0 == 0) w.x = ~w.x;
-  for (uint32_t k = 0; k + 1 < rounds; k++) {
+  const int32_t qf = q0 + (int32_t)(k0 * NT);
+  if (k0 < rounds && qf >= 0) w = load(16u * (uint32_t)qf);
+  if (qf == 0) w.x = ~w.x;
+  for (uint32_t k = k0; k + 1 < rounds; k++) {
     const uint4 wn = load(16u * (uint32_t)(q0 + (int32_t)((k + 1) * NT)));   // q0 + NT > 0
     r = crc_word<ENC>(r ^ w.x, ct->t);
     r = crc_word<ENC>(r ^ w.y, ct->t);
@@ -1020,7 +1023,7 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
     r = crc_word<ENC>(r ^ w.w, ct->tj);
     w = wn;
   }
-  if (rounds) {
+  if (rounds > k0) {
     r = crc_word<ENC>(r ^ w.x, ct->t);
     r = crc_word<ENC>(r ^ w.y, ct->t);
     r = crc_word<ENC>(r ^ w.z, ct->t);
