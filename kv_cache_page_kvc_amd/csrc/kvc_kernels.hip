@@ -1539,8 +1539,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(CallParams p) {
   s.row_bytes = p.row_bytes;
   const uint32_t raw_bytes = (uint32_t)s.n_vec * D * 2;
 
-  // A coded slot that fits is read whole into LDS in one round of 16-byte
-  // loads (header and codes together); otherwise the header is read first.
+  // A coded slot that fits is read whole into LDS with 16-byte loads (header
+  // and codes together); otherwise the header is read first.
   const uint32_t slot_bytes = E.slot_bytes;
   const bool staged = codec != C_RAW && slot_bytes <= p.stage_bytes;
   if constexpr (CRC) {
