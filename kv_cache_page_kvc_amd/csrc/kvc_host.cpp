@@ -303,8 +303,8 @@ struct Plan {
   uint64_t per_page = 0;      // slot bytes of one page over all layers
   uint64_t encodable = 0;     // segments not raw by policy
   uint64_t ans = 0;           // of which KVC_ANS16 (payload in the spill region)
-  bool light = true;          // every component raw, FP8 direct, FP8 dynamic or ANS16 (no
-                              // per-element divide or TurboQuant/uniform arithmetic in encode)
+  bool light = true;          // every component raw, FP8 (direct, dynamic or fixed) or ANS16: no
+                              // TurboQuant, uniform or INT8 arithmetic in encode
 };
 
 // Fill p (whose arrays hold at least L->layers entries).
@@ -324,7 +324,8 @@ void fill_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages, Plan& 
       page += sz;
       if (e != KVC_RAW) p.encodable += n_pages;
       if (e == KVC_ANS16) p.ans += n_pages;
-      if (e != KVC_RAW && e != KVC_FP8_DIRECT && e != KVC_FP8_DYNAMIC && e != KVC_ANS16) p.light = false;
+      if (e != KVC_RAW && e != KVC_FP8_DIRECT && e != KVC_FP8_DYNAMIC && e != KVC_FP8_FIXED && e != KVC_ANS16)
+        p.light = false;
     }
     if (p.layer_off) p.layer_off[l] = off;
     p.per_page += page;
@@ -629,7 +630,7 @@ uint32_t workgroup_threads(const kvc_layout* L, uint32_t big) {
   return seg_bytes <= kSmallSegmentBytes ? (uint32_t)kThreadsSmall : big;
 }
 // Encode: a call whose components all encode with little arithmetic per
-// element (raw, FP8 direct, FP8 dynamic) runs one wave per segment at every
+// element (raw, FP8 direct, dynamic or fixed) runs one wave per segment at every
 // size when it has segments enough to keep 32 in flight on each of 256 CUs
 // -- more segments in flight per CU; the others run two waves above
 // kSmallSegmentBytes.

@@ -551,8 +551,11 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
     // binary32 first, then to BF16
     if constexpr (C == C_I8R)
       s = bf16_round(materialize_f32(div_const<127>(fmaxf(bits_to_f32<DT>(am), bf16_round(1e-12f)))));
-    // per-vector scales (not the caller's fixed scale) divide through RN(1/s)
-    const float rs = C == C_FP8Y || C == C_INT8 || C == C_I8R ? 1.0f / s : 0.0f;
+    // per-vector scales divide through RN(1/s); so does the caller's fixed
+    // scale within [2^-60, 2^60], where the shortcut is the IEEE quotient
+    // (outside, only the IEEE division is used)
+    const float rs = C == C_FP8Y || C == C_INT8 || C == C_I8R || C == C_FP8F ? 1.0f / s : 0.0f;
+    const bool fixed_short = C == C_FP8F && s >= 0x1p-60f && s <= 0x1p60f;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
       uint32_t lo, hi;
@@ -572,7 +575,7 @@ __device__ __forceinline__ int encode_vector(uint4* w, uint32_t cv, uint32_t mv,
         for (int j = 0; j < 8; j++) {
           float t = x[8 * k + j];
           if constexpr (C == C_FP8Y) t = div_scaled(t, s, rs);
-          if constexpr (C == C_FP8F) t = t / s;
+          if constexpr (C == C_FP8F) t = fixed_short ? div_scaled(t, s, rs) : t / s;
           if constexpr (C != C_FP8D) t = fminf(fmaxf(t, -448.0f), 448.0f);
           q[j] = t;
         }

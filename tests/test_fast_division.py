@@ -8,6 +8,9 @@ one FMA correction.  `fast_division_check.c` and
 `fast_division_scaled_check.c` run the same binary32 sequences over every
 input they can see and count results that differ from the correctly
 rounded quotient, or, for the scaled quotients, the stored codes that differ.
+`fast_division_fixed_check.c` checks the same shortcut for a caller's FP8
+fixed scale, where the scales cannot all be enumerated: every source value
+against 256 scales in each binade the kernels take it for.
 `fast_norm_check.c` does the same for the TurboQuant norm and its
 reciprocal in the encoder's common case.
 """
@@ -70,6 +73,31 @@ def test_scaled_division_gives_identical_codes(scaled, codec, src):
     assert (badc if codec != "fp8dyn" else badf) == 0
     if src == "fp16":
         assert badq == 0
+
+
+@pytest.fixture(scope="module")
+def fixed(tmp_path_factory):
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path_factory.mktemp("fastdiv_fixed") / "check")
+    subprocess.run([gcc, "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-o", exe,
+                    os.path.join(HERE, "fast_division_fixed_check.c"), "-lm"], check=True)
+    env = dict(os.environ, OMP_NUM_THREADS=str(min(16, os.cpu_count() or 1)))
+    out = subprocess.run([exe], check=True, capture_output=True, text=True, env=env, timeout=600).stdout
+    return {ln.split()[0]: tuple(int(v) for v in ln.split()[1:]) for ln in out.splitlines()}
+
+
+@pytest.mark.parametrize("src", ["bf16", "fp16"])
+def test_fixed_scale_division_gives_identical_codes(fixed, src):
+    """The FP8 fixed-scale shortcut (the same sequence as above, with the
+    caller's scale in [2^-60, 2^60]) against the IEEE quotient: every source
+    value 0 <= x <= 448 against 256 scales per binade.  Markstein's theorem
+    makes it exact wherever no step underflows, which covers every quotient
+    that is not mapped to FP8 zero; no counted case differs."""
+    bad, cases = fixed[f"fixed_{src}"]
+    assert cases == (0x43E0 + 1 if src == "bf16" else 0x5F00 + 1) * (120 * 256 + 1)
+    assert bad == 0
 
 
 def test_rans_reciprocal_division_exact():

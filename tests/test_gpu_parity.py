@@ -204,6 +204,30 @@ def test_fp8_scaled_quotients(ctx):
     _roundtrip_case(ctx, wl, "FP8_FIXED", "FP8_DYNAMIC", 0, ids, fixed=fixed)
 
 
+def test_fp8_fixed_scales_around_the_division_shortcut(ctx):
+    """FP8 fixed scales below, at and above the bounds of the encoder's
+    division shortcut (2^-60 and 2^60; the IEEE division outside them), and
+    the host's own bounds 2^-100 and 2^100.  Layers with a scale below 1 hold
+    BF16 sources of about 64 times their scale, so their quotients span the
+    E4M3 range (clipping included); larger scales see N(0,1)-sized sources.
+    Slots bit-exact with the oracle's IEEE quotients, pages identical."""
+    print("[case] fp8 fixed scales around 2^-60 and 2^60", flush=True)
+    lo, hi = np.float32(2.0 ** -60), np.float32(2.0 ** 60)
+    scales = np.array([2.0 ** -100, 2.0 ** -80, np.nextafter(lo, np.float32(0)), lo, np.nextafter(lo, np.float32(1)),
+                       0.0123, np.nextafter(hi, np.float32(0)), hi, np.nextafter(hi, np.float32(np.inf)), 2.0 ** 100],
+                      np.float32)
+    L, H, D, T, pool = len(scales) // 2, 2, 128, 16, 12
+    fixed = scales.reshape(L, 2)
+    wl = G.Workload(L, H, D, T, pool, "bf16", "separate", 41)
+    for l in range(L):
+        for comp, t in ((0, wl.k[l]), (1, wl.v[l])):
+            s = float(fixed[l, comp])
+            if s < 1.0:
+                t.mul_(64.0 * s)
+    ids = np.arange(pool, dtype=np.int32)
+    _roundtrip_case(ctx, wl, "FP8_FIXED", "FP8_FIXED", 0, ids, fixed=fixed)
+
+
 def test_zero_and_tiny_vectors(ctx):
     """All-zero vectors (INT8/FP8 floor, TurboQuant n = 0, uniform sigma = 0)
     and subnormal-scale vectors."""
