@@ -303,8 +303,8 @@ struct Plan {
   uint64_t per_page = 0;      // slot bytes of one page over all layers
   uint64_t encodable = 0;     // segments not raw by policy
   uint64_t ans = 0;           // of which KVC_ANS16 (payload in the spill region)
-  bool light = true;          // every component raw, FP8 (direct, dynamic or fixed) or ANS16: no
-                              // TurboQuant, uniform or INT8 arithmetic in encode
+  bool light = true;          // every component raw, FP8 (direct, dynamic or fixed), INT8 or
+                              // ANS16: no TurboQuant, uniform or record arithmetic in encode
 };
 
 // Fill p (whose arrays hold at least L->layers entries).
@@ -324,7 +324,8 @@ void fill_plan(const kvc_layout* L, const kvc_codec* c, uint32_t n_pages, Plan& 
       page += sz;
       if (e != KVC_RAW) p.encodable += n_pages;
       if (e == KVC_ANS16) p.ans += n_pages;
-      if (e != KVC_RAW && e != KVC_FP8_DIRECT && e != KVC_FP8_DYNAMIC && e != KVC_FP8_FIXED && e != KVC_ANS16)
+      if (e != KVC_RAW && e != KVC_FP8_DIRECT && e != KVC_FP8_DYNAMIC && e != KVC_FP8_FIXED && e != KVC_INT8 &&
+          e != KVC_ANS16)
         p.light = false;
     }
     if (p.layer_off) p.layer_off[l] = off;
@@ -629,14 +630,16 @@ uint32_t workgroup_threads(const kvc_layout* L, uint32_t big) {
   const uint32_t seg_bytes = L->kv_heads * L->tokens_per_page * L->head_dim * 2;
   return seg_bytes <= kSmallSegmentBytes ? (uint32_t)kThreadsSmall : big;
 }
-// Encode: a call whose components all encode with little arithmetic per
-// element (raw, FP8 direct, dynamic or fixed) runs one wave per segment at every
-// size when it has segments enough to keep 32 in flight on each of 256 CUs
-// -- more segments in flight per CU; the others run two waves above
-// kSmallSegmentBytes.
+// Encode: a call without CRC32 whose components all encode with little
+// arithmetic per element (raw, FP8 direct, dynamic or fixed, INT8) runs one
+// wave per segment at every size when it has segments enough to keep 32 in
+// flight on each of 256 CUs -- more segments in flight per CU; the others
+// run two waves above kSmallSegmentBytes.  With CRC32 one wave measured
+// 7-16% slower for these calls (one wave's 64 lanes take twice the rounds
+// over the slot that two waves take).
 constexpr uint64_t kLightOneWaveSegments = 32 * 256;
 hipError_t run_encode(const CallParams& P, const kvc_layout* L, const Plan& plan, uint64_t nseg, hipStream_t s) {
-  const uint32_t nt = plan.light && nseg >= kLightOneWaveSegments
+  const uint32_t nt = plan.light && !P.crc && nseg >= kLightOneWaveSegments
                           ? (uint32_t)kThreadsSmall
                           : workgroup_threads(L, P.crc ? kEncodeThreadsCrc : kEncodeThreads);
   hipError_t e = all_ans(L, plan, P) ? hipSuccess : launch_encode(with_threads(P, L, nt), L->head_dim, nseg, s);

@@ -15,8 +15,9 @@ namespace kvc {
 // workgroup with little data in flight per wave, while one-wave workgroups
 // keep up to 32 segments in flight per CU -- else kEncodeThreads for encode
 // (two waves: the compute-heavy TurboQuant encode keeps more vectors in
-// flight per wave; a large call whose components all encode raw or FP8
-// keeps one wave) and kDecodeThreads for decode (four waves).
+// flight per wave; a large call without CRC32 whose components all encode
+// raw, FP8 or INT8 keeps one wave) and kDecodeThreads for decode (four
+// waves).
 constexpr int kEncodeThreads = 128;
 // encode with the CRC option: the CRC tables' LDS halves the workgroups a CU
 // holds, so four waves per workgroup keep as many waves in flight

@@ -982,10 +982,11 @@ def test_ans16_spill_capacity(ctx):
 @pytest.mark.parametrize("crc", [False, True])
 def test_fp8_large_call_one_wave_encode(ctx, crc):
     """A call of raw/FP8-direct/FP8-dynamic components with at least 32 x 256
-    segments encodes one wave per 32 KiB segment: 2 layers x 2048 pages x 8
-    heads x D128 BF16 (8192 segments), K FP8 dynamic, V FP8 direct, layer 1
-    protected, 1% of segments injected with values the FP8 gate keeps raw;
-    with and without CRC, sampled segments compared both ways."""
+    segments encodes one wave per 32 KiB segment without CRC32 (two waves
+    with it): 2 layers x 2048 pages x 8 heads x D128 BF16 (8192 segments), K
+    FP8 dynamic, V FP8 direct, layer 1 protected, 1% of segments injected
+    with values the FP8 gate keeps raw; with and without CRC, sampled
+    segments compared both ways."""
     print(f"[case] fp8 large call one-wave encode crc={crc}", flush=True)
     L, pages = 2, 2048
     wl = G.Workload(L, 8, 128, 16, pages, "bf16", "separate", seed=31)
