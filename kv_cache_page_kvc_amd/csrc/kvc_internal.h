@@ -19,8 +19,9 @@ namespace kvc {
 // raw, FP8 or INT8 keeps one wave) and kDecodeThreads for decode (four
 // waves).
 constexpr int kEncodeThreads = 128;
-// encode with the CRC option: the CRC tables' LDS halves the workgroups a CU
-// holds, so four waves per workgroup keep as many waves in flight
+// encode with the CRC option above kSmallSegmentBytes: two waves as well
+// (the 1 KiB of nibble tables leaves occupancy as it is; four waves would
+// give each wave fewer vectors but nearly as many CRC rounds)
 constexpr int kEncodeThreadsCrc = 128;
 constexpr int kDecodeThreads = 256;
 constexpr int kThreadsSmall = 64;
