@@ -17,7 +17,7 @@ namespace kvc {
 // (two waves: the compute-heavy TurboQuant encode keeps more vectors in
 // flight per wave; a large call without CRC32 whose components all encode
 // raw, FP8 or INT8 keeps one wave) and kDecodeThreads for decode (four
-// waves).
+// waves; one at D = 256 without CRC32).
 constexpr int kEncodeThreads = 128;
 // encode with the CRC option above kSmallSegmentBytes: two waves as well
 // (the 1 KiB of nibble tables leaves occupancy as it is; four waves would
