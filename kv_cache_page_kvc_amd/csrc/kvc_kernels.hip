@@ -744,7 +744,7 @@ __device__ __forceinline__ int encode_segment_vectors(const SegCtx& s, const Lan
 // nontemporal stores, for a destination whose lines each store covers whole
 // (the 256-byte aligned spill copies; a slot body starts 32 bytes into a line)
 template <int D, int NT, bool STREAM>
-__device__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
+__device__ __forceinline__ void copy_out_raw(const SegCtx& s, const Lane& ln, uint8_t* dst) {
   constexpr int P = Geo<D>::P, NCH = Geo<D>::NCH, GW = Geo<D, NT>::GW, U = Geo<D>::U;
   uint4 w[U][NCH];
   VecPos pos = vec_pos(s, ln.g);
@@ -986,12 +986,11 @@ __device__ __forceinline__ void load_crc_levels(uint32_t (*dst)[8][16], const Cr
 // threads of the workgroup (with NT > 64 it synchronises them); every thread
 // returns the CRC.  tables: the call's tables (the lanes' powers); lv: the
 // level tables in LDS (kCarryTree only).  CARRY picks the lane carry (see
-// above); the encode form also masks nibbles with byte-select ANDs.  Each
-// form measured faster where it is used.
-template <int NT, int CARRY, class Load>
+// above); ENC masks nibbles with byte-select ANDs (the encode kernels').
+// Each form measured faster where it is used.
+template <int NT, int CARRY, bool ENC = CARRY == kCarryPowers, class Load>
 __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, const CrcLds* ct, const Tables* tables,
                                                 const uint32_t (*lv)[8][16] = nullptr) {
-  constexpr bool ENC = CARRY == kCarryPowers;
   constexpr int NPW = CARRY == kCarryPowers ? 8 : (CARRY == kCarryChain ? 1 : 0);
   const uint32_t lane = threadIdx.x;
   const uint32_t units = n >> 4;
@@ -1109,6 +1108,21 @@ struct LdsBytes {
   const uint8_t* p;
   __device__ __forceinline__ uint4 operator()(uint32_t o) const { return *reinterpret_cast<const uint4*>(p + o); }
 };
+// a range copied while its CRC is taken: each unit read from src is also
+// stored at the same offset of dst (crc32_lanes reads every unit once);
+// STREAM: nontemporal stores, for a destination whose lines the units cover
+// whole
+template <bool STREAM>
+struct CopiedBytes {
+  const uint8_t* src;
+  uint8_t* dst;
+  __device__ __forceinline__ uint4 operator()(uint32_t o) const {
+    const uint4 w = ld_stream16(src + o);
+    if constexpr (STREAM) st_stream16(dst + o, w);
+    else st_global16(dst + o, w);
+    return w;
+  }
+};
 
 template <int D, int DT, int NT>
 __device__ __forceinline__ int encode_codec(int codec, const SegCtx& s, const Lane& ln, float fixed,
@@ -1189,10 +1203,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 7
   if constexpr (CRC) load_crc_tables<NT>(ct, &p.tables->crc);
 
   const Lane ln = lane_info<D>();
+  // a page whose vectors follow each other (v at element v * D) is the raw
+  // slot body byte for byte: with CRC32 it is copied by the CRC's own pass
+  // (its carry from one power word: 32 held across the 16-byte units of a
+  // whole page would spill)
+  const bool contiguous = s.sh == (uint32_t)D && s.st == (uint32_t)s.heads * D;
   if (codec == C_RAW) {                                        // raw by policy
-    copy_out_raw<D, NT, false>(s, ln, s.slot + kHeaderBytes);
+    uint32_t c = 0;
+    if (crc && contiguous) {
+      c = crc32_lanes<NT, kCarryChain, true>(
+          CopiedBytes<false>{reinterpret_cast<const uint8_t*>(s.src), s.slot + kHeaderBytes}, raw_bytes, ct, p.tables);
+    } else {
+      copy_out_raw<D, NT, false>(s, ln, s.slot + kHeaderBytes);
+      if (crc) c = crc32_written<NT>(s.slot + kHeaderBytes, raw_bytes, ct, p.tables);
+    }
     zero_pad<NT>(s.slot, kHeaderBytes + raw_bytes, slot_bytes);
-    const uint32_t c = crc ? crc32_written<NT>(s.slot + kHeaderBytes, raw_bytes, ct, p.tables) : 0u;
     if (threadIdx.x == 0)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_POLICY | crc_flag, KVC_SEG_RAW_POLICY, DT,
                         comp, D, s.n_vec, raw_bytes, 0, 0, c);
@@ -1278,9 +1303,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 7
   __syncthreads();
   const uint64_t off = s_spill;
   const bool fits = p.slot_region + off + raw_bytes <= p.buf_bytes;
-  if (fits) copy_out_raw<D, NT, true>(s, ln, p.buf + p.slot_region + off);
   // a segment that was not stored (no spill space) carries no CRC
-  const uint32_t c = crc && fits ? crc32_written<NT>(p.buf + p.slot_region + off, raw_bytes, ct, p.tables) : 0u;
+  uint32_t c = 0;
+  if (fits && crc && contiguous) {
+    c = crc32_lanes<NT, kCarryChain, true>(
+        CopiedBytes<true>{reinterpret_cast<const uint8_t*>(s.src), p.buf + p.slot_region + off}, raw_bytes, ct,
+        p.tables);
+  } else if (fits) {
+    copy_out_raw<D, NT, true>(s, ln, p.buf + p.slot_region + off);
+    if (crc) c = crc32_written<NT>(p.buf + p.slot_region + off, raw_bytes, ct, p.tables);
+  }
   if (threadIdx.x == 0) {
     if (fits)
       write_header_desc(s.slot, desc, slot_off, KVC_RAW, KVC_FLAG_RAW_DATA | crc_flag, KVC_SEG_RAW_DATA, DT, comp,
