@@ -106,6 +106,17 @@ __device__ __forceinline__ uint32_t xlane_u(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, xlane_ctrl<Q>(), 0xF, 0xF, true);
 }
 
+// xor of x over the 64 lanes of the wave: over each row of 16 lanes by DPP
+// (partners lane ^ 1, ^ 2, ^ 7, ^ 8), then the four rows' results
+__device__ __forceinline__ uint32_t wave_xor(uint32_t x) {
+  x ^= xlane_u<0>(x);
+  x ^= xlane_u<1>(x);
+  x ^= xlane_u<3>(x);
+  x ^= xlane_u<2>(x);
+  return (uint32_t)(__builtin_amdgcn_readlane((int)x, 0) ^ __builtin_amdgcn_readlane((int)x, 16) ^
+                    __builtin_amdgcn_readlane((int)x, 32) ^ __builtin_amdgcn_readlane((int)x, 48));
+}
+
 template <int LOGP>
 __device__ __forceinline__ float group_sum(float v) {   // sum over element bits 3.. (ascending)
   if constexpr (LOGP >= 1) v = v + xlane<0>(v);
@@ -1086,9 +1097,7 @@ __device__ __forceinline__ uint32_t crc32_lanes(const Load& load, uint32_t n, co
         if (i < 31) v = xor_and(v >> 1, 0u - (v & 1u), 0xEDB88320u);   // v * x
       }
     }
-    r = c;
-#pragma unroll
-    for (int m = kCrcLanes / 2; m >= 1; m >>= 1) r ^= __shfl_xor(r, m, kCrcLanes);
+    r = wave_xor(c);
   }
   if constexpr (NT > kCrcLanes) {                                // xor the waves' registers
     __shared__ uint32_t s_part[NT / kCrcLanes];
